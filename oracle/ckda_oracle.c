@@ -1,0 +1,212 @@
+/*
+ * ckda_oracle.c -- fp64 sequential reference for the (Complex) Kimi Delta
+ * Attention recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file.  Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may use it.  It shares no code, header,
+ * table or helper with the HIP library: it includes only the C standard
+ * library and OpenMP.
+ *
+ * What it computes (written from the method's definition, not from any
+ * kernel design):
+ *
+ *   The transition of a gated delta-rule layer is
+ *       A_t = (I - beta_t k_t k_t^T) Diag(alpha_t)
+ *   (picx.dev summary of the Complex KDA paper, section "Background",
+ *   transition-matrix equation).  The state S is dk x dv; Diag(alpha_t)
+ *   scales its rows, so alpha carries one gate per key channel.  The full
+ *   update adds the rank-one write beta_t k_t v_t^T and the read-out uses
+ *   the updated state:
+ *       S_t = A_t S_{t-1} + beta_t k_t v_t^T,      o_t = scale * S_t^T q_t.
+ *   (The summary prints only A_t; the write term and the read-out are the
+ *   plainest reading consistent with it: a delta-rule write scaled by the
+ *   same beta.)
+ *
+ *   CKDA allows alpha in [-1,1]^dk and beta in [0,2]; KDA keeps alpha
+ *   positive (same summary, section "CKDA Definition").  The oracle does
+ *   not check ranges: it computes the formula as written for any values.
+ *
+ *   Optional query/key L2 normalisation happens inside the op, before the
+ *   recurrence, per (token, head) over the dk channels (dormouse review
+ *   "RoPE into the KDA q/k path", section 2 "Where the L2 norm lives"):
+ *       x_hat = x / sqrt(sum_c x_c^2 + eps).
+ *
+ * Evaluation order per token (the rank-one expansion of A_t S + beta k v^T):
+ *   1. S[c,:] *= alpha[c]                  (Diag(alpha) S)
+ *   2. w = S^T k                           (dv-vector)
+ *   3. S += beta * k (v - w)^T             ((I - beta k k^T) X + beta k v^T)
+ *   4. o = scale * S^T q
+ * Expanding 3 with X = Diag(alpha) S_{t-1} gives X - beta k k^T X + beta k v^T,
+ * which is exactly A_t S_{t-1} + beta k v^T.
+ *
+ * Layout (all row-major, last index fastest; tokens of all sequences packed):
+ *   q, k, alpha : [T_total][H][dk]     v, o : [T_total][H][dv]
+ *   beta        : [T_total][H]         h0, ht : [N][H][dk][dv]
+ *   seq_start   : [N+1], sequence n owns tokens seq_start[n] .. seq_start[n+1]-1
+ * A dense batch [B,T,H,...] is the packed layout with seq_start[n] = n*T.
+ * Sequences and heads are independent; OpenMP runs them in parallel.  Each
+ * (sequence, head) pair is computed by one thread in token order, so the
+ * result does not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+int32_t ckda_oracle_version(void) { return 1; }
+
+void ckda_oracle_set_num_threads(int32_t n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
+int32_t ckda_oracle_max_threads(void) { return (int32_t)omp_get_max_threads(); }
+
+/* x_hat = x / sqrt(sum x^2 + eps), in place, over d values. */
+static void l2_normalise(double* x, int32_t d, double eps) {
+  double ss = 0.0;
+  for (int32_t c = 0; c < d; ++c) ss += x[c] * x[c];
+  const double n = sqrt(ss + eps);
+  for (int32_t c = 0; c < d; ++c) x[c] /= n;
+}
+
+/* Row-wise L2 normalisation of a [rows][d] array (exported so the tests can
+ * pin the normalisation step on its own). */
+int32_t ckda_oracle_l2norm(int64_t rows, int32_t d, const double* x, double* y,
+                           double eps) {
+  if (rows < 0 || d <= 0 || (rows > 0 && (!x || !y))) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < rows; ++r) {
+    memcpy(y + r * d, x + r * d, sizeof(double) * (size_t)d);
+    l2_normalise(y + r * d, d, eps);
+  }
+  return ORACLE_OK;
+}
+
+/* One sequence, one head: runs tokens [t0, t1) in order on the state S. */
+static void run_head(int64_t t0, int64_t t1, int32_t h, int32_t H, int32_t dk,
+                     int32_t dv, const double* q, const double* k,
+                     const double* v, const double* alpha, const double* beta,
+                     double* S, double* o, int32_t use_l2norm, double scale,
+                     double eps, double* xq, double* xk, double* w) {
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t qk_off = (t * H + h) * (int64_t)dk;
+    const int64_t v_off = (t * H + h) * (int64_t)dv;
+    memcpy(xq, q + qk_off, sizeof(double) * (size_t)dk);
+    memcpy(xk, k + qk_off, sizeof(double) * (size_t)dk);
+    if (use_l2norm) {
+      l2_normalise(xq, dk, eps);
+      l2_normalise(xk, dk, eps);
+    }
+    const double* a = alpha + qk_off;
+    const double b = beta[t * H + h];
+    const double* vt = v + v_off;
+
+    /* 1. Diag(alpha) S: channel c of the key space scales row c. */
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= a[c];
+
+    /* 2. w = S^T k. */
+    for (int32_t j = 0; j < dv; ++j) w[j] = 0.0;
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) w[j] += S[c * dv + j] * xk[c];
+
+    /* 3. S += beta k (v - w)^T. */
+    for (int32_t c = 0; c < dk; ++c) {
+      const double bk = b * xk[c];
+      for (int32_t j = 0; j < dv; ++j) S[c * dv + j] += bk * (vt[j] - w[j]);
+    }
+
+    /* 4. o = scale S^T q (read-out after the update). */
+    double* ot = o + v_off;
+    for (int32_t j = 0; j < dv; ++j) ot[j] = 0.0;
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) ot[j] += S[c * dv + j] * xq[c];
+    for (int32_t j = 0; j < dv; ++j) ot[j] *= scale;
+  }
+}
+
+/*
+ * Full forward over N packed sequences.  h0 may be NULL (zero initial
+ * state); ht may be NULL (final state not returned).  o must hold
+ * seq_start[N] * H * dv values.
+ */
+int32_t ckda_oracle_fwd(int32_t N, const int64_t* seq_start, int32_t H,
+                        int32_t dk, int32_t dv, const double* q,
+                        const double* k, const double* v, const double* alpha,
+                        const double* beta, const double* h0, double* o,
+                        double* ht, int32_t use_l2norm, double scale,
+                        double eps) {
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || !seq_start) return ORACLE_BAD_ARG;
+  if (seq_start[0] != 0) return ORACLE_BAD_ARG;
+  for (int32_t n = 0; n < N; ++n)
+    if (seq_start[n + 1] < seq_start[n]) return ORACLE_BAD_ARG;
+  if (seq_start[N] > 0 && (!q || !k || !v || !alpha || !beta || !o))
+    return ORACLE_BAD_ARG;
+
+  int32_t failed = 0;
+  const int64_t pairs = (int64_t)N * H;
+#pragma omp parallel
+  {
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+    double* xq = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* xk = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* w = (double*)malloc(sizeof(double) * (size_t)dv);
+    const int ok = S && xq && xk && w;
+    if (!ok) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t p = 0; p < pairs; ++p) {
+      if (!ok) continue;
+      const int32_t n = (int32_t)(p / H);
+      const int32_t h = (int32_t)(p % H);
+      const size_t sz = (size_t)dk * (size_t)dv;
+      const int64_t st_off = ((int64_t)n * H + h) * (int64_t)sz;
+      if (h0)
+        memcpy(S, h0 + st_off, sizeof(double) * sz);
+      else
+        memset(S, 0, sizeof(double) * sz);
+      run_head(seq_start[n], seq_start[n + 1], h, H, dk, dv, q, k, v, alpha,
+               beta, S, o, use_l2norm, scale, eps, xq, xk, w);
+      if (ht) memcpy(ht + st_off, S, sizeof(double) * sz);
+    }
+    free(S);
+    free(xq);
+    free(xk);
+    free(w);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * One decode step for N independent sequences (one token each): the same
+ * per-token body as the forward, applied to the state cache.  state is
+ * [N][H][dk][dv] and is updated in place; q,k,alpha are [N][H][dk],
+ * v and o are [N][H][dv], beta is [N][H].
+ */
+int32_t ckda_oracle_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                         const double* q, const double* k, const double* v,
+                         const double* alpha, const double* beta,
+                         double* state, double* o, int32_t use_l2norm,
+                         double scale, double eps) {
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return ORACLE_BAD_ARG;
+  if (N == 0) return ORACLE_OK;
+  if (!q || !k || !v || !alpha || !beta || !state || !o) return ORACLE_BAD_ARG;
+  int64_t* starts = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + 1));
+  if (!starts) return ORACLE_NO_MEMORY;
+  for (int32_t n = 0; n <= N; ++n) starts[n] = n;
+  /* The state is both the initial and the final state: each (n,h) block is
+   * copied in before its tokens run and copied out afterwards by the same
+   * thread, so aliasing h0 and ht is safe here. */
+  const int32_t rc = ckda_oracle_fwd(N, starts, H, dk, dv, q, k, v, alpha,
+                                     beta, state, o, state, use_l2norm, scale,
+                                     eps);
+  free(starts);
+  return rc;
+}
