@@ -1,0 +1,205 @@
+"""Python binding of libckda.so: (Complex) Kimi Delta Attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/ckda.h``.  Tensors are torch CUDA
+(HIP) tensors; calls are asynchronous on the current stream.  If the shared
+library is missing the calls raise -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["chunk_fwd", "recurrent_step", "l2norm_debug", "fwd_supported",
+           "library_path", "abi_version", "CkdaError", "BF16", "F32", "GATE_KDA",
+           "GATE_CKDA"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libckda.so")
+_lock = threading.Lock()
+_lib = None
+
+BF16, F32 = 0, 1
+GATE_KDA, GATE_CKDA = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
+
+
+class CkdaError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__("%s: %s" % (_STATUS.get(status, status), detail))
+        self.status = status
+
+
+class FwdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("gate_range", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            raise ImportError(
+                "libckda.so is not built (%s); run `python -m gated_delta_rule_ckda_amd.build` "
+                "or __graft_entry__.build()" % _LIB)
+        lib = ctypes.CDLL(_LIB)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        lib.ckda_chunk_fwd.restype = i32
+        lib.ckda_chunk_fwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, vp]
+        lib.ckda_fwd_supported.restype = i32
+        lib.ckda_fwd_supported.argtypes = [ctypes.POINTER(FwdDesc)]
+        lib.ckda_recurrent_step.restype = i32
+        lib.ckda_recurrent_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                            vp, vp, vp, vp, vp, vp]
+        lib.ckda_l2norm_debug.restype = i32
+        lib.ckda_l2norm_debug.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp]
+        lib.ckda_status_string.restype = ctypes.c_char_p
+        lib.ckda_status_string.argtypes = [i32]
+        lib.ckda_last_error.restype = ctypes.c_char_p
+        lib.ckda_last_error.argtypes = []
+        lib.ckda_abi_version.restype = i32
+        lib.ckda_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def abi_version() -> int:
+    return int(_load().ckda_abi_version())
+
+
+def _check(status):
+    if status != 0:
+        raise CkdaError(status, _load().ckda_last_error().decode())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _gate_code(gate):
+    if gate in ("ckda", GATE_CKDA):
+        return GATE_CKDA
+    if gate in ("kda", GATE_KDA):
+        return GATE_KDA
+    raise ValueError("gate must be 'ckda' or 'kda'")
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens):
+    if cu_seqlens is not None:
+        B, T = 1, q.shape[-3] if q.dim() == 3 else q.shape[1]
+        N = cu_seqlens.numel() - 1
+    else:
+        B, T = q.shape[0], q.shape[1]
+        N = B
+    return FwdDesc(B, T, H, dk, dv, N, chunk_size, _dtype_code(q), _gate_code(gate),
+                   int(bool(use_qk_l2norm)), float(scale))
+
+
+def fwd_supported(chunk_size, dk, dv, dtype) -> bool:
+    d = FwdDesc(1, 1, 1, dk, dv, 1, chunk_size, dtype, GATE_CKDA, 1, 1.0)
+    return bool(_load().ckda_fwd_supported(ctypes.byref(d)))
+
+
+def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
+              use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
+              out=None, final_state=None, stream=None):
+    """Chunked prefill.  Dense: q,k,alpha [B,T,H,dk], v [B,T,H,dv], beta [B,T,H].
+    Packed (cu_seqlens int32 [N+1]): leading [1,T,...] or [T,...].
+    Returns (o, ht) with ht [N,H,dk,dv] float32 (None if not requested)."""
+    import torch
+    lib = _load()
+    H, dk, dv = q.shape[-2], q.shape[-1], v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+        _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _require(alpha.dtype == torch.float32 and beta.dtype == torch.float32,
+             "alpha and beta must be float32")
+    if cu_seqlens is not None:
+        _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda,
+                 "cu_seqlens must be an int32 device tensor")
+    desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens)
+    _require(q.numel() == desc.B * desc.T * H * dk, "q has the wrong number of elements")
+    _require(k.numel() == q.numel() and alpha.numel() == q.numel(), "k/alpha must match q")
+    _require(v.numel() == desc.B * desc.T * H * dv, "v has the wrong number of elements")
+    _require(beta.numel() == desc.B * desc.T * H, "beta has the wrong number of elements")
+    if h0 is not None:
+        _require(h0.dtype == torch.float32 and h0.is_contiguous()
+                 and h0.numel() == desc.num_seqs * H * dk * dv, "h0 must be [N,H,dk,dv] float32")
+    o = torch.empty_like(v) if out is None else out
+    ht = None
+    if output_final_state:
+        ht = (torch.empty((desc.num_seqs, H, dk, dv), device=q.device, dtype=torch.float32)
+              if final_state is None else final_state)
+    _check(lib.ckda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                              _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
+                              _stream(stream)))
+    return o, ht
+
+
+def recurrent_step(q, k, v, alpha, beta, state, *, use_qk_l2norm=True, gate="ckda",
+                   scale=1.0, out=None, new_state=None, stream=None):
+    """One decode token per sequence: q,k,alpha [N,H,dk], v [N,H,dv], beta [N,H],
+    state [N,H,dk,dv] float32, updated in place unless new_state is given.
+    Returns o [N,H,dv]."""
+    import torch
+    lib = _load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("state", state)):
+        _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _require(alpha.dtype == torch.float32 and beta.dtype == torch.float32
+             and state.dtype == torch.float32, "alpha, beta, state must be float32")
+    _require(k.shape == q.shape and alpha.shape == q.shape and v.shape == (N, H, dv)
+             and beta.shape == (N, H) and state.shape == (N, H, dk, dv), "shape mismatch")
+    o = torch.empty_like(v) if out is None else out
+    dst = state if new_state is None else new_state
+    _check(lib.ckda_recurrent_step(N, H, dk, dv, _dtype_code(q), _gate_code(gate),
+                                   int(bool(use_qk_l2norm)), float(scale), _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(dst),
+                                   _ptr(o), _stream(stream)))
+    return o
+
+
+def l2norm_debug(x, stream=None):
+    """Test export of the in-kernel normalisation over the last axis."""
+    import torch
+    lib = _load()
+    _require(x.is_cuda and x.is_contiguous(), "x must be a contiguous device tensor")
+    d = x.shape[-1]
+    y = torch.empty(x.shape, device=x.device, dtype=torch.float32)
+    _check(lib.ckda_l2norm_debug(_ptr(x), _ptr(y), x.numel() // d, d, _dtype_code(x),
+                                 _stream(stream)))
+    return y

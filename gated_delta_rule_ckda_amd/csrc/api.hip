@@ -1,0 +1,202 @@
+// Host side of the C ABI declared in include/ckda.h: argument validation,
+// shape dispatch and error reporting.  Validation never touches the GPU, so a
+// non-OK status means nothing was enqueued; only a launch can return
+// CKDA_ERR_HIP.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "ckda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ckda_status_t fail(ckda_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ckda_status_t fail(ckda_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ckda_status_t ok() {
+  g_last_error.clear();
+  return CKDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char* name, const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+int64_t elem_bytes(int32_t dtype) { return dtype == CKDA_DTYPE_BF16 ? 2 : 4; }
+
+ckda_status_t from_hip(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(CKDA_ERR_HIP, "HIP launch error %d: %s", static_cast<int>(e), hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ckda_abi_version(void) { return CKDA_ABI_VERSION; }
+
+const char* ckda_last_error(void) { return g_last_error.c_str(); }
+
+const char* ckda_status_string(int32_t s) {
+  switch (s) {
+    case CKDA_OK: return "ok";
+    case CKDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CKDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case CKDA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t ckda_fwd_supported(const ckda_fwd_desc_t* d) {
+  if (!d) return 0;
+  return ckda::fwd_supported(d->chunk_size, d->dk, d->dv, d->io_dtype) ? 1 : 0;
+}
+
+ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta,
+                             const int32_t* cu_seqlens, const float* h0, void* o,
+                             float* ht, void* stream) {
+  if (!d) return fail(CKDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->dk <= 0 || d->dv <= 0 || d->num_seqs < 0)
+    return fail(CKDA_ERR_INVALID_ARGUMENT,
+                "non-positive size: B=%d T=%d H=%d dk=%d dv=%d num_seqs=%d", d->B, d->T, d->H,
+                d->dk, d->dv, d->num_seqs);
+  if (d->io_dtype != CKDA_DTYPE_BF16 && d->io_dtype != CKDA_DTYPE_F32)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not a ckda_dtype_t", d->io_dtype);
+  if (d->gate_range != CKDA_GATE_KDA && d->gate_range != CKDA_GATE_CKDA)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_range %d is not a ckda_gate_t", d->gate_range);
+  if (d->use_qk_l2norm != 0 && d->use_qk_l2norm != 1)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
+  if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "chunk_size %d is not 16, 32 or 64", d->chunk_size);
+  if (cu_seqlens) {
+    if (d->B != 1)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "cu_seqlens given with B=%d (must be 1)", d->B);
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+  } else if (d->num_seqs != d->B) {
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "num_seqs=%d must equal B=%d without cu_seqlens",
+                d->num_seqs, d->B);
+  }
+  const int64_t tokens = static_cast<int64_t>(d->B) * d->T;
+  if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !o))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "q, k, v, alpha, beta and o must not be NULL");
+  const void* ptrs[] = {q, k, v, alpha, beta, h0, o, ht};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "o", "ht"};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+
+  const int64_t eb = elem_bytes(d->io_dtype);
+  const int64_t state_bytes = static_cast<int64_t>(d->num_seqs) * d->H * d->dk * d->dv * 4;
+  const Range ro = range("o", o, tokens * d->H * d->dv * eb);
+  const Range ins[] = {range("q", q, tokens * d->H * d->dk * eb),
+                       range("k", k, tokens * d->H * d->dk * eb),
+                       range("v", v, tokens * d->H * d->dv * eb),
+                       range("alpha", alpha, tokens * d->H * d->dk * 4),
+                       range("beta", beta, tokens * d->H * 4),
+                       range("h0", h0, h0 ? state_bytes : 0),
+                       range("ht", ht, ht ? state_bytes : 0),
+                       range("cu_seqlens", cu_seqlens,
+                             cu_seqlens ? 4 * (static_cast<int64_t>(d->num_seqs) + 1) : 0)};
+  for (const Range& r : ins)
+    if (overlap(ro, r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "o overlaps %s", r.name);
+  if (ht) {
+    const Range rh = range("ht", ht, state_bytes);
+    for (int i = 0; i < 5; ++i)
+      if (overlap(rh, ins[i])) return fail(CKDA_ERR_INVALID_ARGUMENT, "ht overlaps %s", ins[i].name);
+    if (h0 && h0 != ht && overlap(rh, ins[5]))
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "ht partially overlaps h0");
+  }
+  if (!ckda::fwd_supported(d->chunk_size, d->dk, d->dv, d->io_dtype))
+    return fail(CKDA_ERR_UNSUPPORTED, "no chunked kernel for chunk_size=%d dk=%d dv=%d io_dtype=%d",
+                d->chunk_size, d->dk, d->dv, d->io_dtype);
+  if (d->num_seqs == 0) return ok();
+
+  ckda::FwdArgs a{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
+                  d->use_qk_l2norm, d->gate_range, d->scale, q, k, v, alpha, beta,
+                  cu_seqlens, h0, o, ht};
+  return from_hip(ckda::launch_fwd(a, d->io_dtype, static_cast<hipStream_t>(stream)));
+}
+
+ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                  int32_t io_dtype, int32_t gate_range, int32_t use_qk_l2norm,
+                                  float scale, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, const float* h0,
+                                  float* ht, void* o, void* stream) {
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "bad size: N=%d H=%d dk=%d dv=%d", N, H, dk, dv);
+  if (io_dtype != CKDA_DTYPE_BF16 && io_dtype != CKDA_DTYPE_F32)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not a ckda_dtype_t", io_dtype);
+  if (gate_range != CKDA_GATE_KDA && gate_range != CKDA_GATE_CKDA)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_range %d is not a ckda_gate_t", gate_range);
+  if (use_qk_l2norm != 0 && use_qk_l2norm != 1)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
+  if (N > 0 && (!q || !k || !v || !alpha || !beta || !h0 || !ht || !o))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "no pointer argument may be NULL");
+  const void* ptrs[] = {q, k, v, alpha, beta, h0, ht, o};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "ht", "o"};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  const int64_t nh = static_cast<int64_t>(N) * H;
+  const int64_t eb = elem_bytes(io_dtype);
+  const int64_t sb = nh * dk * dv * 4;
+  const Range ro = range("o", o, nh * dv * eb);
+  const Range rht = range("ht", ht, sb);
+  const Range ins[] = {range("q", q, nh * dk * eb), range("k", k, nh * dk * eb),
+                       range("v", v, nh * dv * eb), range("alpha", alpha, nh * dk * 4),
+                       range("beta", beta, nh * 4), range("h0", h0, sb)};
+  for (const Range& r : ins)
+    if (overlap(ro, r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "o overlaps %s", r.name);
+  if (overlap(ro, rht)) return fail(CKDA_ERR_INVALID_ARGUMENT, "o overlaps ht");
+  for (int i = 0; i < 5; ++i)
+    if (overlap(rht, ins[i])) return fail(CKDA_ERR_INVALID_ARGUMENT, "ht overlaps %s", ins[i].name);
+  if (h0 != ht && overlap(rht, ins[5]))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "ht partially overlaps h0");
+  if (!ckda::step_supported(dk, dv))
+    return fail(CKDA_ERR_UNSUPPORTED, "no decode kernel for dk=%d dv=%d", dk, dv);
+  if (nh == 0) return ok();
+  ckda::StepArgs a{N, H, dk, dv, use_qk_l2norm, scale, q, k, v, alpha, beta, h0, ht, o};
+  return from_hip(ckda::launch_step(a, io_dtype, static_cast<hipStream_t>(stream)));
+}
+
+ckda_status_t ckda_l2norm_debug(const void* x, float* y, int64_t rows, int32_t d,
+                                int32_t dtype, void* stream) {
+  if (rows < 0 || d <= 0 || d > 1024)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "bad size: rows=%lld d=%d",
+                static_cast<long long>(rows), d);
+  if (dtype != CKDA_DTYPE_BF16 && dtype != CKDA_DTYPE_F32)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "dtype %d is not a ckda_dtype_t", dtype);
+  if (rows > 0 && (!x || !y)) return fail(CKDA_ERR_INVALID_ARGUMENT, "x and y must not be NULL");
+  if ((x && !aligned16(x)) || (y && !aligned16(y)))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned");
+  if (overlap(range("x", x, rows * d * elem_bytes(dtype)), range("y", y, rows * d * 4)))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "y overlaps x");
+  if (rows == 0) return ok();
+  return from_hip(ckda::launch_l2norm_debug(x, y, rows, d, dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

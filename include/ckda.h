@@ -1,0 +1,148 @@
+/*
+ * ckda.h -- C ABI of libckda.so: the (Complex) Kimi Delta Attention
+ * recurrence on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every sequence n and head h the library runs
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * over the sequence's tokens in order, starting from S_0 = h0[n,h] (or 0).
+ * The transition A_t = (I - beta k k^T) Diag(alpha) is the gated delta-rule
+ * transition of the picx.dev summary of the Complex KDA paper (section
+ * "Background", transition-matrix equation); the rank-one write beta k v^T and
+ * the read-out after the update complete it.  S is dk x dv; Diag(alpha)
+ * scales its rows, so alpha holds one gate per key channel.  With
+ * use_qk_l2norm set, q and k are first normalised per (token, head) over the
+ * dk channels, x / sqrt(sum x^2 + 1e-6), inside the kernels (dormouse review
+ * "RoPE into the KDA q/k path", section 2: the norm is an in-op step that the
+ * layer switches on).
+ *
+ * Gate ranges (same summary, section "CKDA Definition"): CKDA takes
+ * alpha in [-1,1] per channel and beta in [0,2]; KDA keeps alpha in (0,1].
+ * Both are computed exactly as written, including alpha = 0 and negative
+ * alpha; values outside the range are computed as written too, but then the
+ * transition may expand and the results are not covered by the tests.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps device memory, and keeps no global
+ *    mutable state apart from a thread-local error message.
+ *  - Layouts are row-major and contiguous (last index fastest).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *    default stream).  The library never synchronises the host and never
+ *    reads device memory on the host.
+ *  - All argument validation happens on the host before any HIP call; a
+ *    non-OK status means nothing was enqueued.  A failed launch returns
+ *    CKDA_ERR_HIP.  Nothing crosses the ABI as an exception.
+ *  - Data-dependent preconditions are documented, not checked: gate ranges,
+ *    and cu_seqlens being non-decreasing with cu_seqlens[0] = 0.
+ *  - Base pointers must be 16-byte aligned.
+ */
+#ifndef CKDA_H_
+#define CKDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CKDA_ABI_VERSION 1
+
+typedef enum {
+  CKDA_OK = 0,
+  CKDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, aliasing */
+  CKDA_ERR_UNSUPPORTED = 2,      /* valid arguments this build has no kernel for */
+  CKDA_ERR_HIP = 3               /* the HIP runtime reported an error at launch */
+} ckda_status_t;
+
+typedef enum {
+  CKDA_DTYPE_BF16 = 0, /* q, k, v, o in bfloat16 (o rounded to nearest even) */
+  CKDA_DTYPE_F32 = 1   /* q, k, v, o in float32 */
+} ckda_dtype_t;
+
+typedef enum {
+  CKDA_GATE_KDA = 0,  /* alpha in (0,1], beta in [0,1] */
+  CKDA_GATE_CKDA = 1  /* alpha in [-1,1], beta in [0,2] */
+} ckda_gate_t;
+
+/*
+ * Descriptor of one chunked forward call.
+ *   Dense batch (cu_seqlens == NULL): num_seqs == B sequences of T tokens;
+ *     q, k, alpha : [B][T][H][dk]   v, o : [B][T][H][dv]   beta : [B][T][H]
+ *   Packed variable-length batch (cu_seqlens != NULL): B must be 1, T is the
+ *     total token count, sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
+ *     (empty sequences allowed; then ht[n] = h0[n]).
+ *   h0, ht : [num_seqs][H][dk][dv] float32.
+ * chunk_size is the number of tokens handled as one block of the chunked
+ * algorithm; the result does not depend on it beyond rounding.
+ */
+typedef struct {
+  int32_t B, T, H, dk, dv;
+  int32_t num_seqs;
+  int32_t chunk_size;    /* 16, 32 or 64 */
+  int32_t io_dtype;      /* ckda_dtype_t */
+  int32_t gate_range;    /* ckda_gate_t */
+  int32_t use_qk_l2norm; /* 0 or 1 */
+  float scale;           /* o = scale * S^T q_hat */
+} ckda_fwd_desc_t;
+
+/*
+ * Chunked prefill.  Computes o for every token and, if ht != NULL, the final
+ * state of every sequence.  h0 == NULL means a zero initial state.  h0 and ht
+ * may be the same buffer (the state is read before it is written).  o must not
+ * overlap any input.  Supported shapes (others return CKDA_ERR_UNSUPPORTED):
+ *   bf16 : dk = dv = 128 with chunk_size 16, 32 or 64; dk = dv = 64 with 16, 32, 64
+ *   f32  : dk = dv in {16, 32, 64} with chunk_size 16 or 32 (<= 64 for dk <= 32)
+ * ckda_fwd_supported() reports whether a descriptor has a kernel.
+ */
+ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
+                             const void* k, const void* v, const float* alpha,
+                             const float* beta, const int32_t* cu_seqlens,
+                             const float* h0, void* o, float* ht, void* stream);
+
+/* 1 if ckda_chunk_fwd has a kernel for this descriptor's (chunk_size, dk, dv,
+ * io_dtype), 0 if not (other fields are not inspected). */
+int32_t ckda_fwd_supported(const ckda_fwd_desc_t* desc);
+
+/*
+ * Fused single-token decode step for N sequences (the recurrent form of the
+ * same recurrence, one token per sequence):
+ *   q, k, alpha : [N][H][dk]   v, o : [N][H][dv]   beta : [N][H]
+ *   h0, ht      : [N][H][dk][dv] float32; h0 == ht (in place) is allowed,
+ *                 other partial overlaps are not.
+ * Supported: dk, dv in {16, 32, 64, 128}, both io dtypes.
+ */
+ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                  int32_t io_dtype, int32_t gate_range,
+                                  int32_t use_qk_l2norm, float scale,
+                                  const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta,
+                                  const float* h0, float* ht, void* o,
+                                  void* stream);
+
+/*
+ * Test export of the in-kernel normalisation: y[r][:] = x[r][:] /
+ * sqrt(sum_c x[r][c]^2 + 1e-6) in float32 with IEEE sqrt and division, for
+ * `rows` rows of d values (x in io dtype `dtype`, y float32).  d <= 1024.
+ */
+ckda_status_t ckda_l2norm_debug(const void* x, float* y, int64_t rows,
+                                int32_t d, int32_t dtype, void* stream);
+
+/* Static description of a status code. */
+const char* ckda_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none): which argument failed validation, or the HIP error string. */
+const char* ckda_last_error(void);
+
+/* CKDA_ABI_VERSION of the library. */
+int32_t ckda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKDA_H_ */

@@ -1,0 +1,140 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/ckda.h declares, and rejects bad arguments on the host before any HIP
+call (dummy, never-dereferenced pointers are used; no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_ckda_amd as ck
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ckda.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckda_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ck.library_path())
+    names = _declared()
+    assert "ckda_chunk_fwd" in names and "ckda_recurrent_step" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define CKDA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert ck.abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    lib = ck._load()
+    for s in range(4):
+        assert lib.ckda_status_string(s)
+    assert lib.ckda_status_string(99) == b"unknown status"
+
+
+# Fake, 16-byte aligned, never-dereferenced device addresses.
+BASE = 0x7F0000000000
+P = {n: ctypes.c_void_p(BASE + i * (1 << 32)) for i, n in
+     enumerate(["q", "k", "v", "alpha", "beta", "cu", "h0", "o", "ht"])}
+
+
+def _desc(**kw):
+    d = dict(B=2, T=64, H=2, dk=128, dv=128, num_seqs=2, chunk_size=64, io_dtype=ck.BF16,
+             gate_range=ck.GATE_CKDA, use_qk_l2norm=1, scale=1.0)
+    d.update(kw)
+    return ck.FwdDesc(**d)
+
+
+def _fwd(desc, **over):
+    p = dict(P)
+    p.update(over)
+    lib = ck._load()
+    st = lib.ckda_chunk_fwd(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"],
+                            p["v"], p["alpha"], p["beta"], p.get("cu_seqlens"), p["h0"], p["o"],
+                            p["ht"], None)
+    return st, lib.ckda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(B=0), "non-positive"), (dict(H=-1), "non-positive"), (dict(dk=0), "non-positive"),
+    (dict(io_dtype=7), "io_dtype"), (dict(gate_range=3), "gate_range"),
+    (dict(use_qk_l2norm=2), "use_qk_l2norm"), (dict(chunk_size=48), "chunk_size"),
+    (dict(num_seqs=3), "num_seqs"),
+])
+def test_fwd_rejects_bad_descriptor(over, needle):
+    st, msg = _fwd(_desc(**over))
+    assert st == 1 and needle in msg
+
+
+def test_fwd_null_and_alignment_and_aliasing():
+    assert _fwd(None)[0] == 1
+    st, msg = _fwd(_desc(), q=None)
+    assert st == 1 and "NULL" in msg
+    st, msg = _fwd(_desc(), k=ctypes.c_void_p(BASE + 8))
+    assert st == 1 and "aligned" in msg
+    st, msg = _fwd(_desc(), o=P["v"])
+    assert st == 1 and "overlaps" in msg, msg
+    st, msg = _fwd(_desc(), ht=ctypes.c_void_p(P["h0"].value + 64))
+    assert st == 1 and "overlap" in msg
+
+
+def test_fwd_cu_seqlens_needs_batch_one():
+    st, msg = _fwd(_desc(B=2, num_seqs=3), cu_seqlens=ctypes.c_void_p(BASE + 5 * (1 << 32)))
+    assert st == 1 and "cu_seqlens" in msg
+    st, msg = _fwd(_desc(B=1, num_seqs=3), cu_seqlens=ctypes.c_void_p(BASE + 5 * (1 << 32) + 2))
+    assert st == 1 and "aligned" in msg
+
+
+def test_fwd_unsupported_shape():
+    st, msg = _fwd(_desc(dk=96, dv=96))
+    assert st == 2 and "no chunked kernel" in msg
+
+
+def test_fwd_empty_is_ok_without_launch():
+    # num_seqs == 0 with a packed batch: nothing to do, nothing enqueued
+    if not ck.fwd_supported(64, 128, 128, ck.BF16):
+        pytest.skip("no bf16 d=128 kernel in this build")
+    st, _ = _fwd(_desc(B=1, T=0, num_seqs=0), cu_seqlens=ctypes.c_void_p(BASE + 5 * (1 << 32)))
+    assert st == 0
+
+
+def _step(N=4, H=2, dk=128, dv=128, dtype=ck.BF16, gate=ck.GATE_CKDA, l2=1, **over):
+    p = dict(P)
+    p.update(over)
+    lib = ck._load()
+    st = lib.ckda_recurrent_step(N, H, dk, dv, dtype, gate, l2, 1.0, p["q"], p["k"], p["v"],
+                                 p["alpha"], p["beta"], p["h0"], p["ht"], p["o"], None)
+    return st, lib.ckda_last_error().decode()
+
+
+def test_step_validation():
+    assert _step(N=-1)[0] == 1
+    assert _step(H=0)[0] == 1
+    assert _step(dtype=5)[0] == 1
+    assert _step(gate=2)[0] == 1
+    assert _step(l2=3)[0] == 1
+    assert _step(q=None)[0] == 1
+    assert _step(v=ctypes.c_void_p(BASE + 4))[0] == 1
+    st, msg = _step(dk=48)
+    assert st == 2
+    st, msg = _step(o=P["q"])
+    assert st == 1 and "overlaps" in msg
+    st, msg = _step(ht=ctypes.c_void_p(P["h0"].value + 256))
+    assert st == 1 and "partially" in msg
+    # N == 0 with valid arguments: ok, nothing enqueued
+    assert _step(N=0)[0] == 0
+
+
+def test_l2norm_debug_validation():
+    lib = ck._load()
+    assert lib.ckda_l2norm_debug(P["q"], P["o"], 10, 0, ck.F32, None) == 1
+    assert lib.ckda_l2norm_debug(P["q"], P["o"], 10, 2048, ck.F32, None) == 1
+    assert lib.ckda_l2norm_debug(P["q"], P["q"], 10, 16, ck.F32, None) == 1
+    assert lib.ckda_l2norm_debug(P["q"], P["o"], 0, 16, ck.F32, None) == 0

@@ -1,0 +1,148 @@
+"""GPU parity of the fused decode step (one token per sequence) and of the
+in-kernel normalisation layout, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_ckda_amd as ck
+import oracle
+from gated_delta_rule_ckda_amd import inputs
+from tests.gpu_util import DEV, TOL, announce, dev, host, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def pow2_rows(rows, d, seed=0):
+    """Rows with 4^m nonzero entries of +-2^e (64 at d=128, 16 at d<=64), zeros
+    elsewhere, and sum x^2 >= 64 so that eps = 1e-6 is absorbed and the
+    normalised row is exactly +-2^-m.  Positions and signs differ per row, so
+    any mix-up of rows, heads or tokens changes bits.  Returns (x, expected)."""
+    rng = np.random.default_rng(seed)
+    nnz, m = (64, 3) if d >= 128 else (16, 2)
+    e = np.arange(rows) % 3 + (0 if nnz == 64 else 1)
+    keys = rng.random((rows, d))
+    pos = np.argsort(keys, axis=1)[:, :nnz]
+    sgn = np.where(rng.random((rows, nnz)) < 0.5, -1.0, 1.0)
+    x = np.zeros((rows, d), dtype=np.float32)
+    np.put_along_axis(x, pos, (sgn * (2.0 ** e)[:, None]).astype(np.float32), axis=1)
+    y = np.zeros_like(x)
+    np.put_along_axis(y, pos, (sgn * 2.0 ** -m).astype(np.float32), axis=1)
+    return x, y
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_l2norm_debug_bit_exact(dtype, d):
+    announce("l2norm_debug %s d=%d" % (dtype, d))
+    x, y = pow2_rows(2 * 37 * 3, d, seed=d)
+    out = ck.l2norm_debug(dev(x.reshape(2, 37, 3, d), dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().reshape(-1, d), y)
+    # random rows: unit norm, and equal to the oracle's normalisation
+    r = inputs.round_bf16(np.random.default_rng(3).standard_normal((500, d)).astype(np.float32))
+    out = host(ck.l2norm_debug(dev(r, dtype)))
+    assert max_rel_err(out, oracle.l2norm(r)) < 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 128])
+def test_step_l2norm_layout_bit_exact(dtype, d):
+    """Through the fused step: with h0 = I, alpha = 1, beta = 0 the read-out
+    is exactly q_hat; with h0 = 0, alpha = 1, beta = 1, v = 1 the new state's
+    column j is exactly k_hat."""
+    announce("step l2norm layout %s d=%d" % (dtype, d))
+    N, H = 5, 3
+    xq, yq = pow2_rows(N * H, d, seed=1)
+    xk, yk = pow2_rows(N * H, d, seed=2)
+    q, k = dev(xq.reshape(N, H, d), dtype), dev(xk.reshape(N, H, d), dtype)
+    ones = torch.ones((N, H, d), device=DEV, dtype=torch.float32)
+    eye = torch.eye(d, device=DEV).expand(N, H, d, d).contiguous()
+    o = ck.recurrent_step(q, k, dev(np.zeros((N, H, d)), dtype), ones,
+                          torch.zeros((N, H), device=DEV), eye)
+    assert np.array_equal(o.float().cpu().numpy().reshape(-1, d), yq)
+    st = torch.zeros((N, H, d, d), device=DEV)
+    ck.recurrent_step(q, k, dev(np.ones((N, H, d)), dtype), ones, torch.ones((N, H), device=DEV), st)
+    stn = st.cpu().numpy().reshape(N * H, d, d)
+    for j in (0, d - 1):
+        assert np.array_equal(stn[:, :, j], yk)
+
+
+def _rand_step(rng, N, H, dk, dv, dtype, zero_rows=False):
+    q = inputs.round_bf16(rng.standard_normal((N, H, dk)).astype(np.float32)) if dtype == "bf16" \
+        else rng.standard_normal((N, H, dk)).astype(np.float32)
+    k = inputs.round_bf16(rng.standard_normal((N, H, dk)).astype(np.float32)) if dtype == "bf16" \
+        else rng.standard_normal((N, H, dk)).astype(np.float32)
+    v = inputs.round_bf16(rng.standard_normal((N, H, dv)).astype(np.float32)) if dtype == "bf16" \
+        else rng.standard_normal((N, H, dv)).astype(np.float32)
+    a = rng.uniform(-1, 1, (N, H, dk)).astype(np.float32)
+    a[0, 0, :3] = 0.0
+    b = rng.uniform(0, 2, (N, H)).astype(np.float32)
+    if zero_rows:
+        q[0, 0] = 0.0
+        k[-1, -1] = 0.0
+    return q, k, v, a, b
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 64), (128, 128), (128, 64), (16, 128),
+                                   (64, 32)])
+@pytest.mark.parametrize("l2", [True, False])
+def test_step_parity(dtype, dk, dv, l2):
+    announce("step parity %s dk=%d dv=%d l2=%s" % (dtype, dk, dv, l2))
+    rng = np.random.default_rng(dk * 7 + dv + l2)
+    N, H, steps = 7, 3, 6
+    S = (0.5 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    st = dev(S)
+    ref = S.astype(np.float64)
+    for s in range(steps):
+        q, k, v, a, b = _rand_step(rng, N, H, dk, dv, dtype, zero_rows=(s == 2))
+        o = ck.recurrent_step(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(a), dev(b), st,
+                              use_qk_l2norm=l2, scale=0.75)
+        ro, ref = oracle.step(q, k, v, a, b, ref, use_l2norm=l2, scale=0.75)
+        assert max_rel_err(host(o), ro) < TOL[dtype], s
+        assert max_rel_err(host(st), ref) < TOL["f32"], s
+
+
+def test_step_in_place_equals_out_of_place_and_is_deterministic():
+    announce("step in-place vs out-of-place")
+    rng = np.random.default_rng(5)
+    N, H, d = 9, 4, 128
+    q, k, v, a, b = _rand_step(rng, N, H, d, d, "bf16")
+    S = dev(rng.standard_normal((N, H, d, d)).astype(np.float32))
+    args = (dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(a), dev(b))
+    s1 = S.clone()
+    o1 = ck.recurrent_step(*args, s1)
+    s2 = torch.empty_like(S)
+    o2 = ck.recurrent_step(*args, S.clone(), new_state=s2)
+    s3 = S.clone()
+    o3 = ck.recurrent_step(*args, s3)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(o1, o2)
+    assert torch.equal(s1, s3) and torch.equal(o1, o3)
+
+
+def test_decode_workload_64_steps_sampled():
+    """The decode workload at full size (256 sequences x 32 heads, d=128, bf16,
+    fp32 state ~N(0,0.02^2)), 64 in-place steps, in the launch configuration
+    the benchmark times; the oracle follows 48 sampled (sequence, head) pairs
+    through all 64 steps (pairs are independent, so this is exact parity on
+    those pairs)."""
+    announce("decode workload 64 steps")
+    N, H, d, steps = 256, 32, 128, 64
+    S0 = inputs.decode_state(N=N, H=H, d=d)
+    st = dev(S0)
+    rng = np.random.default_rng(77)
+    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, N, 48), rng.integers(0, H, 48))]
+    pairs[0], pairs[1] = (0, 0), (N - 1, H - 1)
+    ns = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    ref = S0[ns, hs][:, None].astype(np.float64)     # [P,1,d,d]
+    worst = 0.0
+    for s in range(steps):
+        q, k, v, a, b = inputs.decode_token(s, N=N, H=H, d=d)
+        o = ck.recurrent_step(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(a), dev(b), st)
+        ro, ref = oracle.step(q[ns, hs][:, None], k[ns, hs][:, None], v[ns, hs][:, None],
+                              a[ns, hs][:, None], b[ns, hs][:, None], ref)
+        worst = max(worst, max_rel_err(host(o)[ns, hs], ro[:, 0]))
+    assert worst < TOL["bf16"]
+    assert max_rel_err(host(st)[ns, hs], ref[:, 0]) < TOL["f32"]
