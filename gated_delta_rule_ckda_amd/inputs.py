@@ -69,10 +69,17 @@ def random_case(seed, B, T, H, dk, dv, *, dtype="f32", chunk=16, l2norm=True,
     """Generic dense case: q,k,v ~ N(0,1); alpha ~ U[-1,1] ('uniform'),
     tanh(N(2,1)) ('tanh'), sigmoid(N(2,1)) ('sigmoid'); beta ~ U[0,2]
     ('uniform'), 2 sigmoid(N(0,1)) ('2sig'), sigmoid(N(0,1)) ('sig').
-    zero_frac sets that fraction of alpha entries to exactly 0."""
+    zero_frac sets that fraction of alpha entries to exactly 0.  Without the
+    in-kernel normalisation the keys are drawn as unit-norm directions (the
+    method's range assumes unit keys; raw N(0,1) keys would make the
+    recurrence expand)."""
     rng = np.random.default_rng(seed)
     q = _io(rng.standard_normal((B, T, H, dk), dtype=np.float32), dtype)
-    k = _io(rng.standard_normal((B, T, H, dk), dtype=np.float32), dtype)
+    k = rng.standard_normal((B, T, H, dk), dtype=np.float32)
+    if not l2norm:
+        k64 = k.astype(np.float64)
+        k = (k64 / np.sqrt((k64 * k64).sum(-1, keepdims=True))).astype(np.float32)
+    k = _io(k, dtype)
     v = _io(rng.standard_normal((B, T, H, dv), dtype=np.float32), dtype)
     if alpha == "uniform":
         a = rng.uniform(-1, 1, (B, T, H, dk)).astype(np.float32)

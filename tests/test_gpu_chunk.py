@@ -1,0 +1,233 @@
+"""GPU parity of the chunked forward (ckda_chunk_fwd through the C ABI)
+against the fp64 oracle, the bit-exact normalisation layout through the
+chunked path, and the structural invariants of the recurrence."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_ckda_amd as ck
+import oracle
+from gated_delta_rule_ckda_amd import inputs
+from tests.gpu_util import (DEV, TOL, announce, dev, host, max_rel_err, oracle_pairs,
+                            run_chunk)
+from tests.test_gpu_decode import pow2_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, chunk=None, scale=1.0, tol=None):
+    o, ht = run_chunk(case, chunk=chunk, scale=scale)
+    ro, rh = oracle.fwd(case.q, case.k, case.v, case.alpha, case.beta, h0=case.h0,
+                        seq_start=case.cu_seqlens, use_l2norm=case.l2norm, scale=scale)
+    tol = tol or TOL[case.dtype]
+    eo, eh = max_rel_err(o, ro), max_rel_err(ht, rh)
+    print("  err o=%.3e ht=%.3e (tol %.0e)" % (eo, eh, tol))
+    assert eo < tol and eh < tol
+    return o, ht
+
+
+F32_SHAPES = [(16, 16), (32, 16), (64, 16), (16, 32), (32, 32), (64, 32), (16, 64), (32, 64)]
+
+
+@pytest.mark.parametrize("chunk,d", F32_SHAPES)
+@pytest.mark.parametrize("l2", [True, False])
+def test_f32_parity(chunk, d, l2):
+    announce("f32 parity C=%d d=%d l2=%s" % (chunk, d, l2))
+    c = inputs.random_case(300 + chunk + d, 2, 3 * chunk + 5, 3, d, d, dtype="f32", chunk=chunk,
+                           l2norm=l2, h0_std=0.5, zero_frac=0.02)
+    _check(c, scale=0.8)
+
+
+@pytest.mark.parametrize("chunk,d", [(64, 128), (32, 128), (16, 128), (64, 64), (32, 64), (16, 64)])
+def test_bf16_parity(chunk, d):
+    announce("bf16 parity C=%d d=%d" % (chunk, d))
+    c = inputs.random_case(400 + chunk + d, 2, 4 * chunk + 7, 2, d, d, dtype="bf16", chunk=chunk,
+                           alpha="tanh", beta="2sig", h0_std=0.1, zero_frac=0.01)
+    _check(c)
+
+
+def test_tiny_workload():
+    announce("tiny workload B=1 H=2 T=64 d=16 fp32 chunk 16")
+    _check(inputs.tiny())
+
+
+def test_state_tracking_workload_full():
+    """B=256 H=4 T=512 d=32 fp32 chunk 32, near-orthogonal transitions; also
+    the per-(b,h) relative drift of ||ht||_F against the oracle."""
+    announce("state-tracking workload full size")
+    c = inputs.state_tracking()
+    o, ht = run_chunk(c)
+    ro, rh = oracle.fwd(c.q, c.k, c.v, c.alpha, c.beta, use_l2norm=False)
+    eo, eh = max_rel_err(o, ro), max_rel_err(ht, rh)
+    drift = np.abs(np.linalg.norm(ht, axis=(2, 3)) / np.linalg.norm(rh, axis=(2, 3)) - 1).max()
+    print("  err o=%.3e ht=%.3e max ||S|| drift %.3e" % (eo, eh, drift))
+    assert eo < TOL["f32"] and eh < TOL["f32"] and drift < TOL["f32"]
+
+
+def test_orthogonal_norm_preserved():
+    """Exactly orthogonal transitions (alpha in {+-1}, beta = 2, unit keys,
+    v = 0): ||S_T||_F = ||h0||_F (Theorem 1 of the summary)."""
+    announce("orthogonal norm preservation")
+    rng = np.random.default_rng(8)
+    B, T, H, d = 4, 300, 2, 32
+    k = rng.standard_normal((B, T, H, d))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    c = inputs.Case(rng.standard_normal((B, T, H, d)).astype(np.float32), k,
+                    np.zeros((B, T, H, d), np.float32),
+                    rng.choice([-1.0, 1.0], (B, T, H, d)).astype(np.float32),
+                    np.full((B, T, H), 2.0, np.float32),
+                    rng.standard_normal((B, H, d, d)).astype(np.float32), None, "f32", 32, False)
+    _, ht = run_chunk(c)
+    n0 = np.linalg.norm(c.h0.astype(np.float64), axis=(2, 3))
+    assert np.abs(np.linalg.norm(ht, axis=(2, 3)) / n0 - 1).max() < 1e-4
+
+
+@pytest.mark.parametrize("arm", ["ckda", "kda"])
+def test_lm_layer_workload_full_sampled(arm):
+    """B=8 H=16 T=4096 d=128 bf16 chunk 64 at full size, in the benchmark's
+    launch configuration; oracle on 6 sampled (batch, head) pairs."""
+    announce("LM layer workload full size, %s arm" % arm)
+    c = inputs.lm_layer(arm=arm)
+    o, ht = run_chunk(c, gate=arm)
+    o = o.reshape(c.v.shape)
+    pairs = [(0, 0), (7, 15), (3, 9), (5, 2), (1, 14), (6, 7)]
+    ref = oracle_pairs(c, pairs)
+    worst_o = max(max_rel_err(o[n, :, h], ref[(n, h)][0]) for n, h in pairs)
+    worst_h = max(max_rel_err(ht[n, h], ref[(n, h)][1]) for n, h in pairs)
+    print("  err o=%.3e ht=%.3e" % (worst_o, worst_h))
+    assert worst_o < TOL["bf16"] and worst_h < TOL["bf16"]
+
+
+def test_varlen_workload_full_sampled():
+    announce("varlen workload full size")
+    c = inputs.varlen()
+    o, ht = run_chunk(c)
+    lens = np.diff(c.cu_seqlens)
+    longest, shortest = int(lens.argmax()), int(lens.argmin())
+    pairs = [(longest, 0), (shortest, 15), (0, 3), (15, 8), (7, 11)]
+    ref = oracle_pairs(c, pairs)
+    o = o[0]
+    worst_o = max(max_rel_err(o[c.cu_seqlens[n]:c.cu_seqlens[n + 1], h], ref[(n, h)][0])
+                  for n, h in pairs)
+    worst_h = max(max_rel_err(ht[n, h], ref[(n, h)][1]) for n, h in pairs)
+    print("  err o=%.3e ht=%.3e" % (worst_o, worst_h))
+    assert worst_o < TOL["bf16"] and worst_h < TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("bf16", 64, 32), ("f32", 32, 32),
+                                           ("f32", 16, 16)])
+def test_chunk_l2norm_layout_bit_exact(dtype, d, chunk):
+    """Power-of-two q/k rows through the chunked path: (a) h0 = I, alpha = 1,
+    beta = 0 gives o = q_hat exactly for every token and head; (b) one token
+    per packed sequence with h0 = 0, alpha = 1, beta = 1, v = 1 gives
+    ht[n, h, :, j] = k_hat exactly."""
+    announce("chunk l2norm layout %s d=%d C=%d" % (dtype, d, chunk))
+    B, T, H = 2, 2 * chunk + 3, 3
+    xq, yq = pow2_rows(B * T * H, d, seed=11)
+    xk, yk = pow2_rows(B * T * H, d, seed=12)
+    q = xq.reshape(B, T, H, d)
+    k = xk.reshape(B, T, H, d)
+    ones = np.ones((B, T, H, d), np.float32)
+    eye = np.broadcast_to(np.eye(d, dtype=np.float32), (B, H, d, d)).copy()
+    c = inputs.Case(q, k, np.zeros((B, T, H, d), np.float32), ones,
+                    np.zeros((B, T, H), np.float32), eye, None, dtype, chunk, True)
+    o, _ = run_chunk(c)
+    assert np.array_equal(o.reshape(-1, d).astype(np.float32), yq)
+    # (b) packed: every token its own sequence
+    N = B * T
+    c2 = inputs.Case(q.reshape(1, N, H, d), k.reshape(1, N, H, d), np.ones((1, N, H, d), np.float32),
+                     np.ones((1, N, H, d), np.float32), np.ones((1, N, H), np.float32),
+                     np.zeros((N, H, d, d), np.float32), np.arange(N + 1, dtype=np.int32),
+                     dtype, chunk, True)
+    _, ht = run_chunk(c2)
+    for j in (0, d - 1):
+        assert np.array_equal(ht[:, :, :, j].reshape(-1, d).astype(np.float32), yk)
+
+
+def test_chunk_size_invariance_and_determinism():
+    announce("chunk-size invariance")
+    c = inputs.random_case(21, 2, 200, 2, 128, 128, dtype="bf16", alpha="tanh", beta="2sig")
+    outs = [run_chunk(c, chunk=C) for C in (16, 32, 64)]
+    for o, ht in outs[1:]:
+        assert max_rel_err(o, outs[0][0]) < TOL["bf16"]
+        assert max_rel_err(ht, outs[0][1]) < TOL["bf16"]
+    o2, ht2 = run_chunk(c, chunk=64)
+    assert np.array_equal(o2, outs[2][0]) and np.array_equal(ht2, outs[2][1])
+
+
+def test_split_resume_and_aliasing():
+    """fwd(x[:T1]) -> ht, then fwd(x[T1:], h0=ht) equals fwd(x) on x[T1:];
+    h0 and ht may be the same buffer."""
+    announce("split resume")
+    c = inputs.random_case(22, 2, 190, 2, 32, 32, dtype="f32", chunk=32, h0_std=0.3)
+    o, ht = run_chunk(c)
+    T1 = 77
+    sl = lambda x, a, b: np.ascontiguousarray(x[:, a:b])
+    c1 = inputs.Case(sl(c.q, 0, T1), sl(c.k, 0, T1), sl(c.v, 0, T1), sl(c.alpha, 0, T1),
+                     sl(c.beta, 0, T1), c.h0, None, "f32", 32, True)
+    c2 = inputs.Case(sl(c.q, T1, 190), sl(c.k, T1, 190), sl(c.v, T1, 190), sl(c.alpha, T1, 190),
+                     sl(c.beta, T1, 190), None, None, "f32", 32, True)
+    o1, ht1 = run_chunk(c1)
+    # aliasing: pass one device buffer as both h0 and ht
+    st = dev(ht1.astype(np.float32))
+    o2, _ = ck.chunk_fwd(dev(c2.q), dev(c2.k), dev(c2.v), dev(c2.alpha), dev(c2.beta), h0=st,
+                         chunk_size=32, final_state=st)
+    torch.cuda.synchronize()
+    assert max_rel_err(np.concatenate([o1, host(o2)], 1), o) < TOL["f32"]
+    assert max_rel_err(host(st), ht) < TOL["f32"]
+
+
+def test_varlen_equals_separate_runs_with_empty_sequences():
+    announce("varlen vs separate")
+    rng = np.random.default_rng(23)
+    lens = [70, 0, 1, 128, 33]
+    T, H, d = sum(lens), 2, 64
+    big = inputs.random_case(24, 1, T, H, d, d, dtype="bf16", chunk=32, alpha="tanh", beta="2sig")
+    h0 = (0.1 * rng.standard_normal((len(lens), H, d, d))).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    packed = inputs.Case(big.q, big.k, big.v, big.alpha, big.beta, h0, cu, "bf16", 32, True)
+    po, pht = run_chunk(packed)
+    for i, n in enumerate(lens):
+        s = slice(cu[i], cu[i + 1])
+        one = inputs.Case(big.q[:, s], big.k[:, s], big.v[:, s], big.alpha[:, s], big.beta[:, s],
+                          h0[i:i + 1], None, "bf16", 32, True)
+        if n == 0:
+            assert np.array_equal(pht[i].astype(np.float32), h0[i])
+            continue
+        oo, hh = run_chunk(one)
+        assert np.array_equal(po[:, s], oo) and np.array_equal(pht[i], hh[0])
+
+
+def test_zero_and_tiny_gates_exact_path():
+    """Blocks with exact zero gates and gates of 1e-35 take the direct-product
+    fix-up path; both dtypes stay within tolerance, and a flipped or zeroed
+    gate moves the output by more than the tolerance (vacuity)."""
+    announce("zero and tiny gates")
+    for dtype, d, chunk in (("f32", 32, 32), ("bf16", 128, 64)):
+        c = inputs.random_case(25, 2, 150, 2, d, d, dtype=dtype, chunk=chunk, h0_std=0.2)
+        rng = np.random.default_rng(26)
+        m = rng.random(c.alpha.shape)
+        c.alpha[m < 0.03] = 0.0
+        c.alpha[(m >= 0.03) & (m < 0.06)] = 1e-35
+        c.alpha[:, 40:56, 0, :] = 0.0     # a whole sub-block of zeros
+        o, _ = _check(c)
+        flipped = c.alpha.copy()
+        flipped[0, 3, 0, :] *= -1
+        c2 = inputs.Case(c.q, c.k, c.v, flipped, c.beta, c.h0, None, dtype, chunk, True)
+        o2, _ = run_chunk(c2)
+        assert max_rel_err(o2, o) > TOL[dtype]
+
+
+def test_decode_chain_equals_prefill():
+    announce("decode chain vs prefill")
+    c = inputs.random_case(27, 3, 40, 2, 128, 128, dtype="bf16", chunk=64, alpha="tanh",
+                           beta="2sig", h0_std=0.1)
+    o, ht = run_chunk(c)
+    st = dev(c.h0)
+    outs = []
+    for t in range(40):
+        outs.append(host(ck.recurrent_step(dev(c.q[:, t], "bf16"), dev(c.k[:, t], "bf16"),
+                                           dev(c.v[:, t], "bf16"), dev(c.alpha[:, t]),
+                                           dev(c.beta[:, t]), st)))
+    assert max_rel_err(np.stack(outs, 1), o) < TOL["bf16"]
+    assert max_rel_err(host(st), ht) < TOL["bf16"]
