@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked (Complex) Kimi Delta Attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one ckda_chunk_fwd call over the LM-layer workload (B=8, T=4096,
+H=16, dk=dv=128, bf16 q/k/v, fp32 alpha/beta/state, chunk 64, in-kernel q/k
+L2 norm, CKDA gate range), inputs resident in HBM.  Prints one JSON line with
+the headline throughput (tokens/s), the roofline position of the forward
+kernel (HBM-bound: algorithmic bytes / kernel time against 8 TB/s), the
+oracle's CPU throughput on a bounded sample, and extra lines of context: the
+KDA-range arm (throughput ratio), the packed varlen prefill and the decode
+step.  Inputs are synthetic (seeded), shaped like the method's workloads.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc", "chunk_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_lm_layer_traffic.txt")
+
+
+def chunk_flops(C, dk, dv):
+    """Algorithmic flops of one chunk-head of the chunked form (triangles at
+    half): A and P Gram blocks, the UT/WY transform and the inter-chunk
+    products."""
+    return (C * (C - 1) * dk + 2 * C * (C + 1) * dk + 2 * C * (C + 1) * dv + C ** 3 / 3
+            + 6 * C * dk * dv)
+
+
+def fwd_bytes(B, T, H, dk, dv, io_bytes, nseq, h0):
+    """Algorithmic HBM bytes: every input read once, every output written once."""
+    tok = B * T
+    b = tok * H * (2 * dk + dv) * io_bytes      # q, k, v
+    b += tok * H * dk * 4 + tok * H * 4         # alpha, beta
+    b += tok * H * dv * io_bytes                # o
+    b += nseq * H * dk * dv * 4                 # ht
+    if h0:
+        b += nseq * H * dk * dv * 4
+    return b
+
+
+def src_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch measured with rocprofv3 counters for the current
+    kernel source, or None if the counters were taken on another version."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha256_16") != src_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda:0")
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def time_launches(fn, steps, warmup):
+    """Average time of `fn` (one kernel launch on the current stream) over
+    `steps` launches, with HIP events recorded on that stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1000.0 / steps
+
+
+def bench_fwd(case, steps, warmup, gate):
+    import torch
+    import gated_delta_rule_ckda_amd as ck
+    dt = case.dtype
+    q, k, v = to_dev(case.q, dt), to_dev(case.k, dt), to_dev(case.v, dt)
+    a, b = to_dev(case.alpha, "f32"), to_dev(case.beta, "f32")
+    h0 = None if case.h0 is None else to_dev(case.h0, "f32")
+    cu = None if case.cu_seqlens is None else torch.from_numpy(case.cu_seqlens).to("cuda:0")
+    o = torch.empty_like(v)
+    nseq = case.q.shape[0] if cu is None else len(case.cu_seqlens) - 1
+    H, dk, dv = case.q.shape[2], case.q.shape[3], case.v.shape[3]
+    ht = torch.empty((nseq, H, dk, dv), device="cuda:0", dtype=torch.float32)
+
+    def step():
+        ck.chunk_fwd(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
+                     use_qk_l2norm=case.l2norm, gate=gate, out=o, final_state=ht)
+
+    ms, wall_ms = time_launches(step, steps, warmup)
+    del q, k, v, a, b, o, ht
+    torch.cuda.empty_cache()
+    return ms, wall_ms
+
+
+def bench_decode(steps_inner=64, reps=3):
+    """The decode workload: 64 consecutive in-place steps (fresh inputs per
+    step, resident in HBM), timed as a whole and divided by 64."""
+    import torch
+    import gated_delta_rule_ckda_amd as ck
+    from gated_delta_rule_ckda_amd import inputs
+    N, H, d = 256, 32, 128
+    st = to_dev(inputs.decode_state(N=N, H=H, d=d), "f32")
+    toks = []
+    for s in range(steps_inner):
+        q, k, v, a, b = inputs.decode_token(s, N=N, H=H, d=d)
+        toks.append((to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(a, "f32"),
+                     to_dev(b, "f32")))
+    o = torch.empty((N, H, d), device="cuda:0", dtype=torch.bfloat16)
+
+    def run():
+        for (q, k, v, a, b) in toks:
+            ck.recurrent_step(q, k, v, a, b, st, out=o)
+
+    ms, _ = time_launches(run, reps, 1)
+    per = ms / steps_inner
+    nbytes = N * H * (2 * d * d * 4 + 3 * d * 2 + d * 4 + 4 + d * 2)
+    del st, toks
+    torch.cuda.empty_cache()
+    return per, nbytes
+
+
+def cpu_baseline(case, pairs, scale=1.0):
+    """Oracle throughput on the host cores on a bounded sample: the first
+    `pairs` (batch, head) pairs of the workload over the full sequence length
+    (pairs are independent, so this is the same per-token work)."""
+    import oracle
+    B, T, H = case.q.shape[:3]
+    sel = [(i // H, i % H) for i in range(pairs)]
+    q = np.stack([case.q[b, :, h] for b, h in sel], 0)[:, :, None]
+    k = np.stack([case.k[b, :, h] for b, h in sel], 0)[:, :, None]
+    v = np.stack([case.v[b, :, h] for b, h in sel], 0)[:, :, None]
+    a = np.stack([case.alpha[b, :, h] for b, h in sel], 0)[:, :, None]
+    be = np.stack([case.beta[b, :, h] for b, h in sel], 0)[:, :, None]
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, a, be, use_l2norm=case.l2norm, scale=scale)
+    wall = time.perf_counter() - t0
+    head_tokens = pairs * T
+    return {"value": (head_tokens / H) / wall, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) pairs x T=%d tokens of the same workload, fp64 "
+                      "sequential recurrence on %d OpenMP threads, %.1f s wall; tokens counted "
+                      "as head-tokens / H" % (pairs, B * H, T, threads, wall)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "lm"], default="all",
+                    help="'lm' times only the headline workload (for profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-pairs", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_ckda_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    case = inputs.lm_layer(arm="ckda")
+    B, T, H, dk = case.q.shape
+    dv = case.v.shape[3]
+    C = case.chunk
+    ms, wall_ms = bench_fwd(case, args.steps, args.warmup, "ckda")
+    tokens = B * T
+    tok_s = tokens / (ms / 1000.0)
+    nbytes = fwd_bytes(B, T, H, dk, dv, 2, B, False)
+    flops = chunk_flops(C, dk, dv) * (B * T // C) * H
+    gbs = nbytes / (ms / 1000.0) / 1e9
+    tflops = flops / (ms / 1000.0) / 1e12
+    traffic = load_traffic()
+
+    out = {
+        "metric": "chunked CKDA fwd tokens/s + TFLOP/s (% MFMA peak), H=16 d=128 T=4096 bf16",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.meta["workload"], "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+                   "chunk": C, "gate_range": "ckda", "use_qk_l2norm": True,
+                   "alpha": "tanh(N(2,1))", "beta": "2 sigmoid(N(0,1))"},
+        "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "kernel": "fwd_kernel<bf16, C=64, dk=dv=128, dv tile 64>",
+                     "wall_ms_per_step": round(wall_ms, 4)},
+    }
+
+    if args.only == "all":
+        kda = inputs.lm_layer(arm="kda")
+        ms_kda, _ = bench_fwd(kda, args.steps, args.warmup, "kda")
+        del kda
+        out["kda_range"] = {"tokens_per_s": round(tokens / (ms_kda / 1000.0), 1),
+                            "ms_per_step": round(ms_kda, 4),
+                            "ckda_over_kda": round(ms_kda / ms, 4),
+                            "pages_context": "CKDA keeps ~96-97% of KDA kernel throughput on H100"}
+        vl = inputs.varlen()
+        ms_vl, _ = bench_fwd(vl, max(5, args.steps // 3), 2, "ckda")
+        vl_tok = int(vl.cu_seqlens[-1])
+        vl_bytes = fwd_bytes(1, vl_tok, 16, 128, 128, 2, 16, True)
+        out["varlen"] = {"workload": vl.meta["workload"], "lengths": vl.meta["lengths"],
+                         "tokens_per_s": round(vl_tok / (ms_vl / 1000.0), 1),
+                         "ms_per_step": round(ms_vl, 4),
+                         "hbm_frac": round(vl_bytes / (ms_vl / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+        del vl
+        per, dbytes = bench_decode()
+        out["decode"] = {"workload": "decode step 256 seqs x H=32 x d=128, bf16 q/k/v, fp32 state, "
+                                     "64 in-place steps",
+                         "us_per_step": round(per * 1000.0, 2),
+                         "tokens_per_s": round(256 / (per / 1000.0), 1),
+                         "achieved_GBs": round(dbytes / (per / 1000.0) / 1e9, 1),
+                         "hbm_frac": round(dbytes / (per / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_pairs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

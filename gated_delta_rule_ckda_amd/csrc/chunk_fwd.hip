@@ -49,6 +49,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = 256;  // threads per workgroup
 constexpr int NW = 4;    // waves per workgroup
@@ -65,23 +66,33 @@ constexpr int align16(int x) { return (x + 15) & ~15; }
 struct OpBF16 {
   using T = __bf16;
   static __device__ __forceinline__ T cvt(float x) { return static_cast<__bf16>(x); }
-  // acc += A[16 x K] * B[16 x K]^T for K a multiple of 16.
-  static __device__ __forceinline__ void mma(f32x4& acc, const T* a, int lda, const T* b,
-                                             int ldb, int K, int lane) {
+  // acc += A[16 x K] * B[16 x K]^T, K a compile-time multiple of 16: all
+  // fragments are read before the MFMAs issue.
+  template <int K>
+  static __device__ __forceinline__ void mmaK(f32x4& acc, const T* a, int lda, const T* b, int ldb,
+                                              int lane) {
     const int r = lane & 15, kq = lane >> 4;
     const T* pa = a + r * lda;
     const T* pb = b + r * ldb;
-    int k0 = 0;
-    for (; k0 + 32 <= K; k0 += 32) {
-      const bf16x8 fa = *reinterpret_cast<const bf16x8*>(pa + k0 + 8 * kq);
-      const bf16x8 fb = *reinterpret_cast<const bf16x8*>(pb + k0 + 8 * kq);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+    constexpr int N32 = K / 32;
+    bf16x8 fa[N32 > 0 ? N32 : 1], fb[N32 > 0 ? N32 : 1];
+#pragma unroll
+    for (int s = 0; s < N32; ++s) {
+      fa[s] = *reinterpret_cast<const bf16x8*>(pa + 32 * s + 8 * kq);
+      fb[s] = *reinterpret_cast<const bf16x8*>(pb + 32 * s + 8 * kq);
     }
-    if (k0 < K) {
-      const bf16x4 fa = *reinterpret_cast<const bf16x4*>(pa + k0 + 4 * kq);
-      const bf16x4 fb = *reinterpret_cast<const bf16x4*>(pb + k0 + 4 * kq);
-      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, acc, 0, 0, 0);
+    // A K remainder of 16 runs as one more 16x16x32 MFMA whose upper half of
+    // K is zero (lanes 32..63 supply zeros): every MFMA accumulating into one
+    // tile then has the same shape, so dependent MFMAs never mix pass counts.
+    bf16x8 ta, tb;
+    if constexpr (K % 32 != 0) {
+      const bf16x8 z = {};
+      ta = kq < 2 ? *reinterpret_cast<const bf16x8*>(pa + 32 * N32 + 8 * kq) : z;
+      tb = kq < 2 ? *reinterpret_cast<const bf16x8*>(pb + 32 * N32 + 8 * kq) : z;
     }
+#pragma unroll
+    for (int s = 0; s < N32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s], fb[s], acc, 0, 0, 0);
+    if constexpr (K % 32 != 0) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta, tb, acc, 0, 0, 0);
   }
   // Store 4 consecutive values (one accumulator) at p.
   static __device__ __forceinline__ void store4(T* p, f32x4 x) {
@@ -89,21 +100,60 @@ struct OpBF16 {
     y[0] = cvt(x[0]); y[1] = cvt(x[1]); y[2] = cvt(x[2]); y[3] = cvt(x[3]);
     *reinterpret_cast<bf16x4*>(p) = y;
   }
+  // Store N (1 or 2) consecutive values x[i] (times f[i]) at p.
+  template <int N>
+  static __device__ __forceinline__ void storeN(T* p, const float (&x)[N]) {
+    if constexpr (N == 2) {
+      bf16x2 y;
+      y[0] = cvt(x[0]); y[1] = cvt(x[1]);
+      *reinterpret_cast<bf16x2*>(p) = y;
+    } else {
+      p[0] = cvt(x[0]);
+    }
+  }
+  template <int N>
+  static __device__ __forceinline__ void storeN(T* p, const float (&x)[N], const float (&f)[N]) {
+    float y[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) y[i] = x[i] * f[i];
+    storeN<N>(p, y);
+  }
 };
 
 struct OpF32 {
   using T = float;
   static __device__ __forceinline__ T cvt(float x) { return x; }
-  static __device__ __forceinline__ void mma(f32x4& acc, const T* a, int lda, const T* b,
-                                             int ldb, int K, int lane) {
+  template <int K>
+  static __device__ __forceinline__ void mmaK(f32x4& acc, const T* a, int lda, const T* b, int ldb,
+                                              int lane) {
     const int r = lane & 15, kq = lane >> 4;
     const T* pa = a + r * lda + kq;
     const T* pb = b + r * ldb + kq;
-    for (int k0 = 0; k0 < K; k0 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0], pb[k0], acc, 0, 0, 0);
+    float fa[K / 4], fb[K / 4];
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s) {
+      fa[s] = pa[4 * s];
+      fb[s] = pb[4 * s];
+    }
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[s], fb[s], acc, 0, 0, 0);
   }
   static __device__ __forceinline__ void store4(T* p, f32x4 x) {
     *reinterpret_cast<f32x4*>(p) = x;
+  }
+  template <int N>
+  static __device__ __forceinline__ void storeN(T* p, const float (&x)[N]) {
+    if constexpr (N == 2)
+      *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    else
+      p[0] = x[0];
+  }
+  template <int N>
+  static __device__ __forceinline__ void storeN(T* p, const float (&x)[N], const float (&f)[N]) {
+    float y[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) y[i] = x[i] * f[i];
+    storeN<N>(p, y);
   }
 };
 
@@ -121,50 +171,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(num_bytes), kRsrcWord3);
-}
-
-// N consecutive io elements at (voff + soff) bytes, widened to fp32.
-template <class IO, int N>
-__device__ __forceinline__ void buf_load(rsrc_t r, int voff, int soff, float (&out)[N]);
-
-template <>
-__device__ __forceinline__ void buf_load<io_bf16, 1>(rsrc_t r, int voff, int soff, float (&out)[1]) {
-  const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-  out[0] = __uint_as_float(u << 16);
-}
-template <>
-__device__ __forceinline__ void buf_load<io_bf16, 2>(rsrc_t r, int voff, int soff, float (&out)[2]) {
-  const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-  out[0] = __uint_as_float(u << 16);
-  out[1] = __uint_as_float(u & 0xFFFF0000u);
-}
-template <>
-__device__ __forceinline__ void buf_load<io_f32, 1>(rsrc_t r, int voff, int soff, float (&out)[1]) {
-  out[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-template <>
-__device__ __forceinline__ void buf_load<io_f32, 2>(rsrc_t r, int voff, int soff, float (&out)[2]) {
-  const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-  out[0] = __uint_as_float(u[0]);
-  out[1] = __uint_as_float(u[1]);
-}
-// 16 bytes: 8 bf16 or 4 fp32
-template <class IO>
-__device__ __forceinline__ void buf_load16(rsrc_t r, int voff, int soff, float* out);
-template <>
-__device__ __forceinline__ void buf_load16<io_bf16>(rsrc_t r, int voff, int soff, float* out) {
-  const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = __uint_as_float(u[i] << 16);
-    out[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void buf_load16<io_f32>(rsrc_t r, int voff, int soff, float* out) {
-  const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(u[i]);
 }
 
 // ---- compile-time configuration and LDS map ---------------------------------
@@ -192,9 +198,9 @@ struct Cfg {
   static constexpr int NUT = (C / 16) * (DVT / 16);  // U tiles
   static constexpr int NUW = (NUT + NW - 1) / NW;
   static constexpr int IOES = static_cast<int>(sizeof(typename IO::storage));
-  static constexpr int VEC = 16 / IOES;              // v elements per 16-byte load
-  static constexpr int TPR = DVT / VEC;              // threads per v row
-  static constexpr int RPP = NT / TPR;               // v rows per pass
+  static constexpr int NCP = DVT / 2;                // v column pairs
+  static constexpr int RPL = (C * NCP + NT - 1) / NT; // v rows per thread
+  static constexpr int VW = (2 * IOES) / 4;          // dwords per column pair
 
   // byte offsets
   static constexpr int O_S = 0;                                   // S^T   [DVT][LDK] T
@@ -228,9 +234,92 @@ struct Cfg {
   static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0 && DV % DVT == 0, "tile sizes");
   static_assert(NB <= NW, "one wave per sub-block");
   static_assert(DK <= 128 && NCG <= 64, "two channels per lane at most");
-  static_assert(DVT % VEC == 0 && NT % TPR == 0, "v tile mapping");
+  static_assert(NT % NCP == 0 && (NT / NCP) * RPL >= C, "v tile mapping");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+
+// ---- chunk input prefetch ---------------------------------------------------
+// Raw (undecoded) registers of one chunk's inputs for this thread.  The next
+// chunk's loads are issued into them right after the current chunk has been
+// decoded, so HBM latency hides behind a whole chunk of compute.  Row offsets
+// are clamped to the chunk's last valid row, so every access stays inside the
+// tensors; padded rows are replaced after the load (q = k = v = 0, alpha = 1,
+// beta = 0: identity tokens).
+template <class Cfg>
+struct Prefetch {
+  static constexpr int QB = Cfg::CPT * Cfg::IOES;  // bytes of q (or k) per row and lane
+  static constexpr int QW = (QB + 3) / 4;
+  uint32_t q[16][QW], k[16][QW], al[16][Cfg::CPT];
+  uint32_t v[Cfg::RPL][Cfg::VW];
+  uint32_t vb[Cfg::RPL];
+  uint32_t bt;
+};
+
+template <int BYTES>
+__device__ __forceinline__ void ldraw(rsrc_t r, int voff, int soff, uint32_t* d) {
+  if constexpr (BYTES == 2) {
+    d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  } else if constexpr (BYTES == 4) {
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  } else if constexpr (BYTES == 8) {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    d[0] = u[0];
+    d[1] = u[1];
+  } else {
+    static_assert(BYTES == 16, "load width");
+    const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    d[0] = u[0]; d[1] = u[1]; d[2] = u[2]; d[3] = u[3];
+  }
+}
+
+// element e of a raw row fragment, widened to fp32
+template <class IO>
+__device__ __forceinline__ float dec(const uint32_t* d, int e) {
+  if constexpr (sizeof(typename IO::storage) == 2)
+    return __uint_as_float((e & 1) ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16));
+  else
+    return __uint_as_float(d[e]);
+}
+
+__device__ __forceinline__ int sclamp(int x, int hi) { return x < hi ? x : hi; }
+
+template <class Cfg>
+__device__ __forceinline__ void issue_loads(Prefetch<Cfg>& pf, const FwdArgs& a, int64_t t,
+                                            int Ln, int h, int dv0, int tid, int scan_I,
+                                            bool scan_on, int c0ch) {
+  using IO = typename Cfg::IO;
+  constexpr int DK = Cfg::DK, ES = Cfg::IOES;
+  const int H = a.H;
+  const int krow = H * DK * ES;       // bytes per token in q / k
+  const int arow = H * DK * 4;        // bytes per token in alpha
+  const int vrow = H * a.dv * ES;     // bytes per token in v
+  const int64_t qk_off = (t * H + h) * static_cast<int64_t>(DK);
+  if (scan_on) {
+    const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + qk_off * ES, Ln * krow);
+    const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + qk_off * ES, Ln * krow);
+    const rsrc_t ra = make_rsrc(a.alpha + qk_off, Ln * arow);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = sclamp(16 * scan_I + i, Ln - 1);
+      ldraw<Prefetch<Cfg>::QB>(rq, c0ch * ES + row * krow, 0, pf.q[i]);
+      ldraw<Prefetch<Cfg>::QB>(rk, c0ch * ES + row * krow, 0, pf.k[i]);
+      ldraw<Cfg::CPT * 4>(ra, c0ch * 4 + row * arow, 0, pf.al[i]);
+    }
+  }
+  // v tile: column pair cp, rows rg * RPL + i
+  const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) +
+                                  ((t * H + h) * static_cast<int64_t>(a.dv) + dv0) * ES,
+                              Ln * vrow);
+  const rsrc_t rb = make_rsrc(a.beta + t * H + h, Ln * H * 4);
+  const int cp = tid % Cfg::NCP, rg = tid / Cfg::NCP;
+#pragma unroll
+  for (int i = 0; i < Cfg::RPL; ++i) {
+    const int j = sclamp(rg * Cfg::RPL + i, Ln - 1);
+    ldraw<Cfg::VW * 4>(rv, 2 * cp * ES + j * vrow, 0, pf.v[i]);
+    pf.vb[i] = __builtin_amdgcn_raw_buffer_load_b32(rb, j * H * 4, 0, 0);
+  }
+  pf.bt = __builtin_amdgcn_raw_buffer_load_b32(rb, sclamp(tid, Ln - 1) * H * 4, 0, 0);
+}
 
 template <class Cfg>
 __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
@@ -241,6 +330,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
   constexpr int C = Cfg::C, DK = Cfg::DK, DVT = Cfg::DVT, NB = Cfg::NB;
   constexpr int CPT = Cfg::CPT, NCG = Cfg::NCG;
   constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, LDF = Cfg::LDF;
+  constexpr int NTN = DVT / 16;
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* sS = reinterpret_cast<T*>(smem + Cfg::O_S);
@@ -273,8 +363,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
   const int l16 = lane & 15, lq = lane >> 4;
 
   // ---- which chain: (sequence, head) pairs of one dv-split sit 8 workgroups
-  // apart so that both tiles of a pair land on the same XCD (shared q/k/alpha
-  // reads hit one L2).
+  // apart so that both tiles of a pair land on the same XCD (their shared
+  // q/k/alpha reads then hit one L2).
   const int64_t nblk = gridDim.x;
   const int64_t b = blockIdx.x;
   int64_t pair;
@@ -299,15 +389,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
     eos = bos + a.T;
   }
   const int dv0 = split * DVT;
-
-  const ST* gq = static_cast<const ST*>(a.q);
-  const ST* gk = static_cast<const ST*>(a.k);
-  const ST* gv = static_cast<const ST*>(a.v);
   ST* go = static_cast<ST*>(a.o);
 
   // ---- state tile in accumulator layout: tile t = wave + NW*u covers rows
-  // c = 16*(t / (DVT/16)) + 4*lq + i, columns dv = 16*(t % (DVT/16)) + l16.
-  constexpr int NTN = DVT / 16;
+  // c = 16*(t / NTN) + 4*lq + i, columns dv = 16*(t % NTN) + l16.
   f32x4 sacc[Cfg::NSW];
   const int64_t st_base = (n * H + h) * static_cast<int64_t>(DK) * a.dv + dv0;
 #pragma unroll
@@ -320,7 +405,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 4; ++i) sacc[u][i] = a.h0[st_base + static_cast<int64_t>(c + i) * a.dv + dv];
     }
   }
-  // bf16 (or fp32) operand copy S^T[dv][c]
 #pragma unroll
   for (int u = 0; u < Cfg::NSW; ++u) {
     const int t = wave + NW * u;
@@ -329,62 +413,61 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
       Op::store4(sS + dv * LDK + c, sacc[u]);
     }
   }
+  // The blocks above the diagonal of P and of X's operand copy are never
+  // written later: zero both buffers once.
+  for (int e = tid; e < C * LDC; e += NT) {
+    sP[e] = Op::cvt(0.f);
+    sXb[e] = Op::cvt(0.f);
+  }
 
   const float use_l2 = static_cast<float>(a.use_l2norm);
   const int scan_I = wave;                 // sub-block handled by this wave in the scan
   const bool scan_on = (scan_I < NB) && (lane < NCG);
   const int c0ch = lane * CPT;             // first channel of this lane
+  const int vcp = tid % Cfg::NCP, vrg = tid / Cfg::NCP;
+
+  Prefetch<Cfg> pf;
+  if (bos < eos)
+    issue_loads<Cfg>(pf, a, bos, static_cast<int>((eos - bos) < C ? (eos - bos) : C), h, dv0, tid,
+                     scan_I, scan_on, c0ch);
 
   for (int64_t t0 = bos; t0 < eos; t0 += C) {
     const int L = static_cast<int>((eos - t0) < C ? (eos - t0) : C);
 
-    // ================= phase 1: loads, running products, operands ==========
+    // ================= phase 1: decode, running products, operands =========
     // q/k/alpha of this lane's channels over the 16 rows of its sub-block.
     // Registers are reused in place as the phases go: alpha -> F -> Kt,
     // B -> Kh, q -> Qt.
     float xq[16][CPT], xk[16][CPT], F[16][CPT], Bk[16][CPT];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool in = 16 * scan_I + i < L;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        xq[i][c] = in ? dec<IO>(pf.q[i], c) : 0.f;
+        xk[i][c] = in ? dec<IO>(pf.k[i], c) : 0.f;
+        F[i][c] = in ? __uint_as_float(pf.al[i][c]) : 1.f;
+      }
+    }
+    // (beta V)^T tile: this thread's column pair over RPL rows
     {
-      // (beta V)^T tile: thread loads 16 bytes (VEC columns) of one row per pass
-      const int64_t vrow = static_cast<int64_t>(H) * a.dv * Cfg::IOES;  // bytes per token
-      const rsrc_t rv = make_rsrc(reinterpret_cast<const char*>(gv) +
-                                      ((t0 * H + h) * static_cast<int64_t>(a.dv) + dv0) * Cfg::IOES,
-                                  static_cast<uint32_t>((L - 1) * vrow + DVT * Cfg::IOES));
-      const int vc = (tid % Cfg::TPR) * Cfg::VEC, vr0 = tid / Cfg::TPR;
 #pragma unroll
-      for (int p = 0; p < (C + Cfg::RPP - 1) / Cfg::RPP; ++p) {
-        const int j = vr0 + p * Cfg::RPP;
+      for (int i = 0; i < Cfg::RPL; ++i) {
+        const int j = vrg * Cfg::RPL + i;
         if (j < C) {
-          float x[Cfg::VEC];
-          buf_load16<IO>(rv, vc * Cfg::IOES, static_cast<int>(j * vrow), x);
-          const float bj = (j < L) ? a.beta[(t0 + j) * H + h] : 0.f;
-#pragma unroll
-          for (int e = 0; e < Cfg::VEC; ++e) sVT[(vc + e) * LDC + j] = Op::cvt(x[e] * bj);
+          const float bj = (j < L) ? __uint_as_float(pf.vb[i]) : 0.f;
+          sVT[(2 * vcp) * LDC + j] = Op::cvt(dec<IO>(pf.v[i], 0) * bj);
+          sVT[(2 * vcp + 1) * LDC + j] = Op::cvt(dec<IO>(pf.v[i], 1) * bj);
         }
       }
     }
+    if (tid < C) sbeta[tid] = (tid < L) ? __uint_as_float(pf.bt) : 0.f;
+    // the next chunk's inputs stream in while this chunk is processed
+    if (t0 + C < eos)
+      issue_loads<Cfg>(pf, a, t0 + C, static_cast<int>((eos - t0 - C) < C ? (eos - t0 - C) : C), h,
+                       dv0, tid, scan_I, scan_on, c0ch);
+
     if (scan_on) {
-      const int64_t krow = static_cast<int64_t>(H) * DK * Cfg::IOES;  // bytes per token
-      const int64_t base = (t0 * H + h) * static_cast<int64_t>(DK);
-      const uint32_t nb = static_cast<uint32_t>((L - 1) * krow + DK * Cfg::IOES);
-      const rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(gq) + base * Cfg::IOES, nb);
-      const rsrc_t rk = make_rsrc(reinterpret_cast<const char*>(gk) + base * Cfg::IOES, nb);
-      const rsrc_t ra = make_rsrc(a.alpha + base,
-                                  static_cast<uint32_t>((L - 1) * H * DK * 4 + DK * 4));
-      const int sI = __builtin_amdgcn_readfirstlane(scan_I);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * sI + i;
-        float tq[CPT], tk[CPT], ta[CPT];
-        buf_load<IO, CPT>(rq, c0ch * Cfg::IOES, static_cast<int>(r * krow), tq);
-        buf_load<IO, CPT>(rk, c0ch * Cfg::IOES, static_cast<int>(r * krow), tk);
-        buf_load<io_f32, CPT>(ra, c0ch * 4, r * H * DK * 4, ta);
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          xq[i][c] = tq[c];
-          xk[i][c] = tk[c];
-          F[i][c] = (r < L) ? ta[c] : 1.f;
-        }
-      }
       float mn[CPT];
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
@@ -405,17 +488,20 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
         sG[scan_I * DK + c0ch + c] = F[15][c];
         sSafe[scan_I * DK + c0ch + c] = mn[c] >= kSafeMin ? 1 : 0;
       }
-      // Lk, Lq and the diagonal panel slot of R
+      // Lk, Lq and the diagonal panel slot of R (k / F on safe channels)
       T* rdiag = sR + (8 * scan_I * (scan_I + 1) + 16 * scan_I) * LDK;
+      float rinv[16][CPT];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+          rinv[i][c] = mn[c] >= kSafeMin ? xk[i][c] * __builtin_amdgcn_rcpf(F[i][c]) : 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 16 * scan_I + i;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          sLk[r * LDK + c0ch + c] = Op::cvt(xk[i][c] * F[i][c]);
-          sLq[r * LDK + c0ch + c] = Op::cvt(xq[i][c] * F[i][c]);
-          rdiag[i * LDK + c0ch + c] = Op::cvt(mn[c] >= kSafeMin ? xk[i][c] / F[i][c] : 0.f);
-        }
+        Op::template storeN<CPT>(sLk + r * LDK + c0ch, xk[i], F[i]);
+        Op::template storeN<CPT>(sLq + r * LDK + c0ch, xq[i], F[i]);
+        Op::template storeN<CPT>(rdiag + i * LDK + c0ch, rinv[i]);
       }
       // per-row partial sums of squares (this lane's channels)
 #pragma unroll
@@ -437,7 +523,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
         sKpart[scan_I * Cfg::PART + lane * 17 + i] = 0.f;
       }
     }
-    if (tid < C) sbeta[tid] = (tid < L) ? a.beta[(t0 + tid) * H + h] : 0.f;
     __syncthreads();  // B1
 
     // ================= phase 2: block products, panels, norms ==============
@@ -459,23 +544,25 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
           for (int M = 0; M < NB; ++M) g *= gm[M];
           sg[c0ch + c] = g;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          xq[i][c] = xq[i][c] * F[i][c] * gpre;    // Qt
+          F[i][c] = xk[i][c] * F[i][c] * gpre;     // Kt (unscaled)
+          Bk[i][c] = xk[i][c] * Bk[i][c];          // k B (the anchor factor of the R panels)
+        }
         // R panels of the later blocks: rows of this block, anchor at I2's start
         float mid = 1.f;
 #pragma unroll
         for (int I2 = 1; I2 < NB; ++I2) {
           if (I2 > scan_I) {
             if (I2 > scan_I + 1) mid *= gm[I2 - 1];
-            T* pan = sR + (8 * I2 * (I2 + 1) + 16 * scan_I) * LDK;
+            T* pan = sR + (8 * I2 * (I2 + 1) + 16 * scan_I) * LDK + c0ch + c;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) pan[i * LDK + c0ch + c] = Op::cvt(xk[i][c] * Bk[i][c] * mid);
+            for (int i = 0; i < 16; ++i) pan[i * LDK] = Op::cvt(Bk[i][c] * mid);
           }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          xq[i][c] = xq[i][c] * F[i][c] * gpre;   // Qt
-          F[i][c] = xk[i][c] * F[i][c] * gpre;    // Kt (unscaled)
-          Bk[i][c] = xk[i][c] * Bk[i][c] * gpost; // Kh
-        }
+        for (int i = 0; i < 16; ++i) Bk[i][c] *= gpost;  // Kh
       }
     }
     if (scan_I < NB) {
@@ -502,41 +589,53 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
     // ================= phase 3: A and P^T panels on MFMA ====================
     {
       constexpr int NPT = NB * (NB + 1) / 2;  // tiles per matrix
-      for (int tt = wave; tt < 2 * NPT; tt += NW) {
-        const bool isA = tt < NPT;
-        int idx = isA ? tt : tt - NPT;
-        int I = 0;
-        while (idx > I) {
-          idx -= I + 1;
-          ++I;
-        }
-        const int J = idx;  // 0..I
-        const T* pan = sR + (8 * I * (I + 1) + 16 * J) * LDK;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (isA) {
-          Op::mma(acc, sLk + 16 * I * LDK, LDK, pan, LDK, DK, lane);
-          // rows r = 16I + 4lq + i, column j = 16J + l16; store A^T[j][r]
-          const int j = 16 * J + l16;
-          const float sj = srk[j];
-          f32x4 out;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * I + 4 * lq + i;
-            const float v = acc[i] * sbeta[r] * srk[r] * sj;
-            out[i] = (I == J && j >= r) ? 0.f : v;
+      constexpr int NU = (2 * NPT + NW - 1) / NW;
+#pragma unroll 1
+      for (int u = 0; u < NU; ++u) {
+        const int tt = wave + NW * u;
+        if (tt < 2 * NPT) {
+          const bool isA = tt < NPT;
+          int idx = isA ? tt : tt - NPT;
+          int I = 0;
+          while (idx > I) {
+            idx -= I + 1;
+            ++I;
           }
-          *reinterpret_cast<f32x4*>(sAT + j * LDF + 16 * I + 4 * lq) = out;
-        } else {
-          Op::mma(acc, pan, LDK, sLq + 16 * I * LDK, LDK, DK, lane);
-          // rows j = 16J + 4lq + i, column r = 16I + l16; store P[r][j]
-          const int r = 16 * I + l16;
-          f32x4 out;
+          const int J = idx;  // 0..I
+          const T* pan = sR + (8 * I * (I + 1) + 16 * J) * LDK;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (isA) {
+            Op::template mmaK<DK>(acc, sLk + 16 * I * LDK, LDK, pan, LDK, lane);
+            // rows r = 16I + 4lq + i, column j = 16J + l16; store A^T[j][r]
+            const int j = 16 * J + l16;
+            const float sj = srk[j];
+            f32x4 out;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = 16 * J + 4 * lq + i;
-            out[i] = (I == J && j > r) ? 0.f : acc[i];
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * I + 4 * lq + i;
+              const float v = acc[i] * sbeta[r] * srk[r] * sj;
+              out[i] = (I == J && j >= r) ? 0.f : v;
+            }
+            *reinterpret_cast<f32x4*>(sAT + j * LDF + 16 * I + 4 * lq) = out;
+            if (I == J) {
+              // the diagonal block also goes row-major into the diagonal block
+              // of X's buffer, where the substitution reads it and then
+              // overwrites it with X_II (sXf is not in use during this phase)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sXf[(16 * I + 4 * lq + i) * LDF + 16 * I + l16] = out[i];
+            }
+          } else {
+            Op::template mmaK<DK>(acc, pan, LDK, sLq + 16 * I * LDK, LDK, lane);
+            // rows j = 16J + 4lq + i, column r = 16I + l16; store P[r][j]
+            const int r = 16 * I + l16;
+            f32x4 out;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = 16 * J + 4 * lq + i;
+              out[i] = (I == J && j > r) ? 0.f : acc[i];
+            }
+            Op::store4(sP + r * LDC + 16 * J + 4 * lq, out);
           }
-          Op::store4(sP + r * LDC + 16 * J + 4 * lq, out);
         }
       }
     }
@@ -547,8 +646,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 16 * scan_I + i;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) sQt[r * LDK + c0ch + c] = Op::cvt(xq[i][c]);
+        Op::template storeN<CPT>(sQt + r * LDK + c0ch, xq[i]);
       }
       float wsc[16];  // beta_j rk_j folded into Kt's rows
 #pragma unroll
@@ -579,12 +677,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
         float accA[16], accP[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) accA[r] = accP[r] = 0.f;
-        const int64_t krow = static_cast<int64_t>(H) * DK;  // elements per token
+        const int krow = H * DK;  // elements per token
         const int64_t base = (t0 * H + h) * static_cast<int64_t>(DK);
-        const uint32_t nb = static_cast<uint32_t>(((L - 1) * krow + DK) * Cfg::IOES);
-        const rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(gq) + base * Cfg::IOES, nb);
-        const rsrc_t rk = make_rsrc(reinterpret_cast<const char*>(gk) + base * Cfg::IOES, nb);
-        const rsrc_t ra = make_rsrc(a.alpha + base, static_cast<uint32_t>(((L - 1) * krow + DK) * 4));
+        const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + base * Cfg::IOES,
+                                    L * krow * Cfg::IOES);
+        const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + base * Cfg::IOES,
+                                    L * krow * Cfg::IOES);
+        const rsrc_t ra = make_rsrc(a.alpha + base, L * krow * 4);
         const int sI = __builtin_amdgcn_readfirstlane(I);
         for (int c = lq; c < DK; c += 4) {
           if (sSafe[I * DK + c]) continue;
@@ -592,13 +691,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = 16 * sI + r;
-            float t1[1], t2[1], t3[1];
-            buf_load<IO, 1>(rq, c * Cfg::IOES, static_cast<int>(row * krow * Cfg::IOES), t1);
-            buf_load<IO, 1>(rk, c * Cfg::IOES, static_cast<int>(row * krow * Cfg::IOES), t2);
-            buf_load<io_f32, 1>(ra, c * 4, static_cast<int>(row * krow * 4), t3);
-            qr[r] = t1[0];
-            kr[r] = t2[0];
-            ar[r] = (row < L) ? t3[0] : 1.f;
+            const int crow = sclamp(row, L - 1);
+            uint32_t t1[1], t2[1], t3[1];
+            ldraw<Cfg::IOES>(rq, c * Cfg::IOES, crow * krow * Cfg::IOES, t1);
+            ldraw<Cfg::IOES>(rk, c * Cfg::IOES, crow * krow * Cfg::IOES, t2);
+            ldraw<4>(ra, c * 4, crow * krow * 4, t3);
+            qr[r] = (row < L) ? dec<IO>(t1, 0) : 0.f;
+            kr[r] = (row < L) ? dec<IO>(t2, 0) : 0.f;
+            ar[r] = (row < L) ? __uint_as_float(t3[0]) : 1.f;
             if (r == j) kj = kr[r];
           }
           float d = 1.f;
@@ -624,7 +724,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rr = 16 * I + r;
-            if (r > j) sAT[jj * LDF + rr] += accA[r] * sbeta[rr] * srk[rr] * sj;
+            if (r > j) {
+              const float add = accA[r] * sbeta[rr] * srk[rr] * sj;
+              sAT[jj * LDF + rr] += add;
+              sXf[rr * LDF + jj] += add;
+            }
             if (r >= j) {
               const float p = static_cast<float>(sP[rr * LDC + jj]) + accP[r];
               sP[rr * LDC + jj] = Op::cvt(p);
@@ -637,16 +741,26 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
 
     // ================= phase 5: X = (I + A)^{-1} ============================
     if (wave < NB && lane < 16) {
-      // forward substitution for column j of the diagonal block (I, I)
+      // forward substitution for column j of the diagonal block (I, I):
+      // x_i = delta_ij - sum_{m<i} A(i, m) x_m, with A's rows read in one batch
       const int I = wave, j = lane;
+      const float* arow = sXf + 16 * I * LDF + 16 * I;  // A(16I + i, 16I + m) at [i * LDF + m]
+      f32x4 av[16][4];
+#pragma unroll
+      for (int i = 1; i < 16; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (4 * g < i) av[i][g] = *reinterpret_cast<const f32x4*>(arow + i * LDF + 4 * g);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const float* acol = sAT + (16 * I + m) * LDF + 16 * I;  // A(16I + i, 16I + m)
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) x[i] -= acol[i] * x[m];
+        for (int m = 0; m < i; ++m) acc -= av[i][m >> 2][m & 3] * x[m];
+        x[i] = acc;
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sXf[(16 * I + i) * LDF + 16 * I + j] = x[i];
@@ -658,11 +772,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
         const int I = J + d;
         f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
         for (int M = J; M < I; ++M) {
+          float av[4], xv[4];
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             const int m = 16 * M + 4 * kk + lq;
-            tacc = mfma_f32(sAT[m * LDF + 16 * I + l16], sXf[m * LDF + 16 * J + l16], tacc);
+            av[kk] = sAT[m * LDF + 16 * I + l16];
+            xv[kk] = sXf[m * LDF + 16 * J + l16];
           }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) tacc = mfma_f32(av[kk], xv[kk], tacc);
         }
         float* ts = sTS + wave * Cfg::TSCR;
 #pragma unroll
@@ -670,21 +788,36 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
+        float xa[4], tb[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int m = 4 * kk + lq;
-          xacc = mfma_f32(sXf[(16 * I + l16) * LDF + 16 * I + m], ts[m * 20 + l16], xacc);
+          xa[kk] = sXf[(16 * I + l16) * LDF + 16 * I + m];
+          tb[kk] = ts[m * 20 + l16];
         }
+        f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) xacc = mfma_f32(xa[kk], tb[kk], xacc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sXf[(16 * I + 4 * lq + i) * LDF + 16 * J + l16] = -xacc[i];
       }
       __syncthreads();
     }
-    // X (lower triangle) as an MFMA operand
-    for (int e = tid; e < C * C; e += NT) {
-      const int r = e / C, j = e % C;
-      sXb[r * LDC + j] = Op::cvt((j <= r) ? sXf[r * LDF + j] : 0.f);
+    // X (lower blocks; zeros above the diagonal inside the diagonal blocks) as
+    // an MFMA operand.  Blocks above the diagonal stay zero from the start.
+    {
+      constexpr int NLB = NB * (NB + 1) / 2;   // lower 16x16 blocks
+      constexpr int NQ = NLB * 16 * 4;         // 4-element groups
+      for (int e = tid; e < NQ; e += NT) {
+        int blk = e / 64, w = e % 64;
+        int I = 0;
+        while (blk > I) {
+          blk -= I + 1;
+          ++I;
+        }
+        const int r = 16 * I + w / 4, j = 16 * blk + 4 * (w % 4);
+        Op::store4(sXb + r * LDC + j, *reinterpret_cast<const f32x4*>(sXf + r * LDF + j));
+      }
     }
     __syncthreads();
 
@@ -692,12 +825,17 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
     {
       // W^T tiles (channel block mc, row block nr): -W stored row-major
       constexpr int NWT = (DK / 16) * (C / 16);
-      for (int tt = wave; tt < NWT; tt += NW) {
-        const int mc = tt / (C / 16), nr = tt % (C / 16);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        Op::mma(acc, sKtT + 16 * mc * LDC, LDC, sXb + 16 * nr * LDC, LDC, 16 * (nr + 1), lane);
-        // rows c = 16mc + 4lq + i, column r = 16nr + l16
-        Op::store4(sWn + (16 * nr + l16) * LDK + 16 * mc + 4 * lq, -acc);
+      constexpr int NU = (NWT + NW - 1) / NW;
+#pragma unroll 1
+      for (int u = 0; u < NU; ++u) {
+        const int tt = wave + NW * u;
+        if (tt < NWT) {
+          const int mc = tt / (C / 16), nr = tt % (C / 16);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          Op::template mmaK<C>(acc, sKtT + 16 * mc * LDC, LDC, sXb + 16 * nr * LDC, LDC, lane);
+          // rows c = 16mc + 4lq + i, column r = 16nr + l16
+          Op::store4(sWn + (16 * nr + l16) * LDK + 16 * mc + 4 * lq, -acc);
+        }
       }
     }
     f32x4 uacc[Cfg::NUW];
@@ -707,7 +845,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
       uacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (tt < Cfg::NUT) {
         const int rb = tt / NTN, db = tt % NTN;
-        Op::mma(uacc[u], sXb + 16 * rb * LDC, LDC, sVT + 16 * db * LDC, LDC, 16 * (rb + 1), lane);
+        Op::template mmaK<C>(uacc[u], sXb + 16 * rb * LDC, LDC, sVT + 16 * db * LDC, LDC, lane);
       }
     }
     __syncthreads();
@@ -718,7 +856,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
       const int tt = wave + NW * u;
       if (tt < Cfg::NUT) {
         const int rb = tt / NTN, db = tt % NTN;
-        Op::mma(uacc[u], sWn + 16 * rb * LDK, LDK, sS + 16 * db * LDK, LDK, DK, lane);
+        Op::template mmaK<DK>(uacc[u], sWn + 16 * rb * LDK, LDK, sS + 16 * db * LDK, LDK, lane);
         // rows j = 16rb + 4lq + i, column dv = 16db + l16 -> U'^T[dv][j]
         f32x4 un;
 #pragma unroll
@@ -731,18 +869,23 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
     // ================= phase 8: outputs and state update ====================
     {
       constexpr int NOT = NTN * (C / 16);
-      for (int tt = wave; tt < NOT; tt += NW) {
-        const int db = tt / (C / 16), rb = tt % (C / 16);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        Op::mma(acc, sS + 16 * db * LDK, LDK, sQt + 16 * rb * LDK, LDK, DK, lane);
-        Op::mma(acc, sUn + 16 * db * LDC, LDC, sP + 16 * rb * LDC, LDC, 16 * (rb + 1), lane);
-        // rows dv = 16db + 4lq + i, column r = 16rb + l16
-        const int r = 16 * rb + l16;
-        if (r < L) {
-          const float sc = a.scale * srq[r];
-          const int64_t off = ((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0 + 16 * db + 4 * lq;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) IO::store(go, off + i, acc[i] * sc);
+      constexpr int NU = (NOT + NW - 1) / NW;
+#pragma unroll 1
+      for (int u = 0; u < NU; ++u) {
+        const int tt = wave + NW * u;
+        if (tt < NOT) {
+          const int db = tt / (C / 16), rb = tt % (C / 16);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          Op::template mmaK<DK>(acc, sS + 16 * db * LDK, LDK, sQt + 16 * rb * LDK, LDK, lane);
+          Op::template mmaK<C>(acc, sUn + 16 * db * LDC, LDC, sP + 16 * rb * LDC, LDC, lane);
+          // rows dv = 16db + 4lq + i, column r = 16rb + l16
+          const int r = 16 * rb + l16;
+          if (r < L) {
+            const float sc = a.scale * srq[r];
+            const int64_t off =
+                ((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0 + 16 * db + 4 * lq;
+            IO::store4(go + off, acc * sc);
+          }
         }
       }
     }
@@ -751,9 +894,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
       const int t = wave + NW * u;
       if (t < Cfg::NST) {
         const int mc = t / NTN, db = t % NTN;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[u][i] *= sg[16 * mc + 4 * lq + i];
-        Op::mma(sacc[u], sKhT + 16 * mc * LDC, LDC, sUn + 16 * db * LDC, LDC, C, lane);
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(sg + 16 * mc + 4 * lq);
+        sacc[u] *= gv;
+        Op::template mmaK<C>(sacc[u], sKhT + 16 * mc * LDC, LDC, sUn + 16 * db * LDC, LDC, lane);
       }
     }
     __syncthreads();
@@ -765,8 +908,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_kernel(FwdArgs a) {
         Op::store4(sS + dv * LDK + c, sacc[u]);
       }
     }
-    // the next chunk's first write to shared memory that sS readers could see
-    // comes after its barrier B1
+    // the next chunk's first shared-memory writes that readers of sS could
+    // race with come after its barrier B1
   }
 
   if (a.ht) {

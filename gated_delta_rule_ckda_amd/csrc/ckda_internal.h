@@ -77,11 +77,20 @@ struct io_bf16 {
   static __device__ __forceinline__ void store(storage* p, int64_t i, float x) {
     p[i] = f32_to_bf16(x);
   }
+  // 4 consecutive values at p (8-byte aligned)
+  static __device__ __forceinline__ void store4(storage* p, f32x4 x) {
+    const uint32_t lo = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    const uint32_t hi = f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+  }
 };
 struct io_f32 {
   using storage = float;
   static __device__ __forceinline__ float load(const storage* p, int64_t i) { return p[i]; }
   static __device__ __forceinline__ void store(storage* p, int64_t i, float x) { p[i] = x; }
+  static __device__ __forceinline__ void store4(storage* p, f32x4 x) {
+    *reinterpret_cast<f32x4*>(p) = x;
+  }
 };
 
 constexpr float kL2Eps = 1e-6f;
