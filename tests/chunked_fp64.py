@@ -2,9 +2,9 @@
 
 It exists to pin that algebra against the sequential oracle: if this model
 and the oracle agree to ~1e-12 on inputs with zero and negative gates, short
-final chunks and every sub-block size, the factorisation the kernel uses is
-exact (the kernel then differs from the oracle by rounding only).  It shares
-no code with the HIP library and is used by the tests only.
+final chunks and both code paths, the factorisation the kernel uses is exact
+(the kernel then differs from the oracle by rounding only).  It shares no code
+with the HIP library and is used by the tests only.
 
 Derivation (for one sequence and head; written out because the pages print
 only the transition A_t = (I - beta_t k_t k_t^T) Diag(alpha_t), picx.dev
@@ -21,23 +21,25 @@ and "from the chunk start" means j = -1):
     S_C = Diag(g) S_0 + Kh^T U
 
 with Kt_r = D(r<-(-1)) * k_r, Qt_r = D(r<-(-1)) * q_r, Kh_j = D(C-1<-j) * k_j
-and g = D(C-1<-(-1)).  The per-channel decays are built without division
-from products of alpha inside sub-blocks of `blk` rows:
+and g = D(C-1<-(-1)).
 
-    F_r = prod of alpha over the rows of r's sub-block up to and including r
-    B_r = prod of alpha over the rows of r's sub-block after r
-    G_I = prod of alpha over sub-block I
+Regular chunks.  With the chunk's running gate product Ft_r = prod_{s<=r}
+alpha_s (per channel), D(r<-j) = Ft_r * (1 / Ft_j), so
 
-so that, for r in sub-block I and j in an earlier sub-block J,
-D(r<-j) = F_r * (prod_{J<M<I} G_M) * B_j, a product of factors of modulus at
-most one (exact for zero and negative gates).  Inside one sub-block,
-D(r<-j) = F_r * (1 / F_j) whenever no |F| in the sub-block is below 2^-100
-(then no factor overflows), else the product of alpha is taken directly.
+    A_rj = beta_r <k_r * Ft_r, k_j / Ft_j>,  P_rj = <q_r * Ft_r, k_j / Ft_j>,
+    Kt = k * Ft,  Qt = q * Ft,  Kh_j = g * k_j / Ft_j,  g = Ft_{C-1}.
+
+This is used when every |Ft_r| lies in [2^-100, 2^10]: then no factor
+overflows and no quotient is formed by a zero (signs are exact).
+
+Irregular chunks (an exact zero gate, or gates so small that the running
+product leaves that range) are run token by token, which is exact.
+
 Normalisation enters as row scales: k_hat = rk * k, q_hat = rq * q.
 """
 import numpy as np
 
-SAFE_LOG2 = -100.0
+LO, HI = 2.0 ** -100, 2.0 ** 10
 
 
 def _l2scale(x, use, eps=1e-6):
@@ -46,13 +48,25 @@ def _l2scale(x, use, eps=1e-6):
     return 1.0 / np.sqrt((x * x).sum(-1) + eps)
 
 
-def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, blk, force_unsafe=False):
+def _sequential_chunk(qc, kc, vc, ac, bc, rq, rk, S, scale, L):
+    o = np.zeros((L, vc.shape[1]))
+    for r in range(L):
+        kh = rk[r] * kc[r]
+        qh = rq[r] * qc[r]
+        S = ac[r][:, None] * S
+        w = S.T @ kh
+        S = S + bc[r] * np.outer(kh, vc[r] - w)
+        o[r] = scale * (S.T @ qh)
+    return o, S
+
+
+def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, force_irregular=False,
+               paths=None):
     """One sequence, one head.  q,k,alpha [T,dk], v [T,dv], beta [T], S [dk,dv].
-    Returns (o [T,dv], S_final)."""
+    Returns (o [T,dv], S_final).  `paths`, if a list, receives 'ratio' or
+    'sequential' per chunk."""
     T, dk = q.shape
     dv = v.shape[1]
-    assert C % blk == 0
-    nb = C // blk
     o = np.zeros((T, dv))
     rq_all = _l2scale(q, use_l2norm)
     rk_all = _l2scale(k, use_l2norm)
@@ -67,67 +81,35 @@ def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, blk, force_unsafe=
         rq = np.ones(C); rq[:L] = rq_all[c0:c0 + L]
         rk = np.ones(C); rk[:L] = rk_all[c0:c0 + L]
 
-        F = np.empty((C, dk))
-        Bk = np.empty((C, dk))
-        G = np.empty((nb, dk))
-        safe = np.empty((nb, dk), dtype=bool)
-        for I in range(nb):
-            rows = slice(I * blk, (I + 1) * blk)
-            F[rows] = np.cumprod(ac[rows], axis=0)
-            # B_r: product of the rows after r inside the block
-            rev = np.cumprod(ac[rows][::-1], axis=0)[::-1]
-            Bk[rows][:-1] = rev[1:]
-            Bk[(I + 1) * blk - 1] = 1.0
-            G[I] = F[(I + 1) * blk - 1]
-            with np.errstate(divide="ignore"):
-                safe[I] = np.log2(np.abs(F[rows]).min(axis=0)) >= SAFE_LOG2
-        if force_unsafe:
-            safe[:] = False
-        Gpre = np.ones((nb, dk))
-        Gpost = np.ones((nb, dk))
-        for I in range(1, nb):
-            Gpre[I] = Gpre[I - 1] * G[I - 1]
-        for I in range(nb - 2, -1, -1):
-            Gpost[I] = Gpost[I + 1] * G[I + 1]
-        g = Gpre[nb - 1] * G[nb - 1]
-
-        def decay(r, j):   # D(r<-j) for j <= r, per channel
-            I, J = r // blk, j // blk
-            if I == J:
-                direct = np.prod(ac[j + 1:r + 1], axis=0)
-                with np.errstate(divide="ignore", invalid="ignore"):
-                    fact = F[r] / F[j]
-                return np.where(safe[I], fact, direct)
-            mid = np.ones(dk)
-            for M in range(J + 1, I):
-                mid = mid * G[M]
-            return F[r] * mid * Bk[j]
-
-        A = np.zeros((C, C))
-        P = np.zeros((C, C))
-        for r in range(C):
-            for j in range(r + 1):
-                d = decay(r, j)
-                P[r, j] = np.dot(qc[r] * d, kc[j])
-                if j < r:
-                    A[r, j] = bc[r] * rk[r] * rk[j] * np.dot(kc[r] * d, kc[j])
+        Ft = np.cumprod(ac, axis=0)
+        mag = np.abs(Ft)
+        regular = bool(np.all(np.isfinite(Ft)) and mag.min() >= LO and mag.max() <= HI)
+        if force_irregular or not regular:
+            oo, S = _sequential_chunk(qc, kc, vc, ac, bc, rq, rk, S, scale, L)
+            o[c0:c0 + L] = oo
+            if paths is not None:
+                paths.append("sequential")
+            continue
+        if paths is not None:
+            paths.append("ratio")
+        g = Ft[C - 1]
+        Lk = kc * Ft
+        Lq = qc * Ft
+        Rk = kc / Ft
+        A = np.tril((bc * rk)[:, None] * (Lk @ Rk.T) * rk[None, :], -1)
+        P = np.tril(Lq @ Rk.T)
         X = np.linalg.inv(np.eye(C) + A)
-        D0 = np.empty((C, dk))
-        DC = np.empty((C, dk))
-        for r in range(C):
-            D0[r] = Gpre[r // blk] * F[r]
-            DC[r] = Gpost[r // blk] * Bk[r]
-        W = X @ ((bc * rk)[:, None] * (kc * D0))
+        W = X @ ((bc * rk)[:, None] * Lk)
         Ubar = X @ (bc[:, None] * vc)
         U = Ubar - W @ S
-        Ok = (qc * D0) @ S + P @ (rk[:, None] * U)
+        Ok = Lq @ S + P @ (rk[:, None] * U)
         o[c0:c0 + L] = (scale * rq[:, None] * Ok)[:L]
-        S = g[:, None] * S + (kc * DC).T @ (rk[:, None] * U)
+        S = g[:, None] * S + (g * Rk).T @ (rk[:, None] * U)
     return o, S
 
 
 def fwd(q, k, v, alpha, beta, h0=None, seq_start=None, use_l2norm=True, scale=1.0,
-        C=64, blk=16, force_unsafe=False):
+        C=64, force_irregular=False, paths=None):
     """Same calling convention as oracle.fwd (dense [B,T,H,.] or packed)."""
     q, k, v, alpha, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, beta))
     out_shape = v.shape
@@ -150,7 +132,8 @@ def fwd(q, k, v, alpha, beta, h0=None, seq_start=None, use_l2norm=True, scale=1.
             S = np.zeros((dk, dv)) if h0 is None else np.array(h0[n, h], dtype=np.float64)
             if s1 > s0:
                 oo, S = chunk_head(q[s0:s1, h], k[s0:s1, h], v[s0:s1, h], alpha[s0:s1, h],
-                                   beta[s0:s1, h], S, use_l2norm, scale, C, blk, force_unsafe)
+                                   beta[s0:s1, h], S, use_l2norm, scale, C, force_irregular,
+                                   paths)
                 o[s0:s1, h] = oo
             ht[n, h] = S
     return o.reshape(out_shape), ht

