@@ -110,13 +110,18 @@ def bench_fwd(case, steps, warmup, gate):
     nseq = case.q.shape[0] if cu is None else len(case.cu_seqlens) - 1
     H, dk, dv = case.q.shape[2], case.q.shape[3], case.v.shape[3]
     ht = torch.empty((nseq, H, dk, dv), device="cuda:0", dtype=torch.float32)
+    B, T = (case.q.shape[0], case.q.shape[1]) if cu is None else (1, case.q.shape[0] * case.q.shape[1])
+    desc = ck.FwdDesc(B, T, H, dk, dv, nseq, case.chunk, ck.BF16 if dt == "bf16" else ck.F32,
+                      ck.GATE_CKDA if gate == "ckda" else ck.GATE_KDA, int(case.l2norm), 1.0)
+    ws = torch.empty(ck.chunk_fwd_workspace_size(desc, cu is not None), device="cuda:0",
+                     dtype=torch.uint8)
 
     def step():
         ck.chunk_fwd(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
-                     use_qk_l2norm=case.l2norm, gate=gate, out=o, final_state=ht)
+                     use_qk_l2norm=case.l2norm, gate=gate, out=o, final_state=ht, workspace=ws)
 
     ms, wall_ms = time_launches(step, steps, warmup)
-    del q, k, v, a, b, o, ht
+    del q, k, v, a, b, o, ht, ws
     torch.cuda.empty_cache()
     return ms, wall_ms
 

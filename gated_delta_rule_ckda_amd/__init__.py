@@ -56,7 +56,9 @@ def _load():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         lib.ckda_chunk_fwd.restype = i32
         lib.ckda_chunk_fwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp,
-                                       vp, vp, vp]
+                                       vp, vp, vp, ctypes.c_size_t, vp]
+        lib.ckda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+        lib.ckda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), i32]
         lib.ckda_fwd_supported.restype = i32
         lib.ckda_fwd_supported.argtypes = [ctypes.POINTER(FwdDesc)]
         lib.ckda_recurrent_step.restype = i32
@@ -131,11 +133,18 @@ def fwd_supported(chunk_size, dk, dv, dtype) -> bool:
     return bool(_load().ckda_fwd_supported(ctypes.byref(d)))
 
 
+def chunk_fwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
+    """Bytes of workspace ckda_chunk_fwd needs for `desc`."""
+    return int(_load().ckda_chunk_fwd_workspace_size(ctypes.byref(desc), int(bool(packed))))
+
+
 def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
               use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
-              out=None, final_state=None, stream=None):
+              out=None, final_state=None, workspace=None, stream=None):
     """Chunked prefill.  Dense: q,k,alpha [B,T,H,dk], v [B,T,H,dv], beta [B,T,H].
     Packed (cu_seqlens int32 [N+1]): leading [1,T,...] or [T,...].
+    `workspace`: optional uint8 device tensor of at least
+    chunk_fwd_workspace_size() bytes (allocated per call when omitted).
     Returns (o, ht) with ht [N,H,dk,dv] float32 (None if not requested)."""
     import torch
     lib = _load()
@@ -161,9 +170,14 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
     if output_final_state:
         ht = (torch.empty((desc.num_seqs, H, dk, dv), device=q.device, dtype=torch.float32)
               if final_state is None else final_state)
+    need = chunk_fwd_workspace_size(desc, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _require(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.numel() >= need,
+             "workspace must be a uint8 device tensor of at least %d bytes" % need)
     _check(lib.ckda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                               _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
-                              _stream(stream)))
+                              _ptr(workspace), workspace.numel(), _stream(stream)))
     return o, ht
 
 

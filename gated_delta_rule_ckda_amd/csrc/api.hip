@@ -74,10 +74,19 @@ int32_t ckda_fwd_supported(const ckda_fwd_desc_t* d) {
   return ckda::fwd_supported(d->chunk_size, d->dk, d->dv, d->io_dtype) ? 1 : 0;
 }
 
+size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* d, int32_t packed) {
+  if (!d || d->B <= 0 || d->T < 0 || d->H <= 0 || d->dk <= 0 || d->num_seqs < 0) return 0;
+  if (d->io_dtype != CKDA_DTYPE_BF16 && d->io_dtype != CKDA_DTYPE_F32) return 0;
+  if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64) return 0;
+  if (static_cast<int64_t>(d->B) * d->T == 0 || d->num_seqs == 0) return 0;
+  return ckda::fwd_workspace_bytes(d->B, d->T, d->H, d->dk, d->num_seqs, d->chunk_size,
+                                   d->io_dtype, packed != 0);
+}
+
 ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
                              const void* v, const float* alpha, const float* beta,
                              const int32_t* cu_seqlens, const float* h0, void* o,
-                             float* ht, void* stream) {
+                             float* ht, void* workspace, size_t workspace_bytes, void* stream) {
   if (!d) return fail(CKDA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->dk <= 0 || d->dv <= 0 || d->num_seqs < 0)
     return fail(CKDA_ERR_INVALID_ARGUMENT,
@@ -130,6 +139,20 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void
     if (h0 && h0 != ht && overlap(rh, ins[5]))
       return fail(CKDA_ERR_INVALID_ARGUMENT, "ht partially overlaps h0");
   }
+  const size_t need = ckda_chunk_fwd_workspace_size(d, cu_seqlens ? 1 : 0);
+  if (need > 0) {
+    if (!workspace)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed",
+                  workspace_bytes, need);
+    const Range rw = range("workspace", workspace, static_cast<int64_t>(need));
+    if (overlap(rw, ro)) return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace overlaps o");
+    for (const Range& r : ins)
+      if (overlap(rw, r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+  }
   if (!ckda::fwd_supported(d->chunk_size, d->dk, d->dv, d->io_dtype))
     return fail(CKDA_ERR_UNSUPPORTED, "no chunked kernel for chunk_size=%d dk=%d dv=%d io_dtype=%d",
                 d->chunk_size, d->dk, d->dv, d->io_dtype);
@@ -137,8 +160,9 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void
 
   ckda::FwdArgs a{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
                   d->use_qk_l2norm, d->gate_range, d->scale, q, k, v, alpha, beta,
-                  cu_seqlens, h0, o, ht};
-  return from_hip(ckda::launch_fwd(a, d->io_dtype, static_cast<hipStream_t>(stream)));
+                  cu_seqlens, h0, o, ht, nullptr, nullptr, nullptr, 0, 0, 0};
+  return from_hip(
+      ckda::launch_fwd(a, d->io_dtype, workspace, static_cast<hipStream_t>(stream)));
 }
 
 ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,

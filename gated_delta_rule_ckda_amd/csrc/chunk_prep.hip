@@ -1,0 +1,647 @@
+// Transform pass of the chunked forward: one workgroup per (chunk, head),
+// all chunks independent.  It computes the chunk's gate prefix, the in-op
+// L2 norms, the strictly lower matrix A and its unit-lower inverse
+// X = (I + A)^{-1}, and writes everything the sequential state pass needs as
+// one block of the workspace (layout in ckda_internal.h).
+//
+// Algebra (picx.dev summary of the Complex KDA paper, section "Background":
+// transition A_t = (I - beta_t k_t k_t^T) Diag(alpha_t), with the write
+// beta_t k_t v_t^T and the read-out o_t = S_t^T q_t).  Within a chunk of C
+// tokens entered with state S0, with the per-channel decay
+// D(r<-j) = prod_{j<s<=r} alpha_s:
+//
+//   (I + A) U = Diag(beta) (V - Kt S0),     A_rj = beta_r <k^_r . D(r<-j), k^_j>   (j < r)
+//   O  = scale (Qt S0 + P U),               P_rj = <q^_r . D(r<-j), k^_j>          (j <= r)
+//   S' = Diag(g) S0 + Kh^T U
+//
+// with Kt_r = D(r<-start) . k^_r, Qt_r = D(r<-start) . q^_r,
+// Kh_j = D(end<-j) . k^_j, g = D(end<-start).  Hence U = X' V - W S0 with
+// X' = X Diag(beta) and W = X Diag(beta) Kt, which is what the state pass runs.
+//
+// Gate prefix.  The running product Ft_r = prod_{s<=r} alpha_s (per channel,
+// fp32) carries sign and magnitude together: signs are exact under
+// multiplication and an exact zero gate makes every later product exactly
+// zero.  A chunk is "regular" when every |Ft_r| lies in [2^-100, 2^10]; then
+// D(r<-j) = Ft_r * (1 / Ft_j) with no factor able to overflow, and
+//   Lk = k . Ft (= Kt / rk),  Lq = q . Ft,  Rk = k / Ft,  Kh = rk g . Rk,
+//   A = tril(Diag(beta rk) Lk Rk^T Diag(rk), -1),  P = tril(Diag(rq) Lq Rk^T Diag(rk))
+// run on MFMA.  Other chunks (exact zero gates, products that underflow the
+// range, non-finite values) form A, P and Kh from direct products of the
+// gates instead: exact, slower, absent from realistic gate distributions.
+//
+// q and k enter raw; the in-op L2 normalisation (dormouse review "RoPE into
+// the KDA q/k path", section 2) is applied as the row scales rq, rk above.
+//
+// Phases (eight waves; wave w owns rows w*C/8 .. in the element-wise phases):
+//   1  loads, running products within the wave's rows, row norms
+//   2  chunk-level products Ft, regularity vote, operands Lk, Lq, Rk; Qt', g out
+//   3  A and P on MFMA (or the direct path); P' out
+//   4  Kt'^T to LDS, Kh'^T out; 16x16 diagonal blocks of X by forward substitution
+//   5  off-diagonal blocks X_IJ = -X_II sum_{J<=M<I} A_IM X_MJ on fp32 MFMA
+//   6  X' out, -W = -X Kt' on MFMA, out
+#include "mfma_ops.h"
+
+namespace ckda {
+namespace {
+
+constexpr float kRegularMin = 0x1p-100f;
+constexpr float kRegularMax = 0x1p+10f;
+
+template <class OpT, class IOT, int C_, int DK_>
+struct PrepCfg {
+  using Op = OpT;
+  using IO = IOT;
+  using T = typename Op::T;
+  static constexpr int NW = 8, NT = 64 * NW;
+  static constexpr int C = C_, DK = DK_;
+  static constexpr int NB = C / 16;
+  static constexpr int RPW = C / NW;                 // rows per wave, element-wise phases
+  static constexpr int CPT = DK >= 64 ? DK / 64 : 1; // channels per lane
+  static constexpr int NCG = DK / CPT;               // lanes holding channels
+  static constexpr int ES = static_cast<int>(sizeof(T));
+  static constexpr int IOES = static_cast<int>(sizeof(typename IO::storage));
+  static constexpr int PAD = 16 / ES;
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDC = C + PAD;
+  static constexpr int LDA = 20;                     // fp32 16x16 block stride (conflict-free)
+  static constexpr int BLKF = 16 * LDA;              // floats per 16x16 block
+  static constexpr int NBA = NB * (NB - 1) / 2;      // strictly lower blocks of A
+  static constexpr int NBX = NB * (NB + 1) / 2;      // lower blocks of X (with the diagonal)
+  static constexpr int QB = CPT * IOES;              // bytes of q (or k) per row and lane
+  static constexpr int QW = (QB + 3) / 4;
+  // direct path for irregular chunks: G threads per column, DG channels each
+  static constexpr int DG = (NT / C) < DK ? (NT / C) : DK;
+  static constexpr int DCH = DK / DG;
+
+  // byte offsets
+  static constexpr int O_LQ = 0;                                        // Lq [C][LDK] | Xb [C][LDC]
+  static constexpr int SZ_LQ = align16(cmax(C * LDK, C * LDC) * ES);
+  static constexpr int O_LK = O_LQ + SZ_LQ;                             // Lk [C][LDK] | Kt'^T [DK][LDC]
+  static constexpr int O_RK = O_LK + C * LDK * ES;                      // Rk [C][LDK]
+  static constexpr int O_TS = O_LK + align16(DK * LDC * ES);            // level scratch (after Rk dies)
+  static constexpr int SZ_R = align16(cmax(2 * C * LDK * ES, DK * LDC * ES + NB * BLKF * 4));
+  static constexpr int O_A = O_LK + SZ_R;                               // A blocks (I > J), fp32
+  static constexpr int O_XF = O_A + (NBA > 0 ? NBA : 1) * BLKF * 4;     // X blocks (I >= J), fp32
+  static constexpr int O_G = O_XF + NBX * BLKF * 4;                     // wave-row products [NW][DK]
+  static constexpr int O_RQ = O_G + NW * DK * 4;                        // rq [C]
+  static constexpr int O_RK2 = O_RQ + C * 4;                            // rk [C]
+  static constexpr int O_BETA = O_RK2 + C * 4;                          // beta [C]
+  static constexpr int O_FLAG = O_BETA + C * 4;                         // regularity votes [NW]
+  static constexpr int LDS_BYTES = align16(O_FLAG + NW * 4);
+
+  static_assert(C % 16 == 0 && DK % 16 == 0 && C <= 64 && DK <= 128, "tile sizes");
+  static_assert(NB <= NW && RPW >= 2 && (RPW & (RPW - 1)) == 0 && RPW <= 8, "row split");
+  static_assert(DG * C <= NT && DK % DG == 0 && (DG & (DG - 1)) == 0 && DG <= 64, "direct path");
+  static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+};
+
+template <class Cfg>
+__device__ __forceinline__ float* a_blk(unsigned char* smem, int I, int M) {
+  return reinterpret_cast<float*>(smem + Cfg::O_A) + (I * (I - 1) / 2 + M) * Cfg::BLKF;
+}
+template <class Cfg>
+__device__ __forceinline__ float* x_blk(unsigned char* smem, int I, int J) {
+  return reinterpret_cast<float*>(smem + Cfg::O_XF) + (I * (I + 1) / 2 + J) * Cfg::BLKF;
+}
+
+// I, J of the idx-th lower block (J <= I) in row order
+__device__ __forceinline__ void lower_block(int idx, int& I, int& J) {
+  I = 0;
+  while (idx > I) {
+    idx -= I + 1;
+    ++I;
+  }
+  J = idx;
+}
+
+// Direct products for a chunk that is not regular: column j of A and P from
+// D(r<-j) built one gate at a time (G threads per column, DCH channels each).
+// Row r of the chunk starts at element base + r * rowstride of q, k, alpha.
+template <class Cfg>
+__device__ __noinline__ void direct_ap(const void* gq, const void* gk, const float* galpha,
+                                       int64_t base, int rowstride, int L, float scale,
+                                       typename Cfg::T* gP, unsigned char* smem, int tid) {
+  using IO = typename Cfg::IO;
+  using ST = typename IO::storage;
+  using Op = typename Cfg::Op;
+  constexpr int C = Cfg::C, DG = Cfg::DG, DCH = Cfg::DCH, LDA = Cfg::LDA;
+  const float* srq = reinterpret_cast<const float*>(smem + Cfg::O_RQ);
+  const float* srk = reinterpret_cast<const float*>(smem + Cfg::O_RK2);
+  const float* sbeta = reinterpret_cast<const float*>(smem + Cfg::O_BETA);
+  const ST* q = static_cast<const ST*>(gq);
+  const ST* k = static_cast<const ST*>(gk);
+  if (tid >= DG * C) return;
+  const int j = tid / DG, cg = tid % DG, c0 = cg * DCH;
+  const int J = j / 16;
+  float d[DCH], kj[DCH];
+#pragma unroll
+  for (int e = 0; e < DCH; ++e) {
+    d[e] = 1.f;
+    kj[e] = (j < L) ? IO::load(k, base + static_cast<int64_t>(j) * rowstride + c0 + e) : 0.f;
+  }
+  const float rkj = srk[j];
+  for (int r = 0; r < C; ++r) {
+    float pa = 0.f, pp = 0.f;
+    if (j < L && r >= j && r < L) {
+#pragma unroll
+      for (int e = 0; e < DCH; ++e) {
+        const int64_t off = base + static_cast<int64_t>(r) * rowstride + c0 + e;
+        if (r > j) d[e] *= galpha[off];
+        const float w = d[e] * kj[e];
+        pa += IO::load(k, off) * w;
+        pp += IO::load(q, off) * w;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < DG; m <<= 1) {
+      pa += __shfl_xor(pa, m, 64);
+      pp += __shfl_xor(pp, m, 64);
+    }
+    if (cg == 0) {
+      const int I = r / 16;
+      const float av = (r > j) ? pa * sbeta[r] * srk[r] * rkj : 0.f;
+      if (I > J)
+        a_blk<Cfg>(smem, I, J)[(r % 16) * LDA + j % 16] = av;
+      else if (I == J)
+        x_blk<Cfg>(smem, I, I)[(r % 16) * LDA + j % 16] = av;
+      gP[r * C + j] = Op::cvt((r >= j) ? pp * scale * srq[r] * rkj : 0.f);
+    }
+  }
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(FwdArgs a) {
+  using Op = typename Cfg::Op;
+  using IO = typename Cfg::IO;
+  using T = typename Cfg::T;
+  constexpr int C = Cfg::C, DK = Cfg::DK, NB = Cfg::NB, NW = Cfg::NW, NT = Cfg::NT;
+  constexpr int RPW = Cfg::RPW, CPT = Cfg::CPT, NCG = Cfg::NCG, ES = Cfg::IOES;
+  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, LDA = Cfg::LDA;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sLq = reinterpret_cast<T*>(smem + Cfg::O_LQ);
+  T* sXb = reinterpret_cast<T*>(smem + Cfg::O_LQ);
+  T* sLk = reinterpret_cast<T*>(smem + Cfg::O_LK);
+  T* sRk = reinterpret_cast<T*>(smem + Cfg::O_RK);
+  T* sKtT = reinterpret_cast<T*>(smem + Cfg::O_LK);
+  float* sTS = reinterpret_cast<float*>(smem + Cfg::O_TS);
+  float* sG = reinterpret_cast<float*>(smem + Cfg::O_G);
+  float* srq = reinterpret_cast<float*>(smem + Cfg::O_RQ);
+  float* srk = reinterpret_cast<float*>(smem + Cfg::O_RK2);
+  float* sbeta = reinterpret_cast<float*>(smem + Cfg::O_BETA);
+  int* sFlag = reinterpret_cast<int*>(smem + Cfg::O_FLAG);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int H = a.H;
+
+  // ---- which chunk: blocks of one chunk and consecutive heads are adjacent
+  const int c = static_cast<int>(blockIdx.x / H);
+  const int h = static_cast<int>(blockIdx.x % H);
+  int64_t t0;
+  int L;
+  if (a.cu_seqlens) {
+    const int n = uniform32(a.chunk_seq[c]);
+    if (n < 0) return;  // unused chunk slot
+    const int i = c - uniform32(a.first[n]);
+    const int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
+    t0 = uniform64(s0 + static_cast<int64_t>(i) * C);
+    L = uniform32(static_cast<int>((s1 - t0) < C ? (s1 - t0) : C));
+  } else {
+    const int n = c / a.nc, i = c % a.nc;
+    t0 = static_cast<int64_t>(n) * a.T + static_cast<int64_t>(i) * C;
+    L = (a.T - i * C) < C ? (a.T - i * C) : C;
+  }
+  T* blk = reinterpret_cast<T*>(a.blocks + (static_cast<int64_t>(h) * a.maxc + c) * a.blk_bytes);
+  T* gX = blk;
+  T* gW = blk + blk_off_W(C, DK);
+  T* gQ = blk + blk_off_Q(C, DK);
+  T* gP = blk + blk_off_P(C, DK);
+  T* gK = blk + blk_off_K(C, DK);
+  float* gg = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(blk) + blk_g_byte(C, DK, sizeof(T)));
+
+  const bool use_l2 = a.use_l2norm != 0;
+  const bool scan_on = lane < NCG;
+  const int c0ch = lane * CPT;
+  const int r0 = wave * RPW;
+
+  // ================= 1: loads, running products, norms ======================
+  float xq[RPW][CPT], xk[RPW][CPT], F[RPW][CPT];
+  {
+    const int krow = H * DK * ES, arow = H * DK * 4;
+    const int64_t qk_off = (t0 * H + h) * static_cast<int64_t>(DK);
+    uint32_t rqv[RPW][Cfg::QW], rkv[RPW][Cfg::QW], rav[RPW][CPT];
+    if (scan_on) {
+      const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + qk_off * ES, L * krow);
+      const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + qk_off * ES, L * krow);
+      const rsrc_t ra = make_rsrc(a.alpha + qk_off, L * arow);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int row = iclamp(r0 + i, L - 1);
+        ldraw<Cfg::QB>(rq, c0ch * ES + row * krow, rqv[i]);
+        ldraw<Cfg::QB>(rk, c0ch * ES + row * krow, rkv[i]);
+        ldraw<CPT * 4>(ra, c0ch * 4 + row * arow, rav[i]);
+      }
+    }
+    if (tid < C) sbeta[tid] = (tid < L) ? a.beta[(t0 + tid) * H + h] : 0.f;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const bool in = scan_on && (r0 + i < L);
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        xq[i][cc] = in ? dec<IO>(rqv[i], cc) : 0.f;
+        xk[i][cc] = in ? dec<IO>(rkv[i], cc) : 0.f;
+        F[i][cc] = in ? __uint_as_float(rav[i][cc]) : 1.f;
+      }
+    }
+  }
+  // running products over this wave's rows; their totals go to sG
+#pragma unroll
+  for (int cc = 0; cc < CPT; ++cc) {
+    float f = 1.f;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      f *= F[i][cc];
+      F[i][cc] = f;
+    }
+    if (scan_on) sG[wave * DK + c0ch + cc] = f;
+  }
+  {
+    float pq[RPW], pk[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      pq[i] = 0.f;
+      pk[i] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        pq[i] += xq[i][cc] * xq[i][cc];
+        pk[i] += xk[i][cc] * xk[i][cc];
+      }
+    }
+    const float sq = wave_row_sums<RPW>(pq, lane);
+    const float sk = wave_row_sums<RPW>(pk, lane);
+    constexpr int LPR = 64 / RPW;
+    if ((lane & (LPR - 1)) == 0) {
+      const int row = r0 + lane / LPR;
+      srq[row] = use_l2 ? __fdiv_rn(1.f, __fsqrt_rn(sq + kL2Eps)) : 1.f;
+      srk[row] = use_l2 ? __fdiv_rn(1.f, __fsqrt_rn(sk + kL2Eps)) : 1.f;
+    }
+  }
+  __syncthreads();  // B1
+
+  // ================= 2: chunk products, regularity, operands =================
+  float kt[RPW][CPT], kh[RPW][CPT], gch[CPT], gsuf[CPT];
+  {
+    bool ok = true;
+    float rqs[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) rqs[i] = a.scale * srq[r0 + i];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      float gpre = 1.f, g = 1.f, gs = 1.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float gw = scan_on ? sG[w * DK + c0ch + cc] : 1.f;
+        if (w < wave) gpre *= gw;
+        if (w > wave) gs *= gw;
+        g *= gw;
+      }
+      gch[cc] = g;
+      gsuf[cc] = gs;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const float ft = gpre * F[i][cc];
+        const float mag = fabsf(ft);
+        ok = ok && (!scan_on || ((mag >= kRegularMin) && (mag <= kRegularMax)));
+        const float rinv = __builtin_amdgcn_rcpf(ft);
+        kt[i][cc] = xk[i][cc] * ft;    // Lk
+        xq[i][cc] = xq[i][cc] * ft;    // Lq
+        xk[i][cc] = xk[i][cc] * rinv;  // Rk
+        kh[i][cc] = xk[i][cc] * g;     // Kh / rk (regular chunks)
+      }
+    }
+    if (scan_on) {
+      if (wave == 0) {
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) gg[c0ch + cc] = gch[cc];
+      }
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int r = r0 + i;
+        float qv[CPT];
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) qv[cc] = xq[i][cc] * rqs[i];
+        store_run<Op, CPT>(gQ + r * DK + c0ch, qv);
+        store_run<Op, CPT>(sLk + r * LDK + c0ch, kt[i]);
+        store_run<Op, CPT>(sLq + r * LDK + c0ch, xq[i]);
+        store_run<Op, CPT>(sRk + r * LDK + c0ch, xk[i]);
+      }
+    }
+    const bool wave_ok = __all(ok);
+    if (lane == 0) sFlag[wave] = wave_ok ? 1 : 0;
+  }
+  __syncthreads();  // B2
+  int votes = 1;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) votes &= sFlag[w];
+  const bool regular = uniform32(votes) != 0;
+
+  // ================= 3: A and P ================================================
+  if (regular) {
+    constexpr int NPT = NB * (NB + 1) / 2;  // lower blocks per matrix
+    constexpr int NZ = NB * (NB - 1) / 2;   // zero blocks of P above the diagonal
+    constexpr int NTILE = 2 * NPT + NZ;
+    constexpr int NU = (NTILE + NW - 1) / NW;
+#pragma unroll 1
+    for (int u = 0; u < NU; ++u) {
+      const int tt = wave + NW * u;
+      if (tt < NPT) {
+        int I, J;
+        lower_block(tt, I, J);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        Op::template mmaK<DK>(acc, sLk + 16 * I * LDK, LDK, sRk + 16 * J * LDK, LDK, lane);
+        // rows r = 16I + 4lq + i, column j = 16J + l16
+        const int j = 16 * J + l16;
+        const float sj = srk[j];
+        float* dst = (I == J) ? x_blk<Cfg>(smem, I, I) : a_blk<Cfg>(smem, I, J);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * I + 4 * lq + i;
+          const float v = acc[i] * sbeta[r] * srk[r] * sj;
+          dst[(4 * lq + i) * LDA + l16] = (I == J && j >= r) ? 0.f : v;
+        }
+      } else if (tt < 2 * NPT) {
+        int I, J;
+        lower_block(tt - NPT, I, J);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        Op::template mmaK<DK>(acc, sRk + 16 * J * LDK, LDK, sLq + 16 * I * LDK, LDK, lane);
+        // rows j = 16J + 4lq + i, column r = 16I + l16: P[r][j]
+        const int r = 16 * I + l16;
+        const float sr = a.scale * srq[r];
+        f32x4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * J + 4 * lq + i;
+          out[i] = (I == J && j > r) ? 0.f : acc[i] * sr * srk[j];
+        }
+        Op::store4(gP + r * C + 16 * J + 4 * lq, out);
+      } else if (tt < NTILE) {
+        int I, J;
+        lower_block(tt - 2 * NPT, J, I);  // J > I: a block above the diagonal
+        J += 1;
+        Op::store4(gP + (16 * I + l16) * C + 16 * J + 4 * lq, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    }
+  } else {
+    direct_ap<Cfg>(a.q, a.k, a.alpha, (t0 * H + h) * static_cast<int64_t>(DK), H * DK, L,
+                   a.scale, gP, smem, tid);
+    // Kh from suffix products of the gates (no division)
+    if (scan_on) {
+      const int64_t qk_off = (t0 * H + h) * static_cast<int64_t>(DK);
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        float suf = gsuf[cc];
+#pragma unroll
+        for (int i = RPW - 1; i >= 0; --i) {
+          const int r = r0 + i;
+          // kh = k * prod_{s>r} alpha_s ; xk was overwritten by Rk, so reload k
+          const float kr = (r < L) ? IO::load(static_cast<const typename IO::storage*>(a.k),
+                                              qk_off + static_cast<int64_t>(r) * H * DK + c0ch + cc)
+                                   : 0.f;
+          kh[i][cc] = kr * suf;
+          if (r < L) suf *= a.alpha[qk_off + static_cast<int64_t>(r) * H * DK + c0ch + cc];
+        }
+      }
+    }
+  }
+  __syncthreads();  // B3
+
+  // ================= 4: Kt'^T, Kh'^T; diagonal blocks of X ======================
+  if (scan_on) {
+    float wsc[RPW], rks[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      rks[i] = srk[r0 + i];
+      wsc[i] = sbeta[r0 + i] * rks[i];
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      float ktv[RPW], khv[RPW];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        ktv[i] = kt[i][cc] * wsc[i];
+        khv[i] = kh[i][cc] * rks[i];
+      }
+      store_run<Op, RPW>(sKtT + (c0ch + cc) * LDC + r0, ktv);
+      store_run<Op, RPW>(gK + (c0ch + cc) * C + r0, khv);
+    }
+  }
+  if (wave < NB && lane < 16) {
+    // forward substitution for column j of the diagonal block (I, I):
+    // x_i = delta_ij - sum_{m<i} A(i, m) x_m.  Every lane reads the same row
+    // of A (a broadcast); X overwrites A only after the last read.
+    const int j = lane;
+    float* blkI = x_blk<Cfg>(smem, wave, wave);
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int g = 0; 4 * g < i; ++g) {
+        const f32x4 ar = *reinterpret_cast<const f32x4*>(blkI + i * LDA + 4 * g);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+          if (4 * g + mm < i) acc -= ar[mm] * x[4 * g + mm];
+      }
+      x[i] = acc;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) blkI[i * LDA + j] = x[i];
+  }
+  __syncthreads();  // B4
+
+  // ================= 5: off-diagonal blocks of X ===============================
+  for (int d = 1; d < NB; ++d) {
+    for (int J = wave; J + d < NB; J += NW) {
+      const int I = J + d;
+      f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+      for (int M = J; M < I; ++M) {
+        const float* am = a_blk<Cfg>(smem, I, M);
+        const float* xm = x_blk<Cfg>(smem, M, J);
+        float av[4], xv[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          av[kk] = am[l16 * LDA + 4 * kk + lq];
+          xv[kk] = xm[(4 * kk + lq) * LDA + l16];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) tacc = mfma_f32(av[kk], xv[kk], tacc);
+      }
+      float* ts = sTS + wave * Cfg::BLKF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ts[(4 * lq + i) * LDA + l16] = tacc[i];
+      wave_lds_sync();
+      const float* xi = x_blk<Cfg>(smem, I, I);
+      float xa[4], tb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        xa[kk] = xi[l16 * LDA + 4 * kk + lq];
+        tb[kk] = ts[(4 * kk + lq) * LDA + l16];
+      }
+      f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) xacc = mfma_f32(xa[kk], tb[kk], xacc);
+      float* xo = x_blk<Cfg>(smem, I, J);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xo[(4 * lq + i) * LDA + l16] = -xacc[i];
+    }
+    __syncthreads();
+  }
+
+  // ================= 6: X' out, X operand copy, -W out ==========================
+  {
+    // 4-element groups of the full C x C matrix (zeros above the block diagonal)
+    constexpr int NQ = C * C / 4;
+    for (int e = tid; e < NQ; e += NT) {
+      const int r = e / (C / 4), j = 4 * (e % (C / 4));
+      const int I = r / 16, J = j / 16;
+      f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+      if (J <= I) xv = *reinterpret_cast<const f32x4*>(x_blk<Cfg>(smem, I, J) + (r % 16) * LDA + j % 16);
+      Op::store4(sXb + r * LDC + j, xv);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(sbeta + j);
+      Op::store4(gX + r * C + j, xv * bv);
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int NWT = (DK / 16) * (C / 16);
+    constexpr int NU = (NWT + NW - 1) / NW;
+#pragma unroll 1
+    for (int u = 0; u < NU; ++u) {
+      const int tt = wave + NW * u;
+      if (tt < NWT) {
+        const int mc = tt / (C / 16), nr = tt % (C / 16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        Op::template mmaK<C>(acc, sKtT + 16 * mc * LDC, LDC, sXb + 16 * nr * LDC, LDC, lane);
+        // rows c = 16mc + 4lq + i, column r = 16nr + l16: W[r][c]
+        Op::store4(gW + (16 * nr + l16) * DK + 16 * mc + 4 * lq, -acc);
+      }
+    }
+  }
+}
+
+// Chunk map of a packed batch: first[n] = sum over m < n of ceil(len_m / C),
+// first[N] = the chunk count, chunk_seq[c] = the sequence owning chunk c (or
+// -1 for c >= first[N]).  One workgroup; a block-wide scan per 1024 sequences.
+__global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* cu, int32_t N, int32_t C,
+                                                         int32_t maxc, int32_t* first,
+                                                         int32_t* chunk_seq) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int n = base + tid;
+    int cnt = 0;
+    if (n < N) {
+      const int len = cu[n + 1] - cu[n];
+      cnt = len > 0 ? (len + C - 1) / C : 0;
+    }
+    part[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int add = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    const int carry = carry_s;
+    if (n < N) first[n] = carry + part[tid] - cnt;
+    __syncthreads();
+    if (tid == 1023) carry_s = carry + part[1023];
+    __syncthreads();
+  }
+  if (tid == 0) first[N] = carry_s;
+  __syncthreads();  // first[] complete and visible to the workgroup
+  const int total = carry_s;
+  for (int c = tid; c < maxc; c += 1024) {
+    int owner = -1;
+    if (c < total) {
+      int lo = 0, hi = N - 1;  // last n with first[n] <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      owner = lo;
+    }
+    chunk_seq[c] = owner;
+  }
+}
+
+template <class Cfg>
+launch_result launch_cfg(const FwdArgs& a, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&prep_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = static_cast<int64_t>(a.maxc) * a.H;
+  hipLaunchKernelGGL(prep_kernel<Cfg>, dim3(static_cast<unsigned>(blocks)), dim3(Cfg::NT),
+                     Cfg::LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
+struct Entry {
+  int chunk, dk, dtype;
+  launch_result (*fn)(const FwdArgs&, hipStream_t);
+};
+
+template <class Op, class IO, int C, int D>
+constexpr Entry entry(int dtype) {
+  return Entry{C, D, dtype, &launch_cfg<PrepCfg<Op, IO, C, D>>};
+}
+
+const Entry kEntries[] = {
+    entry<OpBF16, io_bf16, 64, 128>(CKDA_DTYPE_BF16),
+    entry<OpBF16, io_bf16, 32, 128>(CKDA_DTYPE_BF16),
+    entry<OpBF16, io_bf16, 16, 128>(CKDA_DTYPE_BF16),
+    entry<OpBF16, io_bf16, 64, 64>(CKDA_DTYPE_BF16),
+    entry<OpBF16, io_bf16, 32, 64>(CKDA_DTYPE_BF16),
+    entry<OpBF16, io_bf16, 16, 64>(CKDA_DTYPE_BF16),
+    entry<OpF32, io_f32, 16, 16>(CKDA_DTYPE_F32),
+    entry<OpF32, io_f32, 32, 16>(CKDA_DTYPE_F32),
+    entry<OpF32, io_f32, 64, 16>(CKDA_DTYPE_F32),
+    entry<OpF32, io_f32, 16, 32>(CKDA_DTYPE_F32),
+    entry<OpF32, io_f32, 32, 32>(CKDA_DTYPE_F32),
+    entry<OpF32, io_f32, 64, 32>(CKDA_DTYPE_F32),
+    entry<OpF32, io_f32, 16, 64>(CKDA_DTYPE_F32),
+    entry<OpF32, io_f32, 32, 64>(CKDA_DTYPE_F32),
+};
+
+const Entry* find(int32_t chunk, int32_t dk, int32_t dtype) {
+  for (const Entry& e : kEntries)
+    if (e.chunk == chunk && e.dk == dk && e.dtype == dtype) return &e;
+  return nullptr;
+}
+
+}  // namespace
+
+bool prep_supported(int32_t chunk, int32_t dk, int32_t io_dtype) {
+  return find(chunk, dk, io_dtype) != nullptr;
+}
+
+launch_result launch_prep(const FwdArgs& a, int32_t io_dtype, hipStream_t stream) {
+  const Entry* e = find(a.chunk, a.dk, io_dtype);
+  if (!e) return hipErrorInvalidValue;
+  if (static_cast<int64_t>(a.maxc) * a.H == 0) return hipSuccess;
+  return e->fn(a, stream);
+}
+
+launch_result launch_chunk_map(const FwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.num_seqs,
+                     a.chunk, a.maxc, a.first, a.chunk_seq);
+  return hipGetLastError();
+}
+
+}  // namespace ckda

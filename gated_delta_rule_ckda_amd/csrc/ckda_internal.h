@@ -37,7 +37,30 @@ launch_result launch_step(const StepArgs& a, int32_t io_dtype, hipStream_t strea
 launch_result launch_l2norm_debug(const void* x, float* y, int64_t rows,
                                   int32_t d, int32_t dtype, hipStream_t stream);
 
-// Chunked forward.
+// Chunked forward: two passes over a workspace.  The transform pass runs one
+// workgroup per (chunk, head) and writes that chunk's operands as one block;
+// the state pass walks each (sequence, head) chain over its chunks' blocks.
+//
+// Block layout (elements of the handoff type: bf16 for bf16 io, f32 for f32
+// io; C = chunk size):
+//   X'   [C][C]   X Diag(beta),  X = (I + A)^{-1}
+//   -W   [C][dk]  -X Diag(beta) Kt
+//   Qt'  [C][dk]  scale rq . Qt
+//   P'   [C][C]   scale Diag(rq) P Diag(rk)   (zero above the diagonal)
+//   Kh'^T [dk][C] (Diag(rk) Kh)^T
+//   g    [dk]     float32, the chunk's total gate product
+// Blocks are 256-byte aligned; block (h, c) starts at (h * maxc + c) * blk_bytes.
+__host__ __device__ constexpr int64_t blk_off_W(int C, int dk) { return int64_t(C) * C + 0 * dk; }
+__host__ __device__ constexpr int64_t blk_off_Q(int C, int dk) { return int64_t(C) * C + int64_t(C) * dk; }
+__host__ __device__ constexpr int64_t blk_off_P(int C, int dk) { return int64_t(C) * C + 2 * int64_t(C) * dk; }
+__host__ __device__ constexpr int64_t blk_off_K(int C, int dk) { return 2 * int64_t(C) * C + 2 * int64_t(C) * dk; }
+__host__ __device__ constexpr int64_t blk_g_byte(int C, int dk, int es) {
+  return (2 * int64_t(C) * C + 3 * int64_t(C) * dk) * es;
+}
+__host__ __device__ constexpr int64_t blk_bytes(int C, int dk, int es) {
+  return (blk_g_byte(C, dk, es) + 4 * int64_t(dk) + 255) & ~int64_t(255);
+}
+
 struct FwdArgs {
   int32_t B, T, H, dk, dv, num_seqs, chunk;
   int32_t use_l2norm;
@@ -52,9 +75,26 @@ struct FwdArgs {
   const float* h0;
   void* o;
   float* ht;
+  // workspace, laid out by the launcher
+  unsigned char* blocks;  // [H][maxc] blocks of blk_bytes
+  int32_t* first;         // [num_seqs + 1] first chunk of each sequence (packed batches)
+  int32_t* chunk_seq;     // [maxc] sequence owning each chunk slot, -1 if unused (packed)
+  int32_t maxc;           // chunk slots per head
+  int32_t nc;             // chunks per sequence (dense batches)
+  int64_t blk_bytes;
 };
 bool fwd_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype);
-launch_result launch_fwd(const FwdArgs& a, int32_t io_dtype, hipStream_t stream);
+// Workspace bytes ckda_chunk_fwd needs for these sizes (0 for an empty call).
+size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t num_seqs,
+                           int32_t chunk, int32_t io_dtype, bool packed);
+// Lays out the workspace in `a` and enqueues both passes.
+launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream);
+// The passes (one translation unit each).
+bool prep_supported(int32_t chunk, int32_t dk, int32_t io_dtype);
+launch_result launch_prep(const FwdArgs& a, int32_t io_dtype, hipStream_t stream);
+launch_result launch_chunk_map(const FwdArgs& a, hipStream_t stream);
+bool state_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype);
+launch_result launch_state(const FwdArgs& a, int32_t io_dtype, hipStream_t stream);
 
 // ---- small device helpers shared by the kernels --------------------------
 

@@ -26,8 +26,9 @@
  *
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
- *    never allocates, frees or keeps device memory, and keeps no global
- *    mutable state apart from a thread-local error message.
+ *    never allocates, frees or keeps device memory (scratch space comes in
+ *    as a caller-owned workspace argument), and keeps no global mutable
+ *    state apart from a thread-local error message.
  *  - Layouts are row-major and contiguous (last index fastest).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *    default stream).  The library never synchronises the host and never
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 1
+#define CKDA_ABI_VERSION 2
 
 typedef enum {
   CKDA_OK = 0,
@@ -90,10 +91,32 @@ typedef struct {
 } ckda_fwd_desc_t;
 
 /*
+ * Bytes of device workspace ckda_chunk_fwd needs for this descriptor; 0 for
+ * an invalid descriptor or an empty call.  `packed` is 1 when the call will
+ * pass cu_seqlens (a packed batch), else 0.  The size depends only on the
+ * sizes, never on data: one block of chunk operands per (head, chunk), with
+ * at most ceil(T / chunk_size) * B chunks for a dense batch and
+ * ceil(T / chunk_size) + num_seqs for a packed one, plus the chunk map of a
+ * packed batch.  At B=8, T=4096, H=16, dk=128, chunk 64, bf16: 516 MiB.
+ */
+size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed);
+
+/*
  * Chunked prefill.  Computes o for every token and, if ht != NULL, the final
  * state of every sequence.  h0 == NULL means a zero initial state.  h0 and ht
  * may be the same buffer (the state is read before it is written).  o must not
- * overlap any input.  Supported shapes (others return CKDA_ERR_UNSUPPORTED):
+ * overlap any input.
+ *
+ * Two passes run on `stream`: a transform pass over all chunks in parallel
+ * (gate prefix, norms, the chunk's UT/WY transform), which writes each chunk's
+ * operands into `workspace`, then a state pass that walks every
+ * (sequence, head) over its chunks.  `workspace` is a device buffer of at
+ * least ckda_chunk_fwd_workspace_size(desc, cu_seqlens != NULL) bytes,
+ * 256-byte aligned, owned by the caller, not overlapping any argument; its
+ * contents are scratch (undefined before and after the call).  Calls that
+ * share a workspace must be ordered on one stream.
+ *
+ * Supported shapes (others return CKDA_ERR_UNSUPPORTED):
  *   bf16 : dk = dv = 128 with chunk_size 16, 32 or 64; dk = dv = 64 with 16, 32, 64
  *   f32  : dk = dv in {16, 32, 64} with chunk_size 16 or 32 (<= 64 for dk <= 32)
  * ckda_fwd_supported() reports whether a descriptor has a kernel.
@@ -101,7 +124,8 @@ typedef struct {
 ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
                              const void* k, const void* v, const float* alpha,
                              const float* beta, const int32_t* cu_seqlens,
-                             const float* h0, void* o, float* ht, void* stream);
+                             const float* h0, void* o, float* ht,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* 1 if ckda_chunk_fwd has a kernel for this descriptor's (chunk_size, dk, dv,
  * io_dtype), 0 if not (other fields are not inspected). */

@@ -42,7 +42,8 @@ def test_status_strings():
 # Fake, 16-byte aligned, never-dereferenced device addresses.
 BASE = 0x7F0000000000
 P = {n: ctypes.c_void_p(BASE + i * (1 << 32)) for i, n in
-     enumerate(["q", "k", "v", "alpha", "beta", "cu", "h0", "o", "ht"])}
+     enumerate(["q", "k", "v", "alpha", "beta", "cu", "h0", "o", "ht", "ws"])}
+WS_BYTES = 1 << 31
 
 
 def _desc(**kw):
@@ -58,7 +59,7 @@ def _fwd(desc, **over):
     lib = ck._load()
     st = lib.ckda_chunk_fwd(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"],
                             p["v"], p["alpha"], p["beta"], p.get("cu_seqlens"), p["h0"], p["o"],
-                            p["ht"], None)
+                            p["ht"], p["ws"], p.get("ws_bytes", WS_BYTES), None)
     return st, lib.ckda_last_error().decode()
 
 
@@ -90,6 +91,33 @@ def test_fwd_cu_seqlens_needs_batch_one():
     assert st == 1 and "cu_seqlens" in msg
     st, msg = _fwd(_desc(B=1, num_seqs=3), cu_seqlens=ctypes.c_void_p(BASE + 5 * (1 << 32) + 2))
     assert st == 1 and "aligned" in msg
+
+
+def test_workspace_size_formula():
+    """One block per (head, chunk): (2C^2 + 3C dk) elements + dk floats, rounded up to
+    256 bytes; dense batches have B*ceil(T/C) chunks, packed ones ceil(T/C) + N slots
+    plus the chunk map."""
+    d = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8)
+    blk = (2 * 64 * 64 + 3 * 64 * 128) * 2 + 128 * 4
+    assert blk % 256 == 0
+    assert ck.chunk_fwd_workspace_size(d, False) == 16 * 8 * 64 * blk
+    d = _desc(B=1, T=70, H=3, dk=32, dv=32, num_seqs=4, chunk_size=16, io_dtype=ck.F32)
+    blk = -(-((2 * 16 * 16 + 3 * 16 * 32) * 4 + 32 * 4) // 256) * 256
+    maxc = -(-70 // 16) + 4
+    assert ck.chunk_fwd_workspace_size(d, True) == -(-(4 * (4 + 1 + maxc)) // 256) * 256 + 3 * maxc * blk
+    assert ck.chunk_fwd_workspace_size(_desc(T=0), False) == 0
+    assert ck.chunk_fwd_workspace_size(_desc(chunk_size=48), False) == 0
+
+
+def test_fwd_workspace_validation():
+    st, msg = _fwd(_desc(), ws=None)
+    assert st == 1 and "workspace is NULL" in msg
+    st, msg = _fwd(_desc(), ws_bytes=1024)
+    assert st == 1 and "needed" in msg
+    st, msg = _fwd(_desc(), ws=ctypes.c_void_p(P["ws"].value + 128))
+    assert st == 1 and "256-byte" in msg
+    st, msg = _fwd(_desc(), ws=P["v"])
+    assert st == 1 and "workspace overlaps v" in msg
 
 
 def test_fwd_unsupported_shape():
