@@ -54,11 +54,8 @@ struct StateCfg {
   static constexpr int GB_K = GB_P + C * C * ES;
   static constexpr int GB_G = GB_K + DK * C * ES;
   static constexpr int GB_END = GB_G + DK * 4;
-  static constexpr int EP = 16 / ES;                 // elements per 16-byte piece
-  static constexpr int NPB = GB_END / 16;            // pieces of a block
-  static constexpr int VPR = DVT * IOES / 16;        // pieces per V row of the tile
+  static constexpr int VPR = DVT * IOES / 16;        // 16-byte pieces per V row of the tile
   static constexpr int NPV = C * VPR;                // pieces of the V tile
-  static constexpr int NPT = (NPB + NPV + NLT - 1) / NLT;  // pieces per loader thread
 
   // LDS (bytes)
   static constexpr int O_X = 0;                                  // X'  [C][LDC]
@@ -78,80 +75,106 @@ struct StateCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// One loader thread's pieces of one chunk, in flight.
+// Sections of a block as the loaders copy them: global byte offset and row
+// length, LDS byte offset and row stride, and 16-byte pieces.  Every section's
+// rows are whole pieces, so a piece never straddles a row.
+struct Sec {
+  int g0, grow, l0, lrow, n;
+};
 template <class Cfg>
-struct Pieces {
-  uint32_t d[Cfg::NPT][4];
+struct Secs {
+  static constexpr int C = Cfg::C, DK = Cfg::DK, ES = Cfg::ES;
+  static constexpr Sec s[6] = {
+      {Cfg::GB_X, C * ES, Cfg::O_X, Cfg::LDC * ES, C * C * ES / 16},
+      {Cfg::GB_W, DK * ES, Cfg::O_W, Cfg::LDK * ES, C * DK * ES / 16},
+      {Cfg::GB_Q, DK * ES, Cfg::O_Q, Cfg::LDK * ES, C * DK * ES / 16},
+      {Cfg::GB_P, C * ES, Cfg::O_P, Cfg::LDC * ES, C * C * ES / 16},
+      {Cfg::GB_K, C * ES, Cfg::O_K, Cfg::LDC * ES, DK * C * ES / 16},
+      {Cfg::GB_G, DK * 4, Cfg::O_G, DK * 4, DK * 4 / 16},
+  };
+  // loads per loader thread for section k
+  static constexpr int per(int k) { return (s[k].n + Cfg::NLT - 1) / Cfg::NLT; }
+  static constexpr int NV = (Cfg::NPV + Cfg::NLT - 1) / Cfg::NLT;  // V loads per thread
 };
 
-// Issue the loads of chunk (block base, V rows t0 .. t0+L-1) into pf.
-template <class Cfg>
-__device__ __forceinline__ void issue_chunk(Pieces<Cfg>& pf, const unsigned char* blk,
-                                            const void* v, int64_t t0, int L, int H, int h,
-                                            int dv0, int lt) {
-  using ST = typename Cfg::IO::storage;
-  const rsrc_t rb = make_rsrc(blk, Cfg::GB_END);
-  const int vrow = H * Cfg::DV * Cfg::IOES;  // bytes per token in v
-  const rsrc_t rv = make_rsrc(static_cast<const ST*>(v) + (t0 * H + h) * static_cast<int64_t>(Cfg::DV) + dv0,
-                              L * vrow);
+// The loaders move a block in two groups, by when the state waves read them:
+// group A (X', -W and the V tile) feeds U, group B (Qt', P', Kh'^T, g) feeds
+// the outputs and the state update.  Group B of chunk i is written while the
+// state waves compute U(i), group A of chunk i+1 while they compute O(i) and
+// S(i); two groups of each kind are in flight.
+//
+// One loader thread's pieces of sections [K0, K1) (plus the V tile if WITH_V)
+// of one chunk.  Every load is issued unconditionally (indices clamped into
+// range; duplicates are discarded at the store), so the number of loads per
+// group is fixed and each wait can leave the newer groups outstanding.
+template <class Cfg, int K0, int K1, bool WITH_V>
+struct Group {
+  using S = Secs<Cfg>;
+  static constexpr int first(int k) { return k <= K0 ? 0 : first(k - 1) + S::per(k - 1); }
+  static constexpr int NBL = first(K1);
+  static constexpr int NV = WITH_V ? S::NV : 0;
+  uint32_t d[NBL + NV][4];
+
+  __device__ __forceinline__ void issue(const unsigned char* blk, const void* v, int64_t t0, int L,
+                                        int H, int h, int dv0, int lt) {
+    using ST = typename Cfg::IO::storage;
+    const rsrc_t rb = make_rsrc(blk, Cfg::GB_END);
 #pragma unroll
-  for (int u = 0; u < Cfg::NPT; ++u) {
-    const int p = lt + Cfg::NLT * u;
-    if (p < Cfg::NPB) {
-      ldraw<16>(rb, 16 * p, pf.d[u]);
-    } else if (p < Cfg::NPB + Cfg::NPV) {
-      const int pv = p - Cfg::NPB;
-      const int j = iclamp(pv / Cfg::VPR, L - 1);
-      ldraw<16>(rv, j * vrow + 16 * (pv % Cfg::VPR), pf.d[u]);
+    for (int k = K0; k < K1; ++k) {
+#pragma unroll
+      for (int u = 0; u < S::per(k); ++u) {
+        const int p = iclamp(lt + Cfg::NLT * u, S::s[k].n - 1);
+        ldraw<16>(rb, S::s[k].g0 + 16 * p, d[first(k) + u]);
+      }
+    }
+    if constexpr (WITH_V) {
+      const int vrow = H * Cfg::DV * Cfg::IOES;  // bytes per token in v
+      const rsrc_t rv = make_rsrc(
+          static_cast<const ST*>(v) + (t0 * H + h) * static_cast<int64_t>(Cfg::DV) + dv0, L * vrow);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int pv = iclamp(lt + Cfg::NLT * u, Cfg::NPV - 1);
+        const int j = iclamp(pv / Cfg::VPR, L - 1);
+        ldraw<16>(rv, j * vrow + 16 * (pv % Cfg::VPR), d[NBL + u]);
+      }
     }
   }
-}
 
-// Write a chunk's pieces into the padded LDS layout (V rows >= L as zeros).
-template <class Cfg>
-__device__ __forceinline__ void store_chunk(const Pieces<Cfg>& pf, unsigned char* smem, int L,
-                                            int lt) {
-  using T = typename Cfg::T;
-  constexpr int C = Cfg::C, DK = Cfg::DK, ES = Cfg::ES, LDK = Cfg::LDK, LDC = Cfg::LDC;
+  // Write the pieces into the padded LDS layout (V rows >= L as zeros).
+  __device__ __forceinline__ void store(unsigned char* smem, int L, int lt) const {
+    using T = typename Cfg::T;
 #pragma unroll
-  for (int u = 0; u < Cfg::NPT; ++u) {
-    const int p = lt + Cfg::NLT * u;
-    const uint4 val = make_uint4(pf.d[u][0], pf.d[u][1], pf.d[u][2], pf.d[u][3]);
-    if (p < Cfg::NPB) {
-      const int b = 16 * p;
-      int dst;
-      if (b < Cfg::GB_W) {
-        dst = Cfg::O_X + (b / (C * ES)) * LDC * ES + b % (C * ES);
-      } else if (b < Cfg::GB_Q) {
-        const int o = b - Cfg::GB_W;
-        dst = Cfg::O_W + (o / (DK * ES)) * LDK * ES + o % (DK * ES);
-      } else if (b < Cfg::GB_P) {
-        const int o = b - Cfg::GB_Q;
-        dst = Cfg::O_Q + (o / (DK * ES)) * LDK * ES + o % (DK * ES);
-      } else if (b < Cfg::GB_K) {
-        const int o = b - Cfg::GB_P;
-        dst = Cfg::O_P + (o / (C * ES)) * LDC * ES + o % (C * ES);
-      } else if (b < Cfg::GB_G) {
-        const int o = b - Cfg::GB_K;
-        dst = Cfg::O_K + (o / (C * ES)) * LDC * ES + o % (C * ES);
-      } else {
-        dst = Cfg::O_G + (b - Cfg::GB_G);
+    for (int k = K0; k < K1; ++k) {
+#pragma unroll
+      for (int u = 0; u < S::per(k); ++u) {
+        const int p = lt + Cfg::NLT * u;
+        if (S::s[k].n % Cfg::NLT == 0 || p < S::s[k].n) {
+          const int b = 16 * p;
+          const int dst = S::s[k].l0 + (b / S::s[k].grow) * S::s[k].lrow + b % S::s[k].grow;
+          const uint32_t* q = d[first(k) + u];
+          *reinterpret_cast<uint4*>(smem + dst) = make_uint4(q[0], q[1], q[2], q[3]);
+        }
       }
-      *reinterpret_cast<uint4*>(smem + dst) = val;
-    } else if (p < Cfg::NPB + Cfg::NPV) {
-      const int pv = p - Cfg::NPB;
-      const int j = pv / Cfg::VPR, c0 = (pv % Cfg::VPR) * (16 / Cfg::IOES);
+    }
+    if constexpr (WITH_V) {
       T* vt = reinterpret_cast<T*>(smem + Cfg::O_VT);
-      const bool in = j < L;
       constexpr int NE = 16 / Cfg::IOES;
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const float x = in ? dec<typename Cfg::IO>(pf.d[u], e) : 0.f;
-        vt[(c0 + e) * LDC + j] = Cfg::Op::cvt(x);
+      for (int u = 0; u < NV; ++u) {
+        const int pv = lt + Cfg::NLT * u;
+        if (Cfg::NPV % Cfg::NLT == 0 || pv < Cfg::NPV) {
+          const int j = pv / Cfg::VPR, c0 = (pv % Cfg::VPR) * NE;
+          const bool in = j < L;
+#pragma unroll
+          for (int e = 0; e < NE; ++e) {
+            const float x = in ? dec<typename Cfg::IO>(d[NBL + u], e) : 0.f;
+            vt[(c0 + e) * Cfg::LDC + j] = Cfg::Op::cvt(x);
+          }
+        }
       }
     }
   }
-}
+};
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
@@ -233,68 +256,128 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
   if (is_state) {
     ST* go = static_cast<ST*>(a.o);
     for (int i = 0; i < nch; ++i) {
-      __syncthreads();  // LDS holds chunk i
+      __syncthreads();  // group A of chunk i is in LDS
       const int L = chunk_len(i);
       const int64_t t0 = chunk_t0(i);
       Frag sf[Cfg::NFK];
       Op::template frags<DK>(sf, sacc);
-      // U tiles: X' V - W S
+      // U tiles: X' V - W S.  All LDS fragments of the phase are read first
+      // (one exposure of LDS latency), then the MFMAs run.
       f32x4 uacc[NB];
+      {
+        Frag xf[NB][Cfg::NFC], wf[NB][Cfg::NFK], vf[Cfg::NFC];
+        const T* vrow = sVT + (16 * wave + l16) * LDC;
 #pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        uacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Op::template mmaK<C>(uacc[rb], sX + 16 * rb * LDC, LDC, sVT + 16 * wave * LDC, LDC, lane);
-        Op::template mma_perm<DK, true>(uacc[rb], sW + (16 * rb + l16) * LDK, sf, lq);
+        for (int s = 0; s < Cfg::NFC; ++s) vf[s] = Op::template row_frag<C>(vrow, s, lq);
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+          for (int s = 0; s < Cfg::NFC; ++s)
+            xf[rb][s] = Op::template row_frag<C>(sX + (16 * rb + l16) * LDC, s, lq);
+#pragma unroll
+          for (int s = 0; s < Cfg::NFK; ++s)
+            wf[rb][s] = Op::template row_frag<DK>(sW + (16 * rb + l16) * LDK, s, lq);
+        }
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+          uacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < Cfg::NFC; ++s) Op::mma(uacc[rb], xf[rb][s], vf[s]);
+#pragma unroll
+          for (int s = 0; s < Cfg::NFK; ++s) Op::mma(uacc[rb], wf[rb][s], sf[s]);
+        }
       }
       Frag uf[Cfg::NFC];
       Op::template frags<C>(uf, uacc);
+      __syncthreads();  // group B of chunk i is in LDS
       // O^T tiles: S^T Qt'^T + U^T P'^T
+      {
+        Frag qf[NB][Cfg::NFK], pf[NB][Cfg::NFC];
 #pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
-        Op::template mma_perm<DK, false>(oacc, sQ + (16 * rb + l16) * LDK, sf, lq);
-        Op::template mma_perm<C, false>(oacc, sP + (16 * rb + l16) * LDC, uf, lq);
-        const int r = 16 * rb + l16;
-        if (r < L)
-          IO::store4(go + ((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0 + 16 * wave + 4 * lq,
-                     oacc);
+        for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+          for (int s = 0; s < Cfg::NFK; ++s)
+            qf[rb][s] = Op::template row_frag<DK>(sQ + (16 * rb + l16) * LDK, s, lq);
+#pragma unroll
+          for (int s = 0; s < Cfg::NFC; ++s)
+            pf[rb][s] = Op::template row_frag<C>(sP + (16 * rb + l16) * LDC, s, lq);
+        }
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+          f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < Cfg::NFK; ++s) Op::mma(oacc, sf[s], qf[rb][s]);
+#pragma unroll
+          for (int s = 0; s < Cfg::NFC; ++s) Op::mma(oacc, uf[s], pf[rb][s]);
+          const int r = 16 * rb + l16;
+          if (r < L)
+            IO::store4(go + ((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0 + 16 * wave + 4 * lq,
+                       oacc);
+        }
       }
       // S <- Diag(g) S + Kh'^T U
+      {
+        Frag kf[NMC][Cfg::NFC];
+        f32x4 gv[NMC];
 #pragma unroll
-      for (int mc = 0; mc < NMC; ++mc) {
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(sg + 16 * mc + 4 * lq);
-        sacc[mc] *= gv;
-        Op::template mma_perm<C, true>(sacc[mc], sK + (16 * mc + l16) * LDC, uf, lq);
+        for (int mc = 0; mc < NMC; ++mc) {
+          gv[mc] = *reinterpret_cast<const f32x4*>(sg + 16 * mc + 4 * lq);
+#pragma unroll
+          for (int s = 0; s < Cfg::NFC; ++s)
+            kf[mc][s] = Op::template row_frag<C>(sK + (16 * mc + l16) * LDC, s, lq);
+        }
+#pragma unroll
+        for (int mc = 0; mc < NMC; ++mc) {
+          sacc[mc] *= gv[mc];
+#pragma unroll
+          for (int s = 0; s < Cfg::NFC; ++s) Op::mma(sacc[mc], kf[mc][s], uf[s]);
+        }
       }
-      __syncthreads();  // done with chunk i
     }
   } else {
-    // chunks 0 and 1 in flight, chunk 0 into LDS, chunk 2 in flight
-    Pieces<Cfg> pa, pb;
-    auto issue = [&](Pieces<Cfg>& pf, int i) {
-      issue_chunk<Cfg>(pf, blocks + static_cast<int64_t>(c_begin + i) * a.blk_bytes, a.v,
-                       chunk_t0(i), chunk_len(i), H, h, dv0, lt);
+    using GA = Group<Cfg, 0, 2, true>;
+    using GB = Group<Cfg, 2, 6, false>;
+    // Loads are issued for every step (the chunk index clamped to the last
+    // chunk), so each wait counts the same number of newer loads on every path.
+    auto blk = [&](int i) {
+      const int ic = i < nch - 1 ? i : nch - 1;
+      return blocks + static_cast<int64_t>(c_begin + ic) * a.blk_bytes;
     };
-    if (nch > 0) issue(pa, 0);
-    if (nch > 1) issue(pb, 1);
-    if (nch > 0) store_chunk<Cfg>(pa, smem, chunk_len(0), lt);
-    if (nch > 2) issue(pa, 2);
-    // step i: chunk i+1 (in `nxt`) goes to LDS once the state waves are done
-    // with chunk i; `nxt` then takes chunk i+3
-    auto step = [&](int i, Pieces<Cfg>& nxt) {
-      __syncthreads();  // LDS holds chunk i
-      __syncthreads();  // the state waves are done with chunk i
-      if (i + 1 < nch) {
-        store_chunk<Cfg>(nxt, smem, chunk_len(i + 1), lt);
-        if (i + 3 < nch) issue(nxt, i + 3);
-      }
+    auto clampi = [&](int i) { return i < nch - 1 ? i : nch - 1; };
+    auto issueA = [&](GA& g, int i) {
+      const int ic = clampi(i);
+      g.issue(blk(ic), a.v, chunk_t0(ic), chunk_len(ic), H, h, dv0, lt);
+    };
+    auto issueB = [&](GB& g, int i) { g.issue(blk(clampi(i)), nullptr, 0, 1, H, h, dv0, lt); };
+    GA sa0, sa1;
+    GB sb0, sb1;
+    if (nch > 0) {
+      issueA(sa0, 0);
+      issueB(sb0, 0);
+      issueA(sa1, 1);
+      issueB(sb1, 1);
+      sa0.store(smem, chunk_len(0), lt);
+      issueA(sa0, 2);
+    }
+    // step i: B(i) (in gb) goes to LDS while U(i) runs, then A(i+1) (in ga)
+    // while O(i) and S(i) run; gb then takes B(i+2) and ga takes A(i+3)
+    auto step = [&](int i, GB& gb, GA& ga) {
+      __syncthreads();  // U(i) may start; the state waves are done with B(i-1)
+      gb.store(smem, 0, lt);
+      issueB(gb, i + 2);
+      __syncthreads();  // O(i), S(i) may start; the state waves are done with A(i)
+      // unconditional (past the last chunk it rewrites the last chunk's group
+      // A, which nothing reads any more): a skipped store would leave these
+      // registers' loads pending when the next issue overwrites them
+      ga.store(smem, chunk_len(clampi(i + 1)), lt);
+      issueA(ga, i + 3);
     };
     int i = 0;
     for (; i + 1 < nch; i += 2) {
-      step(i, pb);
-      step(i + 1, pa);
+      step(i, sb0, sa1);
+      step(i + 1, sb1, sa0);
     }
-    if (i < nch) step(i, pb);
+    if (i < nch) step(i, sb0, sa1);
   }
 
   if (is_state && a.ht) {

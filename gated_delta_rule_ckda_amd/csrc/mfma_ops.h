@@ -93,6 +93,10 @@ struct OpBF16 {
     }
     return f;
   }
+  // acc += A * B over one K-slice, both operands as fragments in the same K order
+  static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
   // acc += A * B with A from LDS rows (this lane's row pointer) and B from
   // register fragments (reg_is_b) or the other way round.
   template <int K, bool REG_IS_B>
@@ -155,7 +159,11 @@ struct OpF32 {
   static __device__ __forceinline__ Frag row_frag(const T* row, int s, int lq) {
     return *reinterpret_cast<const f32x4*>(row + 16 * s + 4 * lq);
   }
-  // MFMA i of slice s contracts over K-value 16s + 4*lq + i in every lane.
+  // MFMA i of a slice contracts over K-value 16s + 4*lq + i in every lane.
+  static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+  }
   template <int K, bool REG_IS_B>
   static __device__ __forceinline__ void mma_perm(f32x4& acc, const T* row, const Frag* rf, int lq) {
     constexpr int NS = K / 16;
