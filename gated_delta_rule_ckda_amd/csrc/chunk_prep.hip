@@ -39,6 +39,8 @@
 //   4  Kt'^T to LDS, Kh'^T out; 16x16 diagonal blocks of X by forward substitution
 //   5  off-diagonal blocks X_IJ = -X_II sum_{J<=M<I} A_IM X_MJ on fp32 MFMA
 //   6  X' out, -W = -X Kt' on MFMA, out
+// Rows of the block are written in the fragment storage order of
+// mfma_ops.h (perm32 for bf16 rows whose length is a multiple of 32).
 #include "mfma_ops.h"
 
 namespace ckda {
@@ -46,6 +48,19 @@ namespace {
 
 constexpr float kRegularMin = 0x1p-100f;
 constexpr float kRegularMax = 0x1p+10f;
+
+// N consecutive logical entries start .. start+N-1 of a row of length K in
+// the handoff storage order (start a multiple of 4, or of 2 for N == 2).
+template <class Op, int N, int K>
+__device__ __forceinline__ void store_run_pos(typename Op::T* row, int start, const float* v) {
+  if constexpr (N <= 2) {
+    store_run<Op, N>(row + Op::template pos<K>(start), v);
+  } else {
+#pragma unroll
+    for (int g = 0; g < N; g += 4)
+      Op::store4(row + Op::template pos<K>(start + g), f32x4{v[g], v[g + 1], v[g + 2], v[g + 3]});
+  }
+}
 
 template <class OpT, class IOT, int C_, int DK_>
 struct PrepCfg {
@@ -164,7 +179,7 @@ __device__ __noinline__ void direct_ap(const void* gq, const void* gk, const flo
         a_blk<Cfg>(smem, I, J)[(r % 16) * LDA + j % 16] = av;
       else if (I == J)
         x_blk<Cfg>(smem, I, I)[(r % 16) * LDA + j % 16] = av;
-      gP[r * C + j] = Op::cvt((r >= j) ? pp * scale * srq[r] * rkj : 0.f);
+      gP[r * C + Op::template pos<C>(j)] = Op::cvt((r >= j) ? pp * scale * srq[r] * rkj : 0.f);
     }
   }
 }
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
         float qv[CPT];
 #pragma unroll
         for (int cc = 0; cc < CPT; ++cc) qv[cc] = xq[i][cc] * rqs[i];
-        store_run<Op, CPT>(gQ + r * DK + c0ch, qv);
+        store_run<Op, CPT>(gQ + r * DK + Op::template pos<DK>(c0ch), qv);
         store_run<Op, CPT>(sLk + r * LDK + c0ch, kt[i]);
         store_run<Op, CPT>(sLq + r * LDK + c0ch, xq[i]);
         store_run<Op, CPT>(sRk + r * LDK + c0ch, xk[i]);
@@ -384,12 +399,13 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
           const int j = 16 * J + 4 * lq + i;
           out[i] = (I == J && j > r) ? 0.f : acc[i] * sr * srk[j];
         }
-        Op::store4(gP + r * C + 16 * J + 4 * lq, out);
+        Op::store4(gP + r * C + Op::template pos<C>(16 * J + 4 * lq), out);
       } else if (tt < NTILE) {
         int I, J;
         lower_block(tt - 2 * NPT, J, I);  // J > I: a block above the diagonal
         J += 1;
-        Op::store4(gP + (16 * I + l16) * C + 16 * J + 4 * lq, f32x4{0.f, 0.f, 0.f, 0.f});
+        Op::store4(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J + 4 * lq),
+                   f32x4{0.f, 0.f, 0.f, 0.f});
       }
     }
   } else {
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
         khv[i] = kh[i][cc] * rks[i];
       }
       store_run<Op, RPW>(sKtT + (c0ch + cc) * LDC + r0, ktv);
-      store_run<Op, RPW>(gK + (c0ch + cc) * C + r0, khv);
+      store_run_pos<Op, RPW, C>(gK + (c0ch + cc) * C, r0, khv);
     }
   }
   if (wave < NB && lane < 16) {
@@ -510,7 +526,7 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
       if (J <= I) xv = *reinterpret_cast<const f32x4*>(x_blk<Cfg>(smem, I, J) + (r % 16) * LDA + j % 16);
       Op::store4(sXb + r * LDC + j, xv);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(sbeta + j);
-      Op::store4(gX + r * C + j, xv * bv);
+      Op::store4(gX + r * C + Op::template pos<C>(j), xv * bv);
     }
   }
   __syncthreads();
@@ -525,7 +541,7 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         Op::template mmaK<C>(acc, sKtT + 16 * mc * LDC, LDC, sXb + 16 * nr * LDC, LDC, lane);
         // rows c = 16mc + 4lq + i, column r = 16nr + l16: W[r][c]
-        Op::store4(gW + (16 * nr + l16) * DK + 16 * mc + 4 * lq, -acc);
+        Op::store4(gW + (16 * nr + l16) * DK + Op::template pos<DK>(16 * mc + 4 * lq), -acc);
       }
     }
   }

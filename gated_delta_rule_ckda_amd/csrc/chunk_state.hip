@@ -13,7 +13,9 @@
 // registers too, so a chunk step needs no barrier among the state waves.  The
 // operands that are shared by all columns (X', W, Qt', P', Kh'^T, g) and the
 // V tile sit in LDS, read as MFMA row fragments in the permuted K order that
-// matches the register fragments (mfma_ops.h).
+// matches the register fragments; the transform pass stores those rows in
+// that order already (perm32 in mfma_ops.h), so each fragment is one 16-byte
+// read.
 //
 // The last four waves ("loader waves") stream the blocks: a chunk's block and
 // V rows are loaded into registers two chunks ahead and written to LDS while
@@ -55,7 +57,7 @@ struct StateCfg {
   static constexpr int GB_G = GB_K + DK * C * ES;
   static constexpr int GB_END = GB_G + DK * 4;
   static constexpr int VPR = DVT * IOES / 16;        // 16-byte pieces per V row of the tile
-  static constexpr int NPV = C * VPR;                // pieces of the V tile
+  static constexpr int NVU = (C / 2) * VPR;          // V units: one piece of two adjacent rows
 
   // LDS (bytes)
   static constexpr int O_X = 0;                                  // X'  [C][LDC]
@@ -94,7 +96,7 @@ struct Secs {
   };
   // loads per loader thread for section k
   static constexpr int per(int k) { return (s[k].n + Cfg::NLT - 1) / Cfg::NLT; }
-  static constexpr int NV = (Cfg::NPV + Cfg::NLT - 1) / Cfg::NLT;  // V loads per thread
+  static constexpr int NV = (Cfg::NVU + Cfg::NLT - 1) / Cfg::NLT;  // V units per thread
 };
 
 // The loaders move a block in two groups, by when the state waves read them:
@@ -113,7 +115,7 @@ struct Group {
   static constexpr int first(int k) { return k <= K0 ? 0 : first(k - 1) + S::per(k - 1); }
   static constexpr int NBL = first(K1);
   static constexpr int NV = WITH_V ? S::NV : 0;
-  uint32_t d[NBL + NV][4];
+  uint32_t d[NBL + 2 * NV][4];
 
   __device__ __forceinline__ void issue(const unsigned char* blk, const void* v, int64_t t0, int L,
                                         int H, int h, int dv0, int lt) {
@@ -131,11 +133,14 @@ struct Group {
       const int vrow = H * Cfg::DV * Cfg::IOES;  // bytes per token in v
       const rsrc_t rv = make_rsrc(
           static_cast<const ST*>(v) + (t0 * H + h) * static_cast<int64_t>(Cfg::DV) + dv0, L * vrow);
+      // unit -> (row pair jp, piece cp) with jp fastest, so that the
+      // transposed LDS writes of 32 lanes land in 32 different banks
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        const int pv = iclamp(lt + Cfg::NLT * u, Cfg::NPV - 1);
-        const int j = iclamp(pv / Cfg::VPR, L - 1);
-        ldraw<16>(rv, j * vrow + 16 * (pv % Cfg::VPR), d[NBL + u]);
+        const int uv = iclamp(lt + Cfg::NLT * u, Cfg::NVU - 1);
+        const int jp = uv % (Cfg::C / 2), cp = uv / (Cfg::C / 2);
+        ldraw<16>(rv, iclamp(2 * jp, L - 1) * vrow + 16 * cp, d[NBL + 2 * u]);
+        ldraw<16>(rv, iclamp(2 * jp + 1, L - 1) * vrow + 16 * cp, d[NBL + 2 * u + 1]);
       }
     }
   }
@@ -161,14 +166,17 @@ struct Group {
       constexpr int NE = 16 / Cfg::IOES;
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        const int pv = lt + Cfg::NLT * u;
-        if (Cfg::NPV % Cfg::NLT == 0 || pv < Cfg::NPV) {
-          const int j = pv / Cfg::VPR, c0 = (pv % Cfg::VPR) * NE;
-          const bool in = j < L;
+        const int uv = lt + Cfg::NLT * u;
+        if (Cfg::NVU % Cfg::NLT == 0 || uv < Cfg::NVU) {
+          const int jp = uv % (Cfg::C / 2), c0 = (uv / (Cfg::C / 2)) * NE;
+          const bool in0 = 2 * jp < L, in1 = 2 * jp + 1 < L;
+          // rows 2jp and 2jp+1 are adjacent in the storage order too
+          const int q = Cfg::Op::template pos<Cfg::C>(2 * jp);
 #pragma unroll
           for (int e = 0; e < NE; ++e) {
-            const float x = in ? dec<typename Cfg::IO>(d[NBL + u], e) : 0.f;
-            vt[(c0 + e) * Cfg::LDC + j] = Cfg::Op::cvt(x);
+            const float x0 = in0 ? dec<typename Cfg::IO>(d[NBL + 2 * u], e) : 0.f;
+            const float x1 = in1 ? dec<typename Cfg::IO>(d[NBL + 2 * u + 1], e) : 0.f;
+            Cfg::Op::store2(vt + (c0 + e) * Cfg::LDC + q, x0, x1);
           }
         }
       }

@@ -29,11 +29,22 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 // runs over K in the order (tile, lq, i) instead of the natural order; the LDS
 // operand is read in the same permuted order (row fragments at 4*lq and, for
 // bf16, 16 + 4*lq within each 32-wide K slice), which leaves the sum unchanged.
+// Storage order of rows that are read as permuted-order fragments (bf16 rows
+// whose length K is a multiple of 32): logical index 32s + 16h + 4q + i is
+// stored at 32s + 8q + 4h + i, so the 8 values lane group q needs for slice s
+// are contiguous (one 16-byte LDS read).  Rows of length 16 keep their order.
+__host__ __device__ constexpr int perm32(int k) {
+  return (k & ~31) | (((k & 15) >> 2) << 3) | (((k & 31) >> 4) << 2) | (k & 3);
+}
+
 struct OpBF16 {
   using T = __bf16;
   using Frag = bf16x8;                 // K-slice of 32 per MFMA
   static constexpr int KS = 32;
   static __device__ __forceinline__ T cvt(float x) { return static_cast<__bf16>(x); }
+  // storage position of logical index k in a row of length K
+  template <int K>
+  static __device__ __forceinline__ int pos(int k) { return K % 32 == 0 ? perm32(k) : k; }
 
   // acc += A[16 x K] * B[16 x K]^T, K a multiple of 16.  A K remainder of 16
   // runs as one more 16x16x32 MFMA whose upper half of K is zero (lanes 32..63
@@ -76,44 +87,29 @@ struct OpBF16 {
       }
     }
   }
-  // Row fragment of an LDS operand in the permuted K order (row = this lane's row).
+  // Row fragment of an LDS operand in the permuted K order (row = this lane's
+  // row, stored in pos<K> order): 16 contiguous bytes, or 8 bytes and zeros
+  // for a row of length 16.
   template <int K>
   static __device__ __forceinline__ Frag row_frag(const T* row, int s, int lq) {
-    Frag f;
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 32 * s + 4 * lq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = lo[i];
-    if (32 * s + 16 < K) {
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 32 * s + 16 + 4 * lq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f[4 + i] = hi[i];
+    if constexpr (K % 32 == 0) {
+      return *reinterpret_cast<const bf16x8*>(row + 32 * s + 8 * lq);
     } else {
+      static_assert(K == 16, "row length");
+      Frag f;
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 4 * lq);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[4 + i] = cvt(0.f);
+      for (int i = 0; i < 4; ++i) {
+        f[i] = lo[i];
+        f[4 + i] = cvt(0.f);
+      }
+      return f;
     }
-    return f;
   }
   // acc += A * B over one K-slice, both operands as fragments in the same K order
   static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
   }
-  // acc += A * B with A from LDS rows (this lane's row pointer) and B from
-  // register fragments (reg_is_b) or the other way round.
-  template <int K, bool REG_IS_B>
-  static __device__ __forceinline__ void mma_perm(f32x4& acc, const T* row, const Frag* rf, int lq) {
-    constexpr int NS = (K + 31) / 32;
-    Frag lf[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) lf[s] = row_frag<K>(row, s, lq);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if constexpr (REG_IS_B)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf[s], rf[s], acc, 0, 0, 0);
-      else
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[s], lf[s], acc, 0, 0, 0);
-    }
-  }
-
   // Store 4 (or 2, or 1) consecutive values at p.
   static __device__ __forceinline__ void store4(T* p, f32x4 x) {
     bf16x4 y;
@@ -133,6 +129,9 @@ struct OpF32 {
   using Frag = f32x4;                  // K-slice of 16 = 4 MFMAs of depth 4
   static constexpr int KS = 16;
   static __device__ __forceinline__ T cvt(float x) { return x; }
+  // the permuted fragment order is already contiguous for fp32
+  template <int K>
+  static __device__ __forceinline__ int pos(int k) { return k; }
 
   template <int K>
   static __device__ __forceinline__ void mmaK(f32x4& acc, const T* a, int lda, const T* b, int ldb,
@@ -164,23 +163,6 @@ struct OpF32 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
   }
-  template <int K, bool REG_IS_B>
-  static __device__ __forceinline__ void mma_perm(f32x4& acc, const T* row, const Frag* rf, int lq) {
-    constexpr int NS = K / 16;
-    Frag lf[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) lf[s] = row_frag<K>(row, s, lq);
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (REG_IS_B)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(lf[s][i], rf[s][i], acc, 0, 0, 0);
-        else
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(rf[s][i], lf[s][i], acc, 0, 0, 0);
-      }
-  }
-
   static __device__ __forceinline__ void store4(T* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
   static __device__ __forceinline__ void store2(T* p, float x0, float x1) {
     *reinterpret_cast<float2*>(p) = make_float2(x0, x1);
