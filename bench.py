@@ -5,9 +5,11 @@
 
 One step = one ckda_chunk_fwd call over the LM-layer workload (B=8, T=4096,
 H=16, dk=dv=128, bf16 q/k/v, fp32 alpha/beta/state, chunk 64, in-kernel q/k
-L2 norm, CKDA gate range), inputs resident in HBM.  Prints one JSON line with
-the headline throughput (tokens/s), the roofline position of the forward
-kernel (HBM-bound: algorithmic bytes / kernel time against 8 TB/s), the
+L2 norm, CKDA gate range), inputs resident in HBM: the transform pass over
+all chunks, then the state pass.  Prints one JSON line with the headline
+throughput (tokens/s), the roofline position of each pass's kernel timed on
+its own (HBM-bound: algorithmic bytes / kernel time against 8 TB/s; the
+dominant one is the headline roofline), the
 oracle's CPU throughput on a bounded sample, and extra lines of context: the
 KDA-range arm (throughput ratio), the packed varlen prefill and the decode
 step.  Inputs are synthetic (seeded), shaped like the method's workloads.
@@ -26,7 +28,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc", "chunk_fwd.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc")
+# sources each pass's kernel is built from (the traffic summary is keyed on them)
+PASS_SOURCES = {
+    "prep": ["chunk_prep.hip", "mfma_ops.h", "ckda_internal.h"],
+    "state": ["chunk_state.hip", "mfma_ops.h", "ckda_internal.h"],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_lm_layer_traffic.txt")
 
 
@@ -39,7 +46,8 @@ def chunk_flops(C, dk, dv):
 
 
 def fwd_bytes(B, T, H, dk, dv, io_bytes, nseq, h0):
-    """Algorithmic HBM bytes: every input read once, every output written once."""
+    """Algorithmic HBM bytes of the whole forward: every input read once,
+    every output written once."""
     tok = B * T
     b = tok * H * (2 * dk + dv) * io_bytes      # q, k, v
     b += tok * H * dk * 4 + tok * H * 4         # alpha, beta
@@ -50,13 +58,35 @@ def fwd_bytes(B, T, H, dk, dv, io_bytes, nseq, h0):
     return b
 
 
-def src_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def block_bytes(C, dk, es):
+    """Bytes of one (chunk, head) block of the workspace (layout of the
+    transform pass's output, 256-byte aligned)."""
+    return -(-((2 * C * C + 3 * C * dk) * es + 4 * dk) // 256) * 256
 
 
-def load_traffic():
-    """HBM bytes per launch measured with rocprofv3 counters for the current
-    kernel source, or None if the counters were taken on another version."""
+def pass_bytes(B, T, H, dk, dv, C, io_bytes, nseq, h0):
+    """Algorithmic bytes per launch of each pass: its inputs read once and its
+    outputs written once.  The transform pass reads q, k, alpha, beta and
+    writes one block per chunk-head; the state pass reads the blocks, v (and
+    h0) and writes o and ht."""
+    tok = B * T
+    nblk = B * (-(-T // C)) * H
+    blocks = nblk * block_bytes(C, dk, io_bytes)
+    prep = tok * H * (2 * dk * io_bytes + dk * 4 + 4) + blocks
+    state = blocks + tok * H * dv * io_bytes * 2 + nseq * H * dk * dv * 4 * (2 if h0 else 1)
+    return {"prep": prep, "state": state}
+
+
+def src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(CSRC, n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters on
+    the current sources, or None if they were taken on other sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -64,10 +94,10 @@ def load_traffic():
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_src_sha256_16") != src_hash():
+    if kv.get(kernel + ".src_sha256_16") != src_hash(PASS_SOURCES[kernel]):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[kernel + ".hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -98,7 +128,7 @@ def time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall * 1000.0 / steps
 
 
-def bench_fwd(case, steps, warmup, gate):
+def fwd_plan(case, gate):
     import torch
     import gated_delta_rule_ckda_amd as ck
     dt = case.dtype
@@ -106,24 +136,31 @@ def bench_fwd(case, steps, warmup, gate):
     a, b = to_dev(case.alpha, "f32"), to_dev(case.beta, "f32")
     h0 = None if case.h0 is None else to_dev(case.h0, "f32")
     cu = None if case.cu_seqlens is None else torch.from_numpy(case.cu_seqlens).to("cuda:0")
-    o = torch.empty_like(v)
-    nseq = case.q.shape[0] if cu is None else len(case.cu_seqlens) - 1
-    H, dk, dv = case.q.shape[2], case.q.shape[3], case.v.shape[3]
-    ht = torch.empty((nseq, H, dk, dv), device="cuda:0", dtype=torch.float32)
-    B, T = (case.q.shape[0], case.q.shape[1]) if cu is None else (1, case.q.shape[0] * case.q.shape[1])
-    desc = ck.FwdDesc(B, T, H, dk, dv, nseq, case.chunk, ck.BF16 if dt == "bf16" else ck.F32,
-                      ck.GATE_CKDA if gate == "ckda" else ck.GATE_KDA, int(case.l2norm), 1.0)
-    ws = torch.empty(ck.chunk_fwd_workspace_size(desc, cu is not None), device="cuda:0",
-                     dtype=torch.uint8)
+    return ck.ChunkFwdPlan(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
+                           use_qk_l2norm=case.l2norm, gate=gate)
+
+
+def bench_fwd(case, steps, warmup, gate, passes=False):
+    """Whole forward per step (both passes, one ckda_chunk_fwd call on a
+    preallocated workspace); with passes=True also each pass alone."""
+    import torch
+    import gated_delta_rule_ckda_amd as ck
+    plan = fwd_plan(case, gate)
+    q, k, v, a, b, h0, cu = plan.args
 
     def step():
         ck.chunk_fwd(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
-                     use_qk_l2norm=case.l2norm, gate=gate, out=o, final_state=ht, workspace=ws)
+                     use_qk_l2norm=case.l2norm, gate=gate, out=plan.o, final_state=plan.ht,
+                     workspace=plan.ws)
 
     ms, wall_ms = time_launches(step, steps, warmup)
-    del q, k, v, a, b, o, ht, ws
+    per = {}
+    if passes:
+        per["prep"], _ = time_launches(plan.prepare, steps, warmup)
+        per["state"], _ = time_launches(plan.finish, steps, warmup)
+    del plan, q, k, v, a, b, h0, cu
     torch.cuda.empty_cache()
-    return ms, wall_ms
+    return ms, wall_ms, per
 
 
 def bench_decode(steps_inner=64, reps=3):
@@ -153,10 +190,12 @@ def bench_decode(steps_inner=64, reps=3):
     return per, nbytes
 
 
-def cpu_baseline(case, pairs, scale=1.0):
+def cpu_baseline(case, pairs, scale=1.0, min_seconds=10.0):
     """Oracle throughput on the host cores on a bounded sample: the first
     `pairs` (batch, head) pairs of the workload over the full sequence length
-    (pairs are independent, so this is the same per-token work)."""
+    (pairs are independent, so this is the same per-token work), run
+    repeatedly for about `min_seconds` (at least 3 runs); the median run is
+    reported."""
     import oracle
     B, T, H = case.q.shape[:3]
     sel = [(i // H, i % H) for i in range(pairs)]
@@ -166,15 +205,20 @@ def cpu_baseline(case, pairs, scale=1.0):
     a = np.stack([case.alpha[b, :, h] for b, h in sel], 0)[:, :, None]
     be = np.stack([case.beta[b, :, h] for b, h in sel], 0)[:, :, None]
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.fwd(q, k, v, a, be, use_l2norm=case.l2norm, scale=scale)
-    wall = time.perf_counter() - t0
+    runs = []
+    start = time.perf_counter()
+    while len(runs) < 3 or time.perf_counter() - start < min_seconds:
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, a, be, use_l2norm=case.l2norm, scale=scale)
+        runs.append(time.perf_counter() - t0)
+    wall = sorted(runs)[len(runs) // 2]
     head_tokens = pairs * T
     return {"value": (head_tokens / H) / wall, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of %d (batch, head) pairs x T=%d tokens of the same workload, fp64 "
-                      "sequential recurrence on %d OpenMP threads, %.1f s wall; tokens counted "
-                      "as head-tokens / H" % (pairs, B * H, T, threads, wall)}
+                      "sequential recurrence on %d OpenMP threads; median of %d runs (%.2f s each, "
+                      "%.1f s in total); tokens counted as head-tokens / H"
+                      % (pairs, B * H, T, threads, len(runs), wall, sum(runs))}
 
 
 def main():
@@ -183,7 +227,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "lm"], default="all",
-                    help="'lm' times only the headline workload (for profiling)")
+                    help="'lm': only the headline workload and its passes (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-pairs", type=int, default=128)
     args = ap.parse_args()
@@ -202,14 +246,23 @@ def main():
     B, T, H, dk = case.q.shape
     dv = case.v.shape[3]
     C = case.chunk
-    ms, wall_ms = bench_fwd(case, args.steps, args.warmup, "ckda")
+    ms, wall_ms, per = bench_fwd(case, args.steps, args.warmup, "ckda", passes=True)
     tokens = B * T
     tok_s = tokens / (ms / 1000.0)
     nbytes = fwd_bytes(B, T, H, dk, dv, 2, B, False)
     flops = chunk_flops(C, dk, dv) * (B * T // C) * H
-    gbs = nbytes / (ms / 1000.0) / 1e9
     tflops = flops / (ms / 1000.0) / 1e12
-    traffic = load_traffic()
+    pbytes = pass_bytes(B, T, H, dk, dv, C, 2, B, False)
+    names = {"prep": "prep_kernel<bf16, C=64, dk=128> (gate prefix, norms, UT/WY transform)",
+             "state": "state_kernel<bf16, C=64, dk=dv=128, dv tile 64> (inter-chunk state + output)"}
+    passes = {}
+    for kname, kms in per.items():
+        gbs = pbytes[kname] / (kms / 1000.0) / 1e9
+        passes[kname] = {"kernel": names[kname], "ms": round(kms, 4),
+                         "algorithmic_bytes": pbytes[kname], "achieved": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(kname)}
+    dom = max(per, key=per.get)
+    e2e_gbs = nbytes / (ms / 1000.0) / 1e9
 
     out = {
         "metric": "chunked CKDA fwd tokens/s + TFLOP/s (% MFMA peak), H=16 d=128 T=4096 bf16",
@@ -229,23 +282,25 @@ def main():
                    "alpha": "tanh(N(2,1))", "beta": "2 sigmoid(N(0,1))"},
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": nbytes,
-                     "kernel": "fwd_kernel<bf16, C=64, dk=dv=128, dv tile 64>",
+        "roofline": {"bound": "hbm", "achieved": passes[dom]["achieved"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": passes[dom]["frac"], "traffic": passes[dom]["traffic"],
+                     "kernel": passes[dom]["kernel"], "kernel_ms": passes[dom]["ms"],
+                     "algorithmic_bytes": pbytes[dom], "passes": passes,
+                     "end_to_end": {"algorithmic_bytes": nbytes, "achieved": round(e2e_gbs, 1),
+                                    "frac": round(e2e_gbs / HBM_PEAK_GBS, 4)},
                      "wall_ms_per_step": round(wall_ms, 4)},
     }
 
     if args.only == "all":
         kda = inputs.lm_layer(arm="kda")
-        ms_kda, _ = bench_fwd(kda, args.steps, args.warmup, "kda")
+        ms_kda, _, _ = bench_fwd(kda, args.steps, args.warmup, "kda")
         del kda
         out["kda_range"] = {"tokens_per_s": round(tokens / (ms_kda / 1000.0), 1),
                             "ms_per_step": round(ms_kda, 4),
                             "ckda_over_kda": round(ms_kda / ms, 4),
                             "pages_context": "CKDA keeps ~96-97% of KDA kernel throughput on H100"}
         vl = inputs.varlen()
-        ms_vl, _ = bench_fwd(vl, max(5, args.steps // 3), 2, "ckda")
+        ms_vl, _, _ = bench_fwd(vl, max(5, args.steps // 3), 2, "ckda")
         vl_tok = int(vl.cu_seqlens[-1])
         vl_bytes = fwd_bytes(1, vl_tok, 16, 128, 128, 2, 16, True)
         out["varlen"] = {"workload": vl.meta["workload"], "lengths": vl.meta["lengths"],

@@ -57,6 +57,12 @@ def _load():
         lib.ckda_chunk_fwd.restype = i32
         lib.ckda_chunk_fwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, ctypes.c_size_t, vp]
+        lib.ckda_chunk_fwd_prepare.restype = i32
+        lib.ckda_chunk_fwd_prepare.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp,
+                                               ctypes.c_size_t, vp]
+        lib.ckda_chunk_fwd_finish.restype = i32
+        lib.ckda_chunk_fwd_finish.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_size_t, vp]
         lib.ckda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         lib.ckda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), i32]
         lib.ckda_fwd_supported.restype = i32
@@ -179,6 +185,41 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
                               _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
                               _ptr(workspace), workspace.numel(), _stream(stream)))
     return o, ht
+
+
+class ChunkFwdPlan:
+    """The two passes of chunk_fwd as separate launches on one workspace:
+    prepare() runs the transform pass over all chunks, finish() the state
+    pass (o and the final state).  Used to time the passes one by one."""
+
+    def __init__(self, q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
+                 use_qk_l2norm=True, gate="ckda", scale=1.0, out=None, final_state=None,
+                 stream=None):
+        import torch
+        self.lib = _load()
+        H, dk, dv = q.shape[-2], q.shape[-1], v.shape[-1]
+        self.desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens)
+        self.args = (q, k, v, alpha, beta, h0, cu_seqlens)
+        self.o = torch.empty_like(v) if out is None else out
+        self.ht = (torch.empty((self.desc.num_seqs, H, dk, dv), device=q.device,
+                               dtype=torch.float32) if final_state is None else final_state)
+        need = chunk_fwd_workspace_size(self.desc, cu_seqlens is not None)
+        self.ws = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+        self.stream = stream
+
+    def prepare(self):
+        q, k, v, alpha, beta, h0, cu = self.args
+        _check(self.lib.ckda_chunk_fwd_prepare(ctypes.byref(self.desc), _ptr(q), _ptr(k),
+                                               _ptr(alpha), _ptr(beta), _ptr(cu), _ptr(self.ws),
+                                               self.ws.numel(), _stream(self.stream)))
+
+    def finish(self):
+        q, k, v, alpha, beta, h0, cu = self.args
+        _check(self.lib.ckda_chunk_fwd_finish(ctypes.byref(self.desc), _ptr(v), _ptr(cu),
+                                              _ptr(h0), _ptr(self.o), _ptr(self.ht),
+                                              _ptr(self.ws), self.ws.numel(),
+                                              _stream(self.stream)))
+        return self.o, self.ht
 
 
 def recurrent_step(q, k, v, alpha, beta, state, *, use_qk_l2norm=True, gate="ckda",

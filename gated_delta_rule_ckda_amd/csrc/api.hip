@@ -83,10 +83,21 @@ size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* d, int32_t packed) {
                                    d->io_dtype, packed != 0);
 }
 
-ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
-                             const void* v, const float* alpha, const float* beta,
-                             const int32_t* cu_seqlens, const float* h0, void* o,
-                             float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kPrepare = 1, kFinish = 2;
+
+// Host validation shared by the chunked-forward entry points.  `passes` says
+// which tensors the call uses: kPrepare needs q, k, alpha, beta; kFinish
+// needs v and o (and reads h0, writes ht).  Pointers a pass does not use must
+// be NULL.
+ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta,
+                           const int32_t* cu_seqlens, const float* h0, const void* o,
+                           const float* ht, const void* workspace, size_t workspace_bytes,
+                           int passes) {
   if (!d) return fail(CKDA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->dk <= 0 || d->dv <= 0 || d->num_seqs < 0)
     return fail(CKDA_ERR_INVALID_ARGUMENT,
@@ -110,8 +121,10 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void
                 d->num_seqs, d->B);
   }
   const int64_t tokens = static_cast<int64_t>(d->B) * d->T;
-  if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !o))
-    return fail(CKDA_ERR_INVALID_ARGUMENT, "q, k, v, alpha, beta and o must not be NULL");
+  if (tokens > 0 && (passes & kPrepare) && (!q || !k || !alpha || !beta))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "q, k, alpha and beta must not be NULL");
+  if (tokens > 0 && (passes & kFinish) && (!v || !o))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "v and o must not be NULL");
   const void* ptrs[] = {q, k, v, alpha, beta, h0, o, ht};
   const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "o", "ht"};
   for (int i = 0; i < 8; ++i)
@@ -120,12 +133,12 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void
 
   const int64_t eb = elem_bytes(d->io_dtype);
   const int64_t state_bytes = static_cast<int64_t>(d->num_seqs) * d->H * d->dk * d->dv * 4;
-  const Range ro = range("o", o, tokens * d->H * d->dv * eb);
-  const Range ins[] = {range("q", q, tokens * d->H * d->dk * eb),
-                       range("k", k, tokens * d->H * d->dk * eb),
-                       range("v", v, tokens * d->H * d->dv * eb),
-                       range("alpha", alpha, tokens * d->H * d->dk * 4),
-                       range("beta", beta, tokens * d->H * 4),
+  const Range ro = range("o", o, o ? tokens * d->H * d->dv * eb : 0);
+  const Range ins[] = {range("q", q, q ? tokens * d->H * d->dk * eb : 0),
+                       range("k", k, k ? tokens * d->H * d->dk * eb : 0),
+                       range("v", v, v ? tokens * d->H * d->dv * eb : 0),
+                       range("alpha", alpha, alpha ? tokens * d->H * d->dk * 4 : 0),
+                       range("beta", beta, beta ? tokens * d->H * 4 : 0),
                        range("h0", h0, h0 ? state_bytes : 0),
                        range("ht", ht, ht ? state_bytes : 0),
                        range("cu_seqlens", cu_seqlens,
@@ -156,13 +169,50 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void
   if (!ckda::fwd_supported(d->chunk_size, d->dk, d->dv, d->io_dtype))
     return fail(CKDA_ERR_UNSUPPORTED, "no chunked kernel for chunk_size=%d dk=%d dv=%d io_dtype=%d",
                 d->chunk_size, d->dk, d->dv, d->io_dtype);
-  if (d->num_seqs == 0) return ok();
+  return ok();
+}
 
+ckda_status_t run_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const int32_t* cu_seqlens,
+                      const float* h0, void* o, float* ht, void* workspace, size_t workspace_bytes,
+                      void* stream, int passes) {
+  const ckda_status_t st = validate_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht,
+                                        workspace, workspace_bytes, passes);
+  if (st != CKDA_OK) return st;
+  if (d->num_seqs == 0) return ok();
   ckda::FwdArgs a{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
                   d->use_qk_l2norm, d->gate_range, d->scale, q, k, v, alpha, beta,
                   cu_seqlens, h0, o, ht, nullptr, nullptr, nullptr, 0, 0, 0};
-  return from_hip(
-      ckda::launch_fwd(a, d->io_dtype, workspace, static_cast<hipStream_t>(stream)));
+  return from_hip(ckda::launch_fwd(a, d->io_dtype, workspace, static_cast<hipStream_t>(stream),
+                                   (passes & kPrepare) != 0, (passes & kFinish) != 0));
+}
+
+}  // namespace
+
+extern "C" {
+
+ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta,
+                             const int32_t* cu_seqlens, const float* h0, void* o,
+                             float* ht, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht, workspace, workspace_bytes,
+                 stream, kPrepare | kFinish);
+}
+
+ckda_status_t ckda_chunk_fwd_prepare(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                                     const float* alpha, const float* beta,
+                                     const int32_t* cu_seqlens, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return run_fwd(d, q, k, nullptr, alpha, beta, cu_seqlens, nullptr, nullptr, nullptr, workspace,
+                 workspace_bytes, stream, kPrepare);
+}
+
+ckda_status_t ckda_chunk_fwd_finish(const ckda_fwd_desc_t* d, const void* v,
+                                    const int32_t* cu_seqlens, const float* h0, void* o,
+                                    float* ht, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return run_fwd(d, nullptr, nullptr, v, nullptr, nullptr, cu_seqlens, h0, o, ht, workspace,
+                 workspace_bytes, stream, kFinish);
 }
 
 ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,

@@ -466,7 +466,8 @@ size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
   return static_cast<size_t>(map + static_cast<int64_t>(H) * maxc * blk_bytes(chunk, dk, es));
 }
 
-launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream) {
+launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream,
+                         bool prepare, bool finish) {
   if (static_cast<int64_t>(a.B) * a.T == 0) {
     // no tokens: every chain is empty and only copies h0 to ht (or zeros);
     // run the state pass as a dense batch with no chunks and no workspace
@@ -492,15 +493,15 @@ launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stre
   const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
   if (!e) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.num_seqs) * a.H == 0) return hipSuccess;
-  if (packed) {
+  if (prepare && packed) {
     const launch_result r = launch_chunk_map(a, stream);
     if (r != hipSuccess) return r;
   }
-  if (maxc > 0) {
+  if (prepare && maxc > 0) {
     const launch_result r = launch_prep(a, io_dtype, stream);
     if (r != hipSuccess) return r;
   }
-  return e->fn(a, stream);
+  return finish ? e->fn(a, stream) : hipSuccess;
 }
 
 }  // namespace ckda

@@ -87,8 +87,10 @@ bool fwd_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype);
 // Workspace bytes ckda_chunk_fwd needs for these sizes (0 for an empty call).
 size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t num_seqs,
                            int32_t chunk, int32_t io_dtype, bool packed);
-// Lays out the workspace in `a` and enqueues both passes.
-launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream);
+// Lays out the workspace in `a` and enqueues the transform pass (with the
+// chunk map of a packed batch) and/or the state pass.
+launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream,
+                         bool prepare, bool finish);
 // The passes (one translation unit each).
 bool prep_supported(int32_t chunk, int32_t dk, int32_t io_dtype);
 launch_result launch_prep(const FwdArgs& a, int32_t io_dtype, hipStream_t stream);

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 2
+#define CKDA_ABI_VERSION 3
 
 typedef enum {
   CKDA_OK = 0,
@@ -126,6 +126,28 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
                              const float* beta, const int32_t* cu_seqlens,
                              const float* h0, void* o, float* ht,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two passes of ckda_chunk_fwd as separate calls, for callers that time
+ * them, or that let the transform pass of one batch run ahead of the state
+ * pass of another.  ckda_chunk_fwd_prepare runs the transform pass and leaves
+ * every chunk's operands in `workspace`; ckda_chunk_fwd_finish runs the state
+ * pass from a workspace that a prepare call with the same descriptor and
+ * cu_seqlens filled (on the same stream, or otherwise ordered before it), and
+ * may run any number of times on it (each run recomputes o and ht from h0).
+ * Arguments mean what they mean for ckda_chunk_fwd; validation is the same for
+ * the arguments each call takes.  That the workspace was prepared for the same
+ * descriptor is a precondition, not checked.
+ */
+ckda_status_t ckda_chunk_fwd_prepare(const ckda_fwd_desc_t* desc, const void* q,
+                                     const void* k, const float* alpha,
+                                     const float* beta, const int32_t* cu_seqlens,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream);
+ckda_status_t ckda_chunk_fwd_finish(const ckda_fwd_desc_t* desc, const void* v,
+                                    const int32_t* cu_seqlens, const float* h0,
+                                    void* o, float* ht, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* 1 if ckda_chunk_fwd has a kernel for this descriptor's (chunk_size, dk, dv,
  * io_dtype), 0 if not (other fields are not inspected). */

@@ -33,7 +33,11 @@ This is used when every |Ft_r| lies in [2^-100, 2^10]: then no factor
 overflows and no quotient is formed by a zero (signs are exact).
 
 Irregular chunks (an exact zero gate, or gates so small that the running
-product leaves that range) are run token by token, which is exact.
+product leaves that range) form the same A, P and Kh from direct products of
+the gates instead of ratios: D(r<-j) built one gate at a time and Kh_j from
+the suffix product prod_{s>j} alpha_s, with no division (the kernel's
+direct path).  Both kinds of chunk then share X = (I + A)^{-1},
+U = X Diag(beta) V - W S_0 with W = X Diag(beta) Kt, O and S_C.
 
 Normalisation enters as row scales: k_hat = rk * k, q_hat = rq * q.
 """
@@ -48,23 +52,25 @@ def _l2scale(x, use, eps=1e-6):
     return 1.0 / np.sqrt((x * x).sum(-1) + eps)
 
 
-def _sequential_chunk(qc, kc, vc, ac, bc, rq, rk, S, scale, L):
-    o = np.zeros((L, vc.shape[1]))
-    for r in range(L):
-        kh = rk[r] * kc[r]
-        qh = rq[r] * qc[r]
-        S = ac[r][:, None] * S
-        w = S.T @ kh
-        S = S + bc[r] * np.outer(kh, vc[r] - w)
-        o[r] = scale * (S.T @ qh)
-    return o, S
+def _direct_products(ac):
+    """D[r, j] = prod_{j<s<=r} alpha_s (per channel) for j <= r, built one gate
+    at a time (no division); zero above the diagonal."""
+    C, dk = ac.shape
+    D = np.zeros((C, C, dk))
+    for j in range(C):
+        d = np.ones(dk)
+        D[j, j] = d
+        for r in range(j + 1, C):
+            d = d * ac[r]
+            D[r, j] = d
+    return D
 
 
 def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, force_irregular=False,
                paths=None):
     """One sequence, one head.  q,k,alpha [T,dk], v [T,dv], beta [T], S [dk,dv].
     Returns (o [T,dv], S_final).  `paths`, if a list, receives 'ratio' or
-    'sequential' per chunk."""
+    'direct' per chunk."""
     T, dk = q.shape
     dv = v.shape[1]
     o = np.zeros((T, dv))
@@ -82,29 +88,36 @@ def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, force_irregular=Fa
         rk = np.ones(C); rk[:L] = rk_all[c0:c0 + L]
 
         Ft = np.cumprod(ac, axis=0)
+        g = Ft[C - 1]
         mag = np.abs(Ft)
         regular = bool(np.all(np.isfinite(Ft)) and mag.min() >= LO and mag.max() <= HI)
-        if force_irregular or not regular:
-            oo, S = _sequential_chunk(qc, kc, vc, ac, bc, rq, rk, S, scale, L)
-            o[c0:c0 + L] = oo
-            if paths is not None:
-                paths.append("sequential")
-            continue
-        if paths is not None:
-            paths.append("ratio")
-        g = Ft[C - 1]
         Lk = kc * Ft
         Lq = qc * Ft
-        Rk = kc / Ft
-        A = np.tril((bc * rk)[:, None] * (Lk @ Rk.T) * rk[None, :], -1)
-        P = np.tril(Lq @ Rk.T)
+        if regular and not force_irregular:
+            if paths is not None:
+                paths.append("ratio")
+            Rk = kc / Ft
+            A = np.tril((bc * rk)[:, None] * (Lk @ Rk.T) * rk[None, :], -1)
+            P = np.tril(Lq @ Rk.T)
+            Kh = g * Rk                                   # Kh / rk
+        else:
+            if paths is not None:
+                paths.append("direct")
+            D = _direct_products(ac)
+            G = np.einsum("rjc,rc,jc->rj", D, kc, kc)
+            A = np.tril((bc * rk)[:, None] * G * rk[None, :], -1)
+            P = np.tril(np.einsum("rjc,rc,jc->rj", D, qc, kc))
+            suf = np.ones((C, dk))
+            for j in range(C - 2, -1, -1):
+                suf[j] = suf[j + 1] * ac[j + 1]
+            Kh = suf * kc                                 # Kh / rk
         X = np.linalg.inv(np.eye(C) + A)
         W = X @ ((bc * rk)[:, None] * Lk)
         Ubar = X @ (bc[:, None] * vc)
         U = Ubar - W @ S
         Ok = Lq @ S + P @ (rk[:, None] * U)
         o[c0:c0 + L] = (scale * rq[:, None] * Ok)[:L]
-        S = g[:, None] * S + (g * Rk).T @ (rk[:, None] * U)
+        S = g[:, None] * S + Kh.T @ (rk[:, None] * U)
     return o, S
 
 

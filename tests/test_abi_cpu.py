@@ -120,6 +120,23 @@ def test_fwd_workspace_validation():
     assert st == 1 and "workspace overlaps v" in msg
 
 
+def test_prepare_and_finish_validation():
+    lib = ck._load()
+    d = _desc()
+    st = lib.ckda_chunk_fwd_prepare(ctypes.byref(d), P["q"], None, P["alpha"], P["beta"], None,
+                                    P["ws"], WS_BYTES, None)
+    assert st == 1 and "must not be NULL" in lib.ckda_last_error().decode()
+    st = lib.ckda_chunk_fwd_finish(ctypes.byref(d), P["v"], None, P["h0"], None, P["ht"],
+                                   P["ws"], WS_BYTES, None)
+    assert st == 1 and "must not be NULL" in lib.ckda_last_error().decode()
+    st = lib.ckda_chunk_fwd_finish(ctypes.byref(d), P["v"], None, P["h0"], P["o"], P["ht"],
+                                   P["ws"], 64, None)
+    assert st == 1 and "needed" in lib.ckda_last_error().decode()
+    st = lib.ckda_chunk_fwd_prepare(ctypes.byref(d), P["q"], P["k"], P["alpha"], P["beta"], None,
+                                    P["q"], WS_BYTES, None)
+    assert st == 1 and "workspace overlaps q" in lib.ckda_last_error().decode()
+
+
 def test_fwd_unsupported_shape():
     st, msg = _fwd(_desc(dk=96, dv=96))
     assert st == 2 and "no chunked kernel" in msg

@@ -1,6 +1,6 @@
 """P8: the chunked factorisation used by the HIP forward, in fp64, equals the
 sequential oracle to rounding (~1e-12): the chunk-ratio form on regular
-chunks, the token-by-token path on chunks with exact zero or vanishing gates,
+chunks, the direct-product form on chunks with exact zero or vanishing gates,
 partial last chunks and every chunk size."""
 import numpy as np
 import pytest
@@ -55,15 +55,15 @@ def test_sign_changes_stay_on_ratio_form():
     assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
 
 
-def test_irregular_chunks_take_the_sequential_path():
+def test_irregular_chunks_take_the_direct_path():
     """Exact zeros and 1e-35 gates make chunks irregular; forcing every chunk
-    through the token-by-token path gives the same answer as the mix."""
+    through the direct-product form gives the same answer as the mix."""
     q, k, v, a, b, h0 = _case(7, 2, 96, 2, 8, 4, zero_frac=0.02, tiny=True)
     ro, rh = oracle.fwd(q, k, v, a, b, h0=h0)
     for force in (False, True):
         paths = []
         co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=32, force_irregular=force, paths=paths)
-        assert "sequential" in paths
+        assert "direct" in paths and (not force or set(paths) == {"direct"})
         assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
 
 

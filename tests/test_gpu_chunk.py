@@ -231,3 +231,30 @@ def test_decode_chain_equals_prefill():
                                            dev(c.beta[:, t]), st)))
     assert max_rel_err(np.stack(outs, 1), o) < TOL["bf16"]
     assert max_rel_err(host(st), ht) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,packed", [("bf16", 128, 64, False), ("f32", 32, 32, True)])
+def test_prepare_finish_equals_single_call(dtype, d, chunk, packed):
+    """The transform and state passes launched separately (prepare once, finish
+    twice on the same workspace) give bit-identical o and ht to ckda_chunk_fwd."""
+    announce("prepare/finish split %s d=%d C=%d packed=%s" % (dtype, d, chunk, packed))
+    if packed:
+        lens = [37, 0, 100, 64]
+        big = inputs.random_case(77, 1, sum(lens), 2, d, d, dtype=dtype, chunk=chunk)
+        h0 = (0.3 * np.random.default_rng(79).standard_normal((len(lens), 2, d, d))).astype(np.float32)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        c = inputs.Case(big.q, big.k, big.v, big.alpha, big.beta, h0, cu, dtype, chunk, True)
+    else:
+        c = inputs.random_case(78, 2, 3 * chunk + 11, 2, d, d, dtype=dtype, chunk=chunk,
+                               alpha="tanh", beta="2sig", h0_std=0.2)
+    o1, h1 = run_chunk(c)
+    cu = None if c.cu_seqlens is None else torch.from_numpy(c.cu_seqlens).to(DEV)
+    plan = ck.ChunkFwdPlan(dev(c.q, dtype), dev(c.k, dtype), dev(c.v, dtype), dev(c.alpha),
+                           dev(c.beta), h0=None if c.h0 is None else dev(c.h0), cu_seqlens=cu,
+                           chunk_size=chunk, use_qk_l2norm=c.l2norm)
+    plan.prepare()
+    o2, h2 = (host(t) for t in plan.finish())
+    o3, h3 = (host(t) for t in plan.finish())
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+    assert np.array_equal(o2, o3) and np.array_equal(h2, h3)
