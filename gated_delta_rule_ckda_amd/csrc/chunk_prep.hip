@@ -75,9 +75,8 @@ struct PrepCfg {
   static constexpr int NCG = DK / CPT;               // lanes holding channels
   static constexpr int ES = static_cast<int>(sizeof(T));
   static constexpr int IOES = static_cast<int>(sizeof(typename IO::storage));
-  static constexpr int PAD = 16 / ES;
-  static constexpr int LDK = DK + PAD;
-  static constexpr int LDC = C + PAD;
+  static constexpr int LDK = frag_stride(DK, ES);
+  static constexpr int LDC = frag_stride(C, ES);
   static constexpr int LDA = 20;                     // fp32 16x16 block stride (conflict-free)
   static constexpr int BLKF = 16 * LDA;              // floats per 16x16 block
   static constexpr int NBA = NB * (NB - 1) / 2;      // strictly lower blocks of A

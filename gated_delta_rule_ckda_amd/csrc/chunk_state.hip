@@ -34,16 +34,15 @@ struct StateCfg {
   static constexpr int C = C_, DK = DK_, DV = DV_, DVT = DVT_;
   static constexpr int NSPLIT = DV / DVT;
   static constexpr int NSW = DVT / 16;               // state waves
-  static constexpr int NLW = 4;                      // loader waves
+  static constexpr int NLW = 8;                      // loader waves
   static constexpr int NT = 64 * (NSW + NLW);
   static constexpr int NLT = 64 * NLW;               // loader threads
   static constexpr int NB = C / 16;
   static constexpr int NMC = DK / 16;
   static constexpr int ES = static_cast<int>(sizeof(T));
   static constexpr int IOES = static_cast<int>(sizeof(typename IO::storage));
-  static constexpr int PAD = 16 / ES;
-  static constexpr int LDK = DK + PAD;
-  static constexpr int LDC = C + PAD;
+  static constexpr int LDK = frag_stride(DK, ES);
+  static constexpr int LDC = frag_stride(C, ES);
   static constexpr int KS = Op::KS;                  // K per register fragment
   static constexpr int NFK = (DK + KS - 1) / KS;     // fragments over dk
   static constexpr int NFC = (C + KS - 1) / KS;      // fragments over the chunk rows
