@@ -85,6 +85,9 @@ class Oracle:
         lib.ckda_oracle_l2norm.restype = ctypes.c_int32
         lib.ckda_oracle_l2norm.argtypes = [ctypes.c_int64, ctypes.c_int32, dp, dp,
                                            ctypes.c_double]
+        lib.ckda_oracle_gates.restype = ctypes.c_int32
+        lib.ckda_oracle_gates.argtypes = [ctypes.c_int64, dp, ctypes.c_int64, dp,
+                                          ctypes.c_int32, dp, dp]
         lib.ckda_oracle_set_num_threads.restype = None
         lib.ckda_oracle_set_num_threads.argtypes = [ctypes.c_int32]
         lib.ckda_oracle_max_threads.restype = ctypes.c_int32
@@ -107,6 +110,19 @@ class Oracle:
         if rc != 0:
             raise ValueError("ckda_oracle_l2norm failed with code %d" % rc)
         return y
+
+    def gates(self, a, b, ckda_range=True):
+        """Gates from logits: alpha = 2 sigmoid(a) - 1, beta = 2 sigmoid(b) in
+        the CKDA range, sigmoid for both in the KDA range.  fp64, shapes of a
+        and b."""
+        a, b = _f64(a), _f64(b)
+        alpha = np.empty_like(a)
+        beta = np.empty_like(b)
+        rc = self.lib.ckda_oracle_gates(a.size, _ptr(a), b.size, _ptr(b),
+                                        int(bool(ckda_range)), _ptr(alpha), _ptr(beta))
+        if rc != 0:
+            raise ValueError("ckda_oracle_gates failed with code %d" % rc)
+        return alpha, beta
 
     def fwd(self, q, k, v, alpha, beta, h0=None, seq_start=None, use_l2norm=True,
             scale=1.0, eps=EPS):
@@ -181,6 +197,10 @@ def max_threads() -> int:
 
 def l2norm(x, eps: float = EPS) -> np.ndarray:
     return default().l2norm(x, eps)
+
+
+def gates(*args, **kwargs):
+    return default().gates(*args, **kwargs)
 
 
 def fwd(*args, **kwargs):

@@ -87,6 +87,29 @@ int32_t ckda_oracle_l2norm(int64_t rows, int32_t d, const double* x, double* y,
   return ORACLE_OK;
 }
 
+/* Logistic sigmoid 1 / (1 + e^-x). */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/*
+ * Gates from pre-activation logits (picx.dev summary, section "CKDA
+ * Definition": the implementation forms beta = 2 sigmoid(b) and the signed
+ * gate 2 sigmoid(a) - 1).  ckda_range = 0 (KDA) takes the sigmoid itself for
+ * both, the reading that keeps alpha in (0,1) and beta in (0,1).  alpha and a
+ * hold n_alpha values, beta and b n_beta.
+ */
+int32_t ckda_oracle_gates(int64_t n_alpha, const double* a, int64_t n_beta,
+                          const double* b, int32_t ckda_range, double* alpha,
+                          double* beta) {
+  if (n_alpha < 0 || n_beta < 0) return ORACLE_BAD_ARG;
+  if ((n_alpha > 0 && (!a || !alpha)) || (n_beta > 0 && (!b || !beta)))
+    return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < n_alpha; ++i)
+    alpha[i] = ckda_range ? 2.0 * sigmoid(a[i]) - 1.0 : sigmoid(a[i]);
+  for (int64_t i = 0; i < n_beta; ++i)
+    beta[i] = ckda_range ? 2.0 * sigmoid(b[i]) : sigmoid(b[i]);
+  return ORACLE_OK;
+}
+
 /* One sequence, one head: runs tokens [t0, t1) in order on the state S. */
 static void run_head(int64_t t0, int64_t t1, int32_t h, int32_t H, int32_t dk,
                      int32_t dv, const double* q, const double* k,

@@ -427,6 +427,47 @@ def pin_thread_count_does_not_change_results(orc):
     assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
 
 
+# ---------------------------------------------------------------- gate activation
+def pin_gate_activation_closed_forms(orc):
+    """picx.dev summary, 'CKDA Definition': beta = 2 sigmoid(b) and the signed
+    gate 2 sigmoid(a) - 1.  Checked against closed forms that do not share
+    the oracle's expression: 2 sigmoid(a) - 1 = tanh(a/2) and
+    2 sigmoid(b) = 1 + tanh(b/2) (numpy's tanh); the fixed points alpha(0) = 0
+    and beta(0) = 1; odd symmetry of alpha; beta(b) + beta(-b) = 2; the ranges
+    [-1,1] and [0,2] with their limits.  KDA range (the plain sigmoid, a
+    reading): (1 + tanh(a/2)) / 2 and scipy's expit."""
+    from scipy.special import expit
+    a = np.concatenate([np.linspace(-30, 30, 601), [0.0, 1e-9, -1e-9, 50.0, -50.0]])
+    b = np.concatenate([np.linspace(-20, 20, 401), [0.0, 60.0, -60.0]])
+    al, be = orc.gates(a, b, True)
+    np.testing.assert_allclose(al, np.tanh(a / 2), rtol=0, atol=4e-16)
+    np.testing.assert_allclose(be, 1 + np.tanh(b / 2), rtol=0, atol=8e-16)
+    assert al[a == 0.0].tolist() == [0.0] * int((a == 0.0).sum())
+    assert be[b == 0.0].tolist() == [1.0] * int((b == 0.0).sum())
+    al_neg, be_neg = orc.gates(-a, -b, True)
+    np.testing.assert_allclose(al_neg, -al, rtol=0, atol=4e-16)
+    np.testing.assert_allclose(be + be_neg, 2.0, rtol=0, atol=8e-16)
+    assert al.min() >= -1 and al.max() <= 1 and be.min() >= 0 and be.max() <= 2
+    assert abs(al[a == 50.0][0] - 1) < 1e-15 and abs(al[a == -50.0][0] + 1) < 1e-15
+    assert abs(be[b == 60.0][0] - 2) < 1e-15 and be[b == -60.0][0] < 1e-25
+    ak, bk = orc.gates(a, b, False)
+    np.testing.assert_allclose(ak, (1 + np.tanh(a / 2)) / 2, rtol=1e-14, atol=2e-16)
+    np.testing.assert_allclose(ak, expit(a), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(bk, expit(b), rtol=1e-14, atol=0)
+    assert ak.min() > 0 and ak.max() <= 1
+
+
+def pin_gate_activation_feeds_recurrence(orc):
+    """The activated gates drive the recurrence as gates given directly: one
+    token with S_0 = I and beta logit -> -inf (beta = 0) leaves
+    S_1 = Diag(alpha) with alpha = tanh(a/2)."""
+    a = np.array([-3.0, -0.5, 0.0, 0.25, 4.0])
+    al, be = orc.gates(a, np.array([-800.0]), True)
+    assert be[0] == 0.0
+    A = _transition(orc, al, be[0], np.ones(5) / np.sqrt(5.0))
+    np.testing.assert_allclose(A, np.diag(np.tanh(a / 2)), rtol=0, atol=1e-15)
+
+
 # ---------------------------------------------------------------- test wrappers
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
@@ -456,6 +497,11 @@ MUTANTS = {
     "scale_dropped": ("ot[j] *= scale;", "ot[j] *= 1.0;"),
     "norm_without_sqrt": ("const double n = sqrt(ss + eps);", "const double n = ss + eps;"),
     "h0_ignored": ("if (h0)\n", "if (0)\n"),
+    "ckda_alpha_unshifted": ("2.0 * sigmoid(a[i]) - 1.0", "sigmoid(a[i])"),
+    "ckda_beta_undoubled": ("2.0 * sigmoid(b[i])", "sigmoid(b[i])"),
+    "sigmoid_sign_flipped": ("exp(-x)", "exp(x)"),
+    "gate_ranges_swapped": ("ckda_range ? 2.0 * sigmoid(a[i]) - 1.0 : sigmoid(a[i])",
+                            "ckda_range ? sigmoid(a[i]) : 2.0 * sigmoid(a[i]) - 1.0"),
     "gate_after_erase": (
         "    /* 1. Diag(alpha) S: channel c of the key space scales row c. */\n"
         "    for (int32_t c = 0; c < dk; ++c)\n"
