@@ -11,8 +11,8 @@ throughput (tokens/s), the roofline position of each pass's kernel timed on
 its own (HBM-bound: algorithmic bytes / kernel time against 8 TB/s; the
 dominant one is the headline roofline), the
 oracle's CPU throughput on a bounded sample, and extra lines of context: the
-KDA-range arm (throughput ratio), the packed varlen prefill and the decode
-step.  Inputs are synthetic (seeded), shaped like the method's workloads.
+KDA-range arm (throughput ratio), the same layer with bf16 gate logits
+activated in-kernel, the packed varlen prefill and the decode step.  Inputs are synthetic (seeded), shaped like the method's workloads.
 """
 import argparse
 import hashlib
@@ -45,12 +45,12 @@ def chunk_flops(C, dk, dv):
             + 6 * C * dk * dv)
 
 
-def fwd_bytes(B, T, H, dk, dv, io_bytes, nseq, h0):
+def fwd_bytes(B, T, H, dk, dv, io_bytes, nseq, h0, gate_bytes=4):
     """Algorithmic HBM bytes of the whole forward: every input read once,
     every output written once."""
     tok = B * T
     b = tok * H * (2 * dk + dv) * io_bytes      # q, k, v
-    b += tok * H * dk * 4 + tok * H * 4         # alpha, beta
+    b += tok * H * (dk + 1) * gate_bytes        # alpha, beta (or their logits)
     b += tok * H * dv * io_bytes                # o
     b += nseq * H * dk * dv * 4                 # ht
     if h0:
@@ -64,7 +64,7 @@ def block_bytes(C, dk, es):
     return -(-((2 * C * C + 3 * C * dk) * es + 4 * dk) // 256) * 256
 
 
-def pass_bytes(B, T, H, dk, dv, C, io_bytes, nseq, h0):
+def pass_bytes(B, T, H, dk, dv, C, io_bytes, nseq, h0, gate_bytes=4):
     """Algorithmic bytes per launch of each pass: its inputs read once and its
     outputs written once.  The transform pass reads q, k, alpha, beta and
     writes one block per chunk-head; the state pass reads the blocks, v (and
@@ -72,7 +72,7 @@ def pass_bytes(B, T, H, dk, dv, C, io_bytes, nseq, h0):
     tok = B * T
     nblk = B * (-(-T // C)) * H
     blocks = nblk * block_bytes(C, dk, io_bytes)
-    prep = tok * H * (2 * dk * io_bytes + dk * 4 + 4) + blocks
+    prep = tok * H * (2 * dk * io_bytes + (dk + 1) * gate_bytes) + blocks
     state = blocks + tok * H * dv * io_bytes * 2 + nseq * H * dk * dv * 4 * (2 if h0 else 1)
     return {"prep": prep, "state": state}
 
@@ -133,11 +133,11 @@ def fwd_plan(case, gate):
     import gated_delta_rule_ckda_amd as ck
     dt = case.dtype
     q, k, v = to_dev(case.q, dt), to_dev(case.k, dt), to_dev(case.v, dt)
-    a, b = to_dev(case.alpha, "f32"), to_dev(case.beta, "f32")
+    a, b = to_dev(case.alpha, case.gate_dtype), to_dev(case.beta, case.gate_dtype)
     h0 = None if case.h0 is None else to_dev(case.h0, "f32")
     cu = None if case.cu_seqlens is None else torch.from_numpy(case.cu_seqlens).to("cuda:0")
     return ck.ChunkFwdPlan(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
-                           use_qk_l2norm=case.l2norm, gate=gate)
+                           use_qk_l2norm=case.l2norm, gate=gate, gates=case.gates)
 
 
 def bench_fwd(case, steps, warmup, gate, passes=False):
@@ -151,7 +151,7 @@ def bench_fwd(case, steps, warmup, gate, passes=False):
     def step():
         ck.chunk_fwd(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
                      use_qk_l2norm=case.l2norm, gate=gate, out=plan.o, final_state=plan.ht,
-                     workspace=plan.ws)
+                     workspace=plan.ws, gates=case.gates)
 
     ms, wall_ms = time_launches(step, steps, warmup)
     per = {}
@@ -299,6 +299,17 @@ def main():
                             "ms_per_step": round(ms_kda, 4),
                             "ckda_over_kda": round(ms_kda / ms, 4),
                             "pages_context": "CKDA keeps ~96-97% of KDA kernel throughput on H100"}
+        lg = inputs.lm_layer_logits(arm="ckda", gate_dtype="bf16")
+        ms_lg, _, per_lg = bench_fwd(lg, args.steps, args.warmup, "ckda", passes=True)
+        del lg
+        lg_prep = pass_bytes(B, T, H, dk, dv, C, 2, B, False, gate_bytes=2)["prep"]
+        out["gate_logits"] = {
+            "workload": "LM layer as above, gates given as bf16 logits a, b and activated in "
+                        "the transform pass (alpha = 2 sigmoid(a) - 1, beta = 2 sigmoid(b))",
+            "tokens_per_s": round(tokens / (ms_lg / 1000.0), 1), "ms_per_step": round(ms_lg, 4),
+            "prep_ms": round(per_lg["prep"], 4), "state_ms": round(per_lg["state"], 4),
+            "prep_algorithmic_bytes": lg_prep,
+            "prep_frac": round(lg_prep / (per_lg["prep"] / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
         vl = inputs.varlen()
         ms_vl, _, _ = bench_fwd(vl, max(5, args.steps // 3), 2, "ckda")
         vl_tok = int(vl.cu_seqlens[-1])

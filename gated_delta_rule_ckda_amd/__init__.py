@@ -13,7 +13,7 @@ import threading
 
 __all__ = ["chunk_fwd", "recurrent_step", "l2norm_debug", "fwd_supported",
            "library_path", "abi_version", "CkdaError", "BF16", "F32", "GATE_KDA",
-           "GATE_CKDA"]
+           "GATE_CKDA", "GATES_F32", "GATES_LOGITS_F32", "GATES_LOGITS_BF16", "ChunkFwdPlan"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libckda.so")
@@ -22,6 +22,7 @@ _lib = None
 
 BF16, F32 = 0, 1
 GATE_KDA, GATE_CKDA = 0, 1
+GATES_F32, GATES_LOGITS_F32, GATES_LOGITS_BF16 = 0, 1, 2
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
 
 
@@ -36,7 +37,7 @@ class FwdDesc(ctypes.Structure):
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("gate_range", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("gate_input", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -68,8 +69,8 @@ def _load():
         lib.ckda_fwd_supported.restype = i32
         lib.ckda_fwd_supported.argtypes = [ctypes.POINTER(FwdDesc)]
         lib.ckda_recurrent_step.restype = i32
-        lib.ckda_recurrent_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
-                                            vp, vp, vp, vp, vp, vp]
+        lib.ckda_recurrent_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, vp]
         lib.ckda_l2norm_debug.restype = i32
         lib.ckda_l2norm_debug.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp]
         lib.ckda_status_string.restype = ctypes.c_char_p
@@ -118,12 +119,30 @@ def _gate_code(gate):
     raise ValueError("gate must be 'ckda' or 'kda'")
 
 
+def _gate_input(gates, alpha, beta):
+    """ckda_gate_input_t for gates='values' (float32 gates) or gates='logits'
+    (float32 or bfloat16 logits, activated in the kernels)."""
+    import torch
+    _require(alpha.dtype == beta.dtype, "alpha and beta must share a dtype")
+    if gates == "values":
+        _require(alpha.dtype == torch.float32, "gate values must be float32")
+        return GATES_F32
+    if gates == "logits":
+        if alpha.dtype == torch.float32:
+            return GATES_LOGITS_F32
+        if alpha.dtype == torch.bfloat16:
+            return GATES_LOGITS_BF16
+        raise ValueError("gate logits must be float32 or bfloat16")
+    raise ValueError("gates must be 'values' or 'logits'")
+
+
 def _require(cond, msg):
     if not cond:
         raise ValueError(msg)
 
 
-def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens):
+def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens,
+               gate_input=GATES_F32):
     if cu_seqlens is not None:
         B, T = 1, q.shape[-3] if q.dim() == 3 else q.shape[1]
         N = cu_seqlens.numel() - 1
@@ -131,11 +150,11 @@ def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqle
         B, T = q.shape[0], q.shape[1]
         N = B
     return FwdDesc(B, T, H, dk, dv, N, chunk_size, _dtype_code(q), _gate_code(gate),
-                   int(bool(use_qk_l2norm)), float(scale))
+                   int(bool(use_qk_l2norm)), float(scale), gate_input)
 
 
 def fwd_supported(chunk_size, dk, dv, dtype) -> bool:
-    d = FwdDesc(1, 1, 1, dk, dv, 1, chunk_size, dtype, GATE_CKDA, 1, 1.0)
+    d = FwdDesc(1, 1, 1, dk, dv, 1, chunk_size, dtype, GATE_CKDA, 1, 1.0, GATES_F32)
     return bool(_load().ckda_fwd_supported(ctypes.byref(d)))
 
 
@@ -146,9 +165,11 @@ def chunk_fwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
 
 def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
               use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
-              out=None, final_state=None, workspace=None, stream=None):
+              out=None, final_state=None, workspace=None, stream=None, gates="values"):
     """Chunked prefill.  Dense: q,k,alpha [B,T,H,dk], v [B,T,H,dv], beta [B,T,H].
     Packed (cu_seqlens int32 [N+1]): leading [1,T,...] or [T,...].
+    gates='values': alpha, beta are float32 gates; gates='logits': they are
+    float32 or bfloat16 logits that the kernels activate.
     `workspace`: optional uint8 device tensor of at least
     chunk_fwd_workspace_size() bytes (allocated per call when omitted).
     Returns (o, ht) with ht [N,H,dk,dv] float32 (None if not requested)."""
@@ -158,12 +179,11 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
         _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
     _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
-    _require(alpha.dtype == torch.float32 and beta.dtype == torch.float32,
-             "alpha and beta must be float32")
+    gi = _gate_input(gates, alpha, beta)
     if cu_seqlens is not None:
         _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda,
                  "cu_seqlens must be an int32 device tensor")
-    desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens)
+    desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens, gi)
     _require(q.numel() == desc.B * desc.T * H * dk, "q has the wrong number of elements")
     _require(k.numel() == q.numel() and alpha.numel() == q.numel(), "k/alpha must match q")
     _require(v.numel() == desc.B * desc.T * H * dv, "v has the wrong number of elements")
@@ -194,11 +214,12 @@ class ChunkFwdPlan:
 
     def __init__(self, q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
                  use_qk_l2norm=True, gate="ckda", scale=1.0, out=None, final_state=None,
-                 stream=None):
+                 stream=None, gates="values"):
         import torch
         self.lib = _load()
         H, dk, dv = q.shape[-2], q.shape[-1], v.shape[-1]
-        self.desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens)
+        self.desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale,
+                               cu_seqlens, _gate_input(gates, alpha, beta))
         self.args = (q, k, v, alpha, beta, h0, cu_seqlens)
         self.o = torch.empty_like(v) if out is None else out
         self.ht = (torch.empty((self.desc.num_seqs, H, dk, dv), device=q.device,
@@ -223,10 +244,10 @@ class ChunkFwdPlan:
 
 
 def recurrent_step(q, k, v, alpha, beta, state, *, use_qk_l2norm=True, gate="ckda",
-                   scale=1.0, out=None, new_state=None, stream=None):
+                   scale=1.0, out=None, new_state=None, stream=None, gates="values"):
     """One decode token per sequence: q,k,alpha [N,H,dk], v [N,H,dv], beta [N,H],
     state [N,H,dk,dv] float32, updated in place unless new_state is given.
-    Returns o [N,H,dv]."""
+    `gates` as for chunk_fwd.  Returns o [N,H,dv]."""
     import torch
     lib = _load()
     N, H, dk = q.shape
@@ -235,13 +256,13 @@ def recurrent_step(q, k, v, alpha, beta, state, *, use_qk_l2norm=True, gate="ckd
                     ("state", state)):
         _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
     _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
-    _require(alpha.dtype == torch.float32 and beta.dtype == torch.float32
-             and state.dtype == torch.float32, "alpha, beta, state must be float32")
+    gi = _gate_input(gates, alpha, beta)
+    _require(state.dtype == torch.float32, "state must be float32")
     _require(k.shape == q.shape and alpha.shape == q.shape and v.shape == (N, H, dv)
              and beta.shape == (N, H) and state.shape == (N, H, dk, dv), "shape mismatch")
     o = torch.empty_like(v) if out is None else out
     dst = state if new_state is None else new_state
-    _check(lib.ckda_recurrent_step(N, H, dk, dv, _dtype_code(q), _gate_code(gate),
+    _check(lib.ckda_recurrent_step(N, H, dk, dv, _dtype_code(q), _gate_code(gate), gi,
                                    int(bool(use_qk_l2norm)), float(scale), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(dst),
                                    _ptr(o), _stream(stream)))

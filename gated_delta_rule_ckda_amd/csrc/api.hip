@@ -46,6 +46,11 @@ bool overlap(const Range& a, const Range& b) {
 
 int64_t elem_bytes(int32_t dtype) { return dtype == CKDA_DTYPE_BF16 ? 2 : 4; }
 
+static_assert(CKDA_GATES_F32 == 0 && CKDA_GATES_LOGITS_F32 == 1 && CKDA_GATES_LOGITS_BF16 == 2,
+              "the kernels index their variants by ckda_gate_input_t");
+bool valid_gate_input(int32_t g) { return g >= CKDA_GATES_F32 && g <= CKDA_GATES_LOGITS_BF16; }
+int64_t gate_bytes(int32_t g) { return g == CKDA_GATES_LOGITS_BF16 ? 2 : 4; }
+
 ckda_status_t from_hip(hipError_t e) {
   if (e == hipSuccess) return ok();
   return fail(CKDA_ERR_HIP, "HIP launch error %d: %s", static_cast<int>(e), hipGetErrorString(e));
@@ -94,7 +99,7 @@ constexpr int kPrepare = 1, kFinish = 2;
 // needs v and o (and reads h0, writes ht).  Pointers a pass does not use must
 // be NULL.
 ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
-                           const void* v, const float* alpha, const float* beta,
+                           const void* v, const void* alpha, const void* beta,
                            const int32_t* cu_seqlens, const float* h0, const void* o,
                            const float* ht, const void* workspace, size_t workspace_bytes,
                            int passes) {
@@ -107,6 +112,9 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
     return fail(CKDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not a ckda_dtype_t", d->io_dtype);
   if (d->gate_range != CKDA_GATE_KDA && d->gate_range != CKDA_GATE_CKDA)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_range %d is not a ckda_gate_t", d->gate_range);
+  if (!valid_gate_input(d->gate_input))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_input %d is not a ckda_gate_input_t",
+                d->gate_input);
   if (d->use_qk_l2norm != 0 && d->use_qk_l2norm != 1)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
   if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
@@ -132,13 +140,14 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
       return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
 
   const int64_t eb = elem_bytes(d->io_dtype);
+  const int64_t gb = gate_bytes(d->gate_input);
   const int64_t state_bytes = static_cast<int64_t>(d->num_seqs) * d->H * d->dk * d->dv * 4;
   const Range ro = range("o", o, o ? tokens * d->H * d->dv * eb : 0);
   const Range ins[] = {range("q", q, q ? tokens * d->H * d->dk * eb : 0),
                        range("k", k, k ? tokens * d->H * d->dk * eb : 0),
                        range("v", v, v ? tokens * d->H * d->dv * eb : 0),
-                       range("alpha", alpha, alpha ? tokens * d->H * d->dk * 4 : 0),
-                       range("beta", beta, beta ? tokens * d->H * 4 : 0),
+                       range("alpha", alpha, alpha ? tokens * d->H * d->dk * gb : 0),
+                       range("beta", beta, beta ? tokens * d->H * gb : 0),
                        range("h0", h0, h0 ? state_bytes : 0),
                        range("ht", ht, ht ? state_bytes : 0),
                        range("cu_seqlens", cu_seqlens,
@@ -173,7 +182,7 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
 }
 
 ckda_status_t run_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k, const void* v,
-                      const float* alpha, const float* beta, const int32_t* cu_seqlens,
+                      const void* alpha, const void* beta, const int32_t* cu_seqlens,
                       const float* h0, void* o, float* ht, void* workspace, size_t workspace_bytes,
                       void* stream, int passes) {
   const ckda_status_t st = validate_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht,
@@ -181,8 +190,8 @@ ckda_status_t run_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
   if (st != CKDA_OK) return st;
   if (d->num_seqs == 0) return ok();
   ckda::FwdArgs a{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
-                  d->use_qk_l2norm, d->gate_range, d->scale, q, k, v, alpha, beta,
-                  cu_seqlens, h0, o, ht, nullptr, nullptr, nullptr, 0, 0, 0};
+                  d->use_qk_l2norm, d->gate_range, d->gate_input, d->scale, q, k, v, alpha, beta,
+                  cu_seqlens, h0, o, ht, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
   return from_hip(ckda::launch_fwd(a, d->io_dtype, workspace, static_cast<hipStream_t>(stream),
                                    (passes & kPrepare) != 0, (passes & kFinish) != 0));
 }
@@ -192,7 +201,7 @@ ckda_status_t run_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
 extern "C" {
 
 ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
-                             const void* v, const float* alpha, const float* beta,
+                             const void* v, const void* alpha, const void* beta,
                              const int32_t* cu_seqlens, const float* h0, void* o,
                              float* ht, void* workspace, size_t workspace_bytes, void* stream) {
   return run_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht, workspace, workspace_bytes,
@@ -200,7 +209,7 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void
 }
 
 ckda_status_t ckda_chunk_fwd_prepare(const ckda_fwd_desc_t* d, const void* q, const void* k,
-                                     const float* alpha, const float* beta,
+                                     const void* alpha, const void* beta,
                                      const int32_t* cu_seqlens, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   return run_fwd(d, q, k, nullptr, alpha, beta, cu_seqlens, nullptr, nullptr, nullptr, workspace,
@@ -216,9 +225,10 @@ ckda_status_t ckda_chunk_fwd_finish(const ckda_fwd_desc_t* d, const void* v,
 }
 
 ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
-                                  int32_t io_dtype, int32_t gate_range, int32_t use_qk_l2norm,
-                                  float scale, const void* q, const void* k, const void* v,
-                                  const float* alpha, const float* beta, const float* h0,
+                                  int32_t io_dtype, int32_t gate_range, int32_t gate_input,
+                                  int32_t use_qk_l2norm, float scale, const void* q,
+                                  const void* k, const void* v, const void* alpha,
+                                  const void* beta, const float* h0,
                                   float* ht, void* o, void* stream) {
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "bad size: N=%d H=%d dk=%d dv=%d", N, H, dk, dv);
@@ -226,6 +236,8 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
     return fail(CKDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not a ckda_dtype_t", io_dtype);
   if (gate_range != CKDA_GATE_KDA && gate_range != CKDA_GATE_CKDA)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_range %d is not a ckda_gate_t", gate_range);
+  if (!valid_gate_input(gate_input))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_input %d is not a ckda_gate_input_t", gate_input);
   if (use_qk_l2norm != 0 && use_qk_l2norm != 1)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
   if (N > 0 && (!q || !k || !v || !alpha || !beta || !h0 || !ht || !o))
@@ -237,12 +249,13 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
       return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
   const int64_t nh = static_cast<int64_t>(N) * H;
   const int64_t eb = elem_bytes(io_dtype);
+  const int64_t gb = gate_bytes(gate_input);
   const int64_t sb = nh * dk * dv * 4;
   const Range ro = range("o", o, nh * dv * eb);
   const Range rht = range("ht", ht, sb);
   const Range ins[] = {range("q", q, nh * dk * eb), range("k", k, nh * dk * eb),
-                       range("v", v, nh * dv * eb), range("alpha", alpha, nh * dk * 4),
-                       range("beta", beta, nh * 4), range("h0", h0, sb)};
+                       range("v", v, nh * dv * eb), range("alpha", alpha, nh * dk * gb),
+                       range("beta", beta, nh * gb), range("h0", h0, sb)};
   for (const Range& r : ins)
     if (overlap(ro, r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "o overlaps %s", r.name);
   if (overlap(ro, rht)) return fail(CKDA_ERR_INVALID_ARGUMENT, "o overlaps ht");
@@ -253,7 +266,8 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
   if (!ckda::step_supported(dk, dv))
     return fail(CKDA_ERR_UNSUPPORTED, "no decode kernel for dk=%d dv=%d", dk, dv);
   if (nh == 0) return ok();
-  ckda::StepArgs a{N, H, dk, dv, use_qk_l2norm, scale, q, k, v, alpha, beta, h0, ht, o};
+  ckda::StepArgs a{N, H, dk, dv, use_qk_l2norm, gate_range, gate_input, scale, q, k, v,
+                   alpha, beta, h0, ht, o};
   return from_hip(ckda::launch_step(a, io_dtype, static_cast<hipStream_t>(stream)));
 }
 

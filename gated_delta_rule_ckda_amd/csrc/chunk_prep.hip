@@ -26,8 +26,14 @@
 //   Lk = k . Ft (= Kt / rk),  Lq = q . Ft,  Rk = k / Ft,  Kh = rk g . Rk,
 //   A = tril(Diag(beta rk) Lk Rk^T Diag(rk), -1),  P = tril(Diag(rq) Lq Rk^T Diag(rk))
 // run on MFMA.  Other chunks (exact zero gates, products that underflow the
-// range, non-finite values) form A, P and Kh from direct products of the
-// gates instead: exact, slower, absent from realistic gate distributions.
+// range, non-finite values) are flagged and left to a second, short launch
+// that forms A, P and Kh from direct products of the gates (staged in LDS):
+// exact, slower, absent from realistic gate distributions.  Keeping that
+// path out of the MFMA kernel keeps the kernel's registers to what the
+// regular chunks need.
+//
+// Gates arrive as float32 values or as logits (float32 or bf16) activated on
+// load (ckda_internal.h).
 //
 // q and k enter raw; the in-op L2 normalisation (dormouse review "RoPE into
 // the KDA q/k path", section 2) is applied as the row scales rq, rk above.
@@ -35,7 +41,7 @@
 // Phases (eight waves; wave w owns rows w*C/8 .. in the element-wise phases):
 //   1  loads, running products within the wave's rows, row norms
 //   2  chunk-level products Ft, regularity vote, operands Lk, Lq, Rk; Qt', g out
-//   3  A and P on MFMA (or the direct path); P' out
+//   3  A and P on MFMA (the direct kernel: from direct products); P' out
 //   4  Kt'^T to LDS, Kh'^T out; 16x16 diagonal blocks of X by forward substitution
 //   5  off-diagonal blocks X_IJ = -X_II sum_{J<=M<I} A_IM X_MJ on fp32 MFMA
 //   6  X' out, -W = -X Kt' on MFMA, out
@@ -47,6 +53,7 @@ namespace ckda {
 namespace {
 
 constexpr float kRegularMin = 0x1p-100f;
+constexpr int64_t kDirectGrid = 256;  // workgroups of the direct kernel (one per CU)
 constexpr float kRegularMax = 0x1p+10f;
 
 // N consecutive logical entries start .. start+N-1 of a row of length K in
@@ -102,11 +109,15 @@ struct PrepCfg {
   static constexpr int O_BETA = O_RK2 + C * 4;                          // beta [C]
   static constexpr int O_FLAG = O_BETA + C * 4;                         // regularity votes [NW]
   static constexpr int LDS_BYTES = align16(O_FLAG + NW * 4);
+  // direct path staging, inside the operand region it leaves unused
+  static constexpr int O_DGATE = 0;                                     // gates [C][DK] fp32
+  static constexpr int O_DROW = C * DK * 4;                             // q or k rows [C][DK]
 
   static_assert(C % 16 == 0 && DK % 16 == 0 && C <= 64 && DK <= 128, "tile sizes");
   static_assert(NB <= NW && RPW >= 2 && (RPW & (RPW - 1)) == 0 && RPW <= 8, "row split");
   static_assert(DG * C <= NT && DK % DG == 0 && (DG & (DG - 1)) == 0 && DG <= 64, "direct path");
   static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+  static_assert(O_DROW + C * DK * IOES <= O_A, "direct path staging fits the operand region");
 };
 
 template <class Cfg>
@@ -128,63 +139,170 @@ __device__ __forceinline__ void lower_block(int idx, int& I, int& J) {
   J = idx;
 }
 
-// Direct products for a chunk that is not regular: column j of A and P from
-// D(r<-j) built one gate at a time (G threads per column, DCH channels each).
-// Row r of the chunk starts at element base + r * rowstride of q, k, alpha.
-template <class Cfg>
-__device__ __noinline__ void direct_ap(const void* gq, const void* gk, const float* galpha,
-                                       int64_t base, int rowstride, int L, float scale,
-                                       typename Cfg::T* gP, unsigned char* smem, int tid) {
-  using IO = typename Cfg::IO;
-  using ST = typename IO::storage;
-  using Op = typename Cfg::Op;
-  constexpr int C = Cfg::C, DG = Cfg::DG, DCH = Cfg::DCH, LDA = Cfg::LDA;
-  const float* srq = reinterpret_cast<const float*>(smem + Cfg::O_RQ);
-  const float* srk = reinterpret_cast<const float*>(smem + Cfg::O_RK2);
-  const float* sbeta = reinterpret_cast<const float*>(smem + Cfg::O_BETA);
-  const ST* q = static_cast<const ST*>(gq);
-  const ST* k = static_cast<const ST*>(gk);
-  if (tid >= DG * C) return;
-  const int j = tid / DG, cg = tid % DG, c0 = cg * DCH;
-  const int J = j / 16;
-  float d[DCH], kj[DCH];
+// Chunk rows 0..C-1 of a q/k/alpha-shaped tensor (row r at element
+// base + r * rowstride) copied into LDS as [C][DK], with 16-byte loads that
+// are all issued before the first store.  Gates are widened (and activated)
+// to float32 and rows past L read as 1; q and k rows keep their io type and
+// rows past L read as 0.
+template <class Cfg, class G>
+__device__ __forceinline__ void stage_gates(float* sgate, const void* galpha, bool ckda,
+                                            int64_t base, int rowstride, int L, int tid) {
+  using GS = typename G::storage;
+  constexpr int C = Cfg::C, DK = Cfg::DK, NT = Cfg::NT;
+  constexpr int ES = static_cast<int>(sizeof(GS)), VE = 16 / ES, NV = C * DK / VE;
+  constexpr int PER = (NV + NT - 1) / NT;
+  const rsrc_t rs = make_rsrc(static_cast<const GS*>(galpha) + base, ((L - 1) * rowstride + DK) * ES);
+  uint32_t raw[PER][4];
 #pragma unroll
-  for (int e = 0; e < DCH; ++e) {
-    d[e] = 1.f;
-    kj[e] = (j < L) ? IO::load(k, base + static_cast<int64_t>(j) * rowstride + c0 + e) : 0.f;
+  for (int u = 0; u < PER; ++u) {
+    const int e = iclamp(u * NT + tid, NV - 1) * VE;
+    ldraw<16>(rs, (iclamp(e / DK, L - 1) * rowstride + e % DK) * ES, raw[u]);
   }
-  const float rkj = srk[j];
-  for (int r = 0; r < C; ++r) {
-    float pa = 0.f, pp = 0.f;
-    if (j < L && r >= j && r < L) {
 #pragma unroll
-      for (int e = 0; e < DCH; ++e) {
-        const int64_t off = base + static_cast<int64_t>(r) * rowstride + c0 + e;
-        if (r > j) d[e] *= galpha[off];
-        const float w = d[e] * kj[e];
-        pa += IO::load(k, off) * w;
-        pp += IO::load(q, off) * w;
+  for (int u = 0; u < PER; ++u) {
+    const int v = u * NT + tid;
+    if (v < NV) {
+      const int e = v * VE;
+      const bool in = e / DK < L;
+      float x[VE];
+#pragma unroll
+      for (int i = 0; i < VE; ++i) {
+        float g = dec<G>(raw[u], i);
+        if constexpr (G::logits) g = alpha_from_logit(g, ckda);
+        x[i] = in ? g : 1.f;
       }
-    }
 #pragma unroll
-    for (int m = 1; m < DG; m <<= 1) {
-      pa += __shfl_xor(pa, m, 64);
-      pp += __shfl_xor(pp, m, 64);
-    }
-    if (cg == 0) {
-      const int I = r / 16;
-      const float av = (r > j) ? pa * sbeta[r] * srk[r] * rkj : 0.f;
-      if (I > J)
-        a_blk<Cfg>(smem, I, J)[(r % 16) * LDA + j % 16] = av;
-      else if (I == J)
-        x_blk<Cfg>(smem, I, I)[(r % 16) * LDA + j % 16] = av;
-      gP[r * C + Op::template pos<C>(j)] = Op::cvt((r >= j) ? pp * scale * srq[r] * rkj : 0.f);
+      for (int i = 0; i < VE; i += 4)
+        *reinterpret_cast<f32x4*>(sgate + e + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
     }
   }
 }
 
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(FwdArgs a) {
+__device__ __forceinline__ void stage_io(typename Cfg::IO::storage* srow, const void* gsrc,
+                                         int64_t base, int rowstride, int L, int tid) {
+  using ST = typename Cfg::IO::storage;
+  constexpr int C = Cfg::C, DK = Cfg::DK, NT = Cfg::NT;
+  constexpr int ES = static_cast<int>(sizeof(ST)), VE = 16 / ES, NV = C * DK / VE;
+  constexpr int PER = (NV + NT - 1) / NT;
+  const rsrc_t rs = make_rsrc(static_cast<const ST*>(gsrc) + base, ((L - 1) * rowstride + DK) * ES);
+  uint32_t raw[PER][4];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = iclamp(u * NT + tid, NV - 1) * VE;
+    ldraw<16>(rs, (iclamp(e / DK, L - 1) * rowstride + e % DK) * ES, raw[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int v = u * NT + tid;
+    if (v < NV) {
+      const int e = v * VE;
+      const uint32_t m = (e / DK < L) ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<uint4*>(srow + e) =
+          make_uint4(raw[u][0] & m, raw[u][1] & m, raw[u][2] & m, raw[u][3] & m);
+    }
+  }
+}
+
+// One pass of the direct products over the staged rows: for column j (DG
+// lanes, DCH channels each) and every row r, the sum over channels of
+// row_r . D(r<-j) . k_j, with D built one gate at a time (d *= alpha_r for
+// r > j).  Several rows per step, so that their LDS reads and lane
+// reductions overlap.  emit(r, sum) runs in the column's first lane.
+template <class Cfg, class Emit>
+__device__ __forceinline__ void direct_pass(const float* sgate, const typename Cfg::IO::storage* srow,
+                                            const float (&kj)[Cfg::DCH], int j, int c0, bool col,
+                                            Emit emit) {
+  using IO = typename Cfg::IO;
+  constexpr int C = Cfg::C, DK = Cfg::DK, DG = Cfg::DG, DCH = Cfg::DCH;
+  constexpr int RS = DCH > 8 ? 2 : 4;  // rows per step
+  float d[DCH];
+#pragma unroll
+  for (int e = 0; e < DCH; ++e) d[e] = 1.f;
+#pragma unroll 1
+  for (int r0 = 0; r0 < C; r0 += RS) {
+    float p[RS];
+#pragma unroll
+    for (int u = 0; u < RS; ++u) {
+      const int r = r0 + u;
+      const float* gr = sgate + r * DK + c0;
+      const typename IO::storage* xr = srow + r * DK + c0;
+      p[u] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DCH; ++e) {
+        d[e] *= (r > j) ? gr[e] : 1.f;
+        p[u] += IO::load(xr, e) * (d[e] * kj[e]);
+      }
+      p[u] = (col && r >= j) ? p[u] : 0.f;
+    }
+#pragma unroll
+    for (int m = 1; m < DG; m <<= 1)
+#pragma unroll
+      for (int u = 0; u < RS; ++u) p[u] += __shfl_xor(p[u], m, 64);
+#pragma unroll
+    for (int u = 0; u < RS; ++u) emit(r0 + u, p[u]);
+  }
+}
+
+// Direct products for a chunk that is not regular (a zero gate, or running
+// gate products outside [2^-100, 2^10]): A and P from D(r<-j) built one gate
+// at a time, over the chunk's rows staged in LDS (the MFMA operand region,
+// which this path leaves unused): the gates stay, the k rows (A pass) and
+// then the q rows (P pass) take turns in the second slot.  DG lanes per
+// column j, DCH channels each.  Row r of the chunk starts at element
+// base + r * rowstride of q, k, alpha.  Every thread of the workgroup calls
+// this (it holds barriers).
+template <class Cfg, class G>
+__device__ __forceinline__ void direct_ap(const void* gq, const void* gk, const void* galpha,
+                                       bool ckda, int64_t base, int rowstride, int L, float scale,
+                                       typename Cfg::T* gP, unsigned char* smem, int tid) {
+  using IO = typename Cfg::IO;
+  using ST = typename IO::storage;
+  using Op = typename Cfg::Op;
+  constexpr int C = Cfg::C, DK = Cfg::DK, DG = Cfg::DG, DCH = Cfg::DCH, LDA = Cfg::LDA;
+  const float* srq = reinterpret_cast<const float*>(smem + Cfg::O_RQ);
+  const float* srk = reinterpret_cast<const float*>(smem + Cfg::O_RK2);
+  const float* sbeta = reinterpret_cast<const float*>(smem + Cfg::O_BETA);
+  float* sgate = reinterpret_cast<float*>(smem + Cfg::O_DGATE);
+  ST* srow = reinterpret_cast<ST*>(smem + Cfg::O_DROW);
+
+  stage_gates<Cfg, G>(sgate, galpha, ckda, base, rowstride, L, tid);
+  stage_io<Cfg>(srow, gk, base, rowstride, L, tid);
+  __syncthreads();
+  const bool act = tid < DG * C;
+  const int j = act ? tid / DG : 0, cg = tid % DG, c0 = cg * DCH;
+  const int J = j / 16;
+  const bool col = act && j < L;
+  const bool lead = act && cg == 0;
+  float kj[DCH];
+#pragma unroll
+  for (int e = 0; e < DCH; ++e) kj[e] = IO::load(srow, j * DK + c0 + e);
+  const float rkj = srk[j];
+
+  // A_rj = beta_r rk_r rk_j <k_r . D(r<-j), k_j>, j < r (lower blocks of A,
+  // strict lower part of the diagonal blocks, which hold X's diagonal blocks)
+  direct_pass<Cfg>(sgate, srow, kj, j, c0, col, [&](int r, float s) {
+    const int I = r / 16;
+    if (lead && I >= J) {
+      const float av = (r > j) ? s * sbeta[r] * srk[r] * rkj : 0.f;
+      float* blk = (I > J) ? a_blk<Cfg>(smem, I, J) : x_blk<Cfg>(smem, I, I);
+      blk[(r % 16) * LDA + j % 16] = av;
+    }
+  });
+  __syncthreads();
+  stage_io<Cfg>(srow, gq, base, rowstride, L, tid);
+  __syncthreads();
+  // P_rj = scale rq_r rk_j <q_r . D(r<-j), k_j>, j <= r, zero above
+  direct_pass<Cfg>(sgate, srow, kj, j, c0, col, [&](int r, float s) {
+    if (lead) gP[r * C + Op::template pos<C>(j)] = Op::cvt((r >= j) ? s * scale * srq[r] * rkj : 0.f);
+  });
+}
+
+// One (chunk, head) of the transform pass.  DIRECT = false: the MFMA path;
+// a chunk that is not regular gets its flag set and is left to the direct
+// kernel.  DIRECT = true: the same chunk with A and P from direct products.
+template <class Cfg, class G, bool DIRECT>
+__device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsigned char* smem) {
   using Op = typename Cfg::Op;
   using IO = typename Cfg::IO;
   using T = typename Cfg::T;
@@ -192,7 +310,6 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
   constexpr int RPW = Cfg::RPW, CPT = Cfg::CPT, NCG = Cfg::NCG, ES = Cfg::IOES;
   constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, LDA = Cfg::LDA;
 
-  extern __shared__ __align__(16) unsigned char smem[];
   T* sLq = reinterpret_cast<T*>(smem + Cfg::O_LQ);
   T* sXb = reinterpret_cast<T*>(smem + Cfg::O_LQ);
   T* sLk = reinterpret_cast<T*>(smem + Cfg::O_LK);
@@ -209,14 +326,14 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
   const int l16 = lane & 15, lq = lane >> 4;
   const int H = a.H;
 
-  // ---- which chunk: blocks of one chunk and consecutive heads are adjacent
-  const int c = static_cast<int>(blockIdx.x / H);
-  const int h = static_cast<int>(blockIdx.x % H);
   int64_t t0;
   int L;
   if (a.cu_seqlens) {
     const int n = uniform32(a.chunk_seq[c]);
-    if (n < 0) return;  // unused chunk slot
+    if (n < 0) {  // unused chunk slot
+      if (!DIRECT && tid == 0) a.irregular[h * a.maxc + c] = 0;
+      return;
+    }
     const int i = c - uniform32(a.first[n]);
     const int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
     t0 = uniform64(s0 + static_cast<int64_t>(i) * C);
@@ -235,6 +352,7 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
   float* gg = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(blk) + blk_g_byte(C, DK, sizeof(T)));
 
   const bool use_l2 = a.use_l2norm != 0;
+  const bool ckda = a.gate_range == CKDA_GATE_CKDA;
   const bool scan_on = lane < NCG;
   const int c0ch = lane * CPT;
   const int r0 = wave * RPW;
@@ -242,22 +360,24 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
   // ================= 1: loads, running products, norms ======================
   float xq[RPW][CPT], xk[RPW][CPT], F[RPW][CPT];
   {
-    const int krow = H * DK * ES, arow = H * DK * 4;
+    constexpr int GES = static_cast<int>(sizeof(typename G::storage));
+    constexpr int GB = CPT * GES, GW = (GB + 3) / 4;  // gate bytes (words) per row and lane
+    const int krow = H * DK * ES, arow = H * DK * GES;
     const int64_t qk_off = (t0 * H + h) * static_cast<int64_t>(DK);
-    uint32_t rqv[RPW][Cfg::QW], rkv[RPW][Cfg::QW], rav[RPW][CPT];
+    uint32_t rqv[RPW][Cfg::QW], rkv[RPW][Cfg::QW], rav[RPW][GW];
     if (scan_on) {
       const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + qk_off * ES, L * krow);
       const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + qk_off * ES, L * krow);
-      const rsrc_t ra = make_rsrc(a.alpha + qk_off, L * arow);
+      const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + qk_off * GES, L * arow);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int row = iclamp(r0 + i, L - 1);
         ldraw<Cfg::QB>(rq, c0ch * ES + row * krow, rqv[i]);
         ldraw<Cfg::QB>(rk, c0ch * ES + row * krow, rkv[i]);
-        ldraw<CPT * 4>(ra, c0ch * 4 + row * arow, rav[i]);
+        ldraw<GB>(ra, c0ch * GES + row * arow, rav[i]);
       }
     }
-    if (tid < C) sbeta[tid] = (tid < L) ? a.beta[(t0 + tid) * H + h] : 0.f;
+    if (tid < C) sbeta[tid] = (tid < L) ? load_beta<G>(a.beta, (t0 + tid) * H + h, ckda) : 0.f;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const bool in = scan_on && (r0 + i < L);
@@ -265,7 +385,9 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
       for (int cc = 0; cc < CPT; ++cc) {
         xq[i][cc] = in ? dec<IO>(rqv[i], cc) : 0.f;
         xk[i][cc] = in ? dec<IO>(rkv[i], cc) : 0.f;
-        F[i][cc] = in ? __uint_as_float(rav[i][cc]) : 1.f;
+        float g = dec<G>(rav[i], cc);
+        if constexpr (G::logits) g = alpha_from_logit(g, ckda);
+        F[i][cc] = in ? g : 1.f;
       }
     }
   }
@@ -358,10 +480,14 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
   int votes = 1;
 #pragma unroll
   for (int w = 0; w < NW; ++w) votes &= sFlag[w];
-  const bool regular = uniform32(votes) != 0;
+  if constexpr (!DIRECT) {
+    const bool regular = uniform32(votes) != 0;
+    if (tid == 0) a.irregular[h * a.maxc + c] = regular ? 0 : 1;
+    if (!regular) return;
+  }
 
   // ================= 3: A and P ================================================
-  if (regular) {
+  if constexpr (!DIRECT) {
     constexpr int NPT = NB * (NB + 1) / 2;  // lower blocks per matrix
     constexpr int NZ = NB * (NB - 1) / 2;   // zero blocks of P above the diagonal
     constexpr int NTILE = 2 * NPT + NZ;
@@ -408,11 +534,13 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
       }
     }
   } else {
-    direct_ap<Cfg>(a.q, a.k, a.alpha, (t0 * H + h) * static_cast<int64_t>(DK), H * DK, L,
-                   a.scale, gP, smem, tid);
+    direct_ap<Cfg, G>(a.q, a.k, a.alpha, ckda, (t0 * H + h) * static_cast<int64_t>(DK), H * DK,
+                      L, a.scale, gP, smem, tid);
     // Kh from suffix products of the gates (no division)
     if (scan_on) {
+      // the direct path left the gates in LDS (1 past the end)
       const int64_t qk_off = (t0 * H + h) * static_cast<int64_t>(DK);
+      const float* sgate = reinterpret_cast<const float*>(smem + Cfg::O_DGATE);
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
         float suf = gsuf[cc];
@@ -424,7 +552,7 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
                                               qk_off + static_cast<int64_t>(r) * H * DK + c0ch + cc)
                                    : 0.f;
           kh[i][cc] = kr * suf;
-          if (r < L) suf *= a.alpha[qk_off + static_cast<int64_t>(r) * H * DK + c0ch + cc];
+          suf *= sgate[r * DK + c0ch + cc];
         }
       }
     }
@@ -546,6 +674,54 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
 }
 
+// The transform pass: one workgroup per (chunk, head); blocks of one chunk
+// and consecutive heads are adjacent.
+template <class Cfg, class G>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(FwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int H = a.H;
+  prep_chunk<Cfg, G, false>(a, static_cast<int>(blockIdx.x / H), static_cast<int>(blockIdx.x % H),
+                            smem);
+}
+
+// The chunks the transform pass flagged as not regular (exact zero gates, or
+// running gate products outside [2^-100, 2^10]), redone with direct products.
+// Workgroup b reads the flags of (chunk, head) slots b, b + G, b + 2G, ...
+// (G workgroups; at most NT slots each, sized by the launcher) with one load
+// per thread, and redoes the flagged ones in turn; with no flag set it ends
+// after that load.  The stride spreads flagged chunks that sit next to each
+// other (one head's run of zero gates) over different workgroups.
+template <class Cfg, class G>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2))) void prep_direct_kernel(
+    FwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NW = Cfg::NW;
+  const int total = a.maxc * a.H;
+  const int grid = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int slot = b + tid * grid;
+  const bool f = tid < Cfg::NT && slot < total && a.irregular[slot] != 0;
+  const uint64_t m = __ballot(f);
+  uint64_t* smask = reinterpret_cast<uint64_t*>(smem);
+  if (lane == 0) smask[wave] = m;
+  __syncthreads();
+  uint64_t masks[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) masks[w] = static_cast<uint64_t>(uniform64(static_cast<int64_t>(smask[w])));
+  __syncthreads();
+#pragma unroll 1
+  for (int w = 0; w < NW; ++w) {
+    uint64_t mm = masks[w];
+    while (mm != 0) {
+      const int idx = b + (64 * w + __builtin_ctzll(mm)) * grid;
+      mm &= mm - 1;
+      prep_chunk<Cfg, G, true>(a, idx % a.maxc, idx / a.maxc, smem);
+      __syncthreads();
+    }
+  }
+}
+
+
 // Chunk map of a packed batch: first[n] = sum over m < n of ceil(len_m / C),
 // first[N] = the chunk count, chunk_seq[c] = the sequence owning chunk c (or
 // -1 for c >= first[N]).  One workgroup; a block-wide scan per 1024 sequences.
@@ -595,26 +771,42 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* cu, int3
   }
 }
 
-template <class Cfg>
+template <class Cfg, class G>
 launch_result launch_cfg(const FwdArgs& a, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prep_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      Cfg::LDS_BYTES);
+      reinterpret_cast<const void*>(&prep_kernel<Cfg, G>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
+  static const hipError_t attr_d = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&prep_direct_kernel<Cfg, G>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
   if (attr != hipSuccess) return attr;
+  if (attr_d != hipSuccess) return attr_d;
   const int64_t blocks = static_cast<int64_t>(a.maxc) * a.H;
-  hipLaunchKernelGGL(prep_kernel<Cfg>, dim3(static_cast<unsigned>(blocks)), dim3(Cfg::NT),
+  hipLaunchKernelGGL((prep_kernel<Cfg, G>), dim3(static_cast<unsigned>(blocks)), dim3(Cfg::NT),
+                     Cfg::LDS_BYTES, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // one workgroup per CU, each reading at most NT flags
+  int64_t grid = (blocks + Cfg::NT - 1) / Cfg::NT;
+  if (grid < kDirectGrid) grid = blocks < kDirectGrid ? blocks : kDirectGrid;
+  hipLaunchKernelGGL((prep_direct_kernel<Cfg, G>), dim3(static_cast<unsigned>(grid)), dim3(Cfg::NT),
                      Cfg::LDS_BYTES, stream, a);
   return hipGetLastError();
 }
 
+using launch_fn = launch_result (*)(const FwdArgs&, hipStream_t);
+
 struct Entry {
   int chunk, dk, dtype;
-  launch_result (*fn)(const FwdArgs&, hipStream_t);
+  launch_fn fn[3];  // by ckda_gate_input_t
 };
 
 template <class Op, class IO, int C, int D>
 constexpr Entry entry(int dtype) {
-  return Entry{C, D, dtype, &launch_cfg<PrepCfg<Op, IO, C, D>>};
+  using Cfg = PrepCfg<Op, IO, C, D>;
+  return Entry{C, D, dtype,
+               {&launch_cfg<Cfg, gate_f32>, &launch_cfg<Cfg, gate_logit_f32>,
+                &launch_cfg<Cfg, gate_logit_bf16>}};
 }
 
 const Entry kEntries[] = {
@@ -649,8 +841,9 @@ bool prep_supported(int32_t chunk, int32_t dk, int32_t io_dtype) {
 launch_result launch_prep(const FwdArgs& a, int32_t io_dtype, hipStream_t stream) {
   const Entry* e = find(a.chunk, a.dk, io_dtype);
   if (!e) return hipErrorInvalidValue;
+  if (a.gate_input < 0 || a.gate_input > 2) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.maxc) * a.H == 0) return hipSuccess;
-  return e->fn(a, stream);
+  return e->fn[a.gate_input](a, stream);
 }
 
 launch_result launch_chunk_map(const FwdArgs& a, hipStream_t stream) {

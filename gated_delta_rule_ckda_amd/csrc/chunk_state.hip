@@ -462,7 +462,8 @@ size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
   const int64_t maxc = max_chunks(B, T, num_seqs, chunk, packed);
   const int64_t es = io_dtype == CKDA_DTYPE_BF16 ? 2 : 4;
   const int64_t map = packed ? ((4 * (num_seqs + 1 + maxc) + 255) & ~int64_t(255)) : 0;
-  return static_cast<size_t>(map + static_cast<int64_t>(H) * maxc * blk_bytes(chunk, dk, es));
+  const int64_t flags = (4 * static_cast<int64_t>(H) * maxc + 255) & ~int64_t(255);
+  return static_cast<size_t>(map + flags + static_cast<int64_t>(H) * maxc * blk_bytes(chunk, dk, es));
 }
 
 launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream,
@@ -488,6 +489,8 @@ launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stre
     a.chunk_seq = a.first + a.num_seqs + 1;
     base += (4 * (a.num_seqs + 1 + maxc) + 255) & ~int64_t(255);
   }
+  a.irregular = reinterpret_cast<int32_t*>(base);
+  base += (4 * static_cast<int64_t>(a.H) * maxc + 255) & ~int64_t(255);
   a.blocks = base;
   const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
   if (!e) return hipErrorInvalidValue;

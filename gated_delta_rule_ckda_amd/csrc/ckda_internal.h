@@ -20,12 +20,14 @@ using launch_result = hipError_t;
 struct StepArgs {
   int32_t N, H, dk, dv;
   int32_t use_l2norm;
+  int32_t gate_range;  // ckda_gate_t
+  int32_t gate_input;  // ckda_gate_input_t
   float scale;
   const void* q;
   const void* k;
   const void* v;
-  const float* alpha;
-  const float* beta;
+  const void* alpha;
+  const void* beta;
   const float* h0;
   float* ht;
   void* o;
@@ -64,13 +66,14 @@ __host__ __device__ constexpr int64_t blk_bytes(int C, int dk, int es) {
 struct FwdArgs {
   int32_t B, T, H, dk, dv, num_seqs, chunk;
   int32_t use_l2norm;
-  int32_t gate_range;
+  int32_t gate_range;  // ckda_gate_t
+  int32_t gate_input;  // ckda_gate_input_t
   float scale;
   const void* q;
   const void* k;
   const void* v;
-  const float* alpha;
-  const float* beta;
+  const void* alpha;
+  const void* beta;
   const int32_t* cu_seqlens;
   const float* h0;
   void* o;
@@ -79,6 +82,7 @@ struct FwdArgs {
   unsigned char* blocks;  // [H][maxc] blocks of blk_bytes
   int32_t* first;         // [num_seqs + 1] first chunk of each sequence (packed batches)
   int32_t* chunk_seq;     // [maxc] sequence owning each chunk slot, -1 if unused (packed)
+  int32_t* irregular;     // [H][maxc] 1 where the transform pass left a chunk to the direct kernel
   int32_t maxc;           // chunk slots per head
   int32_t nc;             // chunks per sequence (dense batches)
   int64_t blk_bytes;
@@ -136,5 +140,80 @@ struct io_f32 {
 };
 
 constexpr float kL2Eps = 1e-6f;
+
+// ---- gates -----------------------------------------------------------------
+// The gate buffers hold either the gates (float32) or logits (float32 or
+// bf16) that are activated on load (ckda_gate_input_t).  CKDA range (picx.dev
+// summary, section "CKDA Definition"): alpha = 2 sigmoid(a) - 1 and
+// beta = 2 sigmoid(b); KDA range: alpha = sigmoid(a), beta = sigmoid(b).
+// 2 sigmoid(a) - 1 equals sign(a) tanh(|a|/2), formed as (1 - e) / (1 + e)
+// with e = exp(-|a|) for |a| >= 1/2 and by the odd Taylor polynomial of
+// tanh (through degree 9, error below 1e-8 relative) under 1/2, where 1 - e
+// would cancel: a logit of 1e-9 gives a gate of 5e-10, not 0.  So alpha is 0
+// exactly for a logit of 0 only, and +-1 once e underflows.  exp is v_exp_f32
+// on a * log2(e) and the divisions are v_rcp_f32 (about 1 ulp each).
+struct gate_f32 {  // gates as given
+  using storage = float;
+  static constexpr bool logits = false;
+};
+struct gate_logit_f32 {
+  using storage = float;
+  static constexpr bool logits = true;
+};
+struct gate_logit_bf16 {
+  using storage = uint16_t;
+  static constexpr bool logits = true;
+};
+
+__device__ __forceinline__ float exp_neg(float x) {  // e^-x
+  return __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+}
+// Both ranges share one exp and one reciprocal; the range only selects
+// operands (no branch, so unrolled loads and activations stay interleaved).
+__device__ __forceinline__ float alpha_from_logit(float a, bool ckda) {
+  const float x = ckda ? fabsf(a) : a;
+  const float e = exp_neg(x);
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
+  const float y = 0.5f * x, y2 = y * y;
+  const float poly =
+      y * (1.f + y2 * (-1.f / 3 + y2 * (2.f / 15 + y2 * (-17.f / 315 + y2 * (62.f / 2835)))));
+  const float m = (x < 0.5f) ? poly : (1.f - e) * r;  // tanh(|a|/2)
+  return ckda ? copysignf(m, a) : r;
+}
+__device__ __forceinline__ float beta_from_logit(float b, bool ckda) {
+  return (ckda ? 2.f : 1.f) * __builtin_amdgcn_rcpf(1.f + exp_neg(b));
+}
+template <class G>
+__device__ __forceinline__ float gate_raw(const void* p, int64_t i) {
+  const typename G::storage x = static_cast<const typename G::storage*>(p)[i];
+  if constexpr (sizeof(typename G::storage) == 2)
+    return bf16_to_f32(x);
+  else
+    return x;
+}
+// alpha (or beta) element i of a gate buffer of kind G
+template <class G>
+__device__ __forceinline__ float load_alpha(const void* p, int64_t i, bool ckda) {
+  const float x = gate_raw<G>(p, i);
+  if constexpr (G::logits) return alpha_from_logit(x, ckda);
+  return x;
+}
+template <class G>
+__device__ __forceinline__ float load_beta(const void* p, int64_t i, bool ckda) {
+  const float x = gate_raw<G>(p, i);
+  if constexpr (G::logits) return beta_from_logit(x, ckda);
+  return x;
+}
+// the same with the kind chosen at run time (ckda_gate_input_t)
+__device__ __forceinline__ float load_alpha_rt(const void* p, int64_t i, int gi, bool ckda) {
+  if (gi == CKDA_GATES_LOGITS_BF16) return load_alpha<gate_logit_bf16>(p, i, ckda);
+  if (gi == CKDA_GATES_LOGITS_F32) return load_alpha<gate_logit_f32>(p, i, ckda);
+  return load_alpha<gate_f32>(p, i, ckda);
+}
+__device__ __forceinline__ float load_beta_rt(const void* p, int64_t i, int gi, bool ckda) {
+  if (gi == CKDA_GATES_LOGITS_BF16) return load_beta<gate_logit_bf16>(p, i, ckda);
+  if (gi == CKDA_GATES_LOGITS_F32) return load_beta<gate_logit_f32>(p, i, ckda);
+  return load_beta<gate_f32>(p, i, ckda);
+}
 
 }  // namespace ckda

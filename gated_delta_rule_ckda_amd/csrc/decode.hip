@@ -9,6 +9,9 @@
 //   S' = S~ + beta k_hat (v - w)^T          (delta-rule write)
 //   o  = scale (y + beta (k_hat . q_hat) (v - w))   (= scale S'^T q_hat)
 //
+// alpha and beta are read as gates or as logits activated on load (the gate
+// helpers of ckda_internal.h).
+//
 // The transition (I - beta k k^T) Diag(alpha) is the gated delta-rule
 // transition of the picx.dev summary of the Complex KDA paper (section
 // "Background"); q_hat, k_hat are the in-op L2-normalised query and key
@@ -66,10 +69,11 @@ __global__ __launch_bounds__((StepShape<DK, DV>::NT)) void step_kernel(StepArgs 
   const T* q = static_cast<const T*>(a.q) + nh * DK;
   const T* k = static_cast<const T*>(a.k) + nh * DK;
   const T* v = static_cast<const T*>(a.v) + nh * DV;
+  const bool ckda = a.gate_range == CKDA_GATE_CKDA;
   for (int i = t; i < DK; i += NT) {
     s_q[i] = IO::load(q, i);
     s_k[i] = IO::load(k, i);
-    s_a[i] = a.alpha[nh * DK + i];
+    s_a[i] = load_alpha_rt(a.alpha, nh * DK + i, a.gate_input, ckda);
   }
   for (int i = t; i < DV; i += NT) s_v[i] = IO::load(v, i);
   __syncthreads();
@@ -95,7 +99,7 @@ __global__ __launch_bounds__((StepShape<DK, DV>::NT)) void step_kernel(StepArgs 
   }
   __syncthreads();
   const float rq = s_scal[0], rk = s_scal[1], kq = s_scal[2];
-  const float bt = a.beta[nh];
+  const float bt = load_beta_rt(a.beta, nh, a.gate_input, ckda);
 
   f32x4 pw = {0.f, 0.f, 0.f, 0.f}, py = pw;
 #pragma unroll

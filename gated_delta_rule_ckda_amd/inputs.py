@@ -20,6 +20,11 @@ evaluations the pages mention are stood in for by these synthetic tensors):
                  CKDA-arm gates, h0~N(0, 0.02^2)
   decode         256 sequences x 1 token, H=32 d=128, bf16 q/k/v, state
                  ~N(0, 0.02^2), alpha~U[-1,1], beta~U[0,2], fresh draws per step
+  *_logits       the same workloads with the gates given as pre-activation
+                 logits (alpha and beta of the Case hold a and b): CKDA arm
+                 a = 2 N(2,1), b = N(0,1), so that 2 sigmoid(a) - 1 =
+                 tanh(N(2,1)) and 2 sigmoid(b) follow the value workloads'
+                 laws; KDA arm a = N(2,1), b = N(0,1)
 """
 from __future__ import annotations
 
@@ -53,6 +58,9 @@ class Case:
     chunk: int
     l2norm: bool
     meta: dict = field(default_factory=dict)
+    gates: str = "values"     # "values": alpha, beta are the gates; "logits": a, b
+    gate_dtype: str = "f32"   # storage of alpha, beta ("bf16" only for logits)
+    arm: str = "ckda"         # gate range: "ckda" or "kda"
 
     @property
     def shape(self):
@@ -106,6 +114,41 @@ def random_case(seed, B, T, H, dk, dv, *, dtype="f32", chunk=16, l2norm=True,
                 dict(B=B, T=T, H=H, dk=dk, dv=dv, seed=seed))
 
 
+def logit_case(seed, B, T, H, dk, dv, *, dtype="f32", chunk=16, l2norm=True, arm="ckda",
+               gate_dtype="f32", spread="lm", zero_frac=0.0, h0_std=0.0) -> Case:
+    """Dense case with logit gates.  q,k,v ~ N(0,1) (unit keys without the
+    in-kernel norm).  spread='lm': the LM-layer logit laws of the module
+    docstring; spread='wide': a ~ U[-8,8], b ~ U[-6,6] (gates over the whole
+    range, with many negative ones in the CKDA arm).  zero_frac sets that
+    fraction of the a logits to exactly 0 (alpha = 0 in the CKDA range)."""
+    rng = np.random.default_rng(seed)
+    q = _io(rng.standard_normal((B, T, H, dk), dtype=np.float32), dtype)
+    k = rng.standard_normal((B, T, H, dk), dtype=np.float32)
+    if not l2norm:
+        k64 = k.astype(np.float64)
+        k = (k64 / np.sqrt((k64 * k64).sum(-1, keepdims=True))).astype(np.float32)
+    k = _io(k, dtype)
+    v = _io(rng.standard_normal((B, T, H, dv), dtype=np.float32), dtype)
+    if spread == "lm":
+        a = rng.normal(2, 1, (B, T, H, dk)) * (2.0 if arm == "ckda" else 1.0)
+        b = rng.normal(0, 1, (B, T, H))
+    elif spread == "wide":
+        a = rng.uniform(-8, 8, (B, T, H, dk))
+        b = rng.uniform(-6, 6, (B, T, H))
+    else:
+        raise ValueError(spread)
+    a = _io(a.astype(np.float32), gate_dtype)
+    b = _io(b.astype(np.float32), gate_dtype)
+    if zero_frac > 0:
+        a[rng.random(a.shape) < zero_frac] = 0.0
+    h0 = None
+    if h0_std > 0:
+        h0 = (h0_std * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    return Case(q, k, v, a, b, h0, None, dtype, chunk, l2norm,
+                dict(B=B, T=T, H=H, dk=dk, dv=dv, seed=seed), gates="logits",
+                gate_dtype=gate_dtype, arm=arm)
+
+
 def tiny(seed=1000) -> Case:
     c = random_case(seed, 1, 64, 2, 16, 16, dtype="f32", chunk=16, l2norm=True)
     c.meta["workload"] = "tiny CKDA forward B=1 H=2 T=64 d=16 fp32"
@@ -148,7 +191,29 @@ def lm_layer(seed=1002, arm="ckda", B=8, T=4096, H=16, d=128) -> Case:
     return Case(q, k, v, a.astype(np.float32), b, None, None, "bf16", 64, True,
                 dict(B=B, T=T, H=H, dk=d, dv=d, seed=seed, arm=arm,
                      workload="LM layer forward B=%d H=%d T=%d d=%d bf16 %s range"
-                              % (B, H, T, d, arm.upper())))
+                              % (B, H, T, d, arm.upper())), arm=arm)
+
+
+def lm_layer_logits(seed=1002, arm="ckda", B=8, T=4096, H=16, d=128, gate_dtype="bf16") -> Case:
+    """The LM layer with its gates as logits in gate_dtype (laws in the module
+    docstring).  q/k/v are the same draws as lm_layer(seed); the logits come
+    from seed + 2000 (CKDA) or seed + 3000 (KDA)."""
+    rng = np.random.default_rng(seed)
+    q = round_bf16(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    k = round_bf16(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    v = round_bf16(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    if arm not in ("ckda", "kda"):
+        raise ValueError(arm)
+    rng2 = np.random.default_rng(seed + (2000 if arm == "ckda" else 3000))
+    a = rng2.normal(2, 1, (B, T, H, d)) * (2.0 if arm == "ckda" else 1.0)
+    b = rng2.normal(0, 1, (B, T, H))
+    a = _io(a.astype(np.float32), gate_dtype)
+    b = _io(b.astype(np.float32), gate_dtype)
+    return Case(q, k, v, a, b, None, None, "bf16", 64, True,
+                dict(B=B, T=T, H=H, dk=d, dv=d, seed=seed, arm=arm,
+                     workload="LM layer forward B=%d H=%d T=%d d=%d bf16 %s range, %s gate logits"
+                              % (B, H, T, d, arm.upper(), gate_dtype)),
+                gates="logits", gate_dtype=gate_dtype, arm=arm)
 
 
 def varlen_lengths(seed=1003, n=16, total=65536, lo=1024, hi=8192):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 3
+#define CKDA_ABI_VERSION 4
 
 typedef enum {
   CKDA_OK = 0,
@@ -70,9 +70,29 @@ typedef enum {
 } ckda_gate_t;
 
 /*
+ * What the alpha and beta buffers hold.
+ *   CKDA_GATES_F32: the gates themselves, float32.
+ *   CKDA_GATES_LOGITS_F32 / CKDA_GATES_LOGITS_BF16: pre-activation logits a
+ *     (shaped like alpha) and b (shaped like beta), float32 or bfloat16; the
+ *     kernels form the gates on load, in float32.  CKDA range (picx.dev
+ *     summary, section "CKDA Definition"): alpha = 2 sigmoid(a) - 1 and
+ *     beta = 2 sigmoid(b).  KDA range: alpha = sigmoid(a), beta = sigmoid(b)
+ *     (the same activation without the shift and doubling that widen the
+ *     range).  a = 0 gives alpha = 0 exactly in the CKDA range; logits of
+ *     +-inf give the limits; a NaN logit gives NaN results.
+ * Logits in bfloat16 halve the gate bytes the transform pass reads.
+ */
+typedef enum {
+  CKDA_GATES_F32 = 0,
+  CKDA_GATES_LOGITS_F32 = 1,
+  CKDA_GATES_LOGITS_BF16 = 2
+} ckda_gate_input_t;
+
+/*
  * Descriptor of one chunked forward call.
  *   Dense batch (cu_seqlens == NULL): num_seqs == B sequences of T tokens;
  *     q, k, alpha : [B][T][H][dk]   v, o : [B][T][H][dv]   beta : [B][T][H]
+ *   (alpha and beta in the element type gate_input names)
  *   Packed variable-length batch (cu_seqlens != NULL): B must be 1, T is the
  *     total token count, sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
  *     (empty sequences allowed; then ht[n] = h0[n]).
@@ -88,16 +108,18 @@ typedef struct {
   int32_t gate_range;    /* ckda_gate_t */
   int32_t use_qk_l2norm; /* 0 or 1 */
   float scale;           /* o = scale * S^T q_hat */
+  int32_t gate_input;    /* ckda_gate_input_t (0: float32 gate values) */
 } ckda_fwd_desc_t;
 
 /*
  * Bytes of device workspace ckda_chunk_fwd needs for this descriptor; 0 for
  * an invalid descriptor or an empty call.  `packed` is 1 when the call will
  * pass cu_seqlens (a packed batch), else 0.  The size depends only on the
- * sizes, never on data: one block of chunk operands per (head, chunk), with
- * at most ceil(T / chunk_size) * B chunks for a dense batch and
- * ceil(T / chunk_size) + num_seqs for a packed one, plus the chunk map of a
- * packed batch.  At B=8, T=4096, H=16, dk=128, chunk 64, bf16: 516 MiB.
+ * sizes, never on data: one block of chunk operands and one int32 flag per
+ * (head, chunk), with at most ceil(T / chunk_size) * B chunks for a dense
+ * batch and ceil(T / chunk_size) + num_seqs for a packed one, plus the chunk
+ * map of a packed batch.  At B=8, T=4096, H=16, dk=128, chunk 64, bf16:
+ * 516 MiB.
  */
 size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed);
 
@@ -110,7 +132,10 @@ size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed
  * Two passes run on `stream`: a transform pass over all chunks in parallel
  * (gate prefix, norms, the chunk's UT/WY transform), which writes each chunk's
  * operands into `workspace`, then a state pass that walks every
- * (sequence, head) over its chunks.  `workspace` is a device buffer of at
+ * (sequence, head) over its chunks.  The transform pass is two launches: the
+ * MFMA form for every chunk whose running gate products stay within
+ * [2^-100, 2^10], then a short launch that redoes the other chunks (exact
+ * zero gates, products that underflow) with direct products.  `workspace` is a device buffer of at
  * least ckda_chunk_fwd_workspace_size(desc, cu_seqlens != NULL) bytes,
  * 256-byte aligned, owned by the caller, not overlapping any argument; its
  * contents are scratch (undefined before and after the call).  Calls that
@@ -122,8 +147,8 @@ size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed
  * ckda_fwd_supported() reports whether a descriptor has a kernel.
  */
 ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
-                             const void* k, const void* v, const float* alpha,
-                             const float* beta, const int32_t* cu_seqlens,
+                             const void* k, const void* v, const void* alpha,
+                             const void* beta, const int32_t* cu_seqlens,
                              const float* h0, void* o, float* ht,
                              void* workspace, size_t workspace_bytes, void* stream);
 
@@ -140,8 +165,8 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
  * descriptor is a precondition, not checked.
  */
 ckda_status_t ckda_chunk_fwd_prepare(const ckda_fwd_desc_t* desc, const void* q,
-                                     const void* k, const float* alpha,
-                                     const float* beta, const int32_t* cu_seqlens,
+                                     const void* k, const void* alpha,
+                                     const void* beta, const int32_t* cu_seqlens,
                                      void* workspace, size_t workspace_bytes,
                                      void* stream);
 ckda_status_t ckda_chunk_fwd_finish(const ckda_fwd_desc_t* desc, const void* v,
@@ -159,13 +184,14 @@ int32_t ckda_fwd_supported(const ckda_fwd_desc_t* desc);
  *   q, k, alpha : [N][H][dk]   v, o : [N][H][dv]   beta : [N][H]
  *   h0, ht      : [N][H][dk][dv] float32; h0 == ht (in place) is allowed,
  *                 other partial overlaps are not.
- * Supported: dk, dv in {16, 32, 64, 128}, both io dtypes.
+ * alpha and beta hold what gate_input (a ckda_gate_input_t) says.
+ * Supported: dk, dv in {16, 32, 64, 128}, both io dtypes, every gate input.
  */
 ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                   int32_t io_dtype, int32_t gate_range,
-                                  int32_t use_qk_l2norm, float scale,
-                                  const void* q, const void* k, const void* v,
-                                  const float* alpha, const float* beta,
+                                  int32_t gate_input, int32_t use_qk_l2norm,
+                                  float scale, const void* q, const void* k,
+                                  const void* v, const void* alpha, const void* beta,
                                   const float* h0, float* ht, void* o,
                                   void* stream);
 

@@ -33,19 +33,30 @@ def announce(msg):
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def run_chunk(case, chunk=None, h0=None, ht=True, gate="ckda", scale=1.0, l2=None):
+def run_chunk(case, chunk=None, h0=None, ht=True, gate=None, scale=1.0, l2=None):
     """Run ckda_chunk_fwd on an inputs.Case; returns (o, ht) as fp64 numpy."""
     import gated_delta_rule_ckda_amd as ck
     dt = case.dtype
     cu = None if case.cu_seqlens is None else torch.from_numpy(case.cu_seqlens).to(DEV)
     h0a = case.h0 if h0 is None else h0
-    o, st = ck.chunk_fwd(dev(case.q, dt), dev(case.k, dt), dev(case.v, dt), dev(case.alpha),
-                         dev(case.beta), h0=None if h0a is None else dev(h0a), cu_seqlens=cu,
+    o, st = ck.chunk_fwd(dev(case.q, dt), dev(case.k, dt), dev(case.v, dt),
+                         dev(case.alpha, case.gate_dtype), dev(case.beta, case.gate_dtype),
+                         h0=None if h0a is None else dev(h0a), cu_seqlens=cu,
                          chunk_size=chunk or case.chunk,
-                         use_qk_l2norm=case.l2norm if l2 is None else l2, gate=gate,
-                         scale=scale, output_final_state=ht)
+                         use_qk_l2norm=case.l2norm if l2 is None else l2,
+                         gate=gate or case.arm, scale=scale, output_final_state=ht,
+                         gates=case.gates)
     torch.cuda.synchronize()
     return host(o), (None if st is None else host(st))
+
+
+def oracle_gates(case, a, b):
+    """The gates the oracle runs on: the case's own, or the oracle's activation
+    of its logits."""
+    import oracle
+    if case.gates == "logits":
+        return oracle.gates(a, b, ckda_range=(case.arm == "ckda"))
+    return a, b
 
 
 def oracle_pairs(case, pairs, scale=1.0):
@@ -63,9 +74,10 @@ def oracle_pairs(case, pairs, scale=1.0):
         q, k, v, a, b = (x[0] for x in (case.q, case.k, case.v, case.alpha, case.beta))
     for (n, h) in pairs:
         s0, s1 = int(starts[n]), int(starts[n + 1])
+        ga, gb = oracle_gates(case, a[s0:s1, h:h + 1], b[s0:s1, h:h + 1])
         h0 = None if case.h0 is None else case.h0[n:n + 1, h:h + 1]
         o, ht = oracle.fwd(q[None, s0:s1, h:h + 1], k[None, s0:s1, h:h + 1],
-                           v[None, s0:s1, h:h + 1], a[None, s0:s1, h:h + 1],
-                           b[None, s0:s1, h:h + 1], h0=h0, use_l2norm=case.l2norm, scale=scale)
+                           v[None, s0:s1, h:h + 1], ga[None], gb[None], h0=h0,
+                           use_l2norm=case.l2norm, scale=scale)
         out[(n, h)] = (o[0, :, 0], ht[0, 0])
     return out

@@ -48,7 +48,7 @@ WS_BYTES = 1 << 31
 
 def _desc(**kw):
     d = dict(B=2, T=64, H=2, dk=128, dv=128, num_seqs=2, chunk_size=64, io_dtype=ck.BF16,
-             gate_range=ck.GATE_CKDA, use_qk_l2norm=1, scale=1.0)
+             gate_range=ck.GATE_CKDA, use_qk_l2norm=1, scale=1.0, gate_input=ck.GATES_F32)
     d.update(kw)
     return ck.FwdDesc(**d)
 
@@ -66,6 +66,7 @@ def _fwd(desc, **over):
 @pytest.mark.parametrize("over,needle", [
     (dict(B=0), "non-positive"), (dict(H=-1), "non-positive"), (dict(dk=0), "non-positive"),
     (dict(io_dtype=7), "io_dtype"), (dict(gate_range=3), "gate_range"),
+    (dict(gate_input=3), "gate_input"), (dict(gate_input=-1), "gate_input"),
     (dict(use_qk_l2norm=2), "use_qk_l2norm"), (dict(chunk_size=48), "chunk_size"),
     (dict(num_seqs=3), "num_seqs"),
 ])
@@ -95,16 +96,18 @@ def test_fwd_cu_seqlens_needs_batch_one():
 
 def test_workspace_size_formula():
     """One block per (head, chunk): (2C^2 + 3C dk) elements + dk floats, rounded up to
-    256 bytes; dense batches have B*ceil(T/C) chunks, packed ones ceil(T/C) + N slots
-    plus the chunk map."""
+    256 bytes, plus one int32 flag per (head, chunk) slot; dense batches have
+    B*ceil(T/C) chunks, packed ones ceil(T/C) + N slots plus the chunk map."""
+    up = lambda x: -(-x // 256) * 256
     d = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8)
     blk = (2 * 64 * 64 + 3 * 64 * 128) * 2 + 128 * 4
     assert blk % 256 == 0
-    assert ck.chunk_fwd_workspace_size(d, False) == 16 * 8 * 64 * blk
+    assert ck.chunk_fwd_workspace_size(d, False) == up(4 * 16 * 8 * 64) + 16 * 8 * 64 * blk
     d = _desc(B=1, T=70, H=3, dk=32, dv=32, num_seqs=4, chunk_size=16, io_dtype=ck.F32)
-    blk = -(-((2 * 16 * 16 + 3 * 16 * 32) * 4 + 32 * 4) // 256) * 256
+    blk = up((2 * 16 * 16 + 3 * 16 * 32) * 4 + 32 * 4)
     maxc = -(-70 // 16) + 4
-    assert ck.chunk_fwd_workspace_size(d, True) == -(-(4 * (4 + 1 + maxc)) // 256) * 256 + 3 * maxc * blk
+    assert ck.chunk_fwd_workspace_size(d, True) == (up(4 * (4 + 1 + maxc)) + up(4 * 3 * maxc)
+                                                   + 3 * maxc * blk)
     assert ck.chunk_fwd_workspace_size(_desc(T=0), False) == 0
     assert ck.chunk_fwd_workspace_size(_desc(chunk_size=48), False) == 0
 
@@ -137,6 +140,19 @@ def test_prepare_and_finish_validation():
     assert st == 1 and "workspace overlaps q" in lib.ckda_last_error().decode()
 
 
+def test_fwd_gate_byte_ranges_follow_gate_input():
+    """bf16 logits take 2 bytes per gate, float32 gates 4: an o buffer placed
+    right after a bf16 alpha overlaps a float32 alpha of the same shape.  dk=96
+    has no kernel, so a call that passes every other check stops at
+    CKDA_ERR_UNSUPPORTED and nothing is launched."""
+    kw = dict(B=1, num_seqs=1, dk=96, dv=96)
+    o = ctypes.c_void_p(P["alpha"].value + 64 * 2 * 96 * 2)
+    st, msg = _fwd(_desc(gate_input=ck.GATES_LOGITS_BF16, **kw), o=o)
+    assert st == 2, msg
+    st, msg = _fwd(_desc(gate_input=ck.GATES_F32, **kw), o=o)
+    assert st == 1 and "o overlaps alpha" in msg
+
+
 def test_fwd_unsupported_shape():
     st, msg = _fwd(_desc(dk=96, dv=96))
     assert st == 2 and "no chunked kernel" in msg
@@ -150,11 +166,12 @@ def test_fwd_empty_is_ok_without_launch():
     assert st == 0
 
 
-def _step(N=4, H=2, dk=128, dv=128, dtype=ck.BF16, gate=ck.GATE_CKDA, l2=1, **over):
+def _step(N=4, H=2, dk=128, dv=128, dtype=ck.BF16, gate=ck.GATE_CKDA, l2=1, gi=ck.GATES_F32,
+          **over):
     p = dict(P)
     p.update(over)
     lib = ck._load()
-    st = lib.ckda_recurrent_step(N, H, dk, dv, dtype, gate, l2, 1.0, p["q"], p["k"], p["v"],
+    st = lib.ckda_recurrent_step(N, H, dk, dv, dtype, gate, gi, l2, 1.0, p["q"], p["k"], p["v"],
                                  p["alpha"], p["beta"], p["h0"], p["ht"], p["o"], None)
     return st, lib.ckda_last_error().decode()
 
@@ -164,6 +181,8 @@ def test_step_validation():
     assert _step(H=0)[0] == 1
     assert _step(dtype=5)[0] == 1
     assert _step(gate=2)[0] == 1
+    assert _step(gi=3)[0] == 1 and "gate_input" in _step(gi=3)[1]
+    assert _step(N=0, gi=ck.GATES_LOGITS_BF16)[0] == 0
     assert _step(l2=3)[0] == 1
     assert _step(q=None)[0] == 1
     assert _step(v=ctypes.c_void_p(BASE + 4))[0] == 1

@@ -8,8 +8,8 @@ import torch
 import gated_delta_rule_ckda_amd as ck
 import oracle
 from gated_delta_rule_ckda_amd import inputs
-from tests.gpu_util import (DEV, TOL, announce, dev, host, max_rel_err, oracle_pairs,
-                            run_chunk)
+from tests.gpu_util import (DEV, TOL, announce, dev, host, max_rel_err, oracle_gates,
+                            oracle_pairs, run_chunk)
 from tests.test_gpu_decode import pow2_rows
 
 pytestmark = pytest.mark.gpu
@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 
 def _check(case, chunk=None, scale=1.0, tol=None):
     o, ht = run_chunk(case, chunk=chunk, scale=scale)
-    ro, rh = oracle.fwd(case.q, case.k, case.v, case.alpha, case.beta, h0=case.h0,
+    ga, gb = oracle_gates(case, case.alpha, case.beta)
+    ro, rh = oracle.fwd(case.q, case.k, case.v, ga, gb, h0=case.h0,
                         seq_start=case.cu_seqlens, use_l2norm=case.l2norm, scale=scale)
     tol = tol or TOL[case.dtype]
     eo, eh = max_rel_err(o, ro), max_rel_err(ht, rh)
