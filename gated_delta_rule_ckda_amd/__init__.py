@@ -37,7 +37,8 @@ class FwdDesc(ctypes.Structure):
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("gate_range", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("gate_input", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("gate_input", ctypes.c_int32),
+                ("qk_heads", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -69,8 +70,8 @@ def _load():
         lib.ckda_fwd_supported.restype = i32
         lib.ckda_fwd_supported.argtypes = [ctypes.POINTER(FwdDesc)]
         lib.ckda_recurrent_step.restype = i32
-        lib.ckda_recurrent_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
-                                            vp, vp, vp, vp, vp, vp, vp]
+        lib.ckda_recurrent_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, vp,
+                                            vp, vp, vp, vp, vp, vp, vp, vp]
         lib.ckda_l2norm_debug.restype = i32
         lib.ckda_l2norm_debug.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp]
         lib.ckda_status_string.restype = ctypes.c_char_p
@@ -143,6 +144,7 @@ def _require(cond, msg):
 
 def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens,
                gate_input=GATES_F32):
+    """H: value heads (v.shape[-2]); the q/k heads are q.shape[-2]."""
     if cu_seqlens is not None:
         B, T = 1, q.shape[-3] if q.dim() == 3 else q.shape[1]
         N = cu_seqlens.numel() - 1
@@ -150,11 +152,11 @@ def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqle
         B, T = q.shape[0], q.shape[1]
         N = B
     return FwdDesc(B, T, H, dk, dv, N, chunk_size, _dtype_code(q), _gate_code(gate),
-                   int(bool(use_qk_l2norm)), float(scale), gate_input)
+                   int(bool(use_qk_l2norm)), float(scale), gate_input, q.shape[-2])
 
 
 def fwd_supported(chunk_size, dk, dv, dtype) -> bool:
-    d = FwdDesc(1, 1, 1, dk, dv, 1, chunk_size, dtype, GATE_CKDA, 1, 1.0, GATES_F32)
+    d = FwdDesc(1, 1, 1, dk, dv, 1, chunk_size, dtype, GATE_CKDA, 1, 1.0, GATES_F32, 0)
     return bool(_load().ckda_fwd_supported(ctypes.byref(d)))
 
 
@@ -166,8 +168,10 @@ def chunk_fwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
 def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
               use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
               out=None, final_state=None, workspace=None, stream=None, gates="values"):
-    """Chunked prefill.  Dense: q,k,alpha [B,T,H,dk], v [B,T,H,dv], beta [B,T,H].
-    Packed (cu_seqlens int32 [N+1]): leading [1,T,...] or [T,...].
+    """Chunked prefill.  Dense: q,k [B,T,Hk,dk], alpha [B,T,H,dk], v [B,T,H,dv],
+    beta [B,T,H]; Hk divides H (grouped value heads: value head h reads q/k
+    head h // (H // Hk)).  Packed (cu_seqlens int32 [N+1]): leading [1,T,...]
+    or [T,...].
     gates='values': alpha, beta are float32 gates; gates='logits': they are
     float32 or bfloat16 logits that the kernels activate.
     `workspace`: optional uint8 device tensor of at least
@@ -175,7 +179,7 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
     Returns (o, ht) with ht [N,H,dk,dv] float32 (None if not requested)."""
     import torch
     lib = _load()
-    H, dk, dv = q.shape[-2], q.shape[-1], v.shape[-1]
+    H, dk, dv = v.shape[-2], q.shape[-1], v.shape[-1]
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
         _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
     _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
@@ -184,8 +188,9 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
         _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda,
                  "cu_seqlens must be an int32 device tensor")
     desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens, gi)
-    _require(q.numel() == desc.B * desc.T * H * dk, "q has the wrong number of elements")
-    _require(k.numel() == q.numel() and alpha.numel() == q.numel(), "k/alpha must match q")
+    _require(q.numel() == desc.B * desc.T * desc.qk_heads * dk, "q has the wrong number of elements")
+    _require(k.numel() == q.numel(), "k must match q")
+    _require(alpha.numel() == desc.B * desc.T * H * dk, "alpha has the wrong number of elements")
     _require(v.numel() == desc.B * desc.T * H * dv, "v has the wrong number of elements")
     _require(beta.numel() == desc.B * desc.T * H, "beta has the wrong number of elements")
     if h0 is not None:
@@ -217,7 +222,7 @@ class ChunkFwdPlan:
                  stream=None, gates="values"):
         import torch
         self.lib = _load()
-        H, dk, dv = q.shape[-2], q.shape[-1], v.shape[-1]
+        H, dk, dv = v.shape[-2], q.shape[-1], v.shape[-1]
         self.desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale,
                                cu_seqlens, _gate_input(gates, alpha, beta))
         self.args = (q, k, v, alpha, beta, h0, cu_seqlens)
@@ -245,24 +250,24 @@ class ChunkFwdPlan:
 
 def recurrent_step(q, k, v, alpha, beta, state, *, use_qk_l2norm=True, gate="ckda",
                    scale=1.0, out=None, new_state=None, stream=None, gates="values"):
-    """One decode token per sequence: q,k,alpha [N,H,dk], v [N,H,dv], beta [N,H],
-    state [N,H,dk,dv] float32, updated in place unless new_state is given.
-    `gates` as for chunk_fwd.  Returns o [N,H,dv]."""
+    """One decode token per sequence: q,k [N,Hk,dk], alpha [N,H,dk], v [N,H,dv],
+    beta [N,H], state [N,H,dk,dv] float32, updated in place unless new_state
+    is given.  `gates` as for chunk_fwd.  Returns o [N,H,dv]."""
     import torch
     lib = _load()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
+    N, Hk, dk = q.shape
+    H, dv = v.shape[-2], v.shape[-1]
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
                     ("state", state)):
         _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
     _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
     gi = _gate_input(gates, alpha, beta)
     _require(state.dtype == torch.float32, "state must be float32")
-    _require(k.shape == q.shape and alpha.shape == q.shape and v.shape == (N, H, dv)
+    _require(k.shape == q.shape and alpha.shape == (N, H, dk) and v.shape == (N, H, dv)
              and beta.shape == (N, H) and state.shape == (N, H, dk, dv), "shape mismatch")
     o = torch.empty_like(v) if out is None else out
     dst = state if new_state is None else new_state
-    _check(lib.ckda_recurrent_step(N, H, dk, dv, _dtype_code(q), _gate_code(gate), gi,
+    _check(lib.ckda_recurrent_step(N, H, Hk, dk, dv, _dtype_code(q), _gate_code(gate), gi,
                                    int(bool(use_qk_l2norm)), float(scale), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(dst),
                                    _ptr(o), _stream(stream)))

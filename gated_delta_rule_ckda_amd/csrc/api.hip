@@ -48,6 +48,13 @@ int64_t elem_bytes(int32_t dtype) { return dtype == CKDA_DTYPE_BF16 ? 2 : 4; }
 
 static_assert(CKDA_GATES_F32 == 0 && CKDA_GATES_LOGITS_F32 == 1 && CKDA_GATES_LOGITS_BF16 == 2,
               "the kernels index their variants by ckda_gate_input_t");
+// q/k heads: 0 means as many as value heads
+int32_t qk_heads_of(int32_t H, int32_t qk_heads) { return qk_heads == 0 ? H : qk_heads; }
+bool valid_qk_heads(int32_t H, int32_t qk_heads) {
+  const int32_t hk = qk_heads_of(H, qk_heads);
+  return hk > 0 && H > 0 && H % hk == 0;
+}
+
 bool valid_gate_input(int32_t g) { return g >= CKDA_GATES_F32 && g <= CKDA_GATES_LOGITS_BF16; }
 int64_t gate_bytes(int32_t g) { return g == CKDA_GATES_LOGITS_BF16 ? 2 : 4; }
 
@@ -115,6 +122,8 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
   if (!valid_gate_input(d->gate_input))
     return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_input %d is not a ckda_gate_input_t",
                 d->gate_input);
+  if (!valid_qk_heads(d->H, d->qk_heads))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "qk_heads %d does not divide H=%d", d->qk_heads, d->H);
   if (d->use_qk_l2norm != 0 && d->use_qk_l2norm != 1)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
   if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
@@ -141,10 +150,11 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
 
   const int64_t eb = elem_bytes(d->io_dtype);
   const int64_t gb = gate_bytes(d->gate_input);
+  const int64_t hk = qk_heads_of(d->H, d->qk_heads);
   const int64_t state_bytes = static_cast<int64_t>(d->num_seqs) * d->H * d->dk * d->dv * 4;
   const Range ro = range("o", o, o ? tokens * d->H * d->dv * eb : 0);
-  const Range ins[] = {range("q", q, q ? tokens * d->H * d->dk * eb : 0),
-                       range("k", k, k ? tokens * d->H * d->dk * eb : 0),
+  const Range ins[] = {range("q", q, q ? tokens * hk * d->dk * eb : 0),
+                       range("k", k, k ? tokens * hk * d->dk * eb : 0),
                        range("v", v, v ? tokens * d->H * d->dv * eb : 0),
                        range("alpha", alpha, alpha ? tokens * d->H * d->dk * gb : 0),
                        range("beta", beta, beta ? tokens * d->H * gb : 0),
@@ -190,7 +200,7 @@ ckda_status_t run_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
   if (st != CKDA_OK) return st;
   if (d->num_seqs == 0) return ok();
   ckda::FwdArgs a{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
-                  d->use_qk_l2norm, d->gate_range, d->gate_input, d->scale, q, k, v, alpha, beta,
+                  qk_heads_of(d->H, d->qk_heads), d->use_qk_l2norm, d->gate_range, d->gate_input, d->scale, q, k, v, alpha, beta,
                   cu_seqlens, h0, o, ht, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
   return from_hip(ckda::launch_fwd(a, d->io_dtype, workspace, static_cast<hipStream_t>(stream),
                                    (passes & kPrepare) != 0, (passes & kFinish) != 0));
@@ -224,8 +234,8 @@ ckda_status_t ckda_chunk_fwd_finish(const ckda_fwd_desc_t* d, const void* v,
                  workspace_bytes, stream, kFinish);
 }
 
-ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
-                                  int32_t io_dtype, int32_t gate_range, int32_t gate_input,
+ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t qk_heads, int32_t dk,
+                                  int32_t dv, int32_t io_dtype, int32_t gate_range, int32_t gate_input,
                                   int32_t use_qk_l2norm, float scale, const void* q,
                                   const void* k, const void* v, const void* alpha,
                                   const void* beta, const float* h0,
@@ -238,6 +248,8 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
     return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_range %d is not a ckda_gate_t", gate_range);
   if (!valid_gate_input(gate_input))
     return fail(CKDA_ERR_INVALID_ARGUMENT, "gate_input %d is not a ckda_gate_input_t", gate_input);
+  if (!valid_qk_heads(H, qk_heads))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "qk_heads %d does not divide H=%d", qk_heads, H);
   if (use_qk_l2norm != 0 && use_qk_l2norm != 1)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
   if (N > 0 && (!q || !k || !v || !alpha || !beta || !h0 || !ht || !o))
@@ -248,12 +260,13 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
     if (ptrs[i] && !aligned16(ptrs[i]))
       return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
   const int64_t nh = static_cast<int64_t>(N) * H;
+  const int64_t nhk = static_cast<int64_t>(N) * qk_heads_of(H, qk_heads);
   const int64_t eb = elem_bytes(io_dtype);
   const int64_t gb = gate_bytes(gate_input);
   const int64_t sb = nh * dk * dv * 4;
   const Range ro = range("o", o, nh * dv * eb);
   const Range rht = range("ht", ht, sb);
-  const Range ins[] = {range("q", q, nh * dk * eb), range("k", k, nh * dk * eb),
+  const Range ins[] = {range("q", q, nhk * dk * eb), range("k", k, nhk * dk * eb),
                        range("v", v, nh * dv * eb), range("alpha", alpha, nh * dk * gb),
                        range("beta", beta, nh * gb), range("h0", h0, sb)};
   for (const Range& r : ins)
@@ -266,7 +279,7 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
   if (!ckda::step_supported(dk, dv))
     return fail(CKDA_ERR_UNSUPPORTED, "no decode kernel for dk=%d dv=%d", dk, dv);
   if (nh == 0) return ok();
-  ckda::StepArgs a{N, H, dk, dv, use_qk_l2norm, gate_range, gate_input, scale, q, k, v,
+  ckda::StepArgs a{N, H, dk, dv, qk_heads_of(H, qk_heads), use_qk_l2norm, gate_range, gate_input, scale, q, k, v,
                    alpha, beta, h0, ht, o};
   return from_hip(ckda::launch_step(a, io_dtype, static_cast<hipStream_t>(stream)));
 }

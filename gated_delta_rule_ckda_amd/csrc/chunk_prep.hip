@@ -250,11 +250,13 @@ __device__ __forceinline__ void direct_pass(const float* sgate, const typename C
 // which this path leaves unused): the gates stay, the k rows (A pass) and
 // then the q rows (P pass) take turns in the second slot.  DG lanes per
 // column j, DCH channels each.  Row r of the chunk starts at element
-// base + r * rowstride of q, k, alpha.  Every thread of the workgroup calls
+// qbase + r * qstride of q and k and at abase + r * astride of alpha.  Every
+// thread of the workgroup calls
 // this (it holds barriers).
 template <class Cfg, class G>
 __device__ __forceinline__ void direct_ap(const void* gq, const void* gk, const void* galpha,
-                                       bool ckda, int64_t base, int rowstride, int L, float scale,
+                                       bool ckda, int64_t qbase, int qstride, int64_t abase,
+                                       int astride, int L, float scale,
                                        typename Cfg::T* gP, unsigned char* smem, int tid) {
   using IO = typename Cfg::IO;
   using ST = typename IO::storage;
@@ -266,8 +268,8 @@ __device__ __forceinline__ void direct_ap(const void* gq, const void* gk, const 
   float* sgate = reinterpret_cast<float*>(smem + Cfg::O_DGATE);
   ST* srow = reinterpret_cast<ST*>(smem + Cfg::O_DROW);
 
-  stage_gates<Cfg, G>(sgate, galpha, ckda, base, rowstride, L, tid);
-  stage_io<Cfg>(srow, gk, base, rowstride, L, tid);
+  stage_gates<Cfg, G>(sgate, galpha, ckda, abase, astride, L, tid);
+  stage_io<Cfg>(srow, gk, qbase, qstride, L, tid);
   __syncthreads();
   const bool act = tid < DG * C;
   const int j = act ? tid / DG : 0, cg = tid % DG, c0 = cg * DCH;
@@ -290,7 +292,7 @@ __device__ __forceinline__ void direct_ap(const void* gq, const void* gk, const 
     }
   });
   __syncthreads();
-  stage_io<Cfg>(srow, gq, base, rowstride, L, tid);
+  stage_io<Cfg>(srow, gq, qbase, qstride, L, tid);
   __syncthreads();
   // P_rj = scale rq_r rk_j <q_r . D(r<-j), k_j>, j <= r, zero above
   direct_pass<Cfg>(sgate, srow, kj, j, c0, col, [&](int r, float s) {
@@ -324,7 +326,8 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int H = a.H;
+  const int H = a.H, Hk = a.Hk;
+  const int hk = h / (H / Hk);  // query/key head of value head h
 
   int64_t t0;
   int L;
@@ -362,13 +365,14 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   {
     constexpr int GES = static_cast<int>(sizeof(typename G::storage));
     constexpr int GB = CPT * GES, GW = (GB + 3) / 4;  // gate bytes (words) per row and lane
-    const int krow = H * DK * ES, arow = H * DK * GES;
-    const int64_t qk_off = (t0 * H + h) * static_cast<int64_t>(DK);
+    const int krow = Hk * DK * ES, arow = H * DK * GES;
+    const int64_t qk_off = (t0 * Hk + hk) * static_cast<int64_t>(DK);
+    const int64_t a_off = (t0 * H + h) * static_cast<int64_t>(DK);
     uint32_t rqv[RPW][Cfg::QW], rkv[RPW][Cfg::QW], rav[RPW][GW];
     if (scan_on) {
       const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + qk_off * ES, L * krow);
       const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + qk_off * ES, L * krow);
-      const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + qk_off * GES, L * arow);
+      const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + a_off * GES, L * arow);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int row = iclamp(r0 + i, L - 1);
@@ -534,12 +538,12 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
       }
     }
   } else {
-    direct_ap<Cfg, G>(a.q, a.k, a.alpha, ckda, (t0 * H + h) * static_cast<int64_t>(DK), H * DK,
-                      L, a.scale, gP, smem, tid);
+    direct_ap<Cfg, G>(a.q, a.k, a.alpha, ckda, (t0 * Hk + hk) * static_cast<int64_t>(DK), Hk * DK,
+                      (t0 * H + h) * static_cast<int64_t>(DK), H * DK, L, a.scale, gP, smem, tid);
     // Kh from suffix products of the gates (no division)
     if (scan_on) {
       // the direct path left the gates in LDS (1 past the end)
-      const int64_t qk_off = (t0 * H + h) * static_cast<int64_t>(DK);
+      const int64_t qk_off = (t0 * Hk + hk) * static_cast<int64_t>(DK);
       const float* sgate = reinterpret_cast<const float*>(smem + Cfg::O_DGATE);
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
@@ -549,7 +553,7 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
           const int r = r0 + i;
           // kh = k * prod_{s>r} alpha_s ; xk was overwritten by Rk, so reload k
           const float kr = (r < L) ? IO::load(static_cast<const typename IO::storage*>(a.k),
-                                              qk_off + static_cast<int64_t>(r) * H * DK + c0ch + cc)
+                                              qk_off + static_cast<int64_t>(r) * Hk * DK + c0ch + cc)
                                    : 0.f;
           kh[i][cc] = kr * suf;
           suf *= sgate[r * DK + c0ch + cc];

@@ -19,6 +19,7 @@ using launch_result = hipError_t;
 // Decode step (the recurrent form, one token per sequence).
 struct StepArgs {
   int32_t N, H, dk, dv;
+  int32_t Hk;          // q/k heads; value head h reads q/k head h / (H / Hk)
   int32_t use_l2norm;
   int32_t gate_range;  // ckda_gate_t
   int32_t gate_input;  // ckda_gate_input_t
@@ -65,6 +66,7 @@ __host__ __device__ constexpr int64_t blk_bytes(int C, int dk, int es) {
 
 struct FwdArgs {
   int32_t B, T, H, dk, dv, num_seqs, chunk;
+  int32_t Hk;  // q/k heads; value head h reads q/k head h / (H / Hk)
   int32_t use_l2norm;
   int32_t gate_range;  // ckda_gate_t
   int32_t gate_input;  // ckda_gate_input_t

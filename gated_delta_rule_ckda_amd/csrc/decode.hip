@@ -66,8 +66,10 @@ __global__ __launch_bounds__((StepShape<DK, DV>::NT)) void step_kernel(StepArgs 
 #pragma unroll
   for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&S0[(rg + RG * i) * CG + cg]);
 
-  const T* q = static_cast<const T*>(a.q) + nh * DK;
-  const T* k = static_cast<const T*>(a.k) + nh * DK;
+  // query/key head of this value head (grouped value heads share one)
+  const int64_t nhk = (nh / a.H) * a.Hk + (nh % a.H) / (a.H / a.Hk);
+  const T* q = static_cast<const T*>(a.q) + nhk * DK;
+  const T* k = static_cast<const T*>(a.k) + nhk * DK;
   const T* v = static_cast<const T*>(a.v) + nh * DV;
   const bool ckda = a.gate_range == CKDA_GATE_CKDA;
   for (int i = t; i < DK; i += NT) {

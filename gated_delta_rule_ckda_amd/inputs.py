@@ -149,6 +149,26 @@ def logit_case(seed, B, T, H, dk, dv, *, dtype="f32", chunk=16, l2norm=True, arm
                 gate_dtype=gate_dtype, arm=arm)
 
 
+def gva_case(seed, B, T, Hk, H, dk, dv, *, dtype="f32", chunk=16, l2norm=True, h0_std=0.0,
+             zero_frac=0.0) -> Case:
+    """Grouped value heads: q, k with Hk heads; v, alpha, beta, state with H
+    heads (H a multiple of Hk).  q,k,v ~ N(0,1); alpha = tanh(N(2,1)) with
+    zero_frac exact zeros; beta = 2 sigmoid(N(0,1))."""
+    rng = np.random.default_rng(seed)
+    q = _io(rng.standard_normal((B, T, Hk, dk), dtype=np.float32), dtype)
+    k = _io(rng.standard_normal((B, T, Hk, dk), dtype=np.float32), dtype)
+    v = _io(rng.standard_normal((B, T, H, dv), dtype=np.float32), dtype)
+    a = np.tanh(rng.normal(2, 1, (B, T, H, dk))).astype(np.float32)
+    if zero_frac > 0:
+        a[rng.random(a.shape) < zero_frac] = 0.0
+    b = (2 * _sigmoid(rng.normal(0, 1, (B, T, H)))).astype(np.float32)
+    h0 = None
+    if h0_std > 0:
+        h0 = (h0_std * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    return Case(q, k, v, a, b, h0, None, dtype, chunk, l2norm,
+                dict(B=B, T=T, H=H, Hk=Hk, dk=dk, dv=dv, seed=seed))
+
+
 def tiny(seed=1000) -> Case:
     c = random_case(seed, 1, 64, 2, 16, 16, dtype="f32", chunk=16, l2norm=True)
     c.meta["workload"] = "tiny CKDA forward B=1 H=2 T=64 d=16 fp32"

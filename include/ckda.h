@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 4
+#define CKDA_ABI_VERSION 5
 
 typedef enum {
   CKDA_OK = 0,
@@ -91,8 +91,14 @@ typedef enum {
 /*
  * Descriptor of one chunked forward call.
  *   Dense batch (cu_seqlens == NULL): num_seqs == B sequences of T tokens;
- *     q, k, alpha : [B][T][H][dk]   v, o : [B][T][H][dv]   beta : [B][T][H]
- *   (alpha and beta in the element type gate_input names)
+ *     q, k : [B][T][Hk][dk]   alpha : [B][T][H][dk]   v, o : [B][T][H][dv]
+ *     beta : [B][T][H]        (alpha and beta in the type gate_input names)
+ *   H counts the value heads (those of v, o, alpha, beta and the state) and
+ *   Hk = qk_heads the query/key heads (0 means Hk = H).  With Hk < H (grouped
+ *   value heads) H must be a multiple of Hk and value head h reads query/key
+ *   head h / (H / Hk), each q/k head serving H / Hk consecutive value heads
+ *   (dormouse review "RoPE into the KDA q/k path", section 7: q and k sit on
+ *   the key-head axis and are repeated over the value heads).
  *   Packed variable-length batch (cu_seqlens != NULL): B must be 1, T is the
  *     total token count, sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
  *     (empty sequences allowed; then ht[n] = h0[n]).
@@ -109,6 +115,7 @@ typedef struct {
   int32_t use_qk_l2norm; /* 0 or 1 */
   float scale;           /* o = scale * S^T q_hat */
   int32_t gate_input;    /* ckda_gate_input_t (0: float32 gate values) */
+  int32_t qk_heads;      /* Hk, heads of q and k; 0 = H */
 } ckda_fwd_desc_t;
 
 /*
@@ -181,14 +188,16 @@ int32_t ckda_fwd_supported(const ckda_fwd_desc_t* desc);
 /*
  * Fused single-token decode step for N sequences (the recurrent form of the
  * same recurrence, one token per sequence):
- *   q, k, alpha : [N][H][dk]   v, o : [N][H][dv]   beta : [N][H]
+ *   q, k : [N][Hk][dk]   alpha : [N][H][dk]   v, o : [N][H][dv]   beta : [N][H]
  *   h0, ht      : [N][H][dk][dv] float32; h0 == ht (in place) is allowed,
  *                 other partial overlaps are not.
- * alpha and beta hold what gate_input (a ckda_gate_input_t) says.
+ * Hk = qk_heads (0 means H) as for ckda_chunk_fwd: value head h reads
+ * query/key head h / (H / Hk).  alpha and beta hold what gate_input (a
+ * ckda_gate_input_t) says.
  * Supported: dk, dv in {16, 32, 64, 128}, both io dtypes, every gate input.
  */
-ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
-                                  int32_t io_dtype, int32_t gate_range,
+ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t qk_heads, int32_t dk,
+                                  int32_t dv, int32_t io_dtype, int32_t gate_range,
                                   int32_t gate_input, int32_t use_qk_l2norm,
                                   float scale, const void* q, const void* k,
                                   const void* v, const void* alpha, const void* beta,

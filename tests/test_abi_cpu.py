@@ -48,7 +48,8 @@ WS_BYTES = 1 << 31
 
 def _desc(**kw):
     d = dict(B=2, T=64, H=2, dk=128, dv=128, num_seqs=2, chunk_size=64, io_dtype=ck.BF16,
-             gate_range=ck.GATE_CKDA, use_qk_l2norm=1, scale=1.0, gate_input=ck.GATES_F32)
+             gate_range=ck.GATE_CKDA, use_qk_l2norm=1, scale=1.0, gate_input=ck.GATES_F32,
+             qk_heads=0)
     d.update(kw)
     return ck.FwdDesc(**d)
 
@@ -67,6 +68,7 @@ def _fwd(desc, **over):
     (dict(B=0), "non-positive"), (dict(H=-1), "non-positive"), (dict(dk=0), "non-positive"),
     (dict(io_dtype=7), "io_dtype"), (dict(gate_range=3), "gate_range"),
     (dict(gate_input=3), "gate_input"), (dict(gate_input=-1), "gate_input"),
+    (dict(qk_heads=3), "qk_heads"), (dict(qk_heads=-2), "qk_heads"),
     (dict(use_qk_l2norm=2), "use_qk_l2norm"), (dict(chunk_size=48), "chunk_size"),
     (dict(num_seqs=3), "num_seqs"),
 ])
@@ -153,6 +155,18 @@ def test_fwd_gate_byte_ranges_follow_gate_input():
     assert st == 1 and "o overlaps alpha" in msg
 
 
+def test_fwd_qk_byte_ranges_follow_qk_heads():
+    """With grouped value heads q and k span T * Hk * dk elements: o right after
+    q overlaps it at Hk = H but not at Hk = H / 2.  dk=96 has no kernel, so a
+    call that passes every other check stops at CKDA_ERR_UNSUPPORTED."""
+    kw = dict(B=1, num_seqs=1, H=4, dk=96, dv=96)
+    o = ctypes.c_void_p(P["q"].value + 64 * 2 * 96 * 2)
+    st, msg = _fwd(_desc(qk_heads=2, **kw), o=o)
+    assert st == 2, msg
+    st, msg = _fwd(_desc(qk_heads=4, **kw), o=o)
+    assert st == 1 and "o overlaps q" in msg
+
+
 def test_fwd_unsupported_shape():
     st, msg = _fwd(_desc(dk=96, dv=96))
     assert st == 2 and "no chunked kernel" in msg
@@ -167,11 +181,11 @@ def test_fwd_empty_is_ok_without_launch():
 
 
 def _step(N=4, H=2, dk=128, dv=128, dtype=ck.BF16, gate=ck.GATE_CKDA, l2=1, gi=ck.GATES_F32,
-          **over):
+          hk=0, **over):
     p = dict(P)
     p.update(over)
     lib = ck._load()
-    st = lib.ckda_recurrent_step(N, H, dk, dv, dtype, gate, gi, l2, 1.0, p["q"], p["k"], p["v"],
+    st = lib.ckda_recurrent_step(N, H, hk, dk, dv, dtype, gate, gi, l2, 1.0, p["q"], p["k"], p["v"],
                                  p["alpha"], p["beta"], p["h0"], p["ht"], p["o"], None)
     return st, lib.ckda_last_error().decode()
 
@@ -183,6 +197,8 @@ def test_step_validation():
     assert _step(gate=2)[0] == 1
     assert _step(gi=3)[0] == 1 and "gate_input" in _step(gi=3)[1]
     assert _step(N=0, gi=ck.GATES_LOGITS_BF16)[0] == 0
+    assert _step(H=4, hk=3)[0] == 1 and "qk_heads" in _step(H=4, hk=3)[1]
+    assert _step(N=0, H=4, hk=2)[0] == 0
     assert _step(l2=3)[0] == 1
     assert _step(q=None)[0] == 1
     assert _step(v=ctypes.c_void_p(BASE + 4))[0] == 1
