@@ -713,7 +713,9 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
   for (int w = 0; w < NW; ++w) masks[w] = static_cast<uint64_t>(uniform64(static_cast<int64_t>(smask[w])));
   __syncthreads();
-#pragma unroll 1
+  // unrolled, so that masks[] stays in registers (a loop over w with a
+  // run-time index would put the array in scratch memory)
+#pragma unroll
   for (int w = 0; w < NW; ++w) {
     uint64_t mm = masks[w];
     while (mm != 0) {
