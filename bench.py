@@ -12,7 +12,8 @@ its own (HBM-bound: algorithmic bytes / kernel time against 8 TB/s; the
 dominant one is the headline roofline), the
 oracle's CPU throughput on a bounded sample, and extra lines of context: the
 KDA-range arm (throughput ratio), the same layer with bf16 gate logits
-activated in-kernel, the packed varlen prefill and the decode step.  Inputs are synthetic (seeded), shaped like the method's workloads.
+activated in-kernel, the same layer through the sign-absorption comparison
+path, the packed varlen prefill and the decode step.  Inputs are synthetic (seeded), shaped like the method's workloads.
 """
 import argparse
 import hashlib
@@ -128,7 +129,7 @@ def time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall * 1000.0 / steps
 
 
-def fwd_plan(case, gate):
+def fwd_plan(case, gate, sign_absorb=False):
     import torch
     import gated_delta_rule_ckda_amd as ck
     dt = case.dtype
@@ -137,21 +138,22 @@ def fwd_plan(case, gate):
     h0 = None if case.h0 is None else to_dev(case.h0, "f32")
     cu = None if case.cu_seqlens is None else torch.from_numpy(case.cu_seqlens).to("cuda:0")
     return ck.ChunkFwdPlan(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
-                           use_qk_l2norm=case.l2norm, gate=gate, gates=case.gates)
+                           use_qk_l2norm=case.l2norm, gate=gate, gates=case.gates,
+                           sign_absorb=sign_absorb)
 
 
-def bench_fwd(case, steps, warmup, gate, passes=False):
+def bench_fwd(case, steps, warmup, gate, passes=False, sign_absorb=False):
     """Whole forward per step (both passes, one ckda_chunk_fwd call on a
     preallocated workspace); with passes=True also each pass alone."""
     import torch
     import gated_delta_rule_ckda_amd as ck
-    plan = fwd_plan(case, gate)
+    plan = fwd_plan(case, gate, sign_absorb)
     q, k, v, a, b, h0, cu = plan.args
 
     def step():
         ck.chunk_fwd(q, k, v, a, b, h0=h0, cu_seqlens=cu, chunk_size=case.chunk,
                      use_qk_l2norm=case.l2norm, gate=gate, out=plan.o, final_state=plan.ht,
-                     workspace=plan.ws, gates=case.gates)
+                     workspace=plan.ws, gates=case.gates, sign_absorb=sign_absorb)
 
     ms, wall_ms = time_launches(step, steps, warmup)
     per = {}
@@ -310,6 +312,12 @@ def main():
             "prep_ms": round(per_lg["prep"], 4), "state_ms": round(per_lg["state"], 4),
             "prep_algorithmic_bytes": lg_prep,
             "prep_frac": round(lg_prep / (per_lg["prep"] / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+        ms_sa, _, _ = bench_fwd(case, args.steps, args.warmup, "ckda", sign_absorb=True)
+        out["sign_absorbed"] = {
+            "workload": "LM layer as the headline, CKDA range run as a KDA forward on |alpha| "
+                        "with the gates' cumulative signs folded into q and k (comparison path)",
+            "tokens_per_s": round(tokens / (ms_sa / 1000.0), 1), "ms_per_step": round(ms_sa, 4),
+            "native_over_absorbed": round(ms_sa / ms, 4)}
         vl = inputs.varlen()
         ms_vl, _, _ = bench_fwd(vl, max(5, args.steps // 3), 2, "ckda")
         vl_tok = int(vl.cu_seqlens[-1])

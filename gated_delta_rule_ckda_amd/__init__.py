@@ -38,7 +38,7 @@ class FwdDesc(ctypes.Structure):
                 ("chunk_size", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("gate_range", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("gate_input", ctypes.c_int32),
-                ("qk_heads", ctypes.c_int32)]
+                ("qk_heads", ctypes.c_int32), ("sign_absorb", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -143,7 +143,7 @@ def _require(cond, msg):
 
 
 def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens,
-               gate_input=GATES_F32):
+               gate_input=GATES_F32, sign_absorb=False):
     """H: value heads (v.shape[-2]); the q/k heads are q.shape[-2]."""
     if cu_seqlens is not None:
         B, T = 1, q.shape[-3] if q.dim() == 3 else q.shape[1]
@@ -152,11 +152,12 @@ def _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqle
         B, T = q.shape[0], q.shape[1]
         N = B
     return FwdDesc(B, T, H, dk, dv, N, chunk_size, _dtype_code(q), _gate_code(gate),
-                   int(bool(use_qk_l2norm)), float(scale), gate_input, q.shape[-2])
+                   int(bool(use_qk_l2norm)), float(scale), gate_input, q.shape[-2],
+                   int(bool(sign_absorb)))
 
 
 def fwd_supported(chunk_size, dk, dv, dtype) -> bool:
-    d = FwdDesc(1, 1, 1, dk, dv, 1, chunk_size, dtype, GATE_CKDA, 1, 1.0, GATES_F32, 0)
+    d = FwdDesc(1, 1, 1, dk, dv, 1, chunk_size, dtype, GATE_CKDA, 1, 1.0, GATES_F32, 0, 0)
     return bool(_load().ckda_fwd_supported(ctypes.byref(d)))
 
 
@@ -167,13 +168,16 @@ def chunk_fwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
 
 def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
               use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
-              out=None, final_state=None, workspace=None, stream=None, gates="values"):
+              out=None, final_state=None, workspace=None, stream=None, gates="values",
+              sign_absorb=False):
     """Chunked prefill.  Dense: q,k [B,T,Hk,dk], alpha [B,T,H,dk], v [B,T,H,dv],
     beta [B,T,H]; Hk divides H (grouped value heads: value head h reads q/k
     head h // (H // Hk)).  Packed (cu_seqlens int32 [N+1]): leading [1,T,...]
     or [T,...].
     gates='values': alpha, beta are float32 gates; gates='logits': they are
-    float32 or bfloat16 logits that the kernels activate.
+    float32 or bfloat16 logits that the kernels activate.  sign_absorb=True
+    runs the comparison strategy that folds the gates' cumulative signs into
+    q and k (same result, more traffic).
     `workspace`: optional uint8 device tensor of at least
     chunk_fwd_workspace_size() bytes (allocated per call when omitted).
     Returns (o, ht) with ht [N,H,dk,dv] float32 (None if not requested)."""
@@ -187,7 +191,8 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
     if cu_seqlens is not None:
         _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda,
                  "cu_seqlens must be an int32 device tensor")
-    desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens, gi)
+    desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens, gi,
+                      sign_absorb)
     _require(q.numel() == desc.B * desc.T * desc.qk_heads * dk, "q has the wrong number of elements")
     _require(k.numel() == q.numel(), "k must match q")
     _require(alpha.numel() == desc.B * desc.T * H * dk, "alpha has the wrong number of elements")
@@ -219,12 +224,12 @@ class ChunkFwdPlan:
 
     def __init__(self, q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
                  use_qk_l2norm=True, gate="ckda", scale=1.0, out=None, final_state=None,
-                 stream=None, gates="values"):
+                 stream=None, gates="values", sign_absorb=False):
         import torch
         self.lib = _load()
         H, dk, dv = v.shape[-2], q.shape[-1], v.shape[-1]
         self.desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale,
-                               cu_seqlens, _gate_input(gates, alpha, beta))
+                               cu_seqlens, _gate_input(gates, alpha, beta), sign_absorb)
         self.args = (q, k, v, alpha, beta, h0, cu_seqlens)
         self.o = torch.empty_like(v) if out is None else out
         self.ht = (torch.empty((self.desc.num_seqs, H, dk, dv), device=q.device,

@@ -92,7 +92,7 @@ size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* d, int32_t packed) {
   if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64) return 0;
   if (static_cast<int64_t>(d->B) * d->T == 0 || d->num_seqs == 0) return 0;
   return ckda::fwd_workspace_bytes(d->B, d->T, d->H, d->dk, d->num_seqs, d->chunk_size,
-                                   d->io_dtype, packed != 0);
+                                   d->io_dtype, packed != 0, d->sign_absorb == 1);
 }
 
 }  // extern "C"
@@ -124,6 +124,8 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
                 d->gate_input);
   if (!valid_qk_heads(d->H, d->qk_heads))
     return fail(CKDA_ERR_INVALID_ARGUMENT, "qk_heads %d does not divide H=%d", d->qk_heads, d->H);
+  if (d->sign_absorb != 0 && d->sign_absorb != 1)
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "sign_absorb must be 0 or 1");
   if (d->use_qk_l2norm != 0 && d->use_qk_l2norm != 1)
     return fail(CKDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
   if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64)
@@ -200,7 +202,8 @@ ckda_status_t run_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
   if (st != CKDA_OK) return st;
   if (d->num_seqs == 0) return ok();
   ckda::FwdArgs a{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
-                  qk_heads_of(d->H, d->qk_heads), d->use_qk_l2norm, d->gate_range, d->gate_input, d->scale, q, k, v, alpha, beta,
+                  qk_heads_of(d->H, d->qk_heads), d->use_qk_l2norm, d->gate_range, d->gate_input,
+                  d->sign_absorb, d->scale, q, k, v, alpha, beta,
                   cu_seqlens, h0, o, ht, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
   return from_hip(ckda::launch_fwd(a, d->io_dtype, workspace, static_cast<hipStream_t>(stream),
                                    (passes & kPrepare) != 0, (passes & kFinish) != 0));

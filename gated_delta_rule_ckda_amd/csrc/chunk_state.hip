@@ -458,12 +458,14 @@ bool fwd_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype) {
 }
 
 size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t num_seqs,
-                           int32_t chunk, int32_t io_dtype, bool packed) {
+                           int32_t chunk, int32_t io_dtype, bool packed, bool sign_absorb) {
   const int64_t maxc = max_chunks(B, T, num_seqs, chunk, packed);
   const int64_t es = io_dtype == CKDA_DTYPE_BF16 ? 2 : 4;
   const int64_t map = packed ? ((4 * (num_seqs + 1 + maxc) + 255) & ~int64_t(255)) : 0;
   const int64_t flags = (4 * static_cast<int64_t>(H) * maxc + 255) & ~int64_t(255);
-  return static_cast<size_t>(map + flags + static_cast<int64_t>(H) * maxc * blk_bytes(chunk, dk, es));
+  const int64_t sign = sign_absorb ? sign_workspace_bytes(B, T, H, dk, num_seqs, maxc, io_dtype) : 0;
+  return static_cast<size_t>(map + flags + static_cast<int64_t>(H) * maxc * blk_bytes(chunk, dk, es) +
+                             sign);
 }
 
 launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream,
@@ -492,18 +494,39 @@ launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stre
   a.irregular = reinterpret_cast<int32_t*>(base);
   base += (4 * static_cast<int64_t>(a.H) * maxc + 255) & ~int64_t(255);
   a.blocks = base;
+  base += static_cast<int64_t>(a.H) * maxc * a.blk_bytes;
   const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
   if (!e) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.num_seqs) * a.H == 0) return hipSuccess;
+  // sign absorption: a chain with no tokens has nothing to absorb
+  const bool absorb = a.sign_absorb != 0 && static_cast<int64_t>(a.B) * a.T > 0;
+  FwdArgs run = a;
+  if (absorb) {
+    sign_layout(run, base, io_dtype);
+    a = run;  // the sign passes read the caller's tensors through `a`
+    run.q = run.sq;
+    run.k = run.sk;
+    run.alpha = run.sa;
+    run.beta = run.sb;
+    run.Hk = run.H;
+    run.gate_input = CKDA_GATES_F32;
+  }
   if (prepare && packed) {
     const launch_result r = launch_chunk_map(a, stream);
     if (r != hipSuccess) return r;
   }
-  if (prepare && maxc > 0) {
-    const launch_result r = launch_prep(a, io_dtype, stream);
+  if (prepare && absorb) {
+    const launch_result r = launch_sign_absorb(a, io_dtype, stream);
     if (r != hipSuccess) return r;
   }
-  return finish ? e->fn(a, stream) : hipSuccess;
+  if (prepare && maxc > 0) {
+    const launch_result r = launch_prep(run, io_dtype, stream);
+    if (r != hipSuccess) return r;
+  }
+  if (!finish) return hipSuccess;
+  const launch_result r = e->fn(run, stream);
+  if (r != hipSuccess || !absorb) return r;
+  return launch_sign_fix(run, stream);
 }
 
 }  // namespace ckda

@@ -70,6 +70,7 @@ struct FwdArgs {
   int32_t use_l2norm;
   int32_t gate_range;  // ckda_gate_t
   int32_t gate_input;  // ckda_gate_input_t
+  int32_t sign_absorb; // 1: run as a KDA forward on |alpha| with the signs folded into q, k
   float scale;
   const void* q;
   const void* k;
@@ -88,11 +89,18 @@ struct FwdArgs {
   int32_t maxc;           // chunk slots per head
   int32_t nc;             // chunks per sequence (dense batches)
   int64_t blk_bytes;
+  // sign absorption buffers (sign_absorb = 1), laid out by the launcher
+  uint32_t* cmask;        // [H][maxc][ceil(dk/32)] sign parity of each chunk
+  uint32_t* tmask;        // [num_seqs][H][ceil(dk/32)] final parity of each sequence
+  void* sq;               // [B*T][H][dk] Sigma q (io type)
+  void* sk;               // [B*T][H][dk] Sigma k (io type)
+  float* sa;              // [B*T][H][dk] |alpha|
+  float* sb;              // [B*T][H] beta
 };
 bool fwd_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype);
 // Workspace bytes ckda_chunk_fwd needs for these sizes (0 for an empty call).
 size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t num_seqs,
-                           int32_t chunk, int32_t io_dtype, bool packed);
+                           int32_t chunk, int32_t io_dtype, bool packed, bool sign_absorb);
 // Lays out the workspace in `a` and enqueues the transform pass (with the
 // chunk map of a packed batch) and/or the state pass.
 launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream,
@@ -103,6 +111,14 @@ launch_result launch_prep(const FwdArgs& a, int32_t io_dtype, hipStream_t stream
 launch_result launch_chunk_map(const FwdArgs& a, hipStream_t stream);
 bool state_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype);
 launch_result launch_state(const FwdArgs& a, int32_t io_dtype, hipStream_t stream);
+// Sign absorption (sign_absorb.hip): workspace bytes beyond the plain
+// forward's, their layout from `base`, the passes before the transform pass
+// and the row flips of ht after the state pass.
+int64_t sign_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t num_seqs,
+                             int64_t maxc, int32_t io_dtype);
+void sign_layout(FwdArgs& a, unsigned char* base, int32_t io_dtype);
+launch_result launch_sign_absorb(const FwdArgs& a, int32_t io_dtype, hipStream_t stream);
+launch_result launch_sign_fix(const FwdArgs& a, hipStream_t stream);
 
 // ---- small device helpers shared by the kernels --------------------------
 

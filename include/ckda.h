@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 5
+#define CKDA_ABI_VERSION 6
 
 typedef enum {
   CKDA_OK = 0,
@@ -116,7 +116,23 @@ typedef struct {
   float scale;           /* o = scale * S^T q_hat */
   int32_t gate_input;    /* ckda_gate_input_t (0: float32 gate values) */
   int32_t qk_heads;      /* Hk, heads of q and k; 0 = H */
+  int32_t sign_absorb;   /* 0: native signed gates; 1: global sign absorption */
 } ckda_fwd_desc_t;
+
+/*
+ * sign_absorb = 1 selects a second strategy for signed gates, kept for
+ * comparison (picx.dev summary, section "Implementation": cumulative signs
+ * folded into the keys and queries, then an unmodified KDA kernel on
+ * |alpha|).  Before the transform pass, two extra passes compute every key
+ * channel's cumulative sign since the start of its sequence and write
+ * sign * q, sign * k, |alpha| and beta (float32) into the workspace; the
+ * unchanged passes then run on those, and a last pass negates the rows of ht
+ * whose channel ended with a negative sign.  Sign flips are exact, so the
+ * result equals the native one (bit for bit on regular chunks); the extra
+ * passes cost one more read of q, k, alpha and a write of their absorbed
+ * copies.  The default, 0, carries the signs inside the transform pass's
+ * running gate products at no extra cost.
+ */
 
 /*
  * Bytes of device workspace ckda_chunk_fwd needs for this descriptor; 0 for
@@ -125,8 +141,9 @@ typedef struct {
  * sizes, never on data: one block of chunk operands and one int32 flag per
  * (head, chunk), with at most ceil(T / chunk_size) * B chunks for a dense
  * batch and ceil(T / chunk_size) + num_seqs for a packed one, plus the chunk
- * map of a packed batch.  At B=8, T=4096, H=16, dk=128, chunk 64, bf16:
- * 516 MiB.
+ * map of a packed batch, plus (sign_absorb = 1) the absorbed q, k, |alpha|,
+ * beta for every value head and two sign masks.  At B=8, T=4096, H=16,
+ * dk=128, chunk 64, bf16: 516 MiB (1.03 GiB with sign_absorb).
  */
 size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed);
 

@@ -49,7 +49,7 @@ WS_BYTES = 1 << 31
 def _desc(**kw):
     d = dict(B=2, T=64, H=2, dk=128, dv=128, num_seqs=2, chunk_size=64, io_dtype=ck.BF16,
              gate_range=ck.GATE_CKDA, use_qk_l2norm=1, scale=1.0, gate_input=ck.GATES_F32,
-             qk_heads=0)
+             qk_heads=0, sign_absorb=0)
     d.update(kw)
     return ck.FwdDesc(**d)
 
@@ -69,6 +69,7 @@ def _fwd(desc, **over):
     (dict(io_dtype=7), "io_dtype"), (dict(gate_range=3), "gate_range"),
     (dict(gate_input=3), "gate_input"), (dict(gate_input=-1), "gate_input"),
     (dict(qk_heads=3), "qk_heads"), (dict(qk_heads=-2), "qk_heads"),
+    (dict(sign_absorb=2), "sign_absorb"),
     (dict(use_qk_l2norm=2), "use_qk_l2norm"), (dict(chunk_size=48), "chunk_size"),
     (dict(num_seqs=3), "num_seqs"),
 ])
@@ -110,6 +111,13 @@ def test_workspace_size_formula():
     maxc = -(-70 // 16) + 4
     assert ck.chunk_fwd_workspace_size(d, True) == (up(4 * (4 + 1 + maxc)) + up(4 * 3 * maxc)
                                                    + 3 * maxc * blk)
+    # sign absorption adds two sign masks and the absorbed q, k, |alpha|, beta
+    d0 = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8)
+    d1 = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8, sign_absorb=1)
+    tok, maxc = 8 * 4096, 8 * 64
+    extra = (up(4 * 16 * maxc * 4) + up(4 * 8 * 16 * 4) + 2 * up(tok * 16 * 128 * 2)
+             + up(tok * 16 * 128 * 4) + up(tok * 16 * 4))
+    assert ck.chunk_fwd_workspace_size(d1, False) - ck.chunk_fwd_workspace_size(d0, False) == extra
     assert ck.chunk_fwd_workspace_size(_desc(T=0), False) == 0
     assert ck.chunk_fwd_workspace_size(_desc(chunk_size=48), False) == 0
 
