@@ -46,6 +46,9 @@ struct StateCfg {
   static constexpr int KS = Op::KS;                  // K per register fragment
   static constexpr int NFK = (DK + KS - 1) / KS;     // fragments over dk
   static constexpr int NFC = (C + KS - 1) / KS;      // fragments over the chunk rows
+  // X' and P' are lower triangular: K fragment s of row block rb holds a
+  // nonzero only if its first column is at or left of the block's last row
+  static constexpr bool tri_live(int rb, int s) { return KS * s <= 16 * rb + 15; }
 
   // the block in global memory (bytes)
   static constexpr int GB_X = 0;
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
         for (int rb = 0; rb < NB; ++rb) {
 #pragma unroll
           for (int s = 0; s < Cfg::NFC; ++s)
-            xf[rb][s] = Op::template row_frag<C>(sX + (16 * rb + l16) * LDC, s, lq);
+            if (Cfg::tri_live(rb, s)) xf[rb][s] = Op::template row_frag<C>(sX + (16 * rb + l16) * LDC, s, lq);
 #pragma unroll
           for (int s = 0; s < Cfg::NFK; ++s)
             wf[rb][s] = Op::template row_frag<DK>(sW + (16 * rb + l16) * LDK, s, lq);
@@ -289,7 +292,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
         for (int rb = 0; rb < NB; ++rb) {
           uacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < Cfg::NFC; ++s) Op::mma(uacc[rb], xf[rb][s], vf[s]);
+          for (int s = 0; s < Cfg::NFC; ++s)
+            if (Cfg::tri_live(rb, s)) Op::mma(uacc[rb], xf[rb][s], vf[s]);
 #pragma unroll
           for (int s = 0; s < Cfg::NFK; ++s) Op::mma(uacc[rb], wf[rb][s], sf[s]);
         }
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
             qf[rb][s] = Op::template row_frag<DK>(sQ + (16 * rb + l16) * LDK, s, lq);
 #pragma unroll
           for (int s = 0; s < Cfg::NFC; ++s)
-            pf[rb][s] = Op::template row_frag<C>(sP + (16 * rb + l16) * LDC, s, lq);
+            if (Cfg::tri_live(rb, s)) pf[rb][s] = Op::template row_frag<C>(sP + (16 * rb + l16) * LDC, s, lq);
         }
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
@@ -315,7 +319,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
 #pragma unroll
           for (int s = 0; s < Cfg::NFK; ++s) Op::mma(oacc, sf[s], qf[rb][s]);
 #pragma unroll
-          for (int s = 0; s < Cfg::NFC; ++s) Op::mma(oacc, uf[s], pf[rb][s]);
+          for (int s = 0; s < Cfg::NFC; ++s)
+            if (Cfg::tri_live(rb, s)) Op::mma(oacc, uf[s], pf[rb][s]);
           const int r = 16 * rb + l16;
           if (r < L)
             IO::store4(go + ((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0 + 16 * wave + 4 * lq,
