@@ -312,6 +312,15 @@ def main():
             "prep_ms": round(per_lg["prep"], 4), "state_ms": round(per_lg["state"], 4),
             "prep_algorithmic_bytes": lg_prep,
             "prep_frac": round(lg_prep / (per_lg["prep"] / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+        fd = inputs.fast_decay(case)
+        ms_fd, _, per_fd = bench_fwd(fd, args.steps, args.warmup, "ckda", passes=True)
+        out["fast_decay"] = {
+            "workload": fd.meta["workload"] + " (chunk-wide gate products below 2^-100: "
+                        "products restarted every 16 rows)",
+            "tokens_per_s": round(tokens / (ms_fd / 1000.0), 1), "ms_per_step": round(ms_fd, 4),
+            "prep_ms": round(per_fd["prep"], 4), "state_ms": round(per_fd["state"], 4),
+            "over_headline": round(ms_fd / ms, 4)}
+        del fd
         ms_sa, _, _ = bench_fwd(case, args.steps, args.warmup, "ckda", sign_absorb=True)
         out["sign_absorbed"] = {
             "workload": "LM layer as the headline, CKDA range run as a KDA forward on |alpha| "

@@ -18,19 +18,30 @@
 // Kh_j = D(end<-j) . k^_j, g = D(end<-start).  Hence U = X' V - W S0 with
 // X' = X Diag(beta) and W = X Diag(beta) Kt, which is what the state pass runs.
 //
-// Gate prefix.  The running product Ft_r = prod_{s<=r} alpha_s (per channel,
-// fp32) carries sign and magnitude together: signs are exact under
-// multiplication and an exact zero gate makes every later product exactly
-// zero.  A chunk is "regular" when every |Ft_r| lies in [2^-100, 2^10]; then
-// D(r<-j) = Ft_r * (1 / Ft_j) with no factor able to overflow, and
-//   Lk = k . Ft (= Kt / rk),  Lq = q . Ft,  Rk = k / Ft,  Kh = rk g . Rk,
-//   A = tril(Diag(beta rk) Lk Rk^T Diag(rk), -1),  P = tril(Diag(rq) Lq Rk^T Diag(rk))
-// run on MFMA.  Other chunks (exact zero gates, products that underflow the
-// range, non-finite values) are flagged and left to a second, short launch
-// that forms A, P and Kh from direct products of the gates (staged in LDS):
-// exact, slower, absent from realistic gate distributions.  Keeping that
-// path out of the MFMA kernel keeps the kernel's registers to what the
-// regular chunks need.
+// Gate prefix.  Running products of the gates (per channel, fp32) carry sign
+// and magnitude together: signs are exact under multiplication and an exact
+// zero gate makes every later product exactly zero.  Ft_r = prod_{s<=r}
+// alpha_s from the chunk start gives Kt = k . Ft, Qt = q . Ft and g, all
+// plain products.  A and P use ratios of products anchored either at the
+// chunk start or at the start of every 16-row block (the MFMA tile height):
+// with Fb_r the product over block(r)'s rows up to r and T_b the total of
+// block b, for r in block I and j in block J <= I
+//   D(r<-j) = Fb_r * E_IJ * (1 / Fb_j),   E_IJ = prod_{J <= b < I} T_b
+// (E_II = 1), so with Lk = k . Fb, Lq = q . Fb, Rk = k / Fb every tile is one
+// MFMA whose right operand is scaled per channel by E_IJ on its way in:
+//   A_IJ = Diag(beta rk) Lk_I (Rk_J . E_IJ)^T Diag(rk),
+//   P_IJ = Diag(rq) Lq_I (Rk_J . E_IJ)^T Diag(rk),   Kh = rk . Rk . prod_{b>=J} T_b.
+// E_IJ and Kt are products, so gates that decay fast over the chunk only make
+// them small, never wrong.  When every |Ft_r| of the chunk lies in
+// [2^-100, 2^10] (the usual case) the anchor is the chunk start instead
+// (Fb = Ft, every E_IJ = 1, no scaling); otherwise, when every |Fb_r| lies in
+// that range (a condition on 16 consecutive gates), the block anchors are
+// used.  Chunks that pass neither test (exact zero gates, products that
+// underflow over 16 tokens, non-finite values) are flagged and left to a
+// second, short launch that forms A, P and Kh from direct products of the
+// gates (staged in LDS): exact, slower, absent from realistic gate
+// distributions.  Keeping that path out of the MFMA kernel keeps the
+// kernel's registers to what the other chunks need.
 //
 // Gates arrive as float32 values or as logits (float32 or bf16) activated on
 // load (ckda_internal.h).
@@ -40,7 +51,8 @@
 //
 // Phases (eight waves; wave w owns rows w*C/8 .. in the element-wise phases):
 //   1  loads, running products within the wave's rows, row norms
-//   2  chunk-level products Ft, regularity vote, operands Lk, Lq, Rk; Qt', g out
+//   2  chunk-level products Ft, anchor choice, regularity vote, operands Lk,
+//      Lq, Rk (and E_IJ for block anchors); Qt', g out
 //   3  A and P on MFMA (the direct kernel: from direct products); P' out
 //   4  Kt'^T to LDS, Kh'^T out; 16x16 diagonal blocks of X by forward substitution
 //   5  off-diagonal blocks X_IJ = -X_II sum_{J<=M<I} A_IM X_MJ on fp32 MFMA
@@ -107,8 +119,8 @@ struct PrepCfg {
   static constexpr int O_RQ = O_G + NW * DK * 4;                        // rq [C]
   static constexpr int O_RK2 = O_RQ + C * 4;                            // rk [C]
   static constexpr int O_BETA = O_RK2 + C * 4;                          // beta [C]
-  static constexpr int O_FLAG = O_BETA + C * 4;                         // regularity votes [NW]
-  static constexpr int LDS_BYTES = align16(O_FLAG + NW * 4);
+  static constexpr int O_FLAG = O_BETA + C * 4;                         // regularity votes [2][NW]
+  static constexpr int LDS_BYTES = align16(O_FLAG + 2 * NW * 4);
   // direct path staging, inside the operand region it leaves unused
   static constexpr int O_DGATE = 0;                                     // gates [C][DK] fp32
   static constexpr int O_DROW = C * DK * 4;                             // q or k rows [C][DK]
@@ -137,6 +149,60 @@ __device__ __forceinline__ void lower_block(int idx, int& I, int& J) {
     ++I;
   }
   J = idx;
+}
+
+// One lower 16x16 tile (I, J) of A and of P^T from the same right operand:
+// acc_a += Lk_I (Rk_J . E)^T and acc_p += (Rk_J . E) Lq_I^T over K = DK, where
+// the fp32 vector e[0..DK) (the gate product between the blocks) scales the K
+// index of Rk on its way into the MFMA; e == nullptr (a diagonal tile) leaves
+// it unscaled.  Operand rows are [16][LDK] in LDS.
+template <class Cfg>
+__device__ __forceinline__ void tile_ap(f32x4& acc_a, f32x4& acc_p, const typename Cfg::T* lk,
+                                        const typename Cfg::T* lq, const typename Cfg::T* rk,
+                                        const float* e, int lane) {
+  using Op = typename Cfg::Op;
+  constexpr int DK = Cfg::DK, LDK = Cfg::LDK;
+  const int r = lane & 15, kq = lane >> 4;
+  if constexpr (sizeof(typename Op::T) == 2) {
+    static_assert(DK % 32 == 0, "bf16 operand rows");
+    constexpr int NS = DK / 32;
+    // one K slice at a time: three fragments live, not 3 * NS
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 fa = *reinterpret_cast<const bf16x8*>(lk + r * LDK + 32 * s + 8 * kq);
+      const bf16x8 fq = *reinterpret_cast<const bf16x8*>(lq + r * LDK + 32 * s + 8 * kq);
+      bf16x8 fb = *reinterpret_cast<const bf16x8*>(rk + r * LDK + 32 * s + 8 * kq);
+      if (e) {
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(e + 32 * s + 8 * kq);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(e + 32 * s + 8 * kq + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fb[i] = Op::cvt(static_cast<float>(fb[i]) * e0[i]);
+          fb[4 + i] = Op::cvt(static_cast<float>(fb[4 + i]) * e1[i]);
+        }
+      }
+      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc_a, 0, 0, 0);
+      acc_p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fq, acc_p, 0, 0, 0);
+    }
+  } else {
+    constexpr int NS = DK / 4;
+    float fa[NS], fq[NS], fb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      fa[s] = lk[r * LDK + kq + 4 * s];
+      fq[s] = lq[r * LDK + kq + 4 * s];
+      fb[s] = rk[r * LDK + kq + 4 * s];
+    }
+    if (e) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fb[s] *= e[kq + 4 * s];
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      acc_a = mfma_f32(fa[s], fb[s], acc_a);
+      acc_p = mfma_f32(fb[s], fq[s], acc_p);
+    }
+  }
 }
 
 // Chunk rows 0..C-1 of a q/k/alpha-shaped tensor (row r at element
@@ -431,50 +497,102 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
 
   // ================= 2: chunk products, regularity, operands =================
   float kt[RPW][CPT], kh[RPW][CPT], gch[CPT], gsuf[CPT];
+  bool canchor = false;  // operands anchored at the chunk start (no E_IJ)
   {
+    constexpr int WPB = 16 / RPW;       // waves per 16-row block
+    const int wb0 = wave - wave % WPB;  // first wave of this wave's block
     bool ok = true;
-    float rqs[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) rqs[i] = a.scale * srq[r0 + i];
+    // products of the wave totals: before this wave from the chunk start
+    // (gpre) and from the block start (bpre), from the block start to the
+    // chunk end (gbs), after this wave (gsuf), all (gch)
+    float gpre[CPT], bpre[CPT], gbs[CPT];
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
-      float gpre = 1.f, g = 1.f, gs = 1.f;
+      float gp = 1.f, bp = 1.f, g = 1.f, gs = 1.f, bs = 1.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float gw = scan_on ? sG[w * DK + c0ch + cc] : 1.f;
-        if (w < wave) gpre *= gw;
+        if (w < wave) gp *= gw;
+        if (w < wave && w >= wb0) bp *= gw;
         if (w > wave) gs *= gw;
+        if (w >= wb0) bs *= gw;
         g *= gw;
       }
+      gpre[cc] = gp;
+      bpre[cc] = bp;
+      gbs[cc] = bs;
       gch[cc] = g;
       gsuf[cc] = gs;
+    }
+    if (scan_on && wave == 0) {
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const float ft = gpre * F[i][cc];
-        const float mag = fabsf(ft);
-        ok = ok && (!scan_on || ((mag >= kRegularMin) && (mag <= kRegularMax)));
-        const float rinv = __builtin_amdgcn_rcpf(ft);
-        kt[i][cc] = xk[i][cc] * ft;    // Lk
-        xq[i][cc] = xq[i][cc] * ft;    // Lq
-        xk[i][cc] = xk[i][cc] * rinv;  // Rk
-        kh[i][cc] = xk[i][cc] * g;     // Kh / rk (regular chunks)
+      for (int cc = 0; cc < CPT; ++cc) gg[c0ch + cc] = gch[cc];
+    }
+    // chunk anchors when every |Ft| of the chunk is in range (then E_IJ = 1
+    // factors out of every tile), else block anchors
+    if constexpr (!DIRECT) {
+      bool okc = true;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+          const float mag = fabsf(gpre[cc] * F[i][cc]);
+          okc = okc && (!scan_on || ((mag >= kRegularMin) && (mag <= kRegularMax)));
+        }
+      const bool wave_okc = __all(okc);
+      if (lane == 0) sFlag[NW + wave] = wave_okc ? 1 : 0;
+      __syncthreads();  // B1b
+      int cv = 1;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) cv &= sFlag[NW + w];
+      canchor = uniform32(cv) != 0;
+    }
+    if (canchor) {
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        bpre[cc] = gpre[cc];
+        gbs[cc] = gch[cc];
       }
     }
-    if (scan_on) {
-      if (wave == 0) {
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) gg[c0ch + cc] = gch[cc];
+    for (int i = 0; i < RPW; ++i) {
+      const int r = r0 + i;
+      const float rq = a.scale * srq[r];
+      float qv[CPT], lq[CPT], lk[CPT];
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        const float ft = gpre[cc] * F[i][cc];  // D(r <- chunk start)
+        const float fb = bpre[cc] * F[i][cc];  // D(r <- anchor)
+        const float mag = fabsf(fb);
+        ok = ok && (!scan_on || ((mag >= kRegularMin) && (mag <= kRegularMax)));
+        const float rinv = __builtin_amdgcn_rcpf(fb);
+        qv[cc] = xq[i][cc] * ft * rq;     // Qt'
+        lq[cc] = xq[i][cc] * fb;          // Lq
+        lk[cc] = xk[i][cc] * fb;          // Lk
+        kt[i][cc] = xk[i][cc] * ft;       // Kt / rk
+        xk[i][cc] = xk[i][cc] * rinv;     // Rk
+        kh[i][cc] = xk[i][cc] * gbs[cc];  // Kh / rk (regular chunks)
       }
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int r = r0 + i;
-        float qv[CPT];
-#pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) qv[cc] = xq[i][cc] * rqs[i];
+      if (scan_on) {
         store_run<Op, CPT>(gQ + r * DK + Op::template pos<DK>(c0ch), qv);
-        store_run<Op, CPT>(sLk + r * LDK + c0ch, kt[i]);
-        store_run<Op, CPT>(sLq + r * LDK + c0ch, xq[i]);
+        store_run<Op, CPT>(sLk + r * LDK + c0ch, lk);
+        store_run<Op, CPT>(sLq + r * LDK + c0ch, lq);
         store_run<Op, CPT>(sRk + r * LDK + c0ch, xk[i]);
+      }
+    }
+    // E_IJ = prod_{J <= b < I} T_b (the product of the wave totals of waves
+    // WPB*J .. WPB*I-1) for every off-diagonal tile, into the X block (I, J),
+    // which holds nothing until the off-diagonal levels of X are formed
+    if (!DIRECT && NB > 1 && !canchor) {
+      constexpr int NPR = NB * (NB - 1) / 2;
+      for (int e = tid; e < NPR * DK; e += NT) {
+        const int pr = e / DK, ch = e % DK;
+        int I = 1;
+        while (I * (I + 1) / 2 <= pr) ++I;
+        const int J = pr - I * (I - 1) / 2;
+        float v = 1.f;
+        for (int w = WPB * J; w < WPB * I; ++w) v *= sG[w * DK + ch];
+        x_blk<Cfg>(smem, I, J)[ch] = v;
       }
     }
     const bool wave_ok = __all(ok);
@@ -492,9 +610,9 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
 
   // ================= 3: A and P ================================================
   if constexpr (!DIRECT) {
-    constexpr int NPT = NB * (NB + 1) / 2;  // lower blocks per matrix
+    constexpr int NPT = NB * (NB + 1) / 2;  // lower blocks (A and P together)
     constexpr int NZ = NB * (NB - 1) / 2;   // zero blocks of P above the diagonal
-    constexpr int NTILE = 2 * NPT + NZ;
+    constexpr int NTILE = NPT + NZ;
     constexpr int NU = (NTILE + NW - 1) / NW;
 #pragma unroll 1
     for (int u = 0; u < NU; ++u) {
@@ -502,36 +620,36 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
       if (tt < NPT) {
         int I, J;
         lower_block(tt, I, J);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        Op::template mmaK<DK>(acc, sLk + 16 * I * LDK, LDK, sRk + 16 * J * LDK, LDK, lane);
-        // rows r = 16I + 4lq + i, column j = 16J + l16
-        const int j = 16 * J + l16;
-        const float sj = srk[j];
-        float* dst = (I == J) ? x_blk<Cfg>(smem, I, I) : a_blk<Cfg>(smem, I, J);
+        f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_p = {0.f, 0.f, 0.f, 0.f};
+        tile_ap<Cfg>(acc_a, acc_p, sLk + 16 * I * LDK, sLq + 16 * I * LDK, sRk + 16 * J * LDK,
+                     (I > J && !canchor) ? x_blk<Cfg>(smem, I, J) : nullptr, lane);
+        {
+          // A: rows r = 16I + 4lq + i, column j = 16J + l16
+          const int j = 16 * J + l16;
+          const float sj = srk[j];
+          float* dst = (I == J) ? x_blk<Cfg>(smem, I, I) : a_blk<Cfg>(smem, I, J);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * I + 4 * lq + i;
-          const float v = acc[i] * sbeta[r] * srk[r] * sj;
-          dst[(4 * lq + i) * LDA + l16] = (I == J && j >= r) ? 0.f : v;
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * I + 4 * lq + i;
+            const float v = acc_a[i] * sbeta[r] * srk[r] * sj;
+            dst[(4 * lq + i) * LDA + l16] = (I == J && j >= r) ? 0.f : v;
+          }
         }
-      } else if (tt < 2 * NPT) {
-        int I, J;
-        lower_block(tt - NPT, I, J);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        Op::template mmaK<DK>(acc, sRk + 16 * J * LDK, LDK, sLq + 16 * I * LDK, LDK, lane);
-        // rows j = 16J + 4lq + i, column r = 16I + l16: P[r][j]
-        const int r = 16 * I + l16;
-        const float sr = a.scale * srq[r];
-        f32x4 out;
+        {
+          // P: rows j = 16J + 4lq + i, column r = 16I + l16: P[r][j]
+          const int r = 16 * I + l16;
+          const float sr = a.scale * srq[r];
+          f32x4 out;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * J + 4 * lq + i;
-          out[i] = (I == J && j > r) ? 0.f : acc[i] * sr * srk[j];
+          for (int i = 0; i < 4; ++i) {
+            const int j = 16 * J + 4 * lq + i;
+            out[i] = (I == J && j > r) ? 0.f : acc_p[i] * sr * srk[j];
+          }
+          Op::store4(gP + r * C + Op::template pos<C>(16 * J + 4 * lq), out);
         }
-        Op::store4(gP + r * C + Op::template pos<C>(16 * J + 4 * lq), out);
       } else if (tt < NTILE) {
         int I, J;
-        lower_block(tt - 2 * NPT, J, I);  // J > I: a block above the diagonal
+        lower_block(tt - NPT, J, I);  // J > I: a block above the diagonal
         J += 1;
         Op::store4(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J + 4 * lq),
                    f32x4{0.f, 0.f, 0.f, 0.f});

@@ -20,6 +20,10 @@ evaluations the pages mention are stood in for by these synthetic tensors):
                  CKDA-arm gates, h0~N(0, 0.02^2)
   decode         256 sequences x 1 token, H=32 d=128, bf16 q/k/v, state
                  ~N(0, 0.02^2), alpha~U[-1,1], beta~U[0,2], fresh draws per step
+  fast_decay     a case with a fraction of its key channels redrawn as
+                 fast-decaying gates: |alpha| ~ U[0.15, 0.4] with a random
+                 sign (products over 64 tokens reach ~2^-120, over 16 tokens
+                 stay above 2^-44)
   *_logits       the same workloads with the gates given as pre-activation
                  logits (alpha and beta of the Case hold a and b): CKDA arm
                  a = 2 N(2,1), b = N(0,1), so that 2 sigmoid(a) - 1 =
@@ -234,6 +238,27 @@ def lm_layer_logits(seed=1002, arm="ckda", B=8, T=4096, H=16, d=128, gate_dtype=
                      workload="LM layer forward B=%d H=%d T=%d d=%d bf16 %s range, %s gate logits"
                               % (B, H, T, d, arm.upper(), gate_dtype)),
                 gates="logits", gate_dtype=gate_dtype, arm=arm)
+
+
+def fast_decay(case: Case, seed=1005, frac=0.25, lo=0.15, hi=0.4) -> Case:
+    """The case with about `frac` of its key channels (the same channels in
+    every head and token) redrawn as gates of magnitude U[lo, hi] and random
+    sign; the other arrays are shared, not copied.  Gate values only (not
+    logits)."""
+    if case.gates != "values":
+        raise ValueError("fast_decay redraws gate values, not logits")
+    rng = np.random.default_rng(seed)
+    dk = case.alpha.shape[-1]
+    fast = rng.random(dk) < frac
+    a = case.alpha.copy()
+    shape = a[..., fast].shape
+    a[..., fast] = (rng.uniform(lo, hi, shape) * rng.choice([-1.0, 1.0], shape)).astype(np.float32)
+    meta = dict(case.meta, fast_channels=int(fast.sum()),
+                workload=case.meta.get("workload", "case") +
+                ", %d of %d key channels |alpha|~U[%g,%g]" % (fast.sum(), dk, lo, hi))
+    return Case(case.q, case.k, case.v, a, case.beta, case.h0, case.cu_seqlens, case.dtype,
+                case.chunk, case.l2norm, meta, gates=case.gates, gate_dtype=case.gate_dtype,
+                arm=case.arm)
 
 
 def varlen_lengths(seed=1003, n=16, total=65536, lo=1024, hi=8192):

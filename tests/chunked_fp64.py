@@ -32,6 +32,19 @@ alpha_s (per channel), D(r<-j) = Ft_r * (1 / Ft_j), so
 This is used when every |Ft_r| lies in [2^-100, 2^10]: then no factor
 overflows and no quotient is formed by a zero (signs are exact).
 
+Block-anchored chunks.  When the chunk-wide products leave that range (gates
+that decay fast over C tokens) the products restart every 16 rows (the MFMA
+tile height): Fb_r = prod of the gates of block(r) up to r, T_b the total of
+block b and, for r in block I and j in block J <= I,
+D(r<-j) = Fb_r * E_IJ / Fb_j with E_IJ = prod_{J<=b<I} T_b, so
+
+    A_rj = beta_r <k_r * Fb_r * E_IJ, k_j / Fb_j>,  P_rj likewise with q_r,
+    Kh_j = (k_j / Fb_j) * prod_{b>=J} T_b,
+
+while Kt, Qt and g keep the plain products Ft.  This is used when the ratio
+form is not and every |Fb_r| lies in the same range, a condition on 16
+consecutive gates.
+
 Irregular chunks (an exact zero gate, or gates so small that the running
 product leaves that range) form the same A, P and Kh from direct products of
 the gates instead of ratios: D(r<-j) built one gate at a time and Kh_j from
@@ -44,6 +57,12 @@ Normalisation enters as row scales: k_hat = rk * k, q_hat = rq * q.
 import numpy as np
 
 LO, HI = 2.0 ** -100, 2.0 ** 10
+BLOCK = 16
+
+
+def _in_range(F):
+    mag = np.abs(F)
+    return bool(np.all(np.isfinite(F)) and mag.min() >= LO and mag.max() <= HI)
 
 
 def _l2scale(x, use, eps=1e-6):
@@ -69,8 +88,8 @@ def _direct_products(ac):
 def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, force_irregular=False,
                paths=None):
     """One sequence, one head.  q,k,alpha [T,dk], v [T,dv], beta [T], S [dk,dv].
-    Returns (o [T,dv], S_final).  `paths`, if a list, receives 'ratio' or
-    'direct' per chunk."""
+    Returns (o [T,dv], S_final).  `paths`, if a list, receives 'ratio',
+    'block' or 'direct' per chunk."""
     T, dk = q.shape
     dv = v.shape[1]
     o = np.zeros((T, dv))
@@ -89,17 +108,36 @@ def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, force_irregular=Fa
 
         Ft = np.cumprod(ac, axis=0)
         g = Ft[C - 1]
-        mag = np.abs(Ft)
-        regular = bool(np.all(np.isfinite(Ft)) and mag.min() >= LO and mag.max() <= HI)
-        Lk = kc * Ft
-        Lq = qc * Ft
-        if regular and not force_irregular:
+        Kt = kc * Ft
+        Qt = qc * Ft
+        nb = C // BLOCK
+        Fb = np.concatenate([np.cumprod(ac[b * BLOCK:(b + 1) * BLOCK], axis=0)
+                             for b in range(nb)])
+        if _in_range(Ft) and not force_irregular:
             if paths is not None:
                 paths.append("ratio")
             Rk = kc / Ft
-            A = np.tril((bc * rk)[:, None] * (Lk @ Rk.T) * rk[None, :], -1)
-            P = np.tril(Lq @ Rk.T)
+            A = np.tril((bc * rk)[:, None] * (Kt @ Rk.T) * rk[None, :], -1)
+            P = np.tril(Qt @ Rk.T)
             Kh = g * Rk                                   # Kh / rk
+        elif _in_range(Fb) and not force_irregular:
+            if paths is not None:
+                paths.append("block")
+            Tb = Fb[BLOCK - 1::BLOCK]                     # [nb, dk] block totals
+            Lk, Lq, Rk = kc * Fb, qc * Fb, kc / Fb
+            G = np.zeros((C, C))
+            Pm = np.zeros((C, C))
+            for I in range(nb):
+                ri = slice(I * BLOCK, (I + 1) * BLOCK)
+                for J in range(I + 1):
+                    rj = slice(J * BLOCK, (J + 1) * BLOCK)
+                    E = np.prod(Tb[J:I], axis=0)          # 1 when J == I
+                    G[ri, rj] = (Lk[ri] * E) @ Rk[rj].T
+                    Pm[ri, rj] = (Lq[ri] * E) @ Rk[rj].T
+            A = np.tril((bc * rk)[:, None] * G * rk[None, :], -1)
+            P = np.tril(Pm)
+            tail = np.array([np.prod(Tb[J:], axis=0) for J in range(nb)])
+            Kh = Rk * np.repeat(tail, BLOCK, axis=0)      # Kh / rk
         else:
             if paths is not None:
                 paths.append("direct")
@@ -112,10 +150,10 @@ def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, force_irregular=Fa
                 suf[j] = suf[j + 1] * ac[j + 1]
             Kh = suf * kc                                 # Kh / rk
         X = np.linalg.inv(np.eye(C) + A)
-        W = X @ ((bc * rk)[:, None] * Lk)
+        W = X @ ((bc * rk)[:, None] * Kt)
         Ubar = X @ (bc[:, None] * vc)
         U = Ubar - W @ S
-        Ok = Lq @ S + P @ (rk[:, None] * U)
+        Ok = Qt @ S + P @ (rk[:, None] * U)
         o[c0:c0 + L] = (scale * rq[:, None] * Ok)[:L]
         S = g[:, None] * S + Kh.T @ (rk[:, None] * U)
     return o, S

@@ -1,6 +1,7 @@
 """P8: the chunked factorisation used by the HIP forward, in fp64, equals the
 sequential oracle to rounding (~1e-12): the chunk-ratio form on regular
-chunks, the direct-product form on chunks with exact zero or vanishing gates,
+chunks, the block-anchored form on chunks whose gates decay fast, the
+direct-product form on chunks with exact zero or vanishing gates,
 partial last chunks and every chunk size."""
 import numpy as np
 import pytest
@@ -52,6 +53,22 @@ def test_sign_changes_stay_on_ratio_form():
     ro, rh = oracle.fwd(q, k, v, a, b, h0=h0)
     co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=16, paths=paths)
     assert set(paths) == {"ratio"} and (a < 0).any()
+    assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
+
+
+@pytest.mark.parametrize("C", [32, 64])
+def test_fast_decay_takes_the_block_form(C):
+    """Gates of 0.15..0.4 on a quarter of the channels underflow the chunk-wide
+    product (0.27^64 ~ 2^-120) but not a 16-token block's: such chunks take the
+    block-anchored form, which matches the oracle like the other two."""
+    q, k, v, a, b, h0 = _case(11 + C, 2, 2 * C + 9, 2, 8, 4)
+    rng = np.random.default_rng(C)
+    a[..., :2] = rng.uniform(0.15, 0.4, size=a[..., :2].shape) * rng.choice([-1, 1], a[..., :2].shape)
+    a[..., 2] = 0.02                      # 0.02^16 ~ 2^-90, still in range per block
+    ro, rh = oracle.fwd(q, k, v, a, b, h0=h0)
+    paths = []
+    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=C, paths=paths)
+    assert "block" in paths and "direct" not in paths
     assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
 
 

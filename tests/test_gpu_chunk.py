@@ -219,6 +219,44 @@ def test_zero_and_tiny_gates_exact_path():
         assert max_rel_err(o2, o) > TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,chunk,d", [("f32", 32, 32), ("f32", 64, 32), ("f32", 64, 16),
+                                           ("bf16", 64, 128), ("bf16", 32, 64)])
+def test_fast_decay_block_anchored(dtype, chunk, d):
+    """A quarter of the key channels with |alpha| in [0.15, 0.4] (chunk-wide
+    products near 2^-120 at chunk 64) and one channel at |alpha| = 0.02
+    (0.02^16 ~ 2^-90, the edge of the 16-token range; 2^-180 over 32 tokens):
+    these chunks keep the MFMA path with products restarted every 16 rows and
+    match the oracle; a zeroed gate in one chunk still takes the direct path
+    there alone."""
+    announce("fast decay %s C=%d d=%d" % (dtype, chunk, d))
+    c = inputs.random_case(40 + chunk + d, 2, 3 * chunk + 11, 2, d, d, dtype=dtype, chunk=chunk,
+                           alpha="tanh", beta="2sig", h0_std=0.2)
+    c = inputs.fast_decay(c, seed=41 + d)
+    c.alpha = c.alpha.copy()
+    c.alpha[..., 1] = 0.02 * np.sign(c.alpha[..., 1] + 0.5)
+    _check(c)
+    c.alpha[1, chunk + 3, 1, 5] = 0.0
+    _check(c)
+
+
+@pytest.mark.parametrize("arm", ["ckda", "kda"])
+def test_lm_layer_fast_decay_full_sampled(arm):
+    """The LM layer at full size with a quarter of its key channels decaying
+    fast (|alpha| ~ U[0.15, 0.4], random sign); oracle on sampled pairs."""
+    announce("LM layer full size, fast-decay channels, %s arm" % arm)
+    c = inputs.fast_decay(inputs.lm_layer(arm=arm))
+    if arm == "kda":
+        c.alpha = np.abs(c.alpha)
+    o, ht = run_chunk(c, gate=arm)
+    o = o.reshape(c.v.shape)
+    pairs = [(0, 0), (7, 15), (2, 11)]
+    ref = oracle_pairs(c, pairs)
+    worst_o = max(max_rel_err(o[n, :, h], ref[(n, h)][0]) for n, h in pairs)
+    worst_h = max(max_rel_err(ht[n, h], ref[(n, h)][1]) for n, h in pairs)
+    print("  err o=%.3e ht=%.3e" % (worst_o, worst_h))
+    assert worst_o < TOL["bf16"] and worst_h < TOL["bf16"]
+
+
 def test_decode_chain_equals_prefill():
     announce("decode chain vs prefill")
     c = inputs.random_case(27, 3, 40, 2, 128, 128, dtype="bf16", chunk=64, alpha="tanh",
