@@ -107,8 +107,11 @@ struct PrepCfg {
   static constexpr int DCH = DK / DG;
 
   // byte offsets
-  static constexpr int O_LQ = 0;                                        // Lq [C][LDK] | Xb [C][LDC]
+  static constexpr int O_LQ = 0;                                        // Lq [C][LDK] | Kh'^T [DK][LDH] | Xb [C][LDC]
   static constexpr int SZ_LQ = align16(cmax(C * LDK, C * LDC) * ES);
+  // Kh'^T staged for row-wise stores: rows of C in storage order, padded by
+  // 16 bytes where that fits (spreads the column writes over the banks)
+  static constexpr int LDH = (DK * (C * ES + 16) <= SZ_LQ) ? C + 16 / ES : C;
   static constexpr int O_LK = O_LQ + SZ_LQ;                             // Lk [C][LDK] | Kt'^T [DK][LDC]
   static constexpr int O_RK = O_LK + C * LDK * ES;                      // Rk [C][LDK]
   static constexpr int O_TS = O_LK + align16(DK * LDC * ES);            // level scratch (after Rk dies)
@@ -129,6 +132,7 @@ struct PrepCfg {
   static_assert(NB <= NW && RPW >= 2 && (RPW & (RPW - 1)) == 0 && RPW <= 8, "row split");
   static_assert(DG * C <= NT && DK % DG == 0 && (DG & (DG - 1)) == 0 && DG <= 64, "direct path");
   static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+  static_assert(DK * LDH * ES <= SZ_LQ && (C * ES) % 16 == 0 && (LDH * ES) % 16 == 0, "Kh staging");
   static_assert(O_DROW + C * DK * IOES <= O_A, "direct path staging fits the operand region");
 };
 
@@ -380,6 +384,7 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
 
   T* sLq = reinterpret_cast<T*>(smem + Cfg::O_LQ);
   T* sXb = reinterpret_cast<T*>(smem + Cfg::O_LQ);
+  T* sKhT = reinterpret_cast<T*>(smem + Cfg::O_LQ);
   T* sLk = reinterpret_cast<T*>(smem + Cfg::O_LK);
   T* sRk = reinterpret_cast<T*>(smem + Cfg::O_RK);
   T* sKtT = reinterpret_cast<T*>(smem + Cfg::O_LK);
@@ -610,49 +615,91 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
 
   // ================= 3: A and P ================================================
   if constexpr (!DIRECT) {
-    constexpr int NPT = NB * (NB + 1) / 2;  // lower blocks (A and P together)
-    constexpr int NZ = NB * (NB - 1) / 2;   // zero blocks of P above the diagonal
-    constexpr int NTILE = NPT + NZ;
-    constexpr int NU = (NTILE + NW - 1) / NW;
+    // A tile (I, J) from its accumulator: rows r = 16I + 4lq + i, column
+    // j = 16J + l16; the diagonal tile goes to the X block it seeds
+    auto a_out = [&](const f32x4& acc_a, int I, int J) {
+      const int j = 16 * J + l16;
+      const float sj = srk[j];
+      float* dst = (I == J) ? x_blk<Cfg>(smem, I, I) : a_blk<Cfg>(smem, I, J);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * I + 4 * lq + i;
+        const float v = acc_a[i] * sbeta[r] * srk[r] * sj;
+        dst[(4 * lq + i) * LDA + l16] = (I == J && j >= r) ? 0.f : v;
+      }
+    };
+    // P' tile (I, J) from its accumulator: rows j = 16J + 4lq + i, column
+    // r = 16I + l16, as P'[r][j]; zero above the diagonal
+    auto p_vals = [&](const f32x4& acc_p, int I, int J) {
+      const int r = 16 * I + l16;
+      const float sr = a.scale * srq[r];
+      f32x4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * J + 4 * lq + i;
+        out[i] = (J > I || (I == J && j > r)) ? 0.f : acc_p[i] * sr * srk[j];
+      }
+      return out;
+    };
+    auto tile = [&](f32x4& acc_a, f32x4& acc_p, int I, int J) {
+      tile_ap<Cfg>(acc_a, acc_p, sLk + 16 * I * LDK, sLq + 16 * I * LDK, sRk + 16 * J * LDK,
+                   (I > J && !canchor) ? x_blk<Cfg>(smem, I, J) : nullptr, lane);
+    };
+    if constexpr (ES == 2 && NB % 2 == 0) {
+      // one task per (I, column pair J = 2p, 2p+1): in storage order the two
+      // tiles' P' values of a lane are adjacent (16 bytes, 64 per row)
+      constexpr int NPAIR = NB * NB / 2;
+      constexpr int NU = (NPAIR + NW - 1) / NW;
 #pragma unroll 1
-    for (int u = 0; u < NU; ++u) {
-      const int tt = wave + NW * u;
-      if (tt < NPT) {
-        int I, J;
-        lower_block(tt, I, J);
-        f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_p = {0.f, 0.f, 0.f, 0.f};
-        tile_ap<Cfg>(acc_a, acc_p, sLk + 16 * I * LDK, sLq + 16 * I * LDK, sRk + 16 * J * LDK,
-                     (I > J && !canchor) ? x_blk<Cfg>(smem, I, J) : nullptr, lane);
-        {
-          // A: rows r = 16I + 4lq + i, column j = 16J + l16
-          const int j = 16 * J + l16;
-          const float sj = srk[j];
-          float* dst = (I == J) ? x_blk<Cfg>(smem, I, I) : a_blk<Cfg>(smem, I, J);
+      for (int u = 0; u < NU; ++u) {
+        int tt = wave + NW * u;
+        if (tt < NPAIR) {
+          // C = 64: tasks ordered so that each SIMD (waves w, w + 4) gets 2 or 3 tiles
+          if constexpr (NB == 4) tt = (0x31507642u >> (4 * tt)) & 7u;
+          const int I = tt / (NB / 2), J0 = 2 * (tt % (NB / 2)), J1 = J0 + 1;
+          f32x4 ap0 = {0.f, 0.f, 0.f, 0.f}, ap1 = {0.f, 0.f, 0.f, 0.f};
+          if (J0 <= I) {
+            f32x4 aa = {0.f, 0.f, 0.f, 0.f};
+            tile(aa, ap0, I, J0);
+            a_out(aa, I, J0);
+          }
+          if (J1 <= I) {
+            f32x4 aa = {0.f, 0.f, 0.f, 0.f};
+            tile(aa, ap1, I, J1);
+            a_out(aa, I, J1);
+          }
+          const f32x4 o0 = p_vals(ap0, I, J0), o1 = p_vals(ap1, I, J1);
+          bf16x8 y;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int r = 16 * I + 4 * lq + i;
-            const float v = acc_a[i] * sbeta[r] * srk[r] * sj;
-            dst[(4 * lq + i) * LDA + l16] = (I == J && j >= r) ? 0.f : v;
+            y[i] = Op::cvt(o0[i]);
+            y[4 + i] = Op::cvt(o1[i]);
           }
+          *reinterpret_cast<bf16x8*>(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J0 + 4 * lq)) = y;
         }
-        {
-          // P: rows j = 16J + 4lq + i, column r = 16I + l16: P[r][j]
-          const int r = 16 * I + l16;
-          const float sr = a.scale * srq[r];
-          f32x4 out;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = 16 * J + 4 * lq + i;
-            out[i] = (I == J && j > r) ? 0.f : acc_p[i] * sr * srk[j];
-          }
-          Op::store4(gP + r * C + Op::template pos<C>(16 * J + 4 * lq), out);
+      }
+    } else {
+      constexpr int NPT = NB * (NB + 1) / 2;  // lower blocks (A and P together)
+      constexpr int NZ = NB * (NB - 1) / 2;   // zero blocks of P above the diagonal
+      constexpr int NTILE = NPT + NZ;
+      constexpr int NU = (NTILE + NW - 1) / NW;
+#pragma unroll 1
+      for (int u = 0; u < NU; ++u) {
+        const int tt = wave + NW * u;
+        if (tt < NPT) {
+          int I, J;
+          lower_block(tt, I, J);
+          f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_p = {0.f, 0.f, 0.f, 0.f};
+          tile(acc_a, acc_p, I, J);
+          a_out(acc_a, I, J);
+          Op::store4(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J + 4 * lq), p_vals(acc_p, I, J));
+        } else if (tt < NTILE) {
+          int I, J;
+          lower_block(tt - NPT, J, I);  // J > I: a block above the diagonal
+          J += 1;
+          Op::store4(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J + 4 * lq),
+                     f32x4{0.f, 0.f, 0.f, 0.f});
         }
-      } else if (tt < NTILE) {
-        int I, J;
-        lower_block(tt - NPT, J, I);  // J > I: a block above the diagonal
-        J += 1;
-        Op::store4(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J + 4 * lq),
-                   f32x4{0.f, 0.f, 0.f, 0.f});
       }
     }
   } else {
@@ -698,7 +745,7 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
         khv[i] = kh[i][cc] * rks[i];
       }
       store_run<Op, RPW>(sKtT + (c0ch + cc) * LDC + r0, ktv);
-      store_run_pos<Op, RPW, C>(gK + (c0ch + cc) * C, r0, khv);
+      store_run_pos<Op, RPW, C>(sKhT + (c0ch + cc) * Cfg::LDH, r0, khv);
     }
   }
   if (wave < NB && lane < 16) {
@@ -725,6 +772,16 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
     for (int i = 0; i < 16; ++i) blkI[i * LDA + j] = x[i];
   }
   __syncthreads();  // B4
+  {
+    // Kh'^T out row by row, 16 bytes per thread: whole lines per wave
+    // instead of a few bytes in each of 64 rows
+    constexpr int VE = 16 / ES, RV = C / VE, NV = DK * RV;
+    for (int e = tid; e < NV; e += NT) {
+      const int row = e / RV, col = (e % RV) * VE;
+      *reinterpret_cast<uint4*>(gK + row * C + col) =
+          *reinterpret_cast<const uint4*>(sKhT + row * Cfg::LDH + col);
+    }
+  }
 
   // ================= 5: off-diagonal blocks of X ===============================
   for (int d = 1; d < NB; ++d) {
@@ -781,16 +838,41 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   __syncthreads();
   {
     constexpr int NWT = (DK / 16) * (C / 16);
-    constexpr int NU = (NWT + NW - 1) / NW;
+    if constexpr (ES == 2 && DK % 32 == 0) {
+      // tiles mc = 2s, 2s+1 of one row block together: in storage order their
+      // four values per lane are adjacent (16 bytes), 64 bytes per row
+      constexpr int NWP = NWT / 2;
+      constexpr int NU = (NWP + NW - 1) / NW;
 #pragma unroll 1
-    for (int u = 0; u < NU; ++u) {
-      const int tt = wave + NW * u;
-      if (tt < NWT) {
-        const int mc = tt / (C / 16), nr = tt % (C / 16);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        Op::template mmaK<C>(acc, sKtT + 16 * mc * LDC, LDC, sXb + 16 * nr * LDC, LDC, lane);
-        // rows c = 16mc + 4lq + i, column r = 16nr + l16: W[r][c]
-        Op::store4(gW + (16 * nr + l16) * DK + Op::template pos<DK>(16 * mc + 4 * lq), -acc);
+      for (int u = 0; u < NU; ++u) {
+        const int tt = wave + NW * u;
+        if (tt < NWP) {
+          const int sp = tt / (C / 16), nr = tt % (C / 16);
+          f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+          Op::template mmaK<C>(acc0, sKtT + 32 * sp * LDC, LDC, sXb + 16 * nr * LDC, LDC, lane);
+          Op::template mmaK<C>(acc1, sKtT + (32 * sp + 16) * LDC, LDC, sXb + 16 * nr * LDC, LDC, lane);
+          // rows c = 32sp + 16h + 4lq + i, column r = 16nr + l16: W[r][c]
+          bf16x8 y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            y[i] = Op::cvt(-acc0[i]);
+            y[4 + i] = Op::cvt(-acc1[i]);
+          }
+          *reinterpret_cast<bf16x8*>(gW + (16 * nr + l16) * DK + Op::template pos<DK>(32 * sp + 4 * lq)) = y;
+        }
+      }
+    } else {
+      constexpr int NU = (NWT + NW - 1) / NW;
+#pragma unroll 1
+      for (int u = 0; u < NU; ++u) {
+        const int tt = wave + NW * u;
+        if (tt < NWT) {
+          const int mc = tt / (C / 16), nr = tt % (C / 16);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          Op::template mmaK<C>(acc, sKtT + 16 * mc * LDC, LDC, sXb + 16 * nr * LDC, LDC, lane);
+          // rows c = 16mc + 4lq + i, column r = 16nr + l16: W[r][c]
+          Op::store4(gW + (16 * nr + l16) * DK + Op::template pos<DK>(16 * mc + 4 * lq), -acc);
+        }
       }
     }
   }
