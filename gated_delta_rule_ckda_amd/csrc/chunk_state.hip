@@ -17,9 +17,12 @@
 // that order already (perm32 in mfma_ops.h), so each fragment is one 16-byte
 // read.
 //
-// The last four waves ("loader waves") stream the blocks: a chunk's block and
+// The last eight waves ("loader waves") stream the blocks: a chunk's block and
 // V rows are loaded into registers two chunks ahead and written to LDS while
 // the state waves wait at a barrier, so HBM latency overlaps the arithmetic.
+// They also write the outputs: the state waves leave a chunk's O tile in LDS
+// and the loaders store it one chunk later as whole rows of the dv tile (16
+// bytes per thread) rather than 32-byte pieces from each state wave.
 #include "mfma_ops.h"
 
 namespace ckda {
@@ -69,7 +72,9 @@ struct StateCfg {
   static constexpr int O_K = align16(O_P + C * LDC * ES);        // Kh'^T [DK][LDC]
   static constexpr int O_VT = align16(O_K + DK * LDC * ES);      // V^T [DVT][LDC]
   static constexpr int O_G = align16(O_VT + DVT * LDC * ES);     // g [DK] fp32
-  static constexpr int LDS_BYTES = align16(O_G + DK * 4);
+  static constexpr int LDO = DVT * IOES + 16;                    // O tile row stride (bytes)
+  static constexpr int O_O = align16(O_G + DK * 4);              // O tile [C][DVT] (io type)
+  static constexpr int LDS_BYTES = align16(O_O + C * LDO);
 
   static_assert(GB_END == blk_g_byte(C, DK, ES) + 4 * DK, "block layout");
   static_assert(GB_X % 16 == 0 && GB_W % 16 == 0 && GB_P % 16 == 0 && GB_K % 16 == 0 &&
@@ -264,11 +269,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
   // so the loaders' in-flight registers and the state registers never need
   // to be live at the same time.
   if (is_state) {
-    ST* go = static_cast<ST*>(a.o);
     for (int i = 0; i < nch; ++i) {
       __syncthreads();  // group A of chunk i is in LDS
-      const int L = chunk_len(i);
-      const int64_t t0 = chunk_t0(i);
       Frag sf[Cfg::NFK];
       Op::template frags<DK>(sf, sacc);
       // U tiles: X' V - W S.  All LDS fragments of the phase are read first
@@ -321,10 +323,10 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
 #pragma unroll
           for (int s = 0; s < Cfg::NFC; ++s)
             if (Cfg::tri_live(rb, s)) Op::mma(oacc, uf[s], pf[rb][s]);
-          const int r = 16 * rb + l16;
-          if (r < L)
-            IO::store4(go + ((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0 + 16 * wave + 4 * lq,
-                       oacc);
+          // to the O tile; rows >= L are dropped when the tile is written out
+          IO::store4(reinterpret_cast<ST*>(smem + Cfg::O_O + (16 * rb + l16) * Cfg::LDO) +
+                         16 * wave + 4 * lq,
+                     oacc);
         }
       }
       // S <- Diag(g) S + Kh'^T U
@@ -348,6 +350,23 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
     }
   } else {
     using GA = Group<Cfg, 0, 2, true>;
+    // the O tile of chunk i to o: rows < L, 16 bytes per thread
+    auto write_o = [&](int i) {
+      constexpr int PR = DVT * Cfg::IOES / 16, NOP = C * PR;
+      const int L = chunk_len(i);
+      const int64_t t0 = chunk_t0(i);
+#pragma unroll
+      for (int u = 0; u < (NOP + Cfg::NLT - 1) / Cfg::NLT; ++u) {
+        const int p = lt + Cfg::NLT * u;
+        const int r = p / PR, cp = p % PR;
+        if ((NOP % Cfg::NLT == 0 || p < NOP) && r < L) {
+          const uint4 val = *reinterpret_cast<const uint4*>(smem + Cfg::O_O + r * Cfg::LDO + 16 * cp);
+          *reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.o) +
+                                    (((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0) * Cfg::IOES +
+                                    16 * cp) = val;
+        }
+      }
+    };
     using GB = Group<Cfg, 2, 6, false>;
     // Loads are issued for every step (the chunk index clamped to the last
     // chunk), so each wait counts the same number of newer loads on every path.
@@ -374,9 +393,10 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
     // step i: B(i) (in gb) goes to LDS while U(i) runs, then A(i+1) (in ga)
     // while O(i) and S(i) run; gb then takes B(i+2) and ga takes A(i+3)
     auto step = [&](int i, GB& gb, GA& ga) {
-      __syncthreads();  // U(i) may start; the state waves are done with B(i-1)
+      __syncthreads();  // U(i) may start; the state waves are done with B(i-1) and O(i-1)
       gb.store(smem, 0, lt);
       issueB(gb, i + 2);
+      if (i > 0) write_o(i - 1);
       __syncthreads();  // O(i), S(i) may start; the state waves are done with A(i)
       // unconditional (past the last chunk it rewrites the last chunk's group
       // A, which nothing reads any more): a skipped store would leave these
@@ -390,6 +410,19 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
       step(i + 1, sb1, sa0);
     }
     if (i < nch) step(i, sb0, sa1);
+  }
+  __syncthreads();  // the last O tile is in LDS
+  if (!is_state && nch > 0) {
+    constexpr int PR = DVT * Cfg::IOES / 16, NOP = C * PR;
+    const int il = nch - 1, L = chunk_len(il);
+    const int64_t t0 = chunk_t0(il);
+    for (int p = lt; p < NOP; p += Cfg::NLT) {
+      const int r = p / PR, cp = p % PR;
+      if (r < L)
+        *reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.o) +
+                                  (((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0) * Cfg::IOES +
+                                  16 * cp) = *reinterpret_cast<const uint4*>(smem + Cfg::O_O + r * Cfg::LDO + 16 * cp);
+    }
   }
 
   if (is_state && a.ht) {
