@@ -374,7 +374,8 @@ __device__ __forceinline__ void direct_ap(const void* gq, const void* gk, const 
 // a chunk that is not regular gets its flag set and is left to the direct
 // kernel.  DIRECT = true: the same chunk with A and P from direct products.
 template <class Cfg, class G, bool DIRECT>
-__device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsigned char* smem) {
+__device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsigned char* smem,
+                                           int tid = static_cast<int>(threadIdx.x)) {
   using Op = typename Cfg::Op;
   using IO = typename Cfg::IO;
   using T = typename Cfg::T;
@@ -395,7 +396,7 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   float* sbeta = reinterpret_cast<float*>(smem + Cfg::O_BETA);
   int* sFlag = reinterpret_cast<int*>(smem + Cfg::O_FLAG);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   const int H = a.H, Hk = a.Hk;
   const int hk = h / (H / Hk);  // query/key head of value head h
@@ -921,7 +922,12 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2))) vo
     while (mm != 0) {
       const int idx = b + (64 * w + __builtin_ctzll(mm)) * grid;
       mm &= mm - 1;
-      prep_chunk<Cfg, G, true>(a, idx % a.maxc, idx / a.maxc, smem);
+      // threadIdx.x through an opaque move: the chunk's lane-dependent
+      // addresses are then formed here, not hoisted into the kernel's
+      // prologue, where with no chunk flagged they would only cost spills
+      int tid_o;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(tid_o) : "v"(static_cast<int>(threadIdx.x)));
+      prep_chunk<Cfg, G, true>(a, idx % a.maxc, idx / a.maxc, smem, tid_o);
       __syncthreads();
     }
   }
