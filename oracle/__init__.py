@@ -78,6 +78,10 @@ class Oracle:
             dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int32, ctypes.c_double,
             ctypes.c_double]
         lib.ckda_oracle_step.restype = ctypes.c_int32
+        lib.ckda_oracle_bwd.argtypes = [
+            ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32] + [dp] * 14 + [ctypes.c_int32, ctypes.c_double, ctypes.c_double]
+        lib.ckda_oracle_bwd.restype = ctypes.c_int32
         lib.ckda_oracle_step.argtypes = [
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             dp, dp, dp, dp, dp, dp, dp, ctypes.c_int32, ctypes.c_double,
@@ -159,6 +163,42 @@ class Oracle:
             raise ValueError("ckda_oracle_fwd failed with code %d" % rc)
         return o, ht
 
+    def bwd(self, q, k, v, alpha, beta, dout, h0=None, dht=None, seq_start=None,
+            use_l2norm=True, scale=1.0, eps=EPS):
+        """Gradients of fwd (same layouts) for dL/do = dout and dL/dht = dht
+        (None: zero).  Returns (dq, dk, dv, dalpha, dbeta, dh0) in fp64,
+        shaped like q, k, v, alpha, beta and [N,H,dk,dv]."""
+        q, k, v, alpha, beta, dout = (_f64(a) for a in (q, k, v, alpha, beta, dout))
+        if seq_start is None:
+            B, T, H, dk = q.shape
+            starts = np.arange(B + 1, dtype=np.int64) * T
+        else:
+            starts = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+            H, dk = q.shape[-2], q.shape[-1]
+        N = len(starts) - 1
+        dv = v.shape[-1]
+        ttot = int(starts[-1])
+        if (q.size != ttot * H * dk or v.size != ttot * H * dv or beta.size != ttot * H
+                or dout.size != v.size):
+            raise ValueError("oracle.bwd: shapes do not match seq_start")
+        h0a = None if h0 is None else _f64(h0)
+        dhta = None if dht is None else _f64(dht)
+        for x in (h0a, dhta):
+            if x is not None and x.size != N * H * dk * dv:
+                raise ValueError("oracle.bwd: state has the wrong size")
+        dq, dkk, dalpha = (np.empty(q.shape, np.float64) for _ in range(3))
+        dvv = np.empty(v.shape, np.float64)
+        dbeta = np.empty(beta.shape, np.float64)
+        dh0 = np.empty((N, H, dk, dv), np.float64)
+        rc = self.lib.ckda_oracle_bwd(
+            N, starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0a), _ptr(dout),
+            _ptr(dhta), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dalpha), _ptr(dbeta), _ptr(dh0),
+            int(bool(use_l2norm)), float(scale), float(eps))
+        if rc != 0:
+            raise ValueError("ckda_oracle_bwd failed with code %d" % rc)
+        return dq, dkk, dvv, dalpha, dbeta, dh0
+
     def step(self, q, k, v, alpha, beta, state, use_l2norm=True, scale=1.0, eps=EPS):
         """One decode token per sequence: q,k,alpha [N,H,dk], v [N,H,dv],
         beta [N,H], state [N,H,dk,dv].  Returns (o, new_state) in fp64; the
@@ -209,3 +249,7 @@ def fwd(*args, **kwargs):
 
 def step(*args, **kwargs):
     return default().step(*args, **kwargs)
+
+
+def bwd(*args, **kwargs):
+    return default().bwd(*args, **kwargs)

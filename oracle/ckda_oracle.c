@@ -208,6 +208,208 @@ int32_t ckda_oracle_fwd(int32_t N, const int64_t* seq_start, int32_t H,
 }
 
 /*
+ * Gradients of the forward above (reverse mode through the same per-token
+ * steps, in the reverse token order).  Given dL/do (dout, shaped like o) and
+ * dL/dht (dht [N][H][dk][dv], or NULL for zero), returns dL/dq, dL/dk,
+ * dL/dv, dL/dalpha, dL/dbeta and dL/dh0 (dh0 may be NULL).
+ *
+ * Per token the forward computes, with x_q, x_k the (normalised) q and k:
+ *   X = Diag(alpha) S_prev;  w = X^T x_k;  u = v - w;
+ *   S = X + beta x_k u^T;    o = scale S^T x_q.
+ * The adjoints follow step by step (G = dL/dS accumulated from later
+ * tokens and this token's read-out):
+ *   G += scale x_q dout^T               dx_q = scale S dout
+ *   e = G^T x_k;  du = beta e           dbeta = e . u
+ *   dx_k = beta G u - X du              dv = du
+ *   dX = G - x_k du^T
+ *   dalpha[c] = sum_j dX[c,j] S_prev[c,j]
+ *   G <- Diag(alpha) dX                 (dL/dS_prev)
+ * and through x = y / sqrt(|y|^2 + eps) with r = 1/sqrt(|y|^2 + eps):
+ *   dy = r (dx - x (x . dx)).
+ * Every state S_t of the sequence is kept from a first forward sweep (the
+ * plain way to have S_prev at each step of the reverse sweep).
+ */
+static void bwd_head(int64_t t0, int64_t t1, int32_t h, int32_t H, int32_t dk,
+                     int32_t dv, const double* q, const double* k,
+                     const double* v, const double* alpha, const double* beta,
+                     const double* dout, double* G, double* states,
+                     double* dq, double* dk_out, double* dv_out,
+                     double* dalpha, double* dbeta, int32_t use_l2norm,
+                     double scale, double eps, double* xq, double* xk,
+                     double* w, double* dxq, double* dxk, double* e) {
+  const size_t sz = (size_t)dk * (size_t)dv;
+  /* forward sweep: states[i] = S after token t0 + i - 1 (states[0] = S_0) */
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t i = t - t0;
+    double* S = states + (size_t)(i + 1) * sz;
+    memcpy(S, states + (size_t)i * sz, sizeof(double) * sz);
+    const int64_t qk_off = (t * H + h) * (int64_t)dk;
+    memcpy(xk, k + qk_off, sizeof(double) * (size_t)dk);
+    if (use_l2norm) l2_normalise(xk, dk, eps);
+    const double* a = alpha + qk_off;
+    const double b = beta[t * H + h];
+    const double* vt = v + (t * H + h) * (int64_t)dv;
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= a[c];
+    for (int32_t j = 0; j < dv; ++j) w[j] = 0.0;
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) w[j] += S[c * dv + j] * xk[c];
+    for (int32_t c = 0; c < dk; ++c) {
+      const double bk = b * xk[c];
+      for (int32_t j = 0; j < dv; ++j) S[c * dv + j] += bk * (vt[j] - w[j]);
+    }
+  }
+  /* reverse sweep */
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    const int64_t i = t - t0;
+    const double* Sp = states + (size_t)i * sz;       /* S_prev */
+    const double* St = states + (size_t)(i + 1) * sz; /* S after token t */
+    const int64_t qk_off = (t * H + h) * (int64_t)dk;
+    const int64_t v_off = (t * H + h) * (int64_t)dv;
+    memcpy(xq, q + qk_off, sizeof(double) * (size_t)dk);
+    memcpy(xk, k + qk_off, sizeof(double) * (size_t)dk);
+    if (use_l2norm) {
+      l2_normalise(xq, dk, eps);
+      l2_normalise(xk, dk, eps);
+    }
+    const double* a = alpha + qk_off;
+    const double b = beta[t * H + h];
+    const double* vt = v + v_off;
+    const double* go = dout + v_off;
+    /* read-out: o = scale S^T x_q */
+    for (int32_t c = 0; c < dk; ++c) {
+      double acc = 0.0;
+      for (int32_t j = 0; j < dv; ++j) {
+        G[c * dv + j] += scale * xq[c] * go[j];
+        acc += St[c * dv + j] * go[j];
+      }
+      dxq[c] = scale * acc;
+    }
+    /* X = Diag(alpha) S_prev, w = X^T x_k, u = v - w (recomputed) */
+    for (int32_t j = 0; j < dv; ++j) w[j] = 0.0;
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) w[j] += a[c] * Sp[c * dv + j] * xk[c];
+    /* e = G^T x_k; u = v - w */
+    for (int32_t j = 0; j < dv; ++j) e[j] = 0.0;
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) e[j] += G[c * dv + j] * xk[c];
+    double db = 0.0;
+    for (int32_t j = 0; j < dv; ++j) db += e[j] * (vt[j] - w[j]);
+    dbeta[t * H + h] = db;
+    /* dx_k = beta G u - X du, du = beta e */
+    for (int32_t c = 0; c < dk; ++c) {
+      double acc1 = 0.0, acc2 = 0.0;
+      for (int32_t j = 0; j < dv; ++j) {
+        acc1 += G[c * dv + j] * (vt[j] - w[j]);
+        acc2 += a[c] * Sp[c * dv + j] * (b * e[j]);
+      }
+      dxk[c] = b * acc1 - acc2;
+    }
+    for (int32_t j = 0; j < dv; ++j) dv_out[v_off + j] = b * e[j];
+    /* dX = G - x_k du^T; dalpha; G <- Diag(alpha) dX */
+    for (int32_t c = 0; c < dk; ++c) {
+      double da = 0.0;
+      for (int32_t j = 0; j < dv; ++j) {
+        const double dX = G[c * dv + j] - xk[c] * (b * e[j]);
+        da += dX * Sp[c * dv + j];
+        G[c * dv + j] = a[c] * dX;
+      }
+      dalpha[qk_off + c] = da;
+    }
+    /* through the normalisation */
+    if (use_l2norm) {
+      const double* yq = q + qk_off;
+      const double* yk = k + qk_off;
+      double nq = 0.0, nk = 0.0, pq = 0.0, pk = 0.0;
+      for (int32_t c = 0; c < dk; ++c) {
+        nq += yq[c] * yq[c];
+        nk += yk[c] * yk[c];
+        pq += xq[c] * dxq[c];
+        pk += xk[c] * dxk[c];
+      }
+      const double rq = 1.0 / sqrt(nq + eps), rk = 1.0 / sqrt(nk + eps);
+      for (int32_t c = 0; c < dk; ++c) {
+        dq[qk_off + c] = rq * (dxq[c] - xq[c] * pq);
+        dk_out[qk_off + c] = rk * (dxk[c] - xk[c] * pk);
+      }
+    } else {
+      for (int32_t c = 0; c < dk; ++c) {
+        dq[qk_off + c] = dxq[c];
+        dk_out[qk_off + c] = dxk[c];
+      }
+    }
+  }
+}
+
+int32_t ckda_oracle_bwd(int32_t N, const int64_t* seq_start, int32_t H,
+                        int32_t dk, int32_t dv, const double* q,
+                        const double* k, const double* v, const double* alpha,
+                        const double* beta, const double* h0,
+                        const double* dout, const double* dht, double* dq,
+                        double* dk_out, double* dv_out, double* dalpha,
+                        double* dbeta, double* dh0, int32_t use_l2norm,
+                        double scale, double eps) {
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || !seq_start) return ORACLE_BAD_ARG;
+  if (seq_start[0] != 0) return ORACLE_BAD_ARG;
+  int64_t longest = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    if (seq_start[n + 1] < seq_start[n]) return ORACLE_BAD_ARG;
+    if (seq_start[n + 1] - seq_start[n] > longest) longest = seq_start[n + 1] - seq_start[n];
+  }
+  if (seq_start[N] > 0 && (!q || !k || !v || !alpha || !beta || !dout || !dq ||
+                           !dk_out || !dv_out || !dalpha || !dbeta))
+    return ORACLE_BAD_ARG;
+
+  int32_t failed = 0;
+  const int64_t pairs = (int64_t)N * H;
+#pragma omp parallel
+  {
+    const size_t sz = (size_t)dk * (size_t)dv;
+    double* G = (double*)malloc(sizeof(double) * sz);
+    double* states = (double*)malloc(sizeof(double) * sz * (size_t)(longest + 1));
+    double* xq = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* xk = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* dxq = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* dxk = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* w = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+    const int ok = G && states && xq && xk && dxq && dxk && w && e;
+    if (!ok) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t p = 0; p < pairs; ++p) {
+      if (!ok) continue;
+      const int32_t n = (int32_t)(p / H);
+      const int32_t h = (int32_t)(p % H);
+      const int64_t st_off = ((int64_t)n * H + h) * (int64_t)sz;
+      if (h0)
+        memcpy(states, h0 + st_off, sizeof(double) * sz);
+      else
+        memset(states, 0, sizeof(double) * sz);
+      if (dht)
+        memcpy(G, dht + st_off, sizeof(double) * sz);
+      else
+        memset(G, 0, sizeof(double) * sz);
+      bwd_head(seq_start[n], seq_start[n + 1], h, H, dk, dv, q, k, v, alpha, beta,
+               dout, G, states, dq, dk_out, dv_out, dalpha, dbeta, use_l2norm,
+               scale, eps, xq, xk, w, dxq, dxk, e);
+      if (dh0) memcpy(dh0 + st_off, G, sizeof(double) * sz);
+    }
+    free(G);
+    free(states);
+    free(xq);
+    free(xk);
+    free(dxq);
+    free(dxk);
+    free(w);
+    free(e);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
  * One decode step for N independent sequences (one token each): the same
  * per-token body as the forward, applied to the state cache.  state is
  * [N][H][dk][dv] and is updated in place; q,k,alpha are [N][H][dk],
