@@ -67,6 +67,10 @@ def _load():
                                               ctypes.c_size_t, vp]
         lib.ckda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         lib.ckda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), i32]
+        lib.ckda_chunk_bwd.restype = i32
+        lib.ckda_chunk_bwd.argtypes = [ctypes.POINTER(FwdDesc)] + [vp] * 16 + [ctypes.c_size_t, vp]
+        lib.ckda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.ckda_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), i32]
         lib.ckda_fwd_supported.restype = i32
         lib.ckda_fwd_supported.argtypes = [ctypes.POINTER(FwdDesc)]
         lib.ckda_recurrent_step.restype = i32
@@ -215,6 +219,61 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
                               _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
                               _ptr(workspace), workspace.numel(), _stream(stream)))
     return o, ht
+
+
+def chunk_bwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
+    """Bytes of workspace ckda_chunk_bwd needs for `desc`."""
+    return int(_load().ckda_chunk_bwd_workspace_size(ctypes.byref(desc), int(bool(packed))))
+
+
+def chunk_bwd(q, k, v, alpha, beta, dout, *, h0=None, dht=None, cu_seqlens=None, chunk_size=64,
+              use_qk_l2norm=True, gate="ckda", scale=1.0, output_dh0=True, workspace=None,
+              stream=None):
+    """Gradients of chunk_fwd for dL/do = dout (dtype of v) and dL/dht = dht
+    ([N,H,dk,dv] float32, None for zero).  Gate values (not logits), q/k
+    heads equal to value heads.  Returns float32 (dq, dk, dv, dalpha, dbeta,
+    dh0) shaped like q, k, v, alpha, beta and [N,H,dk,dv] (dh0 None unless
+    output_dh0)."""
+    import torch
+    lib = _load()
+    H, dk, dv = v.shape[-2], q.shape[-1], v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("dout", dout)):
+        _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
+    _require(k.dtype == q.dtype and v.dtype == q.dtype and dout.dtype == q.dtype,
+             "q, k, v, dout must share a dtype")
+    _require(alpha.dtype == torch.float32 and beta.dtype == torch.float32,
+             "the backward takes float32 gate values")
+    if cu_seqlens is not None:
+        _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda,
+                 "cu_seqlens must be an int32 device tensor")
+    desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens,
+                      GATES_F32, False)
+    _require(q.numel() == desc.B * desc.T * H * dk, "q must have H heads (no grouped heads)")
+    _require(k.numel() == q.numel() and alpha.numel() == q.numel(), "k, alpha must match q")
+    _require(v.numel() == desc.B * desc.T * H * dv and dout.numel() == v.numel(),
+             "v, dout have the wrong number of elements")
+    _require(beta.numel() == desc.B * desc.T * H, "beta has the wrong number of elements")
+    for name, t in (("h0", h0), ("dht", dht)):
+        if t is not None:
+            _require(t.dtype == torch.float32 and t.is_contiguous() and t.is_cuda
+                     and t.numel() == desc.num_seqs * H * dk * dv,
+                     "%s must be [N,H,dk,dv] float32" % name)
+    f32 = dict(device=q.device, dtype=torch.float32)
+    dq, dkk, dal = (torch.empty(q.shape, **f32) for _ in range(3))
+    dvv = torch.empty(v.shape, **f32)
+    dbe = torch.empty(beta.shape, **f32)
+    dh0 = torch.empty((desc.num_seqs, H, dk, dv), **f32) if output_dh0 else None
+    need = chunk_bwd_workspace_size(desc, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _require(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.numel() >= need,
+             "workspace must be a uint8 device tensor of at least %d bytes" % need)
+    _check(lib.ckda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                              _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(dout), _ptr(dht),
+                              _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dal), _ptr(dbe), _ptr(dh0),
+                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dkk, dvv, dal, dbe, dh0
 
 
 class ChunkFwdPlan:

@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libckda.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "decode.hip", "chunk_prep.hip", "chunk_state.hip", "sign_absorb.hip"]
+SOURCES = ["api.hip", "decode.hip", "chunk_prep.hip", "chunk_state.hip", "sign_absorb.hip",
+           "chunk_bwd.hip"]
 ARCH = os.environ.get("CKDA_ARCH", "gfx950")
 
 CFLAGS = [

@@ -95,6 +95,16 @@ size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* d, int32_t packed) {
                                    d->io_dtype, packed != 0, d->sign_absorb == 1);
 }
 
+size_t ckda_chunk_bwd_workspace_size(const ckda_fwd_desc_t* d, int32_t packed) {
+  if (!d || d->B <= 0 || d->T < 0 || d->H <= 0 || d->dk <= 0 || d->dv <= 0 || d->num_seqs < 0)
+    return 0;
+  if (d->io_dtype != CKDA_DTYPE_BF16 && d->io_dtype != CKDA_DTYPE_F32) return 0;
+  if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64) return 0;
+  if (static_cast<int64_t>(d->B) * d->T == 0 || d->num_seqs == 0) return 0;
+  return ckda::bwd_workspace_bytes(d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
+                                   d->io_dtype, packed != 0);
+}
+
 }  // extern "C"
 
 namespace {
@@ -109,7 +119,7 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
                            const void* v, const void* alpha, const void* beta,
                            const int32_t* cu_seqlens, const float* h0, const void* o,
                            const float* ht, const void* workspace, size_t workspace_bytes,
-                           int passes) {
+                           int passes, bool check_workspace = true) {
   if (!d) return fail(CKDA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->dk <= 0 || d->dv <= 0 || d->num_seqs < 0)
     return fail(CKDA_ERR_INVALID_ARGUMENT,
@@ -173,7 +183,7 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
     if (h0 && h0 != ht && overlap(rh, ins[5]))
       return fail(CKDA_ERR_INVALID_ARGUMENT, "ht partially overlaps h0");
   }
-  const size_t need = ckda_chunk_fwd_workspace_size(d, cu_seqlens ? 1 : 0);
+  const size_t need = check_workspace ? ckda_chunk_fwd_workspace_size(d, cu_seqlens ? 1 : 0) : 0;
   if (need > 0) {
     if (!workspace)
       return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
@@ -209,9 +219,96 @@ ckda_status_t run_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
                                    (passes & kPrepare) != 0, (passes & kFinish) != 0));
 }
 
+// The backward takes the forward's inputs plus dout (in the place of o) and
+// dht, and writes fp32 gradients.
+ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, const void* v,
+                      const void* alpha, const void* beta, const int32_t* cu_seqlens,
+                      const float* h0, const void* dout, const float* dht, float* dq, float* dk,
+                      float* dv, float* dalpha, float* dbeta, float* dh0, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  ckda_status_t st = validate_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, dout, nullptr, nullptr,
+                                  0, kPrepare | kFinish, false);
+  if (st != CKDA_OK) return st;
+  if (d->gate_input != CKDA_GATES_F32)
+    return fail(CKDA_ERR_UNSUPPORTED, "the backward takes gate values (gate_input 0), not logits");
+  if (qk_heads_of(d->H, d->qk_heads) != d->H)
+    return fail(CKDA_ERR_UNSUPPORTED, "the backward needs qk_heads == H (no grouped heads)");
+  if (d->sign_absorb != 0)
+    return fail(CKDA_ERR_UNSUPPORTED, "the backward has no sign-absorption path");
+  const int64_t tokens = static_cast<int64_t>(d->B) * d->T;
+  if (tokens > 0 && (!dq || !dk || !dv || !dalpha || !dbeta))
+    return fail(CKDA_ERR_INVALID_ARGUMENT, "dq, dk, dv, dalpha and dbeta must not be NULL");
+  const void* outp[] = {dq, dk, dv, dalpha, dbeta, dh0};
+  const char* onames[] = {"dq", "dk", "dv", "dalpha", "dbeta", "dh0"};
+  for (int i = 0; i < 6; ++i)
+    if (outp[i] && !aligned16(outp[i]))
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", onames[i]);
+  if (dht && !aligned16(dht)) return fail(CKDA_ERR_INVALID_ARGUMENT, "dht is not 16-byte aligned");
+  const int64_t eb = elem_bytes(d->io_dtype);
+  const int64_t state_bytes = static_cast<int64_t>(d->num_seqs) * d->H * d->dk * d->dv * 4;
+  const int64_t nqk = tokens * d->H * d->dk, nv = tokens * d->H * d->dv;
+  const Range outs[] = {range("dq", dq, dq ? 4 * nqk : 0), range("dk", dk, dk ? 4 * nqk : 0),
+                        range("dv", dv, dv ? 4 * nv : 0), range("dalpha", dalpha, dalpha ? 4 * nqk : 0),
+                        range("dbeta", dbeta, dbeta ? 4 * tokens * d->H : 0),
+                        range("dh0", dh0, dh0 ? state_bytes : 0)};
+  const Range ins[] = {range("q", q, q ? nqk * eb : 0), range("k", k, k ? nqk * eb : 0),
+                       range("v", v, v ? nv * eb : 0), range("alpha", alpha, alpha ? 4 * nqk : 0),
+                       range("beta", beta, beta ? 4 * tokens * d->H : 0),
+                       range("h0", h0, h0 ? state_bytes : 0), range("dout", dout, dout ? nv * eb : 0),
+                       range("dht", dht, dht ? state_bytes : 0),
+                       range("cu_seqlens", cu_seqlens,
+                             cu_seqlens ? 4 * (static_cast<int64_t>(d->num_seqs) + 1) : 0)};
+  for (int i = 0; i < 6; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, r.name);
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(CKDA_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  const size_t need = ckda_chunk_bwd_workspace_size(d, cu_seqlens ? 1 : 0);
+  if (need > 0) {
+    if (!workspace)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed",
+                  workspace_bytes, need);
+    const Range rw = range("workspace", workspace, static_cast<int64_t>(need));
+    for (const Range& r : ins)
+      if (overlap(rw, r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    for (const Range& r : outs)
+      if (overlap(rw, r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+  }
+  if (d->num_seqs == 0) return ok();
+  ckda::BwdArgs b{};
+  b.f = ckda::FwdArgs{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size, d->H,
+                      d->use_qk_l2norm, d->gate_range, d->gate_input, 0, d->scale, q, k, v,
+                      alpha, beta, cu_seqlens, h0, nullptr, nullptr};
+  b.dout = dout;
+  b.dht = dht;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dalpha = dalpha;
+  b.dbeta = dbeta;
+  b.dh0 = dh0;
+  return from_hip(ckda::launch_bwd(b, d->io_dtype, workspace, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
+
+ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                             const void* v, const void* alpha, const void* beta,
+                             const int32_t* cu_seqlens, const float* h0, const void* dout,
+                             const float* dht, float* dq, float* dk, float* dv, float* dalpha,
+                             float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return run_bwd(d, q, k, v, alpha, beta, cu_seqlens, h0, dout, dht, dq, dk, dv, dalpha, dbeta,
+                 dh0, workspace, workspace_bytes, stream);
+}
 
 ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,
                              const void* v, const void* alpha, const void* beta,

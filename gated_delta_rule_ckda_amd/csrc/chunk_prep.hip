@@ -834,6 +834,8 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
       Op::store4(sXb + r * LDC + j, xv);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(sbeta + j);
       Op::store4(gX + r * C + Op::template pos<C>(j), xv * bv);
+      if (a.xout)  // X itself in fp32, for the backward
+        *reinterpret_cast<f32x4*>(a.xout + ((static_cast<int64_t>(h) * a.maxc + c) * C + r) * C + j) = xv;
     }
   }
   __syncthreads();

@@ -270,6 +270,14 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
   // to be live at the same time.
   if (is_state) {
     for (int i = 0; i < nch; ++i) {
+      if (a.hc) {  // the state entering chunk i, for the backward
+        float* hc = a.hc + (static_cast<int64_t>(h) * a.maxc + c_begin + i) * DK * a.dv;
+#pragma unroll
+        for (int mc = 0; mc < NMC; ++mc)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            hc[static_cast<int64_t>(16 * mc + 4 * lq + ii) * a.dv + dv0 + 16 * wave + l16] = sacc[mc][ii];
+      }
       __syncthreads();  // group A of chunk i is in LDS
       Frag sf[Cfg::NFK];
       Op::template frags<DK>(sf, sacc);
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
       __syncthreads();  // U(i) may start; the state waves are done with B(i-1) and O(i-1)
       gb.store(smem, 0, lt);
       issueB(gb, i + 2);
-      if (i > 0) write_o(i - 1);
+      if (i > 0 && a.o) write_o(i - 1);
       __syncthreads();  // O(i), S(i) may start; the state waves are done with A(i)
       // unconditional (past the last chunk it rewrites the last chunk's group
       // A, which nothing reads any more): a skipped store would leave these
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
     if (i < nch) step(i, sb0, sa1);
   }
   __syncthreads();  // the last O tile is in LDS
-  if (!is_state && nch > 0) {
+  if (!is_state && nch > 0 && a.o) {
     constexpr int PR = DVT * Cfg::IOES / 16, NOP = C * PR;
     const int il = nch - 1, L = chunk_len(il);
     const int64_t t0 = chunk_t0(il);
@@ -506,8 +514,10 @@ size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
                              sign);
 }
 
-launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream,
-                         bool prepare, bool finish) {
+namespace {
+// Chunk bookkeeping and the workspace's map, flags and blocks; returns the
+// first byte after them.
+unsigned char* fwd_layout(FwdArgs& a, int32_t io_dtype, void* ws) {
   if (static_cast<int64_t>(a.B) * a.T == 0) {
     // no tokens: every chain is empty and only copies h0 to ht (or zeros);
     // run the state pass as a dense batch with no chunks and no workspace
@@ -533,6 +543,15 @@ launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stre
   base += (4 * static_cast<int64_t>(a.H) * maxc + 255) & ~int64_t(255);
   a.blocks = base;
   base += static_cast<int64_t>(a.H) * maxc * a.blk_bytes;
+  return base;
+}
+}  // namespace
+
+launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream,
+                         bool prepare, bool finish) {
+  unsigned char* base = fwd_layout(a, io_dtype, ws);
+  const bool packed = a.cu_seqlens != nullptr;
+  const int64_t maxc = a.maxc;
   const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
   if (!e) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.num_seqs) * a.H == 0) return hipSuccess;
@@ -565,6 +584,37 @@ launch_result launch_fwd(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stre
   const launch_result r = e->fn(run, stream);
   if (r != hipSuccess || !absorb) return r;
   return launch_sign_fix(run, stream);
+}
+
+size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                           int32_t num_seqs, int32_t chunk, int32_t io_dtype, bool packed) {
+  const int64_t maxc = max_chunks(B, T, num_seqs, chunk, packed);
+  return fwd_workspace_bytes(B, T, H, dk, num_seqs, chunk, io_dtype, packed, false) +
+         static_cast<size_t>(bwd_extra_bytes(H, maxc, chunk, dk, dv));
+}
+
+launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stream) {
+  FwdArgs& a = b.f;
+  a.sign_absorb = 0;
+  unsigned char* base = fwd_layout(a, io_dtype, ws);
+  const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
+  if (!e) return hipErrorInvalidValue;
+  if (static_cast<int64_t>(a.num_seqs) * a.H == 0) return hipSuccess;
+  bwd_layout(b, base);
+  // the forward again, keeping X and the chunk entry states, writing no output
+  a.o = nullptr;
+  a.ht = nullptr;
+  if (a.cu_seqlens) {
+    const launch_result r = launch_chunk_map(a, stream);
+    if (r != hipSuccess) return r;
+  }
+  if (a.maxc > 0) {
+    const launch_result r = launch_prep(a, io_dtype, stream);
+    if (r != hipSuccess) return r;
+  }
+  const launch_result r = e->fn(a, stream);
+  if (r != hipSuccess) return r;
+  return launch_bwd_passes(b, io_dtype, stream);
 }
 
 }  // namespace ckda

@@ -96,6 +96,9 @@ struct FwdArgs {
   void* sk;               // [B*T][H][dk] Sigma k (io type)
   float* sa;              // [B*T][H][dk] |alpha|
   float* sb;              // [B*T][H] beta
+  // records kept for the backward (null in a plain forward)
+  float* xout;            // [H][maxc][C][C] X = (I + A)^{-1} of every chunk, fp32
+  float* hc;              // [H][maxc][dk][dv] state entering every chunk, fp32
 };
 bool fwd_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype);
 // Workspace bytes ckda_chunk_fwd needs for these sizes (0 for an empty call).
@@ -119,6 +122,34 @@ int64_t sign_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_
 void sign_layout(FwdArgs& a, unsigned char* base, int32_t io_dtype);
 launch_result launch_sign_absorb(const FwdArgs& a, int32_t io_dtype, hipStream_t stream);
 launch_result launch_sign_fix(const FwdArgs& a, hipStream_t stream);
+
+// Backward (chunk_bwd.hip).  The forward's arguments plus the gradients.
+struct BwdArgs {
+  FwdArgs f;
+  const void* dout;  // [B,T,H,dv] io type
+  const float* dht;  // [N,H,dk,dv] or null
+  float* dq;         // [B,T,H,dk]
+  float* dk;         // [B,T,H,dk]
+  float* dv;         // [B,T,H,dv]
+  float* dalpha;     // [B,T,H,dk]
+  float* dbeta;      // [B,T,H]
+  float* dh0;        // [N,H,dk,dv] or null
+  // workspace
+  float* dS;         // [H][maxc][dk][dv] state adjoint at each chunk's exit
+  float* dU;         // [H][maxc][C][dv]
+  int32_t* bflag;    // [H][maxc] 1: chunk left to the token-level kernel
+  float* scratch;    // [grid3][10][C * max(dk, dv)]
+  int32_t grid3;
+};
+// Workspace bytes of the backward beyond the forward's, their layout from
+// `base` (sets b.f.xout and b.f.hc too), and the backward's own passes.
+int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv);
+void bwd_layout(BwdArgs& b, unsigned char* base);
+launch_result launch_bwd_passes(const BwdArgs& b, int32_t io_dtype, hipStream_t stream);
+// All of ckda_chunk_bwd: the forward with records, then the backward passes.
+size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                           int32_t num_seqs, int32_t chunk, int32_t io_dtype, bool packed);
+launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stream);
 
 // ---- small device helpers shared by the kernels --------------------------
 

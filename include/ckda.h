@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 6
+#define CKDA_ABI_VERSION 7
 
 typedef enum {
   CKDA_OK = 0,
@@ -201,6 +201,42 @@ ckda_status_t ckda_chunk_fwd_finish(const ckda_fwd_desc_t* desc, const void* v,
 /* 1 if ckda_chunk_fwd has a kernel for this descriptor's (chunk_size, dk, dv,
  * io_dtype), 0 if not (other fields are not inspected). */
 int32_t ckda_fwd_supported(const ckda_fwd_desc_t* desc);
+
+/*
+ * Gradients of ckda_chunk_fwd (reverse mode of the recurrence the forward
+ * computes; picx.dev summary of the Complex KDA paper, section "Background",
+ * transition and update; the in-op L2 norm of the dormouse review "RoPE into
+ * the KDA q/k path", section 2, is differentiated too).  Given the same
+ * descriptor and inputs as the forward, dout = dL/do (io dtype, shaped like o)
+ * and dht = dL/dht ([N][H][dk][dv] float32, NULL for zero), writes float32
+ * gradients:
+ *   dq, dk, dalpha : [B*T][H][dk]    dv : [B*T][H][dv]    dbeta : [B*T][H]
+ *   dh0            : [N][H][dk][dv]  (NULL: not written)
+ * in the forward's token layout (dense or packed).  h0 is the forward's
+ * initial state (NULL for zero).
+ *
+ * It recomputes the forward (keeping each chunk's X = (I + A)^{-1} and entry
+ * state in the workspace), runs the state adjoint backwards over each
+ * sequence's chunks, then the chunk-local gradients in parallel over chunks:
+ * in the ratio form of the forward where the chunk's running gate products
+ * lie in [2^-100, 2^10], token by token (no division) elsewhere.  dalpha in
+ * the ratio form is (sum of later log-derivative terms) / alpha, so its
+ * float32 error grows like 1/|alpha| for small gates; alpha * dalpha is as
+ * accurate as the other gradients.
+ *
+ * Requirements beyond the forward's: gate_input = CKDA_GATES_F32 (gate values),
+ * qk_heads = 0 or H, sign_absorb = 0 (else CKDA_ERR_UNSUPPORTED).  Outputs
+ * must be 16-byte aligned and overlap no input, each other or the workspace.
+ * `workspace`: at least ckda_chunk_bwd_workspace_size(desc, cu_seqlens !=
+ * NULL) bytes, 256-byte aligned, scratch.  Asynchronous on `stream`.
+ */
+size_t ckda_chunk_bwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed);
+ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* desc, const void* q, const void* k,
+                             const void* v, const void* alpha, const void* beta,
+                             const int32_t* cu_seqlens, const float* h0, const void* dout,
+                             const float* dht, float* dq, float* dk, float* dv,
+                             float* dalpha, float* dbeta, float* dh0, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Fused single-token decode step for N sequences (the recurrent form of the

@@ -188,3 +188,131 @@ def fwd(q, k, v, alpha, beta, h0=None, seq_start=None, use_l2norm=True, scale=1.
                 o[s0:s1, h] = oo
             ht[n, h] = S
     return o.reshape(out_shape), ht
+
+
+# ----------------------------------------------------------------- backward
+def chunk_head_bwd(q, k, v, alpha, beta, S_init, dO, dS_end, use_l2norm, scale, C):
+    """Gradients for one sequence and head through the chunked form, as the
+    HIP backward computes them (chunk-anchored ratios; every running product
+    must be nonzero).  Returns (dq, dk, dv, dalpha, dbeta, dS_init).
+
+    Per chunk with entry state S0, exit-state gradient dS1 and output
+    gradient dO, and Y = X Diag(beta), Z = V - Kt S0, U = Y Z:
+      O = scale (Qt S0 + P U),  S1 = Diag(g) S0 + Kh^T U
+      dU  = scale P^T dO + Kh dS1                     (state pass, reverse)
+      dS0 = scale Qt^T dO + Diag(g) dS1 - Kt^T Y^T dU
+      dV  = Y^T dU
+      dQt = scale dO S0^T,  dP = scale dO U^T (lower),  dKh = U dS1^T,
+      dg  = rowsum(dS1 * S0),  dY = dU Z^T,  dKt = -(Y^T dU) S0^T
+      dX  = dY Diag(beta),  dbeta_j += sum_r X_rj dY_rj
+      dA  = -X^T dX X^T (strictly lower),  A = Diag(beta) G
+      dbeta_r += sum_j dA_rj G_rj,  dG = Diag(beta) dA
+      dKt += dG Rk,  dQt += dP Rk,  dRk = dG^T Kt + dP^T Qt + g * dKh,
+      dg += sum_j dKh_j * Rk_j
+      dk_hat = dKt * F + dRk / F,  dq_hat = dQt * F
+      Lam = dKt * Kt + dQt * Qt - dRk * Rk,  Lam_{C-1} += dg * g
+      dalpha_s = (sum_{r>=s} Lam_r) / alpha_s      (d log|alpha| summed)
+    then dx = r (dx_hat - x_hat (x_hat . dx_hat)) through each norm."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    rq_all, rk_all = _l2scale(q, use_l2norm), _l2scale(k, use_l2norm)
+    qh_all, kh_all = q * rq_all[:, None], k * rk_all[:, None]
+    # forward sweep: entry state of every chunk
+    starts = list(range(0, T, C))
+    S = S_init.copy()
+    S0s = []
+    for c0 in starts:
+        S0s.append(S.copy())
+        L = min(C, T - c0)
+        _, S = chunk_head(q[c0:c0 + L], k[c0:c0 + L], v[c0:c0 + L], alpha[c0:c0 + L],
+                          beta[c0:c0 + L], S, use_l2norm, scale, C)
+    dq, dk_, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dal, dbe = np.zeros_like(alpha), np.zeros_like(beta)
+    dS = dS_end.copy()
+    for ci in range(len(starts) - 1, -1, -1):
+        c0 = starts[ci]
+        L = min(C, T - c0)
+        S0 = S0s[ci]
+        qh = np.zeros((C, dk)); qh[:L] = qh_all[c0:c0 + L]
+        kh = np.zeros((C, dk)); kh[:L] = kh_all[c0:c0 + L]
+        V = np.zeros((C, dv)); V[:L] = v[c0:c0 + L]
+        G_O = np.zeros((C, dv)); G_O[:L] = dO[c0:c0 + L]
+        ac = np.ones((C, dk)); ac[:L] = alpha[c0:c0 + L]
+        bc = np.zeros(C); bc[:L] = beta[c0:c0 + L]
+        F = np.cumprod(ac, axis=0)
+        g = F[C - 1]
+        Kt, Qt, Rk = kh * F, qh * F, kh / F
+        Kh = g * Rk
+        G = np.tril(Kt @ Rk.T, -1)
+        A = bc[:, None] * G
+        X = np.linalg.inv(np.eye(C) + A)
+        Y = X * bc[None, :]
+        P = np.tril(Qt @ Rk.T)
+        Z = V - Kt @ S0
+        U = Y @ Z
+        dS1 = dS
+        dU = scale * P.T @ G_O + Kh @ dS1
+        dS = scale * Qt.T @ G_O + g[:, None] * dS1 - Kt.T @ (Y.T @ dU)
+        dvv[c0:c0 + L] = (Y.T @ dU)[:L]
+        dQt = scale * G_O @ S0.T
+        dP = np.tril(scale * G_O @ U.T)
+        dKh = U @ dS1.T
+        dg = (dS1 * S0).sum(1)
+        dY = dU @ Z.T
+        dKt = -(Y.T @ dU) @ S0.T
+        dX = dY * bc[None, :]
+        db = (X * dY).sum(0)
+        dA = np.tril(-X.T @ dX @ X.T, -1)
+        db = db + (dA * G).sum(1)
+        dG = bc[:, None] * dA
+        dKt = dKt + dG @ Rk
+        dQt = dQt + dP @ Rk
+        dRk = dG.T @ Kt + dP.T @ Qt + g * dKh
+        dg = dg + (dKh * Rk).sum(0)
+        dkh = dKt * F + dRk / F
+        dqh = dQt * F
+        Lam = dKt * Kt + dQt * Qt - dRk * Rk
+        Lam[C - 1] += dg * g
+        dlog = np.cumsum(Lam[::-1], axis=0)[::-1]
+        dal[c0:c0 + L] = (dlog / ac)[:L]
+        dbe[c0:c0 + L] = db[:L]
+        for name, xh, dxh, r, out in (("q", qh, dqh, rq_all, dq), ("k", kh, dkh, rk_all, dk_)):
+            if use_l2norm:
+                proj = (xh * dxh).sum(1, keepdims=True)
+                out[c0:c0 + L] = (r[c0:c0 + L, None] * (dxh - xh * proj)[:L])
+            else:
+                out[c0:c0 + L] = dxh[:L]
+    return dq, dk_, dvv, dal, dbe, dS
+
+
+def bwd(q, k, v, alpha, beta, dO, h0=None, dht=None, seq_start=None, use_l2norm=True,
+        scale=1.0, C=64):
+    """Same calling convention as oracle.bwd."""
+    q, k, v, alpha, beta, dO = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, beta, dO))
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if seq_start is None:
+        B, T = q.shape[0], q.shape[1]
+        starts = np.arange(B + 1) * T
+    else:
+        starts = np.asarray(seq_start)
+    shp = [x.shape for x in (q, k, v, alpha, beta)]
+    q, k, alpha = (a.reshape(-1, H, dk) for a in (q, k, alpha))
+    v, dO = v.reshape(-1, H, dv), dO.reshape(-1, H, dv)
+    beta = beta.reshape(-1, H)
+    N = len(starts) - 1
+    outs = [np.zeros_like(x) for x in (q, k, v, alpha, beta)]
+    dh0 = np.zeros((N, H, dk, dv))
+    for n in range(N):
+        s0, s1 = starts[n], starts[n + 1]
+        for h in range(H):
+            S = np.zeros((dk, dv)) if h0 is None else np.array(h0[n, h], dtype=np.float64)
+            dS = np.zeros((dk, dv)) if dht is None else np.array(dht[n, h], dtype=np.float64)
+            if s1 > s0:
+                r = chunk_head_bwd(q[s0:s1, h], k[s0:s1, h], v[s0:s1, h], alpha[s0:s1, h],
+                                   beta[s0:s1, h], S, dO[s0:s1, h], dS, use_l2norm, scale, C)
+                for o_, g_ in zip(outs, r[:5]):
+                    o_[s0:s1, h] = g_
+                dS = r[5]
+            dh0[n, h] = dS
+    return tuple(o.reshape(s) for o, s in zip(outs, shp)) + (dh0,)

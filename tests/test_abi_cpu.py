@@ -226,3 +226,62 @@ def test_l2norm_debug_validation():
     assert lib.ckda_l2norm_debug(P["q"], P["o"], 10, 2048, ck.F32, None) == 1
     assert lib.ckda_l2norm_debug(P["q"], P["q"], 10, 16, ck.F32, None) == 1
     assert lib.ckda_l2norm_debug(P["q"], P["o"], 0, 16, ck.F32, None) == 0
+
+
+# ---------------------------------------------------------------- backward
+PB = {n: ctypes.c_void_p(BASE + (20 + i) * (1 << 32)) for i, n in
+      enumerate(["dout", "dht", "dq", "dk", "dv", "dalpha", "dbeta", "dh0"])}
+
+
+def _bwd(desc, **over):
+    p = dict(P)
+    p.update(PB)
+    p.update(over)
+    lib = ck._load()
+    st = lib.ckda_chunk_bwd(ctypes.byref(desc), p["q"], p["k"], p["v"], p["alpha"], p["beta"],
+                            p.get("cu_seqlens"), p["h0"], p["dout"], p["dht"], p["dq"], p["dk"],
+                            p["dv"], p["dalpha"], p["dbeta"], p["dh0"], p["ws"],
+                            p.get("ws_bytes", WS_BYTES), None)
+    return st, lib.ckda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(gate_input=ck.GATES_LOGITS_F32), 2, "gate values"),
+    (dict(qk_heads=1), 2, "qk_heads == H"),
+    (dict(sign_absorb=1), 2, "sign-absorption"),
+    (dict(chunk_size=48), 1, "chunk_size"),
+    (dict(B=0), 1, "non-positive"),
+])
+def test_bwd_rejects_bad_descriptor(over, status, needle):
+    st, msg = _bwd(_desc(**over))
+    assert st == status and needle in msg, msg
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(dq=None), "must not be NULL"),
+    (dict(dbeta=None), "must not be NULL"),
+    (dict(dalpha=ctypes.c_void_p(BASE + (23 << 32) + 8)), "not 16-byte aligned"),
+    (dict(dv=P["q"]), "dv overlaps q"),
+    (dict(dk=PB["dq"]), "dk overlaps dq"),
+    (dict(ws=PB["dalpha"]), "overlaps"),
+    (dict(ws_bytes=1024), "workspace has 1024 bytes"),
+])
+def test_bwd_rejects_bad_pointers(over, needle):
+    st, msg = _bwd(_desc(), **over)
+    assert st == 1 and needle in msg, msg
+
+
+def test_bwd_workspace_covers_forward_and_records():
+    """The backward's workspace holds the forward's plus X (fp32 C x C), the
+    entry state and the exit-state adjoint (fp32 dk x dv each), dU (fp32
+    C x dv) per (head, chunk), one flag each, and the intra kernel's scratch."""
+    lib = ck._load()
+    d = _desc(B=2, T=130, H=3, dk=64, dv=64, chunk_size=32)
+    fwd = lib.ckda_chunk_fwd_workspace_size(ctypes.byref(d), 0)
+    bwd = lib.ckda_chunk_bwd_workspace_size(ctypes.byref(d), 0)
+    hm = 3 * 2 * 5  # heads x (B * ceil(130 / 32)) chunk slots
+    up = lambda x: (x + 255) // 256 * 256
+    grid = min(hm, 1024)
+    extra = (up(4 * hm * 32 * 32) + 2 * up(4 * hm * 64 * 64) + up(4 * hm * 32 * 64) + up(4 * hm)
+             + up(4 * grid * 10 * 32 * 64))
+    assert bwd == fwd + extra
