@@ -93,6 +93,75 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
+// out(m, n) = alpha * sum_k A(m, k) B(k, n) (+ out(m, n) when acc), fp32, for
+// M <= 64, N <= 128, by the kNT threads of the workgroup: thread (tx, ty) of
+// a 16 x 16 grid owns rows ty + 16 i and columns tx + 16 j.  la(m, k) and
+// lb(k, n) load the operands (any storage); out(m, n) = O[m om + n on] (any
+// address space).  K is walked in slices of 16 staged in LDS (`stage`,
+// kGStage floats); a_mfast / b_nfast say which index of the operand is the
+// contiguous one, so that consecutive threads stage consecutive elements.
+// Ends with a barrier.
+constexpr int kGM = 4, kGN = 8, kGStage = 16 * (16 * kGM + 1) + 16 * (16 * kGN + 1);
+template <class LA, class LB>
+__device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc, LA la,
+                                     bool a_mfast, LB lb, bool b_nfast, float* O, int om, int on,
+                                     float* stage) {
+  constexpr int MP = 16 * kGM, NP = 16 * kGN;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float* sA = stage;                   // [16][MP + 1]
+  float* sB = stage + 16 * (MP + 1);   // [16][NP + 1]
+  float c[kGM][kGN];
+#pragma unroll
+  for (int i = 0; i < kGM; ++i)
+#pragma unroll
+    for (int j = 0; j < kGN; ++j) c[i][j] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    __syncthreads();
+    for (int e = tid; e < 16 * MP; e += kNT) {
+      int kk, m;
+      if (a_mfast) { m = e % MP; kk = e / MP; } else { kk = e % 16; m = e / 16; }
+      sA[kk * (MP + 1) + m] = (m < M && k0 + kk < K) ? la(m, k0 + kk) : 0.f;
+    }
+    for (int e = tid; e < 16 * NP; e += kNT) {
+      int kk, n;
+      if (b_nfast) { n = e % NP; kk = e / NP; } else { kk = e % 16; n = e / 16; }
+      sB[kk * (NP + 1) + n] = (n < N && k0 + kk < K) ? lb(k0 + kk, n) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[kGM], bv[kGN];
+#pragma unroll
+      for (int i = 0; i < kGM; ++i) av[i] = sA[kk * (MP + 1) + ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < kGN; ++j) bv[j] = sB[kk * (NP + 1) + tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < kGM; ++i)
+#pragma unroll
+        for (int j = 0; j < kGN; ++j) c[i][j] += av[i] * bv[j];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kGM; ++i)
+#pragma unroll
+    for (int j = 0; j < kGN; ++j) {
+      const int m = ty + 16 * i, n = tx + 16 * j;
+      if (m < M && n < N) {
+        float* o = O + m * om + n * on;
+        *o = acc ? *o + alpha * c[i][j] : alpha * c[i][j];
+      }
+    }
+  __syncthreads();
+}
+// the same with both operands strided fp32 arrays: A(m, k) = A[m am + k ak],
+// B(k, n) = B[k bk + n bn]
+__device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc, const float* A,
+                                     int am, int ak, const float* B, int bk, int bn, float* O,
+                                     int om, int on, float* stage) {
+  gemm(M, N, K, alpha, acc, [=](int m, int k) { return A[m * am + k * ak]; }, am == 1,
+       [=](int k, int n) { return B[k * bk + n * bn]; }, bn == 1, O, om, on, stage);
+}
+
 // ---------------------------------------------------------------- 2: state
 // One workgroup per (sequence, head, tile of DVB value columns); the columns
 // of the state adjoint are independent, so no tile needs another's.
@@ -124,7 +193,8 @@ __global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
   float* sdO = sm;               // [C][DVB]
   float* sdS = sdO + C * DVB;    // [dk][DVB] adjoint at the chunk's exit
   float* sdU = sdS + dk * DVB;   // [C][DVB]
-  float* sdS0 = sdU + C * DVB;   // [dk][DVB]
+  float* sdS0 = sdU + C * DVB;   // [max(dk, C)][DVB]: dS0, and dV before it
+  float* stage = sdS0 + cmax(dk, C) * DVB;
   const int tid = threadIdx.x;
   const int64_t st = (static_cast<int64_t>(n) * H + h) * dk * dv + dv0;
   for (int e = tid; e < dk * DVB; e += kNT)
@@ -150,33 +220,30 @@ __global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
     for (int e = tid; e < dk * DVB; e += kNT)
       b.dS[(slot * dk + e / DVB) * dv + dv0 + e % DVB] = sdS[e];
     __syncthreads();
+    auto ld_dO = [=](int k, int n) { return sdO[k * DVB + n]; };
+    auto ld_dS = [=](int k, int n) { return sdS[k * DVB + n]; };
     // dU = P'^T dO + Kh' dS1   (P' = scale P, lower; Kh' = Kh)
+    gemm(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bP, k, m, C); }, true, ld_dO,
+         true, sdU, DVB, 1, stage);
+    gemm(C, DVB, dk, 1.f, true, [=](int m, int k) { return blk_at<IO>(bK, k, m, C); }, true, ld_dS,
+         true, sdU, DVB, 1, stage);
+    for (int e = tid; e < C * DVB; e += kNT)
+      b.dU[(slot * C + e / DVB) * dv + dv0 + e % DVB] = sdU[e];
+    // dV = X'^T dU   (X' = Y); rows >= L are not outputs (O into sdS0 first)
+    gemm(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bX, k, m, C); }, true,
+         [=](int k, int n) { return sdU[k * DVB + n]; }, true, sdS0, DVB, 1, stage);
     for (int e = tid; e < C * DVB; e += kNT) {
       const int r = e / DVB, j = e % DVB;
-      float acc = 0.f;
-      for (int rr = r; rr < C; ++rr) acc += blk_at<IO>(bP, rr, r, C) * sdO[rr * DVB + j];
-      for (int cc = 0; cc < dk; ++cc) acc += blk_at<IO>(bK, cc, r, C) * sdS[cc * DVB + j];
-      sdU[e] = acc;
+      if (r < L) b.dv[((t0 + r) * H + h) * dv + dv0 + j] = sdS0[e];
     }
     __syncthreads();
-    for (int e = tid; e < C * DVB; e += kNT) {
-      const int r = e / DVB, j = e % DVB;
-      b.dU[(slot * C + r) * dv + dv0 + j] = sdU[e];
-      if (r < L) {  // dV = X'^T dU   (X' = Y, lower)
-        float acc = 0.f;
-        for (int rr = r; rr < C; ++rr) acc += blk_at<IO>(bX, rr, r, C) * sdU[rr * DVB + j];
-        b.dv[((t0 + r) * H + h) * dv + dv0 + j] = acc;
-      }
-    }
-    // dS0 = Qt'^T dO + Diag(g) dS1 + W'^T dU   (W' = -W as stored)
-    for (int e = tid; e < dk * DVB; e += kNT) {
-      const int cc = e / DVB, j = e % DVB;
-      float acc = bg[cc] * sdS[e];
-      for (int r = 0; r < C; ++r)
-        acc += blk_at<IO>(bQ, r, cc, dk) * sdO[r * DVB + j] + blk_at<IO>(bW, r, cc, dk) * sdU[r * DVB + j];
-      sdS0[e] = acc;
-    }
+    // dS0^T = dO^T Qt' + dU^T W' + dS1^T Diag(g)   (W' = -W as stored)
+    for (int e = tid; e < dk * DVB; e += kNT) sdS0[e] = bg[e / DVB] * sdS[e];
     __syncthreads();
+    gemm(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdO[k * DVB + m]; }, true,
+         [=](int k, int n) { return blk_at<IO>(bQ, k, n, dk); }, true, sdS0, 1, DVB, stage);
+    gemm(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdU[k * DVB + m]; }, true,
+         [=](int k, int n) { return blk_at<IO>(bW, k, n, dk); }, true, sdS0, 1, DVB, stage);
     for (int e = tid; e < dk * DVB; e += kNT) sdS[e] = sdS0[e];
   }
   __syncthreads();
@@ -185,9 +252,9 @@ __global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
 }
 
 // ---------------------------------------------------------------- 3: intra
-// One (chunk, head) at a time per workgroup, items b, b + grid, ...
-// C x C matrices in LDS; C x dk and C x dv intermediates in the workgroup's
-// slice of the scratch.
+// One (chunk, head) at a time per workgroup, items b, b + grid, ...  The
+// products run through gemm(); C x C matrices in LDS where they fit, the rest
+// in the workgroup's slice of the scratch.
 template <class IO>
 __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
   using ST = typename IO::storage;
@@ -196,22 +263,26 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
   const int total = a.maxc * H;
   const bool l2 = a.use_l2norm != 0;
   const float scale = a.scale;
-  const int SC = C * (dk > dv ? dk : dv);
-  float* ws = b.scratch + static_cast<int64_t>(blockIdx.x) * 10 * SC;
+  const int SC = C * cmax(cmax(dk, dv), C);
+  float* ws = b.scratch + static_cast<int64_t>(blockIdx.x) * 14 * SC;
+  // scratch slices: C x dk (stride dk) or C x dv (stride dv) or C x C
   float *sF = ws, *sKt = ws + SC, *sQt = ws + 2 * SC, *sRk = ws + 3 * SC, *sZ = ws + 4 * SC,
-        *sU = ws + 5 * SC, *sT1 = ws + 6 * SC, *sdq = ws + 7 * SC, *sdk = ws + 8 * SC,
-        *sLam = ws + 9 * SC;
+        *sU = ws + 5 * SC, *sT1 = ws + 6 * SC, *sV = ws + 7 * SC, *sdO = ws + 8 * SC,
+        *sG = ws + 9 * SC, *sdP = ws + 10 * SC, *sdQ = ws + 11 * SC, *sdK = ws + 12 * SC,
+        *sdR = ws + 13 * SC;
   extern __shared__ float sm[];
-  float* lX = sm;               // [C][C] X
-  float* ldY = lX + C * C;      // [C][C] dY -> dX -> dA -> dG
-  float* lT = ldY + C * C;      // [C][C] dX X^T
-  float* ldP = lT + C * C;      // [C][C] dP
-  float* lbeta = ldP + C * C;   // [C]
+  float* lY = sm;               // [C][C] Y = X Diag(beta)
+  float* ldX = lY + C * C;      // [C][C] dY -> dX
+  float* lT = ldX + C * C;      // [C][C] dX X^T
+  float* ldA = lT + C * C;      // [C][C] dA -> dG
+  float* stage = ldA + C * C;   // gemm staging
+  float* lbeta = stage + kGStage;  // [C]
   float* lrq = lbeta + C;       // [C]
   float* lrk = lrq + C;         // [C]
   float* ldb = lrk + C;         // [C]
   float* lg = ldb + C;          // [dk]
-  int* lflag = reinterpret_cast<int*>(lg + dk);
+  float* ldg = lg + dk;         // [dk]
+  int* lflag = reinterpret_cast<int*>(ldg + dk);
   const int tid = threadIdx.x;
   const ST* q = static_cast<const ST*>(a.q);
   const ST* k = static_cast<const ST*>(a.k);
@@ -235,7 +306,7 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
     const float* dS1 = b.dS + slot * dk * dv;
     const float* dU = b.dU + slot * C * dv;
     const float* X = a.xout + slot * C * C;
-    // A: norms, beta, gate products, regularity
+    // norms, beta, gate products, regularity
     if (tid == 0) *lflag = 0;
     for (int r = tid; r < C; r += kNT) {
       float sq = 0.f, sk = 0.f;
@@ -250,7 +321,6 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
       lrq[r] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sq + kL2Eps)) : 1.f;
       lrk[r] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sk + kL2Eps)) : 1.f;
       lbeta[r] = r < L ? beta[(t0 + r) * H + h] : 0.f;
-      ldb[r] = 0.f;
     }
     __syncthreads();
     for (int cc = tid; cc < dk; cc += kNT) {
@@ -269,7 +339,7 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
     const bool irregular = *lflag != 0;
     if (tid == 0) b.bflag[slot] = irregular ? 1 : 0;
     if (irregular) continue;
-    // B: Kt, Qt, Rk; X to LDS
+    // operands: Kt, Qt, Rk; V, dO as fp32 (rows >= L zero); Y
     for (int e = tid; e < C * dk; e += kNT) {
       const int r = e / dk, cc = e % dk;
       const int64_t i = ((t0 + r) * H + h) * dk + cc;
@@ -280,126 +350,101 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
       sQt[e] = qh * f;
       sRk[e] = kh / f;
     }
-    for (int e = tid; e < C * C; e += kNT) lX[e] = X[e];
-    __syncthreads();
-    // C: Z = V - Kt S0
     for (int e = tid; e < C * dv; e += kNT) {
       const int r = e / dv, j = e % dv;
-      float acc = r < L ? IO::load(v, ((t0 + r) * H + h) * dv + j) : 0.f;
-      for (int cc = 0; cc < dk; ++cc) acc -= sKt[r * dk + cc] * S0[cc * dv + j];
-      sZ[e] = acc;
+      const int64_t i = ((t0 + r) * H + h) * dv + j;
+      sV[e] = r < L ? IO::load(v, i) : 0.f;
+      sZ[e] = sV[e];
+      sdO[e] = r < L ? IO::load(dO, i) : 0.f;
     }
+    for (int e = tid; e < C * C; e += kNT) lY[e] = X[e] * lbeta[e % C];
     __syncthreads();
-    // D: U = Y Z (Y = X Diag(beta), lower), T1 = Y^T dU
-    for (int e = tid; e < C * dv; e += kNT) {
-      const int r = e / dv, j = e % dv;
-      float u = 0.f, t = 0.f;
-      for (int m = 0; m <= r; ++m) u += lX[r * C + m] * lbeta[m] * sZ[m * dv + j];
-      for (int m = r; m < C; ++m) t += lX[m * C + r] * lbeta[r] * dU[m * dv + j];
-      sU[e] = u;
-      sT1[e] = t;
-    }
-    __syncthreads();
-    // E: dY = dU Z^T (lower with the diagonal), dP = tril(scale dO U^T)
-    for (int e = tid; e < C * C; e += kNT) {
-      const int r = e / C, m = e % C;
-      float y = 0.f, p = 0.f;
-      if (m <= r) {
-        for (int j = 0; j < dv; ++j) y += dU[r * dv + j] * sZ[m * dv + j];
-        if (r < L)
-          for (int j = 0; j < dv; ++j) p += IO::load(dO, ((t0 + r) * H + h) * dv + j) * sU[m * dv + j];
-      }
-      ldY[e] = y;
-      ldP[e] = scale * p;
-    }
-    __syncthreads();
-    // F: dbeta_j = sum_r X_rj dY_rj; dX = dY Diag(beta)
+    // Z = V - Kt S0;  U = Y Z;  T1 = Y^T dU
+    gemm(C, dv, dk, -1.f, true, sKt, dk, 1, S0, dv, 1, sZ, dv, 1, stage);
+    gemm(C, dv, C, 1.f, false, lY, C, 1, sZ, dv, 1, sU, dv, 1, stage);
+    gemm(C, dv, C, 1.f, false, lY, 1, C, dU, dv, 1, sT1, dv, 1, stage);
+    // dY = dU Z^T;  dP = scale dO U^T (both lower with the diagonal);  G = Kt Rk^T
+    gemm(C, C, dv, 1.f, false, dU, dv, 1, sZ, 1, dv, ldX, C, 1, stage);
+    gemm(C, C, dv, scale, false, sdO, dv, 1, sU, 1, dv, sdP, C, 1, stage);
+    gemm(C, C, dk, 1.f, false, sKt, dk, 1, sRk, 1, dk, sG, C, 1, stage);
+    // dbeta_j = sum_r X_rj dY_rj;  dX = dY Diag(beta), masked
     for (int j = tid; j < C; j += kNT) {
       float s = 0.f;
-      for (int r = j; r < C; ++r) s += lX[r * C + j] * ldY[r * C + j];
+      for (int r = j; r < C; ++r) s += X[r * C + j] * ldX[r * C + j];
       ldb[j] = s;
     }
     __syncthreads();
-    for (int e = tid; e < C * C; e += kNT) ldY[e] *= lbeta[e % C];
-    __syncthreads();
-    // G: T = dX X^T
     for (int e = tid; e < C * C; e += kNT) {
-      const int r = e / C, j = e % C;
-      float s = 0.f;
-      for (int m = 0; m < C; ++m) s += ldY[r * C + m] * lX[j * C + m];
-      lT[e] = s;
+      const int r = e / C, m = e % C;
+      ldX[e] = m <= r ? ldX[e] * lbeta[m] : 0.f;
+      if (m > r) sdP[e] = 0.f;
     }
     __syncthreads();
-    // H: dA = -X^T T, strictly lower
-    for (int e = tid; e < C * C; e += kNT) {
-      const int r = e / C, j = e % C;
-      float s = 0.f;
-      if (j < r)
-        for (int m = 0; m < C; ++m) s -= lX[m * C + r] * lT[m * C + j];
-      ldY[e] = s;
-    }
-    __syncthreads();
-    // I: dbeta_r += sum_j dA_rj G_rj (G = Kt Rk^T); dG = Diag(beta) dA
+    // T = dX X^T;  dA = -X^T T (strictly lower)
+    gemm(C, C, C, 1.f, false, ldX, C, 1, X, 1, C, lT, C, 1, stage);
+    gemm(C, C, C, -1.f, false, X, 1, C, lT, C, 1, ldA, C, 1, stage);
+    // dbeta_r += sum_{j<r} dA_rj G_rj;  dG = Diag(beta) dA
     for (int r = tid; r < C; r += kNT) {
       float s = 0.f;
-      for (int j = 0; j < r; ++j) {
-        float gg = 0.f;
-        for (int cc = 0; cc < dk; ++cc) gg += sKt[r * dk + cc] * sRk[j * dk + cc];
-        s += ldY[r * C + j] * gg;
-        ldY[r * C + j] *= lbeta[r];
-      }
+      for (int j = 0; j < r; ++j) s += ldA[r * C + j] * sG[r * C + j];
       ldb[r] += s;
     }
     __syncthreads();
-    // J: per element (r, cc)
-    for (int e = tid; e < C * dk; e += kNT) {
-      const int r = e / dk, cc = e % dk;
-      float dqt = 0.f, dkt = 0.f, dkh = 0.f, drk = 0.f;
-      for (int j = 0; j < dv; ++j) {
-        const float s0 = S0[cc * dv + j];
-        if (r < L) dqt += IO::load(dO, ((t0 + r) * H + h) * dv + j) * s0;
-        dkt -= sT1[r * dv + j] * s0;
-        dkh += sU[r * dv + j] * dS1[cc * dv + j];
-      }
-      dqt *= scale;
-      for (int m = 0; m <= r; ++m) dqt += ldP[r * C + m] * sRk[m * dk + cc];
-      for (int m = 0; m < r; ++m) dkt += ldY[r * C + m] * sRk[m * dk + cc];
-      for (int m = r + 1; m < C; ++m) drk += ldY[m * C + r] * sKt[m * dk + cc];
-      for (int m = r; m < C; ++m) drk += ldP[m * C + r] * sQt[m * dk + cc];
-      drk += lg[cc] * dkh;
-      const float f = sF[e];
-      sdk[e] = dkt * f + drk / f;
-      sdq[e] = dqt * f;
-      sLam[e] = dkt * sKt[e] + dqt * sQt[e] - drk * sRk[e];
-      sZ[e] = dkh * sRk[e];  // Z is no longer needed: dg terms per row
+    for (int e = tid; e < C * C; e += kNT) {
+      const int r = e / C, j = e % C;
+      ldA[e] = j < r ? ldA[e] * lbeta[r] : 0.f;
     }
     __syncthreads();
-    // K: dalpha per channel (reverse running sums of Lam, divided by alpha)
+    // dQt = scale dO S0^T + dP Rk;  dKt = -T1 S0^T + dG Rk;
+    // dRk = dG^T Kt + dP^T Qt + g dKh with dKh = U dS1^T
+    gemm(C, dk, dv, scale, false, sdO, dv, 1, S0, 1, dv, sdQ, dk, 1, stage);
+    gemm(C, dk, C, 1.f, true, sdP, C, 1, sRk, dk, 1, sdQ, dk, 1, stage);
+    gemm(C, dk, dv, -1.f, false, sT1, dv, 1, S0, 1, dv, sdK, dk, 1, stage);
+    gemm(C, dk, C, 1.f, true, ldA, C, 1, sRk, dk, 1, sdK, dk, 1, stage);
+    gemm(C, dk, dv, 1.f, false, sU, dv, 1, dS1, 1, dv, sZ, dk, 1, stage);  // dKh -> Z's slice
+    gemm(C, dk, C, 1.f, false, ldA, 1, C, sKt, dk, 1, sdR, dk, 1, stage);
+    gemm(C, dk, C, 1.f, true, sdP, 1, C, sQt, dk, 1, sdR, dk, 1, stage);
+    // dg = rowsum(dS1 * S0) + sum_r dKh_r Rk_r
     for (int cc = tid; cc < dk; cc += kNT) {
-      float dg = 0.f;
-      for (int j = 0; j < dv; ++j) dg += dS1[cc * dv + j] * S0[cc * dv + j];
-      for (int r = 0; r < C; ++r) dg += sZ[r * dk + cc];
-      float acc = dg * lg[cc];
+      float s = 0.f;
+      for (int j = 0; j < dv; ++j) s += dS1[cc * dv + j] * S0[cc * dv + j];
+      for (int r = 0; r < C; ++r) s += sZ[r * dk + cc] * sRk[r * dk + cc];
+      ldg[cc] = s;
+    }
+    __syncthreads();
+    // elementwise: dk^, dq^ in place; Lam into sF's slice (F read first)
+    for (int e = tid; e < C * dk; e += kNT) {
+      const int cc = e % dk;
+      const float f = sF[e];
+      const float dqt = sdQ[e], dkt = sdK[e], drk = sdR[e] + lg[cc] * sZ[e];
+      sdK[e] = dkt * f + drk / f;
+      sdQ[e] = dqt * f;
+      sF[e] = dkt * sKt[e] + dqt * sQt[e] - drk * sRk[e];
+    }
+    __syncthreads();
+    // dalpha per channel: reverse running sums of Lam, divided by alpha
+    for (int cc = tid; cc < dk; cc += kNT) {
+      float acc = ldg[cc] * lg[cc];
       for (int r = C - 1; r >= 0; --r) {
-        acc += sLam[r * dk + cc];
+        acc += sF[r * dk + cc];
         if (r < L) {
           const int64_t i = ((t0 + r) * H + h) * dk + cc;
           b.dalpha[i] = acc / alpha[i];
         }
       }
     }
-    // L: dq, dk through the norms; dbeta
+    // dq, dk through the norms; dbeta
     for (int r = tid; r < L; r += kNT) {
       float pq = 0.f, pk = 0.f;
       const int64_t base = ((t0 + r) * H + h) * dk;
       for (int cc = 0; cc < dk; ++cc) {
-        pq += IO::load(q, base + cc) * lrq[r] * sdq[r * dk + cc];
-        pk += IO::load(k, base + cc) * lrk[r] * sdk[r * dk + cc];
+        pq += IO::load(q, base + cc) * lrq[r] * sdQ[r * dk + cc];
+        pk += IO::load(k, base + cc) * lrk[r] * sdK[r * dk + cc];
       }
       for (int cc = 0; cc < dk; ++cc) {
         const float qh = IO::load(q, base + cc) * lrq[r], kh = IO::load(k, base + cc) * lrk[r];
-        b.dq[base + cc] = l2 ? lrq[r] * (sdq[r * dk + cc] - qh * pq) : sdq[r * dk + cc];
-        b.dk[base + cc] = l2 ? lrk[r] * (sdk[r * dk + cc] - kh * pk) : sdk[r * dk + cc];
+        b.dq[base + cc] = l2 ? lrq[r] * (sdQ[r * dk + cc] - qh * pq) : sdQ[r * dk + cc];
+        b.dk[base + cc] = l2 ? lrk[r] * (sdK[r * dk + cc] - kh * pk) : sdK[r * dk + cc];
       }
       b.dbeta[(t0 + r) * H + h] = ldb[r];
     }
@@ -571,7 +616,10 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
   const int C = a.chunk, dk = a.dk, dv = a.dv;
   const int DVB = dv < 32 ? dv : 32;
   const int64_t g2 = static_cast<int64_t>(a.num_seqs) * a.H * (dv / DVB);
-  const size_t lds2 = sizeof(float) * (2 * C * DVB + 2 * dk * DVB);
+  const size_t lds2 = sizeof(float) * (2 * C * DVB + dk * DVB + cmax(dk, C) * DVB + kGStage);
+  static const hipError_t attr2 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&bwd_state_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+  if (attr2 != hipSuccess) return attr2;
   if (g2 > 0) {
     hipLaunchKernelGGL((bwd_state_kernel<IO>), dim3(static_cast<unsigned>(g2)), dim3(kNT), lds2, stream, b);
     const hipError_t e = hipGetLastError();
@@ -579,9 +627,9 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
   }
   const int64_t total = static_cast<int64_t>(a.maxc) * a.H;
   if (total == 0) return hipSuccess;
-  const size_t lds3 = sizeof(float) * (4 * C * C + 4 * C + dk) + sizeof(int);
+  const size_t lds3 = sizeof(float) * (4 * C * C + kGStage + 4 * C + 2 * dk) + sizeof(int);
   static const hipError_t attr3 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&bwd_intra_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024 + 4096);
+      reinterpret_cast<const void*>(&bwd_intra_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
   if (attr3 != hipSuccess) return attr3;
   hipLaunchKernelGGL((bwd_intra_kernel<IO>), dim3(static_cast<unsigned>(b.grid3)), dim3(kNT), lds3, stream, b);
   hipError_t e = hipGetLastError();
@@ -602,9 +650,9 @@ int32_t bwd_grid3(int64_t total) { return static_cast<int32_t>(total < 1024 ? (t
 int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv) {
   auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
   const int64_t hm = static_cast<int64_t>(H) * maxc;
-  const int64_t SC = static_cast<int64_t>(C) * (dk > dv ? dk : dv);
+  const int64_t SC = static_cast<int64_t>(C) * cmax(cmax(dk, dv), C);
   return up(4 * hm * C * C) + 2 * up(4 * hm * dk * dv) + up(4 * hm * C * dv) + up(4 * hm) +
-         up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 10 * SC);
+         up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 14 * SC);
 }
 
 void bwd_layout(BwdArgs& b, unsigned char* base) {

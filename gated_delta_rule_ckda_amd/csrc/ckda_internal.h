@@ -138,7 +138,7 @@ struct BwdArgs {
   float* dS;         // [H][maxc][dk][dv] state adjoint at each chunk's exit
   float* dU;         // [H][maxc][C][dv]
   int32_t* bflag;    // [H][maxc] 1: chunk left to the token-level kernel
-  float* scratch;    // [grid3][10][C * max(dk, dv)]
+  float* scratch;    // [grid3][14][C * max(dk, dv, C)]
   int32_t grid3;
 };
 // Workspace bytes of the backward beyond the forward's, their layout from

@@ -283,5 +283,5 @@ def test_bwd_workspace_covers_forward_and_records():
     up = lambda x: (x + 255) // 256 * 256
     grid = min(hm, 1024)
     extra = (up(4 * hm * 32 * 32) + 2 * up(4 * hm * 64 * 64) + up(4 * hm * 32 * 64) + up(4 * hm)
-             + up(4 * grid * 10 * 32 * 64))
+             + up(4 * grid * 14 * 32 * 64))
     assert bwd == fwd + extra
