@@ -102,7 +102,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // contiguous one, so that consecutive threads stage consecutive elements.
 // Ends with a barrier.
 constexpr int kGM = 4, kGN = 8, kGStage = 16 * (16 * kGM + 1) + 16 * (16 * kGN + 1);
-template <class LA, class LB>
+template <bool PREFETCH = true, class LA, class LB>
 __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc, LA la,
                                      bool a_mfast, LB lb, bool b_nfast, float* O, int om, int on,
                                      float* stage) {
@@ -115,19 +115,45 @@ __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc,
   for (int i = 0; i < kGM; ++i)
 #pragma unroll
     for (int j = 0; j < kGN; ++j) c[i][j] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    __syncthreads();
-    for (int e = tid; e < 16 * MP; e += kNT) {
+  // this thread's staging elements of one K slice, loaded one slice ahead
+  constexpr int NA = 16 * MP / kNT, NB2 = 16 * NP / kNT;
+  float ra[NA], rb[NB2];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int e = tid + u * kNT;
       int kk, m;
       if (a_mfast) { m = e % MP; kk = e / MP; } else { kk = e % 16; m = e / 16; }
-      sA[kk * (MP + 1) + m] = (m < M && k0 + kk < K) ? la(m, k0 + kk) : 0.f;
+      ra[u] = (m < M && k0 + kk < K) ? la(m, k0 + kk) : 0.f;
     }
-    for (int e = tid; e < 16 * NP; e += kNT) {
+#pragma unroll
+    for (int u = 0; u < NB2; ++u) {
+      const int e = tid + u * kNT;
       int kk, n;
       if (b_nfast) { n = e % NP; kk = e / NP; } else { kk = e % 16; n = e / 16; }
-      sB[kk * (NP + 1) + n] = (n < N && k0 + kk < K) ? lb(k0 + kk, n) : 0.f;
+      rb[u] = (n < N && k0 + kk < K) ? lb(k0 + kk, n) : 0.f;
+    }
+  };
+  if (PREFETCH) fetch(0);
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    if (!PREFETCH) fetch(k0);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      const int e = tid + u * kNT;
+      int kk, m;
+      if (a_mfast) { m = e % MP; kk = e / MP; } else { kk = e % 16; m = e / 16; }
+      sA[kk * (MP + 1) + m] = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NB2; ++u) {
+      const int e = tid + u * kNT;
+      int kk, n;
+      if (b_nfast) { n = e % NP; kk = e / NP; } else { kk = e % 16; n = e / 16; }
+      sB[kk * (NP + 1) + n] = rb[u];
     }
     __syncthreads();
+    if (PREFETCH && k0 + 16 < K) fetch(k0 + 16);  // in flight while this slice is multiplied
 #pragma unroll 4
     for (int kk = 0; kk < 16; ++kk) {
       float av[kGM], bv[kGN];
@@ -154,11 +180,12 @@ __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc,
   __syncthreads();
 }
 // the same with both operands strided fp32 arrays: A(m, k) = A[m am + k ak],
-// B(k, n) = B[k bk + n bn]
+// B(k, n) = B[k bk + n bn]; no slice prefetch (a kernel with many products
+// inlined would run out of registers)
 __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc, const float* A,
                                      int am, int ak, const float* B, int bk, int bn, float* O,
                                      int om, int on, float* stage) {
-  gemm(M, N, K, alpha, acc, [=](int m, int k) { return A[m * am + k * ak]; }, am == 1,
+  gemm<false>(M, N, K, alpha, acc, [=](int m, int k) { return A[m * am + k * ak]; }, am == 1,
        [=](int k, int n) { return B[k * bk + n * bn]; }, bn == 1, O, om, on, stage);
 }
 
@@ -306,31 +333,56 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
     const float* dS1 = b.dS + slot * dk * dv;
     const float* dU = b.dU + slot * C * dv;
     const float* X = a.xout + slot * C * C;
-    // norms, beta, gate products, regularity
+    // norms (TPR threads per row, lane groups of a wave), beta
     if (tid == 0) *lflag = 0;
-    for (int r = tid; r < C; r += kNT) {
+    {
+      const int TPR = kNT / C, r = tid / TPR, sub = tid % TPR;
       float sq = 0.f, sk = 0.f;
       if (r < L) {
-        for (int cc = 0; cc < dk; ++cc) {
-          const int64_t i = ((t0 + r) * H + h) * dk + cc;
-          const float x = IO::load(q, i), y = IO::load(k, i);
-          sq += x * x;
-          sk += y * y;
+        const int64_t base = ((t0 + r) * H + h) * dk;
+        for (int c0 = sub; c0 < dk; c0 += 8 * TPR) {
+          float xs[8], ys[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int cc = c0 + u * TPR;
+            xs[u] = cc < dk ? IO::load(q, base + cc) : 0.f;
+            ys[u] = cc < dk ? IO::load(k, base + cc) : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            sq += xs[u] * xs[u];
+            sk += ys[u] * ys[u];
+          }
         }
       }
-      lrq[r] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sq + kL2Eps)) : 1.f;
-      lrk[r] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sk + kL2Eps)) : 1.f;
-      lbeta[r] = r < L ? beta[(t0 + r) * H + h] : 0.f;
+      for (int o = 1; o < TPR; o <<= 1) {
+        sq += __shfl_xor(sq, o);
+        sk += __shfl_xor(sk, o);
+      }
+      if (sub == 0) {
+        lrq[r] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sq + kL2Eps)) : 1.f;
+        lrk[r] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sk + kL2Eps)) : 1.f;
+        lbeta[r] = r < L ? beta[(t0 + r) * H + h] : 0.f;
+      }
     }
-    __syncthreads();
+    // gate products per channel, 16 loads in flight at a time; regularity
     for (int cc = tid; cc < dk; cc += kNT) {
       float f = 1.f;
       bool ok = true;
-      for (int r = 0; r < C; ++r) {
-        f *= r < L ? alpha[((t0 + r) * H + h) * dk + cc] : 1.f;
-        sF[r * dk + cc] = f;
-        const float m = fabsf(f);
-        ok = ok && m >= kRegMin && m <= kRegMax;
+      for (int r0 = 0; r0 < C; r0 += 16) {
+        float al[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int r = r0 + u;
+          al[u] = r < L ? alpha[((t0 + r) * H + h) * dk + cc] : 1.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          f *= al[u];
+          sF[(r0 + u) * dk + cc] = f;
+          const float m = fabsf(f);
+          ok = ok && m >= kRegMin && m <= kRegMax;
+        }
       }
       lg[cc] = f;
       if (!ok) *lflag = 1;
@@ -339,23 +391,49 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
     const bool irregular = *lflag != 0;
     if (tid == 0) b.bflag[slot] = irregular ? 1 : 0;
     if (irregular) continue;
-    // operands: Kt, Qt, Rk; V, dO as fp32 (rows >= L zero); Y
-    for (int e = tid; e < C * dk; e += kNT) {
-      const int r = e / dk, cc = e % dk;
-      const int64_t i = ((t0 + r) * H + h) * dk + cc;
-      const float qh = r < L ? IO::load(q, i) * lrq[r] : 0.f;
-      const float kh = r < L ? IO::load(k, i) * lrk[r] : 0.f;
-      const float f = sF[e];
-      sKt[e] = kh * f;
-      sQt[e] = qh * f;
-      sRk[e] = kh / f;
+    // operands: Kt, Qt, Rk; V, dO as fp32 (rows >= L zero); Y.  Loads of 8
+    // elements go out before any of them is used.
+    for (int e0 = tid; e0 < C * dk; e0 += 8 * kNT) {
+      float xq[8], xk[8], xf[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kNT, r = e / dk, cc = e % dk;
+        const int64_t i = ((t0 + r) * H + h) * dk + cc;
+        const bool in = e < C * dk && r < L;
+        xq[u] = in ? IO::load(q, i) : 0.f;
+        xk[u] = in ? IO::load(k, i) : 0.f;
+        xf[u] = e < C * dk ? sF[e] : 1.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kNT, r = e / dk;
+        if (e < C * dk) {
+          const float qh = xq[u] * lrq[r], kh = xk[u] * lrk[r];
+          sKt[e] = kh * xf[u];
+          sQt[e] = qh * xf[u];
+          sRk[e] = kh / xf[u];
+        }
+      }
     }
-    for (int e = tid; e < C * dv; e += kNT) {
-      const int r = e / dv, j = e % dv;
-      const int64_t i = ((t0 + r) * H + h) * dv + j;
-      sV[e] = r < L ? IO::load(v, i) : 0.f;
-      sZ[e] = sV[e];
-      sdO[e] = r < L ? IO::load(dO, i) : 0.f;
+    for (int e0 = tid; e0 < C * dv; e0 += 8 * kNT) {
+      float xv[8], xo[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kNT, r = e / dv, j = e % dv;
+        const int64_t i = ((t0 + r) * H + h) * dv + j;
+        const bool in = e < C * dv && r < L;
+        xv[u] = in ? IO::load(v, i) : 0.f;
+        xo[u] = in ? IO::load(dO, i) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * kNT;
+        if (e < C * dv) {
+          sV[e] = xv[u];
+          sZ[e] = xv[u];
+          sdO[e] = xo[u];
+        }
+      }
     }
     for (int e = tid; e < C * C; e += kNT) lY[e] = X[e] * lbeta[e % C];
     __syncthreads();
@@ -370,6 +448,7 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
     // dbeta_j = sum_r X_rj dY_rj;  dX = dY Diag(beta), masked
     for (int j = tid; j < C; j += kNT) {
       float s = 0.f;
+#pragma unroll 8
       for (int r = j; r < C; ++r) s += X[r * C + j] * ldX[r * C + j];
       ldb[j] = s;
     }
@@ -404,49 +483,137 @@ __global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
     gemm(C, dk, dv, 1.f, false, sU, dv, 1, dS1, 1, dv, sZ, dk, 1, stage);  // dKh -> Z's slice
     gemm(C, dk, C, 1.f, false, ldA, 1, C, sKt, dk, 1, sdR, dk, 1, stage);
     gemm(C, dk, C, 1.f, true, sdP, 1, C, sQt, dk, 1, sdR, dk, 1, stage);
-    // dg = rowsum(dS1 * S0) + sum_r dKh_r Rk_r
-    for (int cc = tid; cc < dk; cc += kNT) {
-      float s = 0.f;
-      for (int j = 0; j < dv; ++j) s += dS1[cc * dv + j] * S0[cc * dv + j];
-      for (int r = 0; r < C; ++r) s += sZ[r * dk + cc] * sRk[r * dk + cc];
-      ldg[cc] = s;
+    // dg = rowsum(dS1 * S0) + sum_r dKh_r Rk_r (TPC threads per channel)
+    {
+      const int TPC = kNT / dk >= 1 ? kNT / dk : 1, cc = tid / TPC, sub = tid % TPC;
+      float sacc = 0.f;
+      if (cc < dk) {
+        for (int j0 = sub; j0 < dv; j0 += 8 * TPC) {
+          float x[8], y[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u * TPC;
+            x[u] = j < dv ? dS1[cc * dv + j] : 0.f;
+            y[u] = j < dv ? S0[cc * dv + j] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sacc += x[u] * y[u];
+        }
+        for (int r0 = sub; r0 < C; r0 += 8 * TPC) {
+          float x[8], y[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int r = r0 + u * TPC;
+            x[u] = r < C ? sZ[r * dk + cc] : 0.f;
+            y[u] = r < C ? sRk[r * dk + cc] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sacc += x[u] * y[u];
+        }
+      }
+      for (int o = 1; o < TPC; o <<= 1) sacc += __shfl_xor(sacc, o);
+      if (cc < dk && sub == 0) ldg[cc] = sacc;
     }
     __syncthreads();
     // elementwise: dk^, dq^ in place; Lam into sF's slice (F read first)
-    for (int e = tid; e < C * dk; e += kNT) {
-      const int cc = e % dk;
-      const float f = sF[e];
-      const float dqt = sdQ[e], dkt = sdK[e], drk = sdR[e] + lg[cc] * sZ[e];
-      sdK[e] = dkt * f + drk / f;
-      sdQ[e] = dqt * f;
-      sF[e] = dkt * sKt[e] + dqt * sQt[e] - drk * sRk[e];
+    for (int e0 = tid; e0 < C * dk; e0 += 4 * kNT) {
+      float f[4], dqt[4], dkt[4], drk[4], kt[4], qt[4], rk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kNT;
+        const bool in = e < C * dk;
+        f[u] = in ? sF[e] : 1.f;
+        dqt[u] = in ? sdQ[e] : 0.f;
+        dkt[u] = in ? sdK[e] : 0.f;
+        drk[u] = in ? sdR[e] + lg[e % dk] * sZ[e] : 0.f;
+        kt[u] = in ? sKt[e] : 0.f;
+        qt[u] = in ? sQt[e] : 0.f;
+        rk[u] = in ? sRk[e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kNT;
+        if (e < C * dk) {
+          sdK[e] = dkt[u] * f[u] + drk[u] / f[u];
+          sdQ[e] = dqt[u] * f[u];
+          sF[e] = dkt[u] * kt[u] + dqt[u] * qt[u] - drk[u] * rk[u];
+        }
+      }
     }
     __syncthreads();
     // dalpha per channel: reverse running sums of Lam, divided by alpha
     for (int cc = tid; cc < dk; cc += kNT) {
       float acc = ldg[cc] * lg[cc];
-      for (int r = C - 1; r >= 0; --r) {
-        acc += sF[r * dk + cc];
-        if (r < L) {
-          const int64_t i = ((t0 + r) * H + h) * dk + cc;
-          b.dalpha[i] = acc / alpha[i];
+      for (int r0 = C - 16; r0 >= 0; r0 -= 16) {
+        float lam[16], al[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int r = r0 + u;
+          lam[u] = sF[r * dk + cc];
+          al[u] = r < L ? alpha[((t0 + r) * H + h) * dk + cc] : 1.f;
+        }
+#pragma unroll
+        for (int u = 15; u >= 0; --u) {
+          const int r = r0 + u;
+          acc += lam[u];
+          if (r < L) b.dalpha[((t0 + r) * H + h) * dk + cc] = acc / al[u];
         }
       }
     }
-    // dq, dk through the norms; dbeta
-    for (int r = tid; r < L; r += kNT) {
-      float pq = 0.f, pk = 0.f;
+    // dq, dk through the norms (TPR threads per row); dbeta
+    {
+      const int TPR = kNT / C, r = tid / TPR, sub = tid % TPR;
       const int64_t base = ((t0 + r) * H + h) * dk;
-      for (int cc = 0; cc < dk; ++cc) {
-        pq += IO::load(q, base + cc) * lrq[r] * sdQ[r * dk + cc];
-        pk += IO::load(k, base + cc) * lrk[r] * sdK[r * dk + cc];
+      float pq = 0.f, pk = 0.f;
+      if (r < L) {
+        for (int c0 = sub; c0 < dk; c0 += 8 * TPR) {
+          float xq[8], xk[8], gq[8], gk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int cc = c0 + u * TPR;
+            const bool in = cc < dk;
+            xq[u] = in ? IO::load(q, base + cc) : 0.f;
+            xk[u] = in ? IO::load(k, base + cc) : 0.f;
+            gq[u] = in ? sdQ[r * dk + cc] : 0.f;
+            gk[u] = in ? sdK[r * dk + cc] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            pq += xq[u] * gq[u];
+            pk += xk[u] * gk[u];
+          }
+        }
       }
-      for (int cc = 0; cc < dk; ++cc) {
-        const float qh = IO::load(q, base + cc) * lrq[r], kh = IO::load(k, base + cc) * lrk[r];
-        b.dq[base + cc] = l2 ? lrq[r] * (sdQ[r * dk + cc] - qh * pq) : sdQ[r * dk + cc];
-        b.dk[base + cc] = l2 ? lrk[r] * (sdK[r * dk + cc] - kh * pk) : sdK[r * dk + cc];
+      for (int o = 1; o < TPR; o <<= 1) {
+        pq += __shfl_xor(pq, o);
+        pk += __shfl_xor(pk, o);
       }
-      b.dbeta[(t0 + r) * H + h] = ldb[r];
+      if (r < L) {
+        pq *= lrq[r];
+        pk *= lrk[r];
+        for (int c0 = sub; c0 < dk; c0 += 8 * TPR) {
+          float xq[8], xk[8], gq[8], gk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int cc = c0 + u * TPR;
+            const bool in = cc < dk;
+            xq[u] = in ? IO::load(q, base + cc) : 0.f;
+            xk[u] = in ? IO::load(k, base + cc) : 0.f;
+            gq[u] = in ? sdQ[r * dk + cc] : 0.f;
+            gk[u] = in ? sdK[r * dk + cc] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int cc = c0 + u * TPR;
+            if (cc < dk) {
+              const float qh = xq[u] * lrq[r], kh = xk[u] * lrk[r];
+              b.dq[base + cc] = l2 ? lrq[r] * (gq[u] - qh * pq) : gq[u];
+              b.dk[base + cc] = l2 ? lrk[r] * (gk[u] - kh * pk) : gk[u];
+            }
+          }
+        }
+        if (sub == 0) b.dbeta[(t0 + r) * H + h] = ldb[r];
+      }
     }
   }
 }
