@@ -165,6 +165,40 @@ def bench_fwd(case, steps, warmup, gate, passes=False, sign_absorb=False):
     return ms, wall_ms, per
 
 
+def bench_bwd(case, steps, warmup):
+    """ckda_chunk_bwd on the case (random dL/do and dL/dht), preallocated
+    outputs and workspace; ms per call (the call recomputes the forward)."""
+    import torch
+    import gated_delta_rule_ckda_amd as ck
+    dt = case.dtype
+    q, k, v = to_dev(case.q, dt), to_dev(case.k, dt), to_dev(case.v, dt)
+    a, b = to_dev(case.alpha, "f32"), to_dev(case.beta, "f32")
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    dout = torch.randn(v.shape, device="cuda:0", generator=g).to(v.dtype)
+    B, T, H, dk = case.q.shape
+    dht = torch.randn((B, H, dk, case.v.shape[-1]), device="cuda:0", generator=g)
+    desc = ck._make_desc(q, v, H, dk, case.v.shape[-1], case.chunk, "ckda", case.l2norm, 1.0,
+                         None, ck.GATES_F32, False)
+    ws = torch.empty(ck.chunk_bwd_workspace_size(desc, False), device="cuda:0", dtype=torch.uint8)
+
+    def step():
+        ck.chunk_bwd(q, k, v, a, b, dout, dht=dht, chunk_size=case.chunk,
+                     use_qk_l2norm=case.l2norm, workspace=ws)
+
+    ms, _ = time_launches(step, steps, warmup)
+    del q, k, v, a, b, dout, dht, ws
+    torch.cuda.empty_cache()
+    return ms
+
+
+def bwd_bytes(B, T, H, dk, dv, es):
+    """Algorithmic bytes of the backward: q, k, v, dout read in the io type,
+    alpha, beta read as fp32 (once); dq, dk, dv, dalpha, dbeta written as
+    fp32 (once)."""
+    tok = B * T * H
+    return tok * (es * (2 * dk + 2 * dv) + 4 * dk + 4) + tok * 4 * (3 * dk + dv + 1)
+
+
 def bench_decode(steps_inner=64, reps=3):
     """The decode workload: 64 consecutive in-place steps (fresh inputs per
     step, resident in HBM), timed as a whole and divided by 64."""
@@ -327,6 +361,14 @@ def main():
                         "with the gates' cumulative signs folded into q and k (comparison path)",
             "tokens_per_s": round(tokens / (ms_sa / 1000.0), 1), "ms_per_step": round(ms_sa, 4),
             "native_over_absorbed": round(ms_sa / ms, 4)}
+        ms_bw = bench_bwd(case, max(5, args.steps // 3), 2)
+        bb = bwd_bytes(B, T, H, dk, dv, 2)
+        out["backward"] = {
+            "workload": "gradients of the headline forward (dq, dk, dv, dalpha, dbeta from "
+                        "random dL/do and dL/dht; the call recomputes the forward)",
+            "ms_per_call": round(ms_bw, 3), "tokens_per_s": round(tokens / (ms_bw / 1000.0), 1),
+            "over_forward": round(ms_bw / ms, 2), "algorithmic_bytes": bb,
+            "hbm_frac": round(bb / (ms_bw / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
         vl = inputs.varlen()
         ms_vl, _, _ = bench_fwd(vl, max(5, args.steps // 3), 2, "ckda")
         vl_tok = int(vl.cu_seqlens[-1])

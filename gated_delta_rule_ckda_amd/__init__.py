@@ -11,7 +11,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["chunk_fwd", "recurrent_step", "l2norm_debug", "fwd_supported",
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_workspace_size", "recurrent_step",
+           "l2norm_debug", "fwd_supported",
            "library_path", "abi_version", "CkdaError", "BF16", "F32", "GATE_KDA",
            "GATE_CKDA", "GATES_F32", "GATES_LOGITS_F32", "GATES_LOGITS_BF16", "ChunkFwdPlan"]
 
