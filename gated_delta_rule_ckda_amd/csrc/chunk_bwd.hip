@@ -45,6 +45,9 @@ namespace {
 
 constexpr float kRegMin = 0x1p-100f, kRegMax = 0x1p+10f;
 constexpr int kNT = 256;
+// workgroups of the intra-chunk kernel: two per CU, all resident at once, so
+// that the scratch they cycle through stays in the last-level caches
+constexpr int64_t kGrid3 = 512;
 
 // tokens of chunk slot c: sequence n, first token t0, length L (n < 0: unused)
 struct Geo {
@@ -812,7 +815,7 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
 
 }  // namespace
 
-int32_t bwd_grid3(int64_t total) { return static_cast<int32_t>(total < 1024 ? (total > 0 ? total : 1) : 1024); }
+int32_t bwd_grid3(int64_t total) { return static_cast<int32_t>(total < kGrid3 ? (total > 0 ? total : 1) : kGrid3); }
 
 int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv) {
   auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };

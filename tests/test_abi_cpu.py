@@ -281,7 +281,7 @@ def test_bwd_workspace_covers_forward_and_records():
     bwd = lib.ckda_chunk_bwd_workspace_size(ctypes.byref(d), 0)
     hm = 3 * 2 * 5  # heads x (B * ceil(130 / 32)) chunk slots
     up = lambda x: (x + 255) // 256 * 256
-    grid = min(hm, 1024)
+    grid = min(hm, 512)
     extra = (up(4 * hm * 32 * 32) + 2 * up(4 * hm * 64 * 64) + up(4 * hm * 32 * 64) + up(4 * hm)
              + up(4 * grid * 14 * 32 * 64))
     assert bwd == fwd + extra
