@@ -97,89 +97,107 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // out(m, n) = alpha * sum_k A(m, k) B(k, n) (+ out(m, n) when acc), fp32, for
-// M <= 64, N <= 128, by the kNT threads of the workgroup: thread (tx, ty) of
-// a 16 x 16 grid owns rows ty + 16 i and columns tx + 16 j.  la(m, k) and
+// M <= 64, N <= 128, by the kNT threads of the workgroup on the fp32 matrix
+// cores (16x16x4 MFMA): wave w owns the 32 x 64 quarter of rows 32 (w & 1)
+// and columns 64 (w >> 1), as 2 x 4 tiles of 16 x 16.  la(m, k) and
 // lb(k, n) load the operands (any storage); out(m, n) = O[m om + n on] (any
 // address space).  K is walked in slices of 16 staged in LDS (`stage`,
 // kGStage floats); a_mfast / b_nfast say which index of the operand is the
 // contiguous one, so that consecutive threads stage consecutive elements.
 // Ends with a barrier.
-constexpr int kGM = 4, kGN = 8, kGStage = 16 * (16 * kGM + 1) + 16 * (16 * kGN + 1);
-template <bool PREFETCH = true, class LA, class LB>
+constexpr int kGM = 4, kGN = 8;
+// staging floats for K slices of ks
+constexpr int gstage(int ks) { return ks * (16 * kGM + 1) + ks * (16 * kGN + 1); }
+constexpr int kGStage = gstage(16);
+template <bool PREFETCH = true, int KS = 16, class LA, class LB>
 __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc, LA la,
                                      bool a_mfast, LB lb, bool b_nfast, float* O, int om, int on,
                                      float* stage) {
   constexpr int MP = 16 * kGM, NP = 16 * kGN;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float* sA = stage;                   // [16][MP + 1]
-  float* sB = stage + 16 * (MP + 1);   // [16][NP + 1]
-  float c[kGM][kGN];
+  // threadIdx.x through an opaque move, so that each product forms its
+  // lane-dependent addresses here instead of having them hoisted out of the
+  // kernel's loops for every product at once (which only costs spills)
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(static_cast<int>(threadIdx.x)));
+  const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int m0 = 32 * (w & 1), n0 = 64 * (w >> 1);
+  float* sA = stage;                   // [KS][MP + 1]
+  float* sB = stage + KS * (MP + 1);   // [KS][NP + 1]
+  f32x4 c[2][4];
 #pragma unroll
-  for (int i = 0; i < kGM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < kGN; ++j) c[i][j] = 0.f;
+    for (int j = 0; j < 4; ++j) c[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // this thread's staging elements of one K slice, loaded one slice ahead
-  constexpr int NA = 16 * MP / kNT, NB2 = 16 * NP / kNT;
+  constexpr int NA = KS * MP / kNT, NB2 = KS * NP / kNT;
   float ra[NA], rb[NB2];
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
       const int e = tid + u * kNT;
       int kk, m;
-      if (a_mfast) { m = e % MP; kk = e / MP; } else { kk = e % 16; m = e / 16; }
+      if (a_mfast) { m = e % MP; kk = e / MP; } else { kk = e % KS; m = e / KS; }
       ra[u] = (m < M && k0 + kk < K) ? la(m, k0 + kk) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < NB2; ++u) {
       const int e = tid + u * kNT;
       int kk, n;
-      if (b_nfast) { n = e % NP; kk = e / NP; } else { kk = e % 16; n = e / 16; }
+      if (b_nfast) { n = e % NP; kk = e / NP; } else { kk = e % KS; n = e / KS; }
       rb[u] = (n < N && k0 + kk < K) ? lb(k0 + kk, n) : 0.f;
     }
   };
+  // tiles wholly outside M x N are skipped (the same for the whole wave)
+  const bool live_m1 = m0 + 16 < M, live_n = n0 < N;
   if (PREFETCH) fetch(0);
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  for (int k0 = 0; k0 < K; k0 += KS) {
     if (!PREFETCH) fetch(k0);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
       const int e = tid + u * kNT;
       int kk, m;
-      if (a_mfast) { m = e % MP; kk = e / MP; } else { kk = e % 16; m = e / 16; }
+      if (a_mfast) { m = e % MP; kk = e / MP; } else { kk = e % KS; m = e / KS; }
       sA[kk * (MP + 1) + m] = ra[u];
     }
 #pragma unroll
     for (int u = 0; u < NB2; ++u) {
       const int e = tid + u * kNT;
       int kk, n;
-      if (b_nfast) { n = e % NP; kk = e / NP; } else { kk = e % 16; n = e / 16; }
+      if (b_nfast) { n = e % NP; kk = e / NP; } else { kk = e % KS; n = e / KS; }
       sB[kk * (NP + 1) + n] = rb[u];
     }
     __syncthreads();
-    if (PREFETCH && k0 + 16 < K) fetch(k0 + 16);  // in flight while this slice is multiplied
-#pragma unroll 4
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[kGM], bv[kGN];
+    if (PREFETCH && k0 + KS < K) fetch(k0 + KS);  // in flight while this slice is multiplied
+    if (live_n) {
 #pragma unroll
-      for (int i = 0; i < kGM; ++i) av[i] = sA[kk * (MP + 1) + ty + 16 * i];
+      for (int k4 = 0; k4 < KS; k4 += 4) {
+        const int kr = k4 + lq;
+        float av[2], bv[4];
 #pragma unroll
-      for (int j = 0; j < kGN; ++j) bv[j] = sB[kk * (NP + 1) + tx + 16 * j];
+        for (int i = 0; i < 2; ++i) av[i] = sA[kr * (MP + 1) + m0 + 16 * i + l16];
 #pragma unroll
-      for (int i = 0; i < kGM; ++i)
+        for (int j = 0; j < 4; ++j) bv[j] = sB[kr * (NP + 1) + n0 + 16 * j + l16];
 #pragma unroll
-        for (int j = 0; j < kGN; ++j) c[i][j] += av[i] * bv[j];
+        for (int j = 0; j < 4; ++j) {
+          c[0][j] = mfma_f32(av[0], bv[j], c[0][j]);
+          if (live_m1) c[1][j] = mfma_f32(av[1], bv[j], c[1][j]);
+        }
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < kGM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < kGN; ++j) {
-      const int m = ty + 16 * i, n = tx + 16 * j;
-      if (m < M && n < N) {
-        float* o = O + m * om + n * on;
-        *o = acc ? *o + alpha * c[i][j] : alpha * c[i][j];
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * lq + r, n = n0 + 16 * j + l16;
+        if (m < M && n < N) {
+          float* o = O + m * om + n * on;
+          *o = acc ? *o + alpha * c[i][j][r] : alpha * c[i][j][r];
+        }
       }
-    }
   __syncthreads();
 }
 // the same with both operands strided fp32 arrays: A(m, k) = A[m am + k ak],
@@ -188,7 +206,7 @@ __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc,
 __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc, const float* A,
                                      int am, int ak, const float* B, int bk, int bn, float* O,
                                      int om, int on, float* stage) {
-  gemm<false>(M, N, K, alpha, acc, [=](int m, int k) { return A[m * am + k * ak]; }, am == 1,
+  gemm<true>(M, N, K, alpha, acc, [=](int m, int k) { return A[m * am + k * ak]; }, am == 1,
        [=](int k, int n) { return B[k * bk + n * bn]; }, bn == 1, O, om, on, stage);
 }
 
@@ -196,7 +214,7 @@ __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc,
 // One workgroup per (sequence, head, tile of DVB value columns); the columns
 // of the state adjoint are independent, so no tile needs another's.
 template <class IO>
-__global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
+__global__ __launch_bounds__(kNT, 2) void bwd_state_kernel(BwdArgs b) {
   using ST = typename IO::storage;
   const FwdArgs& a = b.f;
   const int C = a.chunk, dk = a.dk, dv = a.dv, H = a.H;
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
   float* sdS = sdO + C * DVB;    // [dk][DVB] adjoint at the chunk's exit
   float* sdU = sdS + dk * DVB;   // [C][DVB]
   float* sdS0 = sdU + C * DVB;   // [max(dk, C)][DVB]: dS0, and dV before it
-  float* stage = sdS0 + cmax(dk, C) * DVB;
+  float* stage = sdS0 + cmax(dk, C) * DVB;  // gstage(32) floats
   const int tid = threadIdx.x;
   const int64_t st = (static_cast<int64_t>(n) * H + h) * dk * dv + dv0;
   for (int e = tid; e < dk * DVB; e += kNT)
@@ -253,14 +271,14 @@ __global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
     auto ld_dO = [=](int k, int n) { return sdO[k * DVB + n]; };
     auto ld_dS = [=](int k, int n) { return sdS[k * DVB + n]; };
     // dU = P'^T dO + Kh' dS1   (P' = scale P, lower; Kh' = Kh)
-    gemm(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bP, k, m, C); }, true, ld_dO,
+    gemm<true, 32>(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bP, k, m, C); }, true, ld_dO,
          true, sdU, DVB, 1, stage);
-    gemm(C, DVB, dk, 1.f, true, [=](int m, int k) { return blk_at<IO>(bK, k, m, C); }, true, ld_dS,
+    gemm<true, 32>(C, DVB, dk, 1.f, true, [=](int m, int k) { return blk_at<IO>(bK, k, m, C); }, true, ld_dS,
          true, sdU, DVB, 1, stage);
     for (int e = tid; e < C * DVB; e += kNT)
       b.dU[(slot * C + e / DVB) * dv + dv0 + e % DVB] = sdU[e];
     // dV = X'^T dU   (X' = Y); rows >= L are not outputs (O into sdS0 first)
-    gemm(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bX, k, m, C); }, true,
+    gemm<true, 32>(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bX, k, m, C); }, true,
          [=](int k, int n) { return sdU[k * DVB + n]; }, true, sdS0, DVB, 1, stage);
     for (int e = tid; e < C * DVB; e += kNT) {
       const int r = e / DVB, j = e % DVB;
@@ -270,9 +288,9 @@ __global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
     // dS0^T = dO^T Qt' + dU^T W' + dS1^T Diag(g)   (W' = -W as stored)
     for (int e = tid; e < dk * DVB; e += kNT) sdS0[e] = bg[e / DVB] * sdS[e];
     __syncthreads();
-    gemm(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdO[k * DVB + m]; }, true,
+    gemm<true, 32>(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdO[k * DVB + m]; }, true,
          [=](int k, int n) { return blk_at<IO>(bQ, k, n, dk); }, true, sdS0, 1, DVB, stage);
-    gemm(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdU[k * DVB + m]; }, true,
+    gemm<true, 32>(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdU[k * DVB + m]; }, true,
          [=](int k, int n) { return blk_at<IO>(bW, k, n, dk); }, true, sdS0, 1, DVB, stage);
     for (int e = tid; e < dk * DVB; e += kNT) sdS[e] = sdS0[e];
   }
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(kNT) void bwd_state_kernel(BwdArgs b) {
 // products run through gemm(); C x C matrices in LDS where they fit, the rest
 // in the workgroup's slice of the scratch.
 template <class IO>
-__global__ __launch_bounds__(kNT) void bwd_intra_kernel(BwdArgs b) {
+__global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
   using ST = typename IO::storage;
   const FwdArgs& a = b.f;
   const int C = a.chunk, dk = a.dk, dv = a.dv, H = a.H;
@@ -786,7 +804,7 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
   const int C = a.chunk, dk = a.dk, dv = a.dv;
   const int DVB = dv < 32 ? dv : 32;
   const int64_t g2 = static_cast<int64_t>(a.num_seqs) * a.H * (dv / DVB);
-  const size_t lds2 = sizeof(float) * (2 * C * DVB + dk * DVB + cmax(dk, C) * DVB + kGStage);
+  const size_t lds2 = sizeof(float) * (2 * C * DVB + dk * DVB + cmax(dk, C) * DVB + gstage(32));
   static const hipError_t attr2 = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&bwd_state_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
   if (attr2 != hipSuccess) return attr2;
