@@ -211,92 +211,399 @@ __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc,
 }
 
 // ---------------------------------------------------------------- 2: state
-// One workgroup per (sequence, head, tile of DVB value columns); the columns
-// of the state adjoint are independent, so no tile needs another's.
-template <class IO>
-__global__ __launch_bounds__(kNT, 2) void bwd_state_kernel(BwdArgs b) {
-  using ST = typename IO::storage;
+// The state adjoint on the matrix cores: one workgroup per (sequence, head,
+// dv tile), over the sequence's chunks in reverse.  Per chunk, with dS1 the
+// adjoint at the chunk's end and the block's operands as the transform pass
+// stored them (P' = scale P, X' = Y, W' = -W, Qt' = scale Qt, Kh' = Kh):
+//   dU  = P'^T dO + Kh' dS1
+//   dV  = X'^T dU
+//   dS0 = Diag(g) dS1 + W'^T dU + Qt'^T dO
+// The step has the forward state pass's shape with every block operand
+// transposed, and the same division of labour: state waves own 16 columns of
+// the tile each (the adjoint in fp32 accumulators, dU in registers), loader
+// waves stream the blocks and the dO rows two chunks ahead.  The loaders
+// write the transposes into LDS: a unit is one 16-byte piece of two adjacent
+// source rows, so that each LDS write is a pair of adjacent elements of a
+// transposed row, in the order the state waves read as fragments.
+struct TSec {
+  int g0, R, Kc, l0, ldd;  // R source rows of Kc elements at block byte g0 -> LDS [Kc][ldd] at byte l0
+};
+
+template <class OpT, class IOT, int C_, int DK_, int DV_, int DVT_>
+struct BCfg {
+  using Op = OpT;
+  using IO = IOT;
+  using T = typename Op::T;
+  using Frag = typename Op::Frag;
+  static constexpr int C = C_, DK = DK_, DV = DV_, DVT = DVT_;
+  static constexpr int NSPLIT = DV / DVT;
+  static constexpr int NSW = DVT / 16, NLW = 8;
+  static constexpr int NT = 64 * (NSW + NLW), NLT = 64 * NLW;
+  static constexpr int NB = C / 16, NMC = DK / 16;
+  static constexpr int ES = static_cast<int>(sizeof(T));
+  static constexpr int IOES = static_cast<int>(sizeof(typename IO::storage));
+  static constexpr int LDK = frag_stride(DK, ES), LDC = frag_stride(C, ES);
+  static constexpr int KS = Op::KS;
+  static constexpr int NFK = (DK + KS - 1) / KS, NFC = (C + KS - 1) / KS;
+  // P'^T and X'^T are upper triangular: K fragment s of row block rb holds a
+  // nonzero only if its last column is at or right of the block's first row
+  static constexpr bool up_live(int rb, int s) { return KS * s + KS - 1 >= 16 * rb; }
+  // the block (bytes)
+  static constexpr int GB_X = 0, GB_W = C * C * ES, GB_Q = GB_W + C * DK * ES,
+                       GB_P = GB_Q + C * DK * ES, GB_K = GB_P + C * C * ES,
+                       GB_G = GB_K + DK * C * ES, GB_END = GB_G + DK * 4;
+  // LDS (bytes)
+  static constexpr int O_PT = 0;                                  // P'^T  [C][LDC]
+  static constexpr int O_KH = align16(O_PT + C * LDC * ES);       // Kh'   [C][LDK]
+  static constexpr int O_OT = align16(O_KH + C * LDK * ES);       // dO^T  [DVT][LDC]
+  static constexpr int O_YT = align16(O_OT + DVT * LDC * ES);     // X'^T  [C][LDC]
+  static constexpr int O_WT = align16(O_YT + C * LDC * ES);       // W'^T  [DK][LDC]
+  static constexpr int O_QT = align16(O_WT + DK * LDC * ES);      // Qt'^T [DK][LDC]
+  static constexpr int O_G = align16(O_QT + DK * LDC * ES);       // g [DK] fp32
+  static constexpr int LDS_BYTES = align16(O_G + DK * 4);
+  static_assert(GB_G == blk_g_byte(C, DK, ES), "block layout");
+  static_assert(DV % DVT == 0 && DVT % 16 == 0 && NSW >= 1 && NSW <= 4, "dv tiling");
+  static_assert((C * ES) % 16 == 0 && (DK * ES) % 16 == 0 && (DVT * IOES) % 16 == 0, "rows in pieces");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// logical index of storage position p in a perm32-ordered row (inverse of perm32)
+__host__ __device__ constexpr int unperm32(int p) {
+  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p & 31) >> 3) << 2) | (p & 3);
+}
+
+// One loader thread's share of one chunk's group: A = {P'^T, Kh', dO^T} (what
+// dU needs), B = {X'^T, W'^T, Qt'^T, g}.  Loads are issued for clamped
+// indices whatever the thread's share, so every group has the same number of
+// loads; duplicates are dropped at the store.
+template <class Cfg, bool A>
+struct BGroup {
+  static constexpr int C = Cfg::C, DK = Cfg::DK, ES = Cfg::ES, NLT = Cfg::NLT;
+  static constexpr int NS = A ? 2 : 3;
+  static constexpr TSec sec(int k) {
+    return A ? (k == 0 ? TSec{Cfg::GB_P, C, C, Cfg::O_PT, Cfg::LDC}
+                       : TSec{Cfg::GB_K, DK, C, Cfg::O_KH, Cfg::LDK})
+             : (k == 0   ? TSec{Cfg::GB_X, C, C, Cfg::O_YT, Cfg::LDC}
+                : k == 1 ? TSec{Cfg::GB_W, C, DK, Cfg::O_WT, Cfg::LDC}
+                         : TSec{Cfg::GB_Q, C, DK, Cfg::O_QT, Cfg::LDC});
+  }
+  static constexpr int units(int k) { return sec(k).R / 2 * (sec(k).Kc * ES / 16); }
+  static constexpr int per(int k) { return (units(k) + NLT - 1) / NLT; }
+  static constexpr int first(int k) { return k == 0 ? 0 : first(k - 1) + per(k - 1); }
+  static constexpr int NU = first(NS);
+  static constexpr int NVU = A ? (C / 2) * (Cfg::DVT * Cfg::IOES / 16) : 0;  // dO units
+  static constexpr int NV = (NVU + NLT - 1) / NLT;
+  static constexpr int NGP = DK * 4 / 16;                                 // g pieces
+  static constexpr int NG = A ? 0 : (NGP + NLT - 1) / NLT;
+  uint32_t d[2 * NU + 2 * NV + NG][4];
+
+  __device__ __forceinline__ void issue(const unsigned char* blk, const void* dout, int64_t t0, int L,
+                                        int H, int h, int dv0, int lt) {
+    using ST = typename Cfg::IO::storage;
+    const rsrc_t rb = make_rsrc(blk, Cfg::GB_END);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+#pragma unroll
+      for (int u = 0; u < per(k); ++u) {
+        const TSec s = sec(k);
+        const int uu = iclamp(lt + NLT * u, units(k) - 1);
+        const int jp = uu % (s.R / 2), cp = uu / (s.R / 2);
+        const int off = s.g0 + 2 * jp * s.Kc * ES + 16 * cp;
+        ldraw<16>(rb, off, d[2 * (first(k) + u)]);
+        ldraw<16>(rb, off + s.Kc * ES, d[2 * (first(k) + u) + 1]);
+      }
+    }
+    if constexpr (A) {
+      const int vrow = H * Cfg::DV * Cfg::IOES;
+      const rsrc_t rv = make_rsrc(
+          static_cast<const ST*>(dout) + (t0 * H + h) * static_cast<int64_t>(Cfg::DV) + dv0, L * vrow);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int uv = iclamp(lt + NLT * u, NVU - 1);
+        const int jp = uv % (C / 2), cp = uv / (C / 2);
+        ldraw<16>(rv, iclamp(2 * jp, L - 1) * vrow + 16 * cp, d[2 * NU + 2 * u]);
+        ldraw<16>(rv, iclamp(2 * jp + 1, L - 1) * vrow + 16 * cp, d[2 * NU + 2 * u + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NG; ++u)
+        ldraw<16>(rb, Cfg::GB_G + 16 * iclamp(lt + NLT * u, NGP - 1), d[2 * NU + u]);
+    }
+  }
+
+  __device__ __forceinline__ void store(unsigned char* smem, int L, int lt) const {
+    using Op = typename Cfg::Op;
+    using T = typename Cfg::T;
+    constexpr int NE = 16 / ES;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+#pragma unroll
+      for (int u = 0; u < per(k); ++u) {
+        const TSec s = sec(k);
+        const int uu = lt + NLT * u;
+        if (units(k) % NLT == 0 || uu < units(k)) {
+          const int jp = uu % (s.R / 2), cp = uu / (s.R / 2);
+          const bool sp = ES == 2 && s.Kc % 32 == 0, dp = ES == 2 && s.R % 32 == 0;
+          const int q = dp ? perm32(2 * jp) : 2 * jp;
+          T* dst = reinterpret_cast<T*>(smem + s.l0);
+          const uint32_t* r0 = d[2 * (first(k) + u)];
+          const uint32_t* r1 = d[2 * (first(k) + u) + 1];
+#pragma unroll
+          for (int e = 0; e < NE; ++e) {
+            const int p = NE * cp + e, c = sp ? unperm32(p) : p;
+            Op::store2(dst + c * s.ldd + q, dec<typename Cfg::IO>(r0, e), dec<typename Cfg::IO>(r1, e));
+          }
+        }
+      }
+    }
+    if constexpr (A) {
+      constexpr int NEV = 16 / Cfg::IOES;
+      T* ot = reinterpret_cast<T*>(smem + Cfg::O_OT);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int uv = lt + NLT * u;
+        if (NVU % NLT == 0 || uv < NVU) {
+          const int jp = uv % (C / 2), c0 = (uv / (C / 2)) * NEV;
+          const bool in0 = 2 * jp < L, in1 = 2 * jp + 1 < L;
+          const int q = Op::template pos<C>(2 * jp);
+#pragma unroll
+          for (int e = 0; e < NEV; ++e) {
+            const float x0 = in0 ? dec<typename Cfg::IO>(d[2 * NU + 2 * u], e) : 0.f;
+            const float x1 = in1 ? dec<typename Cfg::IO>(d[2 * NU + 2 * u + 1], e) : 0.f;
+            Op::store2(ot + (c0 + e) * Cfg::LDC + q, x0, x1);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int p = lt + NLT * u;
+        if (p < NGP) {
+          const uint32_t* r = d[2 * NU + u];
+          *reinterpret_cast<uint4*>(smem + Cfg::O_G + 16 * p) = make_uint4(r[0], r[1], r[2], r[3]);
+        }
+      }
+    }
+  }
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
+  using Op = typename Cfg::Op;
+  using T = typename Cfg::T;
+  using Frag = typename Cfg::Frag;
+  constexpr int C = Cfg::C, DK = Cfg::DK, NB = Cfg::NB, NMC = Cfg::NMC;
+  constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, NFC = Cfg::NFC, NFK = Cfg::NFK;
   const FwdArgs& a = b.f;
-  const int C = a.chunk, dk = a.dk, dv = a.dv, H = a.H;
-  const int DVB = dv < 32 ? dv : 32, ntile = dv / DVB;
-  const int64_t wg = blockIdx.x;
-  const int tile = static_cast<int>(wg % ntile);
-  const int64_t pair = wg / ntile;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const T* sPT = reinterpret_cast<const T*>(smem + Cfg::O_PT);
+  const T* sKH = reinterpret_cast<const T*>(smem + Cfg::O_KH);
+  const T* sOT = reinterpret_cast<const T*>(smem + Cfg::O_OT);
+  const T* sYT = reinterpret_cast<const T*>(smem + Cfg::O_YT);
+  const T* sWT = reinterpret_cast<const T*>(smem + Cfg::O_WT);
+  const T* sQT = reinterpret_cast<const T*>(smem + Cfg::O_QT);
+  const float* sg = reinterpret_cast<const float*>(smem + Cfg::O_G);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const bool is_state = wave < Cfg::NSW;
+  const int lt = tid - 64 * Cfg::NSW;
+
+  // the dv tiles of one (sequence, head) 8 workgroups apart: same XCD, so
+  // they share its L2 for the blocks
+  const int64_t nblk = gridDim.x, bi = blockIdx.x;
+  int64_t pair;
+  int split;
+  if (Cfg::NSPLIT > 1 && nblk % (8 * Cfg::NSPLIT) == 0) {
+    const int64_t xcd = bi % 8, slot = bi / 8;
+    pair = (slot / Cfg::NSPLIT) * 8 + xcd;
+    split = static_cast<int>(slot % Cfg::NSPLIT);
+  } else {
+    pair = bi / Cfg::NSPLIT;
+    split = static_cast<int>(bi % Cfg::NSPLIT);
+  }
+  const int H = a.H, dv = a.dv;
   const int n = static_cast<int>(pair / H), h = static_cast<int>(pair % H);
-  const int dv0 = tile * DVB;
-  int64_t s0, s1;
+  int64_t s0;
   int c_begin, nch;
   if (a.cu_seqlens) {
-    s0 = a.cu_seqlens[n];
-    s1 = a.cu_seqlens[n + 1];
-    c_begin = a.first[n];
-    nch = a.first[n + 1] - c_begin;
+    s0 = uniform64(a.cu_seqlens[n]);
+    c_begin = uniform32(a.first[n]);
+    nch = uniform32(a.first[n + 1]) - c_begin;
   } else {
     s0 = static_cast<int64_t>(n) * a.T;
-    s1 = s0 + a.T;
     c_begin = n * a.nc;
     nch = a.nc;
   }
-  extern __shared__ float sm[];
-  float* sdO = sm;               // [C][DVB]
-  float* sdS = sdO + C * DVB;    // [dk][DVB] adjoint at the chunk's exit
-  float* sdU = sdS + dk * DVB;   // [C][DVB]
-  float* sdS0 = sdU + C * DVB;   // [max(dk, C)][DVB]: dS0, and dV before it
-  float* stage = sdS0 + cmax(dk, C) * DVB;  // gstage(32) floats
-  const int tid = threadIdx.x;
-  const int64_t st = (static_cast<int64_t>(n) * H + h) * dk * dv + dv0;
-  for (int e = tid; e < dk * DVB; e += kNT)
-    sdS[e] = b.dht ? b.dht[st + static_cast<int64_t>(e / DVB) * dv + e % DVB] : 0.f;
-  const int es = static_cast<int>(sizeof(ST));
-  for (int i = nch - 1; i >= 0; --i) {
-    const int c = c_begin + i;
-    const int64_t t0 = s0 + static_cast<int64_t>(i) * C;
-    const int L = static_cast<int>((s1 - t0) < C ? (s1 - t0) : C);
-    const int64_t slot = static_cast<int64_t>(h) * a.maxc + c;
-    const unsigned char* blk = a.blocks + slot * a.blk_bytes;
-    const ST* bX = reinterpret_cast<const ST*>(blk);
-    const ST* bW = bX + C * C;
-    const ST* bQ = bW + C * dk;
-    const ST* bP = bQ + C * dk;
-    const ST* bK = bP + C * C;
-    const float* bg = reinterpret_cast<const float*>(blk + blk_g_byte(C, dk, es));
-    __syncthreads();
-    for (int e = tid; e < C * DVB; e += kNT) {
-      const int r = e / DVB, j = e % DVB;
-      sdO[e] = r < L ? IO::load(static_cast<const ST*>(b.dout), ((t0 + r) * H + h) * dv + dv0 + j) : 0.f;
+  const int64_t s1 = a.cu_seqlens ? uniform64(a.cu_seqlens[n + 1]) : s0 + a.T;
+  const int dv0 = split * Cfg::DVT;
+  const unsigned char* blocks = a.blocks + static_cast<int64_t>(h) * a.maxc * a.blk_bytes;
+  auto chunk_t0 = [&](int i) { return s0 + static_cast<int64_t>(i) * C; };
+  auto chunk_len = [&](int i) {
+    const int64_t rem = s1 - chunk_t0(i);
+    return static_cast<int>(rem < C ? rem : C);
+  };
+
+  // adjoint slab: tile mc holds rows 16mc + 4lq + i, column dv0 + 16 wave + l16
+  f32x4 sacc[NMC];
+  const int col = dv0 + 16 * wave + l16;
+  const int64_t st_base = (static_cast<int64_t>(n) * H + h) * DK * dv + col;
+  if (is_state) {
+#pragma unroll
+    for (int mc = 0; mc < NMC; ++mc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[mc][i] = b.dht ? b.dht[st_base + static_cast<int64_t>(16 * mc + 4 * lq + i) * dv] : 0.f;
+
+    for (int k = 0; k < nch; ++k) {
+      const int i = nch - 1 - k;
+      const int64_t slot = static_cast<int64_t>(h) * a.maxc + c_begin + i;
+      // the lane's row and column through an opaque move: the store addresses
+      // below are formed per chunk instead of being hoisted out of the loop
+      // (one 64-bit address per stored value, which only costs spills)
+      int lqo, colo;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(lqo) : "v"(lq));
+      asm volatile("v_mov_b32 %0, %1" : "=v"(colo) : "v"(col));
+      {  // the adjoint at the chunk's end, for the intra-chunk pass
+        float* ds = b.dS + slot * DK * dv + colo + 4 * lqo * dv;
+#pragma unroll
+        for (int mc = 0; mc < NMC; ++mc)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) ds[(16 * mc + ii) * dv] = sacc[mc][ii];
+      }
+      __syncthreads();  // group A of this chunk is in LDS
+      Frag sf[NFK], of[NFC];
+      Op::template frags<DK>(sf, sacc);
+      // dU tiles: P'^T dO + Kh' dS1 (all fragments read first, then the MFMAs)
+      f32x4 uacc[NB];
+      {
+        Frag pf[NB][NFC], kf[NB][NFK];
+        const T* orow = sOT + (16 * wave + l16) * LDC;
+#pragma unroll
+        for (int s = 0; s < NFC; ++s) of[s] = Op::template row_frag<C>(orow, s, lq);
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+          for (int s = 0; s < NFC; ++s)
+            if (Cfg::up_live(rb, s)) pf[rb][s] = Op::template row_frag<C>(sPT + (16 * rb + l16) * LDC, s, lq);
+#pragma unroll
+          for (int s = 0; s < NFK; ++s) kf[rb][s] = Op::template row_frag<DK>(sKH + (16 * rb + l16) * LDK, s, lq);
+        }
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+          uacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NFC; ++s)
+            if (Cfg::up_live(rb, s)) Op::mma(uacc[rb], pf[rb][s], of[s]);
+#pragma unroll
+          for (int s = 0; s < NFK; ++s) Op::mma(uacc[rb], kf[rb][s], sf[s]);
+        }
+      }
+      {
+        float* du = b.dU + slot * C * dv + colo + 4 * lqo * dv;
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) du[(16 * rb + ii) * dv] = uacc[rb][ii];
+      }
+      Frag uf[NFC];
+      Op::template frags<C>(uf, uacc);
+      __syncthreads();  // group B of this chunk is in LDS
+      {  // dV = X'^T dU, rows < L
+        const int L = chunk_len(i);
+        float* dvo = b.dv + (chunk_t0(i) * H + h) * dv + colo;
+        Frag yf[NB][NFC];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+          for (int s = 0; s < NFC; ++s)
+            if (Cfg::up_live(rb, s)) yf[rb][s] = Op::template row_frag<C>(sYT + (16 * rb + l16) * LDC, s, lq);
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NFC; ++s)
+            if (Cfg::up_live(rb, s)) Op::mma(acc, yf[rb][s], uf[s]);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int r = 16 * rb + 4 * lqo + ii;
+            if (r < L) dvo[static_cast<int64_t>(r) * H * dv] = acc[ii];
+          }
+        }
+      }
+      // dS0 = Diag(g) dS1 + W'^T dU + Qt'^T dO, in two halves of the rows
+      constexpr int NH = NMC >= 2 ? 2 : 1, MH = NMC / NH;
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        Frag wf[MH][NFC], qf[MH][NFC];
+        f32x4 gv[MH];
+#pragma unroll
+        for (int m = 0; m < MH; ++m) {
+          const int mc = hf * MH + m;
+          gv[m] = *reinterpret_cast<const f32x4*>(sg + 16 * mc + 4 * lq);
+#pragma unroll
+          for (int s = 0; s < NFC; ++s) {
+            wf[m][s] = Op::template row_frag<C>(sWT + (16 * mc + l16) * LDC, s, lq);
+            qf[m][s] = Op::template row_frag<C>(sQT + (16 * mc + l16) * LDC, s, lq);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MH; ++m) {
+          const int mc = hf * MH + m;
+          sacc[mc] *= gv[m];
+#pragma unroll
+          for (int s = 0; s < NFC; ++s) {
+            Op::mma(sacc[mc], wf[m][s], uf[s]);
+            Op::mma(sacc[mc], qf[m][s], of[s]);
+          }
+        }
+      }
     }
-    for (int e = tid; e < dk * DVB; e += kNT)
-      b.dS[(slot * dk + e / DVB) * dv + dv0 + e % DVB] = sdS[e];
-    __syncthreads();
-    auto ld_dO = [=](int k, int n) { return sdO[k * DVB + n]; };
-    auto ld_dS = [=](int k, int n) { return sdS[k * DVB + n]; };
-    // dU = P'^T dO + Kh' dS1   (P' = scale P, lower; Kh' = Kh)
-    gemm<true, 32>(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bP, k, m, C); }, true, ld_dO,
-         true, sdU, DVB, 1, stage);
-    gemm<true, 32>(C, DVB, dk, 1.f, true, [=](int m, int k) { return blk_at<IO>(bK, k, m, C); }, true, ld_dS,
-         true, sdU, DVB, 1, stage);
-    for (int e = tid; e < C * DVB; e += kNT)
-      b.dU[(slot * C + e / DVB) * dv + dv0 + e % DVB] = sdU[e];
-    // dV = X'^T dU   (X' = Y); rows >= L are not outputs (O into sdS0 first)
-    gemm<true, 32>(C, DVB, C, 1.f, false, [=](int m, int k) { return blk_at<IO>(bX, k, m, C); }, true,
-         [=](int k, int n) { return sdU[k * DVB + n]; }, true, sdS0, DVB, 1, stage);
-    for (int e = tid; e < C * DVB; e += kNT) {
-      const int r = e / DVB, j = e % DVB;
-      if (r < L) b.dv[((t0 + r) * H + h) * dv + dv0 + j] = sdS0[e];
+    if (b.dh0) {
+#pragma unroll
+      for (int mc = 0; mc < NMC; ++mc)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          b.dh0[st_base + static_cast<int64_t>(16 * mc + 4 * lq + ii) * dv] = sacc[mc][ii];
     }
-    __syncthreads();
-    // dS0^T = dO^T Qt' + dU^T W' + dS1^T Diag(g)   (W' = -W as stored)
-    for (int e = tid; e < dk * DVB; e += kNT) sdS0[e] = bg[e / DVB] * sdS[e];
-    __syncthreads();
-    gemm<true, 32>(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdO[k * DVB + m]; }, true,
-         [=](int k, int n) { return blk_at<IO>(bQ, k, n, dk); }, true, sdS0, 1, DVB, stage);
-    gemm<true, 32>(DVB, dk, C, 1.f, true, [=](int m, int k) { return sdU[k * DVB + m]; }, true,
-         [=](int k, int n) { return blk_at<IO>(bW, k, n, dk); }, true, sdS0, 1, DVB, stage);
-    for (int e = tid; e < dk * DVB; e += kNT) sdS[e] = sdS0[e];
+  } else {
+    using GA = BGroup<Cfg, true>;
+    using GB = BGroup<Cfg, false>;
+    // step k works on chunk nch - 1 - k; loads past the last step repeat it
+    auto chunk_of = [&](int k) { return nch - 1 - (k < nch - 1 ? k : nch - 1); };
+    auto blk = [&](int i) { return blocks + static_cast<int64_t>(c_begin + i) * a.blk_bytes; };
+    auto issueA = [&](GA& g, int k) {
+      const int i = chunk_of(k);
+      g.issue(blk(i), b.dout, chunk_t0(i), chunk_len(i), H, h, dv0, lt);
+    };
+    auto issueB = [&](GB& g, int k) { g.issue(blk(chunk_of(k)), nullptr, 0, 1, H, h, dv0, lt); };
+    GA sa0, sa1;
+    GB sb0, sb1;
+    if (nch > 0) {
+      issueA(sa0, 0);
+      issueB(sb0, 0);
+      issueA(sa1, 1);
+      issueB(sb1, 1);
+      sa0.store(smem, chunk_len(chunk_of(0)), lt);
+      issueA(sa0, 2);
+    }
+    // step k: B(k) (in gb) goes to LDS while dU(k) runs, then A(k+1) (in ga)
+    // while dV(k) and dS0(k) run; gb then takes B(k+2) and ga takes A(k+3)
+    auto step = [&](int k, GB& gb, GA& ga) {
+      __syncthreads();
+      gb.store(smem, 0, lt);
+      issueB(gb, k + 2);
+      __syncthreads();
+      ga.store(smem, chunk_len(chunk_of(k + 1)), lt);
+      issueA(ga, k + 3);
+    };
+    int k = 0;
+    for (; k + 1 < nch; k += 2) {
+      step(k, sb0, sa1);
+      step(k + 1, sb1, sa0);
+    }
+    if (k < nch) step(k, sb0, sa1);
   }
-  __syncthreads();
-  if (b.dh0)
-    for (int e = tid; e < dk * DVB; e += kNT) b.dh0[st + static_cast<int64_t>(e / DVB) * dv + e % DVB] = sdS[e];
 }
 
 // ---------------------------------------------------------------- 3: intra
@@ -798,20 +1105,57 @@ __global__ __launch_bounds__(kNT) void bwd_token_kernel(BwdArgs b) {
   }
 }
 
+template <class Cfg>
+launch_result launch_state(const BwdArgs& b, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&bwd_state_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = static_cast<int64_t>(b.f.num_seqs) * b.f.H * Cfg::NSPLIT;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_state_kernel<Cfg>, dim3(static_cast<unsigned>(blocks)), dim3(Cfg::NT),
+                     Cfg::LDS_BYTES, stream, b);
+  return hipGetLastError();
+}
+
+struct BEntry {
+  int chunk, dk, dv;
+  launch_result (*fn)(const BwdArgs&, hipStream_t);
+};
+template <class Op, class IO, int C, int D, int DVT>
+constexpr BEntry bentry() {
+  return BEntry{C, D, D, &launch_state<BCfg<Op, IO, C, D, D, DVT>>};
+}
+// the shapes the forward takes, with the same dv tiles
+const BEntry kStateBF16[] = {
+    bentry<OpBF16, io_bf16, 64, 128, 64>(), bentry<OpBF16, io_bf16, 32, 128, 64>(),
+    bentry<OpBF16, io_bf16, 16, 128, 64>(), bentry<OpBF16, io_bf16, 64, 64, 32>(),
+    bentry<OpBF16, io_bf16, 32, 64, 32>(),  bentry<OpBF16, io_bf16, 16, 64, 32>(),
+};
+const BEntry kStateF32[] = {
+    bentry<OpF32, io_f32, 16, 16, 16>(), bentry<OpF32, io_f32, 32, 16, 16>(),
+    bentry<OpF32, io_f32, 64, 16, 16>(), bentry<OpF32, io_f32, 16, 32, 32>(),
+    bentry<OpF32, io_f32, 32, 32, 32>(), bentry<OpF32, io_f32, 64, 32, 32>(),
+    bentry<OpF32, io_f32, 16, 64, 32>(), bentry<OpF32, io_f32, 32, 64, 32>(),
+};
+
 template <class IO>
 launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
   const FwdArgs& a = b.f;
   const int C = a.chunk, dk = a.dk, dv = a.dv;
-  const int DVB = dv < 32 ? dv : 32;
-  const int64_t g2 = static_cast<int64_t>(a.num_seqs) * a.H * (dv / DVB);
-  const size_t lds2 = sizeof(float) * (2 * C * DVB + dk * DVB + cmax(dk, C) * DVB + gstage(32));
-  static const hipError_t attr2 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&bwd_state_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
-  if (attr2 != hipSuccess) return attr2;
-  if (g2 > 0) {
-    hipLaunchKernelGGL((bwd_state_kernel<IO>), dim3(static_cast<unsigned>(g2)), dim3(kNT), lds2, stream, b);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  constexpr bool bf = sizeof(typename IO::storage) == 2;
+  const BEntry* e2 = nullptr;
+  {
+    const BEntry* first = bf ? kStateBF16 : kStateF32;
+    const int count = bf ? static_cast<int>(sizeof(kStateBF16) / sizeof(BEntry))
+                         : static_cast<int>(sizeof(kStateF32) / sizeof(BEntry));
+    for (int i = 0; i < count; ++i)
+      if (first[i].chunk == C && first[i].dk == dk && first[i].dv == dv) e2 = &first[i];
+  }
+  if (!e2) return hipErrorInvalidValue;
+  {
+    const launch_result r = e2->fn(b, stream);
+    if (r != hipSuccess) return r;
   }
   const int64_t total = static_cast<int64_t>(a.maxc) * a.H;
   if (total == 0) return hipSuccess;
