@@ -619,6 +619,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
   const bool l2 = a.use_l2norm != 0;
   const float scale = a.scale;
   const int SC = C * cmax(cmax(dk, dv), C);
+  // bf16 inputs stop after dP and dG and leave dq, dk, dalpha to bwd_dqk_kernel
+  constexpr bool kHandOff = sizeof(ST) == 2;
   float* ws = b.scratch + static_cast<int64_t>(blockIdx.x) * 14 * SC;
   // scratch slices: C x dk (stride dk) or C x dv (stride dv) or C x C
   float *sF = ws, *sKt = ws + SC, *sQt = ws + 2 * SC, *sRk = ws + 3 * SC, *sZ = ws + 4 * SC,
@@ -802,6 +804,24 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
       ldA[e] = j < r ? ldA[e] * lbeta[r] : 0.f;
     }
     __syncthreads();
+    if constexpr (kHandOff) {
+      // bf16 inputs: dP, dG, U and the norms go to the dq/dk pass; dbeta is
+      // complete here
+      float* odP = b.cdP + slot * C * C;
+      float* odG = b.cdG + slot * C * C;
+      float* oU = b.cU + slot * C * dv;
+      for (int e = tid; e < C * C; e += kNT) {
+        odP[e] = sdP[e];
+        odG[e] = ldA[e];
+      }
+      for (int e = tid; e < C * dv; e += kNT) oU[e] = sU[e];
+      for (int r = tid; r < C; r += kNT) {
+        b.crn[slot * 2 * C + r] = lrq[r];
+        b.crn[slot * 2 * C + C + r] = lrk[r];
+        if (r < L) b.dbeta[(t0 + r) * H + h] = ldb[r];
+      }
+      continue;
+    }
     // dQt = scale dO S0^T + dP Rk;  dKt = -T1 S0^T + dG Rk;
     // dRk = dG^T Kt + dP^T Qt + g dKh with dKh = U dS1^T
     gemm(C, dk, dv, scale, false, sdO, dv, 1, S0, 1, dv, sdQ, dk, 1, stage);
@@ -942,6 +962,432 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
         }
         if (sub == 0) b.dbeta[(t0 + r) * H + h] = ldb[r];
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 3b: dq, dk
+// bf16 inputs: dq, dk and dalpha of the chunks the intra-chunk pass kept, on
+// the matrix cores.  One workgroup per (chunk, head); wave w owns the 16
+// channels 16w .. 16w + 15, and lane (l16, lq) holds rows 16t + 4lq + i of
+// channel 16w + l16 (the layout of an MFMA result tile), so every
+// per-channel quantity (the gate products F, Kt, Qt, Rk, the reverse sums of
+// dalpha) stays in one wave's registers.  The products
+//   dQt = scale dO S0^T + dP Rk       dKt = -dV S0^T + dG Rk
+//   dKh = U dS1^T                     dRk = dG^T Kt + dP^T Qt
+// read the chunk-wide operands (dO, dV, U over dv; dP, dG and their
+// transposes over the chunk rows) from LDS as row fragments, and the
+// per-channel ones from registers: the lane's rows of S0 and dS1 straight
+// from memory, Rk, Kt and Qt from its own tiles in the permuted order.
+// The four products over the chunk rows carry the pair terms that cancel in
+// the reverse sums of dalpha (a pair (r, j) inside [s, C) enters Lam at r
+// and at j with opposite signs, through dG Rk at r and dG^T Kt at j, or dP Rk
+// and dP^T Qt).  Both products of a pair read the same bf16 dG_rj (dP_rj),
+// and the register operands run in split bf16, x = hi + lo with hi = bf16(x)
+// and lo = bf16(x - hi), so each pair term is formed to about 16 significant
+// bits on both sides and the cancellation holds to that precision.
+template <int C_, int DK_>
+struct QCfg {
+  static constexpr int C = C_, DK = DK_, DV = DK_;
+  static constexpr int NW = DK / 16, NT = 64 * NW, NB = C / 16;
+  static constexpr int LDV = frag_stride(DV, 2), LDC = frag_stride(C, 2);
+  static constexpr int NFV = DV / 32, NFC = (C + 31) / 32;
+  static constexpr int O_DO = 0;                                 // dO [C][LDV]
+  static constexpr int O_DV = align16(O_DO + C * LDV * 2);       // dV [C][LDV]
+  static constexpr int O_U = align16(O_DV + C * LDV * 2);        // U  [C][LDV]
+  // dP, dP^T, dG, dG^T as [C][LDC] (permuted order)
+  static constexpr int MCC = align16(C * LDC * 2);
+  static constexpr int O_CC = align16(O_U + C * LDV * 2);
+  static constexpr int O_P = O_CC, O_PT = O_CC + MCC, O_G = O_CC + 2 * MCC, O_GT = O_CC + 3 * MCC;
+  static constexpr int O_RED = O_CC + 4 * MCC;                   // float [2][NW][C] + [2][C] row sums
+  static constexpr int LDS_BYTES = align16(O_RED + 2 * (NW + 1) * C * 4);
+  // dP, dG lower: K fragment s of row tile t is live if it starts at or left
+  // of the tile's last row; their transposes are upper
+  static constexpr bool lo_live(int t, int s) { return 32 * s <= 16 * t + 15; }
+  static constexpr bool up_live(int t, int s) { return 32 * s + 31 >= 16 * t; }
+  static_assert(DV % 32 == 0 && C % 16 == 0, "shapes");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ bf16x8 to_bf16x8(float4 x, float4 y) {
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(x.x); r[1] = static_cast<__bf16>(x.y);
+  r[2] = static_cast<__bf16>(x.z); r[3] = static_cast<__bf16>(x.w);
+  r[4] = static_cast<__bf16>(y.x); r[5] = static_cast<__bf16>(y.y);
+  r[6] = static_cast<__bf16>(y.z); r[7] = static_cast<__bf16>(y.w);
+  return r;
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
+  using Op = OpBF16;
+  using Frag = Op::Frag;
+  constexpr int C = Cfg::C, DK = Cfg::DK, DV = Cfg::DV, NB = Cfg::NB, NW = Cfg::NW, NT = Cfg::NT;
+  constexpr int LDV = Cfg::LDV, LDC = Cfg::LDC, NFV = Cfg::NFV, NFC = Cfg::NFC;
+  const FwdArgs& a = b.f;
+  const int H = a.H;
+  const int c = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);
+  const Geo g = geo_of(a, c);
+  if (g.n < 0) return;
+  const int64_t slot = static_cast<int64_t>(h) * a.maxc + c;
+  if (b.bflag[slot] != 0) return;  // left to the token-level kernel
+  const int64_t t0 = g.t0;
+  const int L = g.L;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* sdO = reinterpret_cast<__bf16*>(smem + Cfg::O_DO);
+  __bf16* sdV = reinterpret_cast<__bf16*>(smem + Cfg::O_DV);
+  __bf16* sU = reinterpret_cast<__bf16*>(smem + Cfg::O_U);
+  __bf16* sP = reinterpret_cast<__bf16*>(smem + Cfg::O_P);
+  __bf16* sPT = reinterpret_cast<__bf16*>(smem + Cfg::O_PT);
+  __bf16* sG = reinterpret_cast<__bf16*>(smem + Cfg::O_G);
+  __bf16* sGT = reinterpret_cast<__bf16*>(smem + Cfg::O_GT);
+  float* red = reinterpret_cast<float*>(smem + Cfg::O_RED);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+  const int ch = 16 * w + l16;  // this lane's channel
+  // global address space (plain global loads rather than flat ones)
+  typedef const __attribute__((address_space(1))) uint16_t gu16;
+  typedef const __attribute__((address_space(1))) float gf32;
+
+  // ---- every load of the chunk goes out first.  Rows >= L of the token
+  // arrays are read from row L - 1 (no branch around a load, so none waits
+  // for another) and replaced afterwards.
+  constexpr int PR = DV / 8;                       // 8-element pieces per row of dv
+  constexpr int NIT = (C * PR + NT - 1) / NT;      // pieces per thread
+  constexpr int NU = (C / 2) * (C / 4);            // dP, dG units: 4 columns of 2 rows
+  constexpr int NUI = (NU + NT - 1) / NT;
+  uint4 xo[NIT];
+  float4 xv[NIT][2], xu[NIT][2];
+  float4 xp[NUI][2], xg[NUI][2];
+  float4 xs[NFV][2], xd[NFV][2];
+  {
+    const uint16_t* o = static_cast<const uint16_t*>(b.dout);
+    const float* dvo = b.dv;
+    const float* U = b.cU + slot * C * DV;
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int p = iclamp(tid + NT * u, C * PR - 1), r = p / PR, cp = p % PR;
+      const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
+      xo[u] = *reinterpret_cast<const uint4*>(o + row * DV + 8 * cp);
+      xv[u][0] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp);
+      xv[u][1] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp + 4);
+      xu[u][0] = *reinterpret_cast<const float4*>(U + r * DV + 8 * cp);
+      xu[u][1] = *reinterpret_cast<const float4*>(U + r * DV + 8 * cp + 4);
+    }
+    const float* P = b.cdP + slot * C * C;
+    const float* G = b.cdG + slot * C * C;
+#pragma unroll
+    for (int u = 0; u < NUI; ++u) {
+      const int uu = iclamp(tid + NT * u, NU - 1);
+      const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
+      xp[u][0] = *reinterpret_cast<const float4*>(P + r * C + j0);
+      xp[u][1] = *reinterpret_cast<const float4*>(P + (r + 1) * C + j0);
+      xg[u][0] = *reinterpret_cast<const float4*>(G + r * C + j0);
+      xg[u][1] = *reinterpret_cast<const float4*>(G + (r + 1) * C + j0);
+    }
+    const float* S0 = a.hc + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
+    const float* D1 = b.dS + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
+#pragma unroll
+    for (int s = 0; s < NFV; ++s) {
+      xs[s][0] = *reinterpret_cast<const float4*>(S0 + 32 * s);
+      xs[s][1] = *reinterpret_cast<const float4*>(S0 + 32 * s + 4);
+      xd[s][0] = *reinterpret_cast<const float4*>(D1 + 32 * s);
+      xd[s][1] = *reinterpret_cast<const float4*>(D1 + 32 * s + 4);
+    }
+  }
+  // chunk-wide operands to LDS as bf16 (rows >= L of dO and dV as zeros)
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int p = tid + NT * u, r = p / PR, cp = p % PR;
+    if ((C * PR) % NT == 0 || p < C * PR) {
+      const bool in = r < L;
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<uint4*>(sdO + r * LDV + 8 * cp) = in ? xo[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<bf16x8*>(sdV + r * LDV + 8 * cp) = to_bf16x8(in ? xv[u][0] : z, in ? xv[u][1] : z);
+      *reinterpret_cast<bf16x8*>(sU + r * LDV + 8 * cp) = to_bf16x8(xu[u][0], xu[u][1]);
+    }
+  }
+  // dP, dG and their transposes; rows fastest over the units, so that the
+  // transposed pair writes of consecutive lanes land in consecutive words
+#pragma unroll
+  for (int u = 0; u < NUI; ++u) {
+    const int uu = tid + NT * u;
+    if (NU % NT == 0 || uu < NU) {
+      const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
+      const int qj = Op::pos<C>(j0), qr = Op::pos<C>(r);
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const float4 pr = xp[u][rr], gr = xg[u][rr];
+        Op::store4(sP + (r + rr) * LDC + qj, f32x4{pr.x, pr.y, pr.z, pr.w});
+        Op::store4(sG + (r + rr) * LDC + qj, f32x4{gr.x, gr.y, gr.z, gr.w});
+      }
+      const float4 p0 = xp[u][0], p1 = xp[u][1], g0 = xg[u][0], g1 = xg[u][1];
+      Op::store2(sPT + (j0 + 0) * LDC + qr, p0.x, p1.x);
+      Op::store2(sPT + (j0 + 1) * LDC + qr, p0.y, p1.y);
+      Op::store2(sPT + (j0 + 2) * LDC + qr, p0.z, p1.z);
+      Op::store2(sPT + (j0 + 3) * LDC + qr, p0.w, p1.w);
+      Op::store2(sGT + (j0 + 0) * LDC + qr, g0.x, g1.x);
+      Op::store2(sGT + (j0 + 1) * LDC + qr, g0.y, g1.y);
+      Op::store2(sGT + (j0 + 2) * LDC + qr, g0.z, g1.z);
+      Op::store2(sGT + (j0 + 3) * LDC + qr, g0.w, g1.w);
+    }
+  }
+  // the lane's rows of S0 and dS1 as fragments over dv (natural order, as
+  // the LDS rows), and their row dot product
+  Frag s0f[NFV], d1f[NFV];
+  float dg = 0.f;
+#pragma unroll
+  for (int s = 0; s < NFV; ++s) {
+    const float4 x0 = xs[s][0], x1 = xs[s][1], y0 = xd[s][0], y1 = xd[s][1];
+    dg += x0.x * y0.x + x0.y * y0.y + x0.z * y0.z + x0.w * y0.w;
+    dg += x1.x * y1.x + x1.y * y1.y + x1.z * y1.z + x1.w * y1.w;
+    s0f[s] = to_bf16x8(x0, x1);
+    d1f[s] = to_bf16x8(y0, y1);
+  }
+  // the lane's q, k, alpha (in flight over the barrier and the first products)
+  const float* rn = b.crn + slot * 2 * C;
+  float xa[NB][4];
+  uint16_t xq[NB][4], xk[NB][4];
+  f32x4 nq[NB], nk[NB];
+  {
+    gu16* qg = (gu16*)a.q;
+    gu16* kg = (gu16*)a.k;
+    gf32* alpha = (gf32*)a.alpha;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      nq[t] = *reinterpret_cast<const f32x4*>(rn + 16 * t + 4 * lq);
+      nk[t] = *reinterpret_cast<const f32x4*>(rn + C + 16 * t + 4 * lq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * t + 4 * lq + i;
+        const int64_t e = ((t0 + (r < L ? r : L - 1)) * H + h) * DK + ch;
+        xa[t][i] = alpha[e];
+        xq[t][i] = qg[e];
+        xk[t][i] = kg[e];
+      }
+    }
+  }
+  __syncthreads();  // LDS operands ready
+
+  const float scale = a.scale;
+  // ---- products over dv
+  f32x4 dKh[NB], dQt[NB], dKt[NB], dRk[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const int ro = 16 * t + l16;
+    dKh[t] = dQt[t] = dKt[t] = dRk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NFV; ++s) {
+      const int o = ro * LDV + 32 * s + 8 * lq;
+      Op::mma(dKh[t], *reinterpret_cast<const bf16x8*>(sU + o), d1f[s]);
+      Op::mma(dQt[t], *reinterpret_cast<const bf16x8*>(sdO + o), s0f[s]);
+      Op::mma(dKt[t], *reinterpret_cast<const bf16x8*>(sdV + o), s0f[s]);
+    }
+    dQt[t] *= scale;
+    dKt[t] = -dKt[t];
+  }
+
+  // ---- normalised q, k; the gate products F, a scan down the rows: within
+  // the lane's 4 rows, across the 4 lane groups of the tile, tile to tile
+  f32x4 qh[NB], kh[NB], F[NB];
+  {
+    float carry = 1.f;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool in = 16 * t + 4 * lq + i < L;
+        al[i] = in ? xa[t][i] : 1.f;
+        qh[t][i] = in ? bf16_to_f32(xq[t][i]) * nq[t][i] : 0.f;
+        kh[t][i] = in ? bf16_to_f32(xk[t][i]) * nk[t][i] : 0.f;
+      }
+      float loc[4];
+      loc[0] = al[0];
+      loc[1] = loc[0] * al[1];
+      loc[2] = loc[1] * al[2];
+      loc[3] = loc[2] * al[3];
+      float inc = loc[3];
+      float y = __shfl_up(inc, 16);
+      if (lq >= 1) inc *= y;
+      y = __shfl_up(inc, 32);
+      if (lq >= 2) inc *= y;
+      float exc = __shfl_up(inc, 16);
+      if (lq == 0) exc = 1.f;
+      const float tot = __shfl(inc, 48 + l16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) F[t][i] = carry * exc * loc[i];
+      carry *= tot;
+    }
+  }
+  const float gch = __shfl(F[NB - 1][3], 48 + l16);  // the chunk's total product, row C - 1
+
+  // ---- products over the chunk rows, split bf16: first those with Rk, then
+  // those with Kt and Qt (fewer fragments live at once)
+  {
+    auto split = [&](const f32x4* x, Frag* hi, Frag* lo) {
+      f32x4 y[NB];
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[t][i] = x[t][i] - static_cast<float>(static_cast<__bf16>(x[t][i]));
+      Op::frags<C>(hi, x);
+      Op::frags<C>(lo, y);
+    };
+    auto mma2 = [&](f32x4& acc, const __bf16* row, int s, const Frag& bh, const Frag& bl) {
+      const Frag ah = Op::row_frag<C>(row, s, lq);
+      Op::mma(acc, ah, bh);
+      Op::mma(acc, ah, bl);
+    };
+    {
+      Frag rkh[NFC], rkl[NFC];
+      f32x4 x[NB];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) x[t] = kh[t] / F[t];
+      split(x, rkh, rkl);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const int ro = (16 * t + l16) * LDC;
+#pragma unroll
+        for (int s = 0; s < NFC; ++s)
+          if (Cfg::lo_live(t, s)) {
+            mma2(dQt[t], sP + ro, s, rkh[s], rkl[s]);
+            mma2(dKt[t], sG + ro, s, rkh[s], rkl[s]);
+          }
+      }
+    }
+    {
+      Frag kth[NFC], ktl[NFC], qth[NFC], qtl[NFC];
+      f32x4 x[NB];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) x[t] = kh[t] * F[t];
+      split(x, kth, ktl);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) x[t] = qh[t] * F[t];
+      split(x, qth, qtl);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const int ro = (16 * t + l16) * LDC;
+#pragma unroll
+        for (int s = 0; s < NFC; ++s)
+          if (Cfg::up_live(t, s)) {
+            mma2(dRk[t], sGT + ro, s, kth[s], ktl[s]);
+            mma2(dRk[t], sPT + ro, s, qth[s], qtl[s]);
+          }
+      }
+    }
+  }
+
+  // ---- per element
+  f32x4 dqh[NB], dkh[NB], lam[NB];
+  float dg2 = 0.f;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = F[t][i], kt = kh[t][i] * f, qt = qh[t][i] * f, rk = kh[t][i] / f;
+      const float drk = dRk[t][i] + gch * dKh[t][i];
+      dg2 += dKh[t][i] * rk;
+      dkh[t][i] = dKt[t][i] * f + drk / f;
+      dqh[t][i] = dQt[t][i] * f;
+      lam[t][i] = dKt[t][i] * kt + dQt[t][i] * qt - drk * rk;
+    }
+  }
+  dg += dg2;
+  dg += __shfl_xor(dg, 16);
+  dg += __shfl_xor(dg, 32);
+
+  // outputs through buffer stores whose range ends at row L: the stores of
+  // rows >= L are dropped by the range check, with no branch around them
+  const int64_t obase = (t0 * H + h) * DK;
+  const int orange = L * H * DK * 4;
+  const int ooff = (4 * lq * H * DK + ch) * 4;  // row 4lq, this lane's channel (bytes)
+  auto ostore = [&](float* out, int t, int i, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), make_rsrc(out + obase, orange),
+                                          ooff + (16 * t + i) * H * DK * 4, 0, 0);
+  };
+
+  // ---- dalpha: reverse running sums of Lam down the rows (within the lane,
+  // across lane groups, tile to tile), divided by alpha
+  {
+    float carry = dg * gch;
+#pragma unroll
+    for (int t = NB - 1; t >= 0; --t) {
+      float suf[4];
+      suf[3] = lam[t][3];
+      suf[2] = suf[3] + lam[t][2];
+      suf[1] = suf[2] + lam[t][1];
+      suf[0] = suf[1] + lam[t][0];
+      float inc = suf[0];
+      float y = __shfl_down(inc, 16);
+      if (lq <= 2) inc += y;
+      y = __shfl_down(inc, 32);
+      if (lq <= 1) inc += y;
+      float exc = __shfl_down(inc, 16);
+      if (lq == 3) exc = 0.f;
+      const float tot = __shfl(inc, l16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ostore(b.dalpha, t, i, (carry + exc + suf[i]) / xa[t][i]);
+      carry += tot;
+    }
+  }
+
+  // ---- through the norms: row sums q^ . dq^ and k^ . dk^ over the
+  // channels.  Over the wave's 16 lanes by a butterfly that halves the
+  // values per step (lane l16 ends with value l16 >> (4 - log2 4NB)), then
+  // over the waves in LDS, one thread per (row, q or k), read back by rows.
+  const bool l2 = a.use_l2norm != 0;
+  {
+    constexpr int NV = 4 * NB, LG = ilog2(NV);
+    float vq[NV], vk[NV];
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vq[4 * t + i] = qh[t][i] * dqh[t][i];
+        vk[4 * t + i] = kh[t][i] * dkh[t][i];
+      }
+    int m = 8;
+#pragma unroll
+    for (int half = NV / 2; half >= 1; half /= 2) {
+      const bool up = (l16 & m) != 0;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float ql = vq[i] + __shfl_xor(vq[i], m, 64), qu = vq[i + half] + __shfl_xor(vq[i + half], m, 64);
+        const float kl = vk[i] + __shfl_xor(vk[i], m, 64), ku = vk[i + half] + __shfl_xor(vk[i + half], m, 64);
+        vq[i] = up ? qu : ql;
+        vk[i] = up ? ku : kl;
+      }
+      m >>= 1;
+    }
+#pragma unroll
+    for (int mm = 8 >> LG; mm >= 1; mm >>= 1) {
+      vq[0] += __shfl_xor(vq[0], mm, 64);
+      vk[0] += __shfl_xor(vk[0], mm, 64);
+    }
+    const int v = l16 >> (4 - LG), r = 16 * (v >> 2) + 4 * lq + (v & 3);
+    if ((l16 & ((1 << (4 - LG)) - 1)) == 0) {
+      red[w * C + r] = vq[0];
+      red[(NW + w) * C + r] = vk[0];
+    }
+  }
+  __syncthreads();
+  float* fin = red + 2 * NW * C;  // [2][C]
+  if (tid < 2 * C) {
+    const int x = tid / C, r = tid % C;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) sum += red[(x * NW + v) * C + r];
+    fin[tid] = sum;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const f32x4 pq = *reinterpret_cast<const f32x4*>(fin + 16 * t + 4 * lq);
+    const f32x4 pk = *reinterpret_cast<const f32x4*>(fin + C + 16 * t + 4 * lq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ostore(b.dq, t, i, l2 ? nq[t][i] * (dqh[t][i] - qh[t][i] * pq[i]) : dqh[t][i]);
+      ostore(b.dk, t, i, l2 ? nk[t][i] * (dkh[t][i] - kh[t][i] * pk[i]) : dkh[t][i]);
     }
   }
 }
@@ -1118,6 +1564,19 @@ launch_result launch_state(const BwdArgs& b, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <class Cfg>
+launch_result launch_dqk(const BwdArgs& b, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&bwd_dqk_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const int64_t items = static_cast<int64_t>(b.f.maxc) * b.f.H;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dqk_kernel<Cfg>, dim3(static_cast<unsigned>(items)), dim3(Cfg::NT),
+                     Cfg::LDS_BYTES, stream, b);
+  return hipGetLastError();
+}
+
 struct BEntry {
   int chunk, dk, dv;
   launch_result (*fn)(const BwdArgs&, hipStream_t);
@@ -1166,6 +1625,17 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_intra_kernel<IO>), dim3(static_cast<unsigned>(b.grid3)), dim3(kNT), lds3, stream, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (bf) {
+    launch_result (*fq)(const BwdArgs&, hipStream_t) = nullptr;
+    if (dk == dv) {
+      if (C == 64) fq = dk == 128 ? &launch_dqk<QCfg<64, 128>> : dk == 64 ? &launch_dqk<QCfg<64, 64>> : nullptr;
+      if (C == 32) fq = dk == 128 ? &launch_dqk<QCfg<32, 128>> : dk == 64 ? &launch_dqk<QCfg<32, 64>> : nullptr;
+      if (C == 16) fq = dk == 128 ? &launch_dqk<QCfg<16, 128>> : dk == 64 ? &launch_dqk<QCfg<16, 64>> : nullptr;
+    }
+    if (!fq) return hipErrorInvalidValue;
+    e = fq(b, stream);
+    if (e != hipSuccess) return e;
+  }
   const size_t lds4 = sizeof(float) * (2 * dk * (dv + 1) + 5 * dk + 4 * dv + kNT / 64);
   static const hipError_t attr4 = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&bwd_token_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -1184,7 +1654,8 @@ int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t 
   const int64_t hm = static_cast<int64_t>(H) * maxc;
   const int64_t SC = static_cast<int64_t>(C) * cmax(cmax(dk, dv), C);
   return up(4 * hm * C * C) + 2 * up(4 * hm * dk * dv) + up(4 * hm * C * dv) + up(4 * hm) +
-         up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 14 * SC);
+         up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 14 * SC) + 2 * up(4 * hm * C * C) +
+         up(4 * hm * C * dv) + up(4 * hm * 2 * C);
 }
 
 void bwd_layout(BwdArgs& b, unsigned char* base) {
@@ -1204,6 +1675,14 @@ void bwd_layout(BwdArgs& b, unsigned char* base) {
   base += up(4 * hm);
   b.scratch = reinterpret_cast<float*>(base);
   b.grid3 = bwd_grid3(hm);
+  base += up(4 * static_cast<int64_t>(b.grid3) * 14 * C * cmax(cmax(dk, dv), C));
+  b.cdP = reinterpret_cast<float*>(base);
+  base += up(4 * hm * C * C);
+  b.cdG = reinterpret_cast<float*>(base);
+  base += up(4 * hm * C * C);
+  b.cU = reinterpret_cast<float*>(base);
+  base += up(4 * hm * C * dv);
+  b.crn = reinterpret_cast<float*>(base);
 }
 
 launch_result launch_bwd_passes(const BwdArgs& b, int32_t io_dtype, hipStream_t stream) {

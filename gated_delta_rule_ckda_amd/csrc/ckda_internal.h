@@ -140,6 +140,11 @@ struct BwdArgs {
   int32_t* bflag;    // [H][maxc] 1: chunk left to the token-level kernel
   float* scratch;    // [grid3][14][C * max(dk, dv, C)]
   int32_t grid3;
+  // handed from the intra-chunk pass to the dq/dk pass (bf16 inputs only)
+  float* cdP;        // [H][maxc][C][C] scale dO U^T, lower
+  float* cdG;        // [H][maxc][C][C] Diag(beta) dA, strictly lower
+  float* cU;         // [H][maxc][C][dv] the chunk's corrected values
+  float* crn;        // [H][maxc][2][C] reciprocal norms of q, k rows
 };
 // Workspace bytes of the backward beyond the forward's, their layout from
 // `base` (sets b.f.xout and b.f.hc too), and the backward's own passes.

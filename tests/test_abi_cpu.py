@@ -274,7 +274,9 @@ def test_bwd_rejects_bad_pointers(over, needle):
 def test_bwd_workspace_covers_forward_and_records():
     """The backward's workspace holds the forward's plus X (fp32 C x C), the
     entry state and the exit-state adjoint (fp32 dk x dv each), dU (fp32
-    C x dv) per (head, chunk), one flag each, and the intra kernel's scratch."""
+    C x dv) per (head, chunk), one flag each, the intra kernel's scratch, and
+    the records the intra-chunk pass hands to the dq/dk pass: dP and dG (fp32
+    C x C), U (fp32 C x dv) and the two row-norm vectors (fp32 C each)."""
     lib = ck._load()
     d = _desc(B=2, T=130, H=3, dk=64, dv=64, chunk_size=32)
     fwd = lib.ckda_chunk_fwd_workspace_size(ctypes.byref(d), 0)
@@ -283,5 +285,6 @@ def test_bwd_workspace_covers_forward_and_records():
     up = lambda x: (x + 255) // 256 * 256
     grid = min(hm, 512)
     extra = (up(4 * hm * 32 * 32) + 2 * up(4 * hm * 64 * 64) + up(4 * hm * 32 * 64) + up(4 * hm)
-             + up(4 * grid * 14 * 32 * 64))
+             + up(4 * grid * 14 * 32 * 64) + 2 * up(4 * hm * 32 * 32) + up(4 * hm * 32 * 64)
+             + up(4 * hm * 2 * 32))
     assert bwd == fwd + extra
