@@ -966,6 +966,430 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
   }
 }
 
+__device__ __forceinline__ bf16x8 to_bf16x8(float4 x, float4 y) {
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(x.x); r[1] = static_cast<__bf16>(x.y);
+  r[2] = static_cast<__bf16>(x.z); r[3] = static_cast<__bf16>(x.w);
+  r[4] = static_cast<__bf16>(y.x); r[5] = static_cast<__bf16>(y.y);
+  r[6] = static_cast<__bf16>(y.z); r[7] = static_cast<__bf16>(y.w);
+  return r;
+}
+
+// ---------------------------------------------------------------- 3a: dP, dG
+// bf16 inputs: the intra-chunk products up to dP and dG, on the matrix
+// cores.  One workgroup per (chunk, head), NW = d / 16 waves (dk = dv = d).
+// Wave w owns channel (and value column) 16w + l16 of the lane, rows
+// 16t + 4lq + i, for everything that lives along d: q, k, the gate products
+// F, Kt, Rk, and the columns of Z and U.  The C x C products (dY, dP, G, T,
+// dA) are spread over the waves tile by tile and read their operands from
+// LDS as rows:
+//   Z  = V - Kt S0           (S0 columns straight from memory)
+//   U  = Y Z                 (Y = X Diag(beta) from LDS, Z from registers)
+//   dY = dU Z^T,  dP = scale tril(dO U^T),  G = Kt Rk^T
+//   dbeta_j = sum_r X_rj dY_rj,  dX = tril(dY) Diag(beta)
+//   T  = dX X^T,  dA = -X^T T (strictly lower),  dbeta_r += sum_j dA_rj G_rj
+//   dG = Diag(beta) dA
+// Out: dP, dG and U for the dq/dk pass, the row norms, dbeta, and the chunk
+// flag (chunks whose gate products leave [2^-100, 2^10] go to the token-level
+// kernel).
+template <int C_, int D_>
+struct PCfg {
+  static constexpr int C = C_, D = D_;
+  static constexpr int NW = D / 16, NT = 64 * NW, NB = C / 16, NBC = C / 16;
+  static constexpr int LDV = frag_stride(D, 2), LDC = frag_stride(C, 2);
+  static constexpr int NFD = D / 32, NFC = (C + 31) / 32;
+  static constexpr int NL = NBC * (NBC + 1) / 2;     // tiles on or below the diagonal
+  static constexpr int NTL = (NL + NW - 1) / NW;     // ... per wave
+  static constexpr int NA = NBC * NBC;               // all tiles
+  static constexpr int NTA = (NA + NW - 1) / NW;
+  static constexpr int MV = align16(C * LDV * 2), MC = align16(C * LDC * 2);
+  // LDS (bytes); dX and T^T reuse the regions of Kt and Rk once G and Z are done
+  static constexpr int O_KT = 0, O_RK = MV, O_Z = 2 * MV, O_U = 3 * MV, O_DU = 4 * MV, O_DO = 5 * MV;
+  static constexpr int O_DX = O_KT, O_TT = O_RK;
+  static constexpr int O_Y = 6 * MV, O_X = O_Y + MC, O_XT = O_X + MC;
+  static constexpr int O_RED = O_XT + MC;            // float [2][C] norms, [C] dbeta, int flag
+  static constexpr int LDS_BYTES = align16(O_RED + (3 * C + 4) * 4);
+  // Y lower: K fragment s of row tile t is live if it starts at or left of
+  // the tile's last row
+  static constexpr bool lo_live(int t, int s) { return 32 * s <= 16 * t + 15; }
+  // lower tile q -> (tr, tc), row by row
+  static constexpr int ltr(int q) { int tr = 0; while ((tr + 1) * (tr + 2) / 2 <= q) ++tr; return tr; }
+  static constexpr int ltc(int q) { return q - ltr(q) * (ltr(q) + 1) / 2; }
+  static_assert(D % 32 == 0 && C % 16 == 0 && C <= D && MC <= MV, "shapes");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
+  using Op = OpBF16;
+  using Frag = Op::Frag;
+  constexpr int C = Cfg::C, D = Cfg::D, NB = Cfg::NB, NW = Cfg::NW, NT = Cfg::NT, NBC = Cfg::NBC;
+  constexpr int LDV = Cfg::LDV, LDC = Cfg::LDC, NFD = Cfg::NFD, NFC = Cfg::NFC;
+  const FwdArgs& a = b.f;
+  const int H = a.H;
+  const int c = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);
+  const int64_t slot = static_cast<int64_t>(h) * a.maxc + c;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+  const Geo g = geo_of(a, c);
+  if (g.n < 0) {
+    if (tid == 0) b.bflag[slot] = 0;
+    return;
+  }
+  const int64_t t0 = g.t0;
+  const int L = g.L;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* sKT = reinterpret_cast<__bf16*>(smem + Cfg::O_KT);
+  __bf16* sRK = reinterpret_cast<__bf16*>(smem + Cfg::O_RK);
+  __bf16* sZ = reinterpret_cast<__bf16*>(smem + Cfg::O_Z);
+  __bf16* sU = reinterpret_cast<__bf16*>(smem + Cfg::O_U);
+  __bf16* sDU = reinterpret_cast<__bf16*>(smem + Cfg::O_DU);
+  __bf16* sDO = reinterpret_cast<__bf16*>(smem + Cfg::O_DO);
+  __bf16* sDX = reinterpret_cast<__bf16*>(smem + Cfg::O_DX);
+  __bf16* sTT = reinterpret_cast<__bf16*>(smem + Cfg::O_TT);
+  __bf16* sY = reinterpret_cast<__bf16*>(smem + Cfg::O_Y);
+  __bf16* sX = reinterpret_cast<__bf16*>(smem + Cfg::O_X);
+  __bf16* sXT = reinterpret_cast<__bf16*>(smem + Cfg::O_XT);
+  float* nrm = reinterpret_cast<float*>(smem + Cfg::O_RED);  // [2][C]
+  float* dbl = nrm + 2 * C;                                    // [C]
+  int* flag = reinterpret_cast<int*>(dbl + C);
+  const int ch = 16 * w + l16;  // this lane's channel / value column
+  typedef const __attribute__((address_space(1))) uint16_t gu16;
+  typedef const __attribute__((address_space(1))) float gf32;
+  for (int i = tid; i < 3 * C + 1; i += NT) nrm[i] = 0.f;  // the flag word too
+
+  // ---- every load goes out first (rows >= L read from row L - 1, no
+  // branch around a load; replaced afterwards)
+  constexpr int PR = D / 8;
+  constexpr int NIT = (C * PR + NT - 1) / NT;
+  constexpr int NU = (C / 2) * (C / 4);
+  constexpr int NUI = (NU + NT - 1) / NT;
+  uint16_t xq[NB][4], xk[NB][4], xv[NB][4];
+  float xa[NB][4], xb[NB][4];
+  float xs[NFD][8];
+  uint4 xo[NIT];
+  float4 xu[NIT][2];
+  float4 xx[NUI][2];
+  {
+    gu16* qg = (gu16*)a.q;
+    gu16* kg = (gu16*)a.k;
+    gu16* vg = (gu16*)a.v;
+    gf32* alpha = (gf32*)a.alpha;
+    gf32* beta = (gf32*)a.beta;
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * t + 4 * lq + i;
+        const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
+        xq[t][i] = qg[row * D + ch];
+        xk[t][i] = kg[row * D + ch];
+        xv[t][i] = vg[row * D + ch];
+        xa[t][i] = alpha[row * D + ch];
+        xb[t][i] = beta[row];
+      }
+    gf32* S0 = (gf32*)(a.hc + slot * D * D + ch);
+#pragma unroll
+    for (int s = 0; s < NFD; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[s][e] = S0[(32 * s + 8 * lq + e) * D];
+    const uint16_t* o = static_cast<const uint16_t*>(b.dout);
+    const float* dU = b.dU + slot * C * D;
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int p = iclamp(tid + NT * u, C * PR - 1), r = p / PR, cp = p % PR;
+      const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
+      xo[u] = *reinterpret_cast<const uint4*>(o + row * D + 8 * cp);
+      xu[u][0] = *reinterpret_cast<const float4*>(dU + r * D + 8 * cp);
+      xu[u][1] = *reinterpret_cast<const float4*>(dU + r * D + 8 * cp + 4);
+    }
+    const float* X = a.xout + slot * C * C;
+#pragma unroll
+    for (int u = 0; u < NUI; ++u) {
+      const int uu = iclamp(tid + NT * u, NU - 1);
+      const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
+      xx[u][0] = *reinterpret_cast<const float4*>(X + r * C + j0);
+      xx[u][1] = *reinterpret_cast<const float4*>(X + (r + 1) * C + j0);
+    }
+  }
+  __syncthreads();  // the LDS accumulators are zero
+
+  // ---- to LDS: dU, dO rows (rows >= L of dO as zeros); X, X^T (natural
+  // order) and Y = X Diag(beta) (permuted order)
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int p = tid + NT * u, r = p / PR, cp = p % PR;
+    if ((C * PR) % NT == 0 || p < C * PR) {
+      *reinterpret_cast<uint4*>(sDO + r * LDV + 8 * cp) = r < L ? xo[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<bf16x8*>(sDU + r * LDV + 8 * cp) = to_bf16x8(xu[u][0], xu[u][1]);
+    }
+  }
+  {
+    const float* beta = static_cast<const float*>(a.beta);
+#pragma unroll
+    for (int u = 0; u < NUI; ++u) {
+      const int uu = tid + NT * u;
+      if (NU % NT == 0 || uu < NU) {
+        const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
+        float bj[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bj[e] = j0 + e < L ? beta[(t0 + j0 + e) * H + h] : 0.f;
+        const int qj = Op::pos<C>(j0);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const float4 x = xx[u][rr];
+          Op::store4(sX + (r + rr) * LDC + j0, f32x4{x.x, x.y, x.z, x.w});
+          Op::store4(sY + (r + rr) * LDC + qj, f32x4{x.x * bj[0], x.y * bj[1], x.z * bj[2], x.w * bj[3]});
+        }
+        const float4 x0 = xx[u][0], x1 = xx[u][1];
+        Op::store2(sXT + (j0 + 0) * LDC + r, x0.x, x1.x);
+        Op::store2(sXT + (j0 + 1) * LDC + r, x0.y, x1.y);
+        Op::store2(sXT + (j0 + 2) * LDC + r, x0.z, x1.z);
+        Op::store2(sXT + (j0 + 3) * LDC + r, x0.w, x1.w);
+      }
+    }
+  }
+  // ---- row norms: sums of squares over the wave's channels by a butterfly
+  // (lane l16 ends with value l16 >> (4 - log2 4NB)), then over the waves by
+  // LDS atomics
+  const bool l2 = a.use_l2norm != 0;
+  {
+    constexpr int NV = 4 * NB, LG = ilog2(NV);
+    float vq[NV], vk[NV];
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool in = 16 * t + 4 * lq + i < L;
+        const float x = in ? bf16_to_f32(xq[t][i]) : 0.f, y = in ? bf16_to_f32(xk[t][i]) : 0.f;
+        vq[4 * t + i] = x * x;
+        vk[4 * t + i] = y * y;
+      }
+    int m = 8;
+#pragma unroll
+    for (int half = NV / 2; half >= 1; half /= 2) {
+      const bool up = (l16 & m) != 0;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float ql = vq[i] + __shfl_xor(vq[i], m, 64), qu = vq[i + half] + __shfl_xor(vq[i + half], m, 64);
+        const float kl = vk[i] + __shfl_xor(vk[i], m, 64), ku = vk[i + half] + __shfl_xor(vk[i + half], m, 64);
+        vq[i] = up ? qu : ql;
+        vk[i] = up ? ku : kl;
+      }
+      m >>= 1;
+    }
+#pragma unroll
+    for (int mm = 8 >> LG; mm >= 1; mm >>= 1) {
+      vq[0] += __shfl_xor(vq[0], mm, 64);
+      vk[0] += __shfl_xor(vk[0], mm, 64);
+    }
+    const int v = l16 >> (4 - LG), r = 16 * (v >> 2) + 4 * lq + (v & 3);
+    if ((l16 & ((1 << (4 - LG)) - 1)) == 0) {
+      atomicAdd(nrm + r, vq[0]);
+      atomicAdd(nrm + C + r, vk[0]);
+    }
+  }
+  __syncthreads();  // LDS operands and the sums of squares
+
+  // ---- reciprocal norms; gate products (scan down the rows as in the dq/dk
+  // pass); regularity; Kt, Rk to LDS rows; Z starts as V
+  f32x4 rkv[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const f32x4 sk = *reinterpret_cast<const f32x4*>(nrm + C + 16 * t + 4 * lq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rkv[t][i] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sk[i] + kL2Eps)) : 1.f;
+  }
+  if (tid < 2 * C) {
+    const float x = nrm[tid];
+    b.crn[slot * 2 * C + tid] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(x + kL2Eps)) : 1.f;
+  }
+  f32x4 zacc[NB];
+  {
+    bool ok = true;
+    float carry = 1.f;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = 16 * t + 4 * lq + i < L ? xa[t][i] : 1.f;
+      float loc[4];
+      loc[0] = al[0];
+      loc[1] = loc[0] * al[1];
+      loc[2] = loc[1] * al[2];
+      loc[3] = loc[2] * al[3];
+      float inc = loc[3];
+      float y = __shfl_up(inc, 16);
+      if (lq >= 1) inc *= y;
+      y = __shfl_up(inc, 32);
+      if (lq >= 2) inc *= y;
+      float exc = __shfl_up(inc, 16);
+      if (lq == 0) exc = 1.f;
+      const float tot = __shfl(inc, 48 + l16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * t + 4 * lq + i;
+        const bool in = r < L;
+        const float f = carry * exc * loc[i], mf = fabsf(f);
+        ok = ok && mf >= kRegMin && mf <= kRegMax;
+        const float kh = in ? bf16_to_f32(xk[t][i]) * rkv[t][i] : 0.f;
+        sKT[r * LDV + ch] = static_cast<__bf16>(kh * f);
+        sRK[r * LDV + ch] = static_cast<__bf16>(kh / f);
+        zacc[t][i] = in ? bf16_to_f32(xv[t][i]) : 0.f;
+      }
+      carry *= tot;
+    }
+    if (!ok) *flag = 1;
+  }
+  __syncthreads();  // Kt, Rk rows; the flag
+  if (*flag != 0) {
+    if (tid == 0) b.bflag[slot] = 1;
+    return;
+  }
+  if (tid == 0) b.bflag[slot] = 0;
+
+  // ---- Z = V - Kt S0 (S0 columns negated), U = Y Z
+  {
+    Frag sf[NFD];
+#pragma unroll
+    for (int s = 0; s < NFD; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sf[s][e] = static_cast<__bf16>(-xs[s][e]);
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int s = 0; s < NFD; ++s)
+        Op::mma(zacc[t], *reinterpret_cast<const bf16x8*>(sKT + (16 * t + l16) * LDV + 32 * s + 8 * lq), sf[s]);
+  }
+  f32x4 uacc[NB];
+  {
+    Frag zf[NFC];
+    Op::frags<C>(zf, zacc);
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      uacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NFC; ++s)
+        if (Cfg::lo_live(t, s)) Op::mma(uacc[t], Op::row_frag<C>(sY + (16 * t + l16) * LDC, s, lq), zf[s]);
+    }
+  }
+  // U to memory (fp32) and, with Z, to LDS rows
+  {
+    float* uo = b.cU + slot * C * D + ch;
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * t + 4 * lq + i;
+        uo[r * D] = uacc[t][i];
+        sZ[r * LDV + ch] = static_cast<__bf16>(zacc[t][i]);
+        sU[r * LDV + ch] = static_cast<__bf16>(uacc[t][i]);
+      }
+  }
+  // G = Kt Rk^T on this wave's lower tiles (kept for dbeta)
+  f32x4 gacc[Cfg::NTL];
+#pragma unroll
+  for (int k = 0; k < Cfg::NTL; ++k) {
+    const int q = w + NW * k;
+    gacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (q < Cfg::NL) {
+      const int tr = Cfg::ltr(q), tc = Cfg::ltc(q);
+      Op::mmaK<D>(gacc[k], sKT + 16 * tr * LDV, LDV, sRK + 16 * tc * LDV, LDV, lane);
+    }
+  }
+  __syncthreads();  // Z, U rows; Kt and Rk no longer read
+
+  // ---- dY, dP on the lower tiles; dbeta (Y part); dX to LDS rows
+  const float scale = a.scale;
+  gf32* Xg = (gf32*)(a.xout + slot * C * C);
+  const float* beta = static_cast<const float*>(a.beta);
+#pragma unroll
+  for (int k = 0; k < Cfg::NTL; ++k) {
+    const int q = w + NW * k;
+    if (q < Cfg::NL) {
+      const int tr = Cfg::ltr(q), tc = Cfg::ltc(q);
+      f32x4 dy = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      Op::mmaK<D>(dy, sDU + 16 * tr * LDV, LDV, sZ + 16 * tc * LDV, LDV, lane);
+      Op::mmaK<D>(dp, sDO + 16 * tr * LDV, LDV, sU + 16 * tc * LDV, LDV, lane);
+      const int j = 16 * tc + l16;
+      const float bj = beta[(t0 + (j < L ? j : L - 1)) * H + h];
+      float xr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[i] = Xg[(16 * tr + 4 * lq + i) * C + j];
+      float colsum = 0.f;
+      float* po = b.cdP + slot * C * C;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * tr + 4 * lq + i;
+        const bool low = j <= r;
+        colsum += xr[i] * dy[i];
+        po[r * C + j] = low ? scale * dp[i] : 0.f;
+        sDX[r * LDC + j] = static_cast<__bf16>(low && j < L ? dy[i] * bj : 0.f);
+      }
+      colsum += __shfl_xor(colsum, 16);
+      colsum += __shfl_xor(colsum, 32);
+      if (lq == 0) atomicAdd(dbl + j, colsum);
+    }
+  }
+  // the upper tiles: dP and dX zero
+  for (int e = tid; e < C * C; e += NT) {
+    const int r = e / C, j = e % C;
+    if (j / 16 > r / 16) {
+      b.cdP[slot * C * C + e] = 0.f;
+      sDX[r * LDC + j] = static_cast<__bf16>(0.f);
+    }
+  }
+  __syncthreads();  // dX rows
+
+  // ---- T = dX X^T on all tiles, to LDS as T^T rows
+#pragma unroll
+  for (int k = 0; k < Cfg::NTA; ++k) {
+    const int q = w + NW * k;
+    if (q < Cfg::NA) {
+      const int tr = q / NBC, tc = q % NBC;
+      f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+      Op::mmaK<C>(tacc, sDX + 16 * tr * LDC, LDC, sX + 16 * tc * LDC, LDC, lane);
+      // T[m][j] (m = 16tr + 4lq + i, j = 16tc + l16) -> T^T[j][m .. m+3]
+      Op::store4(sTT + (16 * tc + l16) * LDC + 16 * tr + 4 * lq, tacc);
+    }
+  }
+  __syncthreads();  // T^T rows
+
+  // ---- dA = -X^T T on the lower tiles (strictly lower); dbeta (A part); dG
+#pragma unroll
+  for (int k = 0; k < Cfg::NTL; ++k) {
+    const int q = w + NW * k;
+    if (q < Cfg::NL) {
+      const int tr = Cfg::ltr(q), tc = Cfg::ltc(q);
+      f32x4 da = {0.f, 0.f, 0.f, 0.f};
+      Op::mmaK<C>(da, sXT + 16 * tr * LDC, LDC, sTT + 16 * tc * LDC, LDC, lane);
+      const int j = 16 * tc + l16;
+      float* go = b.cdG + slot * C * C;
+      float rs[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * tr + 4 * lq + i;
+        const float v = j < r ? -da[i] : 0.f;
+        rs[i] = v * gacc[k][i];
+        const float br = beta[(t0 + (r < L ? r : L - 1)) * H + h];
+        go[r * C + j] = r < L ? v * br : 0.f;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs[i] += __shfl_xor(rs[i], o, 64);
+      if (l16 == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(dbl + 16 * tr + 4 * lq + i, rs[i]);
+    }
+  }
+  for (int e = tid; e < C * C; e += NT) {
+    const int r = e / C, j = e % C;
+    if (j / 16 > r / 16) b.cdG[slot * C * C + e] = 0.f;
+  }
+  __syncthreads();  // dbeta sums
+  if (tid < L) b.dbeta[(t0 + tid) * H + h] = dbl[tid];
+}
+
 // ---------------------------------------------------------------- 3b: dq, dk
 // bf16 inputs: dq, dk and dalpha of the chunks the intra-chunk pass kept, on
 // the matrix cores.  One workgroup per (chunk, head); wave w owns the 16
@@ -1008,15 +1432,6 @@ struct QCfg {
   static_assert(DV % 32 == 0 && C % 16 == 0, "shapes");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
-
-__device__ __forceinline__ bf16x8 to_bf16x8(float4 x, float4 y) {
-  bf16x8 r;
-  r[0] = static_cast<__bf16>(x.x); r[1] = static_cast<__bf16>(x.y);
-  r[2] = static_cast<__bf16>(x.z); r[3] = static_cast<__bf16>(x.w);
-  r[4] = static_cast<__bf16>(y.x); r[5] = static_cast<__bf16>(y.y);
-  r[6] = static_cast<__bf16>(y.z); r[7] = static_cast<__bf16>(y.w);
-  return r;
-}
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
@@ -1565,6 +1980,19 @@ launch_result launch_state(const BwdArgs& b, hipStream_t stream) {
 }
 
 template <class Cfg>
+launch_result launch_dpg(const BwdArgs& b, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&bwd_dpg_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const int64_t items = static_cast<int64_t>(b.f.maxc) * b.f.H;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dpg_kernel<Cfg>, dim3(static_cast<unsigned>(items)), dim3(Cfg::NT),
+                     Cfg::LDS_BYTES, stream, b);
+  return hipGetLastError();
+}
+
+template <class Cfg>
 launch_result launch_dqk(const BwdArgs& b, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&bwd_dqk_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1618,22 +2046,31 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
   }
   const int64_t total = static_cast<int64_t>(a.maxc) * a.H;
   if (total == 0) return hipSuccess;
-  const size_t lds3 = sizeof(float) * (4 * C * C + kGStage + 4 * C + 2 * dk) + sizeof(int);
-  static const hipError_t attr3 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&bwd_intra_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
-  if (attr3 != hipSuccess) return attr3;
-  hipLaunchKernelGGL((bwd_intra_kernel<IO>), dim3(static_cast<unsigned>(b.grid3)), dim3(kNT), lds3, stream, b);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if constexpr (bf) {
+    // bf16 inputs: the intra-chunk work on the matrix cores, in two passes
+    launch_result (*fp)(const BwdArgs&, hipStream_t) = nullptr;
     launch_result (*fq)(const BwdArgs&, hipStream_t) = nullptr;
     if (dk == dv) {
-      if (C == 64) fq = dk == 128 ? &launch_dqk<QCfg<64, 128>> : dk == 64 ? &launch_dqk<QCfg<64, 64>> : nullptr;
-      if (C == 32) fq = dk == 128 ? &launch_dqk<QCfg<32, 128>> : dk == 64 ? &launch_dqk<QCfg<32, 64>> : nullptr;
-      if (C == 16) fq = dk == 128 ? &launch_dqk<QCfg<16, 128>> : dk == 64 ? &launch_dqk<QCfg<16, 64>> : nullptr;
+      if (C == 64 && dk == 128) fp = &launch_dpg<PCfg<64, 128>>, fq = &launch_dqk<QCfg<64, 128>>;
+      if (C == 64 && dk == 64) fp = &launch_dpg<PCfg<64, 64>>, fq = &launch_dqk<QCfg<64, 64>>;
+      if (C == 32 && dk == 128) fp = &launch_dpg<PCfg<32, 128>>, fq = &launch_dqk<QCfg<32, 128>>;
+      if (C == 32 && dk == 64) fp = &launch_dpg<PCfg<32, 64>>, fq = &launch_dqk<QCfg<32, 64>>;
+      if (C == 16 && dk == 128) fp = &launch_dpg<PCfg<16, 128>>, fq = &launch_dqk<QCfg<16, 128>>;
+      if (C == 16 && dk == 64) fp = &launch_dpg<PCfg<16, 64>>, fq = &launch_dqk<QCfg<16, 64>>;
     }
-    if (!fq) return hipErrorInvalidValue;
+    if (!fp || !fq) return hipErrorInvalidValue;
+    e = fp(b, stream);
+    if (e != hipSuccess) return e;
     e = fq(b, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    const size_t lds3 = sizeof(float) * (4 * C * C + kGStage + 4 * C + 2 * dk) + sizeof(int);
+    static const hipError_t attr3 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&bwd_intra_kernel<IO>), hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+    if (attr3 != hipSuccess) return attr3;
+    hipLaunchKernelGGL((bwd_intra_kernel<IO>), dim3(static_cast<unsigned>(b.grid3)), dim3(kNT), lds3, stream, b);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const size_t lds4 = sizeof(float) * (2 * dk * (dv + 1) + 5 * dk + 4 * dv + kNT / 64);
