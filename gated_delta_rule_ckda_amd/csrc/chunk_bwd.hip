@@ -619,8 +619,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
   const bool l2 = a.use_l2norm != 0;
   const float scale = a.scale;
   const int SC = C * cmax(cmax(dk, dv), C);
-  // bf16 inputs stop after dP and dG and leave dq, dk, dalpha to bwd_dqk_kernel
-  constexpr bool kHandOff = sizeof(ST) == 2;
   float* ws = b.scratch + static_cast<int64_t>(blockIdx.x) * 14 * SC;
   // scratch slices: C x dk (stride dk) or C x dv (stride dv) or C x C
   float *sF = ws, *sKt = ws + SC, *sQt = ws + 2 * SC, *sRk = ws + 3 * SC, *sZ = ws + 4 * SC,
@@ -804,24 +802,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
       ldA[e] = j < r ? ldA[e] * lbeta[r] : 0.f;
     }
     __syncthreads();
-    if constexpr (kHandOff) {
-      // bf16 inputs: dP, dG, U and the norms go to the dq/dk pass; dbeta is
-      // complete here
-      float* odP = b.cdP + slot * C * C;
-      float* odG = b.cdG + slot * C * C;
-      float* oU = b.cU + slot * C * dv;
-      for (int e = tid; e < C * C; e += kNT) {
-        odP[e] = sdP[e];
-        odG[e] = ldA[e];
-      }
-      for (int e = tid; e < C * dv; e += kNT) oU[e] = sU[e];
-      for (int r = tid; r < C; r += kNT) {
-        b.crn[slot * 2 * C + r] = lrq[r];
-        b.crn[slot * 2 * C + C + r] = lrk[r];
-        if (r < L) b.dbeta[(t0 + r) * H + h] = ldb[r];
-      }
-      continue;
-    }
     // dQt = scale dO S0^T + dP Rk;  dKt = -T1 S0^T + dG Rk;
     // dRk = dG^T Kt + dP^T Qt + g dKh with dKh = U dS1^T
     gemm(C, dk, dv, scale, false, sdO, dv, 1, S0, 1, dv, sdQ, dk, 1, stage);
@@ -2086,16 +2066,17 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
 
 int32_t bwd_grid3(int64_t total) { return static_cast<int32_t>(total < kGrid3 ? (total > 0 ? total : 1) : kGrid3); }
 
-int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv) {
+int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv, int32_t io_dtype) {
   auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
   const int64_t hm = static_cast<int64_t>(H) * maxc;
+  const int64_t common = up(4 * hm * C * C) + 2 * up(4 * hm * dk * dv) + up(4 * hm * C * dv) + up(4 * hm);
+  if (io_dtype == CKDA_DTYPE_BF16)  // dP, dG, U and the row norms, from the dP/dG pass to the dq/dk pass
+    return common + 2 * up(4 * hm * C * C) + up(4 * hm * C * dv) + up(4 * hm * 2 * C);
   const int64_t SC = static_cast<int64_t>(C) * cmax(cmax(dk, dv), C);
-  return up(4 * hm * C * C) + 2 * up(4 * hm * dk * dv) + up(4 * hm * C * dv) + up(4 * hm) +
-         up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 14 * SC) + 2 * up(4 * hm * C * C) +
-         up(4 * hm * C * dv) + up(4 * hm * 2 * C);
+  return common + up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 14 * SC);  // the intra kernel's scratch
 }
 
-void bwd_layout(BwdArgs& b, unsigned char* base) {
+void bwd_layout(BwdArgs& b, unsigned char* base, int32_t io_dtype) {
   const FwdArgs& a = b.f;
   auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
   const int64_t hm = static_cast<int64_t>(a.H) * a.maxc;
@@ -2110,16 +2091,20 @@ void bwd_layout(BwdArgs& b, unsigned char* base) {
   base += up(4 * hm * C * dv);
   b.bflag = reinterpret_cast<int32_t*>(base);
   base += up(4 * hm);
-  b.scratch = reinterpret_cast<float*>(base);
+  b.scratch = nullptr;
   b.grid3 = bwd_grid3(hm);
-  base += up(4 * static_cast<int64_t>(b.grid3) * 14 * C * cmax(cmax(dk, dv), C));
-  b.cdP = reinterpret_cast<float*>(base);
-  base += up(4 * hm * C * C);
-  b.cdG = reinterpret_cast<float*>(base);
-  base += up(4 * hm * C * C);
-  b.cU = reinterpret_cast<float*>(base);
-  base += up(4 * hm * C * dv);
-  b.crn = reinterpret_cast<float*>(base);
+  b.cdP = b.cdG = b.cU = b.crn = nullptr;
+  if (io_dtype == CKDA_DTYPE_BF16) {
+    b.cdP = reinterpret_cast<float*>(base);
+    base += up(4 * hm * C * C);
+    b.cdG = reinterpret_cast<float*>(base);
+    base += up(4 * hm * C * C);
+    b.cU = reinterpret_cast<float*>(base);
+    base += up(4 * hm * C * dv);
+    b.crn = reinterpret_cast<float*>(base);
+  } else {
+    b.scratch = reinterpret_cast<float*>(base);
+  }
 }
 
 launch_result launch_bwd_passes(const BwdArgs& b, int32_t io_dtype, hipStream_t stream) {

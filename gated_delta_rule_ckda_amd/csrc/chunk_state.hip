@@ -590,7 +590,7 @@ size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
                            int32_t num_seqs, int32_t chunk, int32_t io_dtype, bool packed) {
   const int64_t maxc = max_chunks(B, T, num_seqs, chunk, packed);
   return fwd_workspace_bytes(B, T, H, dk, num_seqs, chunk, io_dtype, packed, false) +
-         static_cast<size_t>(bwd_extra_bytes(H, maxc, chunk, dk, dv));
+         static_cast<size_t>(bwd_extra_bytes(H, maxc, chunk, dk, dv, io_dtype));
 }
 
 launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stream) {
@@ -600,7 +600,7 @@ launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stre
   const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
   if (!e) return hipErrorInvalidValue;
   if (static_cast<int64_t>(a.num_seqs) * a.H == 0) return hipSuccess;
-  bwd_layout(b, base);
+  bwd_layout(b, base, io_dtype);
   // the forward again, keeping X and the chunk entry states, writing no output
   a.o = nullptr;
   a.ht = nullptr;

@@ -138,9 +138,9 @@ struct BwdArgs {
   float* dS;         // [H][maxc][dk][dv] state adjoint at each chunk's exit
   float* dU;         // [H][maxc][C][dv]
   int32_t* bflag;    // [H][maxc] 1: chunk left to the token-level kernel
-  float* scratch;    // [grid3][14][C * max(dk, dv, C)]
+  float* scratch;    // [grid3][14][C * max(dk, dv, C)] (f32 inputs)
   int32_t grid3;
-  // handed from the intra-chunk pass to the dq/dk pass (bf16 inputs only)
+  // handed from the dP/dG pass to the dq/dk pass (bf16 inputs)
   float* cdP;        // [H][maxc][C][C] scale dO U^T, lower
   float* cdG;        // [H][maxc][C][C] Diag(beta) dA, strictly lower
   float* cU;         // [H][maxc][C][dv] the chunk's corrected values
@@ -148,8 +148,8 @@ struct BwdArgs {
 };
 // Workspace bytes of the backward beyond the forward's, their layout from
 // `base` (sets b.f.xout and b.f.hc too), and the backward's own passes.
-int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv);
-void bwd_layout(BwdArgs& b, unsigned char* base);
+int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv, int32_t io_dtype);
+void bwd_layout(BwdArgs& b, unsigned char* base, int32_t io_dtype);
 launch_result launch_bwd_passes(const BwdArgs& b, int32_t io_dtype, hipStream_t stream);
 // All of ckda_chunk_bwd: the forward with records, then the backward passes.
 size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
