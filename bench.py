@@ -262,8 +262,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "lm"], default="all",
-                    help="'lm': only the headline workload and its passes (for profiling)")
+    ap.add_argument("--only", choices=["all", "lm", "bwd"], default="all",
+                    help="'lm': only the headline workload and its passes; 'bwd': only the "
+                         "backward on the headline workload (both for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-pairs", type=int, default=128)
     args = ap.parse_args()
@@ -282,6 +283,11 @@ def main():
     B, T, H, dk = case.q.shape
     dv = case.v.shape[3]
     C = case.chunk
+    if args.only == "bwd":
+        ms_bw = bench_bwd(case, args.steps, args.warmup)
+        print(json.dumps({"workload": "backward of the LM layer", "ms_per_call": round(ms_bw, 3),
+                          "steps": args.steps, "warmup": args.warmup}), flush=True)
+        return
     ms, wall_ms, per = bench_fwd(case, args.steps, args.warmup, "ckda", passes=True)
     tokens = B * T
     tok_s = tokens / (ms / 1000.0)
