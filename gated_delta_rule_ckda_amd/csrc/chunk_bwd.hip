@@ -390,6 +390,8 @@ struct BGroup {
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
   using Op = typename Cfg::Op;
+  using IO = typename Cfg::IO;
+  using ST = typename IO::storage;
   using T = typename Cfg::T;
   using Frag = typename Cfg::Frag;
   constexpr int C = Cfg::C, DK = Cfg::DK, NB = Cfg::NB, NMC = Cfg::NMC;
@@ -465,11 +467,11 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
       asm volatile("v_mov_b32 %0, %1" : "=v"(lqo) : "v"(lq));
       asm volatile("v_mov_b32 %0, %1" : "=v"(colo) : "v"(col));
       {  // the adjoint at the chunk's end, for the intra-chunk pass
-        float* ds = b.dS + slot * DK * dv + colo + 4 * lqo * dv;
+        ST* ds = static_cast<ST*>(b.dS) + slot * DK * dv + colo + 4 * lqo * dv;
 #pragma unroll
         for (int mc = 0; mc < NMC; ++mc)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) ds[(16 * mc + ii) * dv] = sacc[mc][ii];
+          for (int ii = 0; ii < 4; ++ii) IO::store(ds, (16 * mc + ii) * dv, sacc[mc][ii]);
       }
       __syncthreads();  // group A of this chunk is in LDS
       Frag sf[NFK], of[NFC];
@@ -500,11 +502,11 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
         }
       }
       {
-        float* du = b.dU + slot * C * dv + colo + 4 * lqo * dv;
+        ST* du = static_cast<ST*>(b.dU) + slot * C * dv + colo + 4 * lqo * dv;
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) du[(16 * rb + ii) * dv] = uacc[rb][ii];
+          for (int ii = 0; ii < 4; ++ii) IO::store(du, (16 * rb + ii) * dv, uacc[rb][ii]);
       }
       Frag uf[NFC];
       Op::template frags<C>(uf, uacc);
@@ -657,9 +659,10 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
     }
     const int64_t t0 = g.t0;
     const int L = g.L;
-    const float* S0 = a.hc + slot * dk * dv;
-    const float* dS1 = b.dS + slot * dk * dv;
-    const float* dU = b.dU + slot * C * dv;
+    static_assert(sizeof(ST) == 4, "fp32 inputs only (bf16 inputs take bwd_dpg_kernel and bwd_dqk_kernel)");
+    const float* S0 = static_cast<const float*>(a.hc) + slot * dk * dv;
+    const float* dS1 = static_cast<const float*>(b.dS) + slot * dk * dv;
+    const float* dU = static_cast<const float*>(b.dU) + slot * C * dv;
     const float* X = a.xout + slot * C * C;
     // norms (TPR threads per row, lane groups of a wave), beta
     if (tid == 0) *lflag = 0;
@@ -946,6 +949,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
   }
 }
 
+// bits of bf16(x), rounded as the matrix-core operands are
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
 __device__ __forceinline__ bf16x8 to_bf16x8(float4 x, float4 y) {
   bf16x8 r;
   r[0] = static_cast<__bf16>(x.x); r[1] = static_cast<__bf16>(x.y);
@@ -1045,9 +1053,9 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   constexpr int NUI = (NU + NT - 1) / NT;
   uint16_t xq[NB][4], xk[NB][4], xv[NB][4];
   float xa[NB][4], xb[NB][4];
-  float xs[NFD][8];
+  uint16_t xs[NFD][8];
   uint4 xo[NIT];
-  float4 xu[NIT][2];
+  float4 xu[NIT];  // 8 bf16 values each
   float4 xx[NUI][2];
   {
     gu16* qg = (gu16*)a.q;
@@ -1067,20 +1075,19 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         xa[t][i] = alpha[row * D + ch];
         xb[t][i] = beta[row];
       }
-    gf32* S0 = (gf32*)(a.hc + slot * D * D + ch);
+    gu16* S0 = (gu16*)a.hc + slot * D * D + ch;
 #pragma unroll
     for (int s = 0; s < NFD; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) xs[s][e] = S0[(32 * s + 8 * lq + e) * D];
     const uint16_t* o = static_cast<const uint16_t*>(b.dout);
-    const float* dU = b.dU + slot * C * D;
+    const uint16_t* dU = static_cast<const uint16_t*>(b.dU) + slot * C * D;
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
       const int p = iclamp(tid + NT * u, C * PR - 1), r = p / PR, cp = p % PR;
       const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
       xo[u] = *reinterpret_cast<const uint4*>(o + row * D + 8 * cp);
-      xu[u][0] = *reinterpret_cast<const float4*>(dU + r * D + 8 * cp);
-      xu[u][1] = *reinterpret_cast<const float4*>(dU + r * D + 8 * cp + 4);
+      xu[u] = *reinterpret_cast<const float4*>(dU + r * D + 8 * cp);
     }
     const float* X = a.xout + slot * C * C;
 #pragma unroll
@@ -1099,8 +1106,10 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   for (int u = 0; u < NIT; ++u) {
     const int p = tid + NT * u, r = p / PR, cp = p % PR;
     if ((C * PR) % NT == 0 || p < C * PR) {
-      *reinterpret_cast<uint4*>(sDO + r * LDV + 8 * cp) = r < L ? xo[u] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<bf16x8*>(sDU + r * LDV + 8 * cp) = to_bf16x8(xu[u][0], xu[u][1]);
+      uint4 vo = xo[u];
+      if (r >= L) vo = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sDO + r * LDV + 8 * cp) = vo;
+      *reinterpret_cast<float4*>(sDU + r * LDV + 8 * cp) = xu[u];
     }
   }
   {
@@ -1227,13 +1236,13 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   }
   if (tid == 0) b.bflag[slot] = 0;
 
-  // ---- Z = V - Kt S0 (S0 columns negated), U = Y Z
+  // ---- Z = V - Kt S0 (S0 columns negated: the bf16 sign bit flipped), U = Y Z
   {
     Frag sf[NFD];
 #pragma unroll
     for (int s = 0; s < NFD; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sf[s][e] = static_cast<__bf16>(-xs[s][e]);
+      for (int e = 0; e < 8; ++e) sf[s][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(xs[s][e] ^ 0x8000u));
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
@@ -1252,15 +1261,15 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         if (Cfg::lo_live(t, s)) Op::mma(uacc[t], Op::row_frag<C>(sY + (16 * t + l16) * LDC, s, lq), zf[s]);
     }
   }
-  // U to memory (fp32) and, with Z, to LDS rows
+  // U to memory and, with Z, to LDS rows (bf16)
   {
-    float* uo = b.cU + slot * C * D + ch;
+    uint16_t* uo = b.cU + slot * C * D + ch;
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * t + 4 * lq + i;
-        uo[r * D] = uacc[t][i];
+        uo[r * D] = bf16_bits(uacc[t][i]);
         sZ[r * LDV + ch] = static_cast<__bf16>(zacc[t][i]);
         sU[r * LDV + ch] = static_cast<__bf16>(uacc[t][i]);
       }
@@ -1296,13 +1305,13 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) xr[i] = Xg[(16 * tr + 4 * lq + i) * C + j];
       float colsum = 0.f;
-      float* po = b.cdP + slot * C * C;
+      uint16_t* po = b.cdP + slot * C * C;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * tr + 4 * lq + i;
         const bool low = j <= r;
         colsum += xr[i] * dy[i];
-        po[r * C + j] = low ? scale * dp[i] : 0.f;
+        po[r * C + j] = low ? bf16_bits(scale * dp[i]) : 0;
         sDX[r * LDC + j] = static_cast<__bf16>(low && j < L ? dy[i] * bj : 0.f);
       }
       colsum += __shfl_xor(colsum, 16);
@@ -1314,7 +1323,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, j = e % C;
     if (j / 16 > r / 16) {
-      b.cdP[slot * C * C + e] = 0.f;
+      b.cdP[slot * C * C + e] = 0;
       sDX[r * LDC + j] = static_cast<__bf16>(0.f);
     }
   }
@@ -1343,7 +1352,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
       f32x4 da = {0.f, 0.f, 0.f, 0.f};
       Op::mmaK<C>(da, sXT + 16 * tr * LDC, LDC, sTT + 16 * tc * LDC, LDC, lane);
       const int j = 16 * tc + l16;
-      float* go = b.cdG + slot * C * C;
+      uint16_t* go = b.cdG + slot * C * C;
       float rs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1351,7 +1360,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         const float v = j < r ? -da[i] : 0.f;
         rs[i] = v * gacc[k][i];
         const float br = beta[(t0 + (r < L ? r : L - 1)) * H + h];
-        go[r * C + j] = r < L ? v * br : 0.f;
+        go[r * C + j] = r < L ? bf16_bits(v * br) : 0;
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1)
@@ -1364,7 +1373,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   }
   for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, j = e % C;
-    if (j / 16 > r / 16) b.cdG[slot * C * C + e] = 0.f;
+    if (j / 16 > r / 16) b.cdG[slot * C * C + e] = 0;
   }
   __syncthreads();  // dbeta sums
   if (tid < L) b.dbeta[(t0 + tid) * H + h] = dbl[tid];
@@ -1450,14 +1459,14 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   constexpr int NIT = (C * PR + NT - 1) / NT;      // pieces per thread
   constexpr int NU = (C / 2) * (C / 4);            // dP, dG units: 4 columns of 2 rows
   constexpr int NUI = (NU + NT - 1) / NT;
-  uint4 xo[NIT];
-  float4 xv[NIT][2], xu[NIT][2];
-  float4 xp[NUI][2], xg[NUI][2];
-  float4 xs[NFV][2], xd[NFV][2];
+  uint4 xo[NIT], xu[NIT];
+  float4 xv[NIT][2];
+  uint2 xp[NUI][2], xg[NUI][2];
+  uint4 xs[NFV], xd[NFV];
   {
     const uint16_t* o = static_cast<const uint16_t*>(b.dout);
     const float* dvo = b.dv;
-    const float* U = b.cU + slot * C * DV;
+    const uint16_t* U = b.cU + slot * C * DV;
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
       const int p = iclamp(tid + NT * u, C * PR - 1), r = p / PR, cp = p % PR;
@@ -1465,28 +1474,25 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
       xo[u] = *reinterpret_cast<const uint4*>(o + row * DV + 8 * cp);
       xv[u][0] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp);
       xv[u][1] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp + 4);
-      xu[u][0] = *reinterpret_cast<const float4*>(U + r * DV + 8 * cp);
-      xu[u][1] = *reinterpret_cast<const float4*>(U + r * DV + 8 * cp + 4);
+      xu[u] = *reinterpret_cast<const uint4*>(U + r * DV + 8 * cp);
     }
-    const float* P = b.cdP + slot * C * C;
-    const float* G = b.cdG + slot * C * C;
+    const uint16_t* P = b.cdP + slot * C * C;
+    const uint16_t* G = b.cdG + slot * C * C;
 #pragma unroll
     for (int u = 0; u < NUI; ++u) {
       const int uu = iclamp(tid + NT * u, NU - 1);
       const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
-      xp[u][0] = *reinterpret_cast<const float4*>(P + r * C + j0);
-      xp[u][1] = *reinterpret_cast<const float4*>(P + (r + 1) * C + j0);
-      xg[u][0] = *reinterpret_cast<const float4*>(G + r * C + j0);
-      xg[u][1] = *reinterpret_cast<const float4*>(G + (r + 1) * C + j0);
+      xp[u][0] = *reinterpret_cast<const uint2*>(P + r * C + j0);
+      xp[u][1] = *reinterpret_cast<const uint2*>(P + (r + 1) * C + j0);
+      xg[u][0] = *reinterpret_cast<const uint2*>(G + r * C + j0);
+      xg[u][1] = *reinterpret_cast<const uint2*>(G + (r + 1) * C + j0);
     }
-    const float* S0 = a.hc + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
-    const float* D1 = b.dS + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
+    const uint16_t* S0 = static_cast<const uint16_t*>(a.hc) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
+    const uint16_t* D1 = static_cast<const uint16_t*>(b.dS) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
 #pragma unroll
     for (int s = 0; s < NFV; ++s) {
-      xs[s][0] = *reinterpret_cast<const float4*>(S0 + 32 * s);
-      xs[s][1] = *reinterpret_cast<const float4*>(S0 + 32 * s + 4);
-      xd[s][0] = *reinterpret_cast<const float4*>(D1 + 32 * s);
-      xd[s][1] = *reinterpret_cast<const float4*>(D1 + 32 * s + 4);
+      xs[s] = *reinterpret_cast<const uint4*>(S0 + 32 * s);
+      xd[s] = *reinterpret_cast<const uint4*>(D1 + 32 * s);
     }
   }
   // chunk-wide operands to LDS as bf16 (rows >= L of dO and dV as zeros)
@@ -1498,7 +1504,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
       const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
       *reinterpret_cast<uint4*>(sdO + r * LDV + 8 * cp) = in ? xo[u] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<bf16x8*>(sdV + r * LDV + 8 * cp) = to_bf16x8(in ? xv[u][0] : z, in ? xv[u][1] : z);
-      *reinterpret_cast<bf16x8*>(sU + r * LDV + 8 * cp) = to_bf16x8(xu[u][0], xu[u][1]);
+      *reinterpret_cast<uint4*>(sU + r * LDV + 8 * cp) = xu[u];
     }
   }
   // dP, dG and their transposes; rows fastest over the units, so that the
@@ -1511,19 +1517,19 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
       const int qj = Op::pos<C>(j0), qr = Op::pos<C>(r);
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
-        const float4 pr = xp[u][rr], gr = xg[u][rr];
-        Op::store4(sP + (r + rr) * LDC + qj, f32x4{pr.x, pr.y, pr.z, pr.w});
-        Op::store4(sG + (r + rr) * LDC + qj, f32x4{gr.x, gr.y, gr.z, gr.w});
+        *reinterpret_cast<uint2*>(sP + (r + rr) * LDC + qj) = xp[u][rr];
+        *reinterpret_cast<uint2*>(sG + (r + rr) * LDC + qj) = xg[u][rr];
       }
-      const float4 p0 = xp[u][0], p1 = xp[u][1], g0 = xg[u][0], g1 = xg[u][1];
-      Op::store2(sPT + (j0 + 0) * LDC + qr, p0.x, p1.x);
-      Op::store2(sPT + (j0 + 1) * LDC + qr, p0.y, p1.y);
-      Op::store2(sPT + (j0 + 2) * LDC + qr, p0.z, p1.z);
-      Op::store2(sPT + (j0 + 3) * LDC + qr, p0.w, p1.w);
-      Op::store2(sGT + (j0 + 0) * LDC + qr, g0.x, g1.x);
-      Op::store2(sGT + (j0 + 1) * LDC + qr, g0.y, g1.y);
-      Op::store2(sGT + (j0 + 2) * LDC + qr, g0.z, g1.z);
-      Op::store2(sGT + (j0 + 3) * LDC + qr, g0.w, g1.w);
+      // element e of two rows -> one word (row r low, row r + 1 high)
+      auto pair = [](uint2 lo, uint2 hi, int e) {
+        const uint32_t a = e < 2 ? lo.x : lo.y, c = e < 2 ? hi.x : hi.y;
+        return (e & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
+      };
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint32_t*>(sPT + (j0 + e) * LDC + qr) = pair(xp[u][0], xp[u][1], e);
+        *reinterpret_cast<uint32_t*>(sGT + (j0 + e) * LDC + qr) = pair(xg[u][0], xg[u][1], e);
+      }
     }
   }
   // the lane's rows of S0 and dS1 as fragments over dv (natural order, as
@@ -1532,11 +1538,13 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   float dg = 0.f;
 #pragma unroll
   for (int s = 0; s < NFV; ++s) {
-    const float4 x0 = xs[s][0], x1 = xs[s][1], y0 = xd[s][0], y1 = xd[s][1];
-    dg += x0.x * y0.x + x0.y * y0.y + x0.z * y0.z + x0.w * y0.w;
-    dg += x1.x * y1.x + x1.y * y1.y + x1.z * y1.z + x1.w * y1.w;
-    s0f[s] = to_bf16x8(x0, x1);
-    d1f[s] = to_bf16x8(y0, y1);
+    const uint32_t xw[4] = {xs[s].x, xs[s].y, xs[s].z, xs[s].w}, yw[4] = {xd[s].x, xd[s].y, xd[s].z, xd[s].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dg += __uint_as_float(xw[e] << 16) * __uint_as_float(yw[e] << 16) +
+            __uint_as_float(xw[e] & 0xFFFF0000u) * __uint_as_float(yw[e] & 0xFFFF0000u);
+    s0f[s] = __builtin_bit_cast(bf16x8, xs[s]);
+    d1f[s] = __builtin_bit_cast(bf16x8, xd[s]);
   }
   // the lane's q, k, alpha (in flight over the barrier and the first products)
   const float* rn = b.crn + slot * 2 * C;
@@ -1860,13 +1868,14 @@ __global__ __launch_bounds__(kNT) void bwd_token_kernel(BwdArgs b) {
     const int64_t slot = static_cast<int64_t>(h) * a.maxc + c;
     if (b.bflag[slot] == 0) continue;
     const Geo g = geo_of(a, c);
-    const float* S0 = a.hc + slot * dk * dv;
+    const ST* S0 = static_cast<const ST*>(a.hc) + slot * dk * dv;
+    const ST* dS1 = static_cast<const ST*>(b.dS) + slot * dk * dv;
     __syncthreads();
-    for (int i = tid; i < dk * dv; i += kNT) sG[(i / dv) * LD + i % dv] = b.dS[slot * dk * dv + i];
+    for (int i = tid; i < dk * dv; i += kNT) sG[(i / dv) * LD + i % dv] = IO::load(dS1, i);
     for (int t = g.L - 1; t >= 0; --t) {
       // the state before token t
       __syncthreads();
-      for (int i = tid; i < dk * dv; i += kNT) sS[(i / dv) * LD + i % dv] = S0[i];
+      for (int i = tid; i < dk * dv; i += kNT) sS[(i / dv) * LD + i % dv] = IO::load(S0, i);
       __syncthreads();
       for (int tt = 0; tt < t; ++tt) {
         load_token(g.t0 + tt, h);
@@ -2069,9 +2078,11 @@ int32_t bwd_grid3(int64_t total) { return static_cast<int32_t>(total < kGrid3 ? 
 int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t dv, int32_t io_dtype) {
   auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
   const int64_t hm = static_cast<int64_t>(H) * maxc;
-  const int64_t common = up(4 * hm * C * C) + 2 * up(4 * hm * dk * dv) + up(4 * hm * C * dv) + up(4 * hm);
-  if (io_dtype == CKDA_DTYPE_BF16)  // dP, dG, U and the row norms, from the dP/dG pass to the dq/dk pass
-    return common + 2 * up(4 * hm * C * C) + up(4 * hm * C * dv) + up(4 * hm * 2 * C);
+  const bool bf = io_dtype == CKDA_DTYPE_BF16;
+  const int64_t es = bf ? 2 : 4;  // records in the io type
+  const int64_t common = up(4 * hm * C * C) + 2 * up(es * hm * dk * dv) + up(es * hm * C * dv) + up(4 * hm);
+  if (bf)  // dP, dG, U (bf16) and the row norms (fp32), from the dP/dG pass to the dq/dk pass
+    return common + 2 * up(2 * hm * C * C) + up(2 * hm * C * dv) + up(4 * hm * 2 * C);
   const int64_t SC = static_cast<int64_t>(C) * cmax(cmax(dk, dv), C);
   return common + up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 14 * SC);  // the intra kernel's scratch
 }
@@ -2081,26 +2092,29 @@ void bwd_layout(BwdArgs& b, unsigned char* base, int32_t io_dtype) {
   auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
   const int64_t hm = static_cast<int64_t>(a.H) * a.maxc;
   const int C = a.chunk, dk = a.dk, dv = a.dv;
+  const bool bf = io_dtype == CKDA_DTYPE_BF16;
+  const int64_t es = bf ? 2 : 4;
   b.f.xout = reinterpret_cast<float*>(base);
   base += up(4 * hm * C * C);
-  b.f.hc = reinterpret_cast<float*>(base);
-  base += up(4 * hm * dk * dv);
-  b.dS = reinterpret_cast<float*>(base);
-  base += up(4 * hm * dk * dv);
-  b.dU = reinterpret_cast<float*>(base);
-  base += up(4 * hm * C * dv);
+  b.f.hc = base;
+  base += up(es * hm * dk * dv);
+  b.dS = base;
+  base += up(es * hm * dk * dv);
+  b.dU = base;
+  base += up(es * hm * C * dv);
   b.bflag = reinterpret_cast<int32_t*>(base);
   base += up(4 * hm);
   b.scratch = nullptr;
   b.grid3 = bwd_grid3(hm);
-  b.cdP = b.cdG = b.cU = b.crn = nullptr;
-  if (io_dtype == CKDA_DTYPE_BF16) {
-    b.cdP = reinterpret_cast<float*>(base);
-    base += up(4 * hm * C * C);
-    b.cdG = reinterpret_cast<float*>(base);
-    base += up(4 * hm * C * C);
-    b.cU = reinterpret_cast<float*>(base);
-    base += up(4 * hm * C * dv);
+  b.cdP = b.cdG = b.cU = nullptr;
+  b.crn = nullptr;
+  if (bf) {
+    b.cdP = reinterpret_cast<uint16_t*>(base);
+    base += up(2 * hm * C * C);
+    b.cdG = reinterpret_cast<uint16_t*>(base);
+    base += up(2 * hm * C * C);
+    b.cU = reinterpret_cast<uint16_t*>(base);
+    base += up(2 * hm * C * dv);
     b.crn = reinterpret_cast<float*>(base);
   } else {
     b.scratch = reinterpret_cast<float*>(base);

@@ -277,12 +277,12 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
         int lqo, colo;
         asm volatile("v_mov_b32 %0, %1" : "=v"(lqo) : "v"(lq));
         asm volatile("v_mov_b32 %0, %1" : "=v"(colo) : "v"(dv0 + 16 * wave + l16));
-        float* hc = a.hc + (static_cast<int64_t>(h) * a.maxc + c_begin + i) * DK * a.dv + colo +
-                    static_cast<int64_t>(4 * lqo) * a.dv;
+        ST* hc = static_cast<ST*>(a.hc) + (static_cast<int64_t>(h) * a.maxc + c_begin + i) * DK * a.dv +
+                 colo + static_cast<int64_t>(4 * lqo) * a.dv;
 #pragma unroll
         for (int mc = 0; mc < NMC; ++mc)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) hc[static_cast<int64_t>(16 * mc + ii) * a.dv] = sacc[mc][ii];
+          for (int ii = 0; ii < 4; ++ii) IO::store(hc, static_cast<int64_t>(16 * mc + ii) * a.dv, sacc[mc][ii]);
       }
       __syncthreads();  // group A of chunk i is in LDS
       Frag sf[Cfg::NFK];

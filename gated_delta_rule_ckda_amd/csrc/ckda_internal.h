@@ -98,7 +98,7 @@ struct FwdArgs {
   float* sb;              // [B*T][H] beta
   // records kept for the backward (null in a plain forward)
   float* xout;            // [H][maxc][C][C] X = (I + A)^{-1} of every chunk, fp32
-  float* hc;              // [H][maxc][dk][dv] state entering every chunk, fp32
+  void* hc;               // [H][maxc][dk][dv] state entering every chunk (io type)
 };
 bool fwd_supported(int32_t chunk, int32_t dk, int32_t dv, int32_t io_dtype);
 // Workspace bytes ckda_chunk_fwd needs for these sizes (0 for an empty call).
@@ -135,16 +135,18 @@ struct BwdArgs {
   float* dbeta;      // [B,T,H]
   float* dh0;        // [N,H,dk,dv] or null
   // workspace
-  float* dS;         // [H][maxc][dk][dv] state adjoint at each chunk's exit
-  float* dU;         // [H][maxc][C][dv]
+  // records in the io type (bf16 inputs: bf16, consumed as bf16 matrix-core
+  // operands; fp32 inputs: fp32)
+  void* dS;          // [H][maxc][dk][dv] state adjoint at each chunk's exit
+  void* dU;          // [H][maxc][C][dv]
   int32_t* bflag;    // [H][maxc] 1: chunk left to the token-level kernel
   float* scratch;    // [grid3][14][C * max(dk, dv, C)] (f32 inputs)
   int32_t grid3;
-  // handed from the dP/dG pass to the dq/dk pass (bf16 inputs)
-  float* cdP;        // [H][maxc][C][C] scale dO U^T, lower
-  float* cdG;        // [H][maxc][C][C] Diag(beta) dA, strictly lower
-  float* cU;         // [H][maxc][C][dv] the chunk's corrected values
-  float* crn;        // [H][maxc][2][C] reciprocal norms of q, k rows
+  // handed from the dP/dG pass to the dq/dk pass (bf16 inputs; bf16 but crn)
+  uint16_t* cdP;     // [H][maxc][C][C] scale dO U^T, lower
+  uint16_t* cdG;     // [H][maxc][C][C] Diag(beta) dA, strictly lower
+  uint16_t* cU;      // [H][maxc][C][dv] the chunk's corrected values
+  float* crn;        // [H][maxc][2][C] reciprocal norms of q, k rows (fp32)
 };
 // Workspace bytes of the backward beyond the forward's, their layout from
 // `base` (sets b.f.xout and b.f.hc too), and the backward's own passes.

@@ -273,17 +273,18 @@ def test_bwd_rejects_bad_pointers(over, needle):
 
 def test_bwd_workspace_covers_forward_and_records():
     """The backward's workspace holds the forward's plus X (fp32 C x C), the
-    entry state and the exit-state adjoint (fp32 dk x dv each), dU (fp32
-    C x dv) per (head, chunk) and one flag each.  bf16 inputs add what the
-    dP/dG pass hands to the dq/dk pass: dP and dG (fp32 C x C), U (fp32
+    entry state and the exit-state adjoint (dk x dv each), dU (C x dv) per
+    (head, chunk) and one flag each.  bf16 inputs add what the
+    dP/dG pass hands to the dq/dk pass: dP and dG (bf16 C x C), U (bf16
     C x dv) and the two row-norm vectors (fp32 C each); fp32 inputs add the
-    intra kernel's scratch instead."""
+    intra kernel's scratch instead.  The entry states, the adjoints and dU
+    are kept in the io type."""
     lib = ck._load()
     hm = 3 * 2 * 5  # heads x (B * ceil(130 / 32)) chunk slots
     up = lambda x: (x + 255) // 256 * 256
-    common = up(4 * hm * 32 * 32) + 2 * up(4 * hm * 64 * 64) + up(4 * hm * 32 * 64) + up(4 * hm)
-    for dt, extra in ((ck.BF16, common + 2 * up(4 * hm * 32 * 32) + up(4 * hm * 32 * 64) + up(4 * hm * 2 * 32)),
-                      (ck.F32, common + up(4 * min(hm, 512) * 14 * 32 * 64))):
+    common = lambda es: up(4 * hm * 32 * 32) + 2 * up(es * hm * 64 * 64) + up(es * hm * 32 * 64) + up(4 * hm)
+    for dt, extra in ((ck.BF16, common(2) + 2 * up(2 * hm * 32 * 32) + up(2 * hm * 32 * 64) + up(4 * hm * 2 * 32)),
+                      (ck.F32, common(4) + up(4 * min(hm, 512) * 14 * 32 * 64))):
         d = _desc(B=2, T=130, H=3, dk=64, dv=64, chunk_size=32, io_dtype=dt)
         fwd = lib.ckda_chunk_fwd_workspace_size(ctypes.byref(d), 0)
         bwd = lib.ckda_chunk_bwd_workspace_size(ctypes.byref(d), 0)
