@@ -129,6 +129,65 @@ def time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall * 1000.0 / steps
 
 
+def time_each(fn, steps, warmup, between=None):
+    """Per-launch times of `fn` (ms), each bracketed by its own pair of HIP
+    events on the current stream; `between` (untimed) runs before each one."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        if between is not None:
+            between()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def ceilings():
+    """Ceilings of this GPU measured in the same run: a plain device copy
+    (1 GiB read, 1 GiB written), in-place read-modify-writes of a 512 MiB and
+    a 2 GiB fp32 buffer (the decode step's access pattern, through torch's
+    element-wise kernel) and a dense bf16 GEMM of 8192^3 through torch (the
+    matrix cores as the vendor library reaches them)."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, device="cuda:0")
+    b = torch.empty_like(a)
+    ms_copy, _ = time_launches(lambda: b.copy_(a), 20, 3)
+    half = a[: n // 2]
+    ms_rmw, _ = time_launches(lambda: half.mul_(0.999), 20, 3)
+    del a, b, half
+    big = torch.ones(n * 2, device="cuda:0")
+    ms_rmw2, _ = time_launches(lambda: big.mul_(0.999), 10, 2)
+    del big
+    m = 8192
+    g = torch.Generator(device="cuda:0").manual_seed(9)
+    x = torch.randn((m, m), device="cuda:0", generator=g).to(torch.bfloat16)
+    y = torch.randn((m, m), device="cuda:0", generator=g).to(torch.bfloat16)
+    z = torch.empty((m, m), device="cuda:0", dtype=torch.bfloat16)
+    ms_mm, _ = time_launches(lambda: torch.matmul(x, y, out=z), 10, 3)
+    del x, y, z
+    torch.cuda.empty_cache()
+    copy = 2 * n * 4 / (ms_copy / 1000.0) / 1e9
+    rmw = 2 * (n // 2) * 4 / (ms_rmw / 1000.0) / 1e9
+    rmw2 = 2 * (2 * n) * 4 / (ms_rmw2 / 1000.0) / 1e9
+    mm = 2 * m ** 3 / (ms_mm / 1000.0) / 1e12
+    return {"copy_GBs": round(copy, 1), "copy_frac": round(copy / HBM_PEAK_GBS, 4),
+            "rmw_512MiB_GBs": round(rmw, 1), "rmw_512MiB_frac": round(rmw / HBM_PEAK_GBS, 4),
+            "rmw_2GiB_GBs": round(rmw2, 1), "rmw_2GiB_frac": round(rmw2 / HBM_PEAK_GBS, 4),
+            "bf16_gemm_8192_TFLOPs": round(mm, 1), "bf16_gemm_frac": round(mm / BF16_PEAK_TFLOPS, 4),
+            "what": "torch copy_ of 1 GiB fp32; torch mul_ in place on 512 MiB and on 2 GiB "
+                    "fp32 (back to back over 512 MiB, part of the buffer stays in the 256 MiB "
+                    "last-level cache; over 2 GiB it cannot); torch.matmul bf16 "
+                    "8192x8192x8192 (hipBLASLt)"}
+
+
 def fwd_plan(case, gate, sign_absorb=False):
     import torch
     import gated_delta_rule_ckda_amd as ck
@@ -144,7 +203,8 @@ def fwd_plan(case, gate, sign_absorb=False):
 
 def bench_fwd(case, steps, warmup, gate, passes=False, sign_absorb=False):
     """Whole forward per step (both passes, one ckda_chunk_fwd call on a
-    preallocated workspace); with passes=True also each pass alone."""
+    preallocated workspace); with passes=True also each pass alone, and with
+    passes="each" also the median and minimum of single pass launches."""
     import torch
     import gated_delta_rule_ckda_amd as ck
     plan = fwd_plan(case, gate, sign_absorb)
@@ -160,6 +220,11 @@ def bench_fwd(case, steps, warmup, gate, passes=False, sign_absorb=False):
     if passes:
         per["prep"], _ = time_launches(plan.prepare, steps, warmup)
         per["state"], _ = time_launches(plan.finish, steps, warmup)
+        if passes == "each":
+            for name, fn in (("prep", plan.prepare), ("state", plan.finish)):
+                t = sorted(time_each(fn, steps, 0))
+                per[name + "_median"] = t[len(t) // 2]
+                per[name + "_min"] = t[0]
     del plan, q, k, v, a, b, h0, cu
     torch.cuda.empty_cache()
     return ms, wall_ms, per
@@ -221,9 +286,19 @@ def bench_decode(steps_inner=64, reps=3):
     ms, _ = time_launches(run, reps, 1)
     per = ms / steps_inner
     nbytes = N * H * (2 * d * d * 4 + 3 * d * 2 + d * 4 + 4 + d * 2)
-    del st, toks
+    # the same steps with the 256 MiB last-level cache evicted before each
+    # one: a read-modify-write of a 1 GiB scratch buffer, untimed
+    scratch = torch.zeros(1 << 28, device="cuda:0")
+    it = iter(range(1 << 30))
+
+    def one():
+        q, k, v, a, b = toks[next(it) % steps_inner]
+        ck.recurrent_step(q, k, v, a, b, st, out=o)
+
+    cold = sorted(time_each(one, steps_inner, 0, between=lambda: scratch.add_(1.0)))
+    del st, toks, scratch
     torch.cuda.empty_cache()
-    return per, nbytes
+    return per, nbytes, {"median": cold[len(cold) // 2], "min": cold[0]}
 
 
 def cpu_baseline(case, pairs, scale=1.0, min_seconds=10.0):
@@ -249,7 +324,23 @@ def cpu_baseline(case, pairs, scale=1.0, min_seconds=10.0):
         runs.append(time.perf_counter() - t0)
     wall = sorted(runs)[len(runs) // 2]
     head_tokens = pairs * T
+    # one core on a smaller sample of the same pairs
+    p1 = max(1, pairs // 32)
+    oracle.set_num_threads(1)
+    runs1 = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.fwd(q[:p1], k[:p1], v[:p1], a[:p1], be[:p1], use_l2norm=case.l2norm, scale=scale)
+        runs1.append(time.perf_counter() - t0)
+    oracle.set_num_threads(threads)
+    wall1 = sorted(runs1)[1]
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
     return {"value": (head_tokens / H) / wall, "unit": "tokens/s", "cores": threads,
+            "one_core": {"value": (p1 * T / H) / wall1, "pairs": p1, "median_of": 3},
+            "os_cpu_count": os.cpu_count(), "nproc": nproc,
             "kind": "oracle",
             "sample": "%d of %d (batch, head) pairs x T=%d tokens of the same workload, fp64 "
                       "sequential recurrence on %d OpenMP threads; median of %d runs (%.2f s each, "
@@ -262,9 +353,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "lm", "bwd"], default="all",
+    ap.add_argument("--only", choices=["all", "lm", "bwd", "decode"], default="all",
                     help="'lm': only the headline workload and its passes; 'bwd': only the "
-                         "backward on the headline workload (both for profiling)")
+                         "backward on the headline workload; 'decode': only the decode steps "
+                         "(all three for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-pairs", type=int, default=128)
     args = ap.parse_args()
@@ -279,6 +371,13 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.only == "decode":
+        per, dbytes, cold = bench_decode()
+        print(json.dumps({"workload": "decode steps", "us_per_step": round(per * 1000.0, 2),
+                          "achieved_GBs": round(dbytes / (per / 1000.0) / 1e9, 1),
+                          "cold_us_median": round(cold["median"] * 1000.0, 2)}), flush=True)
+        return
+
     case = inputs.lm_layer(arm="ckda")
     B, T, H, dk = case.q.shape
     dv = case.v.shape[3]
@@ -288,7 +387,7 @@ def main():
         print(json.dumps({"workload": "backward of the LM layer", "ms_per_call": round(ms_bw, 3),
                           "steps": args.steps, "warmup": args.warmup}), flush=True)
         return
-    ms, wall_ms, per = bench_fwd(case, args.steps, args.warmup, "ckda", passes=True)
+    ms, wall_ms, per = bench_fwd(case, args.steps, args.warmup, "ckda", passes="each")
     tokens = B * T
     tok_s = tokens / (ms / 1000.0)
     nbytes = fwd_bytes(B, T, H, dk, dv, 2, B, False)
@@ -298,12 +397,15 @@ def main():
     names = {"prep": "prep_kernel<bf16, C=64, dk=128> (gate prefix, norms, UT/WY transform)",
              "state": "state_kernel<bf16, C=64, dk=dv=128, dv tile 64> (inter-chunk state + output)"}
     passes = {}
-    for kname, kms in per.items():
+    for kname in ("prep", "state"):
+        kms = per[kname]
         gbs = pbytes[kname] / (kms / 1000.0) / 1e9
         passes[kname] = {"kernel": names[kname], "ms": round(kms, 4),
+                         "ms_median": round(per[kname + "_median"], 4),
+                         "ms_min": round(per[kname + "_min"], 4),
                          "algorithmic_bytes": pbytes[kname], "achieved": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(kname)}
-    dom = max(per, key=per.get)
+    dom = max(("prep", "state"), key=lambda n: per[n])
     e2e_gbs = nbytes / (ms / 1000.0) / 1e9
 
     out = {
@@ -384,15 +486,27 @@ def main():
                          "ms_per_step": round(ms_vl, 4),
                          "hbm_frac": round(vl_bytes / (ms_vl / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
         del vl
-        per, dbytes = bench_decode()
+        per, dbytes, cold = bench_decode()
+        ceil = ceilings()
         out["decode"] = {"workload": "decode step 256 seqs x H=32 x d=128, bf16 q/k/v, fp32 state, "
                                      "64 in-place steps",
                          "us_per_step": round(per * 1000.0, 2),
                          "tokens_per_s": round(256 / (per / 1000.0), 1),
                          "achieved_GBs": round(dbytes / (per / 1000.0) / 1e9, 1),
-                         "hbm_frac": round(dbytes / (per / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+                         "hbm_frac": round(dbytes / (per / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                         "over_rmw_2GiB": round(dbytes / (per / 1000.0) / 1e9
+                                                / ceil["rmw_2GiB_GBs"], 4),
+                         "cold_cache": {
+                             "what": "each step alone after a 1 GiB read-modify-write that "
+                                     "evicts the last-level cache",
+                             "us_median": round(cold["median"] * 1000.0, 2),
+                             "us_min": round(cold["min"] * 1000.0, 2),
+                             "hbm_frac_median": round(dbytes / (cold["median"] / 1000.0) / 1e9
+                                                      / HBM_PEAK_GBS, 4)}}
+        out["ceilings"] = ceil
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_pairs)
+        out["cpu_baseline"]["gpu_over_cpu"] = round(tok_s / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 
