@@ -360,6 +360,9 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t qk_heads, int32_
     if (ptrs[i] && !aligned16(ptrs[i]))
       return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
   const int64_t nh = static_cast<int64_t>(N) * H;
+  if (nh > (int64_t(1) << 21))  // one launch of up to 2048 work-items per (sequence, head)
+    return fail(CKDA_ERR_UNSUPPORTED, "N*H = %lld exceeds 2^21 for one decode launch",
+                static_cast<long long>(nh));
   const int64_t nhk = static_cast<int64_t>(N) * qk_heads_of(H, qk_heads);
   const int64_t eb = elem_bytes(io_dtype);
   const int64_t gb = gate_bytes(gate_input);

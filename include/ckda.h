@@ -247,7 +247,8 @@ ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* desc, const void* q, const v
  * Hk = qk_heads (0 means H) as for ckda_chunk_fwd: value head h reads
  * query/key head h / (H / Hk).  alpha and beta hold what gate_input (a
  * ckda_gate_input_t) says.
- * Supported: dk, dv in {16, 32, 64, 128}, both io dtypes, every gate input.
+ * Supported: dk, dv in {16, 32, 64, 128}, both io dtypes, every gate input,
+ * N * H up to 2^21 (one launch; larger returns CKDA_ERR_UNSUPPORTED).
  */
 ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t qk_heads, int32_t dk,
                                   int32_t dv, int32_t io_dtype, int32_t gate_range,

@@ -218,6 +218,9 @@ def test_step_validation():
     assert st == 1 and "partially" in msg
     # N == 0 with valid arguments: ok, nothing enqueued
     assert _step(N=0)[0] == 0
+    # one launch covers at most 2^21 (sequence, head) states
+    st, msg = _step(N=(1 << 20) + 1, H=2)
+    assert st == 2 and "2^21" in msg
 
 
 def test_l2norm_debug_validation():
