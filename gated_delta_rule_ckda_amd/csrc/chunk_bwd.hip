@@ -1803,7 +1803,7 @@ template <class IO>
 __global__ __launch_bounds__(kNT) void bwd_token_kernel(BwdArgs b) {
   using ST = typename IO::storage;
   const FwdArgs& a = b.f;
-  const int C = a.chunk, dk = a.dk, dv = a.dv, H = a.H;
+  const int dk = a.dk, dv = a.dv, H = a.H;
   const int total = a.maxc * H;
   const bool l2 = a.use_l2norm != 0;
   const float scale = a.scale;

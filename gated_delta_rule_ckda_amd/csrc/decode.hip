@@ -58,7 +58,7 @@ template <class IO, int DK, int DV>
 __global__ __launch_bounds__((StepShape<DK, DV>::NT), (StepShape<DK, DV>::MINW)) void step_kernel(StepArgs a) {
   using SH = StepShape<DK, DV>;
   constexpr int DVS = SH::DVS, NS = SH::NS, CG = SH::CG, RW = SH::RW, NW = SH::NW, RB = SH::RB,
-                RPT = SH::RPT, NT = SH::NT;
+                RPT = SH::RPT;
   using T = typename IO::storage;
 
   __shared__ float s_q[DK], s_k[DK], s_a[DK];
