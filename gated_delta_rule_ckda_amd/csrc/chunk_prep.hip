@@ -881,14 +881,25 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   }
 }
 
-// The transform pass: one workgroup per (chunk, head); blocks of one chunk
-// and consecutive heads are adjacent.
+// The transform pass: one workgroup per (chunk, head); workgroups of one
+// chunk and consecutive heads are adjacent.  In a batch the chunks go by
+// position in their sequence from last to first (every sequence and head of
+// one position together), so the blocks written last, which the last-level
+// cache still holds when the state pass starts, are the first chunks of
+// every chain: the ones the state pass reads first.  Packed sequences keep
+// the order of their chunk slots.
 template <class Cfg, class G>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) void prep_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int H = a.H;
-  prep_chunk<Cfg, G, false>(a, static_cast<int>(blockIdx.x / H), static_cast<int>(blockIdx.x % H),
-                            smem);
+  const int b = static_cast<int>(blockIdx.x);
+  if (a.cu_seqlens) {
+    prep_chunk<Cfg, G, false>(a, b / H, b % H, smem);
+  } else {
+    const int per = a.B * H;  // workgroups per chunk position
+    const int i = a.nc - 1 - b / per, n = (b % per) / H;
+    prep_chunk<Cfg, G, false>(a, n * a.nc + i, b % H, smem);
+  }
 }
 
 // The chunks the transform pass flagged as not regular (exact zero gates, or
