@@ -448,9 +448,9 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int row = iclamp(r0 + i, L - 1);
-        ldraw<Cfg::QB>(rq, c0ch * ES + row * krow, rqv[i]);
-        ldraw<Cfg::QB>(rk, c0ch * ES + row * krow, rkv[i]);
-        ldraw<GB>(ra, c0ch * GES + row * arow, rav[i]);
+        ldraw<Cfg::QB, kStream>(rq, c0ch * ES + row * krow, rqv[i]);
+        ldraw<Cfg::QB, kStream>(rk, c0ch * ES + row * krow, rkv[i]);
+        ldraw<GB, kStream>(ra, c0ch * GES + row * arow, rav[i]);
       }
     }
     if (tid < C) sbeta[tid] = (tid < L) ? load_beta<G>(a.beta, (t0 + tid) * H + h, ckda) : 0.f;

@@ -22,11 +22,17 @@
 // the state waves wait at a barrier, so HBM latency overlaps the arithmetic.
 // They also write the outputs: the state waves leave a chunk's O tile in LDS
 // and the loaders store it one chunk later as whole rows of the dv tile (16
-// bytes per thread) rather than 32-byte pieces from each state wave.
+// bytes per thread, non-temporal) rather than 32-byte pieces from each state
+// wave.
 #include "mfma_ops.h"
 
 namespace ckda {
 namespace {
+
+// 16 bytes of the output, stored with the non-temporal hint: o is not read
+// again here, and plain stores would displace the workspace blocks the pass
+// still reads from the last-level cache.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <class OpT, class IOT, int C_, int DK_, int DV_, int DVT_>
 struct StateCfg {
@@ -374,10 +380,11 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
         const int p = lt + Cfg::NLT * u;
         const int r = p / PR, cp = p % PR;
         if ((NOP % Cfg::NLT == 0 || p < NOP) && r < L) {
-          const uint4 val = *reinterpret_cast<const uint4*>(smem + Cfg::O_O + r * Cfg::LDO + 16 * cp);
-          *reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.o) +
-                                    (((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0) * Cfg::IOES +
-                                    16 * cp) = val;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(smem + Cfg::O_O + r * Cfg::LDO + 16 * cp);
+          __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(
+                                               static_cast<unsigned char*>(a.o) +
+                                               (((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0) * Cfg::IOES +
+                                               16 * cp));
         }
       }
     };
@@ -433,9 +440,11 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
     for (int p = lt; p < NOP; p += Cfg::NLT) {
       const int r = p / PR, cp = p % PR;
       if (r < L)
-        *reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.o) +
-                                  (((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0) * Cfg::IOES +
-                                  16 * cp) = *reinterpret_cast<const uint4*>(smem + Cfg::O_O + r * Cfg::LDO + 16 * cp);
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(smem + Cfg::O_O + r * Cfg::LDO + 16 * cp),
+            reinterpret_cast<u32x4*>(static_cast<unsigned char*>(a.o) +
+                                     (((t0 + r) * H + h) * static_cast<int64_t>(a.dv) + dv0) * Cfg::IOES +
+                                     16 * cp));
     }
   }
 

@@ -207,19 +207,24 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int num_bytes) {
                                            num_bytes, kRsrcWord3);
 }
 
-template <int BYTES>
+// Cache policy of a buffer load: kStream marks data read once (the gfx950
+// "nt" bit), so streamed inputs do not displace lines that are read again
+// soon (the workspace blocks the transform pass hands to the state pass).
+constexpr int kCached = 0, kStream = 2;
+
+template <int BYTES, int CPOL = kCached>
 __device__ __forceinline__ void ldraw(rsrc_t r, int voff, uint32_t* d) {
   if constexpr (BYTES == 2) {
-    d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+    d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, CPOL);
   } else if constexpr (BYTES == 4) {
-    d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, CPOL);
   } else if constexpr (BYTES == 8) {
-    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, CPOL);
     d[0] = u[0];
     d[1] = u[1];
   } else {
     static_assert(BYTES == 16, "load width");
-    const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, CPOL);
     d[0] = u[0]; d[1] = u[1]; d[2] = u[2]; d[3] = u[3];
   }
 }
