@@ -1,0 +1,74 @@
+"""Host logic of bench.py: the one-GPU contract, the algorithmic byte and
+flop counts of the LM-layer workload, and the traffic keys of the committed
+counter summary.  No GPU is used."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import gated_delta_rule_ckda_amd as ck  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_lm_layer_algorithmic_bytes_and_flops():
+    # q, k, v read once (bf16), alpha (fp32, one per key channel) and beta
+    # read once, o written once (bf16), ht written once (fp32), no h0
+    B, T, H, d = 8, 4096, 16, 128
+    tok = B * T * H
+    expect = tok * 3 * d * 2 + tok * d * 4 + tok * 4 + tok * d * 2 + B * H * d * d * 4
+    assert bench.fwd_bytes(B, T, H, d, d, 2, B, False) == expect == 815792128
+    # chunked-form flops: 73.93 GFLOP over the 8192 chunk-heads of the layer
+    total = bench.chunk_flops(64, d, d) * (B * T // 64) * H
+    assert abs(total / 1e9 - 73.93) < 0.01
+
+
+def test_pass_bytes_match_the_library_block_size():
+    """The transform pass's algorithmic bytes count one block per chunk-head;
+    the block size bench.py uses must be the one the library lays out (the
+    workspace is the blocks plus a 256-byte-aligned flag word per slot)."""
+    B, T, H, d, C = 8, 4096, 16, 128, 64
+    blk = bench.block_bytes(C, d, 2)
+    assert blk == 66048
+    desc = ck.FwdDesc(B, T, H, d, d, B, C, ck.BF16, ck.GATE_CKDA, 1, 1.0, ck.GATES_F32, H, 0)
+    maxc = B * (T // C)
+    flags = -(-(4 * H * maxc) // 256) * 256
+    assert ck.chunk_fwd_workspace_size(desc, False) == flags + H * maxc * blk
+    pb = bench.pass_bytes(B, T, H, d, d, C, 2, B, False)
+    tok = B * T * H
+    assert pb["prep"] == tok * (2 * d * 2 + (d + 1) * 4) + maxc * H * blk
+    assert pb["state"] == maxc * H * blk + tok * d * 2 * 2 + B * H * d * d * 4
+
+
+def test_traffic_keys_follow_the_sources(tmp_path, monkeypatch):
+    # the committed summary matches the current sources of both passes
+    for name in ("prep", "state"):
+        t = bench.load_traffic(name)
+        assert t is not None and t > 0, name
+    # a summary taken on other sources is not used
+    text = open(bench.TRAFFIC_FILE).read().replace(
+        "prep.src_sha256_16 = " + bench.src_hash(bench.PASS_SOURCES["prep"]),
+        "prep.src_sha256_16 = 0000000000000000")
+    f = tmp_path / "traffic.txt"
+    f.write_text(text)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.load_traffic("prep") is None
+    assert bench.load_traffic("state") is not None
+
+
+@pytest.mark.parametrize("arg", ["--steps", "--warmup"])
+def test_bench_flags_parse(arg):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), arg, "x"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "invalid int value" in r.stderr
