@@ -949,10 +949,12 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // Chunk map of a packed batch: first[n] = sum over m < n of ceil(len_m / C),
 // first[N] = the chunk count, chunk_seq[c] = the sequence owning chunk c (or
-// -1 for c >= first[N]).  One workgroup; a block-wide scan per 1024 sequences.
+// -1 for c >= first[N]), seq_order = the sequences by chunk count, most
+// first (the order the state pass starts their chains in).  One workgroup; a
+// block-wide scan per 1024 sequences.
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* cu, int32_t N, int32_t C,
                                                          int32_t maxc, int32_t* first,
-                                                         int32_t* chunk_seq) {
+                                                         int32_t* chunk_seq, int32_t* seq_order) {
   __shared__ int32_t part[1024];
   __shared__ int32_t carry_s;
   const int tid = threadIdx.x;
@@ -993,6 +995,23 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* cu, int3
       owner = lo;
     }
     chunk_seq[c] = owner;
+  }
+  // sequences by chunk count, most first (ties by index): rank of n among
+  // all sequences.  Past kOrderMax sequences the quadratic ranking is not
+  // worth its time and the order stays the identity.
+  constexpr int kOrderMax = 4096;
+  for (int n = tid; n < N; n += 1024) {
+    if (N > kOrderMax) {
+      seq_order[n] = n;
+      continue;
+    }
+    const int cn = first[n + 1] - first[n];
+    int rank = 0;
+    for (int j = 0; j < N; ++j) {
+      const int cj = first[j + 1] - first[j];
+      rank += (cj > cn) || (cj == cn && j < n);
+    }
+    seq_order[rank] = n;
   }
 }
 
@@ -1073,7 +1092,7 @@ launch_result launch_prep(const FwdArgs& a, int32_t io_dtype, hipStream_t stream
 
 launch_result launch_chunk_map(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.num_seqs,
-                     a.chunk, a.maxc, a.first, a.chunk_seq);
+                     a.chunk, a.maxc, a.first, a.chunk_seq, a.seq_order);
   return hipGetLastError();
 }
 

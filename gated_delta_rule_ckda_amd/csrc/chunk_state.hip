@@ -236,7 +236,9 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
     split = static_cast<int>(b % Cfg::NSPLIT);
   }
   const int H = a.H;
-  const int n = static_cast<int>(pair / H);
+  // packed sequences go out longest first, so the chains that decide when
+  // the pass ends start first and the short ones fill in behind them
+  const int n = a.cu_seqlens ? uniform32(a.seq_order[pair / H]) : static_cast<int>(pair / H);
   const int h = static_cast<int>(pair % H);
   int64_t s0;
   int c_begin, nch;
@@ -522,7 +524,7 @@ size_t fwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t 
                            int32_t chunk, int32_t io_dtype, bool packed, bool sign_absorb) {
   const int64_t maxc = max_chunks(B, T, num_seqs, chunk, packed);
   const int64_t es = io_dtype == CKDA_DTYPE_BF16 ? 2 : 4;
-  const int64_t map = packed ? ((4 * (num_seqs + 1 + maxc) + 255) & ~int64_t(255)) : 0;
+  const int64_t map = packed ? ((4 * (2 * int64_t(num_seqs) + 1 + maxc) + 255) & ~int64_t(255)) : 0;
   const int64_t flags = (4 * static_cast<int64_t>(H) * maxc + 255) & ~int64_t(255);
   const int64_t sign = sign_absorb ? sign_workspace_bytes(B, T, H, dk, num_seqs, maxc, io_dtype) : 0;
   return static_cast<size_t>(map + flags + static_cast<int64_t>(H) * maxc * blk_bytes(chunk, dk, es) +
@@ -549,10 +551,12 @@ unsigned char* fwd_layout(FwdArgs& a, int32_t io_dtype, void* ws) {
   a.blk_bytes = blk_bytes(a.chunk, a.dk, es);
   a.first = nullptr;
   a.chunk_seq = nullptr;
+  a.seq_order = nullptr;
   if (packed) {
     a.first = reinterpret_cast<int32_t*>(base);
     a.chunk_seq = a.first + a.num_seqs + 1;
-    base += (4 * (a.num_seqs + 1 + maxc) + 255) & ~int64_t(255);
+    a.seq_order = a.chunk_seq + maxc;
+    base += (4 * (2 * int64_t(a.num_seqs) + 1 + maxc) + 255) & ~int64_t(255);
   }
   a.irregular = reinterpret_cast<int32_t*>(base);
   base += (4 * static_cast<int64_t>(a.H) * maxc + 255) & ~int64_t(255);

@@ -85,6 +85,7 @@ struct FwdArgs {
   unsigned char* blocks;  // [H][maxc] blocks of blk_bytes
   int32_t* first;         // [num_seqs + 1] first chunk of each sequence (packed batches)
   int32_t* chunk_seq;     // [maxc] sequence owning each chunk slot, -1 if unused (packed)
+  int32_t* seq_order;     // [num_seqs] packed sequences by chunk count, most first (state pass)
   int32_t* irregular;     // [H][maxc] 1 where the transform pass left a chunk to the direct kernel
   int32_t maxc;           // chunk slots per head
   int32_t nc;             // chunks per sequence (dense batches)

@@ -52,19 +52,18 @@ def test_pass_bytes_match_the_library_block_size():
 
 
 def test_traffic_keys_follow_the_sources(tmp_path, monkeypatch):
-    # the committed summary matches the current sources of both passes
-    for name in ("prep", "state"):
-        t = bench.load_traffic(name)
-        assert t is not None and t > 0, name
-    # a summary taken on other sources is not used
-    text = open(bench.TRAFFIC_FILE).read().replace(
-        "prep.src_sha256_16 = " + bench.src_hash(bench.PASS_SOURCES["prep"]),
-        "prep.src_sha256_16 = 0000000000000000")
+    """A pass's counter bytes are used only while the summary's key matches
+    the hash of that pass's current sources."""
     f = tmp_path / "traffic.txt"
-    f.write_text(text)
+    f.write_text("# counters\n"
+                 "prep.src_sha256_16 = %s\nprep.hbm_bytes_per_launch = 1234\n"
+                 "state.src_sha256_16 = 0000000000000000\nstate.hbm_bytes_per_launch = 5678\n"
+                 % bench.src_hash(bench.PASS_SOURCES["prep"]))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.load_traffic("prep") == 1234.0
+    assert bench.load_traffic("state") is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
     assert bench.load_traffic("prep") is None
-    assert bench.load_traffic("state") is not None
 
 
 @pytest.mark.parametrize("arg", ["--steps", "--warmup"])
