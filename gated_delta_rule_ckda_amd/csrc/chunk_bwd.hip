@@ -425,7 +425,9 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
     split = static_cast<int>(bi % Cfg::NSPLIT);
   }
   const int H = a.H, dv = a.dv;
-  const int n = static_cast<int>(pair / H), h = static_cast<int>(pair % H);
+  // packed sequences longest first, as in the forward's state pass
+  const int n = a.cu_seqlens ? uniform32(a.seq_order[pair / H]) : static_cast<int>(pair / H);
+  const int h = static_cast<int>(pair % H);
   int64_t s0;
   int c_begin, nch;
   if (a.cu_seqlens) {
