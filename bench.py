@@ -66,16 +66,22 @@ def block_bytes(C, dk, es):
 
 
 def pass_bytes(B, T, H, dk, dv, C, io_bytes, nseq, h0, gate_bytes=4):
-    """Algorithmic bytes per launch of each pass: its inputs read once and its
-    outputs written once.  The transform pass reads q, k, alpha, beta and
-    writes one block per chunk-head; the state pass reads the blocks, v (and
-    h0) and writes o and ht."""
+    """Algorithmic bytes per launch of each pass: the method's inputs it
+    reads, once each, and the method's outputs it writes, once each; the
+    workspace blocks the transform pass hands to the state pass are the
+    implementation's own traffic and are not counted (they are reported apart,
+    see workspace_bytes).  The transform pass reads q, k, alpha, beta; the
+    state pass reads v (and h0) and writes o and ht."""
     tok = B * T
-    nblk = B * (-(-T // C)) * H
-    blocks = nblk * block_bytes(C, dk, io_bytes)
-    prep = tok * H * (2 * dk * io_bytes + (dk + 1) * gate_bytes) + blocks
-    state = blocks + tok * H * dv * io_bytes * 2 + nseq * H * dk * dv * 4 * (2 if h0 else 1)
+    prep = tok * H * (2 * dk * io_bytes + (dk + 1) * gate_bytes)
+    state = tok * H * dv * io_bytes * 2 + nseq * H * dk * dv * 4 * (2 if h0 else 1)
     return {"prep": prep, "state": state}
+
+
+def workspace_bytes(B, T, H, dk, C, io_bytes):
+    """Bytes of the blocks the transform pass writes and the state pass reads
+    back (one per chunk-head): traffic beyond the algorithmic bytes."""
+    return B * (-(-T // C)) * H * block_bytes(C, dk, io_bytes)
 
 
 def src_hash(names):
@@ -204,7 +210,9 @@ def fwd_plan(case, gate, sign_absorb=False):
 def bench_fwd(case, steps, warmup, gate, passes=False, sign_absorb=False):
     """Whole forward per step (both passes, one ckda_chunk_fwd call on a
     preallocated workspace); with passes=True also each pass alone, and with
-    passes="each" also the median and minimum of single pass launches."""
+    passes="each" also the median and minimum of single pass launches and the
+    sorted times of single forward steps, each after the last-level cache was
+    evicted ("cold")."""
     import torch
     import gated_delta_rule_ckda_amd as ck
     plan = fwd_plan(case, gate, sign_absorb)
@@ -217,6 +225,10 @@ def bench_fwd(case, steps, warmup, gate, passes=False, sign_absorb=False):
 
     ms, wall_ms = time_launches(step, steps, warmup)
     per = {}
+    if passes == "each":
+        scratch = torch.zeros(1 << 28, device="cuda:0")
+        per["cold"] = sorted(time_each(step, steps, 0, between=lambda: scratch.add_(1.0)))
+        del scratch
     if passes:
         per["prep"], _ = time_launches(plan.prepare, steps, warmup)
         per["state"], _ = time_launches(plan.finish, steps, warmup)
@@ -394,19 +406,28 @@ def main():
     flops = chunk_flops(C, dk, dv) * (B * T // C) * H
     tflops = flops / (ms / 1000.0) / 1e12
     pbytes = pass_bytes(B, T, H, dk, dv, C, 2, B, False)
+    wbytes = workspace_bytes(B, T, H, dk, C, 2)
     names = {"prep": "prep_kernel<bf16, C=64, dk=128> (gate prefix, norms, UT/WY transform)",
              "state": "state_kernel<bf16, C=64, dk=dv=128, dv tile 64> (inter-chunk state + output)"}
+    what = {"prep": "q, k (bf16), alpha, beta (fp32) read once",
+            "state": "v read once (bf16), o written once (bf16), ht written once (fp32)"}
     passes = {}
     for kname in ("prep", "state"):
         kms = per[kname]
         gbs = pbytes[kname] / (kms / 1000.0) / 1e9
+        tr = load_traffic(kname)
         passes[kname] = {"kernel": names[kname], "ms": round(kms, 4),
                          "ms_median": round(per[kname + "_median"], 4),
                          "ms_min": round(per[kname + "_min"], 4),
-                         "algorithmic_bytes": pbytes[kname], "achieved": round(gbs, 1),
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(kname)}
+                         "algorithmic_bytes": pbytes[kname], "algorithmic": what[kname],
+                         "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "workspace_bytes": wbytes,
+                         "traffic": tr,
+                         "traffic_over_algorithmic": (None if tr is None
+                                                      else round(tr / pbytes[kname], 3))}
     dom = max(("prep", "state"), key=lambda n: per[n])
     e2e_gbs = nbytes / (ms / 1000.0) / 1e9
+    cold = per["cold"]
 
     out = {
         "metric": "chunked CKDA fwd tokens/s + TFLOP/s (% MFMA peak), H=16 d=128 T=4096 bf16",
@@ -433,6 +454,11 @@ def main():
                      "end_to_end": {"algorithmic_bytes": nbytes, "achieved": round(e2e_gbs, 1),
                                     "frac": round(e2e_gbs / HBM_PEAK_GBS, 4)},
                      "wall_ms_per_step": round(wall_ms, 4)},
+        "cold_cache": {"what": "each forward step alone, after a 1 GiB read-modify-write that "
+                               "evicts the 256 MiB last-level cache (untimed)",
+                       "steps": len(cold), "ms_median": round(cold[len(cold) // 2], 4),
+                       "ms_min": round(cold[0], 4),
+                       "tokens_per_s_median": round(tokens / (cold[len(cold) // 2] / 1000.0), 1)},
     }
 
     if args.only == "all":

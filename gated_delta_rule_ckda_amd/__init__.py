@@ -24,7 +24,8 @@ _lib = None
 BF16, F32 = 0, 1
 GATE_KDA, GATE_CKDA = 0, 1
 GATES_F32, GATES_LOGITS_F32, GATES_LOGITS_BF16 = 0, 1, 2
-_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error"}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
+           4: "HIP error"}
 
 
 class CkdaError(RuntimeError):

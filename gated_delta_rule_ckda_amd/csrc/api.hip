@@ -76,6 +76,7 @@ const char* ckda_status_string(int32_t s) {
     case CKDA_OK: return "ok";
     case CKDA_ERR_INVALID_ARGUMENT: return "invalid argument";
     case CKDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case CKDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case CKDA_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
@@ -190,7 +191,7 @@ ckda_status_t validate_fwd(const ckda_fwd_desc_t* d, const void* q, const void* 
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
     if (workspace_bytes < need)
-      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed",
+      return fail(CKDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed",
                   workspace_bytes, need);
     const Range rw = range("workspace", workspace, static_cast<int64_t>(need));
     if (overlap(rw, ro)) return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace overlaps o");
@@ -272,7 +273,7 @@ ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
     if (workspace_bytes < need)
-      return fail(CKDA_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, %zu needed",
+      return fail(CKDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed",
                   workspace_bytes, need);
     const Range rw = range("workspace", workspace, static_cast<int64_t>(need));
     for (const Range& r : ins)

@@ -199,8 +199,10 @@ __global__ __launch_bounds__(64) void l2norm_debug_kernel(const void* xv, float*
       ss += e * e;
     }
     ss = wave_sum(ss);
-    const float n = __fsqrt_rn(ss + kL2Eps);
-    for (int i = threadIdx.x; i < d; i += 64) y[r * d + i] = __fdiv_rn(IO::load(x, r * d + i), n);
+    // one reciprocal per row, then a multiply per element: the arithmetic
+    // of the row scales in the transform pass and the decode step
+    const float rn = __fdiv_rn(1.f, __fsqrt_rn(ss + kL2Eps));
+    for (int i = threadIdx.x; i < d; i += 64) y[r * d + i] = IO::load(x, r * d + i) * rn;
   }
 }
 

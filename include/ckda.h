@@ -50,13 +50,14 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 7
+#define CKDA_ABI_VERSION 8
 
 typedef enum {
   CKDA_OK = 0,
   CKDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, aliasing */
   CKDA_ERR_UNSUPPORTED = 2,      /* valid arguments this build has no kernel for */
-  CKDA_ERR_HIP = 3               /* the HIP runtime reported an error at launch */
+  CKDA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the size the query returns */
+  CKDA_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
 } ckda_status_t;
 
 typedef enum {
@@ -153,6 +154,12 @@ size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed
  * may be the same buffer (the state is read before it is written).  o must not
  * overlap any input.
  *
+ * The chunked form computes exactly the recurrence above (up to rounding): a
+ * chunk of C tokens entered with state S0 is one UT/WY step, the form of the
+ * chunked KDA arm the dormouse review names (section 1: the layer's chunk
+ * arm; section 6: the chunked WY comparison, whose zero-padded partial last
+ * chunk this equals, padding tokens being identity transitions).
+ *
  * Two passes run on `stream`: a transform pass over all chunks in parallel
  * (gate prefix, norms, the chunk's UT/WY transform), which writes each chunk's
  * operands into `workspace`, then a state pass that walks every
@@ -163,7 +170,9 @@ size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed
  * least ckda_chunk_fwd_workspace_size(desc, cu_seqlens != NULL) bytes,
  * 256-byte aligned, owned by the caller, not overlapping any argument; its
  * contents are scratch (undefined before and after the call).  Calls that
- * share a workspace must be ordered on one stream.
+ * share a workspace must be ordered on one stream.  A workspace_bytes below
+ * the query's size returns CKDA_ERR_WORKSPACE_TOO_SMALL; a NULL, misaligned
+ * or overlapping workspace returns CKDA_ERR_INVALID_ARGUMENT.
  *
  * Supported shapes (others return CKDA_ERR_UNSUPPORTED):
  *   bf16 : dk = dv = 128 with chunk_size 16, 32 or 64; dk = dv = 64 with 16, 32, 64
@@ -179,7 +188,11 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
 /*
  * The two passes of ckda_chunk_fwd as separate calls, for callers that time
  * them, or that let the transform pass of one batch run ahead of the state
- * pass of another.  ckda_chunk_fwd_prepare runs the transform pass and leaves
+ * pass of another.  The split is the chunked form's own: everything that does
+ * not depend on the state entering a chunk (gate products, norms, the UT/WY
+ * inverse of the chunked WY form, dormouse review section 6) is the prepare step,
+ * and the walk of the state over the chunks (the recurrence of section
+ * "Background", one chunk at a time) is the finish step.  ckda_chunk_fwd_prepare runs the transform pass and leaves
  * every chunk's operands in `workspace`; ckda_chunk_fwd_finish runs the state
  * pass from a workspace that a prepare call with the same descriptor and
  * cu_seqlens filled (on the same stream, or otherwise ordered before it), and
@@ -239,8 +252,12 @@ ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* desc, const void* q, const v
                              size_t workspace_bytes, void* stream);
 
 /*
- * Fused single-token decode step for N sequences (the recurrent form of the
- * same recurrence, one token per sequence):
+ * Fused single-token decode step for N sequences: the recurrent form of the
+ * same recurrence, one token per sequence (picx.dev summary, section
+ * "Background", the transition A_t applied to the cached state, then the
+ * write and the read-out; the dormouse review, section 1, describes the
+ * recurrent arm beside the chunked one and its returned recurrent state):
+ *   S <- (I - beta k^ k^T) Diag(alpha) S + beta k^ v^T,   o = scale S^T q^
  *   q, k : [N][Hk][dk]   alpha : [N][H][dk]   v, o : [N][H][dv]   beta : [N][H]
  *   h0, ht      : [N][H][dk][dv] float32; h0 == ht (in place) is allowed,
  *                 other partial overlaps are not.
@@ -259,9 +276,14 @@ ckda_status_t ckda_recurrent_step(int32_t N, int32_t H, int32_t qk_heads, int32_
                                   void* stream);
 
 /*
- * Test export of the in-kernel normalisation: y[r][:] = x[r][:] /
- * sqrt(sum_c x[r][c]^2 + 1e-6) in float32 with IEEE sqrt and division, for
+ * Test export of the in-kernel normalisation of q and k (dormouse review
+ * "RoPE into the KDA q/k path", section 2: per head over the key channels):
+ * y[r][:] = x[r][:] * (1 / sqrt(sum_c x[r][c]^2 + 1e-6)), in float32, with
+ * IEEE sqrt and division and the same order of operations as the chunked and
+ * decode kernels (one reciprocal per row, then a multiply per element), for
  * `rows` rows of d values (x in io dtype `dtype`, y float32).  d <= 1024.
+ * Returns CKDA_ERR_INVALID_ARGUMENT for d outside [1, 1024], a NULL or
+ * misaligned pointer, or y overlapping x.
  */
 ckda_status_t ckda_l2norm_debug(const void* x, float* y, int64_t rows,
                                 int32_t d, int32_t dtype, void* stream);

@@ -59,10 +59,25 @@ def oracle_gates(case, a, b):
     return a, b
 
 
+def cover_pairs(N, H, extra=()):
+    """(sequence, head) pairs in which every sequence index and every head
+    index appears at least once: max(N, H) pairs, head (5 i + 3) mod H with
+    sequence i mod N (5 is odd, so for a power-of-two H the heads are a
+    permutation), plus `extra`."""
+    n = max(N, H)
+    step = 5 if np.gcd(5, H) == 1 else 1
+    pairs = [(i % N, (step * i + 3) % H) for i in range(n)]
+    for p in extra:
+        if p not in pairs:
+            pairs.append(p)
+    return pairs
+
+
 def oracle_pairs(case, pairs, scale=1.0):
     """Oracle on selected (sequence, head) pairs of a case; returns
     {(n,h): (o [T_n, dv], ht [dk, dv])}.  Pairs are independent, so this is the
-    exact reference for those outputs."""
+    exact reference for those outputs.  All pairs go to the oracle in one
+    packed call (one sequence per pair, one head), which it runs in parallel."""
     import oracle
     out = {}
     if case.cu_seqlens is None:
@@ -72,12 +87,20 @@ def oracle_pairs(case, pairs, scale=1.0):
     else:
         starts = case.cu_seqlens.astype(np.int64)
         q, k, v, a, b = (x[0] for x in (case.q, case.k, case.v, case.alpha, case.beta))
-    for (n, h) in pairs:
-        s0, s1 = int(starts[n]), int(starts[n + 1])
-        ga, gb = oracle_gates(case, a[s0:s1, h:h + 1], b[s0:s1, h:h + 1])
-        h0 = None if case.h0 is None else case.h0[n:n + 1, h:h + 1]
-        o, ht = oracle.fwd(q[None, s0:s1, h:h + 1], k[None, s0:s1, h:h + 1],
-                           v[None, s0:s1, h:h + 1], ga[None], gb[None], h0=h0,
-                           use_l2norm=case.l2norm, scale=scale)
-        out[(n, h)] = (o[0, :, 0], ht[0, 0])
+    pairs = list(pairs)
+    segs = [(int(starts[n]), int(starts[n + 1]), h) for n, h in pairs]
+
+    def cat(x):
+        return np.concatenate([x[s0:s1, h:h + 1] for s0, s1, h in segs], 0)[None]
+
+    qs, ks, vs, as_, bs = (cat(x) for x in (q, k, v, a, b))
+    ga, gb = oracle_gates(case, as_, bs)
+    seq_start = np.concatenate([[0], np.cumsum([s1 - s0 for s0, s1, _ in segs])]).astype(np.int64)
+    h0 = None
+    if case.h0 is not None:
+        h0 = np.stack([case.h0[n, h:h + 1] for n, h in pairs], 0)
+    o, ht = oracle.fwd(qs, ks, vs, ga, gb, h0=h0, seq_start=seq_start,
+                       use_l2norm=case.l2norm, scale=scale)
+    for i, p in enumerate(pairs):
+        out[p] = (o[0, seq_start[i]:seq_start[i + 1], 0], ht[i, 0])
     return out

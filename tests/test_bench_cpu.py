@@ -34,21 +34,32 @@ def test_lm_layer_algorithmic_bytes_and_flops():
     assert abs(total / 1e9 - 73.93) < 0.01
 
 
-def test_pass_bytes_match_the_library_block_size():
-    """The transform pass's algorithmic bytes count one block per chunk-head;
-    the block size bench.py uses must be the one the library lays out (the
-    workspace is the blocks plus a 256-byte-aligned flag word per slot)."""
+def test_pass_bytes_are_the_method_bytes_only():
+    """Each pass's algorithmic bytes are the method's inputs it reads once and
+    the method's outputs it writes once: the transform pass q, k, alpha,
+    beta; the state pass v, o, ht.  The blocks one pass hands to the other
+    are workspace, reported apart, and their size is the one the library
+    lays out (the workspace is the blocks plus a 256-byte-aligned flag word
+    per slot)."""
     B, T, H, d, C = 8, 4096, 16, 128, 64
+    pb = bench.pass_bytes(B, T, H, d, d, C, 2, B, False)
+    assert pb["prep"] == 538968064      # q, k bf16; alpha fp32 per channel; beta fp32
+    assert pb["state"] == 276824064     # v, o bf16; ht fp32
+    # the two passes together are the whole forward's algorithmic bytes
+    assert pb["prep"] + pb["state"] == bench.fwd_bytes(B, T, H, d, d, 2, B, False)
+    # with h0 the state pass also reads it; bf16 logits halve alpha's bytes
+    assert bench.pass_bytes(B, T, H, d, d, C, 2, B, True)["state"] == 276824064 + B * H * d * d * 4
+    tok = B * T * H
+    assert bench.pass_bytes(B, T, H, d, d, C, 2, B, False, gate_bytes=2)["prep"] == \
+        tok * (2 * d * 2 + (d + 1) * 2)
     blk = bench.block_bytes(C, d, 2)
     assert blk == 66048
     desc = ck.FwdDesc(B, T, H, d, d, B, C, ck.BF16, ck.GATE_CKDA, 1, 1.0, ck.GATES_F32, H, 0)
     maxc = B * (T // C)
     flags = -(-(4 * H * maxc) // 256) * 256
-    assert ck.chunk_fwd_workspace_size(desc, False) == flags + H * maxc * blk
-    pb = bench.pass_bytes(B, T, H, d, d, C, 2, B, False)
-    tok = B * T * H
-    assert pb["prep"] == tok * (2 * d * 2 + (d + 1) * 4) + maxc * H * blk
-    assert pb["state"] == maxc * H * blk + tok * d * 2 * 2 + B * H * d * d * 4
+    ws = bench.workspace_bytes(B, T, H, d, C, 2)
+    assert ws == H * maxc * blk == 541065216
+    assert ck.chunk_fwd_workspace_size(desc, False) == flags + ws
 
 
 def test_traffic_keys_follow_the_sources(tmp_path, monkeypatch):

@@ -8,7 +8,7 @@ import torch
 import gated_delta_rule_ckda_amd as ck
 import oracle
 from gated_delta_rule_ckda_amd import inputs
-from tests.gpu_util import (DEV, TOL, announce, dev, host, max_rel_err, oracle_gates,
+from tests.gpu_util import (DEV, TOL, announce, cover_pairs, dev, host, max_rel_err, oracle_gates,
                             oracle_pairs, run_chunk)
 from tests.test_gpu_decode import pow2_rows
 
@@ -86,12 +86,13 @@ def test_orthogonal_norm_preserved():
 @pytest.mark.parametrize("arm", ["ckda", "kda"])
 def test_lm_layer_workload_full_sampled(arm):
     """B=8 H=16 T=4096 d=128 bf16 chunk 64 at full size, in the benchmark's
-    launch configuration; oracle on 6 sampled (batch, head) pairs."""
+    launch configuration; oracle on 16 sampled (batch, head) pairs that cover
+    every batch index and every head index."""
     announce("LM layer workload full size, %s arm" % arm)
     c = inputs.lm_layer(arm=arm)
     o, ht = run_chunk(c, gate=arm)
     o = o.reshape(c.v.shape)
-    pairs = [(0, 0), (7, 15), (3, 9), (5, 2), (1, 14), (6, 7)]
+    pairs = cover_pairs(8, 16, extra=[(0, 0), (7, 15)])
     ref = oracle_pairs(c, pairs)
     worst_o = max(max_rel_err(o[n, :, h], ref[(n, h)][0]) for n, h in pairs)
     worst_h = max(max_rel_err(ht[n, h], ref[(n, h)][1]) for n, h in pairs)
@@ -105,7 +106,7 @@ def test_varlen_workload_full_sampled():
     o, ht = run_chunk(c)
     lens = np.diff(c.cu_seqlens)
     longest, shortest = int(lens.argmax()), int(lens.argmin())
-    pairs = [(longest, 0), (shortest, 15), (0, 3), (15, 8), (7, 11)]
+    pairs = cover_pairs(len(lens), 16, extra=[(longest, 0), (shortest, 15)])
     ref = oracle_pairs(c, pairs)
     o = o[0]
     worst_o = max(max_rel_err(o[c.cu_seqlens[n]:c.cu_seqlens[n + 1], h], ref[(n, h)][0])
@@ -249,7 +250,7 @@ def test_lm_layer_fast_decay_full_sampled(arm):
         c.alpha = np.abs(c.alpha)
     o, ht = run_chunk(c, gate=arm)
     o = o.reshape(c.v.shape)
-    pairs = [(0, 0), (7, 15), (2, 11)]
+    pairs = cover_pairs(8, 16)
     ref = oracle_pairs(c, pairs)
     worst_o = max(max_rel_err(o[n, :, h], ref[(n, h)][0]) for n, h in pairs)
     worst_h = max(max_rel_err(ht[n, h], ref[(n, h)][1]) for n, h in pairs)

@@ -10,7 +10,7 @@ import torch
 import gated_delta_rule_ckda_amd as ck
 import oracle
 from gated_delta_rule_ckda_amd import inputs
-from tests.gpu_util import (DEV, TOL, announce, dev, host, max_rel_err, oracle_gates,
+from tests.gpu_util import (DEV, TOL, announce, cover_pairs, dev, host, max_rel_err, oracle_gates,
                             oracle_pairs, run_chunk)
 
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,7 @@ def test_lm_layer_bf16_logits_full_sampled(arm):
     c = inputs.lm_layer_logits(arm=arm)
     o, ht = run_chunk(c)
     o = o.reshape(c.v.shape)
-    pairs = [(0, 0), (7, 15), (4, 6)]
+    pairs = cover_pairs(8, 16)
     ref = oracle_pairs(c, pairs)
     worst_o = max(max_rel_err(o[n, :, h], ref[(n, h)][0]) for n, h in pairs)
     worst_h = max(max_rel_err(ht[n, h], ref[(n, h)][1]) for n, h in pairs)

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 from gated_delta_rule_ckda_amd import inputs
-from tests.gpu_util import TOL, announce, max_rel_err, oracle_gates, oracle_pairs, run_chunk
+from tests.gpu_util import (TOL, announce, cover_pairs, max_rel_err, oracle_gates, oracle_pairs,
+                            run_chunk)
 import gated_delta_rule_ckda_amd as ck
 from tests import gpu_util
 
@@ -102,7 +103,7 @@ def test_absorbed_lm_layer_full_size():
     (o1, h1), (o2, h2) = run_both(c)
     _equal((o1, h1), (o2, h2), "bf16")
     o2 = o2.reshape(c.v.shape)
-    pairs = [(0, 0), (7, 15), (3, 9)]
+    pairs = cover_pairs(8, 16)
     ref = oracle_pairs(c, pairs)
     worst_o = max(max_rel_err(o2[n, :, h], ref[(n, h)][0]) for n, h in pairs)
     worst_h = max(max_rel_err(h2[n, h], ref[(n, h)][1]) for n, h in pairs)
