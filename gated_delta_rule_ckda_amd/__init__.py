@@ -24,6 +24,7 @@ _lib = None
 BF16, F32 = 0, 1
 GATE_KDA, GATE_CKDA = 0, 1
 GATES_F32, GATES_LOGITS_F32, GATES_LOGITS_BF16 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024  # CKDA_NOALLOC_SCRATCH_BYTES in include/ckda.h
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
            4: "HIP error"}
 
@@ -61,6 +62,9 @@ def _load():
         lib.ckda_chunk_fwd.restype = i32
         lib.ckda_chunk_fwd.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, ctypes.c_size_t, vp]
+        lib.ckda_chunk_fwd_noalloc.restype = i32
+        lib.ckda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp,
+                                               vp, vp, vp, vp]
         lib.ckda_chunk_fwd_prepare.restype = i32
         lib.ckda_chunk_fwd_prepare.argtypes = [ctypes.POINTER(FwdDesc), vp, vp, vp, vp, vp, vp,
                                                ctypes.c_size_t, vp]
@@ -172,23 +176,10 @@ def chunk_fwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
     return int(_load().ckda_chunk_fwd_workspace_size(ctypes.byref(desc), int(bool(packed))))
 
 
-def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
-              use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
-              out=None, final_state=None, workspace=None, stream=None, gates="values",
-              sign_absorb=False):
-    """Chunked prefill.  Dense: q,k [B,T,Hk,dk], alpha [B,T,H,dk], v [B,T,H,dv],
-    beta [B,T,H]; Hk divides H (grouped value heads: value head h reads q/k
-    head h // (H // Hk)).  Packed (cu_seqlens int32 [N+1]): leading [1,T,...]
-    or [T,...].
-    gates='values': alpha, beta are float32 gates; gates='logits': they are
-    float32 or bfloat16 logits that the kernels activate.  sign_absorb=True
-    runs the comparison strategy that folds the gates' cumulative signs into
-    q and k (same result, more traffic).
-    `workspace`: optional uint8 device tensor of at least
-    chunk_fwd_workspace_size() bytes (allocated per call when omitted).
-    Returns (o, ht) with ht [N,H,dk,dv] float32 (None if not requested)."""
+def _fwd_call(q, k, v, alpha, beta, h0, cu_seqlens, chunk_size, use_qk_l2norm, gate, scale,
+              output_final_state, out, final_state, gates, sign_absorb):
+    """Checks shared by chunk_fwd and chunk_fwd_noalloc; returns (desc, o, ht)."""
     import torch
-    lib = _load()
     H, dk, dv = v.shape[-2], q.shape[-1], v.shape[-1]
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
         _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
@@ -212,6 +203,28 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
     if output_final_state:
         ht = (torch.empty((desc.num_seqs, H, dk, dv), device=q.device, dtype=torch.float32)
               if final_state is None else final_state)
+    return desc, o, ht
+
+
+def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
+              use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
+              out=None, final_state=None, workspace=None, stream=None, gates="values",
+              sign_absorb=False):
+    """Chunked prefill.  Dense: q,k [B,T,Hk,dk], alpha [B,T,H,dk], v [B,T,H,dv],
+    beta [B,T,H]; Hk divides H (grouped value heads: value head h reads q/k
+    head h // (H // Hk)).  Packed (cu_seqlens int32 [N+1]): leading [1,T,...]
+    or [T,...].
+    gates='values': alpha, beta are float32 gates; gates='logits': they are
+    float32 or bfloat16 logits that the kernels activate.  sign_absorb=True
+    runs the comparison strategy that folds the gates' cumulative signs into
+    q and k (same result, more traffic).
+    `workspace`: optional uint8 device tensor of at least
+    chunk_fwd_workspace_size() bytes (allocated per call when omitted).
+    Returns (o, ht) with ht [N,H,dk,dv] float32 (None if not requested)."""
+    import torch
+    lib = _load()
+    desc, o, ht = _fwd_call(q, k, v, alpha, beta, h0, cu_seqlens, chunk_size, use_qk_l2norm, gate,
+                            scale, output_final_state, out, final_state, gates, sign_absorb)
     need = chunk_fwd_workspace_size(desc, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -220,6 +233,23 @@ def chunk_fwd(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
     _check(lib.ckda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                               _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
                               _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o, ht
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
+                      use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
+                      out=None, final_state=None, stream=None, gates="values",
+                      sign_absorb=False):
+    """chunk_fwd through ckda_chunk_fwd_noalloc: no workspace, the library's
+    static per-GPU scratch instead (NOALLOC_SCRATCH_BYTES).  The C call
+    allocates nothing; pass `out` (and `final_state`) to keep this wrapper
+    from allocating them.  Calls on one GPU must not overlap."""
+    lib = _load()
+    desc, o, ht = _fwd_call(q, k, v, alpha, beta, h0, cu_seqlens, chunk_size, use_qk_l2norm, gate,
+                            scale, output_final_state, out, final_state, gates, sign_absorb)
+    _check(lib.ckda_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                      _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
+                                      _stream(stream)))
     return o, ht
 
 

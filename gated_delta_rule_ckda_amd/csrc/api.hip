@@ -4,6 +4,7 @@
 // CKDA_ERR_HIP.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "ckda_internal.h"
@@ -61,6 +62,47 @@ int64_t gate_bytes(int32_t g) { return g == CKDA_GATES_LOGITS_BF16 ? 2 : 4; }
 ckda_status_t from_hip(hipError_t e) {
   if (e == hipSuccess) return ok();
   return fail(CKDA_ERR_HIP, "HIP launch error %d: %s", static_cast<int>(e), hipGetErrorString(e));
+}
+
+// ---- static scratch of ckda_chunk_fwd_noalloc
+// Device memory the allocation-free forward uses as its workspace: every GPU
+// the library runs on holds its own copy for the life of the process.  In
+// host code `scratch` names a host-side stand-in, never a device address:
+// its device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is handed to kernels.
+__device__ __align__(256) unsigned char scratch[CKDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // per device; nullptr until looked up
+
+// The device address of the scratch copy on the device that `stream` belongs
+// to (the current device for the null stream).
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -316,6 +358,32 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void
                              const int32_t* cu_seqlens, const float* h0, void* o,
                              float* ht, void* workspace, size_t workspace_bytes, void* stream) {
   return run_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht, workspace, workspace_bytes,
+                 stream, kPrepare | kFinish);
+}
+
+ckda_status_t ckda_chunk_fwd_noalloc(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                                     const void* v, const void* alpha, const void* beta,
+                                     const int32_t* cu_seqlens, const float* h0, void* o,
+                                     float* ht, void* stream) {
+  if (!d) return fail(CKDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  // sizes first, on the host: a call whose workspace would not fit the
+  // static scratch is refused before anything touches the GPU
+  const size_t need = ckda_chunk_fwd_workspace_size(d, cu_seqlens ? 1 : 0);
+  if (need > CKDA_NOALLOC_SCRATCH_BYTES)
+    return fail(CKDA_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of scratch; the static scratch of "
+                "ckda_chunk_fwd_noalloc holds %zu (use ckda_chunk_fwd with a workspace)",
+                need, static_cast<size_t>(CKDA_NOALLOC_SCRATCH_BYTES));
+  const ckda_status_t st = validate_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht, nullptr,
+                                        0, kPrepare | kFinish, false);
+  if (st != CKDA_OK) return st;
+  if (d->num_seqs == 0 || need == 0) return ok();
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(static_cast<hipStream_t>(stream), &ws);
+  if (e != hipSuccess)
+    return fail(CKDA_ERR_HIP, "looking up the static scratch failed: HIP error %d: %s",
+                static_cast<int>(e), hipGetErrorString(e));
+  return run_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht, ws, CKDA_NOALLOC_SCRATCH_BYTES,
                  stream, kPrepare | kFinish);
 }
 

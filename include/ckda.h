@@ -26,9 +26,11 @@
  *
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
- *    never allocates, frees or keeps device memory (scratch space comes in
- *    as a caller-owned workspace argument), and keeps no global mutable
- *    state apart from a thread-local error message.
+ *    never allocates or frees device memory: scratch space comes in as a
+ *    caller-owned workspace argument, except for ckda_chunk_fwd_noalloc,
+ *    which uses a static device array the library holds per GPU.  Apart from
+ *    that array and its per-device address, it keeps no global mutable state
+ *    but a thread-local error message.
  *  - Layouts are row-major and contiguous (last index fastest).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *    default stream).  The library never synchronises the host and never
@@ -184,6 +186,30 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
                              const void* beta, const int32_t* cu_seqlens,
                              const float* h0, void* o, float* ht,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ckda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: the library keeps a static device scratch of
+ * CKDA_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU it runs on, for the life of
+ * the process, and runs the same two passes on it.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's scratch address once.
+ * Arguments, layouts, supported shapes and validation are those of
+ * ckda_chunk_fwd.  A call whose workspace (ckda_chunk_fwd_workspace_size)
+ * would exceed the scratch returns CKDA_ERR_WORKSPACE_TOO_SMALL before any
+ * HIP call: at dk = dv = 128, chunk 64, bf16 that is about 2,000
+ * (head, chunk) pairs, e.g. 16 heads of 8,000 tokens.  Every call on one GPU
+ * shares that GPU's scratch, and each call rewrites all of it that it reads
+ * (nothing needs to start at zero), so calls on one GPU must not overlap:
+ * order them on one stream, or otherwise one after the other.  Calls that
+ * overlap on one GPU race and give undefined results.
+ */
+#define CKDA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+ckda_status_t ckda_chunk_fwd_noalloc(const ckda_fwd_desc_t* desc, const void* q,
+                                     const void* k, const void* v, const void* alpha,
+                                     const void* beta, const int32_t* cu_seqlens,
+                                     const float* h0, void* o, float* ht, void* stream);
 
 /*
  * The two passes of ckda_chunk_fwd as separate calls, for callers that time

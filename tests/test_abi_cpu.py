@@ -294,3 +294,27 @@ def test_bwd_workspace_covers_forward_and_records():
         fwd = lib.ckda_chunk_fwd_workspace_size(ctypes.byref(d), 0)
         bwd = lib.ckda_chunk_bwd_workspace_size(ctypes.byref(d), 0)
         assert bwd == fwd + extra, dt
+
+
+def test_noalloc_scratch_limit_is_checked_on_the_host():
+    """ckda_chunk_fwd_noalloc refuses a call whose workspace would not fit its
+    static scratch with CKDA_ERR_WORKSPACE_TOO_SMALL, and a NULL descriptor
+    with CKDA_ERR_INVALID_ARGUMENT, before any HIP call (no GPU here); the
+    scratch size the binding states is the header's."""
+    lib = ck._load()
+    m = re.search(r"#define CKDA_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)",
+                  open(HEADER).read())
+    assert int(m.group(1)) << 20 == ck.NOALLOC_SCRATCH_BYTES
+    big = _desc(B=4, T=8192, H=16, num_seqs=4)
+    assert ck.chunk_fwd_workspace_size(big, False) > ck.NOALLOC_SCRATCH_BYTES
+    st = lib.ckda_chunk_fwd_noalloc(ctypes.byref(big), P["q"], P["k"], P["v"], P["alpha"],
+                                    P["beta"], None, P["h0"], P["o"], P["ht"], None)
+    assert st == 3 and "static scratch" in lib.ckda_last_error().decode()
+    assert lib.ckda_chunk_fwd_noalloc(None, P["q"], P["k"], P["v"], P["alpha"], P["beta"], None,
+                                      P["h0"], P["o"], P["ht"], None) == 1
+    # a call that fits but has a bad argument is refused by the shared checks
+    small = _desc()
+    assert ck.chunk_fwd_workspace_size(small, False) <= ck.NOALLOC_SCRATCH_BYTES
+    st = lib.ckda_chunk_fwd_noalloc(ctypes.byref(small), P["q"], None, P["v"], P["alpha"],
+                                    P["beta"], None, P["h0"], P["o"], P["ht"], None)
+    assert st == 1 and "must not be NULL" in lib.ckda_last_error().decode()
