@@ -191,10 +191,119 @@ def fwd(q, k, v, alpha, beta, h0=None, seq_start=None, use_l2norm=True, scale=1.
 
 
 # ----------------------------------------------------------------- backward
-def chunk_head_bwd(q, k, v, alpha, beta, S_init, dO, dS_end, use_l2norm, scale, C):
+def dalpha_straddle(ac, kh, qh, F, dKt0, dQt0, dG, dP, dKh, dg0, block=BLOCK):
+    """dalpha of one chunk with no division by a gate and no cancellation
+    between pair terms that do not depend on it.
+
+    Every gate-dependent quantity of the chunk is a pair (r, j), r > j, of
+    positions with the decay D(r<-j) = prod_{j<t<=r} alpha_t: the chunk rows,
+    plus the chunk start (j = -1, for Kt, Qt and g) and the chunk end (r = C,
+    for Kh and g; D(C<-j) = D(C-1<-j)).  With adj_rj the adjoint of that
+    pair's decay (per channel), dL/dalpha_s is the sum over the pairs that
+    straddle s (j < s <= r) of adj_rj D(r<-s) D(s-1<-j): the two partial
+    products on either side of s, both bounded by 1.  The sum is split by the
+    16-row tiles (tile b = rows [16b, 16b+16), a_b = 16b - 1, e_b = 16b + 15):
+      rows of b and columns before b:  Pre_s * sum_{r>=s in b} D(r<-s) rho_r
+      rows after b and columns of b:   Suf_s * sum_{j<s in b} D(s-1<-j) kappa_j
+      rows after b, columns before b:  Pre_s * Suf_s * Gamma_b
+      both in b:                       pairwise, with products inside the tile
+    with Pre_s = D(s-1<-a_b), Suf_s = D(e_b<-s) (direct products inside the
+    tile), rho_r = sum_{j<=a_b} adj_rj D(a_b<-j), kappa_j = sum_{r>e_b}
+    adj_rj D(r<-e_b) and Gamma_b = sum adj_rj D(r<-e_b) D(a_b<-j) (anchored
+    at the tile's own edges; formed from the chunk's running products F as
+    ratios, which the ratio form's range on F keeps bounded and accurate).
+    The suffix and prefix sums run as recurrences (sigma_s = rho_s +
+    alpha_{s+1} sigma_{s+1}, pi_{s+1} = alpha_s pi_s + kappa_s), so no step
+    divides by a gate and every term is formed once, with its own sign.
+
+    Inputs (per chunk; C rows, last axis the channels): ac gates, kh, qh the
+    normalised keys and queries, F the running products, dKt0 = -(Y^T dU) S0^T
+    and dQt0 = scale dO S0^T (the start pairs' adjoints over Kt and Qt),
+    dG, dP the adjoints of G = tril(Kt Rk^T, -1) and P = tril(Qt Rk^T),
+    dKh = U dS1^T, dg0 = rowsum(dS1 * S0)."""
+    C, dk = ac.shape
+    nb = C // block
+    dt = ac.dtype
+    g = F[C - 1]
+    Rk, Kt, Qt = kh / F, kh * F, qh * F
+    one = np.ones(dk, dtype=dt)
+    Fa = [one if b == 0 else F[block * b - 1] for b in range(nb)]   # F at a_b
+    Fe = [F[block * b + block - 1] for b in range(nb)]               # F at e_b
+    # row tile t: pair terms of its rows with the columns before tile b, for
+    # b = 0..t (chunk-anchored, D = F_r / F_j), from products tile by tile
+    X = {}
+    rho = np.zeros((C, dk), dtype=dt)
+    for t in range(nb):
+        rt = slice(block * t, block * t + block)
+        accK, accQ = dKt0[rt].copy(), dQt0[rt].copy()
+        for b in range(t + 1):
+            X[t, b] = Kt[rt] * accK + Qt[rt] * accQ
+            if b == t:
+                rho[rt] = Fa[t] * (kh[rt] * accK + qh[rt] * accQ)
+            cb = slice(block * b, block * b + block)
+            accK = accK + dG[rt, cb] @ Rk[cb]
+            accQ = accQ + dP[rt, cb] @ Rk[cb]
+    # column tile t: pair terms of its columns with the rows after tile t
+    kap = np.zeros((C, dk), dtype=dt)
+    for t in range(nb):
+        ct = slice(block * t, block * t + block)
+        accR = g * dKh[ct]
+        for I in range(nb - 1, t, -1):
+            ri = slice(block * I, block * I + block)
+            accR = accR + dG[ri, ct].T @ Kt[ri] + dP[ri, ct].T @ Qt[ri]
+        kap[ct] = (kh[ct] / Fe[t]) * accR
+    # corners: rows after tile b (and the end) with columns before it (and the start)
+    endterm = g * dKh * Rk                                           # (end, j) pairs
+    Gam = []
+    for b in range(nb):
+        Z = g * dg0 + endterm[:block * b].sum(0)
+        for I in range(b + 1, nb):
+            Z = Z + X[I, b].sum(0)
+        Gam.append(Z * (Fa[b] / Fe[b]))
+    dal = np.zeros((C, dk), dtype=dt)
+    for b in range(nb):
+        lo = block * b
+        a = ac[lo:lo + block]
+        pre = np.ones((block, dk), dtype=dt)
+        for i in range(1, block):
+            pre[i] = pre[i - 1] * a[i - 1]
+        suf = np.ones((block, dk), dtype=dt)
+        for i in range(block - 2, -1, -1):
+            suf[i] = suf[i + 1] * a[i + 1]
+        sig = np.zeros((block, dk), dtype=dt)
+        sig[block - 1] = rho[lo + block - 1]
+        for i in range(block - 2, -1, -1):
+            sig[i] = rho[lo + i] + a[i + 1] * sig[i + 1]
+        pi = np.zeros((block, dk), dtype=dt)
+        for i in range(1, block):
+            pi[i] = a[i - 1] * pi[i - 1] + kap[lo + i - 1]
+        # pairs inside the tile: for each row r, Phi_r(s) = sum_{j<s} adj_rj
+        # D(s-1<-j) by a recurrence over s, then D(r<-s) Phi_r(s) summed over r
+        psi = np.zeros((block, dk), dtype=dt)
+        for ri in range(1, block):
+            r = lo + ri
+            phi = np.zeros(dk, dtype=dt)
+            phis = []
+            for si in range(1, ri + 1):        # phi = Phi_r(lo + si)
+                j = lo + si - 1
+                adj = (dG[r, j] * kh[r] + dP[r, j] * qh[r]) * kh[j]
+                phi = a[si - 1] * phi + adj
+                phis.append(phi)
+            d = np.ones(dk, dtype=dt)          # D(r <- s), s from r down
+            for si in range(ri, 0, -1):
+                psi[si] += d * phis[si - 1]
+                d = d * a[si]
+        dal[lo:lo + block] = pre * sig + suf * pi + pre * suf * Gam[b] + psi
+    return dal
+
+
+def chunk_head_bwd(q, k, v, alpha, beta, S_init, dO, dS_end, use_l2norm, scale, C,
+                   dalpha_form="straddle", dt=np.float64):
     """Gradients for one sequence and head through the chunked form, as the
     HIP backward computes them (chunk-anchored ratios; every running product
-    must be nonzero).  Returns (dq, dk, dv, dalpha, dbeta, dS_init).
+    must be nonzero).  Returns (dq, dk, dv, dalpha, dbeta, dS_init).  dt is the
+    arithmetic type (float64, or float32 to see rounding behave as on the
+    GPU's float32 path).
 
     Per chunk with entry state S0, exit-state gradient dS1 and output
     gradient dO, and Y = X Diag(beta), Z = V - Kt S0, U = Y Z:
@@ -207,22 +316,27 @@ def chunk_head_bwd(q, k, v, alpha, beta, S_init, dO, dS_end, use_l2norm, scale, 
       dX  = dY Diag(beta),  dbeta_j += sum_r X_rj dY_rj
       dA  = -X^T dX X^T (strictly lower),  A = Diag(beta) G
       dbeta_r += sum_j dA_rj G_rj,  dG = Diag(beta) dA
-      dKt += dG Rk,  dQt += dP Rk,  dRk = dG^T Kt + dP^T Qt + g * dKh,
-      dg += sum_j dKh_j * Rk_j
+      dKt += dG Rk,  dQt += dP Rk,  dRk = dG^T Kt + dP^T Qt + g * dKh
       dk_hat = dKt * F + dRk / F,  dq_hat = dQt * F
-      Lam = dKt * Kt + dQt * Qt - dRk * Rk,  Lam_{C-1} += dg * g
-      dalpha_s = (sum_{r>=s} Lam_r) / alpha_s      (d log|alpha| summed)
-    then dx = r (dx_hat - x_hat (x_hat . dx_hat)) through each norm."""
+    dalpha: dalpha_form="straddle" is dalpha_straddle (what the kernels
+    compute); "ratio" is the earlier form
+      Lam = dKt * Kt + dQt * Qt - dRk * Rk,  Lam_{C-1} += (dg + sum_j dKh_j Rk_j) g
+      dalpha_s = (sum_{r>=s} Lam_r) / alpha_s
+    whose reverse sums cancel pair terms that do not depend on alpha_s, so
+    its rounding error grows like 1/|alpha_s|.
+    Then dx = r (dx_hat - x_hat (x_hat . dx_hat)) through each norm."""
+    q, k, v, alpha, beta, S_init, dO, dS_end = (np.asarray(x, dtype=dt) for x in
+                                                (q, k, v, alpha, beta, S_init, dO, dS_end))
     T, dk = q.shape
     dv = v.shape[1]
-    rq_all, rk_all = _l2scale(q, use_l2norm), _l2scale(k, use_l2norm)
+    rq_all, rk_all = _l2scale(q, use_l2norm).astype(dt), _l2scale(k, use_l2norm).astype(dt)
     qh_all, kh_all = q * rq_all[:, None], k * rk_all[:, None]
     # forward sweep: entry state of every chunk
     starts = list(range(0, T, C))
-    S = S_init.copy()
+    S = S_init.astype(np.float64)
     S0s = []
     for c0 in starts:
-        S0s.append(S.copy())
+        S0s.append(S.astype(dt))
         L = min(C, T - c0)
         _, S = chunk_head(q[c0:c0 + L], k[c0:c0 + L], v[c0:c0 + L], alpha[c0:c0 + L],
                           beta[c0:c0 + L], S, use_l2norm, scale, C)
@@ -233,19 +347,19 @@ def chunk_head_bwd(q, k, v, alpha, beta, S_init, dO, dS_end, use_l2norm, scale, 
         c0 = starts[ci]
         L = min(C, T - c0)
         S0 = S0s[ci]
-        qh = np.zeros((C, dk)); qh[:L] = qh_all[c0:c0 + L]
-        kh = np.zeros((C, dk)); kh[:L] = kh_all[c0:c0 + L]
-        V = np.zeros((C, dv)); V[:L] = v[c0:c0 + L]
-        G_O = np.zeros((C, dv)); G_O[:L] = dO[c0:c0 + L]
-        ac = np.ones((C, dk)); ac[:L] = alpha[c0:c0 + L]
-        bc = np.zeros(C); bc[:L] = beta[c0:c0 + L]
+        qh = np.zeros((C, dk), dtype=dt); qh[:L] = qh_all[c0:c0 + L]
+        kh = np.zeros((C, dk), dtype=dt); kh[:L] = kh_all[c0:c0 + L]
+        V = np.zeros((C, dv), dtype=dt); V[:L] = v[c0:c0 + L]
+        G_O = np.zeros((C, dv), dtype=dt); G_O[:L] = dO[c0:c0 + L]
+        ac = np.ones((C, dk), dtype=dt); ac[:L] = alpha[c0:c0 + L]
+        bc = np.zeros(C, dtype=dt); bc[:L] = beta[c0:c0 + L]
         F = np.cumprod(ac, axis=0)
         g = F[C - 1]
         Kt, Qt, Rk = kh * F, qh * F, kh / F
         Kh = g * Rk
         G = np.tril(Kt @ Rk.T, -1)
         A = bc[:, None] * G
-        X = np.linalg.inv(np.eye(C) + A)
+        X = np.linalg.inv(np.eye(C, dtype=dt) + A)
         Y = X * bc[None, :]
         P = np.tril(Qt @ Rk.T)
         Z = V - Kt @ S0
@@ -254,27 +368,29 @@ def chunk_head_bwd(q, k, v, alpha, beta, S_init, dO, dS_end, use_l2norm, scale, 
         dU = scale * P.T @ G_O + Kh @ dS1
         dS = scale * Qt.T @ G_O + g[:, None] * dS1 - Kt.T @ (Y.T @ dU)
         dvv[c0:c0 + L] = (Y.T @ dU)[:L]
-        dQt = scale * G_O @ S0.T
+        dQt0 = scale * G_O @ S0.T
         dP = np.tril(scale * G_O @ U.T)
         dKh = U @ dS1.T
-        dg = (dS1 * S0).sum(1)
+        dg0 = (dS1 * S0).sum(1)
         dY = dU @ Z.T
-        dKt = -(Y.T @ dU) @ S0.T
+        dKt0 = -(Y.T @ dU) @ S0.T
         dX = dY * bc[None, :]
         db = (X * dY).sum(0)
         dA = np.tril(-X.T @ dX @ X.T, -1)
         db = db + (dA * G).sum(1)
         dG = bc[:, None] * dA
-        dKt = dKt + dG @ Rk
-        dQt = dQt + dP @ Rk
+        dKt = dKt0 + dG @ Rk
+        dQt = dQt0 + dP @ Rk
         dRk = dG.T @ Kt + dP.T @ Qt + g * dKh
-        dg = dg + (dKh * Rk).sum(0)
         dkh = dKt * F + dRk / F
         dqh = dQt * F
-        Lam = dKt * Kt + dQt * Qt - dRk * Rk
-        Lam[C - 1] += dg * g
-        dlog = np.cumsum(Lam[::-1], axis=0)[::-1]
-        dal[c0:c0 + L] = (dlog / ac)[:L]
+        if dalpha_form == "straddle":
+            da = dalpha_straddle(ac, kh, qh, F, dKt0, dQt0, dG, dP, dKh, dg0)
+        else:
+            Lam = dKt * Kt + dQt * Qt - dRk * Rk
+            Lam[C - 1] += (dg0 + (dKh * Rk).sum(0)) * g
+            da = np.cumsum(Lam[::-1], axis=0)[::-1] / ac
+        dal[c0:c0 + L] = da[:L]
         dbe[c0:c0 + L] = db[:L]
         for name, xh, dxh, r, out in (("q", qh, dqh, rq_all, dq), ("k", kh, dkh, rk_all, dk_)):
             if use_l2norm:
@@ -286,8 +402,9 @@ def chunk_head_bwd(q, k, v, alpha, beta, S_init, dO, dS_end, use_l2norm, scale, 
 
 
 def bwd(q, k, v, alpha, beta, dO, h0=None, dht=None, seq_start=None, use_l2norm=True,
-        scale=1.0, C=64):
-    """Same calling convention as oracle.bwd."""
+        scale=1.0, C=64, dalpha_form="straddle", dt=np.float64):
+    """Same calling convention as oracle.bwd (plus the dalpha form and the
+    arithmetic type of chunk_head_bwd)."""
     q, k, v, alpha, beta, dO = (np.asarray(a, dtype=np.float64) for a in (q, k, v, alpha, beta, dO))
     H, dk = q.shape[-2], q.shape[-1]
     dv = v.shape[-1]
@@ -310,7 +427,8 @@ def bwd(q, k, v, alpha, beta, dO, h0=None, dht=None, seq_start=None, use_l2norm=
             dS = np.zeros((dk, dv)) if dht is None else np.array(dht[n, h], dtype=np.float64)
             if s1 > s0:
                 r = chunk_head_bwd(q[s0:s1, h], k[s0:s1, h], v[s0:s1, h], alpha[s0:s1, h],
-                                   beta[s0:s1, h], S, dO[s0:s1, h], dS, use_l2norm, scale, C)
+                                   beta[s0:s1, h], S, dO[s0:s1, h], dS, use_l2norm, scale, C,
+                                   dalpha_form, dt)
                 for o_, g_ in zip(outs, r[:5]):
                     o_[s0:s1, h] = g_
                 dS = r[5]

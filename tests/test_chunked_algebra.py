@@ -95,3 +95,67 @@ def test_packed_varlen():
     ro, rh = oracle.fwd(q, k, v, a, b, h0=h0, seq_start=starts)
     co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, seq_start=starts, C=16)
     assert _err(co, ro) < 1e-11 and _err(ch, rh) < 1e-11
+
+
+# ------------------------------------------------------------------ backward
+def _bwd_case(seed, B, T, H, d, tiny_per_chunk=0, C=64, signed=True):
+    """Gradient case; tiny_per_chunk > 0 plants that many gates of magnitude
+    1e-3 or 1e-5 (random sign) per (chunk, head, channel), few enough that the
+    chunk's running products stay in the ratio form's range."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.normal(size=(B, T, H, d)) for _ in range(3))
+    a = np.tanh(rng.normal(2, 1, (B, T, H, d)))
+    if signed:
+        a *= rng.choice([-1, 1], a.shape)
+    for _ in range(tiny_per_chunk):
+        for b_ in range(B):
+            for c0 in range(0, T, C):
+                for h in range(H):
+                    rows = rng.integers(c0, min(c0 + C, T), d)
+                    a[b_, rows, h, np.arange(d)] = (rng.choice([-1, 1], d)
+                                                    * rng.choice([1e-3, 1e-5], d))
+    a = a.astype(np.float32).astype(np.float64)
+    b = rng.uniform(0, 2, (B, T, H))
+    h0 = 0.3 * rng.normal(size=(B, H, d, d))
+    dO = rng.normal(size=(B, T, H, d))
+    dht = rng.normal(size=(B, H, d, d))
+    return q, k, v, a, b, h0, dO, dht
+
+
+@pytest.mark.parametrize("C,T", [(16, 38), (32, 70), (64, 130), (64, 64)])
+def test_chunked_backward_equals_oracle_gradients(C, T):
+    """The chunked backward (tile-split dalpha with no division by a gate)
+    equals the oracle's reverse mode through the sequential recurrence, every
+    gradient, to fp64 rounding; signed gates, partial last chunks."""
+    q, k, v, a, b, h0, dO, dht = _bwd_case(40 + C, 2, T, 2, 8, C=C)
+    r = oracle.bwd(q, k, v, a, b, dO, h0=h0, dht=dht)
+    g = chunked_fp64.bwd(q, k, v, a, b, dO, h0=h0, dht=dht, C=C)
+    for x, y in zip(g, r):
+        assert _err(x, y) < 1e-12
+
+
+def test_chunked_backward_packed():
+    q, k, v, a, b, h0, dO, dht = _bwd_case(48, 1, 150, 2, 8, C=32)
+    starts = np.array([0, 37, 37, 101, 150])
+    h0 = np.random.default_rng(49).normal(size=(4, 2, 8, 8))
+    dht = np.random.default_rng(50).normal(size=(4, 2, 8, 8))
+    r = oracle.bwd(q, k, v, a, b, dO, h0=h0, dht=dht, seq_start=starts)
+    g = chunked_fp64.bwd(q, k, v, a, b, dO, h0=h0, dht=dht, seq_start=starts, C=32)
+    for x, y in zip(g, r):
+        assert _err(x, y) < 1e-12
+
+
+def test_dalpha_of_tiny_gates_holds_in_float32():
+    """Gates of 1e-3 and 1e-5: evaluated in float32 (the GPU's accumulation
+    type), the tile-split dalpha stays within 1e-5 of the fp64 oracle over the
+    whole tensor (max-normalised), while the earlier ratio form, whose reverse
+    sums cancel O(1) pair terms before dividing by the gate, is off by more
+    than 1e-3: the split removes the 1/|alpha| error growth."""
+    q, k, v, a, b, h0, dO, dht = _bwd_case(51, 1, 128, 2, 16, tiny_per_chunk=1)
+    r = oracle.bwd(q, k, v, a, b, dO, h0=h0, dht=dht)
+    g = chunked_fp64.bwd(q, k, v, a, b, dO, h0=h0, dht=dht, C=64, dt=np.float32)
+    assert max(_err(x, y) for x, y in zip(g, r)) < 1e-5
+    gr = chunked_fp64.bwd(q, k, v, a, b, dO, h0=h0, dht=dht, C=64, dt=np.float32,
+                          dalpha_form="ratio")
+    assert _err(gr[3], r[3]) > 1e-3
+    assert max(_err(x, y) for i, (x, y) in enumerate(zip(gr, r)) if i != 3) < 1e-5
