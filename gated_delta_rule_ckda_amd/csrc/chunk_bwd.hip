@@ -809,14 +809,25 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
     __syncthreads();
     // dQt = scale dO S0^T + dP Rk;  dKt = -T1 S0^T + dG Rk;
     // dRk = dG^T Kt + dP^T Qt + g dKh with dKh = U dS1^T
+    // (the start terms scale dO S0^T and -T1 S0^T are also kept, in the
+    // slices of V and G, which are no longer read: dalpha needs them apart)
     gemm(C, dk, dv, scale, false, sdO, dv, 1, S0, 1, dv, sdQ, dk, 1, stage);
-    gemm(C, dk, C, 1.f, true, sdP, C, 1, sRk, dk, 1, sdQ, dk, 1, stage);
     gemm(C, dk, dv, -1.f, false, sT1, dv, 1, S0, 1, dv, sdK, dk, 1, stage);
+    float* sQ0 = sV;
+    float* sK0 = sG;
+    for (int e = tid; e < C * dk; e += kNT) {
+      sQ0[e] = sdQ[e];
+      sK0[e] = sdK[e];
+    }
+    __syncthreads();
+    gemm(C, dk, C, 1.f, true, sdP, C, 1, sRk, dk, 1, sdQ, dk, 1, stage);
     gemm(C, dk, C, 1.f, true, ldA, C, 1, sRk, dk, 1, sdK, dk, 1, stage);
     gemm(C, dk, dv, 1.f, false, sU, dv, 1, dS1, 1, dv, sZ, dk, 1, stage);  // dKh -> Z's slice
     gemm(C, dk, C, 1.f, false, ldA, 1, C, sKt, dk, 1, sdR, dk, 1, stage);
     gemm(C, dk, C, 1.f, true, sdP, 1, C, sQt, dk, 1, sdR, dk, 1, stage);
-    // dg = rowsum(dS1 * S0) + sum_r dKh_r Rk_r (TPC threads per channel)
+    // dg = rowsum(dS1 * S0) (TPC threads per channel), the adjoint of the
+    // pair (chunk end, chunk start); the end's pairs with the rows (Kh) are
+    // counted where dalpha sums pairs
     {
       const int TPC = kNT / dk >= 1 ? kNT / dk : 1, cc = tid / TPC, sub = tid % TPC;
       float sacc = 0.f;
@@ -832,25 +843,116 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) sacc += x[u] * y[u];
         }
-        for (int r0 = sub; r0 < C; r0 += 8 * TPC) {
-          float x[8], y[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int r = r0 + u * TPC;
-            x[u] = r < C ? sZ[r * dk + cc] : 0.f;
-            y[u] = r < C ? sRk[r * dk + cc] : 0.f;
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sacc += x[u] * y[u];
-        }
       }
       for (int o = 1; o < TPC; o <<= 1) sacc += __shfl_xor(sacc, o);
       if (cc < dk && sub == 0) ldg[cc] = sacc;
     }
     __syncthreads();
-    // elementwise: dk^, dq^ in place; Lam into sF's slice (F read first)
+    // dalpha per channel (one thread each), with no division by a gate: the
+    // sum over the pairs (r, j) of positions that straddle s (j < s <= r;
+    // chunk rows, start j = -1, end r = C) of the pair's adjoint times
+    // D(r<-s) D(s-1<-j), split by 16-row tiles as in the bf16 pass: rows of
+    // the tile with columns before it (rho, suffix recurrence), columns of
+    // the tile with rows after it (kappa, prefix recurrence), rows after
+    // with columns before (Gamma), and the tile's own pairs.  Runs before
+    // dk^ and dq^ overwrite nothing it reads (F, Kt, Qt, Rk, the start terms,
+    // dKh, dG, dP).
+#pragma unroll 1
+    for (int cc = tid; cc < dk; cc += kNT) {
+      const float gg = lg[cc], gdg = gg * ldg[cc];
+      auto at = [&](int r) { return r < L ? alpha[((t0 + r) * H + h) * dk + cc] : 1.f; };
+      auto khat = [&](int r) { return r < L ? IO::load(k, ((t0 + r) * H + h) * dk + cc) * lrk[r] : 0.f; };
+      auto qhat = [&](int r) { return r < L ? IO::load(q, ((t0 + r) * H + h) * dk + cc) * lrq[r] : 0.f; };
+      const int nb = C / 16;
+#pragma unroll 1
+      for (int tb = 0; tb < nb; ++tb) {
+        const int lo = 16 * tb, hi = lo + 16;
+        const float Fa = tb == 0 ? 1.f : sF[(lo - 1) * dk + cc], Fe = sF[(hi - 1) * dk + cc];
+        // Gamma: rows after the tile and the end, columns before it and the start
+        float Z = gdg;
+#pragma unroll 1
+        for (int j = 0; j < lo; ++j) Z += gg * sZ[j * dk + cc] * sRk[j * dk + cc];
+#pragma unroll 1
+        for (int r = hi; r < C; ++r) {
+          float xk = sK0[r * dk + cc], xq = sQ0[r * dk + cc];
+#pragma unroll 1
+          for (int j = 0; j < lo; ++j) {
+            const float rk = sRk[j * dk + cc];
+            xk += ldA[r * C + j] * rk;
+            xq += sdP[r * C + j] * rk;
+          }
+          Z += sKt[r * dk + cc] * xk + sQt[r * dk + cc] * xq;
+        }
+        const float gam = Z * (Fa / Fe);
+        float a[16], kh[16], rho[16], kap[16];
+#pragma unroll 1
+        for (int i = 0; i < 16; ++i) {
+          const int r = lo + i;
+          a[i] = at(r);
+          kh[i] = khat(r);
+          // rho_r: row r with the columns before the tile and the start
+          float xk = sK0[r * dk + cc], xq = sQ0[r * dk + cc];
+#pragma unroll 1
+          for (int j = 0; j < lo; ++j) {
+            const float rk = sRk[j * dk + cc];
+            xk += ldA[r * C + j] * rk;
+            xq += sdP[r * C + j] * rk;
+          }
+          rho[i] = Fa * (kh[i] * xk + qhat(r) * xq);
+          // kappa_r: column r with the rows after the tile and the end
+          float y = gg * sZ[r * dk + cc];
+#pragma unroll 1
+          for (int m = hi; m < C; ++m) y += ldA[m * C + r] * sKt[m * dk + cc] + sdP[m * C + r] * sQt[m * dk + cc];
+          kap[i] = kh[i] / Fe * y;
+        }
+        float sig[16], pi[16], pre[16], suf[16], psi[16];
+        sig[15] = rho[15];
+#pragma unroll 1
+        for (int i = 14; i >= 0; --i) sig[i] = rho[i] + a[i + 1] * sig[i + 1];
+        pi[0] = 0.f;
+#pragma unroll 1
+        for (int i = 1; i < 16; ++i) pi[i] = a[i - 1] * pi[i - 1] + kap[i - 1];
+        pre[0] = 1.f;
+#pragma unroll 1
+        for (int i = 1; i < 16; ++i) pre[i] = pre[i - 1] * a[i - 1];
+        suf[15] = 1.f;
+#pragma unroll 1
+        for (int i = 14; i >= 0; --i) suf[i] = suf[i + 1] * a[i + 1];
+#pragma unroll 1
+        for (int i = 0; i < 16; ++i) psi[i] = 0.f;
+        // the tile's own pairs: Phi_r(s) = sum_{j<s} adj_rj D(s-1<-j) for
+        // each row r, then D(r<-s) Phi_r(s) into s
+#pragma unroll 1
+        for (int ri = 1; ri < 16; ++ri) {
+          const int r = lo + ri;
+          const float kr = kh[ri], qr = qhat(r);
+          float phis[16], phi = 0.f;
+#pragma unroll 1
+          for (int si = 1; si <= ri; ++si) {
+            const int j = si - 1;
+            phi = a[j] * phi + (ldA[r * C + lo + j] * kr + sdP[r * C + lo + j] * qr) * kh[j];
+            phis[si] = phi;
+          }
+          float d = 1.f;
+#pragma unroll 1
+          for (int si = ri; si >= 1; --si) {
+            psi[si] += d * phis[si];
+            d *= a[si];
+          }
+        }
+#pragma unroll 1
+        for (int i = 0; i < 16; ++i) {
+          const int r = lo + i;
+          if (r < L)
+            b.dalpha[((t0 + r) * H + h) * dk + cc] =
+                pre[i] * sig[i] + suf[i] * pi[i] + pre[i] * suf[i] * gam + psi[i];
+        }
+      }
+    }
+    __syncthreads();  // dalpha has read F, Kt, Qt, Rk
+    // elementwise: dk^, dq^ in place
     for (int e0 = tid; e0 < C * dk; e0 += 4 * kNT) {
-      float f[4], dqt[4], dkt[4], drk[4], kt[4], qt[4], rk[4];
+      float f[4], dqt[4], dkt[4], drk[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + u * kNT;
@@ -859,9 +961,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
         dqt[u] = in ? sdQ[e] : 0.f;
         dkt[u] = in ? sdK[e] : 0.f;
         drk[u] = in ? sdR[e] + lg[e % dk] * sZ[e] : 0.f;
-        kt[u] = in ? sKt[e] : 0.f;
-        qt[u] = in ? sQt[e] : 0.f;
-        rk[u] = in ? sRk[e] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -869,30 +968,10 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
         if (e < C * dk) {
           sdK[e] = dkt[u] * f[u] + drk[u] / f[u];
           sdQ[e] = dqt[u] * f[u];
-          sF[e] = dkt[u] * kt[u] + dqt[u] * qt[u] - drk[u] * rk[u];
         }
       }
     }
     __syncthreads();
-    // dalpha per channel: reverse running sums of Lam, divided by alpha
-    for (int cc = tid; cc < dk; cc += kNT) {
-      float acc = ldg[cc] * lg[cc];
-      for (int r0 = C - 16; r0 >= 0; r0 -= 16) {
-        float lam[16], al[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int r = r0 + u;
-          lam[u] = sF[r * dk + cc];
-          al[u] = r < L ? alpha[((t0 + r) * H + h) * dk + cc] : 1.f;
-        }
-#pragma unroll
-        for (int u = 15; u >= 0; --u) {
-          const int r = r0 + u;
-          acc += lam[u];
-          if (r < L) b.dalpha[((t0 + r) * H + h) * dk + cc] = acc / al[u];
-        }
-      }
-    }
     // dq, dk through the norms (TPR threads per row); dbeta
     {
       const int TPR = kNT / C, r = tid / TPR, sub = tid % TPR;
@@ -997,8 +1076,12 @@ struct PCfg {
   static constexpr int O_KT = 0, O_RK = MV, O_Z = 2 * MV, O_U = 3 * MV, O_DU = 4 * MV, O_DO = 5 * MV;
   static constexpr int O_DX = O_KT, O_TT = O_RK;
   static constexpr int O_Y = 6 * MV, O_X = O_Y + MC, O_XT = O_X + MC;
-  static constexpr int O_RED = O_XT + MC;            // float [2][C] norms, [C] dbeta, int flag
-  static constexpr int LDS_BYTES = align16(O_RED + (3 * C + 4) * 4);
+  // floats: [2][C] row sums of squares, [NW][2][C] their per-wave parts,
+  // [NBC][C] dbeta parts from the dY tiles (by tile row) and [NBC][C] from
+  // the dA tiles (by tile column), then the int flag
+  static constexpr int O_RED = O_XT + MC;
+  static constexpr int NRED = 2 * C + 2 * NW * C + 2 * NBC * C;
+  static constexpr int LDS_BYTES = align16(O_RED + (NRED + 4) * 4);
   // Y lower: K fragment s of row tile t is live if it starts at or left of
   // the tile's last row
   static constexpr bool lo_live(int t, int s) { return 32 * s <= 16 * t + 15; }
@@ -1040,12 +1123,15 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   __bf16* sX = reinterpret_cast<__bf16*>(smem + Cfg::O_X);
   __bf16* sXT = reinterpret_cast<__bf16*>(smem + Cfg::O_XT);
   float* nrm = reinterpret_cast<float*>(smem + Cfg::O_RED);  // [2][C]
-  float* dbl = nrm + 2 * C;                                    // [C]
-  int* flag = reinterpret_cast<int*>(dbl + C);
+  float* nrw = nrm + 2 * C;                                    // [NW][2][C]
+  float* dbp = nrw + 2 * NW * C;                               // [NBC][C]
+  float* dba = dbp + NBC * C;                                  // [NBC][C]
+  int* flag = reinterpret_cast<int*>(dba + NBC * C);
   const int ch = 16 * w + l16;  // this lane's channel / value column
   typedef const __attribute__((address_space(1))) uint16_t gu16;
   typedef const __attribute__((address_space(1))) float gf32;
-  for (int i = tid; i < 3 * C + 1; i += NT) nrm[i] = 0.f;  // the flag word too
+  // dbeta parts of tiles that hold none stay zero; the flag too
+  for (int i = tid; i < 2 * NBC * C + 1; i += NT) dbp[i] = 0.f;
 
   // ---- every load goes out first (rows >= L read from row L - 1, no
   // branch around a load; replaced afterwards)
@@ -1140,8 +1226,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
     }
   }
   // ---- row norms: sums of squares over the wave's channels by a butterfly
-  // (lane l16 ends with value l16 >> (4 - log2 4NB)), then over the waves by
-  // LDS atomics
+  // (lane l16 ends with value l16 >> (4 - log2 4NB)), then over the waves in
+  // wave order (a fixed order: the sums are the same on every run)
   const bool l2 = a.use_l2norm != 0;
   {
     constexpr int NV = 4 * NB, LG = ilog2(NV);
@@ -1175,11 +1261,19 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
     }
     const int v = l16 >> (4 - LG), r = 16 * (v >> 2) + 4 * lq + (v & 3);
     if ((l16 & ((1 << (4 - LG)) - 1)) == 0) {
-      atomicAdd(nrm + r, vq[0]);
-      atomicAdd(nrm + C + r, vk[0]);
+      nrw[(2 * w) * C + r] = vq[0];
+      nrw[(2 * w + 1) * C + r] = vk[0];
     }
   }
-  __syncthreads();  // LDS operands and the sums of squares
+  __syncthreads();  // LDS operands and the per-wave sums of squares
+  if (tid < 2 * C) {
+    const int x = tid / C, r = tid % C;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) sum += nrw[(2 * v + x) * C + r];
+    nrm[tid] = sum;
+  }
+  __syncthreads();  // the sums of squares
 
   // ---- reciprocal norms; gate products (scan down the rows as in the dq/dk
   // pass); regularity; Kt, Rk to LDS rows; Z starts as V
@@ -1318,7 +1412,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
       }
       colsum += __shfl_xor(colsum, 16);
       colsum += __shfl_xor(colsum, 32);
-      if (lq == 0) atomicAdd(dbl + j, colsum);
+      if (lq == 0) dbp[tr * C + j] = colsum;
     }
   }
   // the upper tiles: dP and dX zero
@@ -1370,15 +1464,23 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         for (int i = 0; i < 4; ++i) rs[i] += __shfl_xor(rs[i], o, 64);
       if (l16 == 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(dbl + 16 * tr + 4 * lq + i, rs[i]);
+        for (int i = 0; i < 4; ++i) dba[tc * C + 16 * tr + 4 * lq + i] = rs[i];
     }
   }
   for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, j = e % C;
     if (j / 16 > r / 16) b.cdG[slot * C * C + e] = 0;
   }
-  __syncthreads();  // dbeta sums
-  if (tid < L) b.dbeta[(t0 + tid) * H + h] = dbl[tid];
+  __syncthreads();  // dbeta parts
+  if (tid < L) {
+    // the tiles' parts in a fixed order
+    float db = 0.f;
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) db += dbp[u * C + tid];
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) db += dba[u * C + tid];
+    b.dbeta[(t0 + tid) * H + h] = db;
+  }
 }
 
 // ---------------------------------------------------------------- 3b: dq, dk
@@ -1626,80 +1728,129 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   }
   const float gch = __shfl(F[NB - 1][3], 48 + l16);  // the chunk's total product, row C - 1
 
-  // ---- products over the chunk rows, split bf16: first those with Rk, then
-  // those with Kt and Qt (fewer fragments live at once)
+  // ---- products over the chunk rows, one MFMA per (row tile, column tile).
+  // The register operand of column tile u holds only that tile's rows (its
+  // half of the 32-wide K slice, the other half zero), so the accumulators
+  // can be read at every tile boundary: dalpha needs the partial sums over
+  // the columns before each tile (see the dalpha block below).
+  auto tile_frag = [](const f32x4& x, int u) {
+    Frag f;
+    const bool hi = (u & 1) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = static_cast<__bf16>(hi ? 0.f : x[i]);
+      f[4 + i] = static_cast<__bf16>(hi ? x[i] : 0.f);
+    }
+    return f;
+  };
+  // the chunk-anchored operands, formed where they are used
+  auto Kt = [&](int t) { return kh[t] * F[t]; };
+  auto Qt = [&](int t) { return qh[t] * F[t]; };
+  auto Rk = [&](int t) { return kh[t] / F[t]; };
+  // F at the last row of each tile (e_t) and at the row before it (a_t)
+  float Fe[NB], Fa[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    Fe[t] = __shfl(F[t][3], 48 + l16);
+    Fa[t] = t == 0 ? 1.f : Fe[t - 1];
+  }
+  // rows: dKt += dG Rk, dQt += dP Rk over column tiles u <= t.  Before column
+  // tile u the accumulators hold the pair terms of the row with the columns
+  // before u (and the chunk start); for u < t their sum over the tile's rows
+  // goes to the corner of tile u (zp), for u = t it is rho.
+  f32x4 rho[NB];
+  float zp[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) zp[t] = 0.f;
   {
-    auto split = [&](const f32x4* x, Frag* hi, Frag* lo) {
-      f32x4 y[NB];
+    Frag rkm[NB];
 #pragma unroll
-      for (int t = 0; t < NB; ++t)
+    for (int u = 0; u < NB; ++u) rkm[u] = tile_frag(Rk(u), u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[t][i] = x[t][i] - static_cast<float>(static_cast<__bf16>(x[t][i]));
-      Op::frags<C>(hi, x);
-      Op::frags<C>(lo, y);
-    };
-    auto mma2 = [&](f32x4& acc, const __bf16* row, int s, const Frag& bh, const Frag& bl) {
-      const Frag ah = Op::row_frag<C>(row, s, lq);
-      Op::mma(acc, ah, bh);
-      Op::mma(acc, ah, bl);
-    };
-    {
-      Frag rkh[NFC], rkl[NFC];
-      f32x4 x[NB];
+    for (int t = 0; t < NB; ++t) {
+      const int ro = (16 * t + l16) * LDC;
 #pragma unroll
-      for (int t = 0; t < NB; ++t) x[t] = kh[t] / F[t];
-      split(x, rkh, rkl);
+      for (int sl = 0; sl <= t / 2; ++sl) {
+        const Frag gA = Op::row_frag<C>(sG + ro, sl, lq), pA = Op::row_frag<C>(sP + ro, sl, lq);
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const int ro = (16 * t + l16) * LDC;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int u = 2 * sl + hh;
+          if (u > t) continue;
+          if (u < t) {
+            const f32x4 kt = Kt(t), qt = Qt(t);
+            float x = 0.f;
 #pragma unroll
-        for (int s = 0; s < NFC; ++s)
-          if (Cfg::lo_live(t, s)) {
-            mma2(dQt[t], sP + ro, s, rkh[s], rkl[s]);
-            mma2(dKt[t], sG + ro, s, rkh[s], rkl[s]);
+            for (int i = 0; i < 4; ++i) x += kt[i] * dKt[t][i] + qt[i] * dQt[t][i];
+            zp[u] += x;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rho[t][i] = Fa[t] * (kh[t][i] * dKt[t][i] + qh[t][i] * dQt[t][i]);
           }
+          Op::mma(dKt[t], gA, rkm[u]);
+          Op::mma(dQt[t], pA, rkm[u]);
+        }
       }
     }
-    {
-      Frag kth[NFC], ktl[NFC], qth[NFC], qtl[NFC];
-      f32x4 x[NB];
+  }
+  // columns: dRk = g dKh + dG^T Kt + dP^T Qt over row tiles u >= t, last
+  // first.  Before row tile t the accumulator holds the pair terms of the
+  // column with the rows after its tile (and the chunk end): kappa.
+  f32x4 kap[NB];
+  {
+    Frag ktm[NB], qtm[NB];
 #pragma unroll
-      for (int t = 0; t < NB; ++t) x[t] = kh[t] * F[t];
-      split(x, kth, ktl);
+    for (int u = 0; u < NB; ++u) {
+      ktm[u] = tile_frag(Kt(u), u);
+      qtm[u] = tile_frag(Qt(u), u);
+    }
 #pragma unroll
-      for (int t = 0; t < NB; ++t) x[t] = qh[t] * F[t];
-      split(x, qth, qtl);
+    for (int t = 0; t < NB; ++t) {
+      const int ro = (16 * t + l16) * LDC;
+      dRk[t] = gch * dKh[t];
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const int ro = (16 * t + l16) * LDC;
+      for (int sl = (NB - 1) / 2; sl >= t / 2; --sl) {
+        const Frag gA = Op::row_frag<C>(sGT + ro, sl, lq), pA = Op::row_frag<C>(sPT + ro, sl, lq);
 #pragma unroll
-        for (int s = 0; s < NFC; ++s)
-          if (Cfg::up_live(t, s)) {
-            mma2(dRk[t], sGT + ro, s, kth[s], ktl[s]);
-            mma2(dRk[t], sPT + ro, s, qth[s], qtl[s]);
+        for (int hh = 1; hh >= 0; --hh) {
+          const int u = 2 * sl + hh;
+          if (u < t || u >= NB) continue;
+          if (u == t) {
+            const float re = 1.f / Fe[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kap[t][i] = kh[t][i] * re * dRk[t][i];
           }
+          Op::mma(dRk[t], gA, ktm[u]);
+          Op::mma(dRk[t], pA, qtm[u]);
+        }
       }
     }
   }
 
   // ---- per element
-  f32x4 dqh[NB], dkh[NB], lam[NB];
-  float dg2 = 0.f;
+  f32x4 dqh[NB], dkh[NB];
+  float ep[NB];  // the chunk end's pair terms with this lane's rows, per tile
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
+    ep[t] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float f = F[t][i], kt = kh[t][i] * f, qt = qh[t][i] * f, rk = kh[t][i] / f;
-      const float drk = dRk[t][i] + gch * dKh[t][i];
-      dg2 += dKh[t][i] * rk;
-      dkh[t][i] = dKt[t][i] * f + drk / f;
+      const float f = F[t][i];
+      dkh[t][i] = dKt[t][i] * f + dRk[t][i] / f;
       dqh[t][i] = dQt[t][i] * f;
-      lam[t][i] = dKt[t][i] * kt + dQt[t][i] * qt - drk * rk;
+      ep[t] += gch * dKh[t][i] * (kh[t][i] / f);
     }
   }
-  dg += dg2;
+  // over the four lane groups (the tile's 16 rows): the chunk end's pair with
+  // the chunk start (dg), the corner sums and the end pairs per tile
   dg += __shfl_xor(dg, 16);
   dg += __shfl_xor(dg, 32);
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    zp[t] += __shfl_xor(zp[t], 16);
+    zp[t] += __shfl_xor(zp[t], 32);
+    ep[t] += __shfl_xor(ep[t], 16);
+    ep[t] += __shfl_xor(ep[t], 32);
+  }
 
   // outputs through buffer stores whose range ends at row L: the stores of
   // rows >= L are dropped by the range check, with no branch around them
@@ -1710,31 +1861,6 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), make_rsrc(out + obase, orange),
                                           ooff + (16 * t + i) * H * DK * 4, 0, 0);
   };
-
-  // ---- dalpha: reverse running sums of Lam down the rows (within the lane,
-  // across lane groups, tile to tile), divided by alpha
-  {
-    float carry = dg * gch;
-#pragma unroll
-    for (int t = NB - 1; t >= 0; --t) {
-      float suf[4];
-      suf[3] = lam[t][3];
-      suf[2] = suf[3] + lam[t][2];
-      suf[1] = suf[2] + lam[t][1];
-      suf[0] = suf[1] + lam[t][0];
-      float inc = suf[0];
-      float y = __shfl_down(inc, 16);
-      if (lq <= 2) inc += y;
-      y = __shfl_down(inc, 32);
-      if (lq <= 1) inc += y;
-      float exc = __shfl_down(inc, 16);
-      if (lq == 3) exc = 0.f;
-      const float tot = __shfl(inc, l16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ostore(b.dalpha, t, i, (carry + exc + suf[i]) / xa[t][i]);
-      carry += tot;
-    }
-  }
 
   // ---- through the norms: row sums q^ . dq^ and k^ . dk^ over the
   // channels.  Over the wave's 16 lanes by a butterfly that halves the
@@ -1795,6 +1921,153 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
       ostore(b.dk, t, i, l2 ? nk[t][i] * (dkh[t][i] - kh[t][i] * pk[i]) : dkh[t][i]);
     }
   }
+  // ---- dalpha, with no division by a gate.  dL/dalpha_s sums, over the
+  // pairs (r, j) of positions with j < s <= r (rows of the chunk, its start
+  // and its end), the pair's adjoint times D(r<-s) D(s-1<-j), the partial
+  // gate products on either side of s.  For s in tile b (a_b, e_b the rows
+  // before and at its ends), split by where r and j lie:
+  //   r in b, j before b:      Pre_s * sum_{r>=s in b} D(r<-s) rho_r
+  //   r after b, j in b:       Suf_s * sum_{j<s in b} D(s-1<-j) kappa_j
+  //   r after b, j before b:   Pre_s * Suf_s * Gamma_b
+  //   both in b:               Psi_s, pairwise
+  // Pre_s = D(s-1<-a_b), Suf_s = D(e_b<-s) are products inside the tile;
+  // rho, kappa and Gamma_b are the pair terms anchored at the tile's edges,
+  // formed above from the chunk-anchored operands (ratios of running
+  // products within [2^-100, 2^10], so bounded and accurate).  The sums over
+  // the tile run as recurrences across the lane's 4 rows and then across
+  // the 4 lane groups, so no pair term is formed twice and none cancels.
+  {
+    const float gdg = gch * dg;  // the (end, start) pair: adjoint dg times D = g
+    float ecum = 0.f;            // the end's pairs with the columns before tile b
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      const float gam = (gdg + ecum + zp[tb]) * (Fa[tb] / Fe[tb]);
+      ecum += ep[tb];
+      // the lane's gates in tile b (1 beyond the chunk's rows); exclusive
+      // products inside the lane (lp: rows before, ls: rows after) and over
+      // the lane groups below and above inside the tile
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = 16 * tb + 4 * lq + i < L ? xa[tb][i] : 1.f;
+      float lp[4], ls[4];
+      lp[0] = 1.f;
+      lp[1] = al[0];
+      lp[2] = lp[1] * al[1];
+      lp[3] = lp[2] * al[2];
+      ls[3] = 1.f;
+      ls[2] = al[3];
+      ls[1] = ls[2] * al[2];
+      ls[0] = ls[1] * al[1];
+      const float tot = lp[3] * al[3];
+      float up = tot, y;
+      y = __shfl_up(up, 16);
+      if (lq >= 1) up *= y;
+      y = __shfl_up(up, 32);
+      if (lq >= 2) up *= y;
+      float below = __shfl_up(up, 16);
+      if (lq == 0) below = 1.f;
+      float dn = tot;
+      y = __shfl_down(dn, 16);
+      if (lq <= 2) dn *= y;
+      y = __shfl_down(dn, 32);
+      if (lq <= 1) dn *= y;
+      float above = __shfl_down(dn, 16);
+      if (lq == 3) above = 1.f;
+      // sigma_s = rho_s + alpha_{s+1} sigma_{s+1}: inside the lane, then the
+      // carry alpha sigma of the next lane group's first row, top down
+      float sg[4];
+      sg[3] = rho[tb][3];
+      sg[2] = rho[tb][2] + al[3] * sg[3];
+      sg[1] = rho[tb][1] + al[2] * sg[2];
+      sg[0] = rho[tb][0] + al[1] * sg[1];
+      float cin = 0.f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float x = __shfl_down(al[0] * (sg[0] + ls[0] * cin), 16);
+        cin = lq == 3 ? 0.f : x;
+      }
+      // pi_{s+1} = alpha_s pi_s + kappa_s: inside the lane, then the carry of
+      // the lane group below, bottom up
+      float pg[4];
+      pg[0] = 0.f;
+      pg[1] = kap[tb][0];
+      pg[2] = al[1] * pg[1] + kap[tb][1];
+      pg[3] = al[2] * pg[2] + kap[tb][2];
+      float pin = 0.f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float x = __shfl_up(al[3] * (pg[3] + lp[3] * pin) + kap[tb][3], 16);
+        pin = lq == 0 ? 0.f : x;
+      }
+      // pairs inside the tile.  The tile's gates and keys from the lanes
+      // that hold them; for each of the lane's rows r,
+      // Phi_r(s) = sum_{j<s} adj_rj D(s-1<-j) by a recurrence over s, then
+      // D(r<-s) Phi_r(s) added to s's sum (ps); ps is then reduced over the
+      // four lane groups, each keeping its own rows.
+      float aj[16], kj[16];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          aj[4 * q2 + i2] = __shfl(al[i2], l16 + 16 * q2);
+          kj[4 * q2 + i2] = __shfl(kh[tb][i2], l16 + 16 * q2);
+        }
+      float ps[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ps[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * lq + i;  // the row inside the tile
+        const __bf16* gr = sG + (16 * tb + rr) * LDC;
+        const __bf16* pr = sP + (16 * tb + rr) * LDC;
+        const float kr = kh[tb][i], qr = qh[tb][i];
+        float phi = 0.f, phis[16];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          // dG_rj, dP_rj for the 4 columns j = 4 q2 .. 4 q2 + 3 of the tile
+          const int off = C % 32 == 0 ? 32 * (tb >> 1) + 8 * q2 + 4 * (tb & 1) : 4 * q2;
+          const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gr + off);
+          const bf16x4 p4 = *reinterpret_cast<const bf16x4*>(pr + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * q2 + e;
+            if (j == 15) break;  // the last column pairs with no later row
+            const float adj = j < rr ? (static_cast<float>(g4[e]) * kr + static_cast<float>(p4[e]) * qr) * kj[j] : 0.f;
+            phi = aj[j] * phi + adj;
+            phis[j + 1] = phi;
+          }
+        }
+        float d = 1.f;
+#pragma unroll
+        for (int si = 15; si >= 1; --si) {
+          const bool tk = si <= rr;
+          ps[si] += tk ? d * phis[si] : 0.f;
+          d = tk ? d * aj[si] : d;
+        }
+      }
+      float h8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool hi = lq >= 2;
+        const float keep = hi ? ps[8 + e] : ps[e], send = hi ? ps[e] : ps[8 + e];
+        h8[e] = keep + __shfl_xor(send, 32);
+      }
+      float psi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool odd = (lq & 1) != 0;
+        const float keep = odd ? h8[4 + e] : h8[e], send = odd ? h8[e] : h8[4 + e];
+        psi[e] = keep + __shfl_xor(send, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pre = below * lp[i], suf = ls[i] * above;
+        const float sigma = sg[i] + ls[i] * cin, pi = pg[i] + lp[i] * pin;
+        ostore(b.dalpha, tb, i, pre * sigma + suf * pi + pre * suf * gam + psi[i]);
+      }
+    }
+  }
+
 }
 
 // ---------------------------------------------------------------- 4: token

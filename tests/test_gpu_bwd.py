@@ -1,13 +1,11 @@
 """GPU parity of the chunked backward (ckda_chunk_bwd through the C ABI)
 against the oracle's gradients (oracle.bwd, pinned by finite differences).
 
-Tolerances (max-normalised error per tensor): float32 io 1e-4 and bf16 io
-2e-2 for dq, dk, dv, dbeta, dh0 and for alpha * dalpha (the log-derivative of
-the gates), everywhere.  dalpha itself is that log-derivative divided by
-alpha in the ratio form, so its absolute error grows like 1/|alpha| as a gate
-approaches zero (the derivative with respect to a near-zero gate is
-ill-conditioned there); it is held to the same tolerances where
-|alpha| >= 1/16, and the token-level path (exact zero gates) is exact."""
+Tolerances (max-normalised error per tensor, every element): float32 io 1e-4
+and bf16 io 2e-2 for dq, dk, dv, dalpha, dbeta and dh0.  dalpha is formed
+with no division by a gate (pairs of positions that straddle the gate, times
+the partial gate products on either side of it), so gates near zero (1e-3,
+1e-5) are held to the same bound as the others."""
 import numpy as np
 import pytest
 import torch
@@ -15,24 +13,17 @@ import torch
 import gated_delta_rule_ckda_amd as ck
 import oracle
 from gated_delta_rule_ckda_amd import inputs
-from tests.gpu_util import DEV, announce, dev, host, max_rel_err
+from tests.gpu_util import DEV, announce, cover_pairs, dev, host, max_rel_err
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-ALPHA_MIN = 1.0 / 16
 NAMES = ["dq", "dk", "dv", "dalpha", "dbeta", "dh0"]
 
 
-def _grad_errs(g, r, alpha):
-    """Errors per gradient; dalpha over |alpha| >= ALPHA_MIN (normalised by
-    the max over all elements), a*dalpha everywhere."""
-    errs = {n: max_rel_err(x, y) for n, x, y in zip(NAMES, g, r) if n != "dalpha"}
-    m = np.abs(alpha) >= ALPHA_MIN
-    den = np.abs(r[3]).max()
-    errs["dalpha"] = float(np.abs(g[3] - r[3])[m].max() / den) if m.any() and den > 0 else 0.0
-    errs["a*dalpha"] = max_rel_err(g[3] * alpha, r[3] * alpha)
-    return errs
+def _grad_errs(g, r):
+    """Max-normalised error of each gradient over all of its elements."""
+    return {n: max_rel_err(x, y) for n, x, y in zip(NAMES, g, r)}
 
 
 def _grad_case(seed, B, T, H, d, dtype, l2=True, zero_frac=0.0, gates="tanh", h0=True,
@@ -41,8 +32,11 @@ def _grad_case(seed, B, T, H, d, dtype, l2=True, zero_frac=0.0, gates="tanh", h0
     q, k, v = (rng.standard_normal((B, T, H, d)).astype(np.float32) for _ in range(3))
     if not l2:  # unit keys: the method's range assumes them without the norm
         k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
-    if gates == "tanh":
+    if gates in ("tanh", "tiny"):
         a = np.tanh(rng.normal(2, 1, (B, T, H, d))) * rng.choice([-1, 1], (B, T, H, d))
+        if gates == "tiny":  # 4% of the gates at +-1e-3 or +-1e-5
+            m = rng.random(a.shape) < 0.04
+            a[m] = rng.choice([-1, 1], m.sum()) * rng.choice([1e-3, 1e-5], m.sum())
     elif gates == "uniform":
         a = rng.uniform(-1, 1, (B, T, H, d))
     else:  # kda: positive
@@ -71,7 +65,7 @@ def _check(c, dtype, chunk, l2=True, scale=1.0, gate="ckda"):
     g = [host(x) for x in g]
     r = oracle.bwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["dO"], h0=c["h0"],
                    dht=c["dht"], seq_start=c["cu"], use_l2norm=l2, scale=scale)
-    errs = _grad_errs(g, r, c["alpha"])
+    errs = _grad_errs(g, r)
     print("  " + " ".join("%s=%.2e" % kv for kv in errs.items()))
     for n, e in errs.items():
         assert e < TOL[dtype], (n, e)
@@ -125,10 +119,28 @@ def test_bwd_gradient_of_zero_gate_is_not_zero():
     assert np.abs(r[3][0, 10, 0]).max() > 1e-3 and np.abs(g[3][0, 10, 0]).max() > 1e-3
 
 
+def _oracle_bwd_pairs(q, k, v, a, b, dO, dht, pairs):
+    """oracle.bwd on (batch, head) pairs of a dense case, all in one packed
+    call (one sequence per pair, one head), which the oracle runs in
+    parallel; returns {(n, h): six gradients shaped [T, ...]}."""
+    T = q.shape[1]
+    cat = lambda x: np.concatenate([x[n, :, h:h + 1] for n, h in pairs], 0)[None]
+    starts = np.arange(len(pairs) + 1, dtype=np.int64) * T
+    dh = np.stack([dht[n, h:h + 1] for n, h in pairs], 0)
+    r = oracle.bwd(cat(q), cat(k), cat(v), cat(a), cat(b), cat(dO), dht=dh, seq_start=starts)
+    out = {}
+    for i, p in enumerate(pairs):
+        sl = slice(i * T, (i + 1) * T)
+        out[p] = [r[0][0, sl, 0], r[1][0, sl, 0], r[2][0, sl, 0], r[3][0, sl, 0],
+                  r[4][0, sl, 0], r[5][i, 0]]
+    return out
+
+
 def test_bwd_lm_layer_full_sampled():
     """The LM layer (B=8, T=4096, H=16, d=128, bf16, chunk 64) at full size,
-    random output and final-state gradients; oracle gradients on sampled
-    (batch, head) pairs."""
+    random output and final-state gradients; oracle gradients on 16 sampled
+    (batch, head) pairs covering every batch and head index, every element
+    of every gradient (dalpha included) held to the bf16 bound."""
     announce("bwd LM layer full size")
     c = inputs.lm_layer(arm="ckda")
     rng = np.random.default_rng(77)
@@ -138,16 +150,60 @@ def test_bwd_lm_layer_full_sampled():
                      dev(c.beta), dev(dO, "bf16"), dht=dev(dht), chunk_size=64)
     torch.cuda.synchronize()
     g = [host(x) for x in g]
-    oracle.set_num_threads(1)
-    try:
-        for (n, h) in [(0, 0), (5, 11)]:
-            sl = lambda x: x[n:n + 1, :, h:h + 1]
-            r = oracle.bwd(sl(c.q), sl(c.k), sl(c.v), sl(c.alpha), c.beta[n:n + 1, :, h:h + 1],
-                           sl(dO), dht=dht[n:n + 1, h:h + 1])
-            ours = [sl(g[0]), sl(g[1]), sl(g[2]), sl(g[3]), g[4][n:n + 1, :, h:h + 1],
-                    g[5][n:n + 1, h:h + 1]]
-            errs = _grad_errs(ours, r, sl(c.alpha))
-            print("  pair", (n, h), " ".join("%s=%.2e" % kv for kv in errs.items()))
-            assert max(errs.values()) < TOL["bf16"]
-    finally:
-        oracle.set_num_threads(oracle.max_threads())
+    pairs = cover_pairs(8, 16)
+    ref = _oracle_bwd_pairs(c.q, c.k, c.v, c.alpha, c.beta, dO, dht, pairs)
+    worst = {}
+    for (n, h) in pairs:
+        ours = [g[0][n, :, h], g[1][n, :, h], g[2][n, :, h], g[3][n, :, h], g[4][n, :, h],
+                g[5][n, h]]
+        for name, e in _grad_errs(ours, ref[(n, h)]).items():
+            worst[name] = max(worst.get(name, 0.0), e)
+    print("  " + " ".join("%s=%.2e" % kv for kv in worst.items()))
+    assert max(worst.values()) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,chunk,d", [("f32", 32, 32), ("f32", 64, 32), ("f32", 16, 64),
+                                           ("bf16", 64, 128), ("bf16", 32, 64),
+                                           ("bf16", 16, 128)])
+def test_bwd_gates_near_zero(dtype, chunk, d):
+    """Gates of +-1e-3 and +-1e-5 among tanh gates of both signs: dalpha is
+    held to the bound on every element, with no mask (chunks whose running
+    products stay in range take the MFMA form, the others the token path)."""
+    announce("bwd gates near zero %s C=%d d=%d" % (dtype, chunk, d))
+    _check(_grad_case(1100 + chunk + d, 2, 2 * chunk + 5, 2, d, dtype, gates="tiny"), dtype,
+           chunk)
+
+
+@pytest.mark.parametrize("dtype,chunk,d", [("f32", 16, 16), ("bf16", 16, 64), ("bf16", 64, 128)])
+def test_bwd_uniform_gates(dtype, chunk, d):
+    """alpha ~ U[-1, 1]: gates anywhere in the CKDA range, near zero included."""
+    announce("bwd U[-1,1] gates %s C=%d d=%d" % (dtype, chunk, d))
+    _check(_grad_case(1200 + chunk + d, 2, 3 * chunk + 1, 2, d, dtype, gates="uniform"), dtype,
+           chunk)
+
+
+def test_bwd_bf16_packed_chunk64():
+    """bf16 packed batch at chunk 64, d=128 on the matrix-core passes: unequal
+    lengths with empty sequences and a long chain, N * H = 16 (so the adjoint
+    state pass's longest-first order and its workgroup mapping both act)."""
+    announce("bwd bf16 packed C=64 d=128")
+    lens = [0, 300, 17, 64, 0, 129, 451, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    c = _grad_case(1300, 1, cu[-1], 2, 128, "bf16", cu=cu)
+    _check(c, "bf16", 64)
+
+
+@pytest.mark.parametrize("dtype,chunk,d", [("bf16", 64, 128), ("f32", 32, 32)])
+def test_bwd_is_deterministic(dtype, chunk, d):
+    """Two calls on the same inputs give bit-identical gradients (every
+    reduction runs in a fixed order; no atomics)."""
+    announce("bwd determinism %s C=%d d=%d" % (dtype, chunk, d))
+    c = _grad_case(1400 + d, 2, 4 * chunk + 9, 4, d, dtype, gates="tiny")
+    args = (dev(c["q"], dtype), dev(c["k"], dtype), dev(c["v"], dtype), dev(c["alpha"]),
+            dev(c["beta"]), dev(c["dO"], dtype))
+    kw = dict(h0=dev(c["h0"]), dht=dev(c["dht"]), chunk_size=chunk)
+    g1 = [host(x) for x in ck.chunk_bwd(*args, **kw)]
+    g2 = [host(x) for x in ck.chunk_bwd(*args, **kw)]
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, g1, g2):
+        assert np.array_equal(x, y), n
