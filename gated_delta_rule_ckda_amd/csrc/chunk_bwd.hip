@@ -1914,11 +1914,14 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const f32x4 pq = *reinterpret_cast<const f32x4*>(fin + 16 * t + 4 * lq);
+    // the row scales, read again here rather than held through the products
+    const f32x4 rq4 = *reinterpret_cast<const f32x4*>(rn + 16 * t + 4 * lq);
+    const f32x4 rk4 = *reinterpret_cast<const f32x4*>(rn + C + 16 * t + 4 * lq);
     const f32x4 pk = *reinterpret_cast<const f32x4*>(fin + C + 16 * t + 4 * lq);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ostore(b.dq, t, i, l2 ? nq[t][i] * (dqh[t][i] - qh[t][i] * pq[i]) : dqh[t][i]);
-      ostore(b.dk, t, i, l2 ? nk[t][i] * (dkh[t][i] - kh[t][i] * pk[i]) : dkh[t][i]);
+      ostore(b.dq, t, i, l2 ? rq4[i] * (dqh[t][i] - qh[t][i] * pq[i]) : dqh[t][i]);
+      ostore(b.dk, t, i, l2 ? rk4[i] * (dkh[t][i] - kh[t][i] * pk[i]) : dkh[t][i]);
     }
   }
   // ---- dalpha, with no division by a gate.  dL/dalpha_s sums, over the
@@ -1929,7 +1932,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   //   r in b, j before b:      Pre_s * sum_{r>=s in b} D(r<-s) rho_r
   //   r after b, j in b:       Suf_s * sum_{j<s in b} D(s-1<-j) kappa_j
   //   r after b, j before b:   Pre_s * Suf_s * Gamma_b
-  //   both in b:               Psi_s, pairwise
+  //   both in b:               Psi_s, pairwise (below)
   // Pre_s = D(s-1<-a_b), Suf_s = D(e_b<-s) are products inside the tile;
   // rho, kappa and Gamma_b are the pair terms anchored at the tile's edges,
   // formed above from the chunk-anchored operands (ratios of running
@@ -2000,10 +2003,11 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
         pin = lq == 0 ? 0.f : x;
       }
       // pairs inside the tile.  The tile's gates and keys from the lanes
-      // that hold them; for each of the lane's rows r,
-      // Phi_r(s) = sum_{j<s} adj_rj D(s-1<-j) by a recurrence over s, then
-      // D(r<-s) Phi_r(s) added to s's sum (ps); ps is then reduced over the
-      // four lane groups, each keeping its own rows.
+      // that hold them.  With Suf_r = D(e_b<-r), D(r<-s) = Suf_s / Suf_r (a
+      // ratio of gates after s), so for each of the lane's rows r one pass
+      //   phi = alpha_j phi + adj_rj / Suf_r  (j < r),  ps_{j+1} += phi
+      // leaves Psi_s = Suf_s * (ps_s summed over the rows r >= s); ps is
+      // then reduced over the four lane groups, each keeping its own rows.
       float aj[16], kj[16];
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2)
@@ -2020,8 +2024,9 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
         const int rr = 4 * lq + i;  // the row inside the tile
         const __bf16* gr = sG + (16 * tb + rr) * LDC;
         const __bf16* pr = sP + (16 * tb + rr) * LDC;
-        const float kr = kh[tb][i], qr = qh[tb][i];
-        float phi = 0.f, phis[16];
+        const float is = 1.f / (ls[i] * above);
+        const float kr = kh[tb][i] * is, qr = qh[tb][i] * is;
+        float phi = 0.f;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
           // dG_rj, dP_rj for the 4 columns j = 4 q2 .. 4 q2 + 3 of the tile
@@ -2032,17 +2037,9 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * q2 + e;
             if (j == 15) break;  // the last column pairs with no later row
-            const float adj = j < rr ? (static_cast<float>(g4[e]) * kr + static_cast<float>(p4[e]) * qr) * kj[j] : 0.f;
-            phi = aj[j] * phi + adj;
-            phis[j + 1] = phi;
+            phi = aj[j] * phi + (static_cast<float>(g4[e]) * kr + static_cast<float>(p4[e]) * qr) * kj[j];
+            ps[j + 1] += j < rr ? phi : 0.f;
           }
-        }
-        float d = 1.f;
-#pragma unroll
-        for (int si = 15; si >= 1; --si) {
-          const bool tk = si <= rr;
-          ps[si] += tk ? d * phis[si] : 0.f;
-          d = tk ? d * aj[si] : d;
         }
       }
       float h8[8];
@@ -2063,7 +2060,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
       for (int i = 0; i < 4; ++i) {
         const float pre = below * lp[i], suf = ls[i] * above;
         const float sigma = sg[i] + ls[i] * cin, pi = pg[i] + lp[i] * pin;
-        ostore(b.dalpha, tb, i, pre * sigma + suf * pi + pre * suf * gam + psi[i]);
+        ostore(b.dalpha, tb, i, pre * sigma + suf * pi + pre * suf * gam + suf * psi[i]);
       }
     }
   }
