@@ -92,6 +92,9 @@ class Oracle:
         lib.ckda_oracle_gates.restype = ctypes.c_int32
         lib.ckda_oracle_gates.argtypes = [ctypes.c_int64, dp, ctypes.c_int64, dp,
                                           ctypes.c_int32, dp, dp]
+        lib.ckda_oracle_gates_bwd.restype = ctypes.c_int32
+        lib.ckda_oracle_gates_bwd.argtypes = [ctypes.c_int64, dp, dp, ctypes.c_int64, dp, dp,
+                                              ctypes.c_int32, dp, dp]
         lib.ckda_oracle_set_num_threads.restype = None
         lib.ckda_oracle_set_num_threads.argtypes = [ctypes.c_int32]
         lib.ckda_oracle_max_threads.restype = ctypes.c_int32
@@ -127,6 +130,22 @@ class Oracle:
         if rc != 0:
             raise ValueError("ckda_oracle_gates failed with code %d" % rc)
         return alpha, beta
+
+    def gates_bwd(self, a, b, dalpha, dbeta, ckda_range=True):
+        """Gradients with respect to the logits a, b given those with respect
+        to the gates they activate (chain rule through gates()).  fp64,
+        shapes of a and b."""
+        a, b, dalpha, dbeta = _f64(a), _f64(b), _f64(dalpha), _f64(dbeta)
+        if dalpha.shape != a.shape or dbeta.shape != b.shape:
+            raise ValueError("oracle.gates_bwd: gradients must match the logits' shapes")
+        da = np.empty_like(a)
+        db = np.empty_like(b)
+        rc = self.lib.ckda_oracle_gates_bwd(a.size, _ptr(a), _ptr(dalpha), b.size, _ptr(b),
+                                            _ptr(dbeta), int(bool(ckda_range)), _ptr(da),
+                                            _ptr(db))
+        if rc != 0:
+            raise ValueError("ckda_oracle_gates_bwd failed with code %d" % rc)
+        return da, db
 
     def fwd(self, q, k, v, alpha, beta, h0=None, seq_start=None, use_l2norm=True,
             scale=1.0, eps=EPS):
@@ -241,6 +260,10 @@ def l2norm(x, eps: float = EPS) -> np.ndarray:
 
 def gates(*args, **kwargs):
     return default().gates(*args, **kwargs)
+
+
+def gates_bwd(*args, **kwargs):
+    return default().gates_bwd(*args, **kwargs)
 
 
 def fwd(*args, **kwargs):

@@ -110,6 +110,31 @@ int32_t ckda_oracle_gates(int64_t n_alpha, const double* a, int64_t n_beta,
   return ORACLE_OK;
 }
 
+/*
+ * Gradients through the gate activation above: given dL/dalpha and dL/dbeta
+ * (the gates' gradients, e.g. from ckda_oracle_bwd), dL/da = dL/dalpha *
+ * dalpha/da and dL/db = dL/dbeta * dbeta/db, with the derivative of the
+ * sigmoid s(x) = 1 / (1 + e^-x) being s(x) (1 - s(x)); the CKDA range doubles
+ * it for both gates (alpha = 2 s(a) - 1, beta = 2 s(b)).
+ */
+int32_t ckda_oracle_gates_bwd(int64_t n_alpha, const double* a, const double* dalpha,
+                              int64_t n_beta, const double* b, const double* dbeta,
+                              int32_t ckda_range, double* da, double* db) {
+  if (n_alpha < 0 || n_beta < 0) return ORACLE_BAD_ARG;
+  if ((n_alpha > 0 && (!a || !dalpha || !da)) || (n_beta > 0 && (!b || !dbeta || !db)))
+    return ORACLE_BAD_ARG;
+  const double f = ckda_range ? 2.0 : 1.0;
+  for (int64_t i = 0; i < n_alpha; ++i) {
+    const double s = sigmoid(a[i]);
+    da[i] = dalpha[i] * f * s * (1.0 - s);
+  }
+  for (int64_t i = 0; i < n_beta; ++i) {
+    const double s = sigmoid(b[i]);
+    db[i] = dbeta[i] * f * s * (1.0 - s);
+  }
+  return ORACLE_OK;
+}
+
 /* One sequence, one head: runs tokens [t0, t1) in order on the state S. */
 static void run_head(int64_t t0, int64_t t1, int32_t h, int32_t H, int32_t dk,
                      int32_t dv, const double* q, const double* k,

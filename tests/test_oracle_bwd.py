@@ -140,3 +140,98 @@ def test_pins_catch_bwd_mutants(name, tmp_path):
         except (AssertionError, ValueError):
             red.append(pin.__name__)
     assert red, "mutant %s passed every pin" % name
+
+
+# ---------------------------------------------------------- gates from logits
+def _gates_loss_grads(orc, seed, ckda_range):
+    """A small case with logit gates; the loss L = <o, Ro> + <ht, Rh> through
+    gates(a, b) and the forward; returns (a, b, loss function of (a, b),
+    (dL/da, dL/db) from bwd and gates_bwd)."""
+    rng = np.random.default_rng(seed)
+    B, T, H, dk, dv = 2, 9, 2, 4, 3
+    q, k, v = rng.normal(size=(B, T, H, dk)), rng.normal(size=(B, T, H, dk)), rng.normal(size=(B, T, H, dv))
+    a = rng.normal(0, 2, size=(B, T, H, dk))
+    b = rng.normal(0, 1.5, size=(B, T, H))
+    h0 = rng.normal(size=(B, H, dk, dv))
+    Ro, Rh = rng.normal(size=v.shape), rng.normal(size=(B, H, dk, dv))
+
+    def loss(a_, b_):
+        al, be = orc.gates(a_, b_, ckda_range=ckda_range)
+        o, ht = orc.fwd(q, k, v, al, be, h0=h0)
+        return float((o * Ro).sum() + (ht * Rh).sum())
+
+    al, be = orc.gates(a, b, ckda_range=ckda_range)
+    g = orc.bwd(q, k, v, al, be, Ro, h0=h0, dht=Rh)
+    da, db = orc.gates_bwd(a, b, g[3], g[4], ckda_range=ckda_range)
+    return a, b, loss, da, db
+
+
+def pin_gates_bwd_finite_differences(orc):
+    """dL/da and dL/db through the activation (both ranges) against central
+    differences of the loss computed with the oracle's gates and forward."""
+    for ckda_range in (True, False):
+        a, b, loss, da, db = _gates_loss_grads(orc, 31 + int(ckda_range), ckda_range)
+        rng = np.random.default_rng(33)
+        eps = 1e-6
+        for x, g, name in ((a, da, "a"), (b, db, "b")):
+            d = rng.normal(size=x.shape)
+            if name == "a":
+                fd = (loss(a + eps * d, b) - loss(a - eps * d, b)) / (2 * eps)
+            else:
+                fd = (loss(a, b + eps * d) - loss(a, b - eps * d)) / (2 * eps)
+            an = float((g * d).sum())
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (ckda_range, name, fd, an)
+
+
+def pin_gates_bwd_closed_forms(orc):
+    """At a logit of 0: dalpha/da = 1/2 (CKDA, alpha = 2 s(a) - 1) and 1/4
+    (KDA, alpha = s(a)); the same for beta.  The derivative is even in the
+    logit, and the CKDA derivative is twice the KDA one everywhere."""
+    z = np.zeros(3)
+    one = np.ones(3)
+    da, db = orc.gates_bwd(z, z, one, one, ckda_range=True)
+    assert np.all(da == 0.5) and np.all(db == 0.5)
+    da, db = orc.gates_bwd(z, z, one, one, ckda_range=False)
+    assert np.all(da == 0.25) and np.all(db == 0.25)
+    x = np.linspace(-9, 9, 37)
+    g = np.random.default_rng(34).normal(size=x.shape)
+    c1, _ = orc.gates_bwd(x, x, g, g, ckda_range=True)
+    c2, _ = orc.gates_bwd(-x, x, g, g, ckda_range=True)
+    k1, _ = orc.gates_bwd(x, x, g, g, ckda_range=False)
+    # (1 - s) is formed after s, so large |logit| lose a few digits to rounding
+    np.testing.assert_allclose(c1, c2, rtol=1e-10, atol=0)
+    np.testing.assert_allclose(c1, 2 * k1, rtol=1e-15, atol=0)
+
+
+GATE_PINS = [pin_gates_bwd_finite_differences, pin_gates_bwd_closed_forms]
+
+
+@pytest.mark.parametrize("pin", GATE_PINS, ids=[p.__name__[4:] for p in GATE_PINS])
+def test_gate_pin(pin):
+    pin(oracle.default())
+
+
+GATE_MUTANTS = {
+    "range_factor_dropped": ("const double f = ckda_range ? 2.0 : 1.0;",
+                             "const double f = 1.0;"),
+    "sigmoid_not_its_derivative": ("da[i] = dalpha[i] * f * s * (1.0 - s);",
+                                   "da[i] = dalpha[i] * f * s;"),
+    "beta_uses_alpha_logit": ("const double s = sigmoid(b[i]);", "const double s = sigmoid(a[i]);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATE_MUTANTS))
+def test_gate_pins_catch_mutants(name, tmp_path):
+    src = open(oracle.SOURCE).read()
+    old, new = GATE_MUTANTS[name]
+    assert src.count(old) == 1, "mutation target must appear once in the oracle source"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    orc = oracle.Oracle(oracle.compile_source(str(path), str(tmp_path / ("libg_%s.so" % name))))
+    red = []
+    for pin in GATE_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError):
+            red.append(pin.__name__)
+    assert red, "mutant %s passed every gate pin" % name
