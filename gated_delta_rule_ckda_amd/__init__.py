@@ -260,11 +260,13 @@ def chunk_bwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
 
 def chunk_bwd(q, k, v, alpha, beta, dout, *, h0=None, dht=None, cu_seqlens=None, chunk_size=64,
               use_qk_l2norm=True, gate="ckda", scale=1.0, output_dh0=True, workspace=None,
-              stream=None):
+              stream=None, gates="values"):
     """Gradients of chunk_fwd for dL/do = dout (dtype of v) and dL/dht = dht
-    ([N,H,dk,dv] float32, None for zero).  Gate values (not logits), q/k
-    heads equal to value heads.  Returns float32 (dq, dk, dv, dalpha, dbeta,
-    dh0) shaped like q, k, v, alpha, beta and [N,H,dk,dv] (dh0 None unless
+    ([N,H,dk,dv] float32, None for zero).  Same layouts as chunk_fwd: q, k on
+    Hk heads (grouped value heads when Hk < H), gates='values' (float32
+    gates) or 'logits' (float32 or bfloat16 logits; the gradients are then
+    those of the logits).  Returns float32 (dq, dk, dv, dalpha, dbeta, dh0)
+    shaped like q, k, v, alpha, beta and [N,H,dk,dv] (dh0 None unless
     output_dh0)."""
     import torch
     lib = _load()
@@ -274,15 +276,17 @@ def chunk_bwd(q, k, v, alpha, beta, dout, *, h0=None, dht=None, cu_seqlens=None,
         _require(t.is_cuda and t.is_contiguous(), "%s must be a contiguous device tensor" % name)
     _require(k.dtype == q.dtype and v.dtype == q.dtype and dout.dtype == q.dtype,
              "q, k, v, dout must share a dtype")
-    _require(alpha.dtype == torch.float32 and beta.dtype == torch.float32,
-             "the backward takes float32 gate values")
+    gi = _gate_input(gates, alpha, beta)
     if cu_seqlens is not None:
         _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda,
                  "cu_seqlens must be an int32 device tensor")
     desc = _make_desc(q, v, H, dk, dv, chunk_size, gate, use_qk_l2norm, scale, cu_seqlens,
-                      GATES_F32, False)
-    _require(q.numel() == desc.B * desc.T * H * dk, "q must have H heads (no grouped heads)")
-    _require(k.numel() == q.numel() and alpha.numel() == q.numel(), "k, alpha must match q")
+                      gi, False)
+    Hk = desc.qk_heads
+    _require(H % Hk == 0, "the q/k heads must divide the value heads")
+    _require(q.numel() == desc.B * desc.T * Hk * dk, "q has the wrong number of elements")
+    _require(k.numel() == q.numel(), "k must match q")
+    _require(alpha.numel() == desc.B * desc.T * H * dk, "alpha has the wrong number of elements")
     _require(v.numel() == desc.B * desc.T * H * dv and dout.numel() == v.numel(),
              "v, dout have the wrong number of elements")
     _require(beta.numel() == desc.B * desc.T * H, "beta has the wrong number of elements")
@@ -292,7 +296,8 @@ def chunk_bwd(q, k, v, alpha, beta, dout, *, h0=None, dht=None, cu_seqlens=None,
                      and t.numel() == desc.num_seqs * H * dk * dv,
                      "%s must be [N,H,dk,dv] float32" % name)
     f32 = dict(device=q.device, dtype=torch.float32)
-    dq, dkk, dal = (torch.empty(q.shape, **f32) for _ in range(3))
+    dq, dkk = (torch.empty(q.shape, **f32) for _ in range(2))
+    dal = torch.empty(alpha.shape, **f32)
     dvv = torch.empty(v.shape, **f32)
     dbe = torch.empty(beta.shape, **f32)
     dh0 = torch.empty((desc.num_seqs, H, dk, dv), **f32) if output_dh0 else None

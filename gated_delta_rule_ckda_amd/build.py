@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libckda.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.hip", "decode.hip", "chunk_prep.hip", "chunk_state.hip", "sign_absorb.hip",
-           "chunk_bwd.hip"]
+           "chunk_bwd.hip", "bwd_gates.hip"]
 ARCH = os.environ.get("CKDA_ARCH", "gfx950")
 
 CFLAGS = [

@@ -144,8 +144,12 @@ size_t ckda_chunk_bwd_workspace_size(const ckda_fwd_desc_t* d, int32_t packed) {
   if (d->io_dtype != CKDA_DTYPE_BF16 && d->io_dtype != CKDA_DTYPE_F32) return 0;
   if (d->chunk_size != 16 && d->chunk_size != 32 && d->chunk_size != 64) return 0;
   if (static_cast<int64_t>(d->B) * d->T == 0 || d->num_seqs == 0) return 0;
-  return ckda::bwd_workspace_bytes(d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size,
-                                   d->io_dtype, packed != 0);
+  if (!valid_gate_input(d->gate_input) || !valid_qk_heads(d->H, d->qk_heads)) return 0;
+  const size_t core = ckda::bwd_workspace_bytes(d->B, d->T, d->H, d->dk, d->dv, d->num_seqs,
+                                                d->chunk_size, d->io_dtype, packed != 0);
+  const size_t extra = ckda::bwd_gates_extra_bytes(d->B, d->T, d->H, qk_heads_of(d->H, d->qk_heads),
+                                                   d->dk, d->io_dtype, d->gate_input != CKDA_GATES_F32);
+  return extra == 0 ? core : ((core + 255) & ~size_t(255)) + extra;
 }
 
 }  // extern "C"
@@ -272,10 +276,6 @@ ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
   ckda_status_t st = validate_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, dout, nullptr, nullptr,
                                   0, kPrepare | kFinish, false);
   if (st != CKDA_OK) return st;
-  if (d->gate_input != CKDA_GATES_F32)
-    return fail(CKDA_ERR_UNSUPPORTED, "the backward takes gate values (gate_input 0), not logits");
-  if (qk_heads_of(d->H, d->qk_heads) != d->H)
-    return fail(CKDA_ERR_UNSUPPORTED, "the backward needs qk_heads == H (no grouped heads)");
   if (d->sign_absorb != 0)
     return fail(CKDA_ERR_UNSUPPORTED, "the backward has no sign-absorption path");
   const int64_t tokens = static_cast<int64_t>(d->B) * d->T;
@@ -287,16 +287,18 @@ ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
     if (outp[i] && !aligned16(outp[i]))
       return fail(CKDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", onames[i]);
   if (dht && !aligned16(dht)) return fail(CKDA_ERR_INVALID_ARGUMENT, "dht is not 16-byte aligned");
-  const int64_t eb = elem_bytes(d->io_dtype);
+  const int64_t eb = elem_bytes(d->io_dtype), gb = gate_bytes(d->gate_input);
+  const int32_t Hk = qk_heads_of(d->H, d->qk_heads);
   const int64_t state_bytes = static_cast<int64_t>(d->num_seqs) * d->H * d->dk * d->dv * 4;
-  const int64_t nqk = tokens * d->H * d->dk, nv = tokens * d->H * d->dv;
+  // q, k, dq, dk on the q/k heads; alpha, dalpha, beta, dbeta on the value heads
+  const int64_t nqk = tokens * Hk * d->dk, na = tokens * d->H * d->dk, nv = tokens * d->H * d->dv;
   const Range outs[] = {range("dq", dq, dq ? 4 * nqk : 0), range("dk", dk, dk ? 4 * nqk : 0),
-                        range("dv", dv, dv ? 4 * nv : 0), range("dalpha", dalpha, dalpha ? 4 * nqk : 0),
+                        range("dv", dv, dv ? 4 * nv : 0), range("dalpha", dalpha, dalpha ? 4 * na : 0),
                         range("dbeta", dbeta, dbeta ? 4 * tokens * d->H : 0),
                         range("dh0", dh0, dh0 ? state_bytes : 0)};
   const Range ins[] = {range("q", q, q ? nqk * eb : 0), range("k", k, k ? nqk * eb : 0),
-                       range("v", v, v ? nv * eb : 0), range("alpha", alpha, alpha ? 4 * nqk : 0),
-                       range("beta", beta, beta ? 4 * tokens * d->H : 0),
+                       range("v", v, v ? nv * eb : 0), range("alpha", alpha, alpha ? gb * na : 0),
+                       range("beta", beta, beta ? gb * tokens * d->H : 0),
                        range("h0", h0, h0 ? state_bytes : 0), range("dout", dout, dout ? nv * eb : 0),
                        range("dht", dht, dht ? state_bytes : 0),
                        range("cu_seqlens", cu_seqlens,
@@ -325,7 +327,7 @@ ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
   }
   if (d->num_seqs == 0) return ok();
   ckda::BwdArgs b{};
-  b.f = ckda::FwdArgs{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size, d->H,
+  b.f = ckda::FwdArgs{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size, Hk,
                       d->use_qk_l2norm, d->gate_range, d->gate_input, 0, d->scale, q, k, v,
                       alpha, beta, cu_seqlens, h0, nullptr, nullptr};
   b.dout = dout;
@@ -336,7 +338,10 @@ ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
   b.dalpha = dalpha;
   b.dbeta = dbeta;
   b.dh0 = dh0;
-  return from_hip(ckda::launch_bwd(b, d->io_dtype, workspace, static_cast<hipStream_t>(stream)));
+  const size_t core = ckda::bwd_workspace_bytes(d->B, d->T, d->H, d->dk, d->dv, d->num_seqs,
+                                                d->chunk_size, d->io_dtype, cu_seqlens != nullptr);
+  return from_hip(ckda::launch_bwd_full(b, d->io_dtype, workspace, core,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace

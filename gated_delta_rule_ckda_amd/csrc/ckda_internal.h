@@ -158,6 +158,14 @@ launch_result launch_bwd_passes(const BwdArgs& b, int32_t io_dtype, hipStream_t 
 size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                            int32_t num_seqs, int32_t chunk, int32_t io_dtype, bool packed);
 launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stream);
+// The backward for gate logits and grouped value heads (bwd_gates.hip): the
+// workspace beyond the backward's own `core_bytes`, and the passes around
+// launch_bwd that prepare float32 gates and one q/k head per value head and
+// finish the gradients of the logits and of the shared q/k heads.
+size_t bwd_gates_extra_bytes(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t dk,
+                             int32_t io_dtype, bool logits);
+launch_result launch_bwd_full(BwdArgs b, int32_t io_dtype, void* ws, size_t core_bytes,
+                              hipStream_t stream);
 
 // ---- small device helpers shared by the kernels --------------------------
 

@@ -249,25 +249,33 @@ int32_t ckda_fwd_supported(const ckda_fwd_desc_t* desc);
  * descriptor and inputs as the forward, dout = dL/do (io dtype, shaped like o)
  * and dht = dL/dht ([N][H][dk][dv] float32, NULL for zero), writes float32
  * gradients:
- *   dq, dk, dalpha : [B*T][H][dk]    dv : [B*T][H][dv]    dbeta : [B*T][H]
- *   dh0            : [N][H][dk][dv]  (NULL: not written)
+ *   dq, dk : [B*T][Hk][dk]   dalpha : [B*T][H][dk]   dv : [B*T][H][dv]
+ *   dbeta  : [B*T][H]        dh0 : [N][H][dk][dv]  (NULL: not written)
  * in the forward's token layout (dense or packed).  h0 is the forward's
- * initial state (NULL for zero).
+ * initial state (NULL for zero).  With gate logits (gate_input 1 or 2) dalpha
+ * and dbeta are the gradients of the logits a and b, through the activation
+ * of "CKDA Definition" (the sigmoid itself in the KDA range).  With grouped
+ * value heads (Hk < H) dq and dk of a q/k head sum the gradients of the value
+ * heads that read it (dormouse review, section 7).
  *
  * It recomputes the forward (keeping each chunk's X = (I + A)^{-1} and entry
  * state in the workspace), runs the state adjoint backwards over each
  * sequence's chunks, then the chunk-local gradients in parallel over chunks:
- * in the ratio form of the forward where the chunk's running gate products
- * lie in [2^-100, 2^10], token by token (no division) elsewhere.  dalpha in
- * the ratio form is (sum of later log-derivative terms) / alpha, so its
- * float32 error grows like 1/|alpha| for small gates; alpha * dalpha is as
- * accurate as the other gradients.
+ * from the forward's running gate products where they lie in [2^-100, 2^10],
+ * token by token elsewhere.  dalpha is formed with no division by a gate:
+ * it sums the pairs of positions that straddle the gate, each times the
+ * partial gate products on either side of it, so gates near zero are as
+ * accurate as the others.  Every reduction runs in a fixed order: two calls
+ * on the same inputs give the same bits.  With logits or grouped heads, extra
+ * passes before and after prepare float32 gates and one q/k head per value
+ * head in the workspace and finish the gradients.
  *
- * Requirements beyond the forward's: gate_input = CKDA_GATES_F32 (gate values),
- * qk_heads = 0 or H, sign_absorb = 0 (else CKDA_ERR_UNSUPPORTED).  Outputs
- * must be 16-byte aligned and overlap no input, each other or the workspace.
- * `workspace`: at least ckda_chunk_bwd_workspace_size(desc, cu_seqlens !=
- * NULL) bytes, 256-byte aligned, scratch.  Asynchronous on `stream`.
+ * Requirements beyond the forward's: sign_absorb = 0 (else
+ * CKDA_ERR_UNSUPPORTED).  Outputs must be 16-byte aligned and overlap no
+ * input, each other or the workspace.  `workspace`: at least
+ * ckda_chunk_bwd_workspace_size(desc, cu_seqlens != NULL) bytes, 256-byte
+ * aligned, scratch (CKDA_ERR_WORKSPACE_TOO_SMALL below that size).
+ * Asynchronous on `stream`.
  */
 size_t ckda_chunk_bwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed);
 ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* desc, const void* q, const void* k,

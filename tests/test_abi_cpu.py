@@ -249,9 +249,9 @@ def _bwd(desc, **over):
 
 
 @pytest.mark.parametrize("over,status,needle", [
-    (dict(gate_input=ck.GATES_LOGITS_F32), 2, "gate values"),
-    (dict(qk_heads=1), 2, "qk_heads == H"),
     (dict(sign_absorb=1), 2, "sign-absorption"),
+    (dict(qk_heads=3), 1, "qk_heads"),
+    (dict(gate_input=7), 1, "gate_input"),
     (dict(chunk_size=48), 1, "chunk_size"),
     (dict(B=0), 1, "non-positive"),
 ])
@@ -318,3 +318,25 @@ def test_noalloc_scratch_limit_is_checked_on_the_host():
     st = lib.ckda_chunk_fwd_noalloc(ctypes.byref(small), P["q"], None, P["v"], P["alpha"],
                                     P["beta"], None, P["h0"], P["o"], P["ht"], None)
     assert st == 1 and "must not be NULL" in lib.ckda_last_error().decode()
+
+
+def test_bwd_workspace_for_logits_and_grouped_heads():
+    """Logit gates add float32 alpha and beta; grouped value heads add q and k
+    on every value head (io type) and their float32 gradients; each part
+    256-byte aligned after the plain backward's workspace."""
+    lib = ck._load()
+    up = lambda x: (x + 255) // 256 * 256
+    B, T, H, d = 2, 130, 4, 64
+    tok = B * T
+    base = _desc(B=B, T=T, H=H, dk=d, dv=d, chunk_size=32, io_dtype=ck.BF16)
+    core = lib.ckda_chunk_bwd_workspace_size(ctypes.byref(base), 0)
+    lg = _desc(B=B, T=T, H=H, dk=d, dv=d, chunk_size=32, io_dtype=ck.BF16,
+               gate_input=ck.GATES_LOGITS_BF16)
+    assert lib.ckda_chunk_bwd_workspace_size(ctypes.byref(lg), 0) == \
+        up(core) + up(4 * tok * H * d) + up(4 * tok * H)
+    gv = _desc(B=B, T=T, H=H, dk=d, dv=d, chunk_size=32, io_dtype=ck.BF16, qk_heads=2)
+    assert lib.ckda_chunk_bwd_workspace_size(ctypes.byref(gv), 0) == \
+        up(core) + 2 * up(2 * tok * H * d) + 2 * up(4 * tok * H * d)
+    # a workspace for the plain call is too small for the logits call
+    st, msg = _bwd(lg, ws_bytes=core)
+    assert st == 3 and "needed" in msg

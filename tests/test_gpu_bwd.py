@@ -207,3 +207,84 @@ def test_bwd_is_deterministic(dtype, chunk, d):
     torch.cuda.synchronize()
     for n, x, y in zip(NAMES, g1, g2):
         assert np.array_equal(x, y), n
+
+
+def _check_general(c, dtype, chunk, gates="values", arm="ckda", gate_dtype="f32", Hk=None):
+    """ckda_chunk_bwd with gate logits and/or grouped q/k heads against the
+    oracle: logits through oracle.gates and oracle.gates_bwd, grouped heads
+    as q, k repeated over the value heads (each q/k head serving H / Hk
+    consecutive value heads) with their gradients summed back."""
+    H = c["v"].shape[2]
+    Hk = Hk or H
+    G = H // Hk
+    q, k = c["q"][:, :, ::G].copy(), c["k"][:, :, ::G].copy()  # the q/k heads
+    a, b = c["alpha"], c["beta"]
+    if gates == "logits" and gate_dtype == "bf16":
+        a, b = inputs.round_bf16(a), inputs.round_bf16(b)
+    cu = None if c["cu"] is None else torch.from_numpy(np.asarray(c["cu"], np.int32)).to(DEV)
+    g = ck.chunk_bwd(dev(q, dtype), dev(k, dtype), dev(c["v"], dtype), dev(a, gate_dtype),
+                     dev(b, gate_dtype), dev(c["dO"], dtype),
+                     h0=None if c["h0"] is None else dev(c["h0"]),
+                     dht=None if c["dht"] is None else dev(c["dht"]), cu_seqlens=cu,
+                     chunk_size=chunk, gate=arm, gates=gates)
+    torch.cuda.synchronize()
+    g = [host(x) for x in g]
+    qr, kr = np.repeat(q, G, axis=2), np.repeat(k, G, axis=2)
+    if gates == "logits":
+        al, be = oracle.gates(a, b, ckda_range=(arm == "ckda"))
+    else:
+        al, be = a, b
+    r = list(oracle.bwd(qr, kr, c["v"], al, be, c["dO"], h0=c["h0"], dht=c["dht"],
+                        seq_start=c["cu"]))
+    if gates == "logits":
+        r[3], r[4] = oracle.gates_bwd(a, b, r[3], r[4], ckda_range=(arm == "ckda"))
+    if G > 1:
+        sh = r[0].shape
+        r[0] = r[0].reshape(sh[:2] + (Hk, G, sh[3])).sum(3)
+        r[1] = r[1].reshape(sh[:2] + (Hk, G, sh[3])).sum(3)
+    errs = _grad_errs(g, r)
+    print("  " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    for n, e in errs.items():
+        assert e < TOL[dtype], (n, e)
+
+
+@pytest.mark.parametrize("dtype,chunk,d,gate_dtype,arm", [
+    ("f32", 32, 32, "f32", "ckda"), ("f32", 16, 16, "f32", "kda"),
+    ("bf16", 64, 128, "bf16", "ckda"), ("bf16", 64, 128, "f32", "kda"),
+    ("bf16", 32, 64, "bf16", "kda")])
+def test_bwd_gate_logits(dtype, chunk, d, gate_dtype, arm):
+    """Gates given as logits: the gradients of the logits a, b (and of q, k,
+    v, h0) against the oracle's gradients taken through its activation."""
+    announce("bwd logits %s C=%d d=%d %s logits, %s range" % (dtype, chunk, d, gate_dtype, arm))
+    rng = np.random.default_rng(1500 + d + chunk)
+    c = _grad_case(1500 + d, 2, 2 * chunk + 11, 2, d, dtype)
+    if arm == "ckda":
+        c["alpha"] = rng.normal(2, 2, c["alpha"].shape).astype(np.float32)
+        c["alpha"][rng.random(c["alpha"].shape) < 0.02] = 0.0  # exact zero gates
+    else:
+        c["alpha"] = rng.normal(2, 1, c["alpha"].shape).astype(np.float32)
+    c["beta"] = rng.normal(0, 1, c["beta"].shape).astype(np.float32)
+    _check_general(c, dtype, chunk, gates="logits", arm=arm, gate_dtype=gate_dtype)
+
+
+@pytest.mark.parametrize("dtype,chunk,d,Hk", [("f32", 32, 32, 2), ("f32", 16, 16, 1),
+                                              ("bf16", 64, 128, 2), ("bf16", 32, 64, 1)])
+def test_bwd_grouped_value_heads(dtype, chunk, d, Hk):
+    """q, k on Hk heads serving H = 4 value heads: dq, dk of a q/k head are
+    the sums over its value heads."""
+    announce("bwd grouped heads %s C=%d d=%d Hk=%d" % (dtype, chunk, d, Hk))
+    c = _grad_case(1600 + d + Hk, 2, 2 * chunk + 3, 4, d, dtype)
+    _check_general(c, dtype, chunk, Hk=Hk)
+
+
+def test_bwd_logits_grouped_packed():
+    """bf16 logits, two q/k heads for four value heads, a packed batch with
+    an empty sequence, chunk 64 at d = 128."""
+    announce("bwd logits + grouped heads + packed")
+    lens = [150, 0, 64, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    c = _grad_case(1700, 1, cu[-1], 4, 128, "bf16", cu=cu)
+    rng = np.random.default_rng(1701)
+    c["alpha"] = rng.normal(2, 2, c["alpha"].shape).astype(np.float32)
+    c["beta"] = rng.normal(0, 1, c["beta"].shape).astype(np.float32)
+    _check_general(c, "bf16", 64, gates="logits", gate_dtype="bf16", Hk=2)
