@@ -489,6 +489,19 @@ def main():
             "prep_ms": round(per_fd["prep"], 4), "state_ms": round(per_fd["state"], 4),
             "over_headline": round(ms_fd / ms, 4)}
         del fd
+        zg = inputs.zero_gates(case)
+        ms_zg, _, per_zg = bench_fwd(zg, args.steps, args.warmup, "ckda", passes=True)
+        del zg
+        zl = inputs.zero_gates(inputs.lm_layer_logits(arm="ckda", gate_dtype="bf16"))
+        ms_zl, _, per_zl = bench_fwd(zl, args.steps, args.warmup, "ckda", passes=True)
+        del zl
+        out["zero_gates"] = {
+            "workload": "LM layer as the headline with 648 gates exactly 0 (token, head, channel "
+                        "drawn uniformly); and the bf16-logit arm with 648 logits exactly 0",
+            "ms_per_step": round(ms_zg, 4), "prep_ms": round(per_zg["prep"], 4),
+            "over_headline": round(ms_zg / ms, 4),
+            "logits_ms_per_step": round(ms_zl, 4), "logits_prep_ms": round(per_zl["prep"], 4),
+            "logits_over_headline": round(ms_zl / ms, 4)}
         ms_sa, _, _ = bench_fwd(case, args.steps, args.warmup, "ckda", sign_absorb=True)
         out["sign_absorbed"] = {
             "workload": "LM layer as the headline, CKDA range run as a KDA forward on |alpha| "

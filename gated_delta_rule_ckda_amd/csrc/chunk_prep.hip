@@ -65,7 +65,7 @@ namespace ckda {
 namespace {
 
 constexpr float kRegularMin = 0x1p-100f;
-constexpr int64_t kDirectGrid = 256;  // workgroups of the direct kernel (one per CU)
+constexpr int64_t kRedoGrid = 256;  // workgroups of the second transform launch (one per CU)
 constexpr float kRegularMax = 0x1p+10f;
 
 // N consecutive logical entries start .. start+N-1 of a row of length K in
@@ -122,8 +122,14 @@ struct PrepCfg {
   static constexpr int O_RQ = O_G + NW * DK * 4;                        // rq [C]
   static constexpr int O_RK2 = O_RQ + C * 4;                            // rk [C]
   static constexpr int O_BETA = O_RK2 + C * 4;                          // beta [C]
-  static constexpr int O_FLAG = O_BETA + C * 4;                         // regularity votes [2][NW]
-  static constexpr int LDS_BYTES = align16(O_FLAG + 2 * NW * 4);
+  static constexpr int O_FLAG = O_BETA + C * 4;                         // votes [3][NW]
+  // rows whose gate is exactly zero: one byte per (wave, channel), bit i for
+  // the wave's row i, laid out [block][channel][wave in block] so that a
+  // channel's 16-row mask is WPB adjacent bytes
+  static constexpr int WPB = 16 / RPW;                                  // waves per 16-row block
+  static constexpr int O_ZB = O_FLAG + 3 * NW * 4;
+  static constexpr int O_BC = O_ZB + NW * DK;                           // second launch: the next slot
+  static constexpr int LDS_BYTES = align16(O_BC + 4);
   // direct path staging, inside the operand region it leaves unused
   static constexpr int O_DGATE = 0;                                     // gates [C][DK] fp32
   static constexpr int O_DROW = C * DK * 4;                             // q or k rows [C][DK]
@@ -205,6 +211,81 @@ __device__ __forceinline__ void tile_ap(f32x4& acc_a, f32x4& acc_p, const typena
     for (int s = 0; s < NS; ++s) {
       acc_a = mfma_f32(fa[s], fb[s], acc_a);
       acc_p = mfma_f32(fb[s], fq[s], acc_p);
+    }
+  }
+}
+
+// The zero rows of a 16-row block for one channel as a 16-bit mask (bit r for
+// the block's row r), from the block's bytes of the zero map.
+template <class Cfg>
+__device__ __forceinline__ uint32_t zmask16(const uint8_t* zb, int ch) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int w = 0; w < Cfg::WPB; ++w) m |= static_cast<uint32_t>(zb[ch * Cfg::WPB + w]) << (w * Cfg::RPW);
+  return m;
+}
+
+// tile_ap for a chunk with exact zero gates (block anchors; the operands
+// Lk, Lq, Rk use the products restarted after a zero: D(r<-j) is their ratio
+// for r, j on the same side of every zero, and 0 across one).  zi, zj: the
+// zero map of the row block I and of the column block J.
+//   mode 0, off-diagonal tile: row r of I keeps channel c while no zero of
+//     c lies at or before r in I (the prefix D(r<-a_I)); row j of J keeps it
+//     while no zero lies after j in J (the suffix D(e_J<-j)); e scales the
+//     right operand by the products between the blocks;
+//   mode 1, diagonal tile: the pairs before the block's zero of c;
+//   mode 2, diagonal tile: the pairs at or after it (one zero per block and
+//     channel; more take the direct path).
+template <class Cfg>
+__device__ __forceinline__ void tile_ap_z(f32x4& acc_a, f32x4& acc_p,
+                                                    const typename Cfg::T* lk,
+                                                    const typename Cfg::T* lq,
+                                                    const typename Cfg::T* rk, const float* e,
+                                                    const uint8_t* zi, const uint8_t* zj,
+                                                    int mode, int lane) {
+  using Op = typename Cfg::Op;
+  constexpr int DK = Cfg::DK, LDK = Cfg::LDK;
+  const int r = lane & 15, kq = lane >> 4;
+  const uint32_t upto = (2u << r) - 1u;  // rows 0..r
+  // left: mode 2 keeps rows with a zero at or before them, modes 0 and 1
+  // those without; right: mode 0 keeps rows with no zero after them, mode 1
+  // rows with no zero at or before them, mode 2 rows with one
+  const uint32_t lsel = mode == 2 ? 1u : 0u;
+  auto keep_left = [&](uint32_t m) { return ((m & upto) != 0u ? 1u : 0u) == lsel; };
+  auto keep_right = [&](uint32_t m) {
+    return mode == 0 ? (m >> (r + 1)) == 0u : (((m & upto) != 0u ? 1u : 0u) == lsel);
+  };
+  if constexpr (sizeof(typename Op::T) == 2) {
+    static_assert(DK % 32 == 0, "bf16 operand rows");
+    constexpr int NS = DK / 32;
+#pragma unroll 1
+    for (int s = 0; s < NS; ++s) {
+      const int c0 = 32 * s + 8 * kq;
+      bf16x8 fa = *reinterpret_cast<const bf16x8*>(lk + r * LDK + c0);
+      bf16x8 fq = *reinterpret_cast<const bf16x8*>(lq + r * LDK + c0);
+      bf16x8 fb = *reinterpret_cast<const bf16x8*>(rk + r * LDK + c0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool kl = keep_left(zmask16<Cfg>(zi, c0 + i)), kr = keep_right(zmask16<Cfg>(zj, c0 + i));
+        const float ev = e ? e[c0 + i] : 1.f;
+        fa[i] = kl ? fa[i] : Op::cvt(0.f);
+        fq[i] = kl ? fq[i] : Op::cvt(0.f);
+        fb[i] = kr ? Op::cvt(static_cast<float>(fb[i]) * ev) : Op::cvt(0.f);
+      }
+      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc_a, 0, 0, 0);
+      acc_p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fq, acc_p, 0, 0, 0);
+    }
+  } else {
+    constexpr int NS = DK / 4;
+#pragma unroll 1
+    for (int s = 0; s < NS; ++s) {
+      const int ch = kq + 4 * s;
+      const bool kl = keep_left(zmask16<Cfg>(zi, ch)), kr = keep_right(zmask16<Cfg>(zj, ch));
+      const float fa = kl ? lk[r * LDK + ch] : 0.f;
+      const float fq = kl ? lq[r * LDK + ch] : 0.f;
+      const float fb = kr ? rk[r * LDK + ch] * (e ? e[ch] : 1.f) : 0.f;
+      acc_a = mfma_f32(fa, fb, acc_a);
+      acc_p = mfma_f32(fb, fq, acc_p);
     }
   }
 }
@@ -370,10 +451,18 @@ __device__ __forceinline__ void direct_ap(const void* gq, const void* gk, const 
   });
 }
 
-// One (chunk, head) of the transform pass.  DIRECT = false: the MFMA path;
-// a chunk that is not regular gets its flag set and is left to the direct
-// kernel.  DIRECT = true: the same chunk with A and P from direct products.
-template <class Cfg, class G, bool DIRECT>
+// Flags of the transform pass's first launch, per (head, chunk slot)
+constexpr int kFlagRegular = 0;  // done by the first launch
+constexpr int kFlagRedo = 1;     // left to the second launch
+
+// One (chunk, head) of the transform pass.  MODE = kFlagRegular (the first
+// launch): the MFMA form for chunks whose plain running products are in
+// range (so none with a zero gate); any other chunk gets its flag set and is
+// left to the second launch.  MODE = kFlagRedo (the second launch): products
+// restarted after zero gates; in range with one zero per (block, channel) at
+// most, the masked MFMA form (tile_ap_z); anything else, A and P from direct
+// products.
+template <class Cfg, class G, int MODE>
 __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsigned char* smem,
                                            int tid = static_cast<int>(threadIdx.x)) {
   using Op = typename Cfg::Op;
@@ -406,7 +495,7 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   if (a.cu_seqlens) {
     const int n = uniform32(a.chunk_seq[c]);
     if (n < 0) {  // unused chunk slot
-      if (!DIRECT && tid == 0) a.irregular[h * a.maxc + c] = 0;
+      if (MODE == kFlagRegular && tid == 0) a.irregular[h * a.maxc + c] = kFlagRegular;
       return;
     }
     const int i = c - uniform32(a.first[n]);
@@ -467,16 +556,46 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
       }
     }
   }
-  // running products over this wave's rows; their totals go to sG
+  // running products over this wave's rows, restarted after a gate that is
+  // exactly zero (the zero's row takes 1, the empty product of the gates
+  // after it); their totals go to sG and the zero rows to the zero map
+  // (the first launch keeps plain products: a zero gate makes its chunk
+  // irregular there, and the later launches take it)
+  constexpr bool ZL = MODE != kFlagRegular;
+  uint32_t zbits[CPT];
+  if constexpr (!ZL) {
 #pragma unroll
-  for (int cc = 0; cc < CPT; ++cc) {
-    float f = 1.f;
+    for (int cc = 0; cc < CPT; ++cc) {
+      float f = 1.f;
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      f *= F[i][cc];
-      F[i][cc] = f;
+      for (int i = 0; i < RPW; ++i) {
+        f *= F[i][cc];
+        F[i][cc] = f;
+      }
+      zbits[cc] = 0u;
+      if (scan_on) sG[wave * DK + c0ch + cc] = f;
     }
-    if (scan_on) sG[wave * DK + c0ch + cc] = f;
+  } else {
+    uint8_t* zmap = reinterpret_cast<uint8_t*>(smem + Cfg::O_ZB);
+    constexpr int WPB = Cfg::WPB;
+    const int blk = wave / WPB, wib = wave % WPB;
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      float f = 1.f;
+      uint32_t zb = 0;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const bool z = F[i][cc] == 0.f;
+        zb |= z ? (1u << i) : 0u;
+        f = z ? 1.f : f * F[i][cc];
+        F[i][cc] = f;
+      }
+      zbits[cc] = zb;
+      if (scan_on) {
+        sG[wave * DK + c0ch + cc] = f;
+        zmap[(blk * DK + c0ch + cc) * WPB + wib] = static_cast<uint8_t>(zb);
+      }
+    }
   }
   {
     float pq[RPW], pk[RPW];
@@ -504,31 +623,41 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   // ================= 2: chunk products, regularity, operands =================
   float kt[RPW][CPT], kh[RPW][CPT], gch[CPT], gsuf[CPT];
   bool canchor = false;  // operands anchored at the chunk start (no E_IJ)
+  const uint8_t* zmap = reinterpret_cast<const uint8_t*>(smem + Cfg::O_ZB);
   {
-    constexpr int WPB = 16 / RPW;       // waves per 16-row block
+    constexpr int WPB = Cfg::WPB;       // waves per 16-row block
     const int wb0 = wave - wave % WPB;  // first wave of this wave's block
     bool ok = true;
-    // products of the wave totals: before this wave from the chunk start
-    // (gpre) and from the block start (bpre), from the block start to the
-    // chunk end (gbs), after this wave (gsuf), all (gch)
+    // products of the wave totals.  Plain products (exactly zero across a
+    // zero gate): before this wave from the chunk start (gpre), after this
+    // wave (gsuf), all (gch).  Restarted after the block's zeros: from the
+    // block start before this wave (bpre, the block anchor); the block's
+    // total after its last zero times the plain totals of the later blocks
+    // (gbs, for Kh).  Every (block, channel) may hold one zero gate at most.
     float gpre[CPT], bpre[CPT], gbs[CPT];
+    uint32_t bz[CPT];  // this wave's block: the channel's zero rows
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
-      float gp = 1.f, bp = 1.f, g = 1.f, gs = 1.f, bs = 1.f;
+      float gp = 1.f, bp = 1.f, g = 1.f, gs = 1.f, bt = 1.f, later = 1.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float gw = scan_on ? sG[w * DK + c0ch + cc] : 1.f;
-        if (w < wave) gp *= gw;
-        if (w < wave && w >= wb0) bp *= gw;
-        if (w > wave) gs *= gw;
-        if (w >= wb0) bs *= gw;
-        g *= gw;
+        const float tw = scan_on ? sG[w * DK + c0ch + cc] : 1.f;
+        const bool zw = ZL && scan_on && zmap[((w / WPB) * DK + c0ch + cc) * WPB + w % WPB] != 0;
+        const float pw = zw ? 0.f : tw;  // the plain total
+        if (w < wave) gp *= pw;
+        if (w > wave) gs *= pw;
+        g *= pw;
+        if (w >= wb0 && w < wave) bp = zw ? tw : bp * tw;
+        if (w >= wb0 && w < wb0 + WPB) bt = zw ? tw : bt * tw;
+        if (w >= wb0 + WPB) later *= pw;
       }
       gpre[cc] = gp;
       bpre[cc] = bp;
-      gbs[cc] = bs;
+      gbs[cc] = bt * later;
       gch[cc] = g;
       gsuf[cc] = gs;
+      bz[cc] = (ZL && scan_on) ? zmask16<Cfg>(zmap + (wave / WPB) * DK * WPB, c0ch + cc) : 0u;
+      ok = ok && (bz[cc] & (bz[cc] - 1u)) == 0;  // one zero per block and channel at most
     }
     if (scan_on && wave == 0) {
 #pragma unroll
@@ -536,14 +665,15 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
     }
     // chunk anchors when every |Ft| of the chunk is in range (then E_IJ = 1
     // factors out of every tile), else block anchors
-    if constexpr (!DIRECT) {
+    if constexpr (MODE == kFlagRegular) {
+      // (a zero gate anywhere rules them out: F restarts after it)
       bool okc = true;
 #pragma unroll
       for (int i = 0; i < RPW; ++i)
 #pragma unroll
         for (int cc = 0; cc < CPT; ++cc) {
           const float mag = fabsf(gpre[cc] * F[i][cc]);
-          okc = okc && (!scan_on || ((mag >= kRegularMin) && (mag <= kRegularMax)));
+          okc = okc && (!scan_on || ((mag >= kRegularMin) && (mag <= kRegularMax) && zbits[cc] == 0u));
         }
       const bool wave_okc = __all(okc);
       if (lane == 0) sFlag[NW + wave] = wave_okc ? 1 : 0;
@@ -560,6 +690,7 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
         gbs[cc] = gch[cc];
       }
     }
+    const int rb0 = r0 % 16;  // this wave's first row inside its block
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int r = r0 + i;
@@ -567,8 +698,10 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
       float qv[CPT], lq[CPT], lk[CPT];
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
-        const float ft = gpre[cc] * F[i][cc];  // D(r <- chunk start)
-        const float fb = bpre[cc] * F[i][cc];  // D(r <- anchor)
+        // a zero at or before row i among this wave's rows
+        const bool zb = (zbits[cc] & ((2u << i) - 1u)) != 0;
+        const float ft = gpre[cc] * (zb ? 0.f : F[i][cc]);  // D(r <- chunk start)
+        const float fb = zb ? F[i][cc] : bpre[cc] * F[i][cc];  // restarted, from the anchor
         const float mag = fabsf(fb);
         ok = ok && (!scan_on || ((mag >= kRegularMin) && (mag <= kRegularMax)));
         const float rinv = __builtin_amdgcn_rcpf(fb);
@@ -577,7 +710,8 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
         lk[cc] = xk[i][cc] * fb;          // Lk
         kt[i][cc] = xk[i][cc] * ft;       // Kt / rk
         xk[i][cc] = xk[i][cc] * rinv;     // Rk
-        kh[i][cc] = xk[i][cc] * gbs[cc];  // Kh / rk (regular chunks)
+        // Kh / rk (regular chunks): zero while a zero of the block follows
+        kh[i][cc] = (bz[cc] >> (rb0 + i + 1)) != 0 ? 0.f : xk[i][cc] * gbs[cc];
       }
       if (scan_on) {
         store_run<Op, CPT>(gQ + r * DK + Op::template pos<DK>(c0ch), qv);
@@ -586,10 +720,13 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
         store_run<Op, CPT>(sRk + r * LDK + c0ch, xk[i]);
       }
     }
-    // E_IJ = prod_{J <= b < I} T_b (the product of the wave totals of waves
-    // WPB*J .. WPB*I-1) for every off-diagonal tile, into the X block (I, J),
-    // which holds nothing until the off-diagonal levels of X are formed
-    if (!DIRECT && NB > 1 && !canchor) {
+    // E_IJ = T'_J prod_{J < b < I} T_b for every off-diagonal tile: block
+    // J's total after its last zero (the suffix products of its rows are
+    // taken relative to that) times the plain totals of the blocks between
+    // (zero if one holds a zero gate); from the wave totals of waves
+    // WPB*J .. WPB*I-1.  Into the X block (I, J), which holds nothing until
+    // the off-diagonal levels of X are formed.
+    if (NB > 1 && !canchor) {
       constexpr int NPR = NB * (NB - 1) / 2;
       for (int e = tid; e < NPR * DK; e += NT) {
         const int pr = e / DK, ch = e % DK;
@@ -597,25 +734,44 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
         while (I * (I + 1) / 2 <= pr) ++I;
         const int J = pr - I * (I - 1) / 2;
         float v = 1.f;
-        for (int w = WPB * J; w < WPB * I; ++w) v *= sG[w * DK + ch];
+        for (int w = WPB * J; w < WPB * I; ++w) {
+          const float tw = sG[w * DK + ch];
+          const bool zw = ZL && zmap[((w / WPB) * DK + ch) * WPB + w % WPB] != 0;
+          v = (w < WPB * (J + 1)) ? (zw ? tw : v * tw) : (zw ? 0.f : v * tw);
+        }
         x_blk<Cfg>(smem, I, J)[ch] = v;
       }
     }
     const bool wave_ok = __all(ok);
-    if (lane == 0) sFlag[wave] = wave_ok ? 1 : 0;
+    bool anyz = false;
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) anyz = anyz || (ZL && scan_on && zbits[cc] != 0u);
+    const bool wave_z = ZL && __any(anyz);
+    if (lane == 0) {
+      sFlag[wave] = wave_ok ? 1 : 0;
+      sFlag[2 * NW + wave] = wave_z ? 1 : 0;
+    }
   }
   __syncthreads();  // B2
-  int votes = 1;
+  int votes = 1, zvotes = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) votes &= sFlag[w];
-  if constexpr (!DIRECT) {
-    const bool regular = uniform32(votes) != 0;
-    if (tid == 0) a.irregular[h * a.maxc + c] = regular ? 0 : 1;
-    if (!regular) return;
+  for (int w = 0; w < NW; ++w) {
+    votes &= sFlag[w];
+    zvotes |= sFlag[2 * NW + w];
   }
+  const bool haszero = uniform32(zvotes) != 0;  // some gate of the chunk is exactly zero
+  // in range with at most one zero per (block, channel): the MFMA form
+  // applies (with the zero masks of tile_ap_z when a gate is exactly zero)
+  const bool in_range = uniform32(votes) != 0;
+  if constexpr (MODE == kFlagRegular) {
+    // plain products: a chunk with a zero gate is out of range here
+    if (tid == 0) a.irregular[h * a.maxc + c] = in_range ? kFlagRegular : kFlagRedo;
+    if (!in_range) return;
+  }
+  (void)haszero;
 
   // ================= 3: A and P ================================================
-  if constexpr (!DIRECT) {
+  if (MODE == kFlagRegular || in_range) {
     // A tile (I, J) from its accumulator: rows r = 16I + 4lq + i, column
     // j = 16J + l16; the diagonal tile goes to the X block it seeds
     auto a_out = [&](const f32x4& acc_a, int I, int J) {
@@ -643,6 +799,20 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
       return out;
     };
     auto tile = [&](f32x4& acc_a, f32x4& acc_p, int I, int J) {
+      if constexpr (MODE == kFlagRedo) {
+        const uint8_t* zi = zmap + I * DK * Cfg::WPB;
+        const uint8_t* zj = zmap + J * DK * Cfg::WPB;
+        if (I > J) {
+          tile_ap_z<Cfg>(acc_a, acc_p, sLk + 16 * I * LDK, sLq + 16 * I * LDK, sRk + 16 * J * LDK,
+                         x_blk<Cfg>(smem, I, J), zi, zj, 0, lane);
+        } else {
+          tile_ap_z<Cfg>(acc_a, acc_p, sLk + 16 * I * LDK, sLq + 16 * I * LDK, sRk + 16 * J * LDK,
+                         nullptr, zi, zj, 1, lane);
+          tile_ap_z<Cfg>(acc_a, acc_p, sLk + 16 * I * LDK, sLq + 16 * I * LDK, sRk + 16 * J * LDK,
+                         nullptr, zi, zj, 2, lane);
+        }
+        return;
+      }
       tile_ap<Cfg>(acc_a, acc_p, sLk + 16 * I * LDK, sLq + 16 * I * LDK, sRk + 16 * J * LDK,
                    (I > J && !canchor) ? x_blk<Cfg>(smem, I, J) : nullptr, lane);
     };
@@ -894,55 +1064,93 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(4))) vo
   const int H = a.H;
   const int b = static_cast<int>(blockIdx.x);
   if (a.cu_seqlens) {
-    prep_chunk<Cfg, G, false>(a, b / H, b % H, smem);
+    prep_chunk<Cfg, G, kFlagRegular>(a, b / H, b % H, smem);
   } else {
     const int per = a.B * H;  // workgroups per chunk position
     const int i = a.nc - 1 - b / per, n = (b % per) / H;
-    prep_chunk<Cfg, G, false>(a, n * a.nc + i, b % H, smem);
+    prep_chunk<Cfg, G, kFlagRegular>(a, n * a.nc + i, b % H, smem);
   }
 }
 
-// The chunks the transform pass flagged as not regular (exact zero gates, or
-// running gate products outside [2^-100, 2^10]), redone with direct products.
-// Workgroup b reads the flags of (chunk, head) slots b, b + G, b + 2G, ...
-// (G workgroups; at most NT slots each, sized by the launcher) with one load
-// per thread, and redoes the flagged ones in turn; with no flag set it ends
-// after that load.  The stride spreads flagged chunks that sit next to each
-// other (one head's run of zero gates) over different workgroups.
+// The chunks the first launch flagged (exact zero gates, running products
+// outside [2^-100, 2^10]), redone in the masked MFMA form or by direct
+// products.  The flagged slots are dealt out evenly: each workgroup scans
+// every flag (16 per thread and step; prefix sums over the lanes and the
+// waves give each flagged slot its rank among them) and takes the slots of
+// rank b, b + G, b + 2G, ... (G workgroups), which it then redoes in turn;
+// with no flag set it ends after the scan.  The launcher sizes G so that no workgroup gets
+// more than NT slots.
 template <class Cfg, class G>
-__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2))) void prep_direct_kernel(
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2))) void prep_redo_kernel(
     FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NW = Cfg::NW;
+  constexpr int NW = Cfg::NW, NT = Cfg::NT;
   const int total = a.maxc * a.H;
   const int grid = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int slot = b + tid * grid;
-  const bool f = tid < Cfg::NT && slot < total && a.irregular[slot] != 0;
-  const uint64_t m = __ballot(f);
-  uint64_t* smask = reinterpret_cast<uint64_t*>(smem);
-  if (lane == 0) smask[wave] = m;
-  __syncthreads();
-  uint64_t masks[NW];
+  int* list = reinterpret_cast<int*>(smem);  // [NT] this workgroup's slots (scan only)
+  int* wcnt = list + NT;                     // [NW] flagged slots per wave, this step
+  constexpr int SPT = 16;                    // flags per thread and step (four 16-byte loads)
+  int seen = 0;                              // flagged slots before this step
+  for (int s0 = 0; s0 < total; s0 += NT * SPT) {
+    const int base = s0 + SPT * tid;
+    int fl[SPT];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) masks[w] = static_cast<uint64_t>(uniform64(static_cast<int64_t>(smask[w])));
-  __syncthreads();
-  // unrolled, so that masks[] stays in registers (a loop over w with a
-  // run-time index would put the array in scratch memory)
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    uint64_t mm = masks[w];
-    while (mm != 0) {
-      const int idx = b + (64 * w + __builtin_ctzll(mm)) * grid;
-      mm &= mm - 1;
-      // threadIdx.x through an opaque move: the chunk's lane-dependent
-      // addresses are then formed here, not hoisted into the kernel's
-      // prologue, where with no chunk flagged they would only cost spills
-      int tid_o;
-      asm volatile("v_mov_b32 %0, %1" : "=v"(tid_o) : "v"(static_cast<int>(threadIdx.x)));
-      prep_chunk<Cfg, G, true>(a, idx % a.maxc, idx / a.maxc, smem, tid_o);
-      __syncthreads();
+    for (int u = 0; u < SPT / 4; ++u) {
+      // the flag array is padded to 256 bytes, so a load that starts below
+      // `total` stays inside it
+      const int4 v = base + 4 * u < total ? *reinterpret_cast<const int4*>(a.irregular + base + 4 * u)
+                                          : make_int4(0, 0, 0, 0);
+      fl[4 * u] = v.x;
+      fl[4 * u + 1] = v.y;
+      fl[4 * u + 2] = v.z;
+      fl[4 * u + 3] = v.w;
     }
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) cnt += (base + u < total && fl[u] != kFlagRegular) ? 1 : 0;
+    // ranks: prefix of the counts over the lanes, then over the waves
+    int x = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wcnt[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int cw = wcnt[w];
+      before += w < wave ? cw : 0;
+      all += cw;
+    }
+    int rank = seen + before + x - cnt;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      if (base + u < total && fl[u] != kFlagRegular) {
+        if (rank % grid == b && rank / grid < NT) list[rank / grid] = base + u;
+        ++rank;
+      }
+    }
+    seen += uniform32(all);
+    __syncthreads();
+  }
+  const int items = seen > b ? (seen - b + grid - 1) / grid : 0;
+  const int mine = tid < items ? list[tid] : 0;
+  __syncthreads();  // the list is read; LDS goes to the chunks
+  int* bcast = reinterpret_cast<int*>(smem + Cfg::O_BC);
+  for (int i = 0; i < items && i < NT; ++i) {
+    if (tid == i) *bcast = mine;
+    __syncthreads();
+    const int idx = uniform32(*bcast);
+    // threadIdx.x through an opaque move: the chunk's lane-dependent
+    // addresses are then formed here, not hoisted into the kernel's
+    // prologue, where with no chunk flagged they would only cost spills
+    int tid_o;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid_o) : "v"(static_cast<int>(threadIdx.x)));
+    prep_chunk<Cfg, G, kFlagRedo>(a, idx % a.maxc, idx / a.maxc, smem, tid_o);
+    __syncthreads();
   }
 }
 
@@ -1021,7 +1229,7 @@ launch_result launch_cfg(const FwdArgs& a, hipStream_t stream) {
       reinterpret_cast<const void*>(&prep_kernel<Cfg, G>),
       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
   static const hipError_t attr_d = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prep_direct_kernel<Cfg, G>),
+      reinterpret_cast<const void*>(&prep_redo_kernel<Cfg, G>),
       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   if (attr_d != hipSuccess) return attr_d;
@@ -1030,10 +1238,10 @@ launch_result launch_cfg(const FwdArgs& a, hipStream_t stream) {
                      Cfg::LDS_BYTES, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one workgroup per CU, each reading at most NT flags
+  // one workgroup per CU, more when that would leave one more than NT slots
   int64_t grid = (blocks + Cfg::NT - 1) / Cfg::NT;
-  if (grid < kDirectGrid) grid = blocks < kDirectGrid ? blocks : kDirectGrid;
-  hipLaunchKernelGGL((prep_direct_kernel<Cfg, G>), dim3(static_cast<unsigned>(grid)), dim3(Cfg::NT),
+  if (grid < kRedoGrid) grid = blocks < kRedoGrid ? blocks : kRedoGrid;
+  hipLaunchKernelGGL((prep_redo_kernel<Cfg, G>), dim3(static_cast<unsigned>(grid)), dim3(Cfg::NT),
                      Cfg::LDS_BYTES, stream, a);
   return hipGetLastError();
 }

@@ -261,6 +261,23 @@ def fast_decay(case: Case, seed=1005, frac=0.25, lo=0.15, hi=0.4) -> Case:
                 arm=case.arm)
 
 
+def zero_gates(case: Case, n=648, seed=1006) -> Case:
+    """The case with `n` gate entries (token, head, channel drawn uniformly)
+    set to exactly zero: a gate value of 0, or a logit of 0 (which the CKDA
+    activation 2 sigmoid(a) - 1 takes to exactly 0).  The other arrays are
+    shared, not copied."""
+    rng = np.random.default_rng(seed)
+    a = case.alpha.copy()
+    flat = a.reshape(-1)
+    idx = rng.choice(flat.size, size=n, replace=False)
+    flat[idx] = 0.0
+    meta = dict(case.meta, zero_gates=n,
+                workload=case.meta.get("workload", "case") + ", %d gates exactly 0" % n)
+    return Case(case.q, case.k, case.v, a, case.beta, case.h0, case.cu_seqlens, case.dtype,
+                case.chunk, case.l2norm, meta, gates=case.gates, gate_dtype=case.gate_dtype,
+                arm=case.arm)
+
+
 def varlen_lengths(seed=1003, n=16, total=65536, lo=1024, hi=8192):
     """n lengths ~ U{lo..hi} rescaled to sum to `total` (rounded; the
     remainder goes to the last length); redrawn with seed+1 while any length

@@ -71,6 +71,80 @@ def _l2scale(x, use, eps=1e-6):
     return 1.0 / np.sqrt((x * x).sum(-1) + eps)
 
 
+def _restarted(ac):
+    """Per 16-row block and channel: the running product from the block start,
+    restarted after a gate that is exactly zero (the zero's row takes 1, the
+    empty product of the gates after it), and the block's zero mask."""
+    C, dk = ac.shape
+    Fr = np.ones((C, dk))
+    Z = np.zeros((C, dk), dtype=bool)
+    for b in range(C // BLOCK):
+        f = np.ones(dk)
+        for r in range(b * BLOCK, (b + 1) * BLOCK):
+            z = ac[r] == 0
+            f = np.where(z, 1.0, f * ac[r])
+            Fr[r] = f
+            Z[r] = z
+    return Fr, Z
+
+
+def _zero_form_ok(ac):
+    """The masked block form applies: some gate is exactly zero, every
+    (block, channel) holds one zero at most, and the restarted products are
+    in range (nonzero gates that do not underflow over a block)."""
+    if not np.any(ac == 0):
+        return False
+    Fr, Z = _restarted(ac)
+    C = ac.shape[0]
+    zc = Z.reshape(C // BLOCK, BLOCK, -1).sum(1)
+    return bool(zc.max() <= 1) and _in_range(Fr)
+
+
+def _zero_form(ac, kc, qc):
+    """G = Kt Rk^T-like pair sums (without beta and the norms), P and Kh of a
+    chunk with exact zero gates, in the masked block form the second
+    transform kernel runs: with Fr the restarted block products, Lk = k Fr,
+    Lq = q Fr, Rk = k / Fr;
+      off-diagonal tile (I > J): rows r of I while no zero lies at or before r
+        in I (the prefix D(r<-a_I)), rows j of J while no zero lies after j in
+        J (the suffix D(e_J<-j)), the right side scaled by E_IJ = T'_J prod_{J<b<I} T_b
+        (T'_J block J's product after its zero, T_b the plain block products);
+      diagonal tile: the pairs before the block's zero plus the pairs at or
+        after it (D across a zero is 0);
+      Kh_j = Rk_j T'_J prod_{b>J} T_b while no zero follows j in its block, else 0."""
+    C, dk = ac.shape
+    nb = C // BLOCK
+    Fr, Z = _restarted(ac)
+    Lk, Lq, Rk = kc * Fr, qc * Fr, kc / Fr
+    T = np.array([np.prod(ac[b * BLOCK:(b + 1) * BLOCK], axis=0) for b in range(nb)])
+    Tr = Fr[BLOCK - 1::BLOCK]                       # T'_b: after the block's zero
+    zb = Z.reshape(nb, BLOCK, dk)
+    # per row: a zero at or before it in its block / after it in its block
+    before = np.cumsum(zb, axis=1).reshape(C, dk) > 0
+    after = (np.cumsum(zb[:, ::-1], axis=1)[:, ::-1] - zb).reshape(C, dk) > 0
+    G = np.zeros((C, C))
+    Pm = np.zeros((C, C))
+    for I in range(nb):
+        ri = slice(I * BLOCK, (I + 1) * BLOCK)
+        for J in range(I + 1):
+            rj = slice(J * BLOCK, (J + 1) * BLOCK)
+            if I > J:
+                E = Tr[J] * np.prod(T[J + 1:I], axis=0)
+                left = ~before[ri]
+                right = ~after[rj]
+                G[ri, rj] = (Lk[ri] * left) @ (Rk[rj] * right * E).T
+                Pm[ri, rj] = (Lq[ri] * left) @ (Rk[rj] * right * E).T
+            else:
+                for side in (False, True):            # before / at-or-after the zero
+                    m_i = before[ri] == side
+                    m_j = before[rj] == side
+                    G[ri, rj] += (Lk[ri] * m_i) @ (Rk[rj] * m_j).T
+                    Pm[ri, rj] += (Lq[ri] * m_i) @ (Rk[rj] * m_j).T
+    later = np.array([np.prod(T[J + 1:], axis=0) for J in range(nb)])
+    Kh = np.where(after, 0.0, Rk * np.repeat(Tr * later, BLOCK, axis=0))  # Kh / rk
+    return G, Pm, Kh
+
+
 def _direct_products(ac):
     """D[r, j] = prod_{j<s<=r} alpha_s (per channel) for j <= r, built one gate
     at a time (no division); zero above the diagonal."""
@@ -120,6 +194,12 @@ def chunk_head(q, k, v, alpha, beta, S, use_l2norm, scale, C, force_irregular=Fa
             A = np.tril((bc * rk)[:, None] * (Kt @ Rk.T) * rk[None, :], -1)
             P = np.tril(Qt @ Rk.T)
             Kh = g * Rk                                   # Kh / rk
+        elif _zero_form_ok(ac) and not force_irregular:
+            if paths is not None:
+                paths.append("zero")
+            G, Pm, Kh = _zero_form(ac, kc, qc)
+            A = np.tril((bc * rk)[:, None] * G * rk[None, :], -1)
+            P = np.tril(Pm)
         elif _in_range(Fb) and not force_irregular:
             if paths is not None:
                 paths.append("block")

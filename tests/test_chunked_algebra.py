@@ -159,3 +159,32 @@ def test_dalpha_of_tiny_gates_holds_in_float32():
                           dalpha_form="ratio")
     assert _err(gr[3], r[3]) > 1e-3
     assert max(_err(x, y) for i, (x, y) in enumerate(zip(gr, r)) if i != 3) < 1e-5
+
+
+@pytest.mark.parametrize("C,T", [(64, 150), (32, 70), (16, 40)])
+def test_single_zero_gates_take_the_masked_block_form(C, T):
+    """Chunks whose exact zero gates are one per (16-row block, channel) run
+    the masked block form (products restarted after the zero, prefix and
+    suffix masks on the off-diagonal tiles, the diagonal tiles split at the
+    zero) and equal the sequential oracle; a block with two zeros of one
+    channel takes the direct form.  Zeros at a block's first and last rows,
+    at the chunk's last row, in adjacent blocks and in a partial last chunk."""
+    rng = np.random.default_rng(60 + C)
+    q, k, v, a, b, h0 = _case(61 + C, 2, T, 2, 8, 8)
+    a = a * rng.choice([-1, 1], a.shape)
+    for (bb, t, h, c) in [(0, 0, 0, 1), (0, 15, 1, 2), (0, C - 1, 0, 3), (1, 15, 0, 4),
+                          (1, 16, 0, 4), (0, T - 1, 1, 5), (1, C + 3, 1, 0), (0, C + 20, 0, 6)]:
+        a[bb, t, h, c] = 0.0
+    paths = []
+    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=C, paths=paths)
+    ro, rh = oracle.fwd(q, k, v, a, b, h0=h0)
+    assert _err(co, ro) < 1e-12 and _err(ch, rh) < 1e-12
+    assert "zero" in paths and "direct" not in paths
+    # two zeros of one channel in one block: the direct form
+    a[0, 2, 0, 7] = 0.0
+    a[0, 9, 0, 7] = 0.0
+    paths = []
+    co, ch = chunked_fp64.fwd(q, k, v, a, b, h0=h0, C=C, paths=paths)
+    ro, rh = oracle.fwd(q, k, v, a, b, h0=h0)
+    assert _err(co, ro) < 1e-12 and _err(ch, rh) < 1e-12
+    assert "direct" in paths

@@ -298,3 +298,50 @@ def test_prepare_finish_equals_single_call(dtype, d, chunk, packed):
     torch.cuda.synchronize()
     assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
     assert np.array_equal(o2, o3) and np.array_equal(h2, h3)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("bf16", 64, 32), ("f32", 32, 32),
+                                           ("f32", 16, 16)])
+def test_single_zero_gates_masked_form(dtype, d, chunk):
+    """Exact zero gates, at most one per (16-row block, channel) (the masked
+    MFMA form of the second transform kernel), at block edges and in
+    adjacent blocks, signed gates, a ragged tail; plus a block with two zeros
+    of one channel (direct products)."""
+    announce("single zero gates %s d=%d C=%d" % (dtype, d, chunk))
+    c = inputs.random_case(311 + d, 2, 3 * chunk + 9, 2, d, d, dtype=dtype, chunk=chunk,
+                           alpha="tanh", beta="2sig", h0_std=0.1)
+    rng = np.random.default_rng(312)
+    c.alpha = c.alpha * rng.choice([-1.0, 1.0], c.alpha.shape).astype(np.float32)
+    T = c.alpha.shape[1]
+    for (b, t, h, ch) in [(0, 0, 0, 1), (0, 15, 1, 2), (0, chunk - 1, 0, 3), (1, 15, 0, 4),
+                          (1, 16, 0, 4), (0, T - 1, 1, 5), (1, chunk + 3, 1, 0),
+                          (0, 2 * chunk + 5, 0, d - 1)]:
+        c.alpha[b, t, h, ch] = 0.0
+    o, ht = run_chunk(c)
+    ro, rh = oracle.fwd(c.q, c.k, c.v, c.alpha, c.beta, h0=c.h0)
+    eo, eh = max_rel_err(o, ro), max_rel_err(ht, rh)
+    print("  err o=%.3e ht=%.3e" % (eo, eh))
+    assert eo < TOL[dtype] and eh < TOL[dtype]
+    c.alpha[0, 2, 1, 6] = 0.0
+    c.alpha[0, 9, 1, 6] = 0.0
+    o, ht = run_chunk(c)
+    ro, rh = oracle.fwd(c.q, c.k, c.v, c.alpha, c.beta, h0=c.h0)
+    assert max_rel_err(o, ro) < TOL[dtype] and max_rel_err(ht, rh) < TOL[dtype]
+
+
+@pytest.mark.parametrize("logits", [False, True])
+def test_lm_layer_zero_gates_full_sampled(logits):
+    """The LM layer at full size with 648 gates exactly zero (gate values, or
+    bf16 logits of 0, which the CKDA activation takes to 0); oracle on 16
+    pairs covering every batch and head."""
+    announce("LM layer full size, 648 zero gates, logits=%s" % logits)
+    base = inputs.lm_layer_logits(arm="ckda", gate_dtype="bf16") if logits else inputs.lm_layer()
+    c = inputs.zero_gates(base)
+    o, ht = run_chunk(c, gate="ckda")
+    o = o.reshape(c.v.shape)
+    pairs = cover_pairs(8, 16)
+    ref = oracle_pairs(c, pairs)
+    worst_o = max(max_rel_err(o[n, :, h], ref[(n, h)][0]) for n, h in pairs)
+    worst_h = max(max_rel_err(ht[n, h], ref[(n, h)][1]) for n, h in pairs)
+    print("  err o=%.3e ht=%.3e" % (worst_o, worst_h))
+    assert worst_o < TOL["bf16"] and worst_h < TOL["bf16"]
