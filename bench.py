@@ -268,6 +268,51 @@ def bench_bwd(case, steps, warmup):
     return ms
 
 
+def bench_train(case, steps, warmup):
+    """A training step's forward and backward on the case, two ways: the
+    forward (ckda_chunk_fwd) then the backward that recomputes it
+    (ckda_chunk_bwd), and the forward that keeps the backward's records
+    (ckda_chunk_fwd_save) then the backward that reads them
+    (ckda_chunk_bwd_saved); plus the saved backward alone.  ms per step."""
+    import torch
+    import gated_delta_rule_ckda_amd as ck
+    dt = case.dtype
+    q, k, v = to_dev(case.q, dt), to_dev(case.k, dt), to_dev(case.v, dt)
+    a, b = to_dev(case.alpha, "f32"), to_dev(case.beta, "f32")
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    dout = torch.randn(v.shape, device="cuda:0", generator=g).to(v.dtype)
+    B, T, H, dk = case.q.shape
+    dv = case.v.shape[-1]
+    dht = torch.randn((B, H, dk, dv), device="cuda:0", generator=g)
+    desc = ck._make_desc(q, v, H, dk, dv, case.chunk, "ckda", case.l2norm, 1.0, None,
+                         ck.GATES_F32, False)
+    bws = torch.empty(ck.chunk_bwd_workspace_size(desc, False), device="cuda:0", dtype=torch.uint8)
+    fws = torch.empty(ck.chunk_fwd_workspace_size(desc, False), device="cuda:0", dtype=torch.uint8)
+    o = torch.empty_like(v)
+    ht = torch.empty((B, H, dk, dv), device="cuda:0", dtype=torch.float32)
+    kw = dict(chunk_size=case.chunk, use_qk_l2norm=case.l2norm)
+
+    def step_recompute():
+        ck.chunk_fwd(q, k, v, a, b, out=o, final_state=ht, workspace=fws, **kw)
+        ck.chunk_bwd(q, k, v, a, b, dout, dht=dht, workspace=bws, **kw)
+
+    def step_saved():
+        ck.chunk_fwd_save(q, k, v, a, b, out=o, final_state=ht, saved=bws, **kw)
+        ck.chunk_bwd(q, k, v, a, b, dout, dht=dht, saved=bws, **kw)
+
+    def bwd_saved():
+        ck.chunk_bwd(q, k, v, a, b, dout, dht=dht, saved=bws, **kw)
+
+    out = {}
+    out["step_recompute"], _ = time_launches(step_recompute, steps, warmup)
+    out["step_saved"], _ = time_launches(step_saved, steps, warmup)
+    out["bwd_saved"], _ = time_launches(bwd_saved, steps, warmup)  # on the last step's save
+    out["saved_bytes"] = bws.numel()
+    del q, k, v, a, b, dout, dht, bws, fws, o, ht
+    torch.cuda.empty_cache()
+    return out
+
+
 def bwd_bytes(B, T, H, dk, dv, es):
     """Algorithmic bytes of the backward: q, k, v, dout read in the io type,
     alpha, beta read as fp32 (once); dq, dk, dv, dalpha, dbeta written as
@@ -396,7 +441,11 @@ def main():
     C = case.chunk
     if args.only == "bwd":
         ms_bw = bench_bwd(case, args.steps, args.warmup)
+        tr = bench_train(case, args.steps, args.warmup)
         print(json.dumps({"workload": "backward of the LM layer", "ms_per_call": round(ms_bw, 3),
+                          "bwd_saved_ms": round(tr["bwd_saved"], 3),
+                          "step_recompute_ms": round(tr["step_recompute"], 3),
+                          "step_saved_ms": round(tr["step_saved"], 3),
                           "steps": args.steps, "warmup": args.warmup}), flush=True)
         return
     ms, wall_ms, per = bench_fwd(case, args.steps, args.warmup, "ckda", passes="each")
@@ -516,6 +565,17 @@ def main():
             "ms_per_call": round(ms_bw, 3), "tokens_per_s": round(tokens / (ms_bw / 1000.0), 1),
             "over_forward": round(ms_bw / ms, 2), "algorithmic_bytes": bb,
             "hbm_frac": round(bb / (ms_bw / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+        tr = bench_train(case, max(5, args.steps // 3), 2)
+        out["training_step"] = {
+            "workload": "forward + backward of the headline layer per step: with the backward "
+                        "recomputing the forward (ckda_chunk_fwd + ckda_chunk_bwd), and with the "
+                        "forward keeping the backward's records (ckda_chunk_fwd_save + "
+                        "ckda_chunk_bwd_saved)",
+            "ms_recompute": round(tr["step_recompute"], 3), "ms_saved": round(tr["step_saved"], 3),
+            "saved_over_recompute": round(tr["step_saved"] / tr["step_recompute"], 4),
+            "bwd_saved_ms": round(tr["bwd_saved"], 3),
+            "bwd_saved_hbm_frac": round(bb / (tr["bwd_saved"] / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+            "saved_bytes": tr["saved_bytes"]}
         vl = inputs.varlen()
         ms_vl, _, _ = bench_fwd(vl, max(5, args.steps // 3), 2, "ckda")
         vl_tok = int(vl.cu_seqlens[-1])

@@ -13,7 +13,7 @@ import threading
 
 __all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_workspace_size", "recurrent_step",
            "l2norm_debug", "fwd_supported",
-           "library_path", "abi_version", "CkdaError", "BF16", "F32", "GATE_KDA",
+           "library_path", "abi_version", "chunk_fwd_save", "CkdaError", "BF16", "F32", "GATE_KDA",
            "GATE_CKDA", "GATES_F32", "GATES_LOGITS_F32", "GATES_LOGITS_BF16", "ChunkFwdPlan"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +75,10 @@ def _load():
         lib.ckda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), i32]
         lib.ckda_chunk_bwd.restype = i32
         lib.ckda_chunk_bwd.argtypes = [ctypes.POINTER(FwdDesc)] + [vp] * 16 + [ctypes.c_size_t, vp]
+        lib.ckda_chunk_fwd_save.restype = i32
+        lib.ckda_chunk_fwd_save.argtypes = [ctypes.POINTER(FwdDesc)] + [vp] * 10 + [ctypes.c_size_t, vp]
+        lib.ckda_chunk_bwd_saved.restype = i32
+        lib.ckda_chunk_bwd_saved.argtypes = [ctypes.POINTER(FwdDesc)] + [vp] * 16 + [ctypes.c_size_t, vp]
         lib.ckda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
         lib.ckda_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), i32]
         lib.ckda_fwd_supported.restype = i32
@@ -253,6 +257,28 @@ def chunk_fwd_noalloc(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_s
     return o, ht
 
 
+def chunk_fwd_save(q, k, v, alpha, beta, *, h0=None, cu_seqlens=None, chunk_size=64,
+                   use_qk_l2norm=True, gate="ckda", scale=1.0, output_final_state=True,
+                   out=None, final_state=None, saved=None, stream=None, gates="values"):
+    """chunk_fwd through ckda_chunk_fwd_save: the same (o, ht), plus the
+    backward's records kept in `saved` (uint8 device tensor of at least
+    chunk_bwd_workspace_size() bytes, allocated when omitted) for
+    chunk_bwd(..., saved=saved).  Returns (o, ht, saved)."""
+    import torch
+    lib = _load()
+    desc, o, ht = _fwd_call(q, k, v, alpha, beta, h0, cu_seqlens, chunk_size, use_qk_l2norm, gate,
+                            scale, output_final_state, out, final_state, gates, False)
+    need = chunk_bwd_workspace_size(desc, cu_seqlens is not None)
+    if saved is None:
+        saved = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _require(saved.is_cuda and saved.dtype == torch.uint8 and saved.numel() >= need,
+             "saved must be a uint8 device tensor of at least %d bytes" % need)
+    _check(lib.ckda_chunk_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
+                                   _ptr(saved), saved.numel(), _stream(stream)))
+    return o, ht, saved
+
+
 def chunk_bwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
     """Bytes of workspace ckda_chunk_bwd needs for `desc`."""
     return int(_load().ckda_chunk_bwd_workspace_size(ctypes.byref(desc), int(bool(packed))))
@@ -260,14 +286,16 @@ def chunk_bwd_workspace_size(desc: FwdDesc, packed: bool) -> int:
 
 def chunk_bwd(q, k, v, alpha, beta, dout, *, h0=None, dht=None, cu_seqlens=None, chunk_size=64,
               use_qk_l2norm=True, gate="ckda", scale=1.0, output_dh0=True, workspace=None,
-              stream=None, gates="values"):
+              stream=None, gates="values", saved=None):
     """Gradients of chunk_fwd for dL/do = dout (dtype of v) and dL/dht = dht
     ([N,H,dk,dv] float32, None for zero).  Same layouts as chunk_fwd: q, k on
     Hk heads (grouped value heads when Hk < H), gates='values' (float32
     gates) or 'logits' (float32 or bfloat16 logits; the gradients are then
-    those of the logits).  Returns float32 (dq, dk, dv, dalpha, dbeta, dh0)
-    shaped like q, k, v, alpha, beta and [N,H,dk,dv] (dh0 None unless
-    output_dh0)."""
+    those of the logits).  With `saved` (from chunk_fwd_save on the same
+    inputs) the records are read from it (ckda_chunk_bwd_saved) instead of
+    recomputed, and it serves as the workspace.  Returns float32 (dq, dk, dv,
+    dalpha, dbeta, dh0) shaped like q, k, v, alpha, beta and [N,H,dk,dv] (dh0
+    None unless output_dh0)."""
     import torch
     lib = _load()
     H, dk, dv = v.shape[-2], q.shape[-1], v.shape[-1]
@@ -302,14 +330,18 @@ def chunk_bwd(q, k, v, alpha, beta, dout, *, h0=None, dht=None, cu_seqlens=None,
     dbe = torch.empty(beta.shape, **f32)
     dh0 = torch.empty((desc.num_seqs, H, dk, dv), **f32) if output_dh0 else None
     need = chunk_bwd_workspace_size(desc, cu_seqlens is not None)
+    fn = lib.ckda_chunk_bwd
+    if saved is not None:
+        _require(workspace is None, "pass either workspace or saved")
+        workspace, fn = saved, lib.ckda_chunk_bwd_saved
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     _require(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.numel() >= need,
              "workspace must be a uint8 device tensor of at least %d bytes" % need)
-    _check(lib.ckda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                              _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(dout), _ptr(dht),
-                              _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dal), _ptr(dbe), _ptr(dh0),
-                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+              _ptr(cu_seqlens), _ptr(h0), _ptr(dout), _ptr(dht), _ptr(dq), _ptr(dkk), _ptr(dvv),
+              _ptr(dal), _ptr(dbe), _ptr(dh0), _ptr(workspace), workspace.numel(),
+              _stream(stream)))
     return dq, dkk, dvv, dal, dbe, dh0
 
 

@@ -272,7 +272,7 @@ ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
                       const void* alpha, const void* beta, const int32_t* cu_seqlens,
                       const float* h0, const void* dout, const float* dht, float* dq, float* dk,
                       float* dv, float* dalpha, float* dbeta, float* dh0, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, bool recompute) {
   ckda_status_t st = validate_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, dout, nullptr, nullptr,
                                   0, kPrepare | kFinish, false);
   if (st != CKDA_OK) return st;
@@ -341,7 +341,48 @@ ckda_status_t run_bwd(const ckda_fwd_desc_t* d, const void* q, const void* k, co
   const size_t core = ckda::bwd_workspace_bytes(d->B, d->T, d->H, d->dk, d->dv, d->num_seqs,
                                                 d->chunk_size, d->io_dtype, cu_seqlens != nullptr);
   return from_hip(ckda::launch_bwd_full(b, d->io_dtype, workspace, core,
-                                        static_cast<hipStream_t>(stream)));
+                                        static_cast<hipStream_t>(stream), recompute));
+}
+
+// The forward that also keeps the backward's records in `saved` (laid out as
+// the backward's workspace), for ckda_chunk_bwd_saved.
+ckda_status_t run_fwd_save(const ckda_fwd_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* alpha, const void* beta, const int32_t* cu_seqlens,
+                           const float* h0, void* o, float* ht, void* saved, size_t saved_bytes,
+                           void* stream) {
+  ckda_status_t st = validate_fwd(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht, nullptr, 0,
+                                  kPrepare | kFinish, false);
+  if (st != CKDA_OK) return st;
+  if (d->sign_absorb != 0)
+    return fail(CKDA_ERR_UNSUPPORTED, "the backward's records have no sign-absorption path");
+  const int64_t tokens = static_cast<int64_t>(d->B) * d->T;
+  const int64_t eb = elem_bytes(d->io_dtype), gb = gate_bytes(d->gate_input);
+  const int32_t Hk = qk_heads_of(d->H, d->qk_heads);
+  const int64_t state_bytes = static_cast<int64_t>(d->num_seqs) * d->H * d->dk * d->dv * 4;
+  const int64_t nqk = tokens * Hk * d->dk, na = tokens * d->H * d->dk, nv = tokens * d->H * d->dv;
+  const Range others[] = {range("q", q, q ? nqk * eb : 0), range("k", k, k ? nqk * eb : 0),
+                          range("v", v, v ? nv * eb : 0), range("alpha", alpha, alpha ? gb * na : 0),
+                          range("beta", beta, beta ? gb * tokens * d->H : 0),
+                          range("h0", h0, h0 ? state_bytes : 0), range("o", o, o ? nv * eb : 0),
+                          range("ht", ht, ht ? state_bytes : 0),
+                          range("cu_seqlens", cu_seqlens,
+                                cu_seqlens ? 4 * (static_cast<int64_t>(d->num_seqs) + 1) : 0)};
+  const size_t need = ckda_chunk_bwd_workspace_size(d, cu_seqlens ? 1 : 0);
+  if (need > 0) {
+    if (!saved) return fail(CKDA_ERR_INVALID_ARGUMENT, "saved is NULL (%zu bytes needed)", need);
+    if ((reinterpret_cast<uintptr_t>(saved) & 255u) != 0)
+      return fail(CKDA_ERR_INVALID_ARGUMENT, "saved is not 256-byte aligned");
+    if (saved_bytes < need)
+      return fail(CKDA_ERR_WORKSPACE_TOO_SMALL, "saved has %zu bytes, %zu needed", saved_bytes, need);
+    const Range rs = range("saved", saved, static_cast<int64_t>(need));
+    for (const Range& r : others)
+      if (overlap(rs, r)) return fail(CKDA_ERR_INVALID_ARGUMENT, "saved overlaps %s", r.name);
+  }
+  if (d->num_seqs == 0) return ok();
+  ckda::FwdArgs a{d->B, d->T, d->H, d->dk, d->dv, d->num_seqs, d->chunk_size, Hk,
+                  d->use_qk_l2norm, d->gate_range, d->gate_input, 0, d->scale, q, k, v, alpha,
+                  beta, cu_seqlens, h0, o, ht, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+  return from_hip(ckda::launch_fwd_save(a, d->io_dtype, saved, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -355,7 +396,24 @@ ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* d, const void* q, const void
                              float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
                              void* stream) {
   return run_bwd(d, q, k, v, alpha, beta, cu_seqlens, h0, dout, dht, dq, dk, dv, dalpha, dbeta,
-                 dh0, workspace, workspace_bytes, stream);
+                 dh0, workspace, workspace_bytes, stream, true);
+}
+
+ckda_status_t ckda_chunk_fwd_save(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                                  const void* v, const void* alpha, const void* beta,
+                                  const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
+                                  void* saved, size_t saved_bytes, void* stream) {
+  return run_fwd_save(d, q, k, v, alpha, beta, cu_seqlens, h0, o, ht, saved, saved_bytes, stream);
+}
+
+ckda_status_t ckda_chunk_bwd_saved(const ckda_fwd_desc_t* d, const void* q, const void* k,
+                                   const void* v, const void* alpha, const void* beta,
+                                   const int32_t* cu_seqlens, const float* h0, const void* dout,
+                                   const float* dht, float* dq, float* dk, float* dv,
+                                   float* dalpha, float* dbeta, float* dh0, void* saved,
+                                   size_t saved_bytes, void* stream) {
+  return run_bwd(d, q, k, v, alpha, beta, cu_seqlens, h0, dout, dht, dq, dk, dv, dalpha, dbeta,
+                 dh0, saved, saved_bytes, stream, false);
 }
 
 ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* d, const void* q, const void* k,

@@ -114,11 +114,14 @@ size_t bwd_gates_extra_bytes(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_
 }
 
 launch_result launch_bwd_full(BwdArgs b, int32_t io_dtype, void* ws, size_t core_bytes,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool recompute) {
   FwdArgs& a = b.f;
   const bool logits = a.gate_input != CKDA_GATES_F32;
   const bool grouped = a.Hk != a.H;
-  if (!logits && !grouped) return launch_bwd(b, io_dtype, ws, stream);
+  auto core = [&]() {
+    return recompute ? launch_bwd(b, io_dtype, ws, stream) : launch_bwd_saved(b, io_dtype, ws, stream);
+  };
+  if (!logits && !grouped) return core();
   const int64_t tok = static_cast<int64_t>(a.B) * a.T;
   const int64_t es = io_dtype == CKDA_DTYPE_BF16 ? 2 : 4;
   const int64_t na = tok * a.H * a.dk, nb = tok * a.H;
@@ -173,7 +176,7 @@ launch_result launch_bwd_full(BwdArgs b, int32_t io_dtype, void* ws, size_t core
     b.dk = dkx;
   }
   {
-    const launch_result r = launch_bwd(b, io_dtype, ws, stream);
+    const launch_result r = core();
     if (r != hipSuccess) return r;
   }
   if (tok == 0) return hipSuccess;

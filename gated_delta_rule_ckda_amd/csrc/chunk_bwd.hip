@@ -1531,7 +1531,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   using Op = OpBF16;
   using Frag = Op::Frag;
   constexpr int C = Cfg::C, DK = Cfg::DK, DV = Cfg::DV, NB = Cfg::NB, NW = Cfg::NW, NT = Cfg::NT;
-  constexpr int LDV = Cfg::LDV, LDC = Cfg::LDC, NFV = Cfg::NFV, NFC = Cfg::NFC;
+  constexpr int LDV = Cfg::LDV, LDC = Cfg::LDC, NFV = Cfg::NFV;
   const FwdArgs& a = b.f;
   const int H = a.H;
   const int c = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);

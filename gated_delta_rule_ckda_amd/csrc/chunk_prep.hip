@@ -36,12 +36,17 @@
 // [2^-100, 2^10] (the usual case) the anchor is the chunk start instead
 // (Fb = Ft, every E_IJ = 1, no scaling); otherwise, when every |Fb_r| lies in
 // that range (a condition on 16 consecutive gates), the block anchors are
-// used.  Chunks that pass neither test (exact zero gates, products that
-// underflow over 16 tokens, non-finite values) are flagged and left to a
-// second, short launch that forms A, P and Kh from direct products of the
-// gates (staged in LDS): exact, slower, absent from realistic gate
-// distributions.  Keeping that path out of the MFMA kernel keeps the
-// kernel's registers to what the other chunks need.
+// used.  Chunks that pass neither test (exact zero gates among them: a zero
+// makes every later plain product zero; products that underflow over 16
+// tokens; non-finite values) are flagged and left to a second launch.  It
+// restarts the products after each zero gate and masks the MFMA operands per
+// (row, channel) with a map of the zero rows, so the pairs that straddle a
+// zero drop out of A, P and Kh exactly (sign, magnitude and zero kept apart,
+// as in Proposition 2 of the picx.dev summary, "Theoretical Framework").
+// Chunks with two zeros in one (16-row block, channel), or with restarted
+// products still out of range, get A, P and Kh from direct products of the
+// gates staged in LDS.  Keeping both forms out of the first launch keeps its
+// registers to what the other chunks need.
 //
 // Gates arrive as float32 values or as logits (float32 or bf16) activated on
 // load (ckda_internal.h).
@@ -53,7 +58,7 @@
 //   1  loads, running products within the wave's rows, row norms
 //   2  chunk-level products Ft, anchor choice, regularity vote, operands Lk,
 //      Lq, Rk (and E_IJ for block anchors); Qt', g out
-//   3  A and P on MFMA (the direct kernel: from direct products); P' out
+//   3  A and P on MFMA (masked in the second launch, or direct products); P' out
 //   4  Kt'^T to LDS, Kh'^T out; 16x16 diagonal blocks of X by forward substitution
 //   5  off-diagonal blocks X_IJ = -X_II sum_{J<=M<I} A_IM X_MJ on fp32 MFMA
 //   6  X' out, -W = -X Kt' on MFMA, out

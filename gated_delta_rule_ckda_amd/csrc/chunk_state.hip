@@ -636,4 +636,39 @@ launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stre
   return launch_bwd_passes(b, io_dtype, stream);
 }
 
+launch_result launch_fwd_save(FwdArgs fa, int32_t io_dtype, void* ws, hipStream_t stream) {
+  BwdArgs b{};
+  b.f = fa;
+  FwdArgs& a = b.f;
+  a.sign_absorb = 0;
+  unsigned char* base = fwd_layout(a, io_dtype, ws);
+  const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
+  if (!e) return hipErrorInvalidValue;
+  if (static_cast<int64_t>(a.num_seqs) * a.H == 0) return hipSuccess;
+  // the records go where launch_bwd would put them; o and ht are written too
+  bwd_layout(b, base, io_dtype);
+  if (a.cu_seqlens) {
+    const launch_result r = launch_chunk_map(a, stream);
+    if (r != hipSuccess) return r;
+  }
+  if (a.maxc > 0) {
+    const launch_result r = launch_prep(a, io_dtype, stream);
+    if (r != hipSuccess) return r;
+  }
+  return e->fn(a, stream);
+}
+
+launch_result launch_bwd_saved(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stream) {
+  FwdArgs& a = b.f;
+  a.sign_absorb = 0;
+  unsigned char* base = fwd_layout(a, io_dtype, ws);
+  const Entry* e = find(a.chunk, a.dk, a.dv, io_dtype);
+  if (!e) return hipErrorInvalidValue;
+  if (static_cast<int64_t>(a.num_seqs) * a.H == 0) return hipSuccess;
+  bwd_layout(b, base, io_dtype);
+  a.o = nullptr;
+  a.ht = nullptr;
+  return launch_bwd_passes(b, io_dtype, stream);
+}
+
 }  // namespace ckda

@@ -86,7 +86,7 @@ struct FwdArgs {
   int32_t* first;         // [num_seqs + 1] first chunk of each sequence (packed batches)
   int32_t* chunk_seq;     // [maxc] sequence owning each chunk slot, -1 if unused (packed)
   int32_t* seq_order;     // [num_seqs] packed sequences by chunk count, most first (state pass)
-  int32_t* irregular;     // [H][maxc] 1 where the transform pass left a chunk to the direct kernel
+  int32_t* irregular;     // [H][maxc] 1 where the transform pass left a chunk to its second launch
   int32_t maxc;           // chunk slots per head
   int32_t nc;             // chunks per sequence (dense batches)
   int64_t blk_bytes;
@@ -158,6 +158,11 @@ launch_result launch_bwd_passes(const BwdArgs& b, int32_t io_dtype, hipStream_t 
 size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                            int32_t num_seqs, int32_t chunk, int32_t io_dtype, bool packed);
 launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stream);
+// The same split in two for training steps: the forward (o and ht written)
+// that leaves the records in the backward's workspace layout, and the
+// backward passes that read them there instead of recomputing them.
+launch_result launch_fwd_save(FwdArgs a, int32_t io_dtype, void* ws, hipStream_t stream);
+launch_result launch_bwd_saved(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stream);
 // The backward for gate logits and grouped value heads (bwd_gates.hip): the
 // workspace beyond the backward's own `core_bytes`, and the passes around
 // launch_bwd that prepare float32 gates and one q/k head per value head and
@@ -165,7 +170,7 @@ launch_result launch_bwd(BwdArgs b, int32_t io_dtype, void* ws, hipStream_t stre
 size_t bwd_gates_extra_bytes(int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t dk,
                              int32_t io_dtype, bool logits);
 launch_result launch_bwd_full(BwdArgs b, int32_t io_dtype, void* ws, size_t core_bytes,
-                              hipStream_t stream);
+                              hipStream_t stream, bool recompute = true);
 
 // ---- small device helpers shared by the kernels --------------------------
 

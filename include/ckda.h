@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 8
+#define CKDA_ABI_VERSION 9
 
 typedef enum {
   CKDA_OK = 0,
@@ -284,6 +284,45 @@ ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* desc, const void* q, const v
                              const float* dht, float* dq, float* dk, float* dv,
                              float* dalpha, float* dbeta, float* dh0, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * The forward and the backward of a training step, with the backward's
+ * records kept in between instead of recomputed (same chunked form and
+ * gradients as ckda_chunk_fwd and ckda_chunk_bwd; picx.dev summary of the
+ * Complex KDA paper, section "Background").
+ *
+ * ckda_chunk_fwd_save is ckda_chunk_fwd (same arguments, validation, o and
+ * ht) that also leaves in `saved` what ckda_chunk_bwd would recompute: every
+ * chunk's transform-pass block, X = (I + A)^{-1} in float32 and the state
+ * entering the chunk (io dtype).  `saved`: at least
+ * ckda_chunk_bwd_workspace_size(desc, cu_seqlens != NULL) bytes, 256-byte
+ * aligned, overlapping no input or output (CKDA_ERR_WORKSPACE_TOO_SMALL
+ * below that size); sign_absorb = 0 (else CKDA_ERR_UNSUPPORTED).
+ *
+ * ckda_chunk_bwd_saved is ckda_chunk_bwd with `saved` in the place of the
+ * workspace, from which it reads the records rather than running the
+ * forward again.  Precondition, not checked: `saved` was filled by
+ * ckda_chunk_fwd_save with the same descriptor, cu_seqlens and forward
+ * inputs, on the same stream or ordered before, and left untouched since.
+ * The call only reads the records (it writes its own passes' data to the
+ * rest of `saved`), so it may run any number of times on one save.  The
+ * gradients are ckda_chunk_bwd's: the records are the same kernels' output
+ * on the same inputs.
+ *
+ * For a layer of B=8, T=4096, H=16, d=128 in bf16, `saved` is 1.62 GB, of
+ * which the records take 0.94 GB; the backward call no longer runs the
+ * forward's two passes.
+ */
+ckda_status_t ckda_chunk_fwd_save(const ckda_fwd_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const void* alpha, const void* beta,
+                                  const int32_t* cu_seqlens, const float* h0, void* o,
+                                  float* ht, void* saved, size_t saved_bytes, void* stream);
+ckda_status_t ckda_chunk_bwd_saved(const ckda_fwd_desc_t* desc, const void* q, const void* k,
+                                   const void* v, const void* alpha, const void* beta,
+                                   const int32_t* cu_seqlens, const float* h0,
+                                   const void* dout, const float* dht, float* dq, float* dk,
+                                   float* dv, float* dalpha, float* dbeta, float* dh0,
+                                   void* saved, size_t saved_bytes, void* stream);
 
 /*
  * Fused single-token decode step for N sequences: the recurrent form of the

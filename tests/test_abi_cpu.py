@@ -340,3 +340,46 @@ def test_bwd_workspace_for_logits_and_grouped_heads():
     # a workspace for the plain call is too small for the logits call
     st, msg = _bwd(lg, ws_bytes=core)
     assert st == 3 and "needed" in msg
+
+
+def _fwd_save(desc, **over):
+    p = dict(P)
+    p.update(over)
+    lib = ck._load()
+    st = lib.ckda_chunk_fwd_save(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"],
+                                 p["v"], p["alpha"], p["beta"], p.get("cu_seqlens"), p["h0"],
+                                 p["o"], p["ht"], p["ws"], p.get("ws_bytes", WS_BYTES), None)
+    return st, lib.ckda_last_error().decode()
+
+
+@pytest.mark.parametrize("desc_over,over,status,needle", [
+    (dict(sign_absorb=1), {}, 2, "sign-absorption"),
+    (dict(B=0), {}, 1, "non-positive"),
+    ({}, dict(ws=None), 1, "saved is NULL"),
+    ({}, dict(ws=ctypes.c_void_p(P["ws"].value + 16)), 1, "256-byte aligned"),
+    ({}, dict(ws_bytes=4096), 3, "saved has 4096 bytes"),
+    ({}, dict(ws=P["o"]), 1, "saved overlaps o"),
+    ({}, dict(ws=P["alpha"]), 1, "saved overlaps alpha"),
+    ({}, dict(o=P["q"]), 1, "overlaps"),
+])
+def test_fwd_save_validation(desc_over, over, status, needle):
+    """The forward that keeps the backward's records takes the forward's
+    checks plus the backward workspace's size, alignment and overlaps for
+    `saved`, on the host before any HIP call."""
+    st, msg = _fwd_save(_desc(**desc_over), **over)
+    assert st == status and needle in msg, msg
+
+
+def test_bwd_saved_takes_the_backward_checks():
+    lib = ck._load()
+    d = _desc()
+    p = dict(P)
+    p.update(PB)
+    args = [p["q"], p["k"], p["v"], p["alpha"], p["beta"], None, p["h0"], p["dout"], p["dht"],
+            p["dq"], p["dk"], p["dv"], p["dalpha"], p["dbeta"], p["dh0"], p["ws"]]
+    assert lib.ckda_chunk_bwd_saved(ctypes.byref(d), *args, 1024, None) == 3
+    assert "workspace has 1024 bytes" in lib.ckda_last_error().decode()
+    assert lib.ckda_chunk_bwd_saved(ctypes.byref(_desc(sign_absorb=1)), *args, WS_BYTES, None) == 2
+    bad = list(args)
+    bad[9] = None  # dq
+    assert lib.ckda_chunk_bwd_saved(ctypes.byref(d), *bad, WS_BYTES, None) == 1
