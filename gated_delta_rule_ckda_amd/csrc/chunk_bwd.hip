@@ -1746,7 +1746,12 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   // the chunk-anchored operands, formed where they are used
   auto Kt = [&](int t) { return kh[t] * F[t]; };
   auto Qt = [&](int t) { return qh[t] * F[t]; };
-  auto Rk = [&](int t) { return kh[t] / F[t]; };
+  auto Rk = [&](int t) {
+    f32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = kh[t][i] * __builtin_amdgcn_rcpf(F[t][i]);
+    return x;
+  };
   // F at the last row of each tile (e_t) and at the row before it (a_t)
   float Fe[NB], Fa[NB];
 #pragma unroll
@@ -1815,7 +1820,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
           const int u = 2 * sl + hh;
           if (u < t || u >= NB) continue;
           if (u == t) {
-            const float re = 1.f / Fe[t];
+            const float re = __builtin_amdgcn_rcpf(Fe[t]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) kap[t][i] = kh[t][i] * re * dRk[t][i];
           }
@@ -1834,10 +1839,10 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
     ep[t] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float f = F[t][i];
-      dkh[t][i] = dKt[t][i] * f + dRk[t][i] / f;
+      const float f = F[t][i], rf = __builtin_amdgcn_rcpf(f);  // F in [2^-100, 2^10]
+      dkh[t][i] = dKt[t][i] * f + dRk[t][i] * rf;
       dqh[t][i] = dQt[t][i] * f;
-      ep[t] += gch * dKh[t][i] * (kh[t][i] / f);
+      ep[t] += gch * dKh[t][i] * (kh[t][i] * rf);
     }
   }
   // over the four lane groups (the tile's 16 rows): the chunk end's pair with
@@ -1936,132 +1941,111 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   // Pre_s = D(s-1<-a_b), Suf_s = D(e_b<-s) are products inside the tile;
   // rho, kappa and Gamma_b are the pair terms anchored at the tile's edges,
   // formed above from the chunk-anchored operands (ratios of running
-  // products within [2^-100, 2^10], so bounded and accurate).  The sums over
-  // the tile run as recurrences across the lane's 4 rows and then across
-  // the 4 lane groups, so no pair term is formed twice and none cancels.
+  // products within [2^-100, 2^10], so bounded and accurate).  The sums run
+  // down the rows of a tile, so each tile goes to one lane: through a
+  // per-wave LDS buffer (in the dO, dV, U rows, which no wave reads any
+  // more), lane (l16, lq) takes the 16 rows of tile lq of its channel.  All
+  // lanes of the wave then take the same row at the same step: the pairwise
+  // loop runs the 120 (r, j) pairs of a tile with no masked steps, and the
+  // recurrences need no carries between lanes.
   {
-    const float gdg = gch * dg;  // the (end, start) pair: adjoint dg times D = g
-    float ecum = 0.f;            // the end's pairs with the columns before tile b
+    constexpr int LDT = C + 4;  // floats per channel in the buffer (a 16-byte pad)
+    static_assert(NW * 16 * LDT * 4 <= Cfg::O_CC - Cfg::O_DO, "transpose buffer");
+    float* tbuf = reinterpret_cast<float*>(smem + Cfg::O_DO) + w * 16 * LDT;
+    const bool own = lq < NB;  // with fewer than 4 tiles the other lane groups only help move data
+    const int T = own ? lq : 0;
+    // rows 16t + 4lq + i held by lane (l16, lq) -> rows 16T + m of this lane
+    auto to_tile = [&](const f32x4(&x)[NB], float(&y)[16]) {
+      wave_lds_sync();  // this wave's earlier reads of the buffer are done
 #pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-      const float gam = (gdg + ecum + zp[tb]) * (Fa[tb] / Fe[tb]);
-      ecum += ep[tb];
-      // the lane's gates in tile b (1 beyond the chunk's rows); exclusive
-      // products inside the lane (lp: rows before, ls: rows after) and over
-      // the lane groups below and above inside the tile
-      float al[4];
+      for (int t = 0; t < NB; ++t) *reinterpret_cast<f32x4*>(tbuf + l16 * LDT + 16 * t + 4 * lq) = x[t];
+      wave_lds_sync();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = 16 * tb + 4 * lq + i < L ? xa[tb][i] : 1.f;
-      float lp[4], ls[4];
-      lp[0] = 1.f;
-      lp[1] = al[0];
-      lp[2] = lp[1] * al[1];
-      lp[3] = lp[2] * al[2];
-      ls[3] = 1.f;
-      ls[2] = al[3];
-      ls[1] = ls[2] * al[2];
-      ls[0] = ls[1] * al[1];
-      const float tot = lp[3] * al[3];
-      float up = tot, y;
-      y = __shfl_up(up, 16);
-      if (lq >= 1) up *= y;
-      y = __shfl_up(up, 32);
-      if (lq >= 2) up *= y;
-      float below = __shfl_up(up, 16);
-      if (lq == 0) below = 1.f;
-      float dn = tot;
-      y = __shfl_down(dn, 16);
-      if (lq <= 2) dn *= y;
-      y = __shfl_down(dn, 32);
-      if (lq <= 1) dn *= y;
-      float above = __shfl_down(dn, 16);
-      if (lq == 3) above = 1.f;
-      // sigma_s = rho_s + alpha_{s+1} sigma_{s+1}: inside the lane, then the
-      // carry alpha sigma of the next lane group's first row, top down
-      float sg[4];
-      sg[3] = rho[tb][3];
-      sg[2] = rho[tb][2] + al[3] * sg[3];
-      sg[1] = rho[tb][1] + al[2] * sg[2];
-      sg[0] = rho[tb][0] + al[1] * sg[1];
-      float cin = 0.f;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tbuf + l16 * LDT + 16 * T + 4 * g4);
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const float x = __shfl_down(al[0] * (sg[0] + ls[0] * cin), 16);
-        cin = lq == 3 ? 0.f : x;
+        for (int i = 0; i < 4; ++i) y[4 * g4 + i] = v[i];
       }
-      // pi_{s+1} = alpha_s pi_s + kappa_s: inside the lane, then the carry of
-      // the lane group below, bottom up
-      float pg[4];
-      pg[0] = 0.f;
-      pg[1] = kap[tb][0];
-      pg[2] = al[1] * pg[1] + kap[tb][1];
-      pg[3] = al[2] * pg[2] + kap[tb][2];
-      float pin = 0.f;
+    };
+    // Gamma of this lane's tile: the end's pair with the start (adjoint dg,
+    // D = g), the end's pairs with the columns before the tile and the
+    // tile's corner, moved to the tile's edges
+    float gam = 0.f;
+    {
+      const float gdg = gch * dg;
+      float ecum = 0.f;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const float x = __shfl_up(al[3] * (pg[3] + lp[3] * pin) + kap[tb][3], 16);
-        pin = lq == 0 ? 0.f : x;
+      for (int tb = 0; tb < NB; ++tb) {
+        const float gt = (gdg + ecum + zp[tb]) * (Fa[tb] / Fe[tb]);
+        ecum += ep[tb];
+        gam = tb == T ? gt : gam;
       }
-      // pairs inside the tile.  The tile's gates and keys from the lanes
-      // that hold them.  With Suf_r = D(e_b<-r), D(r<-s) = Suf_s / Suf_r (a
-      // ratio of gates after s), so for each of the lane's rows r one pass
-      //   phi = alpha_j phi + adj_rj / Suf_r  (j < r),  ps_{j+1} += phi
-      // leaves Psi_s = Suf_s * (ps_s summed over the rows r >= s); ps is
-      // then reduced over the four lane groups, each keeping its own rows.
-      float aj[16], kj[16];
+    }
+    float al[16], kt[16], qt[16];  // the tile's gates (1 past the chunk), k^, q^
+    {
+      f32x4 alx[NB];
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2)
+      for (int t = 0; t < NB; ++t)
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          aj[4 * q2 + i2] = __shfl(al[i2], l16 + 16 * q2);
-          kj[4 * q2 + i2] = __shfl(kh[tb][i2], l16 + 16 * q2);
-        }
-      float ps[16];
+        for (int i = 0; i < 4; ++i) alx[t][i] = 16 * t + 4 * lq + i < L ? xa[t][i] : 1.f;
+      to_tile(alx, al);
+    }
+    to_tile(kh, kt);
+    to_tile(qh, qt);
+    float suf[16];  // Suf_m: the tile's gates after row m
+    suf[15] = 1.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ps[e] = 0.f;
+    for (int m = 14; m >= 0; --m) suf[m] = suf[m + 1] * al[m + 1];
+    // pairs inside the tile.  With Suf_r = D(e_b<-r), D(r<-s) = Suf_s / Suf_r
+    // (a ratio of gates after s), so for each row r one pass
+    //   phi = alpha_j phi + adj_rj / Suf_r  (j < r),  ps_{j+1} += phi
+    // over its columns leaves Psi_s = Suf_s * ps_s, ps_s summed over the rows
+    // r >= s.  adj_rj = (dG_rj k^_r + dP_rj q^_r) k^_j.
+    float ps[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * lq + i;  // the row inside the tile
-        const __bf16* gr = sG + (16 * tb + rr) * LDC;
-        const __bf16* pr = sP + (16 * tb + rr) * LDC;
-        const float is = 1.f / (ls[i] * above);
-        const float kr = kh[tb][i] * is, qr = qh[tb][i] * is;
+    for (int m = 0; m < 16; ++m) ps[m] = 0.f;
+    {
+      // columns 4 q2 .. 4 q2 + 3 of tile T sit together in the storage order
+      const int tcol = C % 32 == 0 ? 32 * (T >> 1) + 4 * (T & 1) : 0;
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        const __bf16* gr = sG + (16 * T + r) * LDC + tcol;
+        const __bf16* pr = sP + (16 * T + r) * LDC + tcol;
+        const float is = 1.f / suf[r];
+        const float kr = kt[r] * is, qr = qt[r] * is;
         float phi = 0.f;
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          // dG_rj, dP_rj for the 4 columns j = 4 q2 .. 4 q2 + 3 of the tile
-          const int off = C % 32 == 0 ? 32 * (tb >> 1) + 8 * q2 + 4 * (tb & 1) : 4 * q2;
-          const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gr + off);
-          const bf16x4 p4 = *reinterpret_cast<const bf16x4*>(pr + off);
+        for (int q2 = 0; 4 * q2 < r; ++q2) {
+          const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gr + (C % 32 == 0 ? 8 : 4) * q2);
+          const bf16x4 p4 = *reinterpret_cast<const bf16x4*>(pr + (C % 32 == 0 ? 8 : 4) * q2);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * q2 + e;
-            if (j == 15) break;  // the last column pairs with no later row
-            phi = aj[j] * phi + (static_cast<float>(g4[e]) * kr + static_cast<float>(p4[e]) * qr) * kj[j];
-            ps[j + 1] += j < rr ? phi : 0.f;
+            if (j < r) {
+              phi = al[j] * phi + (static_cast<float>(g4[e]) * kr + static_cast<float>(p4[e]) * qr) * kt[j];
+              ps[j + 1] += phi;
+            }
           }
         }
       }
-      float h8[8];
+    }
+    // sigma_m = rho_m + alpha_{m+1} sigma_{m+1} from the bottom (into rt),
+    // then down the rows with Pre (running) and pi_{m+1} = alpha_m pi_m +
+    // kappa_m:  dalpha_m = Pre_m sigma_m + Suf_m (pi_m + Pre_m Gamma + ps_m)
+    float rt[16];
+    to_tile(rho, rt);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool hi = lq >= 2;
-        const float keep = hi ? ps[8 + e] : ps[e], send = hi ? ps[e] : ps[8 + e];
-        h8[e] = keep + __shfl_xor(send, 32);
-      }
-      float psi[4];
+    for (int m = 14; m >= 0; --m) rt[m] += al[m + 1] * rt[m + 1];
+    to_tile(kap, kt);  // k^ is no longer needed: kappa in its place
+    const rsrc_t rd = make_rsrc(b.dalpha + obase, orange);
+    float pre = 1.f, pi = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool odd = (lq & 1) != 0;
-        const float keep = odd ? h8[4 + e] : h8[e], send = odd ? h8[e] : h8[4 + e];
-        psi[e] = keep + __shfl_xor(send, 16);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pre = below * lp[i], suf = ls[i] * above;
-        const float sigma = sg[i] + ls[i] * cin, pi = pg[i] + lp[i] * pin;
-        ostore(b.dalpha, tb, i, pre * sigma + suf * pi + pre * suf * gam + suf * psi[i]);
-      }
+    for (int m = 0; m < 16; ++m) {
+      const float x = pre * rt[m] + suf[m] * (pi + pre * gam + ps[m]);
+      if (own)  // rows >= L fall outside the buffer range and are dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rd, ((16 * T + m) * H * DK + ch) * 4, 0, 0);
+      pi = al[m] * pi + kt[m];
+      pre *= al[m];
     }
   }
 
