@@ -260,7 +260,16 @@ struct BCfg {
   static constexpr int O_WT = align16(O_YT + C * LDC * ES);       // W'^T  [DK][LDC]
   static constexpr int O_QT = align16(O_WT + DK * LDC * ES);      // Qt'^T [DK][LDC]
   static constexpr int O_G = align16(O_QT + DK * LDC * ES);       // g [DK] fp32
-  static constexpr int LDS_BYTES = align16(O_G + DK * 4);
+  // the step's outputs, staged for whole-row stores by the loader waves:
+  // dS1 [DK][DVT] and dU [C][DVT] in the io type, dV [C][DVT] fp32; rows
+  // padded so that the four rows a state-wave store touches fall in
+  // different banks
+  static constexpr int SROW = DVT * IOES, LDS_S = SROW + 16, LDS_V = DVT * 4 + (DVT * 4 >= 64 ? 64 : 16);
+  static constexpr int O_SS = align16(O_G + DK * 4);
+  static constexpr int O_SU = O_SS + DK * LDS_S;
+  static constexpr int O_SV = O_SU + C * LDS_S;
+  static constexpr int LDS_BYTES = align16(O_SV + C * LDS_V);
+  static_assert(SROW % 16 == 0 && (DVT * 4) % 16 == 0, "staged rows in 16-byte pieces");
   static_assert(GB_G == blk_g_byte(C, DK, ES), "block layout");
   static_assert(DV % DVT == 0 && DVT % 16 == 0 && NSW >= 1 && NSW <= 4, "dv tiling");
   static_assert((C * ES) % 16 == 0 && (DK * ES) % 16 == 0 && (DVT * IOES) % 16 == 0, "rows in pieces");
@@ -387,6 +396,25 @@ struct BGroup {
   }
 };
 
+// One staged tile out to memory as 16-byte pieces by the loader threads: R
+// rows of ROWB bytes from LDS (row stride LD) to rows at `g` + r * gstride
+// bytes; rows >= rmax are not written.
+template <int R, int ROWB, int LD, int NLT>
+__device__ __forceinline__ void flush_rows(const unsigned char* st, unsigned char* g, int64_t gstride,
+                                           int rmax, int lt) {
+  constexpr int PPR = ROWB / 16, NP = R * PPR;
+#pragma unroll
+  for (int u = 0; u < (NP + NLT - 1) / NLT; ++u) {
+    const int pc = lt + NLT * u;
+    if (NP % NLT == 0 || pc < NP) {
+      const int r = pc / PPR, c = pc % PPR;
+      if (r < rmax)
+        *reinterpret_cast<uint4*>(g + r * gstride + 16 * c) =
+            *reinterpret_cast<const uint4*>(st + r * LD + 16 * c);
+    }
+  }
+}
+
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
   using Op = typename Cfg::Op;
@@ -461,19 +489,14 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
 
     for (int k = 0; k < nch; ++k) {
       const int i = nch - 1 - k;
-      const int64_t slot = static_cast<int64_t>(h) * a.maxc + c_begin + i;
-      // the lane's row and column through an opaque move: the store addresses
-      // below are formed per chunk instead of being hoisted out of the loop
-      // (one 64-bit address per stored value, which only costs spills)
-      int lqo, colo;
-      asm volatile("v_mov_b32 %0, %1" : "=v"(lqo) : "v"(lq));
-      asm volatile("v_mov_b32 %0, %1" : "=v"(colo) : "v"(col));
-      {  // the adjoint at the chunk's end, for the intra-chunk pass
-        ST* ds = static_cast<ST*>(b.dS) + slot * DK * dv + colo + 4 * lqo * dv;
+      {  // the adjoint at the chunk's end, for the intra-chunk pass (staged;
+         // the loaders store it)
+        ST* ds = reinterpret_cast<ST*>(smem + Cfg::O_SS) + 16 * wave + l16;
 #pragma unroll
         for (int mc = 0; mc < NMC; ++mc)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) IO::store(ds, (16 * mc + ii) * dv, sacc[mc][ii]);
+          for (int ii = 0; ii < 4; ++ii)
+            IO::store(ds, (16 * mc + 4 * lq + ii) * (Cfg::LDS_S / Cfg::IOES), sacc[mc][ii]);
       }
       __syncthreads();  // group A of this chunk is in LDS
       Frag sf[NFK], of[NFC];
@@ -504,18 +527,18 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
         }
       }
       {
-        ST* du = static_cast<ST*>(b.dU) + slot * C * dv + colo + 4 * lqo * dv;
+        ST* du = reinterpret_cast<ST*>(smem + Cfg::O_SU) + 16 * wave + l16;
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) IO::store(du, (16 * rb + ii) * dv, uacc[rb][ii]);
+          for (int ii = 0; ii < 4; ++ii)
+            IO::store(du, (16 * rb + 4 * lq + ii) * (Cfg::LDS_S / Cfg::IOES), uacc[rb][ii]);
       }
       Frag uf[NFC];
       Op::template frags<C>(uf, uacc);
       __syncthreads();  // group B of this chunk is in LDS
-      {  // dV = X'^T dU, rows < L
-        const int L = chunk_len(i);
-        float* dvo = b.dv + (chunk_t0(i) * H + h) * dv + colo;
+      {  // dV = X'^T dU (staged; the loaders store rows < L one step later)
+        float* dvo = reinterpret_cast<float*>(smem + Cfg::O_SV) + 16 * wave + l16;
         Frag yf[NB][NFC];
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb)
@@ -529,10 +552,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
           for (int s = 0; s < NFC; ++s)
             if (Cfg::up_live(rb, s)) Op::mma(acc, yf[rb][s], uf[s]);
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int r = 16 * rb + 4 * lqo + ii;
-            if (r < L) dvo[static_cast<int64_t>(r) * H * dv] = acc[ii];
-          }
+          for (int ii = 0; ii < 4; ++ii) dvo[(16 * rb + 4 * lq + ii) * (Cfg::LDS_V / 4)] = acc[ii];
         }
       }
       // dS0 = Diag(g) dS1 + W'^T dU + Qt'^T dO, in two halves of the rows
@@ -563,6 +583,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
         }
       }
     }
+    __syncthreads();  // the loaders store the last chunk's dV
     if (b.dh0) {
 #pragma unroll
       for (int mc = 0; mc < NMC; ++mc)
@@ -591,15 +612,40 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
       sa0.store(smem, chunk_len(chunk_of(0)), lt);
       issueA(sa0, 2);
     }
+    // the state waves' staged outputs of step k, as whole rows
+    constexpr int NLT = Cfg::NLT, IOES = Cfg::IOES;
+    auto slot_of = [&](int k) { return static_cast<int64_t>(h) * a.maxc + c_begin + chunk_of(k); };
+    auto flush_dS = [&](int k) {
+      flush_rows<DK, Cfg::SROW, Cfg::LDS_S, NLT>(
+          smem + Cfg::O_SS, static_cast<unsigned char*>(b.dS) + (slot_of(k) * DK * dv + dv0) * IOES,
+          static_cast<int64_t>(dv) * IOES, DK, lt);
+    };
+    auto flush_dU = [&](int k) {
+      flush_rows<C, Cfg::SROW, Cfg::LDS_S, NLT>(
+          smem + Cfg::O_SU, static_cast<unsigned char*>(b.dU) + (slot_of(k) * C * dv + dv0) * IOES,
+          static_cast<int64_t>(dv) * IOES, C, lt);
+    };
+    auto flush_dV = [&](int k) {
+      const int i = chunk_of(k);
+      flush_rows<C, Cfg::DVT * 4, Cfg::LDS_V, NLT>(
+          smem + Cfg::O_SV, reinterpret_cast<unsigned char*>(b.dv + (chunk_t0(i) * H + h) * dv + dv0),
+          static_cast<int64_t>(H) * dv * 4, chunk_len(i), lt);
+    };
     // step k: B(k) (in gb) goes to LDS while dU(k) runs, then A(k+1) (in ga)
-    // while dV(k) and dS0(k) run; gb then takes B(k+2) and ga takes A(k+3)
+    // while dV(k) and dS0(k) run; gb then takes B(k+2) and ga takes A(k+3).
+    // dS1(k) and dV(k-1) were staged before the first barrier of step k, dU(k)
+    // before the second; each is read here before the state waves stage the
+    // next one (after the other barrier).
     auto step = [&](int k, GB& gb, GA& ga) {
       __syncthreads();
       gb.store(smem, 0, lt);
       issueB(gb, k + 2);
+      flush_dS(k);
+      if (k > 0) flush_dV(k - 1);
       __syncthreads();
       ga.store(smem, chunk_len(chunk_of(k + 1)), lt);
       issueA(ga, k + 3);
+      flush_dU(k);
     };
     int k = 0;
     for (; k + 1 < nch; k += 2) {
@@ -607,6 +653,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
       step(k + 1, sb1, sa0);
     }
     if (k < nch) step(k, sb0, sa1);
+    __syncthreads();  // the last chunk's dV is staged
+    if (nch > 0) flush_dV(nch - 1);
   }
 }
 
