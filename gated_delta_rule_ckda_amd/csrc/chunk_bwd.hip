@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   __bf16* sY = reinterpret_cast<__bf16*>(smem + Cfg::O_Y);
   __bf16* sX = reinterpret_cast<__bf16*>(smem + Cfg::O_X);
   __bf16* sXT = reinterpret_cast<__bf16*>(smem + Cfg::O_XT);
-  float* nrm = reinterpret_cast<float*>(smem + Cfg::O_RED);  // [2][C]
+  float* nrm = reinterpret_cast<float*>(smem + Cfg::O_RED);  // [2][C] reciprocal row norms
   float* nrw = nrm + 2 * C;                                    // [NW][2][C]
   float* dbp = nrw + 2 * NW * C;                               // [NBC][C]
   float* dba = dbp + NBC * C;                                  // [NBC][C]
@@ -1315,27 +1315,22 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   }
   __syncthreads();  // LDS operands and the per-wave sums of squares
   if (tid < 2 * C) {
+    // the reciprocal norm of one row of q or k, once per row
     const int x = tid / C, r = tid % C;
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) sum += nrw[(2 * v + x) * C + r];
-    nrm[tid] = sum;
+    const float rn = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sum + kL2Eps)) : 1.f;
+    nrm[tid] = rn;
+    b.crn[slot * 2 * C + tid] = rn;
   }
-  __syncthreads();  // the sums of squares
+  __syncthreads();  // the reciprocal norms
 
-  // ---- reciprocal norms; gate products (scan down the rows as in the dq/dk
-  // pass); regularity; Kt, Rk to LDS rows; Z starts as V
+  // ---- gate products (scan down the rows as in the dq/dk pass);
+  // regularity; Kt, Rk to LDS rows; Z starts as V
   f32x4 rkv[NB];
 #pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    const f32x4 sk = *reinterpret_cast<const f32x4*>(nrm + C + 16 * t + 4 * lq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rkv[t][i] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sk[i] + kL2Eps)) : 1.f;
-  }
-  if (tid < 2 * C) {
-    const float x = nrm[tid];
-    b.crn[slot * 2 * C + tid] = l2 ? __fdiv_rn(1.f, __fsqrt_rn(x + kL2Eps)) : 1.f;
-  }
+  for (int t = 0; t < NB; ++t) rkv[t] = *reinterpret_cast<const f32x4*>(nrm + C + 16 * t + 4 * lq);
   f32x4 zacc[NB];
   {
     bool ok = true;
@@ -1366,7 +1361,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         ok = ok && mf >= kRegMin && mf <= kRegMax;
         const float kh = in ? bf16_to_f32(xk[t][i]) * rkv[t][i] : 0.f;
         sKT[r * LDV + ch] = static_cast<__bf16>(kh * f);
-        sRK[r * LDV + ch] = static_cast<__bf16>(kh / f);
+        sRK[r * LDV + ch] = static_cast<__bf16>(kh * __builtin_amdgcn_rcpf(f));  // f in range below
         zacc[t][i] = in ? bf16_to_f32(xv[t][i]) : 0.f;
       }
       carry *= tot;
