@@ -487,8 +487,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
       for (int i = 0; i < 4; ++i)
         sacc[mc][i] = b.dht ? b.dht[st_base + static_cast<int64_t>(16 * mc + 4 * lq + i) * dv] : 0.f;
 
-    for (int k = 0; k < nch; ++k) {
-      const int i = nch - 1 - k;
+    for (int k = 0; k < nch; ++k) {  // chunk nch - 1 - k; the loaders store its outputs
       {  // the adjoint at the chunk's end, for the intra-chunk pass (staged;
          // the loaders store it)
         ST* ds = reinterpret_cast<ST*>(smem + Cfg::O_SS) + 16 * wave + l16;
@@ -1188,7 +1187,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   constexpr int NU = (C / 2) * (C / 4);
   constexpr int NUI = (NU + NT - 1) / NT;
   uint16_t xq[NB][4], xk[NB][4], xv[NB][4];
-  float xa[NB][4], xb[NB][4];
+  float xa[NB][4];
   uint16_t xs[NFD][8];
   uint4 xo[NIT];
   float4 xu[NIT];  // 8 bf16 values each
@@ -1198,7 +1197,6 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
     gu16* kg = (gu16*)a.k;
     gu16* vg = (gu16*)a.v;
     gf32* alpha = (gf32*)a.alpha;
-    gf32* beta = (gf32*)a.beta;
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
@@ -1209,7 +1207,6 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         xk[t][i] = kg[row * D + ch];
         xv[t][i] = vg[row * D + ch];
         xa[t][i] = alpha[row * D + ch];
-        xb[t][i] = beta[row];
       }
     gu16* S0 = (gu16*)a.hc + slot * D * D + ch;
 #pragma unroll
