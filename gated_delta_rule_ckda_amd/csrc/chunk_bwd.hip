@@ -396,25 +396,6 @@ struct BGroup {
   }
 };
 
-// One staged tile out to memory as 16-byte pieces by the loader threads: R
-// rows of ROWB bytes from LDS (row stride LD) to rows at `g` + r * gstride
-// bytes; rows >= rmax are not written.
-template <int R, int ROWB, int LD, int NLT>
-__device__ __forceinline__ void flush_rows(const unsigned char* st, unsigned char* g, int64_t gstride,
-                                           int rmax, int lt) {
-  constexpr int PPR = ROWB / 16, NP = R * PPR;
-#pragma unroll
-  for (int u = 0; u < (NP + NLT - 1) / NLT; ++u) {
-    const int pc = lt + NLT * u;
-    if (NP % NLT == 0 || pc < NP) {
-      const int r = pc / PPR, c = pc % PPR;
-      if (r < rmax)
-        *reinterpret_cast<uint4*>(g + r * gstride + 16 * c) =
-            *reinterpret_cast<const uint4*>(st + r * LD + 16 * c);
-    }
-  }
-}
-
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT, 1) void bwd_state_kernel(BwdArgs b) {
   using Op = typename Cfg::Op;

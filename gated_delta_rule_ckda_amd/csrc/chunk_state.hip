@@ -80,7 +80,11 @@ struct StateCfg {
   static constexpr int O_G = align16(O_VT + DVT * LDC * ES);     // g [DK] fp32
   static constexpr int LDO = DVT * IOES + 16;                    // O tile row stride (bytes)
   static constexpr int O_O = align16(O_G + DK * 4);              // O tile [C][DVT] (io type)
-  static constexpr int LDS_BYTES = align16(O_O + C * LDO);
+  // the state entering a chunk [DK][DVT] (io type; only when the backward's
+  // records are kept), staged for whole-row stores by the loader waves
+  static constexpr int LDH = DVT * IOES + 16;
+  static constexpr int O_HC = align16(O_O + C * LDO);
+  static constexpr int LDS_BYTES = align16(O_HC + DK * LDH);
 
   static_assert(GB_END == blk_g_byte(C, DK, ES) + 4 * DK, "block layout");
   static_assert(GB_X % 16 == 0 && GB_W % 16 == 0 && GB_P % 16 == 0 && GB_K % 16 == 0 &&
@@ -278,19 +282,14 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
   // to be live at the same time.
   if (is_state) {
     for (int i = 0; i < nch; ++i) {
-      if (a.hc) {  // the state entering chunk i, for the backward
-        // the lane's row and column through opaque moves: the addresses are
-        // formed here, not hoisted out of the loop for every stored value
-        // (which costs the plain forward spills)
-        int lqo, colo;
-        asm volatile("v_mov_b32 %0, %1" : "=v"(lqo) : "v"(lq));
-        asm volatile("v_mov_b32 %0, %1" : "=v"(colo) : "v"(dv0 + 16 * wave + l16));
-        ST* hc = static_cast<ST*>(a.hc) + (static_cast<int64_t>(h) * a.maxc + c_begin + i) * DK * a.dv +
-                 colo + static_cast<int64_t>(4 * lqo) * a.dv;
+      if (a.hc) {  // the state entering chunk i, for the backward: staged,
+                   // the loaders store it as whole rows
+        ST* hs = reinterpret_cast<ST*>(smem + Cfg::O_HC) + 16 * wave + l16;
 #pragma unroll
         for (int mc = 0; mc < NMC; ++mc)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) IO::store(hc, static_cast<int64_t>(16 * mc + ii) * a.dv, sacc[mc][ii]);
+          for (int ii = 0; ii < 4; ++ii)
+            IO::store(hs, (16 * mc + 4 * lq + ii) * (Cfg::LDH / Cfg::IOES), sacc[mc][ii]);
       }
       __syncthreads();  // group A of chunk i is in LDS
       Frag sf[Cfg::NFK];
@@ -420,6 +419,12 @@ __global__ __launch_bounds__(Cfg::NT, 1) void state_kernel(FwdArgs a) {
       gb.store(smem, 0, lt);
       issueB(gb, i + 2);
       if (i > 0 && a.o) write_o(i - 1);
+      if (a.hc)  // staged before this barrier; the next one is staged after the next
+        flush_rows<DK, DVT * Cfg::IOES, Cfg::LDH, Cfg::NLT>(
+            smem + Cfg::O_HC,
+            static_cast<unsigned char*>(a.hc) +
+                ((static_cast<int64_t>(h) * a.maxc + c_begin + i) * DK * a.dv + dv0) * Cfg::IOES,
+            static_cast<int64_t>(a.dv) * Cfg::IOES, DK, lt);
       __syncthreads();  // O(i), S(i) may start; the state waves are done with A(i)
       // unconditional (past the last chunk it rewrites the last chunk's group
       // A, which nothing reads any more): a skipped store would leave these

@@ -277,6 +277,26 @@ __device__ __forceinline__ float wave_row_sums(float (&v)[N], int lane) {
 
 // Barrier among the lanes of one wave with LDS visibility (lanes of a wave
 // exchange data through LDS between the two sides).
+// One tile staged in LDS out to memory as 16-byte pieces, by NTH threads
+// (this one is thread t): R rows of ROWB bytes from `st` (row stride LD
+// bytes) to rows at `g` + r * gstride bytes; rows >= rmax are not written.
+template <int R, int ROWB, int LD, int NTH>
+__device__ __forceinline__ void flush_rows(const unsigned char* st, unsigned char* g, int64_t gstride,
+                                           int rmax, int t) {
+  static_assert(ROWB % 16 == 0 && LD % 16 == 0, "rows in 16-byte pieces");
+  constexpr int PPR = ROWB / 16, NP = R * PPR;
+#pragma unroll
+  for (int u = 0; u < (NP + NTH - 1) / NTH; ++u) {
+    const int pc = t + NTH * u;
+    if (NP % NTH == 0 || pc < NP) {
+      const int r = pc / PPR, c = pc % PPR;
+      if (r < rmax)
+        *reinterpret_cast<uint4*>(g + r * gstride + 16 * c) =
+            *reinterpret_cast<const uint4*>(st + r * LD + 16 * c);
+    }
+  }
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
