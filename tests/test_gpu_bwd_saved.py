@@ -102,3 +102,27 @@ def test_bwd_saved_against_the_oracle():
     print("  " + " ".join("%s=%.2e" % kv for kv in errs.items()))
     for n, e in errs.items():
         assert e < 2e-2, (n, e)
+
+
+def test_training_step_split_at_full_size():
+    """The LM layer at full size (B=8, T=4096, H=16, d=128, bf16, chunk 64),
+    with 648 exact zero gates (so the transform pass's second launch and the
+    backward's token path take part): ckda_chunk_fwd_save's o, ht and
+    ckda_chunk_bwd_saved's six gradients equal ckda_chunk_fwd's and
+    ckda_chunk_bwd's bit for bit."""
+    announce("fwd_save / bwd_saved LM layer full size with zero gates")
+    c = inputs.zero_gates(inputs.lm_layer(arm="ckda"))
+    rng = np.random.default_rng(78)
+    args = (dev(c.q, "bf16"), dev(c.k, "bf16"), dev(c.v, "bf16"), dev(c.alpha), dev(c.beta))
+    dO = dev(inputs.round_bf16(rng.standard_normal(c.v.shape).astype(np.float32)), "bf16")
+    dht = dev(rng.standard_normal((8, 16, 128, 128)).astype(np.float32))
+    o1, ht1 = ck.chunk_fwd(*args, chunk_size=64)
+    o2, ht2, saved = ck.chunk_fwd_save(*args, chunk_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    del o1, ht1, o2, ht2
+    g1 = ck.chunk_bwd(*args, dO, dht=dht, chunk_size=64)
+    g2 = ck.chunk_bwd(*args, dO, dht=dht, chunk_size=64, saved=saved)
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, g1, g2):
+        assert torch.equal(x, y), n
