@@ -28,11 +28,14 @@
 //
 // Launches (all on the caller's stream):
 //   1. the forward's two passes, also recording X (fp32) and every chunk's
-//      entry state, and writing no output
+//      entry state, and writing no output (skipped when the caller kept
+//      these records from a forward of its own)
 //   2. bwd_state_kernel: per (sequence, head, dv tile), chunks in reverse:
 //      dU and dS1 of every chunk to the workspace, dv, dh0
-//   3. bwd_intra_kernel: per (chunk, head), the ratio form: dq, dk, dalpha,
-//      dbeta; flags chunks it cannot take
+//   3. per (chunk, head), the ratio form: dq, dk, dalpha, dbeta; flags the
+//      chunks it cannot take.  bf16 inputs: bwd_chunk_kernel on the matrix
+//      cores (a dP/dG part, then a dq/dk part on what the first left in
+//      LDS); fp32 inputs: bwd_intra_kernel
 //   4. bwd_token_kernel: the flagged chunks, token by token
 // All arithmetic is fp32 (gradients are fp32 buffers); the forward's blocks
 // are read in their storage type.
@@ -689,7 +692,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_intra_kernel(BwdArgs b) {
     }
     const int64_t t0 = g.t0;
     const int L = g.L;
-    static_assert(sizeof(ST) == 4, "fp32 inputs only (bf16 inputs take bwd_dpg_kernel and bwd_dqk_kernel)");
+    static_assert(sizeof(ST) == 4, "fp32 inputs only (bf16 inputs take bwd_chunk_kernel)");
     const float* S0 = static_cast<const float*>(a.hc) + slot * dk * dv;
     const float* dS1 = static_cast<const float*>(b.dS) + slot * dk * dv;
     const float* dU = static_cast<const float*>(b.dU) + slot * C * dv;
@@ -1086,9 +1089,10 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float4 x, float4 y) {
 //   dbeta_j = sum_r X_rj dY_rj,  dX = tril(dY) Diag(beta)
 //   T  = dX X^T,  dA = -X^T T (strictly lower),  dbeta_r += sum_j dA_rj G_rj
 //   dG = Diag(beta) dA
-// Out: dP, dG and U for the dq/dk pass, the row norms, dbeta, and the chunk
-// flag (chunks whose gate products leave [2^-100, 2^10] go to the token-level
-// kernel).
+// Out: dbeta and the chunk flag (chunks whose gate products leave
+// [2^-100, 2^10] go to the token-level kernel) to memory; dP, dG, their
+// transposes, U, dO and the reciprocal row norms left in LDS for the dq/dk
+// part.
 template <int C_, int D_>
 struct PCfg {
   static constexpr int C = C_, D = D_;
@@ -1120,8 +1124,13 @@ struct PCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
+// The dq/dk part follows in the same workgroup, so dP, dG, U and the row
+// norms stay in LDS (in the dq/dk part's layout, in regions this part is
+// done with) instead of going through memory.  Returns whether the chunk
+// goes on to the dq/dk part (false: an unused slot, or left to the
+// token-level kernel).
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
+__device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
   using Op = OpBF16;
   using Frag = Op::Frag;
   constexpr int C = Cfg::C, D = Cfg::D, NB = Cfg::NB, NW = Cfg::NW, NT = Cfg::NT, NBC = Cfg::NBC;
@@ -1134,7 +1143,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   const Geo g = geo_of(a, c);
   if (g.n < 0) {
     if (tid == 0) b.bflag[slot] = 0;
-    return;
+    return false;
   }
   const int64_t t0 = g.t0;
   const int L = g.L;
@@ -1300,7 +1309,6 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
     for (int v = 0; v < NW; ++v) sum += nrw[(2 * v + x) * C + r];
     const float rn = l2 ? __fdiv_rn(1.f, __fsqrt_rn(sum + kL2Eps)) : 1.f;
     nrm[tid] = rn;
-    b.crn[slot * 2 * C + tid] = rn;
   }
   __syncthreads();  // the reciprocal norms
 
@@ -1349,7 +1357,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   __syncthreads();  // Kt, Rk rows; the flag
   if (*flag != 0) {
     if (tid == 0) b.bflag[slot] = 1;
-    return;
+    return false;
   }
   if (tid == 0) b.bflag[slot] = 0;
 
@@ -1378,15 +1386,13 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         if (Cfg::lo_live(t, s)) Op::mma(uacc[t], Op::row_frag<C>(sY + (16 * t + l16) * LDC, s, lq), zf[s]);
     }
   }
-  // U to memory and, with Z, to LDS rows (bf16)
+  // Z and U to LDS rows (bf16)
   {
-    uint16_t* uo = b.cU + slot * C * D + ch;
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * t + 4 * lq + i;
-        uo[r * D] = bf16_bits(uacc[t][i]);
         sZ[r * LDV + ch] = static_cast<__bf16>(zacc[t][i]);
         sU[r * LDV + ch] = static_cast<__bf16>(uacc[t][i]);
       }
@@ -1408,6 +1414,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
   const float scale = a.scale;
   gf32* Xg = (gf32*)(a.xout + slot * C * C);
   const float* beta = static_cast<const float*>(a.beta);
+  float dpk[Cfg::NTL][4], dgk[Cfg::NTL][4];  // this wave's dP, dG tiles, to LDS at the end
 #pragma unroll
   for (int k = 0; k < Cfg::NTL; ++k) {
     const int q = w + NW * k;
@@ -1422,13 +1429,12 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) xr[i] = Xg[(16 * tr + 4 * lq + i) * C + j];
       float colsum = 0.f;
-      uint16_t* po = b.cdP + slot * C * C;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * tr + 4 * lq + i;
         const bool low = j <= r;
         colsum += xr[i] * dy[i];
-        po[r * C + j] = low ? bf16_bits(scale * dp[i]) : 0;
+        dpk[k][i] = low ? scale * dp[i] : 0.f;
         sDX[r * LDC + j] = static_cast<__bf16>(low && j < L ? dy[i] * bj : 0.f);
       }
       colsum += __shfl_xor(colsum, 16);
@@ -1436,13 +1442,10 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
       if (lq == 0) dbp[tr * C + j] = colsum;
     }
   }
-  // the upper tiles: dP and dX zero
+  // the upper tiles of dX: zero
   for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, j = e % C;
-    if (j / 16 > r / 16) {
-      b.cdP[slot * C * C + e] = 0;
-      sDX[r * LDC + j] = static_cast<__bf16>(0.f);
-    }
+    if (j / 16 > r / 16) sDX[r * LDC + j] = static_cast<__bf16>(0.f);
   }
   __syncthreads();  // dX rows
 
@@ -1469,7 +1472,6 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
       f32x4 da = {0.f, 0.f, 0.f, 0.f};
       Op::mmaK<C>(da, sXT + 16 * tr * LDC, LDC, sTT + 16 * tc * LDC, LDC, lane);
       const int j = 16 * tc + l16;
-      uint16_t* go = b.cdG + slot * C * C;
       float rs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1477,7 +1479,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
         const float v = j < r ? -da[i] : 0.f;
         rs[i] = v * gacc[k][i];
         const float br = beta[(t0 + (r < L ? r : L - 1)) * H + h];
-        go[r * C + j] = r < L ? bf16_bits(v * br) : 0;
+        dgk[k][i] = r < L ? v * br : 0.f;
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1)
@@ -1487,10 +1489,6 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dba[tc * C + 16 * tr + 4 * lq + i] = rs[i];
     }
-  }
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, j = e % C;
-    if (j / 16 > r / 16) b.cdG[slot * C * C + e] = 0;
   }
   __syncthreads();  // dbeta parts
   if (tid < L) {
@@ -1502,11 +1500,52 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dpg_kernel(BwdArgs b) {
     for (int u = 0; u < NBC; ++u) db += dba[u * C + tid];
     b.dbeta[(t0 + tid) * H + h] = db;
   }
+  {
+    // dP and dG for the dq/dk part, as rows (permuted column order) and as
+    // transposed rows, in the regions of Y, X, X^T and dU (none read any
+    // more): the lower tiles from this wave's registers, zeros elsewhere
+    uint16_t* hP = reinterpret_cast<uint16_t*>(smem + Cfg::O_Y);
+    uint16_t* hPT = reinterpret_cast<uint16_t*>(smem + Cfg::O_X);
+    uint16_t* hG = reinterpret_cast<uint16_t*>(smem + Cfg::O_XT);
+    uint16_t* hGT = reinterpret_cast<uint16_t*>(smem + Cfg::O_DU);
+#pragma unroll
+    for (int k = 0; k < Cfg::NTL; ++k) {
+      const int q = w + NW * k;
+      if (q < Cfg::NL) {
+        const int tr = Cfg::ltr(q), tc = Cfg::ltc(q);
+        const int j = 16 * tc + l16, qj = Op::pos<C>(j), qr = Op::pos<C>(16 * tr + 4 * lq);
+        uint16_t pb[4], gb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * tr + 4 * lq + i;
+          pb[i] = bf16_bits(dpk[k][i]);
+          gb[i] = bf16_bits(dgk[k][i]);
+          hP[r * LDC + qj] = pb[i];
+          hG[r * LDC + qj] = gb[i];
+        }
+        // rows 16tr + 4lq .. + 3 are adjacent in the permuted order
+        *reinterpret_cast<uint2*>(hPT + j * LDC + qr) =
+            make_uint2(pb[0] | (static_cast<uint32_t>(pb[1]) << 16), pb[2] | (static_cast<uint32_t>(pb[3]) << 16));
+        *reinterpret_cast<uint2*>(hGT + j * LDC + qr) =
+            make_uint2(gb[0] | (static_cast<uint32_t>(gb[1]) << 16), gb[2] | (static_cast<uint32_t>(gb[3]) << 16));
+      }
+    }
+    for (int e = tid; e < C * C; e += NT) {
+      const int r = e / C, j = e % C;
+      if (j / 16 > r / 16) {  // above the diagonal tiles: zero, and below them in the transposes
+        hP[r * LDC + Op::pos<C>(j)] = 0;
+        hG[r * LDC + Op::pos<C>(j)] = 0;
+        hPT[j * LDC + Op::pos<C>(r)] = 0;
+        hGT[j * LDC + Op::pos<C>(r)] = 0;
+      }
+    }
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------- 3b: dq, dk
-// bf16 inputs: dq, dk and dalpha of the chunks the intra-chunk pass kept, on
-// the matrix cores.  One workgroup per (chunk, head); wave w owns the 16
+// bf16 inputs: dq, dk and dalpha of the chunks the dP/dG part kept, on the
+// matrix cores, in the same workgroup right after it.  Wave w owns the 16
 // channels 16w .. 16w + 15, and lane (l16, lq) holds rows 16t + 4lq + i of
 // channel 16w + l16 (the layout of an MFMA result tile), so every
 // per-channel quantity (the gate products F, Kt, Qt, Rk, the reverse sums of
@@ -1530,87 +1569,81 @@ struct QCfg {
   static constexpr int NW = DK / 16, NT = 64 * NW, NB = C / 16;
   static constexpr int LDV = frag_stride(DV, 2), LDC = frag_stride(C, 2);
   static constexpr int NFV = DV / 32, NFC = (C + 31) / 32;
-  static constexpr int O_DO = 0;                                 // dO [C][LDV]
-  static constexpr int O_DV = align16(O_DO + C * LDV * 2);       // dV [C][LDV]
-  static constexpr int O_U = align16(O_DV + C * LDV * 2);        // U  [C][LDV]
-  // dP, dP^T, dG, dG^T as [C][LDC] (permuted order)
-  static constexpr int MCC = align16(C * LDC * 2);
-  static constexpr int O_CC = align16(O_U + C * LDV * 2);
-  static constexpr int O_P = O_CC, O_PT = O_CC + MCC, O_G = O_CC + 2 * MCC, O_GT = O_CC + 3 * MCC;
-  static constexpr int O_RED = O_CC + 4 * MCC;                   // float [2][NW][C] + [2][C] row sums
-  static constexpr int LDS_BYTES = align16(O_RED + 2 * (NW + 1) * C * 4);
   // dP, dG lower: K fragment s of row tile t is live if it starts at or left
   // of the tile's last row; their transposes are upper
   static constexpr bool lo_live(int t, int s) { return 32 * s <= 16 * t + 15; }
   static constexpr bool up_live(int t, int s) { return 32 * s + 31 >= 16 * t; }
   static_assert(DV % 32 == 0 && C % 16 == 0, "shapes");
+};
+
+// Where the dq/dk part finds its LDS operands, in the dP/dG part's regions:
+// dO and U are already there, dP, dG and their transposes were written by
+// that part, the row norms are its reciprocal norms; dV, the reductions and
+// dalpha's transposes go where nothing is read any more.
+template <class QC, class PC>
+struct QMap {
+  static constexpr int DO = PC::O_DO;
+  static constexpr int DV = PC::O_Z;
+  static constexpr int U = PC::O_U;
+  static constexpr int P = PC::O_Y;
+  static constexpr int PT = PC::O_X;
+  static constexpr int G = PC::O_XT;
+  static constexpr int GT = PC::O_DU;
+  static constexpr int RN = PC::O_RED;  // the reciprocal row norms [2][C]
+  static constexpr int RED = align16(PC::LDS_BYTES);
+  // dalpha's transposes: after the products over dv, over the Kt, Rk (dX,
+  // T^T) and dV rows
+  static constexpr int TB = PC::O_KT;
+  static constexpr int TB_END = PC::O_U;
+  static constexpr int LDS_BYTES = align16(RED + 2 * (QC::NW + 1) * QC::C * 4);
+  static_assert(QC::LDV == PC::LDV && QC::LDC == PC::LDC && QC::NT == PC::NT, "shared strides");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
+template <class Cfg, class PC>
+__device__ __forceinline__ void dqk_part(const BwdArgs& b) {
   using Op = OpBF16;
   using Frag = Op::Frag;
+  using M = QMap<Cfg, PC>;
   constexpr int C = Cfg::C, DK = Cfg::DK, DV = Cfg::DV, NB = Cfg::NB, NW = Cfg::NW, NT = Cfg::NT;
   constexpr int LDV = Cfg::LDV, LDC = Cfg::LDC, NFV = Cfg::NFV;
   const FwdArgs& a = b.f;
   const int H = a.H;
   const int c = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);
-  const Geo g = geo_of(a, c);
-  if (g.n < 0) return;
+  const Geo g = geo_of(a, c);  // a used slot, not flagged (the dP/dG part returned true)
   const int64_t slot = static_cast<int64_t>(h) * a.maxc + c;
-  if (b.bflag[slot] != 0) return;  // left to the token-level kernel
   const int64_t t0 = g.t0;
   const int L = g.L;
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* sdO = reinterpret_cast<__bf16*>(smem + Cfg::O_DO);
-  __bf16* sdV = reinterpret_cast<__bf16*>(smem + Cfg::O_DV);
-  __bf16* sU = reinterpret_cast<__bf16*>(smem + Cfg::O_U);
-  __bf16* sP = reinterpret_cast<__bf16*>(smem + Cfg::O_P);
-  __bf16* sPT = reinterpret_cast<__bf16*>(smem + Cfg::O_PT);
-  __bf16* sG = reinterpret_cast<__bf16*>(smem + Cfg::O_G);
-  __bf16* sGT = reinterpret_cast<__bf16*>(smem + Cfg::O_GT);
-  float* red = reinterpret_cast<float*>(smem + Cfg::O_RED);
+  __bf16* sdO = reinterpret_cast<__bf16*>(smem + M::DO);
+  __bf16* sdV = reinterpret_cast<__bf16*>(smem + M::DV);
+  __bf16* sU = reinterpret_cast<__bf16*>(smem + M::U);
+  __bf16* sP = reinterpret_cast<__bf16*>(smem + M::P);
+  __bf16* sPT = reinterpret_cast<__bf16*>(smem + M::PT);
+  __bf16* sG = reinterpret_cast<__bf16*>(smem + M::G);
+  __bf16* sGT = reinterpret_cast<__bf16*>(smem + M::GT);
+  float* red = reinterpret_cast<float*>(smem + M::RED);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
   const int ch = 16 * w + l16;  // this lane's channel
   // global address space (plain global loads rather than flat ones)
   typedef const __attribute__((address_space(1))) uint16_t gu16;
   typedef const __attribute__((address_space(1))) float gf32;
 
-  // ---- every load of the chunk goes out first.  Rows >= L of the token
-  // arrays are read from row L - 1 (no branch around a load, so none waits
-  // for another) and replaced afterwards.
+  // ---- the loads this part adds to the dP/dG part's LDS operands go out
+  // first: dV rows, the lane's rows of S0 and dS1.  Rows >= L of dV are
+  // read from row L - 1 (no branch around a load) and replaced by zeros.
   constexpr int PR = DV / 8;                       // 8-element pieces per row of dv
   constexpr int NIT = (C * PR + NT - 1) / NT;      // pieces per thread
-  constexpr int NU = (C / 2) * (C / 4);            // dP, dG units: 4 columns of 2 rows
-  constexpr int NUI = (NU + NT - 1) / NT;
-  uint4 xo[NIT], xu[NIT];
   float4 xv[NIT][2];
-  uint2 xp[NUI][2], xg[NUI][2];
   uint4 xs[NFV], xd[NFV];
   {
-    const uint16_t* o = static_cast<const uint16_t*>(b.dout);
     const float* dvo = b.dv;
-    const uint16_t* U = b.cU + slot * C * DV;
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
       const int p = iclamp(tid + NT * u, C * PR - 1), r = p / PR, cp = p % PR;
       const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
-      xo[u] = *reinterpret_cast<const uint4*>(o + row * DV + 8 * cp);
       xv[u][0] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp);
       xv[u][1] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp + 4);
-      xu[u] = *reinterpret_cast<const uint4*>(U + r * DV + 8 * cp);
-    }
-    const uint16_t* P = b.cdP + slot * C * C;
-    const uint16_t* G = b.cdG + slot * C * C;
-#pragma unroll
-    for (int u = 0; u < NUI; ++u) {
-      const int uu = iclamp(tid + NT * u, NU - 1);
-      const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
-      xp[u][0] = *reinterpret_cast<const uint2*>(P + r * C + j0);
-      xp[u][1] = *reinterpret_cast<const uint2*>(P + (r + 1) * C + j0);
-      xg[u][0] = *reinterpret_cast<const uint2*>(G + r * C + j0);
-      xg[u][1] = *reinterpret_cast<const uint2*>(G + (r + 1) * C + j0);
     }
     const uint16_t* S0 = static_cast<const uint16_t*>(a.hc) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
     const uint16_t* D1 = static_cast<const uint16_t*>(b.dS) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
@@ -1620,41 +1653,14 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
       xd[s] = *reinterpret_cast<const uint4*>(D1 + 32 * s);
     }
   }
-  // chunk-wide operands to LDS as bf16 (rows >= L of dO and dV as zeros)
+  // dV to LDS as bf16 (rows >= L as zeros)
 #pragma unroll
   for (int u = 0; u < NIT; ++u) {
     const int p = tid + NT * u, r = p / PR, cp = p % PR;
     if ((C * PR) % NT == 0 || p < C * PR) {
       const bool in = r < L;
       const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<uint4*>(sdO + r * LDV + 8 * cp) = in ? xo[u] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<bf16x8*>(sdV + r * LDV + 8 * cp) = to_bf16x8(in ? xv[u][0] : z, in ? xv[u][1] : z);
-      *reinterpret_cast<uint4*>(sU + r * LDV + 8 * cp) = xu[u];
-    }
-  }
-  // dP, dG and their transposes; rows fastest over the units, so that the
-  // transposed pair writes of consecutive lanes land in consecutive words
-#pragma unroll
-  for (int u = 0; u < NUI; ++u) {
-    const int uu = tid + NT * u;
-    if (NU % NT == 0 || uu < NU) {
-      const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
-      const int qj = Op::pos<C>(j0), qr = Op::pos<C>(r);
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        *reinterpret_cast<uint2*>(sP + (r + rr) * LDC + qj) = xp[u][rr];
-        *reinterpret_cast<uint2*>(sG + (r + rr) * LDC + qj) = xg[u][rr];
-      }
-      // element e of two rows -> one word (row r low, row r + 1 high)
-      auto pair = [](uint2 lo, uint2 hi, int e) {
-        const uint32_t a = e < 2 ? lo.x : lo.y, c = e < 2 ? hi.x : hi.y;
-        return (e & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
-      };
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint32_t*>(sPT + (j0 + e) * LDC + qr) = pair(xp[u][0], xp[u][1], e);
-        *reinterpret_cast<uint32_t*>(sGT + (j0 + e) * LDC + qr) = pair(xg[u][0], xg[u][1], e);
-      }
     }
   }
   // the lane's rows of S0 and dS1 as fragments over dv (natural order, as
@@ -1672,7 +1678,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
     d1f[s] = __builtin_bit_cast(bf16x8, xd[s]);
   }
   // the lane's q, k, alpha (in flight over the barrier and the first products)
-  const float* rn = b.crn + slot * 2 * C;
+  const float* rn = reinterpret_cast<const float*>(smem + M::RN);
   float xa[NB][4];
   uint16_t xq[NB][4], xk[NB][4];
   f32x4 nq[NB], nk[NB];
@@ -1971,8 +1977,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
   // recurrences need no carries between lanes.
   {
     constexpr int LDT = C + 4;  // floats per channel in the buffer (a 16-byte pad)
-    static_assert(NW * 16 * LDT * 4 <= Cfg::O_CC - Cfg::O_DO, "transpose buffer");
-    float* tbuf = reinterpret_cast<float*>(smem + Cfg::O_DO) + w * 16 * LDT;
+    static_assert(NW * 16 * LDT * 4 <= M::TB_END - M::TB, "transpose buffer");
+    float* tbuf = reinterpret_cast<float*>(smem + M::TB) + w * 16 * LDT;
     const bool own = lq < NB;  // with fewer than 4 tiles the other lane groups only help move data
     const int T = own ? lq : 0;
     // rows 16t + 4lq + i held by lane (l16, lq) -> rows 16T + m of this lane
@@ -2070,6 +2076,15 @@ __global__ __launch_bounds__(Cfg::NT, 1) void bwd_dqk_kernel(BwdArgs b) {
     }
   }
 
+}
+
+// Both chunk passes in one workgroup per (chunk, head): the dP/dG part,
+// then (unless the chunk is left to the token-level kernel) the dq/dk part
+// on the operands the first part left in LDS.
+template <class PC, class QC>
+__global__ __launch_bounds__(PC::NT, 1) void bwd_chunk_kernel(BwdArgs b) {
+  if (!dpg_part<PC>(b)) return;
+  dqk_part<QC, PC>(b);
 }
 
 // ---------------------------------------------------------------- 4: token
@@ -2245,29 +2260,17 @@ launch_result launch_state(const BwdArgs& b, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class Cfg>
-launch_result launch_dpg(const BwdArgs& b, hipStream_t stream) {
+template <class PC, class QC>
+launch_result launch_chunk(const BwdArgs& b, hipStream_t stream) {
+  using M = QMap<QC, PC>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&bwd_dpg_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      Cfg::LDS_BYTES);
+      reinterpret_cast<const void*>(&bwd_chunk_kernel<PC, QC>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      M::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   const int64_t items = static_cast<int64_t>(b.f.maxc) * b.f.H;
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dpg_kernel<Cfg>, dim3(static_cast<unsigned>(items)), dim3(Cfg::NT),
-                     Cfg::LDS_BYTES, stream, b);
-  return hipGetLastError();
-}
-
-template <class Cfg>
-launch_result launch_dqk(const BwdArgs& b, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&bwd_dqk_kernel<Cfg>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      Cfg::LDS_BYTES);
-  if (attr != hipSuccess) return attr;
-  const int64_t items = static_cast<int64_t>(b.f.maxc) * b.f.H;
-  if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dqk_kernel<Cfg>, dim3(static_cast<unsigned>(items)), dim3(Cfg::NT),
-                     Cfg::LDS_BYTES, stream, b);
+  hipLaunchKernelGGL((bwd_chunk_kernel<PC, QC>), dim3(static_cast<unsigned>(items)), dim3(PC::NT),
+                     M::LDS_BYTES, stream, b);
   return hipGetLastError();
 }
 
@@ -2314,21 +2317,19 @@ launch_result launch_io(const BwdArgs& b, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   hipError_t e = hipSuccess;
   if constexpr (bf) {
-    // bf16 inputs: the intra-chunk work on the matrix cores, in two passes
-    launch_result (*fp)(const BwdArgs&, hipStream_t) = nullptr;
-    launch_result (*fq)(const BwdArgs&, hipStream_t) = nullptr;
+    // bf16 inputs: the intra-chunk work on the matrix cores, both passes in
+    // one workgroup per (chunk, head)
+    launch_result (*fc)(const BwdArgs&, hipStream_t) = nullptr;
     if (dk == dv) {
-      if (C == 64 && dk == 128) fp = &launch_dpg<PCfg<64, 128>>, fq = &launch_dqk<QCfg<64, 128>>;
-      if (C == 64 && dk == 64) fp = &launch_dpg<PCfg<64, 64>>, fq = &launch_dqk<QCfg<64, 64>>;
-      if (C == 32 && dk == 128) fp = &launch_dpg<PCfg<32, 128>>, fq = &launch_dqk<QCfg<32, 128>>;
-      if (C == 32 && dk == 64) fp = &launch_dpg<PCfg<32, 64>>, fq = &launch_dqk<QCfg<32, 64>>;
-      if (C == 16 && dk == 128) fp = &launch_dpg<PCfg<16, 128>>, fq = &launch_dqk<QCfg<16, 128>>;
-      if (C == 16 && dk == 64) fp = &launch_dpg<PCfg<16, 64>>, fq = &launch_dqk<QCfg<16, 64>>;
+      if (C == 64 && dk == 128) fc = &launch_chunk<PCfg<64, 128>, QCfg<64, 128>>;
+      if (C == 64 && dk == 64) fc = &launch_chunk<PCfg<64, 64>, QCfg<64, 64>>;
+      if (C == 32 && dk == 128) fc = &launch_chunk<PCfg<32, 128>, QCfg<32, 128>>;
+      if (C == 32 && dk == 64) fc = &launch_chunk<PCfg<32, 64>, QCfg<32, 64>>;
+      if (C == 16 && dk == 128) fc = &launch_chunk<PCfg<16, 128>, QCfg<16, 128>>;
+      if (C == 16 && dk == 64) fc = &launch_chunk<PCfg<16, 64>, QCfg<16, 64>>;
     }
-    if (!fp || !fq) return hipErrorInvalidValue;
-    e = fp(b, stream);
-    if (e != hipSuccess) return e;
-    e = fq(b, stream);
+    if (!fc) return hipErrorInvalidValue;
+    e = fc(b, stream);
     if (e != hipSuccess) return e;
   } else {
     const size_t lds3 = sizeof(float) * (4 * C * C + kGStage + 4 * C + 2 * dk) + sizeof(int);
@@ -2358,8 +2359,7 @@ int64_t bwd_extra_bytes(int32_t H, int64_t maxc, int32_t C, int32_t dk, int32_t 
   const bool bf = io_dtype == CKDA_DTYPE_BF16;
   const int64_t es = bf ? 2 : 4;  // records in the io type
   const int64_t common = up(4 * hm * C * C) + 2 * up(es * hm * dk * dv) + up(es * hm * C * dv) + up(4 * hm);
-  if (bf)  // dP, dG, U (bf16) and the row norms (fp32), from the dP/dG pass to the dq/dk pass
-    return common + 2 * up(2 * hm * C * C) + up(2 * hm * C * dv) + up(4 * hm * 2 * C);
+  if (bf) return common;
   const int64_t SC = static_cast<int64_t>(C) * cmax(cmax(dk, dv), C);
   return common + up(4 * static_cast<int64_t>(bwd_grid3(hm)) * 14 * SC);  // the intra kernel's scratch
 }
@@ -2383,19 +2383,7 @@ void bwd_layout(BwdArgs& b, unsigned char* base, int32_t io_dtype) {
   base += up(4 * hm);
   b.scratch = nullptr;
   b.grid3 = bwd_grid3(hm);
-  b.cdP = b.cdG = b.cU = nullptr;
-  b.crn = nullptr;
-  if (bf) {
-    b.cdP = reinterpret_cast<uint16_t*>(base);
-    base += up(2 * hm * C * C);
-    b.cdG = reinterpret_cast<uint16_t*>(base);
-    base += up(2 * hm * C * C);
-    b.cU = reinterpret_cast<uint16_t*>(base);
-    base += up(2 * hm * C * dv);
-    b.crn = reinterpret_cast<float*>(base);
-  } else {
-    b.scratch = reinterpret_cast<float*>(base);
-  }
+  if (!bf) b.scratch = reinterpret_cast<float*>(base);  // the intra kernel's scratch
 }
 
 launch_result launch_bwd_passes(const BwdArgs& b, int32_t io_dtype, hipStream_t stream) {

@@ -143,11 +143,6 @@ struct BwdArgs {
   int32_t* bflag;    // [H][maxc] 1: chunk left to the token-level kernel
   float* scratch;    // [grid3][14][C * max(dk, dv, C)] (f32 inputs)
   int32_t grid3;
-  // handed from the dP/dG pass to the dq/dk pass (bf16 inputs; bf16 but crn)
-  uint16_t* cdP;     // [H][maxc][C][C] scale dO U^T, lower
-  uint16_t* cdG;     // [H][maxc][C][C] Diag(beta) dA, strictly lower
-  uint16_t* cU;      // [H][maxc][C][dv] the chunk's corrected values
-  float* crn;        // [H][maxc][2][C] reciprocal norms of q, k rows (fp32)
 };
 // Workspace bytes of the backward beyond the forward's, their layout from
 // `base` (sets b.f.xout and b.f.hc too), and the backward's own passes.

@@ -309,7 +309,7 @@ ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* desc, const void* q, const v
  * gradients are ckda_chunk_bwd's: the records are the same kernels' output
  * on the same inputs.
  *
- * For a layer of B=8, T=4096, H=16, d=128 in bf16, `saved` is 1.62 GB, of
+ * For a layer of B=8, T=4096, H=16, d=128 in bf16, `saved` is 1.35 GB, of
  * which the records take 0.94 GB; the backward call no longer runs the
  * forward's two passes.
  */
