@@ -2075,7 +2075,6 @@ __device__ __forceinline__ void dqk_part(const BwdArgs& b) {
       pre *= al[m];
     }
   }
-
 }
 
 // Both chunk passes in one workgroup per (chunk, head): the dP/dG part,
