@@ -80,7 +80,7 @@ def test_bwd_f32_parity(chunk, d, l2):
            l2=l2, scale=0.8)
 
 
-@pytest.mark.parametrize("chunk,d", [(64, 128), (32, 128), (64, 64), (16, 64)])
+@pytest.mark.parametrize("chunk,d", [(64, 128), (32, 128), (16, 128), (64, 64), (32, 64), (16, 64)])
 def test_bwd_bf16_parity(chunk, d):
     announce("bwd bf16 C=%d d=%d" % (chunk, d))
     _check(_grad_case(950 + chunk + d, 2, 3 * chunk + 7, 2, d, "bf16"), "bf16", chunk)
