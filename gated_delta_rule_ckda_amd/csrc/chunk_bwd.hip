@@ -1170,12 +1170,12 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
   // dbeta parts of tiles that hold none stay zero; the flag too
   for (int i = tid; i < 2 * NBC * C + 1; i += NT) dbp[i] = 0.f;
 
-  // ---- the loads go out first, in two batches (rows >= L read from row
-  // L - 1, no branch around a load; replaced afterwards): q, k, alpha and the
-  // dO, dU, X rows before the first barrier, v and the S0 columns (first
-  // needed for Z) once the rows are in LDS.  One batch of all of them would
-  // be more loads than a wave can have in flight, and its issue would stall
-  // for a whole memory latency.
+  // ---- the loads go out in three batches (rows >= L read from row L - 1,
+  // no branch around a load; replaced afterwards): q, k and the dO, dU, X
+  // rows before the first barrier; alpha and v once those rows are in LDS;
+  // the S0 columns (first needed for Z) after the norms' first barrier.  All
+  // at once they would be more loads than a wave can have in flight, and
+  // their issue would stall for a whole memory latency.
   constexpr int PR = D / 8;
   constexpr int NIT = (C * PR + NT - 1) / NT;
   constexpr int NU = (C / 2) * (C / 4);
@@ -1189,7 +1189,6 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
   {
     gu16* qg = (gu16*)a.q;
     gu16* kg = (gu16*)a.k;
-    gf32* alpha = (gf32*)a.alpha;
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
@@ -1198,7 +1197,6 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
         const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
         xq[t][i] = qg[row * D + ch];
         xk[t][i] = kg[row * D + ch];
-        xa[t][i] = alpha[row * D + ch];
       }
     const uint16_t* o = static_cast<const uint16_t*>(b.dout);
     const uint16_t* dU = static_cast<const uint16_t*>(b.dU) + slot * C * D;
@@ -1259,18 +1257,15 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
   }
   {  // the second batch of loads
     gu16* vg = (gu16*)a.v;
+    gf32* alpha = (gf32*)a.alpha;
 #pragma unroll
     for (int t = 0; t < NB; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * t + 4 * lq + i;
+        xa[t][i] = alpha[((t0 + (r < L ? r : L - 1)) * H + h) * D + ch];
         xv[t][i] = vg[((t0 + (r < L ? r : L - 1)) * H + h) * D + ch];
       }
-    gu16* S0 = (gu16*)a.hc + slot * D * D + ch;
-#pragma unroll
-    for (int s = 0; s < NFD; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xs[s][e] = S0[(32 * s + 8 * lq + e) * D];
   }
   // ---- row norms: sums of squares over the wave's channels by a butterfly
   // (lane l16 ends with value l16 >> (4 - log2 4NB)), then over the waves in
@@ -1313,6 +1308,14 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
     }
   }
   __syncthreads();  // LDS operands and the per-wave sums of squares
+  {  // the third batch of loads
+    gu16* S0 = (gu16*)a.hc + slot * D * D + ch;
+#pragma unroll
+    for (int s = 0; s < NFD; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[s][e] = S0[(32 * s + 8 * lq + e) * D];
+  }
+
   if (tid < 2 * C) {
     // the reciprocal norm of one row of q or k, once per row
     const int x = tid / C, r = tid % C;
