@@ -1093,6 +1093,39 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float4 x, float4 y) {
 // [2^-100, 2^10] go to the token-level kernel) to memory; dP, dG, their
 // transposes, U, dO and the reciprocal row norms left in LDS for the dq/dk
 // part.
+// The dq/dk part's first loads (its dV rows, the lane's rows of S0 and
+// dS1), issued by the dP/dG part during its last products so that they are
+// in flight while those run.  Rows >= L of dV are read from row L - 1 (no
+// branch around a load) and replaced by zeros when they go to LDS.
+template <class QC>
+struct QLoads {
+  static constexpr int PR = QC::DV / 8, NIT = (QC::C * PR + QC::NT - 1) / QC::NT;
+  float4 xv[NIT][2];
+  uint4 xs[QC::NFV], xd[QC::NFV];
+};
+template <class QC>
+__device__ __forceinline__ void issue_qloads(const BwdArgs& b, QLoads<QC>& ql, int64_t t0, int L, int h,
+                                             int64_t slot, int tid, int ch, int lq) {
+  constexpr int C = QC::C, DK = QC::DK, DV = QC::DV, NT = QC::NT, NFV = QC::NFV;
+  constexpr int PR = QLoads<QC>::PR, NIT = QLoads<QC>::NIT;
+  const int H = b.f.H;
+  const float* dvo = b.dv;
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int p = iclamp(tid + NT * u, C * PR - 1), r = p / PR, cp = p % PR;
+    const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
+    ql.xv[u][0] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp);
+    ql.xv[u][1] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp + 4);
+  }
+  const uint16_t* S0 = static_cast<const uint16_t*>(b.f.hc) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
+  const uint16_t* D1 = static_cast<const uint16_t*>(b.dS) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
+#pragma unroll
+  for (int s = 0; s < NFV; ++s) {
+    ql.xs[s] = *reinterpret_cast<const uint4*>(S0 + 32 * s);
+    ql.xd[s] = *reinterpret_cast<const uint4*>(D1 + 32 * s);
+  }
+}
+
 template <int C_, int D_>
 struct PCfg {
   static constexpr int C = C_, D = D_;
@@ -1129,8 +1162,8 @@ struct PCfg {
 // done with) instead of going through memory.  Returns whether the chunk
 // goes on to the dq/dk part (false: an unused slot, or left to the
 // token-level kernel).
-template <class Cfg>
-__device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
+template <class Cfg, class QC>
+__device__ __forceinline__ bool dpg_part(const BwdArgs& b, QLoads<QC>& ql) {
   using Op = OpBF16;
   using Frag = Op::Frag;
   constexpr int C = Cfg::C, D = Cfg::D, NB = Cfg::NB, NW = Cfg::NW, NT = Cfg::NT, NBC = Cfg::NBC;
@@ -1477,6 +1510,7 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b) {
     }
   }
   __syncthreads();  // T^T rows
+  issue_qloads<QC>(b, ql, t0, L, h, slot, tid, ch, lq);  // for the dq/dk part
 
   // ---- dA = -X^T T on the lower tiles (strictly lower); dbeta (A part); dG
 #pragma unroll
@@ -1616,7 +1650,7 @@ struct QMap {
 };
 
 template <class Cfg, class PC>
-__device__ __forceinline__ void dqk_part(const BwdArgs& b) {
+__device__ __forceinline__ void dqk_part(const BwdArgs& b, const QLoads<Cfg>& ql) {
   using Op = OpBF16;
   using Frag = Op::Frag;
   using M = QMap<Cfg, PC>;
@@ -1644,30 +1678,13 @@ __device__ __forceinline__ void dqk_part(const BwdArgs& b) {
   typedef const __attribute__((address_space(1))) uint16_t gu16;
   typedef const __attribute__((address_space(1))) float gf32;
 
-  // ---- the loads this part adds to the dP/dG part's LDS operands go out
-  // first: dV rows, the lane's rows of S0 and dS1.  Rows >= L of dV are
-  // read from row L - 1 (no branch around a load) and replaced by zeros.
-  constexpr int PR = DV / 8;                       // 8-element pieces per row of dv
-  constexpr int NIT = (C * PR + NT - 1) / NT;      // pieces per thread
-  float4 xv[NIT][2];
-  uint4 xs[NFV], xd[NFV];
-  {
-    const float* dvo = b.dv;
-#pragma unroll
-    for (int u = 0; u < NIT; ++u) {
-      const int p = iclamp(tid + NT * u, C * PR - 1), r = p / PR, cp = p % PR;
-      const int64_t row = (t0 + (r < L ? r : L - 1)) * H + h;
-      xv[u][0] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp);
-      xv[u][1] = *reinterpret_cast<const float4*>(dvo + row * DV + 8 * cp + 4);
-    }
-    const uint16_t* S0 = static_cast<const uint16_t*>(a.hc) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
-    const uint16_t* D1 = static_cast<const uint16_t*>(b.dS) + slot * DK * DV + static_cast<int64_t>(ch) * DV + 8 * lq;
-#pragma unroll
-    for (int s = 0; s < NFV; ++s) {
-      xs[s] = *reinterpret_cast<const uint4*>(S0 + 32 * s);
-      xd[s] = *reinterpret_cast<const uint4*>(D1 + 32 * s);
-    }
-  }
+  // ---- the loads this part adds to the dP/dG part's LDS operands (dV
+  // rows, the lane's rows of S0 and dS1) were issued by that part
+  constexpr int PR = QLoads<Cfg>::PR;              // 8-element pieces per row of dv
+  constexpr int NIT = QLoads<Cfg>::NIT;            // pieces per thread
+  const auto& xv = ql.xv;
+  const auto& xs = ql.xs;
+  const auto& xd = ql.xd;
   // dV to LDS as bf16 (rows >= L as zeros)
 #pragma unroll
   for (int u = 0; u < NIT; ++u) {
@@ -2097,8 +2114,9 @@ __device__ __forceinline__ void dqk_part(const BwdArgs& b) {
 // on the operands the first part left in LDS.
 template <class PC, class QC>
 __global__ __launch_bounds__(PC::NT, 1) void bwd_chunk_kernel(BwdArgs b) {
-  if (!dpg_part<PC>(b)) return;
-  dqk_part<QC, PC>(b);
+  QLoads<QC> ql;
+  if (!dpg_part<PC, QC>(b, ql)) return;
+  dqk_part<QC, PC>(b, ql);
 }
 
 // ---------------------------------------------------------------- 4: token
