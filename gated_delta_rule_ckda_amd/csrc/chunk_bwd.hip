@@ -52,7 +52,12 @@ constexpr int kNT = 256;
 // that the scratch they cycle through stays in the last-level caches
 constexpr int64_t kGrid3 = 512;
 
-// tokens of chunk slot c: sequence n, first token t0, length L (n < 0: unused)
+// tokens of chunk slot c: sequence n, first token t0, length L (n < 0: unused).
+// Every caller passes a c that is the same across its workgroup.  The chunk
+// map is read through generic pointers, whose loads the compiler takes as
+// per-lane, so the values are made uniform explicitly: buffer descriptors
+// formed from t0 and L then stay in scalar registers (a descriptor the
+// compiler takes as per-lane costs a loop around every store that uses it).
 struct Geo {
   int64_t t0;
   int L, n;
@@ -61,10 +66,10 @@ __device__ __forceinline__ Geo geo_of(const FwdArgs& a, int c) {
   Geo g{0, 0, -1};
   const int C = a.chunk;
   if (a.cu_seqlens) {
-    const int n = a.chunk_seq[c];
+    const int n = uniform32(a.chunk_seq[c]);
     if (n < 0) return g;
-    const int i = c - a.first[n];
-    const int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
+    const int i = c - uniform32(a.first[n]);
+    const int64_t s0 = uniform64(a.cu_seqlens[n]), s1 = uniform64(a.cu_seqlens[n + 1]);
     g.n = n;
     g.t0 = s0 + static_cast<int64_t>(i) * C;
     g.L = static_cast<int>((s1 - g.t0) < C ? (s1 - g.t0) : C);
@@ -2035,7 +2040,7 @@ __device__ __forceinline__ void dqk_part(const BwdArgs& b, const QLoads<Cfg>& ql
       float ecum = 0.f;
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
-        const float gt = (gdg + ecum + zp[tb]) * (Fa[tb] / Fe[tb]);
+        const float gt = (gdg + ecum + zp[tb]) * (Fa[tb] * __builtin_amdgcn_rcpf(Fe[tb]));
         ecum += ep[tb];
         gam = tb == T ? gt : gam;
       }
@@ -2070,7 +2075,7 @@ __device__ __forceinline__ void dqk_part(const BwdArgs& b, const QLoads<Cfg>& ql
       for (int r = 1; r < 16; ++r) {
         const __bf16* gr = sG + (16 * T + r) * LDC + tcol;
         const __bf16* pr = sP + (16 * T + r) * LDC + tcol;
-        const float is = 1.f / suf[r];
+        const float is = __builtin_amdgcn_rcpf(suf[r]);  // suf in [2^-110, 1]: a normal float
         const float kr = kt[r] * is, qr = qt[r] * is;
         float phi = 0.f;
 #pragma unroll
@@ -2096,13 +2101,16 @@ __device__ __forceinline__ void dqk_part(const BwdArgs& b, const QLoads<Cfg>& ql
 #pragma unroll
     for (int m = 14; m >= 0; --m) rt[m] += al[m + 1] * rt[m + 1];
     to_tile(kap, kt);  // k^ is no longer needed: kappa in its place
-    const rsrc_t rd = make_rsrc(b.dalpha + obase, orange);
     float pre = 1.f, pi = 0.f;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       const float x = pre * rt[m] + suf[m] * (pi + pre * gam + ps[m]);
-      if (own)  // rows >= L fall outside the buffer range and are dropped
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rd, ((16 * T + m) * H * DK + ch) * 4, 0, 0);
+      // rows >= L fall outside the buffer range and are dropped; the
+      // descriptor is formed here from uniform values, so that it stays in
+      // scalar registers
+      if (own)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), make_rsrc(b.dalpha + obase, orange),
+                                              ((16 * T + m) * H * DK + ch) * 4, 0, 0);
       pi = al[m] * pi + kt[m];
       pre *= al[m];
     }
