@@ -1205,13 +1205,14 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b, QLoads<QC>& ql) {
   const int ch = 16 * w + l16;  // this lane's channel / value column
   typedef const __attribute__((address_space(1))) uint16_t gu16;
   typedef const __attribute__((address_space(1))) float gf32;
-  // dbeta parts of tiles that hold none stay zero; the flag too
+  // dbeta parts of tiles that hold none stay zero; the flag too (nothing
+  // reads or adds to them before the norms' first barrier)
   for (int i = tid; i < 2 * NBC * C + 1; i += NT) dbp[i] = 0.f;
 
   // ---- the loads go out in three batches (rows >= L read from row L - 1,
-  // no branch around a load; replaced afterwards): q, k and the dO, dU, X
-  // rows before the first barrier; alpha and v once those rows are in LDS;
-  // the S0 columns (first needed for Z) after the norms' first barrier.  All
+  // no branch around a load; replaced afterwards): q, k, the dO, dU, X rows
+  // and beta first; alpha and v once those rows are in LDS; the S0 columns
+  // (first needed for Z) after the norms' first barrier.  All
   // at once they would be more loads than a wave can have in flight, and
   // their issue would stall for a whole memory latency.
   constexpr int PR = D / 8;
@@ -1224,6 +1225,7 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b, QLoads<QC>& ql) {
   uint4 xo[NIT];
   float4 xu[NIT];  // 8 bf16 values each
   float4 xx[NUI][2];
+  float xb[NUI][4];  // beta of the unit's 4 columns
   {
     gu16* qg = (gu16*)a.q;
     gu16* kg = (gu16*)a.k;
@@ -1253,8 +1255,14 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b, QLoads<QC>& ql) {
       xx[u][0] = *reinterpret_cast<const float4*>(X + r * C + j0);
       xx[u][1] = *reinterpret_cast<const float4*>(X + (r + 1) * C + j0);
     }
+    gf32* beta = (gf32*)a.beta;
+#pragma unroll
+    for (int u = 0; u < NUI; ++u) {
+      const int j0 = 4 * (iclamp(tid + NT * u, NU - 1) / (C / 2));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xb[u][e] = beta[(t0 + (j0 + e < L ? j0 + e : L - 1)) * H + h];
+    }
   }
-  __syncthreads();  // the LDS accumulators are zero
 
   // ---- to LDS: dU, dO rows (rows >= L of dO as zeros); X, X^T (natural
   // order) and Y = X Diag(beta) (permuted order)
@@ -1269,7 +1277,6 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b, QLoads<QC>& ql) {
     }
   }
   {
-    const float* beta = static_cast<const float*>(a.beta);
 #pragma unroll
     for (int u = 0; u < NUI; ++u) {
       const int uu = tid + NT * u;
@@ -1277,7 +1284,7 @@ __device__ __forceinline__ bool dpg_part(const BwdArgs& b, QLoads<QC>& ql) {
         const int r = 2 * (uu % (C / 2)), j0 = 4 * (uu / (C / 2));
         float bj[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bj[e] = j0 + e < L ? beta[(t0 + j0 + e) * H + h] : 0.f;
+        for (int e = 0; e < 4; ++e) bj[e] = j0 + e < L ? xb[u][e] : 0.f;
         const int qj = Op::pos<C>(j0);
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
