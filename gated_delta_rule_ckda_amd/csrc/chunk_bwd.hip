@@ -1100,13 +1100,17 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float4 x, float4 y) {
 // part.
 // The dq/dk part's first loads (its dV rows, the lane's rows of S0 and
 // dS1), issued by the dP/dG part during its last products so that they are
-// in flight while those run.  Rows >= L of dV are read from row L - 1 (no
-// branch around a load) and replaced by zeros when they go to LDS.
+// in flight while those run, and the chunk's first token and length (for a
+// packed batch, three dependent loads of the chunk map the dq/dk part need
+// not repeat).  Rows >= L of dV are read from row L - 1 (no branch around a
+// load) and replaced by zeros when they go to LDS.
 template <class QC>
 struct QLoads {
   static constexpr int PR = QC::DV / 8, NIT = (QC::C * PR + QC::NT - 1) / QC::NT;
   float4 xv[NIT][2];
   uint4 xs[QC::NFV], xd[QC::NFV];
+  int64_t t0;
+  int L;
 };
 template <class QC>
 __device__ __forceinline__ void issue_qloads(const BwdArgs& b, QLoads<QC>& ql, int64_t t0, int L, int h,
@@ -1114,6 +1118,8 @@ __device__ __forceinline__ void issue_qloads(const BwdArgs& b, QLoads<QC>& ql, i
   constexpr int C = QC::C, DK = QC::DK, DV = QC::DV, NT = QC::NT, NFV = QC::NFV;
   constexpr int PR = QLoads<QC>::PR, NIT = QLoads<QC>::NIT;
   const int H = b.f.H;
+  ql.t0 = t0;
+  ql.L = L;
   const float* dvo = b.dv;
 #pragma unroll
   for (int u = 0; u < NIT; ++u) {
@@ -1671,10 +1677,10 @@ __device__ __forceinline__ void dqk_part(const BwdArgs& b, const QLoads<Cfg>& ql
   const FwdArgs& a = b.f;
   const int H = a.H;
   const int c = static_cast<int>(blockIdx.x / H), h = static_cast<int>(blockIdx.x % H);
-  const Geo g = geo_of(a, c);  // a used slot, not flagged (the dP/dG part returned true)
+  // a used slot, not flagged (the dP/dG part returned true)
   const int64_t slot = static_cast<int64_t>(h) * a.maxc + c;
-  const int64_t t0 = g.t0;
-  const int L = g.L;
+  const int64_t t0 = ql.t0;
+  const int L = ql.L;
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* sdO = reinterpret_cast<__bf16*>(smem + M::DO);
   __bf16* sdV = reinterpret_cast<__bf16*>(smem + M::DV);
