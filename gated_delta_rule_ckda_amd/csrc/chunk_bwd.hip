@@ -52,7 +52,7 @@ constexpr int kNT = 256;
 // that the scratch they cycle through stays in the last-level caches
 constexpr int64_t kGrid3 = 512;
 
-// tokens of chunk slot c: sequence n, first token t0, length L (n < 0: unused).
+// tokens of chunk slot c: first token t0, length L (n < 0: unused slot).
 // Every caller passes a c that is the same across its workgroup.  The chunk
 // map is read through generic pointers, whose loads the compiler takes as
 // per-lane, so the values are made uniform explicitly: buffer descriptors
@@ -60,19 +60,18 @@ constexpr int64_t kGrid3 = 512;
 // compiler takes as per-lane costs a loop around every store that uses it).
 struct Geo {
   int64_t t0;
-  int L, n;
+  int L, n;  // n: 0 for a used slot, -1 for an unused one
 };
 __device__ __forceinline__ Geo geo_of(const FwdArgs& a, int c) {
   Geo g{0, 0, -1};
   const int C = a.chunk;
   if (a.cu_seqlens) {
-    const int n = uniform32(a.chunk_seq[c]);
-    if (n < 0) return g;
-    const int i = c - uniform32(a.first[n]);
-    const int64_t s0 = uniform64(a.cu_seqlens[n]), s1 = uniform64(a.cu_seqlens[n + 1]);
-    g.n = n;
-    g.t0 = s0 + static_cast<int64_t>(i) * C;
-    g.L = static_cast<int>((s1 - g.t0) < C ? (s1 - g.t0) : C);
+    const int2 gc = a.chunk_geo[c];  // one load: the chunk's first token and length
+    const int L = uniform32(gc.y);
+    if (L == 0) return g;
+    g.n = 0;
+    g.t0 = uniform32(gc.x);
+    g.L = L;
   } else {
     const int n = c / a.nc, i = c % a.nc;
     g.n = n;

@@ -498,15 +498,13 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   int64_t t0;
   int L;
   if (a.cu_seqlens) {
-    const int n = uniform32(a.chunk_seq[c]);
-    if (n < 0) {  // unused chunk slot
+    const int2 gc = a.chunk_geo[c];  // one load: the chunk's first token and length
+    L = uniform32(gc.y);
+    if (L == 0) {  // unused chunk slot
       if (MODE == kFlagRegular && tid == 0) a.irregular[h * a.maxc + c] = kFlagRegular;
       return;
     }
-    const int i = c - uniform32(a.first[n]);
-    const int64_t s0 = a.cu_seqlens[n], s1 = a.cu_seqlens[n + 1];
-    t0 = uniform64(s0 + static_cast<int64_t>(i) * C);
-    L = uniform32(static_cast<int>((s1 - t0) < C ? (s1 - t0) : C));
+    t0 = uniform32(gc.x);
   } else {
     const int n = c / a.nc, i = c % a.nc;
     t0 = static_cast<int64_t>(n) * a.T + static_cast<int64_t>(i) * C;
@@ -1167,7 +1165,8 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2))) vo
 // block-wide scan per 1024 sequences.
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* cu, int32_t N, int32_t C,
                                                          int32_t maxc, int32_t* first,
-                                                         int32_t* chunk_seq, int32_t* seq_order) {
+                                                         int32_t* chunk_seq, int32_t* seq_order,
+                                                         int2* geo) {
   __shared__ int32_t part[1024];
   __shared__ int32_t carry_s;
   const int tid = threadIdx.x;
@@ -1208,6 +1207,12 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* cu, int3
       owner = lo;
     }
     chunk_seq[c] = owner;
+    int2 gc = make_int2(0, 0);
+    if (owner >= 0) {
+      gc.x = cu[owner] + (c - first[owner]) * C;
+      gc.y = cu[owner + 1] - gc.x < C ? cu[owner + 1] - gc.x : C;
+    }
+    geo[c] = gc;
   }
   // sequences by chunk count, most first (ties by index): rank of n among
   // all sequences.  Past kOrderMax sequences the quadratic ranking is not
@@ -1305,7 +1310,7 @@ launch_result launch_prep(const FwdArgs& a, int32_t io_dtype, hipStream_t stream
 
 launch_result launch_chunk_map(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.num_seqs,
-                     a.chunk, a.maxc, a.first, a.chunk_seq, a.seq_order);
+                     a.chunk, a.maxc, a.first, a.chunk_seq, a.seq_order, a.chunk_geo);
   return hipGetLastError();
 }
 

@@ -86,6 +86,7 @@ struct FwdArgs {
   int32_t* first;         // [num_seqs + 1] first chunk of each sequence (packed batches)
   int32_t* chunk_seq;     // [maxc] sequence owning each chunk slot, -1 if unused (packed)
   int32_t* seq_order;     // [num_seqs] packed sequences by chunk count, most first (state pass)
+  int2* chunk_geo;        // [maxc] first token and length of each chunk slot, length 0 if unused (packed)
   int32_t* irregular;     // [H][maxc] 1 where the transform pass left a chunk to its second launch
   int32_t maxc;           // chunk slots per head
   int32_t nc;             // chunks per sequence (dense batches)

@@ -100,7 +100,8 @@ def test_fwd_cu_seqlens_needs_batch_one():
 def test_workspace_size_formula():
     """One block per (head, chunk): (2C^2 + 3C dk) elements + dk floats, rounded up to
     256 bytes, plus one int32 flag per (head, chunk) slot; dense batches have
-    B*ceil(T/C) chunks, packed ones ceil(T/C) + N slots plus the chunk map."""
+    B*ceil(T/C) chunks, packed ones ceil(T/C) + N slots plus the chunk map
+    (an int32 pair per slot, first[N+1], the owner per slot, the order[N])."""
     up = lambda x: -(-x // 256) * 256
     d = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8)
     blk = (2 * 64 * 64 + 3 * 64 * 128) * 2 + 128 * 4
@@ -109,8 +110,12 @@ def test_workspace_size_formula():
     d = _desc(B=1, T=70, H=3, dk=32, dv=32, num_seqs=4, chunk_size=16, io_dtype=ck.F32)
     blk = up((2 * 16 * 16 + 3 * 16 * 32) * 4 + 32 * 4)
     maxc = -(-70 // 16) + 4
-    assert ck.chunk_fwd_workspace_size(d, True) == (up(4 * (4 + 1 + maxc)) + up(4 * 3 * maxc)
-                                                   + 3 * maxc * blk)
+    assert ck.chunk_fwd_workspace_size(d, True) == (up(8 * maxc + 4 * (2 * 4 + 1 + maxc))
+                                                   + up(4 * 3 * maxc) + 3 * maxc * blk)
+    d = _desc(B=1, T=70000, H=3, dk=32, dv=32, num_seqs=100, chunk_size=16, io_dtype=ck.F32)
+    maxc = -(-70000 // 16) + 100
+    assert ck.chunk_fwd_workspace_size(d, True) == (up(8 * maxc + 4 * (2 * 100 + 1 + maxc))
+                                                   + up(4 * 3 * maxc) + 3 * maxc * blk)
     # sign absorption adds two sign masks and the absorbed q, k, |alpha|, beta
     d0 = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8)
     d1 = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8, sign_absorb=1)
