@@ -34,7 +34,9 @@
  *  - Layouts are row-major and contiguous (last index fastest).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *    default stream).  The library never synchronises the host and never
- *    reads device memory on the host.
+ *    reads device memory on the host.  It enqueues kernel launches only (no
+ *    memsets, copies or allocations), so a call made once outside a capture
+ *    (one-time set-up) can then be captured into a HIP graph and replayed.
  *  - All argument validation happens on the host before any HIP call; a
  *    non-OK status means nothing was enqueued.  A failed launch returns
  *    CKDA_ERR_HIP.  Nothing crosses the ABI as an exception.
