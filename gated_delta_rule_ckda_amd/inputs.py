@@ -326,3 +326,41 @@ def decode_token(step, seed=1004, N=256, H=32, d=128, dtype="bf16"):
     a = rng.uniform(-1, 1, (N, H, d)).astype(np.float32)
     b = rng.uniform(0, 2, (N, H)).astype(np.float32)
     return q, k, v, a, b
+
+
+def device_lm_like(seed, B, T, H, d, h0_std=0.02, device="cuda:0"):
+    """A dense bf16 case too large to draw on the host in reasonable time,
+    drawn on the device with torch's seeded generator in the order q, k, v,
+    alpha, beta, h0: q, k, v ~ N(0,1) rounded to bfloat16 (nearest even),
+    alpha = tanh(N(2,1)) and beta = 2 sigmoid(N(0,1)) in float32 (the LM
+    layer's CKDA-range laws), h0 ~ N(0, h0_std^2).  Returns a dict of device
+    tensors q, k, v [B,T,H,d], alpha [B,T,H,d], beta [B,T,H], h0 [B,H,d,d];
+    the caller copies to the host the slices it checks."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+
+    def n(shape):
+        return torch.randn(shape, device=device, generator=g, dtype=torch.float32)
+
+    out = {}
+    for name in ("q", "k", "v"):
+        out[name] = n((B, T, H, d)).to(torch.bfloat16)
+    out["alpha"] = torch.tanh(n((B, T, H, d)).add_(2.0))
+    out["beta"] = torch.sigmoid(n((B, T, H))).mul_(2.0)
+    out["h0"] = n((B, H, d, d)).mul_(h0_std)
+    return out
+
+
+def device_decode(seed, N, H, d, device="cuda:0"):
+    """One decode step's inputs and state, drawn on the device with torch's
+    seeded generator (order: state, q, k, v, alpha, beta): state ~ N(0, 0.02^2)
+    float32 [N,H,d,d], q, k, v ~ N(0,1) rounded to bfloat16 [N,H,d],
+    alpha ~ U[-1,1] [N,H,d], beta ~ U[0,2] [N,H]."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = {"state": torch.randn((N, H, d, d), device=device, generator=g).mul_(0.02)}
+    for name in ("q", "k", "v"):
+        out[name] = torch.randn((N, H, d), device=device, generator=g).to(torch.bfloat16)
+    out["alpha"] = torch.rand((N, H, d), device=device, generator=g).mul_(2.0).sub_(1.0)
+    out["beta"] = torch.rand((N, H), device=device, generator=g).mul_(2.0)
+    return out
