@@ -328,14 +328,16 @@ def decode_token(step, seed=1004, N=256, H=32, d=128, dtype="bf16"):
     return q, k, v, a, b
 
 
-def device_lm_like(seed, B, T, H, d, h0_std=0.02, device="cuda:0"):
+def device_lm_like(seed, B, T, H, d, h0_std=0.02, device="cuda:0", grads=False):
     """A dense bf16 case too large to draw on the host in reasonable time,
     drawn on the device with torch's seeded generator in the order q, k, v,
     alpha, beta, h0: q, k, v ~ N(0,1) rounded to bfloat16 (nearest even),
     alpha = tanh(N(2,1)) and beta = 2 sigmoid(N(0,1)) in float32 (the LM
     layer's CKDA-range laws), h0 ~ N(0, h0_std^2).  Returns a dict of device
     tensors q, k, v [B,T,H,d], alpha [B,T,H,d], beta [B,T,H], h0 [B,H,d,d];
-    the caller copies to the host the slices it checks."""
+    the caller copies to the host the slices it checks.  With grads=True it
+    also draws, after those, dout ~ N(0,1) in bfloat16 [B,T,H,d] and
+    dht ~ N(0,1) float32 [B,H,d,d] for a backward call."""
     import torch
     g = torch.Generator(device=device).manual_seed(seed)
 
@@ -348,6 +350,9 @@ def device_lm_like(seed, B, T, H, d, h0_std=0.02, device="cuda:0"):
     out["alpha"] = torch.tanh(n((B, T, H, d)).add_(2.0))
     out["beta"] = torch.sigmoid(n((B, T, H))).mul_(2.0)
     out["h0"] = n((B, H, d, d)).mul_(h0_std)
+    if grads:
+        out["dout"] = n((B, T, H, d)).to(torch.bfloat16)
+        out["dht"] = n((B, H, d, d))
     return out
 
 

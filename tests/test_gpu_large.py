@@ -1,7 +1,7 @@
 """Sizes where 32-bit offsets would wrap: a long-context chunked forward
 (4 sequences of 69,632 tokens) whose workspace is above 4 GiB and whose gate
-tensor is above 2 GiB, and a decode step whose state has more than 2^31
-elements (9.7 GB).  Inputs are drawn on the device (seeded); the sampled
+tensor is above 2 GiB, a backward over 64 heads whose workspace is above
+4 GiB, and a decode step whose state has more than 2^31 elements (9.7 GB).  Inputs are drawn on the device (seeded); the sampled
 (sequence, head) pairs are copied to the host and held to the oracle: o at
 the bf16 bound, the fp32 state of the decode step at the fp32 bound."""
 import numpy as np
@@ -63,3 +63,40 @@ def test_decode_step_state_beyond_2pow31_elements():
     es = max(max_rel_err(host(st[n, h]), rs[i, 0]) for i, (n, h) in enumerate(pairs))
     print("  err o=%.3e state=%.3e" % (eo, es))
     assert eo < TOL["bf16"] and es < TOL["f32"]
+
+
+def test_chunk_bwd_beyond_4gib_workspace():
+    B, T, H, d = 2, 16384, 64, 128
+    announce("chunk bwd B=%d T=%d H=%d d=%d bf16 (workspace above 4 GiB)" % (B, T, H, d))
+    x = inputs.device_lm_like(5200, B, T, H, d, grads=True)
+    desc = ck._make_desc(x["q"], x["v"], H, d, d, 64, "ckda", True, 1.0, None, ck.GATES_F32,
+                         False)
+    need = ck.chunk_bwd_workspace_size(desc, False)
+    assert need > 4 << 30, need
+    g = ck.chunk_bwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["dout"], h0=x["h0"],
+                     dht=x["dht"], chunk_size=64)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (1, 21), (0, 42), (1, 63), (1, 0), (0, 63)]
+
+    def sel(t):
+        return np.stack([host(t[n, :, h]) for n, h in pairs], 0)[:, :, None]
+
+    q, k, v, a, dO = (sel(x[n]) for n in ("q", "k", "v", "alpha", "dout"))
+    b = np.stack([host(x["beta"][n, :, h]) for n, h in pairs], 0)[:, :, None]
+    h0 = np.stack([host(x["h0"][n, h]) for n, h in pairs], 0)[:, None]
+    dht = np.stack([host(x["dht"][n, h]) for n, h in pairs], 0)[:, None]
+    r = oracle.bwd(q, k, v, a, b, dO, h0=h0, dht=dht, use_l2norm=True)
+    names = ["dq", "dk", "dv", "dalpha", "dbeta", "dh0"]
+    errs = {}
+    for j, name in enumerate(names):
+        gj = g[j]
+        if name == "dh0":
+            got = np.stack([host(gj[n, h]) for n, h in pairs], 0)[:, None]
+        elif name == "dbeta":
+            got = np.stack([host(gj[n, :, h]) for n, h in pairs], 0)[:, :, None]
+        else:
+            got = sel(gj)
+        errs[name] = max_rel_err(got, r[j])
+    print("  " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    for name, e in errs.items():
+        assert e < TOL["bf16"], (name, e)
