@@ -61,8 +61,11 @@ def fwd_bytes(B, T, H, dk, dv, io_bytes, nseq, h0, gate_bytes=4):
 
 def block_bytes(C, dk, es):
     """Bytes of one (chunk, head) block of the workspace (layout of the
-    transform pass's output, 256-byte aligned)."""
-    return -(-((2 * C * C + 3 * C * dk) * es + 4 * dk) // 256) * 256
+    transform pass's output, 256-byte aligned): X', -W, Qt', P', Kh'^T in the
+    handoff type and g in float32; at chunk 64 in bf16 the first 32 rows of
+    the lower-triangular X' and P' are stored half long (3/4 of C x C each)."""
+    tri = (C // 2) * (C // 2) + (C // 2) * C if (C == 64 and es == 2) else C * C
+    return -(-((2 * tri + 3 * C * dk) * es + 4 * dk) // 256) * 256
 
 
 def pass_bytes(B, T, H, dk, dv, C, io_bytes, nseq, h0, gate_bytes=4):

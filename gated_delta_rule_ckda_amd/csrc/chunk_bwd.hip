@@ -234,6 +234,7 @@ __device__ __forceinline__ void gemm(int M, int N, int K, float alpha, bool acc,
 // transposed row, in the order the state waves read as fragments.
 struct TSec {
   int g0, R, Kc, l0, ldd;  // R source rows of Kc elements at block byte g0 -> LDS [Kc][ldd] at byte l0
+  bool tri;                // X' or P' (packed rows when the block is packed)
 };
 
 template <class OpT, class IOT, int C_, int DK_, int DV_, int DVT_>
@@ -255,9 +256,11 @@ struct BCfg {
   // P'^T and X'^T are upper triangular: K fragment s of row block rb holds a
   // nonzero only if its last column is at or right of the block's first row
   static constexpr bool up_live(int rb, int s) { return KS * s + KS - 1 >= 16 * rb; }
-  // the block (bytes)
-  static constexpr int GB_X = 0, GB_W = C * C * ES, GB_Q = GB_W + C * DK * ES,
-                       GB_P = GB_Q + C * DK * ES, GB_K = GB_P + C * C * ES,
+  // the block (bytes); X' and P' packed when TRI (first C/2 rows half long)
+  static constexpr bool TRI = tri_packed(C, ES);
+  static constexpr int TRIB = static_cast<int>(tri_elems(C, ES)) * ES;
+  static constexpr int GB_X = 0, GB_W = TRIB, GB_Q = GB_W + C * DK * ES,
+                       GB_P = GB_Q + C * DK * ES, GB_K = GB_P + TRIB,
                        GB_G = GB_K + DK * C * ES, GB_END = GB_G + DK * 4;
   // LDS (bytes)
   static constexpr int O_PT = 0;                                  // P'^T  [C][LDC]
@@ -297,11 +300,22 @@ struct BGroup {
   static constexpr int C = Cfg::C, DK = Cfg::DK, ES = Cfg::ES, NLT = Cfg::NLT;
   static constexpr int NS = A ? 2 : 3;
   static constexpr TSec sec(int k) {
-    return A ? (k == 0 ? TSec{Cfg::GB_P, C, C, Cfg::O_PT, Cfg::LDC}
-                       : TSec{Cfg::GB_K, DK, C, Cfg::O_KH, Cfg::LDK})
-             : (k == 0   ? TSec{Cfg::GB_X, C, C, Cfg::O_YT, Cfg::LDC}
-                : k == 1 ? TSec{Cfg::GB_W, C, DK, Cfg::O_WT, Cfg::LDC}
-                         : TSec{Cfg::GB_Q, C, DK, Cfg::O_QT, Cfg::LDC});
+    return A ? (k == 0 ? TSec{Cfg::GB_P, C, C, Cfg::O_PT, Cfg::LDC, true}
+                       : TSec{Cfg::GB_K, DK, C, Cfg::O_KH, Cfg::LDK, false})
+             : (k == 0   ? TSec{Cfg::GB_X, C, C, Cfg::O_YT, Cfg::LDC, true}
+                : k == 1 ? TSec{Cfg::GB_W, C, DK, Cfg::O_WT, Cfg::LDC, false}
+                         : TSec{Cfg::GB_Q, C, DK, Cfg::O_QT, Cfg::LDC, false});
+  }
+  // unit (row pair jp, piece cp) of a packed X' or P' that is not stored
+  // (rows below C/2, pieces past the half row); its load reads the live
+  // piece cp - C/2 * ES / 16 of the same rows instead, and it is not stored
+  static constexpr int HP = C / 2 * ES / 16;
+  static __device__ __forceinline__ bool dead(const TSec& s, int jp, int cp) {
+    return Cfg::TRI && s.tri && 2 * jp < C / 2 && cp >= HP;
+  }
+  // byte offset of row r of a section
+  static __device__ __forceinline__ int row_off(const TSec& s, int r) {
+    return (Cfg::TRI && s.tri) ? static_cast<int>(tri_row(C, ES, r)) * ES : r * s.Kc * ES;
   }
   static constexpr int units(int k) { return sec(k).R / 2 * (sec(k).Kc * ES / 16); }
   static constexpr int per(int k) { return (units(k) + NLT - 1) / NLT; }
@@ -323,10 +337,10 @@ struct BGroup {
       for (int u = 0; u < per(k); ++u) {
         const TSec s = sec(k);
         const int uu = iclamp(lt + NLT * u, units(k) - 1);
-        const int jp = uu % (s.R / 2), cp = uu / (s.R / 2);
-        const int off = s.g0 + 2 * jp * s.Kc * ES + 16 * cp;
-        ldraw<16>(rb, off, d[2 * (first(k) + u)]);
-        ldraw<16>(rb, off + s.Kc * ES, d[2 * (first(k) + u) + 1]);
+        const int jp = uu % (s.R / 2), cp0 = uu / (s.R / 2);
+        const int cp = dead(s, jp, cp0) ? cp0 - HP : cp0;
+        ldraw<16>(rb, s.g0 + row_off(s, 2 * jp) + 16 * cp, d[2 * (first(k) + u)]);
+        ldraw<16>(rb, s.g0 + row_off(s, 2 * jp + 1) + 16 * cp, d[2 * (first(k) + u) + 1]);
       }
     }
     if constexpr (A) {
@@ -357,8 +371,8 @@ struct BGroup {
       for (int u = 0; u < per(k); ++u) {
         const TSec s = sec(k);
         const int uu = lt + NLT * u;
-        if (units(k) % NLT == 0 || uu < units(k)) {
-          const int jp = uu % (s.R / 2), cp = uu / (s.R / 2);
+        const int jp = uu % (s.R / 2), cp = uu / (s.R / 2);
+        if ((units(k) % NLT == 0 || uu < units(k)) && !dead(s, jp, cp)) {
           const bool sp = ES == 2 && s.Kc % 32 == 0, dp = ES == 2 && s.R % 32 == 0;
           const int q = dp ? perm32(2 * jp) : 2 * jp;
           T* dst = reinterpret_cast<T*>(smem + s.l0);

@@ -452,7 +452,10 @@ __device__ __forceinline__ void direct_ap(const void* gq, const void* gk, const 
   __syncthreads();
   // P_rj = scale rq_r rk_j <q_r . D(r<-j), k_j>, j <= r, zero above
   direct_pass<Cfg>(sgate, srow, kj, j, c0, col, [&](int r, float s) {
-    if (lead) gP[r * C + Op::template pos<C>(j)] = Op::cvt((r >= j) ? s * scale * srq[r] * rkj : 0.f);
+    constexpr int TES = static_cast<int>(sizeof(typename Cfg::T));
+    const int pj = Op::template pos<C>(j);
+    if (lead && !tri_dead(C, TES, r, pj))
+      gP[tri_row(C, TES, r) + pj] = Op::cvt((r >= j) ? s * scale * srq[r] * rkj : 0.f);
   });
 }
 
@@ -512,10 +515,11 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
   }
   T* blk = reinterpret_cast<T*>(a.blocks + (static_cast<int64_t>(h) * a.maxc + c) * a.blk_bytes);
   T* gX = blk;
-  T* gW = blk + blk_off_W(C, DK);
-  T* gQ = blk + blk_off_Q(C, DK);
-  T* gP = blk + blk_off_P(C, DK);
-  T* gK = blk + blk_off_K(C, DK);
+  constexpr int TES = static_cast<int>(sizeof(T));  // handoff element size
+  T* gW = blk + blk_off_W(C, DK, TES);
+  T* gQ = blk + blk_off_Q(C, DK, TES);
+  T* gP = blk + blk_off_P(C, DK, TES);
+  T* gK = blk + blk_off_K(C, DK, TES);
   float* gg = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(blk) + blk_g_byte(C, DK, sizeof(T)));
 
   const bool use_l2 = a.use_l2norm != 0;
@@ -849,7 +853,8 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
             y[i] = Op::cvt(o0[i]);
             y[4 + i] = Op::cvt(o1[i]);
           }
-          *reinterpret_cast<bf16x8*>(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J0 + 4 * lq)) = y;
+          const int pr = 16 * I + l16, pp = Op::template pos<C>(16 * J0 + 4 * lq);
+          if (!tri_dead(C, TES, pr, pp)) *reinterpret_cast<bf16x8*>(gP + tri_row(C, TES, pr) + pp) = y;
         }
       }
     } else {
@@ -866,13 +871,14 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
           f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_p = {0.f, 0.f, 0.f, 0.f};
           tile(acc_a, acc_p, I, J);
           a_out(acc_a, I, J);
-          Op::store4(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J + 4 * lq), p_vals(acc_p, I, J));
+          const int pr = 16 * I + l16, pp = Op::template pos<C>(16 * J + 4 * lq);
+          if (!tri_dead(C, TES, pr, pp)) Op::store4(gP + tri_row(C, TES, pr) + pp, p_vals(acc_p, I, J));
         } else if (tt < NTILE) {
           int I, J;
           lower_block(tt - NPT, J, I);  // J > I: a block above the diagonal
           J += 1;
-          Op::store4(gP + (16 * I + l16) * C + Op::template pos<C>(16 * J + 4 * lq),
-                     f32x4{0.f, 0.f, 0.f, 0.f});
+          const int pr = 16 * I + l16, pp = Op::template pos<C>(16 * J + 4 * lq);
+          if (!tri_dead(C, TES, pr, pp)) Op::store4(gP + tri_row(C, TES, pr) + pp, f32x4{0.f, 0.f, 0.f, 0.f});
         }
       }
     }
@@ -1006,7 +1012,8 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, int c, int h, unsig
       if (J <= I) xv = *reinterpret_cast<const f32x4*>(x_blk<Cfg>(smem, I, J) + (r % 16) * LDA + j % 16);
       Op::store4(sXb + r * LDC + j, xv);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(sbeta + j);
-      Op::store4(gX + r * C + Op::template pos<C>(j), xv * bv);
+      const int xp = Op::template pos<C>(j);
+      if (!tri_dead(C, TES, r, xp)) Op::store4(gX + tri_row(C, TES, r) + xp, xv * bv);
       if (a.xout)  // X itself in fp32, for the backward
         *reinterpret_cast<f32x4*>(a.xout + ((static_cast<int64_t>(h) * a.maxc + c) * C + r) * C + j) = xv;
     }

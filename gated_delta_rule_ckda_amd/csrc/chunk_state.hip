@@ -59,12 +59,14 @@ struct StateCfg {
   // nonzero only if its first column is at or left of the block's last row
   static constexpr bool tri_live(int rb, int s) { return KS * s <= 16 * rb + 15; }
 
-  // the block in global memory (bytes)
+  // the block in global memory (bytes); X' and P' packed when TRI
+  static constexpr bool TRI = tri_packed(C, ES);
+  static constexpr int TRIB = static_cast<int>(tri_elems(C, ES)) * ES;  // bytes of X' (or P')
   static constexpr int GB_X = 0;
-  static constexpr int GB_W = C * C * ES;
+  static constexpr int GB_W = TRIB;
   static constexpr int GB_Q = GB_W + C * DK * ES;
   static constexpr int GB_P = GB_Q + C * DK * ES;
-  static constexpr int GB_K = GB_P + C * C * ES;
+  static constexpr int GB_K = GB_P + TRIB;
   static constexpr int GB_G = GB_K + DK * C * ES;
   static constexpr int GB_END = GB_G + DK * 4;
   static constexpr int VPR = DVT * IOES / 16;        // 16-byte pieces per V row of the tile
@@ -96,21 +98,38 @@ struct StateCfg {
 
 // Sections of a block as the loaders copy them: global byte offset and row
 // length, LDS byte offset and row stride, and 16-byte pieces.  Every section's
-// rows are whole pieces, so a piece never straddles a row.
+// rows are whole pieces, so a piece never straddles a row.  tri: X' or P',
+// whose first C/2 rows hold half a row each when the block is packed.
 struct Sec {
   int g0, grow, l0, lrow, n;
+  bool tri;
 };
 template <class Cfg>
 struct Secs {
   static constexpr int C = Cfg::C, DK = Cfg::DK, ES = Cfg::ES;
   static constexpr Sec s[6] = {
-      {Cfg::GB_X, C * ES, Cfg::O_X, Cfg::LDC * ES, C * C * ES / 16},
-      {Cfg::GB_W, DK * ES, Cfg::O_W, Cfg::LDK * ES, C * DK * ES / 16},
-      {Cfg::GB_Q, DK * ES, Cfg::O_Q, Cfg::LDK * ES, C * DK * ES / 16},
-      {Cfg::GB_P, C * ES, Cfg::O_P, Cfg::LDC * ES, C * C * ES / 16},
-      {Cfg::GB_K, C * ES, Cfg::O_K, Cfg::LDC * ES, DK * C * ES / 16},
-      {Cfg::GB_G, DK * 4, Cfg::O_G, DK * 4, DK * 4 / 16},
+      {Cfg::GB_X, C * ES, Cfg::O_X, Cfg::LDC * ES, Cfg::TRIB / 16, true},
+      {Cfg::GB_W, DK * ES, Cfg::O_W, Cfg::LDK * ES, C * DK * ES / 16, false},
+      {Cfg::GB_Q, DK * ES, Cfg::O_Q, Cfg::LDK * ES, C * DK * ES / 16, false},
+      {Cfg::GB_P, C * ES, Cfg::O_P, Cfg::LDC * ES, Cfg::TRIB / 16, true},
+      {Cfg::GB_K, C * ES, Cfg::O_K, Cfg::LDC * ES, DK * C * ES / 16, false},
+      {Cfg::GB_G, DK * 4, Cfg::O_G, DK * 4, DK * 4 / 16, false},
   };
+  // LDS byte offset of piece p of section k (the packed rows of X' and P'
+  // first: C/2 rows of C/2 elements, then C/2 rows of C)
+  static __device__ __forceinline__ int lds_of(int k, int p) {
+    int row, col;
+    if (Cfg::TRI && s[k].tri) {
+      constexpr int HP = C / 2 * ES / 16;  // pieces of a half row
+      constexpr int NH = C / 2 * HP;       // pieces of the packed rows
+      row = p < NH ? p / HP : C / 2 + (p - NH) / (2 * HP);
+      col = 16 * (p < NH ? p % HP : (p - NH) % (2 * HP));
+    } else {
+      row = 16 * p / s[k].grow;
+      col = 16 * p % s[k].grow;
+    }
+    return s[k].l0 + row * s[k].lrow + col;
+  }
   // loads per loader thread for section k
   static constexpr int per(int k) { return (s[k].n + Cfg::NLT - 1) / Cfg::NLT; }
   static constexpr int NV = (Cfg::NVU + Cfg::NLT - 1) / Cfg::NLT;  // V units per thread
@@ -171,8 +190,7 @@ struct Group {
       for (int u = 0; u < S::per(k); ++u) {
         const int p = lt + Cfg::NLT * u;
         if (S::s[k].n % Cfg::NLT == 0 || p < S::s[k].n) {
-          const int b = 16 * p;
-          const int dst = S::s[k].l0 + (b / S::s[k].grow) * S::s[k].lrow + b % S::s[k].grow;
+          const int dst = S::lds_of(k, p);
           const uint32_t* q = d[first(k) + u];
           *reinterpret_cast<uint4*>(smem + dst) = make_uint4(q[0], q[1], q[2], q[3]);
         }

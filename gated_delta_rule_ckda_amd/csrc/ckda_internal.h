@@ -46,19 +46,37 @@ launch_result launch_l2norm_debug(const void* x, float* y, int64_t rows,
 //
 // Block layout (elements of the handoff type: bf16 for bf16 io, f32 for f32
 // io; C = chunk size):
-//   X'   [C][C]   X Diag(beta),  X = (I + A)^{-1}
+//   X'   [C][C]   X Diag(beta),  X = (I + A)^{-1}          (lower triangular)
 //   -W   [C][dk]  -X Diag(beta) Kt
 //   Qt'  [C][dk]  scale rq . Qt
 //   P'   [C][C]   scale Diag(rq) P Diag(rk)   (zero above the diagonal)
 //   Kh'^T [dk][C] (Diag(rk) Kh)^T
 //   g    [dk]     float32, the chunk's total gate product
+// X' and P' are packed when tri_packed(C, es) (bf16 at C = 64): their first
+// C/2 rows, zero past column C/2 - 1, keep only their first C/2 stored
+// elements (in the perm32 storage order logical columns 0..31 are the first
+// 32 positions of a row), so each of the two matrices takes 3/4 of C x C and
+// every 128-byte line of it is written whole.  tri_row(r) is the element
+// offset of row r inside either matrix.
 // Blocks are 256-byte aligned; block (h, c) starts at (h * maxc + c) * blk_bytes.
-__host__ __device__ constexpr int64_t blk_off_W(int C, int dk) { return int64_t(C) * C + 0 * dk; }
-__host__ __device__ constexpr int64_t blk_off_Q(int C, int dk) { return int64_t(C) * C + int64_t(C) * dk; }
-__host__ __device__ constexpr int64_t blk_off_P(int C, int dk) { return int64_t(C) * C + 2 * int64_t(C) * dk; }
-__host__ __device__ constexpr int64_t blk_off_K(int C, int dk) { return 2 * int64_t(C) * C + 2 * int64_t(C) * dk; }
+__host__ __device__ constexpr bool tri_packed(int C, int es) { return C == 64 && es == 2; }
+__host__ __device__ constexpr int64_t tri_elems(int C, int es) {
+  return tri_packed(C, es) ? int64_t(C / 2) * (C / 2) + int64_t(C / 2) * C : int64_t(C) * C;
+}
+__host__ __device__ constexpr int64_t tri_row(int C, int es, int r) {
+  return !tri_packed(C, es) ? int64_t(r) * C
+         : (r < C / 2 ? int64_t(r) * (C / 2) : int64_t(C / 2) * (C / 2) + int64_t(r - C / 2) * C);
+}
+// element (r, stored position p) of a packed matrix is not stored
+__host__ __device__ constexpr bool tri_dead(int C, int es, int r, int p) {
+  return tri_packed(C, es) && r < C / 2 && p >= C / 2;
+}
+__host__ __device__ constexpr int64_t blk_off_W(int C, int dk, int es) { return tri_elems(C, es); }
+__host__ __device__ constexpr int64_t blk_off_Q(int C, int dk, int es) { return tri_elems(C, es) + int64_t(C) * dk; }
+__host__ __device__ constexpr int64_t blk_off_P(int C, int dk, int es) { return tri_elems(C, es) + 2 * int64_t(C) * dk; }
+__host__ __device__ constexpr int64_t blk_off_K(int C, int dk, int es) { return 2 * tri_elems(C, es) + 2 * int64_t(C) * dk; }
 __host__ __device__ constexpr int64_t blk_g_byte(int C, int dk, int es) {
-  return (2 * int64_t(C) * C + 3 * int64_t(C) * dk) * es;
+  return (2 * tri_elems(C, es) + 3 * int64_t(C) * dk) * es;
 }
 __host__ __device__ constexpr int64_t blk_bytes(int C, int dk, int es) {
   return (blk_g_byte(C, dk, es) + 4 * int64_t(dk) + 255) & ~int64_t(255);

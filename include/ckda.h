@@ -148,7 +148,7 @@ typedef struct {
  * batch and ceil(T / chunk_size) + num_seqs for a packed one, plus the chunk
  * map of a packed batch, plus (sign_absorb = 1) the absorbed q, k, |alpha|,
  * beta for every value head and two sign masks.  At B=8, T=4096, H=16,
- * dk=128, chunk 64, bf16: 516 MiB (1.03 GiB with sign_absorb).
+ * dk=128, chunk 64, bf16: 484 MiB (0.97 GiB with sign_absorb).
  */
 size_t ckda_chunk_fwd_workspace_size(const ckda_fwd_desc_t* desc, int32_t packed);
 
@@ -200,7 +200,7 @@ ckda_status_t ckda_chunk_fwd(const ckda_fwd_desc_t* desc, const void* q,
  * Arguments, layouts, supported shapes and validation are those of
  * ckda_chunk_fwd.  A call whose workspace (ckda_chunk_fwd_workspace_size)
  * would exceed the scratch returns CKDA_ERR_WORKSPACE_TOO_SMALL before any
- * HIP call: at dk = dv = 128, chunk 64, bf16 that is about 2,000
+ * HIP call: at dk = dv = 128, chunk 64, bf16 that is about 2,160
  * (head, chunk) pairs, e.g. 16 heads of 8,000 tokens.  Every call on one GPU
  * shares that GPU's scratch, and each call rewrites all of it that it reads
  * (nothing needs to start at zero), so calls on one GPU must not overlap:
@@ -311,8 +311,8 @@ ckda_status_t ckda_chunk_bwd(const ckda_fwd_desc_t* desc, const void* q, const v
  * gradients are ckda_chunk_bwd's: the records are the same kernels' output
  * on the same inputs.
  *
- * For a layer of B=8, T=4096, H=16, d=128 in bf16, `saved` is 1.35 GB, of
- * which the records take 0.94 GB; the backward call no longer runs the
+ * For a layer of B=8, T=4096, H=16, d=128 in bf16, `saved` is 1.31 GB, of
+ * which the records take 0.91 GB; the backward call no longer runs the
  * forward's two passes.
  */
 ckda_status_t ckda_chunk_fwd_save(const ckda_fwd_desc_t* desc, const void* q, const void* k,

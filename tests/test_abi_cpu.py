@@ -99,13 +99,15 @@ def test_fwd_cu_seqlens_needs_batch_one():
 
 def test_workspace_size_formula():
     """One block per (head, chunk): (2C^2 + 3C dk) elements + dk floats, rounded up to
-    256 bytes, plus one int32 flag per (head, chunk) slot; dense batches have
-    B*ceil(T/C) chunks, packed ones ceil(T/C) + N slots plus the chunk map
-    (an int32 pair per slot, first[N+1], the owner per slot, the order[N])."""
+    256 bytes (at chunk 64 in bf16 the lower-triangular X' and P' keep 3/4 of
+    C^2 each: their first 32 rows half long), plus one int32 flag per (head,
+    chunk) slot; dense batches have B*ceil(T/C) chunks, packed ones
+    ceil(T/C) + N slots plus the chunk map (an int32 pair per slot, first[N+1],
+    the owner per slot, the order[N])."""
     up = lambda x: -(-x // 256) * 256
     d = _desc(B=8, T=4096, H=16, dk=128, dv=128, num_seqs=8)
-    blk = (2 * 64 * 64 + 3 * 64 * 128) * 2 + 128 * 4
-    assert blk % 256 == 0
+    blk = (2 * (32 * 32 + 32 * 64) + 3 * 64 * 128) * 2 + 128 * 4
+    assert blk % 256 == 0 and blk == 61952
     assert ck.chunk_fwd_workspace_size(d, False) == up(4 * 16 * 8 * 64) + 16 * 8 * 64 * blk
     d = _desc(B=1, T=70, H=3, dk=32, dv=32, num_seqs=4, chunk_size=16, io_dtype=ck.F32)
     blk = up((2 * 16 * 16 + 3 * 16 * 32) * 4 + 32 * 4)
